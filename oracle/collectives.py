@@ -1,0 +1,250 @@
+"""Plain, slow, obviously-correct collective reductions (test infrastructure).
+
+Every function takes the p rank buffers as a 2-D NumPy array ``xs`` of shape
+(p, n): row r is rank r's buffer.  Storage types:
+
+    "int32"    -> numpy.int32
+    "float32"  -> numpy.float32
+    "bfloat16" -> numpy.uint16 holding bf16 bit patterns (see ``bf16``)
+
+Accumulator type (the type every partial result is held in): int32 for int32,
+float32 for float32 and for bfloat16 (bf16 inputs are widened exactly, folded
+in float32 and rounded to bf16 once, at the end).
+
+Readings of what the pages leave open (each one is also listed in the design
+notes of the repository):
+
+* Ring direction: every rank sends to rank r+1 (mod p) -- "the next card on
+  the ring" in page "LLM Parallelism 基础", section "Ring AllReduce".
+* Which chunk moves at which step: in reduce-scatter step s (0-based) rank r
+  sends chunk (r-1-s) mod p; in all-gather step s it sends chunk (r-s) mod p.
+  It is the only assignment with that direction that leaves rank c holding
+  the reduced chunk c after p-1 steps, which the same section states (and
+  which the worked example of page "分布式训练/推理", section "通信原语",
+  shows: rank 0 receives [6]).
+* The receiver combines ``op(message, local)``: the partial that arrives is
+  the running accumulator, the local value is the next term.  For chunk c the
+  fold order is therefore x_{c+1}, x_{c+2}, ..., x_{c+p-1}, x_c (mod p).
+* Uneven split: the pages cut the data evenly.  When p does not divide n the
+  chunk bounds are floor(c*n/p); reduce-scatter and all-gather require p | n.
+* Reduce folds ranks in ascending order 0..p-1, the order of the sum in the
+  all-reduce formula of page "分布式训练/推理"; the pages give no reduce
+  algorithm.
+* Sum of int32 wraps modulo 2**32 (two's complement).
+* max / min are compare-and-select with the running value as first operand:
+  max keeps the running value unless the new value is strictly greater (min:
+  strictly less).  Ties, including +0 against -0, keep the earlier operand;
+  a NaN running value stays; a NaN new value is skipped.
+* Hierarchical: contiguous groups [jG, jG+G), representative = the group's
+  first rank; group partials fold ascending in the accumulator type and stay
+  in it (no rounding at the representative); the representatives' partials
+  fold ascending over groups; one final conversion; every rank receives the
+  result.
+"""
+
+import numpy as np
+
+from . import bf16
+
+DTYPES = ("int32", "float32", "bfloat16")
+OPS = ("sum", "max", "min")
+
+_STORAGE = {"int32": np.int32, "float32": np.float32, "bfloat16": np.uint16}
+
+
+def _check(xs, dtype, op=None):
+    if dtype not in _STORAGE:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    if op is not None and op not in OPS:
+        raise ValueError(f"unknown op {op!r}")
+    xs = np.asarray(xs)
+    if xs.ndim != 2:
+        raise ValueError("xs must have shape (p, n)")
+    if xs.dtype != _STORAGE[dtype]:
+        raise TypeError(f"{dtype} buffers must be stored as {_STORAGE[dtype].__name__}")
+    return xs
+
+
+def to_acc(x, dtype):
+    """One rank's buffer (or a slice of it) -> a fresh accumulator-type copy."""
+    if dtype == "bfloat16":
+        return bf16.widen(x)
+    return np.array(x, dtype=_STORAGE[dtype], copy=True)
+
+
+def from_acc(a, dtype):
+    """Accumulator values -> storage type (one rounding, for bf16 only)."""
+    if dtype == "bfloat16":
+        return bf16.narrow(a)
+    return np.array(a, dtype=_STORAGE[dtype], copy=True)
+
+
+def combine(acc, v, op):
+    """One fold step: the running value ``acc`` combined with the next term ``v``."""
+    if op == "sum":
+        return acc + v  # NumPy array addition: IEEE RNE for float32, wrap for int32
+    if op == "max":
+        return np.where(v > acc, v, acc)
+    if op == "min":
+        return np.where(v < acc, v, acc)
+    raise ValueError(f"unknown op {op!r}")
+
+
+def chunk_bounds(n, p):
+    """Start of every chunk plus the end: [floor(c*n/p) for c in 0..p]."""
+    return [(c * n) // p for c in range(p + 1)]
+
+
+def ring_schedule(p):
+    """The ring's transfers as (phase, step, src, dst, chunk) tuples.
+
+    Page "LLM Parallelism 基础", section "Ring AllReduce": phase "rs" has p-1
+    steps in which each rank passes one chunk to the next rank and the
+    receiver accumulates; phase "ag" has p-1 steps in which the receiver
+    overwrites.  2(p-1) steps, p transfers per step.
+    """
+    out = []
+    for s in range(p - 1):
+        for r in range(p):
+            out.append(("rs", s, r, (r + 1) % p, (r - 1 - s) % p))
+    for s in range(p - 1):
+        for r in range(p):
+            out.append(("ag", s, r, (r + 1) % p, (r - s) % p))
+    return out
+
+
+def simulate_ring(xs, op, dtype, phases=("rs", "ag")):
+    """Run the ring schedule literally on p separate accumulator buffers.
+
+    Returns the list of p buffers (accumulator type) after the given phases.
+    Within one step every message is read before any receiver updates (all
+    ranks send at once).
+    """
+    xs = _check(xs, dtype, op)
+    p, n = xs.shape
+    b = chunk_bounds(n, p)
+    buf = [to_acc(xs[r], dtype) for r in range(p)]
+    sched = ring_schedule(p)
+    for phase in phases:
+        for s in range(p - 1):
+            moves = [t for t in sched if t[0] == phase and t[1] == s]
+            msgs = [buf[src][b[c]:b[c + 1]].copy() for (_, _, src, _, c) in moves]
+            for (_, _, _, dst, c), msg in zip(moves, msgs):
+                lo, hi = b[c], b[c + 1]
+                if phase == "rs":
+                    buf[dst][lo:hi] = combine(msg, buf[dst][lo:hi], op)
+                else:
+                    buf[dst][lo:hi] = msg
+    return buf
+
+
+def all_reduce_ring(xs, op, dtype):
+    """Ring all-reduce (reduce-scatter then all-gather); shape (p, n) result."""
+    buf = simulate_ring(xs, op, dtype)
+    return np.stack([from_acc(bb, dtype) for bb in buf])
+
+
+def reduce_scatter_ring(xs, op, dtype):
+    """Ring reduce-scatter: row c of the (p, n/p) result is reduced chunk c."""
+    xs = _check(xs, dtype, op)
+    p, n = xs.shape
+    if n % p:
+        raise ValueError("reduce-scatter needs p | n")
+    buf = simulate_ring(xs, op, dtype, phases=("rs",))
+    L = n // p
+    return np.stack([from_acc(buf[c][c * L:(c + 1) * L], dtype) for c in range(p)])
+
+
+def all_gather(shards):
+    """All-gather: every rank receives the concatenation of the p shards."""
+    shards = np.asarray(shards)
+    p = shards.shape[0]
+    full = np.concatenate([shards[c] for c in range(p)])
+    return np.stack([full.copy() for _ in range(p)])
+
+
+def fold_elements_ring_order(cols, chunk_of, op, dtype):
+    """Ring-order fold of selected elements.
+
+    ``cols`` has shape (p, m): the p ranks' values at m element positions;
+    ``chunk_of`` (m,) gives the chunk each position lies in.  Position i of
+    chunk c folds x_{c+1}, x_{c+2}, ..., x_c (mod p).  Returns (m,) results in
+    the storage type.
+    """
+    cols = _check(cols, dtype, op)
+    chunk_of = np.asarray(chunk_of, dtype=np.int64)
+    p, m = cols.shape
+    acc_rows = [to_acc(cols[r], dtype) for r in range(p)]
+    res = to_acc(cols[0], dtype)
+    for c in np.unique(chunk_of):
+        sel = chunk_of == c
+        acc = acc_rows[(c + 1) % p][sel]
+        for k in range(2, p + 1):
+            acc = combine(acc, acc_rows[(c + k) % p][sel], op)
+        res[sel] = acc
+    return from_acc(res, dtype)
+
+
+def all_reduce_fold(xs, op, dtype):
+    """Ring all-reduce written as the per-chunk formula (independent of the
+    schedule simulation): chunk c folds x_{c+1}, ..., x_c; every rank gets y."""
+    xs = _check(xs, dtype, op)
+    p, n = xs.shape
+    b = chunk_bounds(n, p)
+    y = np.empty(n, dtype=xs.dtype)
+    for c in range(p):
+        lo, hi = b[c], b[c + 1]
+        acc = to_acc(xs[(c + 1) % p, lo:hi], dtype)
+        for k in range(2, p + 1):
+            acc = combine(acc, to_acc(xs[(c + k) % p, lo:hi], dtype), op)
+        y[lo:hi] = from_acc(acc, dtype)
+    return np.stack([y.copy() for _ in range(p)])
+
+
+def reduce(xs, op, dtype):
+    """Reduce to one rank: ascending fold x_0, x_1, ..., x_{p-1}; shape (n,)."""
+    xs = _check(xs, dtype, op)
+    acc = to_acc(xs[0], dtype)
+    for r in range(1, xs.shape[0]):
+        acc = combine(acc, to_acc(xs[r], dtype), op)
+    return from_acc(acc, dtype)
+
+
+def broadcast(x, p):
+    """Broadcast: every one of the p ranks receives a copy of the root's buffer."""
+    x = np.asarray(x)
+    return np.stack([x.copy() for _ in range(p)])
+
+
+def all_reduce_hier(xs, op, dtype, group_size):
+    """Hierarchical all-reduce in the steps of page "大模型并行的最小闭环",
+    section "Source Log: 2026-05-05" (hierarchical AllReduce + SHARP).
+
+    Step 1: inside each group the members' buffers are reduced (ascending) into
+    the representative, kept in the accumulator type.  Step 2: the
+    representative is the group's first rank.  Steps 3-4: the representatives'
+    partials are combined (ascending over groups).  Step 5: the result goes back
+    to every representative.  Step 6: each representative broadcasts it inside
+    its group.  Returns the (p, n) outputs.
+    """
+    xs = _check(xs, dtype, op)
+    p, n = xs.shape
+    G = int(group_size)
+    if G < 1 or p % G:
+        raise ValueError("group_size must divide p")
+    groups = [list(range(j * G, (j + 1) * G)) for j in range(p // G)]
+    partial = []
+    for members in groups:  # steps 1-2
+        acc = to_acc(xs[members[0]], dtype)
+        for r in members[1:]:
+            acc = combine(acc, to_acc(xs[r], dtype), op)
+        partial.append(acc)
+    total = partial[0]  # steps 3-4
+    for g in partial[1:]:
+        total = combine(total, g, op)
+    result = from_acc(total, dtype)
+    out = np.empty_like(xs)
+    for members in groups:  # steps 5-6
+        for r in members:
+            out[r] = result
+    return out

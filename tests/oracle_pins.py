@@ -1,0 +1,483 @@
+"""Pins of the CPU oracle to facts outside the oracle itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+a value printed on the pages, a closed form, a hand-derived IEEE-754 probe, a
+library routine or brute force.  ``test_oracle.py`` runs them all;
+``test_oracle_mutations.py`` plants plausible mistakes in the oracle (on the
+CPU) and checks that at least one pin catches each.
+
+Pins resolve every oracle function through its module at call time, so a
+monkeypatched mistake is seen.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+
+from oracle import bf16 as B
+from oracle import collectives as C
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+TWO24 = float(2 ** 24)
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        return json.load(f)
+
+
+def enc(values, dtype):
+    """Python numbers (exactly representable) -> oracle storage array."""
+    a = np.asarray(values, dtype=np.float64)
+    if dtype == "int32":
+        return a.astype(np.int32)
+    if dtype == "float32":
+        return a.astype(np.float32)
+    f = a.astype(np.float32)
+    u = f.view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0), "test value not exactly representable in bf16"
+    return (u >> 16).astype(np.uint16)
+
+
+def dec(arr, dtype):
+    """Oracle storage array -> float64 values (bf16 decoded by bit shifting here,
+    not by the oracle's codec)."""
+    arr = np.asarray(arr)
+    if dtype == "bfloat16":
+        return (arr.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return arr.astype(np.float64)
+
+
+def bits(arr):
+    arr = np.ascontiguousarray(arr)
+    return arr.view({1: np.uint8, 2: np.uint16, 4: np.uint32, 8: np.uint64}[arr.itemsize])
+
+
+# ---------------------------------------------------------------------------
+# Worked example printed on page "分布式训练/推理", section "通信原语".
+
+def pin_worked_example(dtype):
+    g = _golden("worked_example.json")
+    xs = enc(g["inputs"], dtype)
+    p = g["p"]
+    want = np.array(g["all_reduce"], dtype=np.float64)
+    for f in (C.all_reduce_ring, C.all_reduce_fold):
+        y = f(xs, "sum", dtype)
+        assert y.shape == (p, 4)
+        for r in range(p):
+            assert np.array_equal(dec(y[r], dtype), want), (f.__name__, r, y[r])
+    rs = C.reduce_scatter_ring(xs, "sum", dtype)
+    assert np.array_equal(dec(rs, dtype), np.array(g["reduce_scatter"], dtype=np.float64)), rs
+    ag = C.all_gather(rs)
+    for r in range(p):
+        assert np.array_equal(dec(ag[r], dtype), np.array(g["all_gather_of_reduce_scatter"], dtype=np.float64))
+    # Reduce to one rank then broadcast has the same effect (page "LLM
+    # Parallelism 基础", section "MPI Collective Operations").
+    red = C.reduce(xs, "sum", dtype)
+    assert np.array_equal(dec(red, dtype), want)
+    bc = C.broadcast(red, p)
+    assert np.array_equal(dec(bc, dtype), np.stack([want] * p))
+    # The hierarchical variant reaches the same sum (2 groups of 2, 4 of 1, 1 of 4).
+    for G in (1, 2, 4):
+        h = C.all_reduce_hier(xs, "sum", dtype, G)
+        assert np.array_equal(dec(h, dtype), np.stack([want] * p)), (G, h)
+
+
+def pin_worked_example_max_min(dtype):
+    """max/min of the same inputs, derived from the definitions: the largest
+    input row is x_3 = [3,4,5,6], the smallest x_0 = [0,1,2,3]."""
+    g = _golden("worked_example.json")
+    xs = enc(g["inputs"], dtype)
+    for op, want in (("max", [3, 4, 5, 6]), ("min", [0, 1, 2, 3])):
+        for f in (C.all_reduce_ring, C.all_reduce_fold):
+            y = f(xs, op, dtype)
+            assert np.array_equal(dec(y, dtype), np.stack([np.array(want, float)] * 4)), (op, f.__name__)
+        rs = C.reduce_scatter_ring(xs, op, dtype)
+        assert np.array_equal(dec(rs, dtype).ravel(), np.array(want, float))
+        assert np.array_equal(dec(C.reduce(xs, op, dtype), dtype), np.array(want, float))
+
+
+# ---------------------------------------------------------------------------
+# Closed form: x_r[j] = (j mod 16) + r  =>  sum y[j] = p (j mod 16) + p(p-1)/2,
+# max y[j] = (j mod 16) + p - 1, min y[j] = j mod 16 (all exact in every dtype
+# for the p used here).
+
+def closed_form_inputs(p, n, dtype):
+    j = np.arange(n) % 16
+    return enc(np.stack([j + r for r in range(p)]), dtype)
+
+
+def closed_form_expected(p, n, op):
+    j = (np.arange(n) % 16).astype(np.float64)
+    if op == "sum":
+        return p * j + p * (p - 1) / 2
+    if op == "max":
+        return j + p - 1
+    return j
+
+
+def pin_closed_form(p, n, dtype):
+    xs = closed_form_inputs(p, n, dtype)
+    for op in C.OPS:
+        want = closed_form_expected(p, n, op)
+        for f in (C.all_reduce_ring, C.all_reduce_fold):
+            y = f(xs, op, dtype)
+            assert np.array_equal(dec(y, dtype), np.stack([want] * p)), (f.__name__, op, p, n)
+        assert np.array_equal(dec(C.reduce(xs, op, dtype), dtype), want), (op, p, n)
+        for G in [g for g in range(1, p + 1) if p % g == 0]:
+            assert np.array_equal(dec(C.all_reduce_hier(xs, op, dtype, G), dtype), np.stack([want] * p))
+        if n % p == 0:
+            rs = C.reduce_scatter_ring(xs, op, dtype)
+            L = n // p
+            assert np.array_equal(dec(rs, dtype), want.reshape(p, L))
+            assert np.array_equal(dec(C.all_gather(rs), dtype), np.stack([want] * p))
+
+
+# ---------------------------------------------------------------------------
+# Hand-derived IEEE-754 probes of the fold order.
+#
+# fp32 has a 24-bit significand: 2^24 + 1 is exactly halfway between 2^24 and
+# 2^24 + 2 and rounds (ties to even) to 2^24, while -2^24 + 1 = -16777215 is
+# exact.  So the order of the additions decides the result.
+
+def ring_order_probe_inputs():
+    """p = 4, n = 4, chunk c = element c.  Ring order folds chunk c as
+    x_{c+1}, x_{c+2}, x_{c+3}, x_c; the probe puts 2^24, 1, 1, -2^24 there:
+    (((2^24 + 1) + 1) - 2^24) = 0 in fp32.  Ascending rank order would give
+    [2, 2, 2, 0]; starting at rank c, or running the ring backwards, gives
+    [2, 2, 2, 2]."""
+    p = 4
+    rows = np.zeros((p, p), dtype=np.float64)
+    for c in range(p):
+        rows[(c + 1) % p, c] = TWO24
+        rows[(c + 2) % p, c] = 1.0
+        rows[(c + 3) % p, c] = 1.0
+        rows[c % p, c] = -TWO24
+    return rows
+
+
+def pin_ring_order_probe(dtype):
+    assert dtype in ("float32", "bfloat16")
+    xs = enc(ring_order_probe_inputs(), dtype)
+    want = np.zeros(4)
+    for f in (C.all_reduce_ring, C.all_reduce_fold):
+        y = f(xs, "sum", dtype)
+        assert np.array_equal(dec(y, dtype), np.stack([want] * 4)), (f.__name__, y)
+    rs = C.reduce_scatter_ring(xs, "sum", dtype)
+    assert np.array_equal(dec(rs, dtype).ravel(), want), rs
+    cols = xs
+    got = C.fold_elements_ring_order(cols, np.arange(4), "sum", dtype)
+    assert np.array_equal(dec(got, dtype), want), got
+
+
+def pin_reduce_order_probe(dtype):
+    """Reduce folds ranks 0..p-1: x = [2^24, 1, 1, -2^24] gives 0 in fp32
+    (descending order would give 2)."""
+    assert dtype in ("float32", "bfloat16")
+    xs = enc(np.array([[TWO24], [1.0], [1.0], [-TWO24]]), dtype)
+    assert dec(C.reduce(xs, "sum", dtype), dtype).tolist() == [0.0]
+
+
+def hier_probe_inputs():
+    """p = 8, groups of 4 = ranks {0..3} and {4..7}: x0 = 2^24, x2 = 1, x4 = 1,
+    x5 = -2^24, the rest 0.  Group 0 folds to 2^24 (the 1 is lost), group 1 to
+    1 - 2^24 = -16777215 (exact), and their sum is 1.  A flat fold in any rank
+    order that meets 2^24 before both ones gives 0; groups taken by stride
+    ({0,2,4,6}, {1,3,5,7}) give 0; rounding group 1's partial to bf16 at the
+    representative gives -2^24 and then 0."""
+    x = np.zeros((8, 1))
+    x[0, 0] = TWO24
+    x[2, 0] = 1.0
+    x[4, 0] = 1.0
+    x[5, 0] = -TWO24
+    return x
+
+
+def hier_probe_groups_of_2_inputs():
+    """p = 8, groups of 2: partials g0 = 2^24, g1 = 1, g2 = 1, g3 = -2^24 fold
+    ascending over groups to 0 (descending would give 2)."""
+    x = np.zeros((8, 1))
+    x[0, 0] = TWO24
+    x[2, 0] = 1.0
+    x[4, 0] = 1.0
+    x[6, 0] = -TWO24
+    return x
+
+
+def pin_hier_probe(dtype):
+    assert dtype in ("float32", "bfloat16")
+    y = C.all_reduce_hier(enc(hier_probe_inputs(), dtype), "sum", dtype, 4)
+    assert np.array_equal(dec(y, dtype), np.ones((8, 1))), y
+    y2 = C.all_reduce_hier(enc(hier_probe_groups_of_2_inputs(), dtype), "sum", dtype, 2)
+    assert np.array_equal(dec(y2, dtype), np.zeros((8, 1))), y2
+
+
+# ---------------------------------------------------------------------------
+# bf16 codec: round to nearest even, checked by hand and against torch (CPU).
+
+def pin_bf16_rounding_hand():
+    cases = [
+        (1.0 + 2.0 ** -8, 0x3F80),          # halfway, even neighbour below
+        (1.0 + 3 * 2.0 ** -8, 0x3F82),      # halfway, even neighbour above
+        (1.0 + 2.0 ** -8 + 2.0 ** -20, 0x3F81),  # just above halfway
+        (1.0 + 2.0 ** -8 - 2.0 ** -20, 0x3F80),  # just below halfway
+        (TWO24 + 1.0, 0x4B80),              # fp32 rounds 2^24+1 first; bf16 of 2^24
+        (-1.5, 0xBFC0),
+        (0.0, 0x0000),
+        (-0.0, 0x8000),
+        (float(np.finfo(np.float32).max), 0x7F80),  # rounds up to +inf
+        (-float(np.finfo(np.float32).max), 0xFF80),
+        (float("inf"), 0x7F80),
+        (float("-inf"), 0xFF80),
+        (2.0 ** -133, 0x0001),              # smallest bf16 denormal (2^-126 * 2^-7)
+        (2.0 ** -134, 0x0000),              # half of it: tie to even (0)
+        (3 * 2.0 ** -134, 0x0002),          # 1.5 of it: tie to even (2)
+    ]
+    f = np.array([c[0] for c in cases], dtype=np.float32)
+    got = B.narrow(f)
+    want = np.array([c[1] for c in cases], dtype=np.uint16)
+    assert np.array_equal(got, want), [(hex(a), hex(b)) for a, b in zip(got, want)]
+    # widen is exact: every bf16 pattern survives widen -> narrow unchanged
+    # (non-NaN patterns) and widen places the 16 bits in the upper half.
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    w = B.widen(h)
+    assert np.array_equal(w.view(np.uint32), h.astype(np.uint32) << 16)
+    nonnan = (h & 0x7FFF) <= 0x7F80
+    assert np.array_equal(B.narrow(w)[nonnan], h[nonnan])
+
+
+def pin_bf16_nan():
+    """A NaN keeps its sign and is quiet after narrowing, even when its payload
+    sits only in the low 16 bits (truncation would turn it into an infinity)."""
+    u = np.array([0x7F800001, 0xFF800001, 0x7FC00000, 0x7FA00000, 0xFFFFFFFF], dtype=np.uint32)
+    got = B.narrow(u.view(np.float32))
+    want = np.array([0x7FC0, 0xFFC0, 0x7FC0, 0x7FE0, 0xFFFF], dtype=np.uint16)
+    assert np.array_equal(got, want), [hex(x) for x in got]
+
+
+def pin_bf16_vs_torch(seed=7, count=1 << 20):
+    """Independent check against torch's CPU float32 -> bfloat16 conversion
+    (round to nearest even) on special classes and a stratified sample of bit
+    patterns (NaNs excluded: torch returns one canonical NaN)."""
+    import torch
+
+    rng = np.random.default_rng(seed)
+    u = rng.integers(0, 2 ** 32, size=count, dtype=np.uint64).astype(np.uint32)
+    # make sure every exponent and the tie / near-tie low halves are present
+    u[: 1 << 16] = (np.arange(1 << 16, dtype=np.uint32) << 16) | np.uint32(0x8000)
+    u[1 << 16: 2 << 16] = (np.arange(1 << 16, dtype=np.uint32) << 16) | np.uint32(0x7FFF)
+    u[2 << 16: 3 << 16] = (np.arange(1 << 16, dtype=np.uint32) << 16) | np.uint32(0x8001)
+    f = u.view(np.float32)
+    f = f[~np.isnan(f)]
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(B.narrow(f), want)
+
+
+# ---------------------------------------------------------------------------
+# Integer and max/min rules.
+
+def pin_int32_wrap():
+    xs = np.array([[2 ** 31 - 1, -(2 ** 31), 5], [1, -1, -7]], dtype=np.int32)
+    want = np.array([-(2 ** 31), 2 ** 31 - 1, -2], dtype=np.int32)
+    for f in (C.all_reduce_ring, C.all_reduce_fold):
+        assert np.array_equal(f(xs, "sum", "int32"), np.stack([want, want]))
+    assert np.array_equal(C.reduce(xs, "sum", "int32"), want)
+
+
+def pin_max_min_signed_zero():
+    """p = 2, one element (chunk 1 holds it, so the fold is x_0 then x_1).
+    Compare-and-select keeps the running value on ties: max(-0, +0) and
+    min(-0, +0) with -0 first both give -0; with +0 first both give +0."""
+    for first, second in ((-0.0, 0.0), (0.0, -0.0)):
+        xs = np.array([[first], [second]], dtype=np.float32)
+        for op in ("max", "min"):
+            for f in (C.all_reduce_ring, C.all_reduce_fold):
+                y = f(xs, op, "float32")
+                assert np.all(np.signbit(y) == np.signbit(np.float32(first))), (op, first, y)
+            red = C.reduce(xs, op, "float32")
+            assert np.signbit(red[0]) == np.signbit(np.float32(first))
+    # A chunk whose fold starts at rank 1: p = 2, n = 2, element 0 is chunk 0,
+    # whose fold is x_1 then x_0.
+    xs = np.array([[0.0, 0.0], [-0.0, 0.0]], dtype=np.float32)
+    y = C.all_reduce_ring(xs, "max", "float32")
+    assert np.signbit(y[0, 0]) and np.signbit(y[1, 0]), y
+
+
+# ---------------------------------------------------------------------------
+# Brute force on tiny random inputs.
+
+def _wrap32(v):
+    v &= 0xFFFFFFFF
+    return v - (1 << 32) if v >= (1 << 31) else v
+
+
+def pin_bruteforce_int(seed):
+    rng = np.random.default_rng(seed)
+    for _ in range(25):
+        p = int(rng.integers(1, 9))
+        n = int(rng.integers(0, 65))
+        big = bool(rng.integers(0, 2))
+        lim = 2 ** 31 if big else 2 ** 20
+        xs = rng.integers(-lim, lim, size=(p, n), dtype=np.int64).astype(np.int32)
+        want_sum = np.array([_wrap32(sum(int(xs[r, j]) for r in range(p))) for j in range(n)], dtype=np.int32)
+        want_max = np.array([max(int(xs[r, j]) for r in range(p)) for j in range(n)], dtype=np.int32)
+        want_min = np.array([min(int(xs[r, j]) for r in range(p)) for j in range(n)], dtype=np.int32)
+        for op, want in (("sum", want_sum), ("max", want_max), ("min", want_min)):
+            for f in (C.all_reduce_ring, C.all_reduce_fold):
+                assert np.array_equal(f(xs, op, "int32"), np.stack([want] * p)), (op, p, n)
+            assert np.array_equal(C.reduce(xs, op, "int32"), want)
+            if n % p == 0:
+                assert np.array_equal(C.reduce_scatter_ring(xs, op, "int32").ravel(), want)
+            for G in [g for g in range(1, p + 1) if p % g == 0]:
+                assert np.array_equal(C.all_reduce_hier(xs, op, "int32", G), np.stack([want] * p))
+
+
+def _gamma(k):
+    u = 2.0 ** -24
+    return k * u / (1 - k * u)
+
+
+def pin_bruteforce_float(seed):
+    """float32 sums lie within the a-priori bound of recursive summation,
+    |y - exact| <= gamma_{p-1} * sum_r |x_r| (exact sum by math.fsum); bf16
+    outputs add half an ulp of the result.  max/min equal numpy's reductions
+    (no signed zeros or NaNs in these inputs).  Integer-valued float inputs
+    give exact sums."""
+    rng = np.random.default_rng(seed)
+    for _ in range(20):
+        p = int(rng.integers(1, 9))
+        n = int(rng.integers(0, 65))
+        x = rng.standard_normal((p, n)) * np.exp(rng.uniform(-8, 8, size=(p, n)))
+        for dtype in ("float32", "bfloat16"):
+            xs = enc(x.astype(np.float32).astype(np.float64), "float32") if dtype == "float32" else B.narrow(x.astype(np.float32))
+            vals = dec(xs, dtype)
+            exact = np.array([math.fsum(vals[:, j]) for j in range(n)])
+            absum = np.abs(vals).sum(axis=0)
+            outs = [C.all_reduce_ring(xs, "sum", dtype)[0], C.all_reduce_fold(xs, "sum", dtype)[0],
+                    C.reduce(xs, "sum", dtype)]
+            outs += [C.all_reduce_hier(xs, "sum", dtype, G)[0] for G in range(1, p + 1) if p % G == 0]
+            for y in outs:
+                err = np.abs(dec(y, dtype) - exact)
+                bound = _gamma(max(p - 1, 0)) * absum * (1 + 1e-12)
+                if dtype == "bfloat16":
+                    bound = bound + np.abs(exact) * 2.0 ** -8 + 1e-300
+                assert np.all(err <= bound), (dtype, p, n, err.max())
+            for op, ref in (("max", np.max), ("min", np.min)):
+                if n == 0:
+                    continue
+                want = ref(vals, axis=0)
+                for y in (C.all_reduce_ring(xs, op, dtype)[0], C.all_reduce_fold(xs, op, dtype)[0],
+                          C.reduce(xs, op, dtype)):
+                    assert np.array_equal(dec(y, dtype), want), (op, dtype)
+        ints = rng.integers(-1000, 1000, size=(p, n)).astype(np.float32)
+        y = C.all_reduce_ring(ints, "sum", "float32")
+        assert np.array_equal(y[0].astype(np.float64), ints.astype(np.float64).sum(axis=0))
+
+
+# ---------------------------------------------------------------------------
+# Identities and the schedule.
+
+def random_inputs(rng, p, n, dtype):
+    if dtype == "int32":
+        return rng.integers(-(2 ** 31), 2 ** 31, size=(p, n), dtype=np.int64).astype(np.int32)
+    f = rng.standard_normal((p, n)).astype(np.float32)
+    return f if dtype == "float32" else B.narrow(f)
+
+
+def pin_identities(seed):
+    """all_reduce == all_gather(reduce_scatter) bitwise (page "分布式训练/推理",
+    section "通信原语"); the schedule simulation equals the per-chunk formula
+    bitwise; for int32 and max/min, all-reduce equals broadcast(reduce)
+    (page "LLM Parallelism 基础", section "MPI Collective Operations")."""
+    rng = np.random.default_rng(seed)
+    for p in (1, 2, 3, 4, 8):
+        for n in (0, p, 5 * p, 64 * p + p):
+            for dtype in C.DTYPES:
+                xs = random_inputs(rng, p, n, dtype)
+                for op in C.OPS:
+                    ar = C.all_reduce_ring(xs, op, dtype)
+                    assert np.array_equal(bits(ar), bits(C.all_reduce_fold(xs, op, dtype)))
+                    for r in range(p):
+                        assert np.array_equal(bits(ar[r]), bits(ar[0]))
+                    if n % p == 0:
+                        ag = C.all_gather(C.reduce_scatter_ring(xs, op, dtype))
+                        assert np.array_equal(bits(ag), bits(ar))
+                    if dtype == "int32" or op != "sum":
+                        bc = C.broadcast(C.reduce(xs, op, dtype), p)
+                        assert np.array_equal(bits(bc), bits(ar)), (dtype, op)
+                    chunk_of = np.searchsorted(np.array(C.chunk_bounds(n, p)[1:]), np.arange(n), side="right")
+                    sampled = C.fold_elements_ring_order(xs, chunk_of, op, dtype)
+                    assert np.array_equal(bits(sampled), bits(ar[0]))
+
+
+def pin_schedule_symbolic(p):
+    """Page "LLM Parallelism 基础", section "Ring AllReduce": 2(p-1) steps; in
+    every step each rank sends exactly one chunk to the next rank and receives
+    exactly one; after reduce-scatter rank c holds chunk c with every rank's
+    contribution exactly once, gathered in the order c+1, c+2, ..., c; after
+    all-gather every rank holds every chunk complete."""
+    sched = C.ring_schedule(p)
+    assert len(sched) == 2 * (p - 1) * p
+    steps = sorted({(ph, s) for ph, s, *_ in sched})
+    assert len(steps) == 2 * (p - 1)
+    order = [[[r] for c in range(p)] for r in range(p)]  # order[rank][chunk]
+    for ph, s in [("rs", s) for s in range(p - 1)] + [("ag", s) for s in range(p - 1)]:
+        moves = [t for t in sched if t[0] == ph and t[1] == s]
+        assert sorted(t[2] for t in moves) == list(range(p))
+        assert sorted(t[3] for t in moves) == list(range(p))
+        assert all(t[3] == (t[2] + 1) % p for t in moves)
+        msgs = [list(order[t[2]][t[4]]) for t in moves]
+        for (_, _, src, dst, c), msg in zip(moves, msgs):
+            if ph == "rs":
+                assert not set(msg) & set(order[dst][c])
+                order[dst][c] = msg + order[dst][c]
+            else:
+                order[dst][c] = msg
+        if ph == "rs" and s == p - 2:
+            for c in range(p):
+                assert order[c][c] == [(c + k) % p for k in range(1, p + 1)], (c, order[c][c])
+    full = {c: [(c + k) % p for k in range(1, p + 1)] for c in range(p)}
+    for r in range(p):
+        for c in range(p):
+            assert order[r][c] == full[c] or p == 1
+
+
+def pin_hier_vs_flat(seed):
+    """int32: hierarchical == flat bitwise; float32: within the recursive
+    summation bound of each other."""
+    rng = np.random.default_rng(seed)
+    for p, G in ((8, 4), (8, 2), (6, 3), (4, 4), (4, 1)):
+        xi = random_inputs(rng, p, 257, "int32")
+        for op in C.OPS:
+            assert np.array_equal(C.all_reduce_hier(xi, op, "int32", G), C.all_reduce_ring(xi, op, "int32"))
+        xf = random_inputs(rng, p, 257, "float32")
+        h = C.all_reduce_hier(xf, "sum", "float32", G)[0].astype(np.float64)
+        f = C.all_reduce_ring(xf, "sum", "float32")[0].astype(np.float64)
+        absum = np.abs(xf.astype(np.float64)).sum(axis=0)
+        assert np.all(np.abs(h - f) <= 2 * _gamma(p - 1) * absum * (1 + 1e-12))
+        for op in ("max", "min"):
+            assert np.array_equal(C.all_reduce_hier(xf, op, "float32", G), C.all_reduce_ring(xf, op, "float32"))
+
+
+def pin_edge_cases():
+    for dtype in C.DTYPES:
+        st = {"int32": np.int32, "float32": np.float32, "bfloat16": np.uint16}[dtype]
+        empty = np.zeros((4, 0), dtype=st)
+        for op in C.OPS:
+            assert C.all_reduce_ring(empty, op, dtype).shape == (4, 0)
+            assert C.all_reduce_fold(empty, op, dtype).shape == (4, 0)
+            assert C.reduce_scatter_ring(empty, op, dtype).shape == (4, 0)
+            assert C.reduce(empty, op, dtype).shape == (0,)
+        one = enc([[3, -2, 7]], dtype if dtype != "int32" else "int32")
+        for op in C.OPS:
+            assert np.array_equal(C.all_reduce_ring(one, op, dtype), one)
+            assert np.array_equal(C.reduce(one, op, dtype), one[0])
+        # fewer elements than ranks: some chunks are empty
+        xs = enc([[1, 2], [3, 4], [5, 6], [7, 8], [9, 10]], dtype)
+        y = C.all_reduce_ring(xs, "sum", dtype)
+        assert np.array_equal(dec(y, dtype), np.stack([np.array([25.0, 30.0])] * 5))
+    assert C.chunk_bounds(10, 4) == [0, 2, 5, 7, 10]
+    assert C.chunk_bounds(2, 5) == [0, 0, 0, 1, 1, 2]

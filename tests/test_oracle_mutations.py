@@ -1,0 +1,185 @@
+"""Plant plausible mistakes in the CPU oracle and check that its pins catch
+every one (a pin set that a dropped term, a swapped operand, a wrong index or
+a wrong rounding can pass would not be pinning anything).  CPU only; the
+mistakes live in monkeypatched copies of oracle functions for one test."""
+
+import numpy as np
+import pytest
+
+import oracle_pins as P
+from oracle import bf16 as B
+from oracle import collectives as C
+
+_combine = C.combine
+_narrow = B.narrow
+_to_acc = C.to_acc
+
+
+def _run_all_pins():
+    """Return the names of the pins that fail."""
+    failed = []
+    checks = [
+        ("worked_example", lambda: [P.pin_worked_example(d) for d in C.DTYPES]),
+        ("worked_example_max_min", lambda: [P.pin_worked_example_max_min(d) for d in C.DTYPES]),
+        ("closed_form", lambda: [P.pin_closed_form(p, n, d) for d in C.DTYPES for p, n in ((3, 100), (8, 4099))]),
+        ("ring_order_probe", lambda: [P.pin_ring_order_probe(d) for d in ("float32", "bfloat16")]),
+        ("reduce_order_probe", lambda: [P.pin_reduce_order_probe(d) for d in ("float32", "bfloat16")]),
+        ("hier_probe", lambda: [P.pin_hier_probe(d) for d in ("float32", "bfloat16")]),
+        ("bf16_hand", P.pin_bf16_rounding_hand),
+        ("bf16_nan", P.pin_bf16_nan),
+        ("bf16_torch", lambda: P.pin_bf16_vs_torch(count=1 << 18)),
+        ("int32_wrap", P.pin_int32_wrap),
+        ("signed_zero", P.pin_max_min_signed_zero),
+        ("bruteforce_int", lambda: P.pin_bruteforce_int(0)),
+        ("bruteforce_float", lambda: P.pin_bruteforce_float(0)),
+        ("identities", lambda: P.pin_identities(3)),
+        ("schedule", lambda: [P.pin_schedule_symbolic(p) for p in (2, 3, 4, 8)]),
+        ("hier_vs_flat", lambda: P.pin_hier_vs_flat(1)),
+        ("edge_cases", P.pin_edge_cases),
+    ]
+    for name, fn in checks:
+        try:
+            with np.errstate(all="ignore"):
+                fn()
+        except Exception:  # noqa: BLE001 - any failure counts as caught
+            failed.append(name)
+    return failed
+
+
+def _sched_rs_off_by_one(p):
+    out = []
+    for s in range(p - 1):
+        for r in range(p):
+            out.append(("rs", s, r, (r + 1) % p, (r - s) % p))
+    for s in range(p - 1):
+        for r in range(p):
+            out.append(("ag", s, r, (r + 1) % p, (r - s) % p))
+    return out
+
+
+def _sched_backwards(p):
+    out = []
+    for s in range(p - 1):
+        for r in range(p):
+            out.append(("rs", s, r, (r - 1) % p, (r + 1 + s) % p))
+    for s in range(p - 1):
+        for r in range(p):
+            out.append(("ag", s, r, (r - 1) % p, (r + s) % p))
+    return out
+
+
+def _fold_from_c(xs, op, dtype):
+    xs = np.asarray(xs)
+    p, n = xs.shape
+    b = C.chunk_bounds(n, p)
+    y = np.empty(n, dtype=xs.dtype)
+    for c in range(p):
+        lo, hi = b[c], b[c + 1]
+        acc = C.to_acc(xs[c % p, lo:hi], dtype)
+        for k in range(1, p):
+            acc = C.combine(acc, C.to_acc(xs[(c + k) % p, lo:hi], dtype), op)
+        y[lo:hi] = C.from_acc(acc, dtype)
+    return np.stack([y.copy() for _ in range(p)])
+
+
+def _reduce_descending(xs, op, dtype):
+    xs = np.asarray(xs)
+    acc = C.to_acc(xs[-1], dtype)
+    for r in range(xs.shape[0] - 2, -1, -1):
+        acc = C.combine(acc, C.to_acc(xs[r], dtype), op)
+    return C.from_acc(acc, dtype)
+
+
+def _hier_strided(xs, op, dtype, group_size):
+    xs = np.asarray(xs)
+    p, n = xs.shape
+    G = group_size
+    ng = p // G
+    parts = []
+    for j in range(ng):
+        members = list(range(j, p, ng))
+        acc = C.to_acc(xs[members[0]], dtype)
+        for r in members[1:]:
+            acc = C.combine(acc, C.to_acc(xs[r], dtype), op)
+        parts.append(acc)
+    t = parts[0]
+    for g in parts[1:]:
+        t = C.combine(t, g, op)
+    return np.stack([C.from_acc(t, dtype)] * p)
+
+
+def _hier_round_at_rep(xs, op, dtype, group_size):
+    xs = np.asarray(xs)
+    p, n = xs.shape
+    G = group_size
+    parts = []
+    for j in range(p // G):
+        acc = C.to_acc(xs[j * G], dtype)
+        for r in range(j * G + 1, (j + 1) * G):
+            acc = C.combine(acc, C.to_acc(xs[r], dtype), op)
+        parts.append(C.to_acc(C.from_acc(acc, dtype), dtype))
+    t = parts[0]
+    for g in parts[1:]:
+        t = C.combine(t, g, op)
+    return np.stack([C.from_acc(t, dtype)] * p)
+
+
+def _narrow_truncate(f):
+    f = np.ascontiguousarray(f, dtype=np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _narrow_ties_away(f):
+    f = np.ascontiguousarray(f, dtype=np.float32)
+    u = f.view(np.uint32)
+    is_nan = (u & 0x7FFFFFFF) > 0x7F800000
+    r = (u + np.uint32(0x8000)) >> 16
+    return np.where(is_nan, (u >> 16) | 0x40, r).astype(np.uint16)
+
+
+def _narrow_no_quiet(f):
+    f = np.ascontiguousarray(f, dtype=np.float32)
+    u = f.view(np.uint32)
+    return ((u + np.uint32(0x7FFF) + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _to_acc_int_as_float(x, dtype):
+    if dtype == "int32":
+        return np.asarray(x).astype(np.float32)
+    return _to_acc(x, dtype)
+
+
+MUTATIONS = {
+    "rs_chunk_off_by_one": lambda m: m.setattr(C, "ring_schedule", _sched_rs_off_by_one),
+    "ring_runs_backwards": lambda m: m.setattr(C, "ring_schedule", _sched_backwards),
+    "receiver_folds_local_first": lambda m: m.setattr(C, "combine", lambda a, v, op: _combine(v, a, op)),
+    "max_min_non_strict": lambda m: m.setattr(
+        C, "combine", lambda a, v, op: np.where(v >= a, v, a) if op == "max" else
+        (np.where(v <= a, v, a) if op == "min" else _combine(a, v, op))),
+    "sum_drops_a_term": lambda m: m.setattr(
+        C, "combine", lambda a, v, op: a if (op == "sum" and np.size(a) % 3 == 1) else _combine(a, v, op)),
+    "max_min_swapped": lambda m: m.setattr(
+        C, "combine", lambda a, v, op: _combine(a, v, {"max": "min", "min": "max"}.get(op, op))),
+    "fold_starts_at_own_rank": lambda m: m.setattr(C, "all_reduce_fold", _fold_from_c),
+    "reduce_descending": lambda m: m.setattr(C, "reduce", _reduce_descending),
+    "hier_groups_strided": lambda m: m.setattr(C, "all_reduce_hier", _hier_strided),
+    "hier_rounds_at_representative": lambda m: m.setattr(C, "all_reduce_hier", _hier_round_at_rep),
+    "bf16_truncates": lambda m: m.setattr(B, "narrow", _narrow_truncate),
+    "bf16_ties_away": lambda m: m.setattr(B, "narrow", _narrow_ties_away),
+    "bf16_nan_not_quieted": lambda m: m.setattr(B, "narrow", _narrow_no_quiet),
+    "int32_accumulates_in_float": lambda m: m.setattr(C, "to_acc", _to_acc_int_as_float),
+    "chunk_bounds_ceil": lambda m: m.setattr(C, "chunk_bounds", lambda n, p: [-((-c * n) // p) for c in range(p + 1)]),
+    "all_gather_reversed": lambda m: m.setattr(
+        C, "all_gather", lambda sh: np.stack([np.concatenate(list(np.asarray(sh))[::-1])] * np.asarray(sh).shape[0])),
+}
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert _run_all_pins() == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    MUTATIONS[name](monkeypatch)
+    failed = _run_all_pins()
+    assert failed, f"planted mistake {name!r} passed every pin"
