@@ -1,0 +1,355 @@
+#!/usr/bin/env python3
+"""Throughput of the fused ring all-reduce over p virtual ranks on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--extra]
+
+One step is one collective call over one batch of synthetic rank buffers
+already resident in HBM: for the default workload, a sum all-reduce of p = 8
+ranks x 2,097,152 float32 (8 MiB per rank) through ``rr_all_reduce`` -- host
+validation and planning, the ring chunk plan, and the single fused kernel that
+folds every chunk in ring order and writes all p outputs (reduce-scatter and
+all-gather in one pass).
+
+Metric: algorithmic HBM bytes per step / time, bytes = 2 p n s for an
+all-reduce (every input read once, every output written once), in GB/s
+(10^9 B/s), and its fraction of MI355X's 8 TB/s HBM peak.  The 128 MiB of
+rank buffers fit in the 256 MB Infinity Cache, so steps rotate over enough
+buffer sets that each set is evicted by >= 512 MiB of other traffic before it
+is used again (cold cache).  A bounded spin kernel queued before the timed
+region lets the host run ahead, so host launch cost does not idle the GPU.
+
+Prints ONE JSON line on stdout.  ``--extra`` prints further measurements
+(other collectives, staged algorithms, cache-hot figures, copy ceiling) as
+JSON lines on stderr.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "all-reduce effective HBM GB/s (p·N bytes in+out / time) and % of MI355X HBM peak"
+HBM_PEAK_GBPS = 8000.0
+COLD_BYTES = 512 << 20
+DTYPE_TAG = {"int32": "i32", "float32": "f32", "bfloat16": "bf16"}
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="ar_fp32_p8_8MiB")
+    ap.add_argument("--op", default=None, help="sum, max or min (default: the workload's first op)")
+    ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate over (0 = enough for a cold cache)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--extra", action="store_true", help="also measure the other collectives (stderr)")
+    return ap.parse_args(argv)
+
+
+def busbw_gibps(kind, p, s_bytes, t_seconds):
+    """The bandwidth formulas of page "分布式训练/推理", section "带宽怎么核算"
+    (all-reduce 2s(p-1)/(p t); reduce-scatter s_in(p-1)/(p t)), in the page's
+    printed unit, which is 2^30 bytes per second."""
+    if kind == "all_reduce":
+        return 2.0 * s_bytes * (p - 1) / (p * t_seconds) / 2 ** 30
+    if kind == "reduce_scatter":
+        return s_bytes * (p - 1) / (p * t_seconds) / 2 ** 30
+    raise ValueError(kind)
+
+
+class Runner:
+    """Pre-marshalled calls of one collective over rotating buffer sets."""
+
+    def __init__(self, rr, torch, spec, coll, op, algo, group, host_x, nsets, stream):
+        import ctypes
+
+        self.rr, self.torch, self.stream = rr, torch, stream
+        self.L = rr.lib()
+        p, n, dtype = spec["p"], spec["n"], spec["dtype"]
+        self.p, self.n, self.dtype, self.coll, self.algo = p, n, dtype, coll, algo
+        tdt = {"int32": torch.int32, "float32": torch.float32, "bfloat16": torch.bfloat16}[dtype]
+        dev = torch.device("cuda", 0)
+        import numpy as np
+
+        if dtype == "bfloat16":
+            host = torch.from_numpy(host_x.view(np.int16)).view(torch.bfloat16)
+        else:
+            host = torch.from_numpy(host_x)
+        L = n // p
+        self.sets = []
+        dt = rr.DTYPES[dtype]
+        opc = rr.OPS[op]
+        sh = stream.cuda_stream
+        for _ in range(nsets):
+            if coll == "all_gather":
+                x = host[:, :L].contiguous().to(dev)
+                y = torch.empty((p, n), dtype=tdt, device=dev)
+            else:
+                x = host.to(dev)
+                if coll == "reduce_scatter":
+                    y = torch.empty((p, L), dtype=tdt, device=dev)
+                elif coll == "reduce":
+                    y = torch.empty((1, n), dtype=tdt, device=dev)
+                else:
+                    y = torch.empty((p, n), dtype=tdt, device=dev)
+            ws = None
+            need = rr.workspace_size(algo, p, group, n, dtype) if coll == "all_reduce" else 0
+            if need:
+                ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            send = rr._ptr_array([x[r].data_ptr() for r in range(x.shape[0])])
+            recv = rr._ptr_array([y[r].data_ptr() for r in range(y.shape[0])])
+            Lb = self.L
+            if coll == "all_reduce" and algo == "ring":
+                call = (lambda s=send, d=recv: Lb.rr_all_reduce(s, d, p, n, dt, opc, sh))
+            elif coll == "all_reduce":
+                ap, gp = rr.ALGOS[algo], group
+                wp, wb = (ws.data_ptr(), need) if ws is not None else (None, 0)
+                call = (lambda s=send, d=recv, ap=ap, gp=gp, wp=wp, wb=wb:
+                        Lb.rr_all_reduce_ex(s, d, p, n, dt, opc, ap, gp, wp, wb, sh))
+            elif coll == "reduce_scatter":
+                call = (lambda s=send, d=recv: Lb.rr_reduce_scatter(s, d, p, n, dt, opc, sh))
+            elif coll == "all_gather":
+                call = (lambda s=send, d=recv: Lb.rr_all_gather(s, d, p, n, dt, sh))
+            elif coll == "reduce":
+                yp = y[0].data_ptr()
+                call = (lambda s=send, yp=yp: Lb.rr_reduce(s, yp, 0, p, n, dt, opc, sh))
+            elif coll == "broadcast":
+                xp = x[0].data_ptr()
+                call = (lambda xp=xp, d=recv: Lb.rr_broadcast(xp, d, 0, p, n, dt, sh))
+            else:
+                raise ValueError(coll)
+            self.sets.append((x, y, ws, send, recv, call))
+        self.bytes = rr.algorithmic_bytes(coll, p, n, dtype)
+        self._ctypes = ctypes
+
+    def step(self, i):
+        st = self.sets[i % len(self.sets)][5]()
+        if st != 0:
+            raise RuntimeError(f"librr call failed: {self.L.rr_last_error().decode()}")
+
+
+def spin_cycles_per_ms(torch, stream):
+    """Calibrate torch's bounded spin kernel (used to let the host queue ahead)."""
+    try:
+        with torch.cuda.stream(stream):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            torch.cuda._sleep(1_000_000)
+            b.record(stream)
+        stream.synchronize()
+        ms = a.elapsed_time(b)
+        return 1_000_000 / ms if ms > 0 else None
+    except Exception:  # noqa: BLE001 - the spin is an optimisation of the harness only
+        return None
+
+
+def timed(torch, runner, steps, warmup, stream, cycles_per_ms, per_launch=True):
+    """Run `warmup` untimed steps, then exactly `steps` timed steps bracketed by
+    synchronizations.  Returns (ms_per_step from the region events, mean
+    per-launch kernel ms from per-launch events or None, wall seconds)."""
+    for i in range(warmup):
+        runner.step(i)
+    torch.cuda.synchronize()
+    # host cost of one step, to size the lead the spin kernel gives the host
+    t0 = time.perf_counter()
+    for i in range(5):
+        runner.step(i)
+    host_ms = (time.perf_counter() - t0) / 5 * 1e3
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        if cycles_per_ms:
+            lead_ms = min(50.0, 1.5 * steps * (host_ms + (0.02 if per_launch else 0.0)) + 0.5)
+            torch.cuda._sleep(int(lead_ms * cycles_per_ms))
+        start.record(stream)
+        for i in range(steps):
+            if per_launch:
+                evs[i][0].record(stream)
+            runner.step(warmup + i)
+            if per_launch:
+                evs[i][1].record(stream)
+        end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    region_ms = start.elapsed_time(end)
+    kern = None
+    if per_launch:
+        kern = sum(a.elapsed_time(b) for a, b in evs) / steps
+    return region_ms / steps, kern, wall
+
+
+def cpu_baseline(spec, host_x, op, seconds):
+    """Time the oracle's literal ring simulation (as it stands, NumPy, one
+    thread) on a bounded sample of the same inputs."""
+    import numpy as np
+
+    from oracle import collectives as C
+
+    p, n, dtype = spec["p"], spec["n"], spec["dtype"]
+    s = np.dtype(np.uint16 if dtype == "bfloat16" else np.float32).itemsize
+    m = min(n, 1 << 21)  # elements per rank in the sample
+    sample = np.ascontiguousarray(host_x[:, :m])
+    fn = C.all_reduce_hier if spec["coll"] == "all_reduce" and spec["algo"] == "hier" else None
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        if fn is not None:
+            fn(sample, op, dtype, spec["group"])
+        else:
+            C.all_reduce_ring(sample, op, dtype)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 1000:
+            break
+    bytes_per = 2 * p * m * s
+    what = "all_reduce_hier" if fn is not None else "all_reduce_ring"
+    return {
+        "value": round(bytes_per * reps / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"oracle.{what} (NumPy, 1 thread) on the first {m} of {n} elements of each of the {p} "
+                  f"ranks of the same inputs, {reps} calls in {el:.1f} s",
+        "host_cpus": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+        "numpy": np.__version__,
+    }
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the p virtual ranks live in one GPU's HBM and no collective crosses "
+              f"GPUs; --gpus {args.gpus} is not supported (run with --gpus 1).", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    import collective_communication_reduction_way_amd as rr
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    spec = W.WORKLOADS[args.workload]
+    op = args.op or spec["ops"][0]
+    algo = "hier" if spec["algo"] == "hier" else "ring"
+    group = spec.get("group", 0)
+    p, n, dtype = spec["p"], spec["n"], spec["dtype"]
+    host_x = W.make_inputs(args.workload)
+    stream = torch.cuda.Stream()  # default priority
+    footprint = 2 * p * n * np.dtype(W.STORAGE[dtype]).itemsize
+    nsets = args.sets or (1 + math.ceil(COLD_BYTES / footprint))
+    runner = Runner(rr, torch, spec, "all_reduce", op, algo, group, host_x, nsets, stream)
+    cpm = spin_cycles_per_ms(torch, stream)
+    ms_step, kern_ms, wall = timed(torch, runner, args.steps, args.warmup, stream, cpm, per_launch=True)
+    value = runner.bytes / (ms_step * 1e-3) / 1e9
+    achieved = runner.bytes / (kern_ms * 1e-3) / 1e9
+    kernel = {"ring": "k_fold<..., FoldMode::kRingAll> (fused ring all-reduce)",
+              "hier": "k_fold<..., FoldMode::kHierAll> (fused hierarchical all-reduce)"}[algo]
+    traffic = None
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_TAG[dtype],
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload, "p": p, "n_per_rank": n, "op": op,
+            "algo": "ring_fused" if algo == "ring" else f"hier_fused_g{group}",
+            "bytes_per_step": runner.bytes, "cold_cache_buffer_sets": nsets,
+        },
+        "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": kernel,
+            "kernel_ms": round(kern_ms, 6),
+        },
+        "wall_s_timed_region": round(wall, 4),
+        "page_busbw_GiBps": round(busbw_gibps("all_reduce", p, n * np.dtype(W.STORAGE[dtype]).itemsize,
+                                              ms_step * 1e-3), 2),
+    }
+    if args.extra:
+        extra(args, torch, rr, W, spec, host_x, stream, cpm, op, runner)
+    del runner
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(spec, host_x, op, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def extra(args, torch, rr, W, spec, host_x, stream, cpm, op, main_runner):
+    import numpy as np
+
+    p, n, dtype = spec["p"], spec["n"], spec["dtype"]
+    esz = np.dtype(W.STORAGE[dtype]).itemsize
+
+    def report(tag, runner, steps, cold):
+        ms, kern, _ = timed(torch, runner, steps, 5, stream, cpm, per_launch=True)
+        print(json.dumps({"extra": tag, "workload": args.workload, "cold_cache": cold, "GBps": round(runner.bytes / ms / 1e6, 2),
+                          "kernel_GBps": round(runner.bytes / kern / 1e6, 2), "ms_per_step": round(ms, 6),
+                          "frac_of_peak": round(runner.bytes / ms / 1e6 / HBM_PEAK_GBPS, 4)}), file=sys.stderr,
+              flush=True)
+
+    nsets = len(main_runner.sets)
+    # cache-hot figure of the main collective: one buffer set, back to back
+    hot = Runner(rr, torch, spec, "all_reduce", op, main_runner.algo, spec.get("group", 0), host_x, 1, stream)
+    report(f"all_reduce_{main_runner.algo}_cache_hot", hot, args.steps, False)
+    del hot
+    for coll in ("reduce_scatter", "all_gather", "reduce", "broadcast"):
+        fp = {"reduce_scatter": (p + 1) * n * esz, "all_gather": (p + 1) * n * esz, "reduce": (p + 1) * n * esz,
+              "broadcast": (2 * p) * n * esz}[coll]
+        k = 1 + math.ceil(COLD_BYTES / fp)
+        r = Runner(rr, torch, spec, coll, op, "ring", 0, host_x, k, stream)
+        report(coll, r, max(10, args.steps // 2), True)
+        del r
+        torch.cuda.empty_cache()
+    for algo, G in (("ring_staged", 0), ("hier", 4), ("hier_staged", 4)):
+        if p % max(G, 1):
+            continue
+        r = Runner(rr, torch, spec, "all_reduce", op, algo, G, host_x, nsets, stream)
+        report(f"all_reduce_{algo}" + (f"_g{G}" if G else ""), r, max(10, args.steps // 4), True)
+        del r
+        torch.cuda.empty_cache()
+    # copy ceiling: torch's device-to-device copy of 1 GiB
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    print(json.dumps({"extra": "copy_ceiling_torch_d2d_1GiB", "GBps": round(2 * (1 << 30) / ms / 1e6, 2)}),
+          file=sys.stderr, flush=True)
+    del a, b
+    torch.cuda.empty_cache()
+
+
+if __name__ == "__main__":
+    sys.exit(main())

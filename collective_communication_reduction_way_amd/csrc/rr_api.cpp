@@ -1,0 +1,671 @@
+// rr_api.cpp -- the C ABI of librr.so: argument validation, planning and
+// kernel dispatch for the collective reductions over p virtual ranks.
+//
+// Semantics follow page "分布式训练/推理", section "通信原语：rank、world size
+// 和 collective operations" (broadcast, reduce, all-gather, reduce-scatter,
+// all-reduce; all_reduce = reduce_scatter + all_gather), page "LLM Parallelism
+// 基础", sections "MPI Collective Operations" and "Ring AllReduce", and page
+// "大模型并行的最小闭环：集合通信、TP、FSDP/ZeRO-3 到权重分片", section
+// "Source Log: 2026-05-05" (hierarchical AllReduce).  Each entry point checks
+// every argument before the first launch, so a rejected call writes nothing,
+// then enqueues its kernels on the caller's stream and returns without
+// synchronizing.
+#include <hip/hip_runtime_api.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "rr.h"
+#include "rr_kernels.h"
+#include "rr_plan.h"
+
+namespace {
+
+using rr::Kind;
+
+thread_local std::string g_last_error;
+
+rr_status_t fail(rr_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+rr_status_t ok() {
+  g_last_error.clear();
+  return RR_SUCCESS;
+}
+
+rr_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(RR_ERROR_HIP, "%s: HIP error %d (%s)", what, static_cast<int>(e), hipGetErrorString(e));
+}
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  if (!v || !*v) return dflt;
+  return atoi(v);
+}
+
+// Tuning knobs (all optional): RR_UNROLL (1, 2 or 4 groups per lane on the
+// tunable fold kernels), RR_NT (1 = nontemporal loads/stores there),
+// RR_GRID_CAP (maximum workgroups per launch; 0 = one tile per workgroup),
+// RR_LOG (1 = print each launch plan to stderr).
+struct Tuning {
+  int unroll;
+  int nontemporal;
+  int grid_cap;
+  int log;
+};
+
+Tuning tuning() {
+  Tuning t;
+  t.unroll = env_int("RR_UNROLL", 2);
+  if (t.unroll != 1 && t.unroll != 2 && t.unroll != 4) t.unroll = 2;
+  t.nontemporal = env_int("RR_NT", 0) ? 1 : 0;
+  t.grid_cap = env_int("RR_GRID_CAP", 0);
+  if (t.grid_cap < 0) t.grid_cap = 0;
+  t.log = env_int("RR_LOG", 0);
+  return t;
+}
+
+constexpr uint64_t kMaxElems = 1ull << 56;
+
+
+Kind kind_of(rr_dtype_t d) {
+  switch (d) {
+    case RR_INT32: return Kind::kI32;
+    case RR_FLOAT32: return Kind::kF32;
+    default: return Kind::kBF16;
+  }
+}
+
+Kind acc_kind_of(rr_dtype_t d) { return d == RR_INT32 ? Kind::kI32 : Kind::kF32; }
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+rr_status_t check_dtype(rr_dtype_t dt) {
+  if (rr::elem_size(dt) == 0) return fail(RR_ERROR_UNSUPPORTED, "unknown dtype %d", static_cast<int>(dt));
+  return RR_SUCCESS;
+}
+
+rr_status_t check_op(rr_op_t op) {
+  if (op != RR_SUM && op != RR_MAX && op != RR_MIN)
+    return fail(RR_ERROR_UNSUPPORTED, "unknown op %d", static_cast<int>(op));
+  return RR_SUCCESS;
+}
+
+rr_status_t check_p(int p) {
+  if (p < 1 || p > RR_MAX_RANKS) return fail(RR_ERROR_INVALID_ARGUMENT, "p=%d outside [1, %d]", p, RR_MAX_RANKS);
+  return RR_SUCCESS;
+}
+
+rr_status_t check_n(size_t n) {
+  if (static_cast<uint64_t>(n) > kMaxElems)
+    return fail(RR_ERROR_INVALID_ARGUMENT, "n=%zu exceeds the limit of 2^56 elements", n);
+  return RR_SUCCESS;
+}
+
+rr_status_t check_buf(const void* ptr, size_t esz, const char* what, int r) {
+  if (!ptr) return fail(RR_ERROR_INVALID_ARGUMENT, "%s[%d] is NULL", what, r);
+  if (reinterpret_cast<uintptr_t>(ptr) % esz)
+    return fail(RR_ERROR_INVALID_ARGUMENT, "%s[%d] is not aligned to the element size %zu", what, r, esz);
+  return RR_SUCCESS;
+}
+
+// Byte range of one buffer, for the aliasing rules.
+struct Range {
+  uintptr_t lo;
+  uintptr_t hi;  // exclusive
+  int rank;
+};
+
+Range range_of(const void* ptr, uint64_t bytes, int rank) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(ptr);
+  return Range{lo, lo + static_cast<uintptr_t>(bytes), rank};
+}
+
+bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+// Outputs must be pairwise disjoint; output r may overlap input q only when
+// allowed(r, q) says the pair is the entry point's exact in-place form.
+template <class ALLOWED>
+rr_status_t check_aliasing(const std::vector<Range>& outs, const std::vector<Range>& ins, ALLOWED allowed) {
+  for (size_t i = 0; i < outs.size(); ++i)
+    for (size_t j = i + 1; j < outs.size(); ++j)
+      if (overlap(outs[i], outs[j]))
+        return fail(RR_ERROR_INVALID_ARGUMENT, "output buffers of ranks %d and %d overlap", outs[i].rank,
+                    outs[j].rank);
+  for (const Range& o : outs)
+    for (const Range& in : ins)
+      if (overlap(o, in) && !allowed(o, in))
+        return fail(RR_ERROR_INVALID_ARGUMENT,
+                    "output of rank %d overlaps input of rank %d (only the exact in-place form is allowed)",
+                    o.rank, in.rank);
+  return RR_SUCCESS;
+}
+
+// Widest unit (16/4/2/1 bytes) dividing every address and byte count.
+int copy_unit(const std::vector<uintptr_t>& addrs, const std::vector<uint64_t>& sizes) {
+  uintptr_t acc = 0;
+  for (uintptr_t a : addrs) acc |= a;
+  for (uint64_t s : sizes) acc |= static_cast<uintptr_t>(s);
+  if ((acc & 15u) == 0) return 16;
+  if ((acc & 3u) == 0) return 4;
+  if ((acc & 1u) == 0) return 2;
+  return 1;
+}
+
+rr::FoldLaunch base_fold(const Tuning& t) {
+  rr::FoldLaunch f;
+  memset(&f, 0, sizeof(f));
+  f.unroll = t.unroll;
+  f.nontemporal = t.nontemporal;
+  f.grid_cap = t.grid_cap;
+  return f;
+}
+
+void log_fold(const Tuning& t, const char* what, const rr::FoldLaunch& f) {
+  if (!t.log) return;
+  fprintf(stderr, "[rr] %s: mode=%d p=%d group=%d n=%llu segments=%d vec=%d unroll=%d nt=%d grid_cap=%d\n", what,
+          static_cast<int>(f.mode), f.args.p, f.args.group, static_cast<unsigned long long>(f.args.n), f.segments,
+          f.args.vec, f.unroll, f.nontemporal, f.grid_cap);
+}
+
+rr_status_t run_fold(const Tuning& t, const char* what, const rr::FoldLaunch& f, hipStream_t s) {
+  log_fold(t, what, f);
+  const hipError_t e = rr::launch_fold(f, s);
+  if (e != hipSuccess) return hip_fail(e, what);
+  return RR_SUCCESS;
+}
+
+// Common validation of a rank-array collective.
+rr_status_t check_rank_arrays(const void* const* send, void* const* recv, int p, size_t esz, size_t n) {
+  if (!send) return fail(RR_ERROR_INVALID_ARGUMENT, "sendbufs is NULL");
+  if (!recv) return fail(RR_ERROR_INVALID_ARGUMENT, "recvbufs is NULL");
+  if (n == 0) return RR_SUCCESS;
+  for (int r = 0; r < p; ++r) {
+    rr_status_t st = check_buf(send[r], esz, "sendbufs", r);
+    if (st) return st;
+    st = check_buf(recv[r], esz, "recvbufs", r);
+    if (st) return st;
+  }
+  return RR_SUCCESS;
+}
+
+// ---------------------------------------------------------------------------
+// All-reduce variants.
+
+rr_status_t ar_ring_fused(const void* const* send, void* const* recv, int p, uint64_t n, rr_dtype_t dt, rr_op_t op,
+                          const Tuning& t, hipStream_t s) {
+  rr::FoldLaunch f = base_fold(t);
+  f.mode = rr::FoldMode::kRingAll;
+  f.in_kind = f.out_kind = kind_of(dt);
+  f.op = op;
+  f.segments = p;
+  f.args.n = n;
+  f.args.p = p;
+  f.args.group = p;
+  bool vec = true;
+  for (int r = 0; r < p; ++r) {
+    f.args.in[r] = send[r];
+    f.args.out[r] = recv[r];
+    vec = vec && aligned16(send[r]) && aligned16(recv[r]);
+  }
+  f.args.vec = vec ? 1 : 0;
+  rr::chunk_bounds(p, n, f.args.bound);
+  return run_fold(t, "all_reduce(ring, fused)", f, s);
+}
+
+rr_status_t ar_hier_fused(const void* const* send, void* const* recv, int p, uint64_t n, rr_dtype_t dt, rr_op_t op,
+                          int G, const Tuning& t, hipStream_t s) {
+  rr::FoldLaunch f = base_fold(t);
+  f.mode = rr::FoldMode::kHierAll;
+  f.in_kind = f.out_kind = kind_of(dt);
+  f.op = op;
+  f.segments = 1;
+  f.args.n = n;
+  f.args.p = p;
+  f.args.group = G;
+  bool vec = true;
+  for (int r = 0; r < p; ++r) {
+    f.args.in[r] = send[r];
+    f.args.out[r] = recv[r];
+    vec = vec && aligned16(send[r]) && aligned16(recv[r]);
+  }
+  f.args.vec = vec ? 1 : 0;
+  return run_fold(t, "all_reduce(hierarchical, fused)", f, s);
+}
+
+rr_status_t launch_pairs_copy(const Tuning& t, const std::vector<const void*>& src, const std::vector<void*>& dst,
+                              const std::vector<uint64_t>& bytes, const char* what, hipStream_t s) {
+  for (size_t base = 0; base < src.size(); base += RR_MAX_RANKS) {
+    rr::PairArgs a;
+    memset(&a, 0, sizeof(a));
+    std::vector<uintptr_t> addrs;
+    std::vector<uint64_t> sizes;
+    const size_t m = src.size() - base < RR_MAX_RANKS ? src.size() - base : RR_MAX_RANKS;
+    for (size_t i = 0; i < m; ++i) {
+      a.src[i] = src[base + i];
+      a.dst[i] = dst[base + i];
+      a.len[i] = bytes[base + i];
+      addrs.push_back(reinterpret_cast<uintptr_t>(src[base + i]));
+      addrs.push_back(reinterpret_cast<uintptr_t>(dst[base + i]));
+      sizes.push_back(bytes[base + i]);
+    }
+    a.npairs = static_cast<int>(m);
+    const int unit = copy_unit(addrs, sizes);
+    if (t.log) fprintf(stderr, "[rr] %s: copy pairs=%d unit=%d\n", what, a.npairs, unit);
+    const hipError_t e = rr::launch_copy_pairs(a, unit, t.grid_cap, s);
+    if (e != hipSuccess) return hip_fail(e, what);
+  }
+  return RR_SUCCESS;
+}
+
+rr_status_t ar_ring_staged(const void* const* send, void* const* recv, int p, uint64_t n, rr_dtype_t dt, rr_op_t op,
+                           void* ws, const Tuning& t, hipStream_t s) {
+  const size_t esz = rr::elem_size(dt);
+  uint64_t b[RR_MAX_RANKS + 1];
+  rr::chunk_bounds(p, n, b);
+  const std::vector<rr::Transfer> sched = rr::ring_schedule(p);
+  const bool bf16 = dt == RR_BFLOAT16;
+  // Working buffers of the reduce-scatter phase (accumulator type).
+  std::vector<char*> work(p);
+  for (int r = 0; r < p; ++r)
+    work[r] = bf16 ? static_cast<char*>(ws) + static_cast<uint64_t>(r) * n * 4 : static_cast<char*>(recv[r]);
+  const size_t wsz = bf16 ? 4 : esz;
+  rr_status_t st;
+  // Load every rank's input into its working buffer.
+  if (bf16) {
+    rr::PairArgs a;
+    memset(&a, 0, sizeof(a));
+    bool vec = true;
+    for (int r = 0; r < p; ++r) {
+      a.src[r] = send[r];
+      a.dst[r] = work[r];
+      a.len[r] = n;
+      vec = vec && aligned16(send[r]) && aligned16(work[r]);
+    }
+    a.npairs = p;
+    a.vec = vec;
+    const hipError_t e = rr::launch_convert_pairs(a, Kind::kBF16, Kind::kF32, t.grid_cap, s);
+    if (e != hipSuccess) return hip_fail(e, "all_reduce(ring, staged): widen");
+  } else {
+    std::vector<const void*> src;
+    std::vector<void*> dst;
+    std::vector<uint64_t> bytes;
+    for (int r = 0; r < p; ++r)
+      if (send[r] != recv[r]) {
+        src.push_back(send[r]);
+        dst.push_back(recv[r]);
+        bytes.push_back(n * esz);
+      }
+    if (!src.empty()) {
+      st = launch_pairs_copy(t, src, dst, bytes, "all_reduce(ring, staged): copy in", s);
+      if (st) return st;
+    }
+  }
+  // Reduce-scatter: one launch per step, p transfers each.
+  for (int step = 0; step < p - 1; ++step) {
+    rr::PairArgs a;
+    memset(&a, 0, sizeof(a));
+    bool vec = true;
+    int m = 0;
+    for (const rr::Transfer& x : sched) {
+      if (x.phase != 0 || x.step != step) continue;
+      const uint64_t off = b[x.chunk] * wsz;
+      a.src[m] = work[x.src] + off;
+      a.dst[m] = work[x.dst] + off;
+      a.len[m] = b[x.chunk + 1] - b[x.chunk];
+      vec = vec && aligned16(a.src[m]) && aligned16(a.dst[m]);
+      ++m;
+    }
+    a.npairs = m;
+    a.vec = vec;
+    if (t.log) fprintf(stderr, "[rr] ring reduce-scatter step %d: %d transfers vec=%d\n", step, m, a.vec);
+    const hipError_t e = rr::launch_ring_step(a, acc_kind_of(dt), op, t.grid_cap, s);
+    if (e != hipSuccess) return hip_fail(e, "all_reduce(ring, staged): reduce-scatter step");
+  }
+  // bf16: the owner of each chunk rounds its reduced chunk once.
+  if (bf16) {
+    rr::PairArgs a;
+    memset(&a, 0, sizeof(a));
+    bool vec = true;
+    for (int c = 0; c < p; ++c) {
+      a.src[c] = work[c] + b[c] * 4;
+      a.dst[c] = static_cast<char*>(recv[c]) + b[c] * esz;
+      a.len[c] = b[c + 1] - b[c];
+      vec = vec && aligned16(a.src[c]) && aligned16(a.dst[c]);
+    }
+    a.npairs = p;
+    a.vec = vec;
+    const hipError_t e = rr::launch_convert_pairs(a, Kind::kF32, Kind::kBF16, t.grid_cap, s);
+    if (e != hipSuccess) return hip_fail(e, "all_reduce(ring, staged): narrow");
+  }
+  // All-gather: one launch per step; the receiver overwrites.
+  for (int step = 0; step < p - 1; ++step) {
+    std::vector<const void*> src;
+    std::vector<void*> dst;
+    std::vector<uint64_t> bytes;
+    for (const rr::Transfer& x : sched) {
+      if (x.phase != 1 || x.step != step) continue;
+      const uint64_t off = b[x.chunk] * esz;
+      src.push_back(static_cast<const char*>(recv[x.src]) + off);
+      dst.push_back(static_cast<char*>(recv[x.dst]) + off);
+      bytes.push_back((b[x.chunk + 1] - b[x.chunk]) * esz);
+    }
+    st = launch_pairs_copy(t, src, dst, bytes, "all_reduce(ring, staged): all-gather step", s);
+    if (st) return st;
+  }
+  return RR_SUCCESS;
+}
+
+rr_status_t ar_hier_staged(const void* const* send, void* const* recv, int p, uint64_t n, rr_dtype_t dt, rr_op_t op,
+                           int G, void* ws, const Tuning& t, hipStream_t s) {
+  const int J = p / G;
+  const size_t esz = rr::elem_size(dt);
+  // Steps 1-2: each group reduces into its representative's partial
+  // (accumulator type, in the workspace).
+  rr::FoldLaunch f1 = base_fold(t);
+  f1.mode = rr::FoldMode::kAscOne;
+  f1.in_kind = kind_of(dt);
+  f1.out_kind = acc_kind_of(dt);
+  f1.op = op;
+  f1.segments = J;
+  f1.args.n = n;
+  f1.args.p = G;
+  f1.args.group = G;
+  bool vec = aligned16(ws);
+  for (int r = 0; r < p; ++r) {
+    f1.args.in[r] = send[r];
+    vec = vec && aligned16(send[r]) && aligned16(recv[r]);
+  }
+  for (int j = 0; j < J; ++j) f1.args.out[j] = static_cast<char*>(ws) + static_cast<uint64_t>(j) * n * 4;
+  f1.args.vec = vec ? 1 : 0;
+  rr_status_t st = run_fold(t, "all_reduce(hierarchical, staged): group reduce", f1, s);
+  if (st) return st;
+  // Steps 3-5: the representatives' partials are combined across groups and
+  // the result lands at every representative.
+  rr::FoldLaunch f2 = base_fold(t);
+  f2.mode = rr::FoldMode::kHierAll;
+  f2.in_kind = acc_kind_of(dt);
+  f2.out_kind = kind_of(dt);
+  f2.op = op;
+  f2.segments = 1;
+  f2.args.n = n;
+  f2.args.p = J;
+  f2.args.group = J;
+  for (int j = 0; j < J; ++j) {
+    f2.args.in[j] = f1.args.out[j];
+    f2.args.out[j] = recv[j * G];
+  }
+  f2.args.vec = vec ? 1 : 0;
+  st = run_fold(t, "all_reduce(hierarchical, staged): cross-group reduce", f2, s);
+  if (st) return st;
+  // Step 6: each representative broadcasts inside its group.
+  if (G > 1) {
+    std::vector<const void*> src;
+    std::vector<void*> dst;
+    std::vector<uint64_t> bytes;
+    for (int j = 0; j < J; ++j)
+      for (int i = 1; i < G; ++i) {
+        src.push_back(recv[j * G]);
+        dst.push_back(recv[j * G + i]);
+        bytes.push_back(n * esz);
+      }
+    st = launch_pairs_copy(t, src, dst, bytes, "all_reduce(hierarchical, staged): group broadcast", s);
+    if (st) return st;
+  }
+  return RR_SUCCESS;
+}
+
+size_t workspace_bytes(rr_algo_t algo, int p, int G, uint64_t n, rr_dtype_t dt) {
+  switch (algo) {
+    case RR_ALGO_RING_STAGED: return dt == RR_BFLOAT16 ? static_cast<size_t>(p) * n * 4 : 0;
+    case RR_ALGO_HIER_STAGED: return static_cast<size_t>(p / G) * n * 4;
+    default: return 0;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+rr_status_t rr_all_reduce_ex(const void* const* sendbufs, void* const* recvbufs, int p, size_t n, rr_dtype_t dtype,
+                             rr_op_t op, rr_algo_t algo, int group_size, void* workspace, size_t ws_bytes,
+                             rr_stream_t stream) {
+  rr_status_t st;
+  if ((st = check_p(p)) || (st = check_dtype(dtype)) || (st = check_op(op)) || (st = check_n(n))) return st;
+  if (algo != RR_ALGO_RING_FUSED && algo != RR_ALGO_RING_STAGED && algo != RR_ALGO_HIER_FUSED &&
+      algo != RR_ALGO_HIER_STAGED)
+    return fail(RR_ERROR_INVALID_ARGUMENT, "unknown algo %d", static_cast<int>(algo));
+  const bool hier = algo == RR_ALGO_HIER_FUSED || algo == RR_ALGO_HIER_STAGED;
+  if (hier && (group_size < 1 || group_size > p || p % group_size))
+    return fail(RR_ERROR_INVALID_ARGUMENT, "group_size=%d must be in [1, p] and divide p=%d", group_size, p);
+  const size_t esz = rr::elem_size(dtype);
+  if ((st = check_rank_arrays(sendbufs, recvbufs, p, esz, n))) return st;
+  const size_t need = workspace_bytes(algo, p, hier ? group_size : 1, n, dtype);
+  if (need > 0 && n > 0) {
+    if (!workspace) return fail(RR_ERROR_INVALID_ARGUMENT, "algo %d needs %zu bytes of workspace", algo, need);
+    if (ws_bytes < need)
+      return fail(RR_ERROR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
+                  need);
+    if (!aligned16(workspace)) return fail(RR_ERROR_INVALID_ARGUMENT, "workspace is not 16-byte aligned");
+  }
+  if (n == 0) return ok();
+  std::vector<Range> outs, ins;
+  for (int r = 0; r < p; ++r) {
+    outs.push_back(range_of(recvbufs[r], n * esz, r));
+    ins.push_back(range_of(sendbufs[r], n * esz, r));
+  }
+  if (need > 0) {
+    // The workspace is written: it must not touch any rank buffer.
+    const Range w = range_of(workspace, need, -1);
+    for (const Range& o : outs)
+      if (overlap(w, o)) return fail(RR_ERROR_INVALID_ARGUMENT, "workspace overlaps the output of rank %d", o.rank);
+    for (const Range& i : ins)
+      if (overlap(w, i)) return fail(RR_ERROR_INVALID_ARGUMENT, "workspace overlaps the input of rank %d", i.rank);
+  }
+  st = check_aliasing(outs, ins, [](const Range& o, const Range& i) { return o.rank == i.rank && o.lo == i.lo; });
+  if (st) return st;
+  const Tuning t = tuning();
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  switch (algo) {
+    case RR_ALGO_RING_FUSED: st = ar_ring_fused(sendbufs, recvbufs, p, n, dtype, op, t, s); break;
+    case RR_ALGO_RING_STAGED: st = ar_ring_staged(sendbufs, recvbufs, p, n, dtype, op, workspace, t, s); break;
+    case RR_ALGO_HIER_FUSED: st = ar_hier_fused(sendbufs, recvbufs, p, n, dtype, op, group_size, t, s); break;
+    case RR_ALGO_HIER_STAGED:
+      st = ar_hier_staged(sendbufs, recvbufs, p, n, dtype, op, group_size, workspace, t, s);
+      break;
+  }
+  return st ? st : ok();
+}
+
+rr_status_t rr_all_reduce(const void* const* sendbufs, void* const* recvbufs, int p, size_t n, rr_dtype_t dtype,
+                          rr_op_t op, rr_stream_t stream) {
+  return rr_all_reduce_ex(sendbufs, recvbufs, p, n, dtype, op, RR_ALGO_RING_FUSED, 0, nullptr, 0, stream);
+}
+
+rr_status_t rr_reduce_scatter(const void* const* sendbufs, void* const* recvbufs, int p, size_t n, rr_dtype_t dtype,
+                              rr_op_t op, rr_stream_t stream) {
+  rr_status_t st;
+  if ((st = check_p(p)) || (st = check_dtype(dtype)) || (st = check_op(op)) || (st = check_n(n))) return st;
+  if (n % static_cast<size_t>(p))
+    return fail(RR_ERROR_INVALID_ARGUMENT, "reduce-scatter needs p | n (p=%d, n=%zu)", p, n);
+  const size_t esz = rr::elem_size(dtype);
+  if ((st = check_rank_arrays(sendbufs, recvbufs, p, esz, n))) return st;
+  if (n == 0) return ok();
+  const uint64_t L = n / p;
+  std::vector<Range> outs, ins;
+  for (int r = 0; r < p; ++r) {
+    outs.push_back(range_of(recvbufs[r], L * esz, r));
+    ins.push_back(range_of(sendbufs[r], n * esz, r));
+  }
+  st = check_aliasing(outs, ins, [&](const Range& o, const Range& i) {
+    return o.rank == i.rank && o.lo == i.lo + static_cast<uintptr_t>(o.rank) * L * esz;
+  });
+  if (st) return st;
+  const Tuning t = tuning();
+  rr::FoldLaunch f = base_fold(t);
+  f.mode = rr::FoldMode::kRingShard;
+  f.in_kind = f.out_kind = kind_of(dtype);
+  f.op = op;
+  f.segments = p;
+  f.args.n = n;
+  f.args.p = p;
+  f.args.group = p;
+  bool vec = (L * esz) % 16 == 0;
+  for (int r = 0; r < p; ++r) {
+    f.args.in[r] = sendbufs[r];
+    f.args.out[r] = recvbufs[r];
+    vec = vec && aligned16(sendbufs[r]) && aligned16(recvbufs[r]);
+  }
+  f.args.vec = vec ? 1 : 0;
+  rr::chunk_bounds(p, n, f.args.bound);
+  st = run_fold(t, "reduce_scatter", f, reinterpret_cast<hipStream_t>(stream));
+  return st ? st : ok();
+}
+
+rr_status_t rr_all_gather(const void* const* sendbufs, void* const* recvbufs, int p, size_t n, rr_dtype_t dtype,
+                          rr_stream_t stream) {
+  rr_status_t st;
+  if ((st = check_p(p)) || (st = check_dtype(dtype)) || (st = check_n(n))) return st;
+  if (n % static_cast<size_t>(p))
+    return fail(RR_ERROR_INVALID_ARGUMENT, "all-gather needs p | n (p=%d, n=%zu)", p, n);
+  const size_t esz = rr::elem_size(dtype);
+  if ((st = check_rank_arrays(sendbufs, recvbufs, p, esz, n))) return st;
+  if (n == 0) return ok();
+  const uint64_t L = n / p;
+  std::vector<Range> outs, ins;
+  for (int r = 0; r < p; ++r) {
+    outs.push_back(range_of(recvbufs[r], n * esz, r));
+    ins.push_back(range_of(sendbufs[r], L * esz, r));
+  }
+  st = check_aliasing(outs, ins, [&](const Range& o, const Range& i) {
+    return o.rank == i.rank && i.lo == o.lo + static_cast<uintptr_t>(o.rank) * L * esz;
+  });
+  if (st) return st;
+  rr::FanoutArgs a;
+  memset(&a, 0, sizeof(a));
+  std::vector<uintptr_t> addrs;
+  for (int r = 0; r < p; ++r) {
+    a.src[r] = sendbufs[r];
+    a.dst[r] = recvbufs[r];
+    addrs.push_back(reinterpret_cast<uintptr_t>(sendbufs[r]));
+    addrs.push_back(reinterpret_cast<uintptr_t>(recvbufs[r]));
+    if (static_cast<const char*>(sendbufs[r]) == static_cast<const char*>(recvbufs[r]) + L * esz * r)
+      a.skip_diag |= 1ull << r;
+  }
+  a.seg_bytes = L * esz;
+  a.dst_seg_stride = L * esz;
+  a.nseg = p;
+  a.ndst = p;
+  const Tuning t = tuning();
+  const int unit = copy_unit(addrs, {L * esz});
+  if (t.log) fprintf(stderr, "[rr] all_gather: p=%d shard_bytes=%llu unit=%d\n", p, (unsigned long long)(L * esz), unit);
+  const hipError_t e = rr::launch_fanout(a, unit, t.grid_cap, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "all_gather");
+  return ok();
+}
+
+rr_status_t rr_reduce(const void* const* sendbufs, void* recvbuf, int root, int p, size_t n, rr_dtype_t dtype,
+                      rr_op_t op, rr_stream_t stream) {
+  rr_status_t st;
+  if ((st = check_p(p)) || (st = check_dtype(dtype)) || (st = check_op(op)) || (st = check_n(n))) return st;
+  if (root < 0 || root >= p) return fail(RR_ERROR_INVALID_ARGUMENT, "root=%d outside [0, p=%d)", root, p);
+  if (!sendbufs) return fail(RR_ERROR_INVALID_ARGUMENT, "sendbufs is NULL");
+  const size_t esz = rr::elem_size(dtype);
+  if (n == 0) return ok();
+  for (int r = 0; r < p; ++r)
+    if ((st = check_buf(sendbufs[r], esz, "sendbufs", r))) return st;
+  if ((st = check_buf(recvbuf, esz, "recvbuf", root))) return st;
+  std::vector<Range> outs{range_of(recvbuf, n * esz, root)}, ins;
+  for (int r = 0; r < p; ++r) ins.push_back(range_of(sendbufs[r], n * esz, r));
+  st = check_aliasing(outs, ins, [](const Range& o, const Range& i) { return o.rank == i.rank && o.lo == i.lo; });
+  if (st) return st;
+  const Tuning t = tuning();
+  rr::FoldLaunch f = base_fold(t);
+  f.mode = rr::FoldMode::kAscOne;
+  f.in_kind = f.out_kind = kind_of(dtype);
+  f.op = op;
+  f.segments = 1;
+  f.args.n = n;
+  f.args.p = p;
+  f.args.group = p;
+  bool vec = aligned16(recvbuf);
+  for (int r = 0; r < p; ++r) {
+    f.args.in[r] = sendbufs[r];
+    vec = vec && aligned16(sendbufs[r]);
+  }
+  f.args.out[0] = recvbuf;
+  f.args.vec = vec ? 1 : 0;
+  st = run_fold(t, "reduce", f, reinterpret_cast<hipStream_t>(stream));
+  return st ? st : ok();
+}
+
+rr_status_t rr_broadcast(const void* sendbuf, void* const* recvbufs, int root, int p, size_t n, rr_dtype_t dtype,
+                         rr_stream_t stream) {
+  rr_status_t st;
+  if ((st = check_p(p)) || (st = check_dtype(dtype)) || (st = check_n(n))) return st;
+  if (root < 0 || root >= p) return fail(RR_ERROR_INVALID_ARGUMENT, "root=%d outside [0, p=%d)", root, p);
+  if (!recvbufs) return fail(RR_ERROR_INVALID_ARGUMENT, "recvbufs is NULL");
+  const size_t esz = rr::elem_size(dtype);
+  if (n == 0) return ok();
+  if ((st = check_buf(sendbuf, esz, "sendbuf", root))) return st;
+  for (int r = 0; r < p; ++r)
+    if ((st = check_buf(recvbufs[r], esz, "recvbufs", r))) return st;
+  std::vector<Range> outs, ins{range_of(sendbuf, n * esz, root)};
+  for (int r = 0; r < p; ++r) outs.push_back(range_of(recvbufs[r], n * esz, r));
+  st = check_aliasing(outs, ins, [](const Range& o, const Range& i) { return o.rank == i.rank && o.lo == i.lo; });
+  if (st) return st;
+  rr::FanoutArgs a;
+  memset(&a, 0, sizeof(a));
+  std::vector<uintptr_t> addrs{reinterpret_cast<uintptr_t>(sendbuf)};
+  int m = 0;
+  for (int r = 0; r < p; ++r) {
+    if (recvbufs[r] == sendbuf) continue;  // the root's in-place copy
+    a.dst[m++] = recvbufs[r];
+    addrs.push_back(reinterpret_cast<uintptr_t>(recvbufs[r]));
+  }
+  if (m == 0) return ok();
+  a.src[0] = sendbuf;
+  a.seg_bytes = n * esz;
+  a.dst_seg_stride = 0;
+  a.nseg = 1;
+  a.ndst = m;
+  const Tuning t = tuning();
+  const int unit = copy_unit(addrs, {n * esz});
+  if (t.log) fprintf(stderr, "[rr] broadcast: %d copies of %llu bytes unit=%d\n", m, (unsigned long long)(n * esz), unit);
+  const hipError_t e = rr::launch_fanout(a, unit, t.grid_cap, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "broadcast");
+  return ok();
+}
+
+size_t rr_workspace_size(rr_algo_t algo, int p, int group_size, size_t n, rr_dtype_t dtype) {
+  if (p < 1 || p > RR_MAX_RANKS || rr::elem_size(dtype) == 0 || static_cast<uint64_t>(n) > kMaxElems) return 0;
+  if (algo == RR_ALGO_HIER_STAGED && (group_size < 1 || group_size > p || p % group_size)) return 0;
+  return workspace_bytes(algo, p, group_size, n, dtype);
+}
+
+const char* rr_status_string(rr_status_t status) {
+  switch (status) {
+    case RR_SUCCESS: return "success";
+    case RR_ERROR_INVALID_ARGUMENT: return "invalid argument";
+    case RR_ERROR_UNSUPPORTED: return "unsupported dtype or op";
+    case RR_ERROR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* rr_last_error(void) { return g_last_error.c_str(); }
+
+const char* rr_version(void) { return "rr 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,224 @@
+// rr_copy.hip -- data-movement kernels (gfx950): one-to-many copies
+// (all-gather, broadcast), independent transfers (the ring's all-gather steps,
+// the staged hierarchy's in-group broadcast), type conversions and the ring's
+// reduce-scatter step.
+//
+// Page "分布式训练/推理", section "通信原语": broadcast copies one rank's tensor
+// to every rank; all-gather gives every rank the concatenation of all shards.
+// Page "LLM Parallelism 基础", section "Ring AllReduce": in a reduce-scatter
+// step the receiver accumulates the incoming chunk into its own; in an
+// all-gather step it overwrites its own chunk.
+//
+// Each lane moves whole units (16, 4, 2 or 1 bytes, the widest that every
+// address and length allows); a lane loads U units and stores them to every
+// destination, so a one-to-many copy reads its source once.
+#include "rr_device.h"
+#include "rr_kernels.h"
+
+namespace rr {
+
+namespace {
+
+template <int B>
+struct UnitT;
+template <>
+struct UnitT<16> {
+  using T = u32x4;
+};
+template <>
+struct UnitT<4> {
+  using T = uint32_t;
+};
+template <>
+struct UnitT<2> {
+  using T = uint16_t;
+};
+template <>
+struct UnitT<1> {
+  using T = uint8_t;
+};
+
+constexpr int kCopyU = 4;
+
+template <int B>
+__global__ __launch_bounds__(kBlock) void k_fanout(FanoutArgs a) {
+  using T = typename UnitT<B>::T;
+  const int seg = blockIdx.y;
+  const uint64_t units = a.seg_bytes / B;
+  const T* src = static_cast<const T*>(a.src[seg]);
+  const uint64_t dst_off = static_cast<uint64_t>(seg) * (a.dst_seg_stride / B);
+  constexpr uint64_t kTile = static_cast<uint64_t>(kBlock) * kCopyU;
+  for (uint64_t base = static_cast<uint64_t>(blockIdx.x) * kTile + threadIdx.x; base < units;
+       base += static_cast<uint64_t>(gridDim.x) * kTile) {
+    T v[kCopyU];
+#pragma unroll
+    for (int u = 0; u < kCopyU; ++u) {
+      const uint64_t i = base + static_cast<uint64_t>(u) * kBlock;
+      if (i < units) v[u] = src[i];
+    }
+    for (int r = 0; r < a.ndst; ++r) {
+      if (r == seg && ((a.skip_diag >> seg) & 1ull)) continue;
+      T* dst = static_cast<T*>(a.dst[r]) + dst_off;
+#pragma unroll
+      for (int u = 0; u < kCopyU; ++u) {
+        const uint64_t i = base + static_cast<uint64_t>(u) * kBlock;
+        if (i < units) dst[i] = v[u];
+      }
+    }
+  }
+}
+
+template <int B>
+__global__ __launch_bounds__(kBlock) void k_copy_pairs(PairArgs a) {
+  using T = typename UnitT<B>::T;
+  const int y = blockIdx.y;
+  const uint64_t units = a.len[y] / B;
+  const T* src = static_cast<const T*>(a.src[y]);
+  T* dst = static_cast<T*>(a.dst[y]);
+  constexpr uint64_t kTile = static_cast<uint64_t>(kBlock) * kCopyU;
+  for (uint64_t base = static_cast<uint64_t>(blockIdx.x) * kTile + threadIdx.x; base < units;
+       base += static_cast<uint64_t>(gridDim.x) * kTile) {
+    T v[kCopyU];
+#pragma unroll
+    for (int u = 0; u < kCopyU; ++u) {
+      const uint64_t i = base + static_cast<uint64_t>(u) * kBlock;
+      if (i < units) v[u] = src[i];
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyU; ++u) {
+      const uint64_t i = base + static_cast<uint64_t>(u) * kBlock;
+      if (i < units) dst[i] = v[u];
+    }
+  }
+}
+
+// Element-wise conversion (bf16 <-> f32 for the staged paths) or the ring's
+// reduce-scatter step (dst = src (+) dst, message first).  8 elements per
+// group on the vector path, scalar otherwise (and for the last partial group).
+template <class EF, class ET, class OP, bool STEP>
+__global__ __launch_bounds__(kBlock) void k_pairs_elem(PairArgs a) {
+  constexpr int V = 8;
+  using A = typename EF::A;
+  const int y = blockIdx.y;
+  const uint64_t n = a.len[y];
+  const typename EF::S* src = static_cast<const typename EF::S*>(a.src[y]);
+  typename ET::S* dst = static_cast<typename ET::S*>(a.dst[y]);
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
+  const uint64_t ngroups = a.vec ? n / V : 0;
+  for (uint64_t g = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; g < ngroups; g += stride) {
+    Raw<EF, V> rs;
+    load_group<false>(rs, src + g * V);
+    A x[V];
+    unpack(rs, x);
+    if constexpr (STEP) {
+      Raw<ET, V> rd;
+      load_group<false>(rd, dst + g * V);
+      A d[V];
+      unpack(rd, d);
+#pragma unroll
+      for (int j = 0; j < V; ++j) x[j] = OP::apply(x[j], d[j]);
+    }
+    Raw<ET, V> o;
+    pack(x, o);
+    store_group<false>(dst + g * V, o);
+  }
+  for (uint64_t i = ngroups * V + static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n; i += stride) {
+    A x = load_one<EF>(src + i);
+    if constexpr (STEP) x = OP::apply(x, load_one<ET>(dst + i));
+    store_one<ET>(dst + i, x);
+  }
+}
+
+uint64_t blocks_for(uint64_t units, uint64_t per_block, int rows, int grid_cap) {
+  uint64_t b = (units + per_block - 1) / per_block;
+  if (b < 1) b = 1;
+  if (grid_cap > 0) {
+    uint64_t cap = static_cast<uint64_t>(grid_cap) / static_cast<uint64_t>(rows > 0 ? rows : 1);
+    if (cap < 1) cap = 1;
+    if (b > cap) b = cap;
+  }
+  if (b > 0x7FFFFFFFull) b = 0x7FFFFFFFull;
+  return b;
+}
+
+template <class K, class ARGS>
+hipError_t go(K kernel, const ARGS& args, uint64_t bx, int rows, hipStream_t s) {
+  ARGS copy = args;
+  void* kp[] = {&copy};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(static_cast<unsigned>(bx), rows, 1),
+                         dim3(kBlock), kp, 0, s);
+}
+
+template <class EF, class ET, class OP, bool STEP>
+hipError_t pairs_elem(const PairArgs& a, int grid_cap, hipStream_t s) {
+  uint64_t longest = 0;
+  for (int y = 0; y < a.npairs; ++y) longest = a.len[y] > longest ? a.len[y] : longest;
+  const uint64_t bx = blocks_for(a.vec ? longest / 8 + 1 : longest, kBlock, a.npairs, grid_cap);
+  return go(&k_pairs_elem<EF, ET, OP, STEP>, a, bx, a.npairs, s);
+}
+
+template <class E>
+hipError_t ring_step_kind(const PairArgs& a, rr_op_t op, int grid_cap, hipStream_t s) {
+  switch (op) {
+    case RR_SUM: return pairs_elem<E, E, OpSum, true>(a, grid_cap, s);
+    case RR_MAX: return pairs_elem<E, E, OpMax, true>(a, grid_cap, s);
+    case RR_MIN: return pairs_elem<E, E, OpMin, true>(a, grid_cap, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_fanout(const FanoutArgs& a, int unit_bytes, int grid_cap, hipStream_t s) {
+  const uint64_t units = a.seg_bytes / static_cast<uint64_t>(unit_bytes);
+  const uint64_t bx = blocks_for(units, static_cast<uint64_t>(kBlock) * kCopyU, a.nseg, grid_cap);
+  switch (unit_bytes) {
+    case 16: return go(&k_fanout<16>, a, bx, a.nseg, s);
+    case 4: return go(&k_fanout<4>, a, bx, a.nseg, s);
+    case 2: return go(&k_fanout<2>, a, bx, a.nseg, s);
+    case 1: return go(&k_fanout<1>, a, bx, a.nseg, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_copy_pairs(const PairArgs& a, int unit_bytes, int grid_cap, hipStream_t s) {
+  uint64_t longest = 0;
+  for (int y = 0; y < a.npairs; ++y) longest = a.len[y] > longest ? a.len[y] : longest;
+  const uint64_t bx =
+      blocks_for(longest / static_cast<uint64_t>(unit_bytes), static_cast<uint64_t>(kBlock) * kCopyU, a.npairs,
+                 grid_cap);
+  switch (unit_bytes) {
+    case 16: return go(&k_copy_pairs<16>, a, bx, a.npairs, s);
+    case 4: return go(&k_copy_pairs<4>, a, bx, a.npairs, s);
+    case 2: return go(&k_copy_pairs<2>, a, bx, a.npairs, s);
+    case 1: return go(&k_copy_pairs<1>, a, bx, a.npairs, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_convert_pairs(const PairArgs& a, Kind from, Kind to, int grid_cap, hipStream_t s) {
+  if (from == Kind::kBF16 && to == Kind::kF32) return pairs_elem<EBF16, EF32, OpSum, false>(a, grid_cap, s);
+  if (from == Kind::kF32 && to == Kind::kBF16) return pairs_elem<EF32, EBF16, OpSum, false>(a, grid_cap, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_ring_step(const PairArgs& a, Kind acc_kind, rr_op_t op, int grid_cap, hipStream_t s) {
+  switch (acc_kind) {
+    case Kind::kI32: return ring_step_kind<EI32>(a, op, grid_cap, s);
+    case Kind::kF32: return ring_step_kind<EF32>(a, op, grid_cap, s);
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fold(const FoldLaunch& f, hipStream_t s) {
+  switch (f.mode) {
+    case FoldMode::kRingAll: return launch_fold_ring_all(f, s);
+    case FoldMode::kRingShard: return launch_fold_ring_shard(f, s);
+    case FoldMode::kAscOne: return launch_fold_asc_one(f, s);
+    case FoldMode::kHierAll: return launch_fold_hier_all(f, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace rr

@@ -1,0 +1,380 @@
+// rr_fold_impl.h -- the p-way streaming fold kernel (gfx950) and its dispatch.
+//
+// One kernel template serves every reduction of the library: ring all-reduce
+// (each chunk folded in the ring's reduce-scatter order, all p outputs written
+// in the same pass, i.e. reduce-scatter and all-gather fused), ring
+// reduce-scatter, reduce, the fused hierarchical all-reduce and the steps of
+// the staged hierarchy.  The ring order comes from page "LLM Parallelism 基础",
+// section "Ring AllReduce" (every rank sends to the next rank; the receiver
+// accumulates), which folds chunk c as x_{c+1}, x_{c+2}, ..., x_c.
+//
+// Work decomposition.  Workgroup row blockIdx.y is a chunk (ring modes) or a
+// segment; along x, workgroups stride over tiles of kBlock*U groups, a group
+// being V elements moved with 16-byte accesses.  Each lane owns whole groups:
+// it issues the loads of all p inputs for its U groups first (p*U 16-byte
+// loads in flight per lane), then folds in registers in the fixed order,
+// converts once and stores to every output.  The reduction across ranks thus
+// happens inside each lane; no LDS, no barriers, no cross-lane traffic, so the
+// float order is exactly the specified one and in-place operation is safe
+// (a lane reads all inputs of an element before writing any output of it).
+// Chunk heads and tails that do not fill a group, and buffers that are not
+// 16-byte aligned, take a scalar path with the same order.
+#pragma once
+
+#include "rr_device.h"
+#include "rr_kernels.h"
+
+namespace rr {
+
+template <class TI, class TO>
+constexpr int group_len() {
+  return 16 / static_cast<int>(sizeof(typename TI::S) < sizeof(typename TO::S) ? sizeof(typename TI::S)
+                                                                               : sizeof(typename TO::S));
+}
+
+constexpr bool is_ring(FoldMode m) { return m == FoldMode::kRingAll || m == FoldMode::kRingShard; }
+constexpr bool writes_all(FoldMode m) { return m == FoldMode::kRingAll || m == FoldMode::kHierAll; }
+
+// k-th input in the fold order of row `seg`.
+template <FoldMode M>
+__device__ __forceinline__ int fold_src(int k, int seg, int p) {
+  if constexpr (is_ring(M)) {
+    const int r = seg + 1 + k;  // seg <= p-1 and k <= p-1, so r <= 2p-1
+    return r >= p ? r - p : r;
+  } else if constexpr (M == FoldMode::kAscOne) {
+    return seg * p + k;
+  } else {
+    return k;
+  }
+}
+
+// Fold step k (k >= 1) of value x into the running state.  For the hierarchy,
+// `acc` is the running group partial and `tot` the running fold of finished
+// groups; a new group starts at every multiple of `group`.
+template <class OP, FoldMode M, class A>
+__device__ __forceinline__ void fold_step(A& acc, A& tot, A x, int k, int group) {
+  if constexpr (M == FoldMode::kHierAll) {
+    if (k % group == 0) {
+      tot = (k == group) ? acc : OP::apply(tot, acc);
+      acc = x;
+    } else {
+      acc = OP::apply(acc, x);
+    }
+  } else {
+    acc = OP::apply(acc, x);
+  }
+}
+
+template <class OP, FoldMode M, class A>
+__device__ __forceinline__ A fold_finish(A acc, A tot, int p, int group) {
+  if constexpr (M == FoldMode::kHierAll) {
+    return (p > group) ? OP::apply(tot, acc) : acc;
+  } else {
+    return acc;
+  }
+}
+
+// Scalar path: element i of row seg.
+template <class TI, class TO, class OP, FoldMode M>
+__device__ __forceinline__ void fold_scalar(const FoldArgs& a, uint64_t i, uint64_t lo, int seg, int p) {
+  using SI = typename TI::S;
+  using SO = typename TO::S;
+  using A = typename TI::A;
+  A acc = load_one<TI>(static_cast<const SI*>(a.in[fold_src<M>(0, seg, p)]) + i);
+  A tot = acc;
+  for (int k = 1; k < p; ++k) {
+    const A x = load_one<TI>(static_cast<const SI*>(a.in[fold_src<M>(k, seg, p)]) + i);
+    fold_step<OP, M>(acc, tot, x, k, a.group);
+  }
+  acc = fold_finish<OP, M>(acc, tot, p, a.group);
+  if constexpr (writes_all(M)) {
+    for (int r = 0; r < p; ++r) store_one<TO>(static_cast<SO*>(a.out[r]) + i, acc);
+  } else if constexpr (M == FoldMode::kRingShard) {
+    store_one<TO>(static_cast<SO*>(a.out[seg]) + (i - lo), acc);
+  } else {
+    store_one<TO>(static_cast<SO*>(a.out[seg]) + i, acc);
+  }
+}
+
+// Vector path, compile-time p: all p*U loads first, then the folds.
+template <class TI, class TO, class OP, int P, int U, bool NT, FoldMode M, bool GUARD>
+__device__ __forceinline__ void fold_tile(const typename TI::S* const* src, typename TO::S* const* dst,
+                                          uint64_t g0, uint64_t g_end, uint64_t lo, int group) {
+  constexpr int V = group_len<TI, TO>();
+  using A = typename TI::A;
+  Raw<TI, V> raw[U][P];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint64_t g = g0 + static_cast<uint64_t>(u) * kBlock;
+    if (!GUARD || g < g_end) {
+#pragma unroll
+      for (int k = 0; k < P; ++k) load_group<NT>(raw[u][k], src[k] + g * V);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint64_t g = g0 + static_cast<uint64_t>(u) * kBlock;
+    if (GUARD && g >= g_end) continue;
+    A acc[V];
+    A tot[V];
+    unpack(raw[u][0], acc);
+#pragma unroll
+    for (int j = 0; j < V; ++j) tot[j] = acc[j];
+#pragma unroll
+    for (int k = 1; k < P; ++k) {
+      A x[V];
+      unpack(raw[u][k], x);
+#pragma unroll
+      for (int j = 0; j < V; ++j) fold_step<OP, M>(acc[j], tot[j], x[j], k, group);
+    }
+#pragma unroll
+    for (int j = 0; j < V; ++j) acc[j] = fold_finish<OP, M>(acc[j], tot[j], P, group);
+    Raw<TO, V> o;
+    pack(acc, o);
+    if constexpr (writes_all(M)) {
+#pragma unroll
+      for (int r = 0; r < P; ++r) store_group<NT>(dst[r] + g * V, o);
+    } else if constexpr (M == FoldMode::kRingShard) {
+      store_group<NT>(dst[0] + (g * V - lo), o);
+    } else {
+      store_group<NT>(dst[0] + g * V, o);
+    }
+  }
+}
+
+// Vector path, run-time p: inputs are streamed one rank at a time, U groups
+// per lane in flight.
+template <class TI, class TO, class OP, int U, bool NT, FoldMode M, bool GUARD>
+__device__ __forceinline__ void fold_tile_dyn(const FoldArgs& a, int seg, int p, uint64_t g0, uint64_t g_end,
+                                              uint64_t lo) {
+  constexpr int V = group_len<TI, TO>();
+  using SI = typename TI::S;
+  using SO = typename TO::S;
+  using A = typename TI::A;
+  A acc[U][V];
+  A tot[U][V];
+  {
+    const SI* s0 = static_cast<const SI*>(a.in[fold_src<M>(0, seg, p)]);
+    Raw<TI, V> raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t g = g0 + static_cast<uint64_t>(u) * kBlock;
+      if (!GUARD || g < g_end) load_group<NT>(raw[u], s0 + g * V);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      unpack(raw[u], acc[u]);
+#pragma unroll
+      for (int j = 0; j < V; ++j) tot[u][j] = acc[u][j];
+    }
+  }
+  for (int k = 1; k < p; ++k) {
+    const SI* sk = static_cast<const SI*>(a.in[fold_src<M>(k, seg, p)]);
+    Raw<TI, V> raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t g = g0 + static_cast<uint64_t>(u) * kBlock;
+      if (!GUARD || g < g_end) load_group<NT>(raw[u], sk + g * V);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      A x[V];
+      unpack(raw[u], x);
+#pragma unroll
+      for (int j = 0; j < V; ++j) fold_step<OP, M>(acc[u][j], tot[u][j], x[j], k, a.group);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint64_t g = g0 + static_cast<uint64_t>(u) * kBlock;
+    if (GUARD && g >= g_end) continue;
+#pragma unroll
+    for (int j = 0; j < V; ++j) acc[u][j] = fold_finish<OP, M>(acc[u][j], tot[u][j], p, a.group);
+    Raw<TO, V> o;
+    pack(acc[u], o);
+    if constexpr (writes_all(M)) {
+      for (int r = 0; r < p; ++r) store_group<NT>(static_cast<SO*>(a.out[r]) + g * V, o);
+    } else if constexpr (M == FoldMode::kRingShard) {
+      store_group<NT>(static_cast<SO*>(a.out[seg]) + (g * V - lo), o);
+    } else {
+      store_group<NT>(static_cast<SO*>(a.out[seg]) + g * V, o);
+    }
+  }
+}
+
+template <class TI, class TO, class OP, int P, int U, bool NT, FoldMode M>
+__global__ __launch_bounds__(kBlock) void k_fold(FoldArgs a) {
+  constexpr int V = group_len<TI, TO>();
+  using SI = typename TI::S;
+  using SO = typename TO::S;
+  const int p = (P > 0) ? P : a.p;
+  const int seg = blockIdx.y;
+  uint64_t lo = 0;
+  uint64_t hi = a.n;
+  if constexpr (is_ring(M)) {
+    lo = a.bound[seg];
+    hi = a.bound[seg + 1];
+  }
+  if (!a.vec) {
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
+    for (uint64_t i = lo + static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; i < hi; i += stride)
+      fold_scalar<TI, TO, OP, M>(a, i, lo, seg, p);
+    return;
+  }
+  const uint64_t g_lo = (lo + V - 1) / V;
+  uint64_t g_hi = hi / V;
+  if (g_hi < g_lo) g_hi = g_lo;
+  const uint64_t ngroups = g_hi - g_lo;
+  constexpr uint64_t kTile = static_cast<uint64_t>(kBlock) * U;
+  const uint64_t ntiles = (ngroups + kTile - 1) / kTile;
+  if constexpr (P > 0) {
+    // Rotated input pointers and output pointers, uniform across the
+    // workgroup (scalar registers).
+    const SI* src[P];
+#pragma unroll
+    for (int k = 0; k < P; ++k) src[k] = static_cast<const SI*>(a.in[fold_src<M>(k, seg, P)]);
+    constexpr int ND = writes_all(M) ? P : 1;
+    SO* dst[ND];
+    if constexpr (writes_all(M)) {
+#pragma unroll
+      for (int r = 0; r < P; ++r) dst[r] = static_cast<SO*>(a.out[r]);
+    } else {
+      dst[0] = static_cast<SO*>(a.out[seg]);
+    }
+    for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+      const uint64_t g0 = g_lo + t * kTile + threadIdx.x;
+      if ((t + 1) * kTile <= ngroups) {
+        fold_tile<TI, TO, OP, P, U, NT, M, false>(src, dst, g0, g_hi, lo, a.group);
+      } else {
+        fold_tile<TI, TO, OP, P, U, NT, M, true>(src, dst, g0, g_hi, lo, a.group);
+      }
+    }
+  } else {
+    for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+      const uint64_t g0 = g_lo + t * kTile + threadIdx.x;
+      if ((t + 1) * kTile <= ngroups) {
+        fold_tile_dyn<TI, TO, OP, U, NT, M, false>(a, seg, p, g0, g_hi, lo);
+      } else {
+        fold_tile_dyn<TI, TO, OP, U, NT, M, true>(a, seg, p, g0, g_hi, lo);
+      }
+    }
+  }
+  // Head [lo, g_lo*V) and tail [g_hi*V, hi) of the row: fewer than V elements
+  // each, done by the first 2V lanes of workgroup 0 of the row.
+  if (blockIdx.x == 0 && threadIdx.x < 2 * V) {
+    const uint64_t vb = g_lo * V;
+    const uint64_t head_end = vb < hi ? vb : hi;
+    const bool is_head = threadIdx.x < V;
+    const uint64_t i = is_head ? lo + threadIdx.x : g_hi * V + (threadIdx.x - V);
+    if (is_head ? (i < head_end) : (i < hi)) fold_scalar<TI, TO, OP, M>(a, i, lo, seg, p);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side dispatch.
+
+template <class TI, class TO, class OP, int P, int U, bool NT, FoldMode M>
+hipError_t fold_go(const FoldLaunch& f, hipStream_t s) {
+  constexpr int V = group_len<TI, TO>();
+  uint64_t longest = 0;
+  if constexpr (is_ring(M)) {
+    for (int c = 0; c < f.segments; ++c) {
+      const uint64_t len = f.args.bound[c + 1] - f.args.bound[c];
+      if (len > longest) longest = len;
+    }
+  } else {
+    longest = f.args.n;
+  }
+  uint64_t blocks_x;
+  if (f.args.vec) {
+    const uint64_t groups = longest / V + 1;
+    blocks_x = (groups + static_cast<uint64_t>(kBlock) * U - 1) / (static_cast<uint64_t>(kBlock) * U);
+  } else {
+    blocks_x = (longest + kBlock - 1) / kBlock;
+  }
+  if (blocks_x < 1) blocks_x = 1;
+  if (f.grid_cap > 0) {
+    uint64_t cap_x = static_cast<uint64_t>(f.grid_cap) / static_cast<uint64_t>(f.segments);
+    if (cap_x < 1) cap_x = 1;
+    if (blocks_x > cap_x) blocks_x = cap_x;
+  }
+  if (blocks_x > 0x7FFFFFFFull) blocks_x = 0x7FFFFFFFull;
+  dim3 grid(static_cast<unsigned>(blocks_x), static_cast<unsigned>(f.segments), 1);
+  FoldArgs args = f.args;
+  void* kp[] = {&args};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&k_fold<TI, TO, OP, P, U, NT, M>), grid, dim3(kBlock),
+                         kp, 0, s);
+}
+
+// Variants compiled for the tunable path (sum, p in {4, 8}): U in {1, 2, 4},
+// nontemporal on/off.  Everything else uses U = 2 (U = 1 for p = 16) and
+// ordinary loads/stores.
+template <class TI, class TO, class OP, int P, FoldMode M>
+hipError_t fold_variants(const FoldLaunch& f, hipStream_t s) {
+  constexpr bool kTunable = __is_same(OP, OpSum) && (P == 4 || P == 8);
+  if constexpr (kTunable) {
+    const int u = f.unroll;
+    const bool nt = f.nontemporal != 0;
+    if (u == 1) return nt ? fold_go<TI, TO, OP, P, 1, true, M>(f, s) : fold_go<TI, TO, OP, P, 1, false, M>(f, s);
+    if (u == 4) return nt ? fold_go<TI, TO, OP, P, 4, true, M>(f, s) : fold_go<TI, TO, OP, P, 4, false, M>(f, s);
+    return nt ? fold_go<TI, TO, OP, P, 2, true, M>(f, s) : fold_go<TI, TO, OP, P, 2, false, M>(f, s);
+  } else {
+    constexpr int kU = (P >= 16) ? 1 : 2;
+    return fold_go<TI, TO, OP, P, kU, false, M>(f, s);
+  }
+}
+
+template <class TI, class TO, class OP, FoldMode M>
+hipError_t fold_by_p(const FoldLaunch& f, hipStream_t s) {
+  switch (f.args.p) {
+    case 2: return fold_variants<TI, TO, OP, 2, M>(f, s);
+    case 4: return fold_variants<TI, TO, OP, 4, M>(f, s);
+    case 8: return fold_variants<TI, TO, OP, 8, M>(f, s);
+    case 16: return fold_variants<TI, TO, OP, 16, M>(f, s);
+    default: return fold_go<TI, TO, OP, 0, 2, false, M>(f, s);
+  }
+}
+
+template <class TI, class TO, FoldMode M>
+hipError_t fold_by_op(const FoldLaunch& f, hipStream_t s) {
+  switch (f.op) {
+    case RR_SUM: return fold_by_p<TI, TO, OpSum, M>(f, s);
+    case RR_MAX: return fold_by_p<TI, TO, OpMax, M>(f, s);
+    case RR_MIN: return fold_by_p<TI, TO, OpMin, M>(f, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// Same-kind folds for every mode; the mixed bf16 <-> f32 pairs exist for the
+// staged hierarchy (kAscOne writes float32 partials, kHierAll reads them) and
+// always take the run-time-p kernel.
+template <FoldMode M>
+hipError_t fold_by_kind(const FoldLaunch& f, hipStream_t s) {
+  if (f.in_kind == f.out_kind) {
+    switch (f.in_kind) {
+      case Kind::kI32: return fold_by_op<EI32, EI32, M>(f, s);
+      case Kind::kF32: return fold_by_op<EF32, EF32, M>(f, s);
+      case Kind::kBF16: return fold_by_op<EBF16, EBF16, M>(f, s);
+    }
+    return hipErrorInvalidValue;
+  }
+  if constexpr (M == FoldMode::kAscOne || M == FoldMode::kHierAll) {
+    if (f.in_kind == Kind::kBF16 && f.out_kind == Kind::kF32) {
+      switch (f.op) {
+        case RR_SUM: return fold_go<EBF16, EF32, OpSum, 0, 2, false, M>(f, s);
+        case RR_MAX: return fold_go<EBF16, EF32, OpMax, 0, 2, false, M>(f, s);
+        case RR_MIN: return fold_go<EBF16, EF32, OpMin, 0, 2, false, M>(f, s);
+      }
+    }
+    if (f.in_kind == Kind::kF32 && f.out_kind == Kind::kBF16) {
+      switch (f.op) {
+        case RR_SUM: return fold_go<EF32, EBF16, OpSum, 0, 2, false, M>(f, s);
+        case RR_MAX: return fold_go<EF32, EBF16, OpMax, 0, 2, false, M>(f, s);
+        case RR_MIN: return fold_go<EF32, EBF16, OpMin, 0, 2, false, M>(f, s);
+      }
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace rr

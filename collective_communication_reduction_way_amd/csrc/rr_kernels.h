@@ -1,0 +1,96 @@
+// rr_kernels.h -- kernel argument blocks and launchers (internal to librr.so).
+//
+// Every argument block is passed to its kernel by value (kernarg segment, at
+// most a few KiB), so a launch needs no device-side pointer table, no copy
+// and no allocation.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "rr.h"
+
+namespace rr {
+
+constexpr int kBlock = 256;  // threads per workgroup: 4 wavefronts of 64 lanes
+
+// Which inputs a fold reads, in which order, and where it writes.
+enum class FoldMode : int {
+  // Ring all-reduce: workgroup row y = chunk c; element i of chunk c folds
+  // in[(c+1)%p], in[(c+2)%p], ..., in[c]; the result goes to out[0..p-1][i].
+  kRingAll = 0,
+  // Ring reduce-scatter: same fold; chunk c goes to out[c][i - bound[c]].
+  kRingShard = 1,
+  // Ascending fold per segment: row y = segment j folds in[j*p + 0..p-1] in
+  // that order into out[j][i].  (Reduce: one segment.  Staged hierarchy step
+  // one: one segment per group.)
+  kAscOne = 2,
+  // Hierarchical: in[0..p-1] folded ascending inside groups of `group`
+  // consecutive inputs, the group partials folded ascending; the result goes
+  // to out[0..p-1][i].
+  kHierAll = 3,
+};
+
+enum class Kind : int { kI32 = 0, kF32 = 1, kBF16 = 2 };
+
+struct FoldArgs {
+  const void* in[RR_MAX_RANKS];
+  void* out[RR_MAX_RANKS];
+  uint64_t bound[RR_MAX_RANKS + 1];  // ring modes: chunk bounds floor(c*n/p)
+  uint64_t n;                         // elements per input buffer
+  int32_t p;                          // inputs folded per output element
+  int32_t group;                      // kHierAll: group size (divides p)
+  int32_t vec;                        // 1: every buffer is 16-byte aligned
+  int32_t pad;
+};
+
+struct FoldLaunch {
+  FoldArgs args;
+  FoldMode mode;
+  Kind in_kind;
+  Kind out_kind;
+  rr_op_t op;
+  int segments;    // grid rows: chunks (ring modes), segments (kAscOne) or 1
+  int unroll;      // groups per lane per tile (1, 2 or 4); 0 = default
+  int nontemporal; // 1 = nontemporal loads/stores
+  int grid_cap;    // max workgroups in total (0 = one tile per workgroup)
+};
+
+// One source to many destinations: row y copies seg_bytes from src[y] to
+// dst[r] + y*dst_seg_stride for every r < ndst, except r == y when bit y of
+// skip_diag is set (an in-place shard that already sits in its slot).
+struct FanoutArgs {
+  const void* src[RR_MAX_RANKS];
+  void* dst[RR_MAX_RANKS];
+  uint64_t seg_bytes;
+  uint64_t dst_seg_stride;
+  uint64_t skip_diag;
+  int32_t nseg;
+  int32_t ndst;
+};
+
+// Independent transfers: row y moves len[y] elements from src[y] to dst[y]
+// (copy, type conversion, or, for the ring step, dst = src (+) dst).
+struct PairArgs {
+  const void* src[RR_MAX_RANKS];
+  void* dst[RR_MAX_RANKS];
+  uint64_t len[RR_MAX_RANKS];
+  int32_t npairs;
+  int32_t vec;
+};
+
+hipError_t launch_fold(const FoldLaunch& f, hipStream_t stream);
+hipError_t launch_fold_ring_all(const FoldLaunch& f, hipStream_t stream);
+hipError_t launch_fold_ring_shard(const FoldLaunch& f, hipStream_t stream);
+hipError_t launch_fold_asc_one(const FoldLaunch& f, hipStream_t stream);
+hipError_t launch_fold_hier_all(const FoldLaunch& f, hipStream_t stream);
+hipError_t launch_fanout(const FanoutArgs& a, int unit_bytes, int grid_cap, hipStream_t stream);
+// Plain copy: len[] in bytes, unit_bytes in {16, 4, 2, 1}.
+hipError_t launch_copy_pairs(const PairArgs& a, int unit_bytes, int grid_cap, hipStream_t stream);
+// Element conversion: len[] in elements.
+hipError_t launch_convert_pairs(const PairArgs& a, Kind from, Kind to, int grid_cap, hipStream_t stream);
+// Ring reduce-scatter step on accumulator-type buffers: dst = src (+) dst.
+hipError_t launch_ring_step(const PairArgs& a, Kind acc_kind, rr_op_t op, int grid_cap,
+                            hipStream_t stream);
+
+}  // namespace rr

@@ -1,0 +1,264 @@
+/*
+ * rr.h -- collective reductions over p virtual ranks resident in one GPU's HBM.
+ *
+ * C ABI of librr.so (AMD Instinct MI355X, gfx950).  A "virtual rank" r is a
+ * device buffer; one call performs the whole collective for all p ranks, so
+ * each entry point takes arrays of p rank buffers where a per-process API
+ * (torch.distributed, MPI) takes one.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [SEM]  page "分布式训练/推理" (llm-from-scratch, chapter 7), section
+ *          "通信原语：rank、world size 和 collective operations": the semantics
+ *          table of the primitives, y = sum_{r=0}^{p-1} x_r, the worked example
+ *          x_r = [0,1,2,3] + r (p = 4), all_reduce = reduce_scatter + all_gather;
+ *          section "PyTorch distributed": all-reduce works in place,
+ *          reduce-scatter writes a separate, p times smaller output.
+ *   [RING] page "LLM Parallelism 基础", section "Ring AllReduce": N chunks,
+ *          reduce-scatter phase then all-gather phase, 2(N-1) steps, each
+ *          rank passes one chunk per step to the next rank on the ring; the
+ *          receiver accumulates (phase 1) or overwrites (phase 2); rank c ends
+ *          phase 1 holding the reduced chunk c.  Section "MPI Collective
+ *          Operations": reduce, broadcast; all-reduce has the effect of a
+ *          reduce followed by a broadcast.
+ *   [HIER] page "大模型并行的最小闭环：集合通信、TP、FSDP/ZeRO-3 到权重分片",
+ *          section "Source Log: 2026-05-05" (hierarchical AllReduce + SHARP,
+ *          steps 1-6 and the traffic comparison).
+ *
+ * Conventions common to every entry point
+ * ----------------------------------------
+ *  - p: number of virtual ranks, 1 <= p <= RR_MAX_RANKS.
+ *  - n: ALWAYS the full per-rank vector length in elements (for
+ *    reduce-scatter and all-gather the shard length is n / p).
+ *  - Buffers are device pointers owned by the caller; rank arrays
+ *    (sendbufs, recvbufs) are host arrays of p device pointers, read only
+ *    during the call and passed to the kernels by value (no device-side
+ *    table, no host-to-device copy, no device allocation on these paths).
+ *  - Every pointer must be aligned to its element size.  16-byte alignment of
+ *    every buffer selects the 128-bit vector path; otherwise a scalar path
+ *    with the same arithmetic order runs, so results are identical.
+ *  - Arithmetic: int32 sums wrap modulo 2^32; float32 sums are IEEE-754
+ *    round-to-nearest-even additions; bfloat16 inputs are widened exactly to
+ *    float32, folded in float32 and rounded once to bfloat16 (nearest even;
+ *    a NaN stays NaN, sign kept, made quiet); denormals are kept (no flush).
+ *    max/min are compare-and-select with the running value first: it is
+ *    replaced only by a strictly greater (max) / strictly smaller (min)
+ *    value, so ties (+0 vs -0) keep the earlier operand, a NaN running value
+ *    stays and a NaN new value is skipped.
+ *  - Fold orders (they decide float results bit for bit):
+ *      ring all-reduce and reduce-scatter: element i of chunk c is folded as
+ *        x_{c+1}, x_{c+2}, ..., x_{c+p-1}, x_c (indices mod p) -- the order in
+ *        which the ring's reduce-scatter phase accumulates chunk c when every
+ *        rank sends to rank r+1 [RING];
+ *      reduce: x_0, x_1, ..., x_{p-1} (the order of the sum in [SEM]);
+ *      hierarchical: ascending inside each group, then ascending over groups.
+ *    Chunk c of a rank's vector is [floor(c*n/p), floor((c+1)*n/p)).
+ *  - Asynchrony: every call validates on the host, enqueues its kernels on
+ *    `stream` (NULL = the null stream of the current device) and returns.
+ *    The library never synchronizes.  Completion is observed through the
+ *    stream.  Buffers must stay valid until the work completes.
+ *  - Errors: return codes only.  All validation happens before the first
+ *    launch, so a call that returns RR_ERROR_INVALID_ARGUMENT or
+ *    RR_ERROR_UNSUPPORTED has written nothing.  A launch failure returns
+ *    RR_ERROR_HIP; asynchronous faults surface on the stream's next sync.
+ *    rr_last_error() gives a message for the calling thread's last failure.
+ *  - n == 0 is a valid no-op (RR_SUCCESS, nothing launched) once p, dtype,
+ *    op and the rank arrays are valid.
+ *  - Aliasing: output buffers must not overlap each other or any input,
+ *    except the exact in-place forms named per entry point.  Input buffers
+ *    may alias each other (they are only read).
+ *  - Calls on different streams that write the same buffers race; calls on
+ *    one stream are ordered.
+ */
+#ifndef RR_H
+#define RR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RR_MAX_RANKS 64
+
+/* Opaque HIP stream handle (the same type as hipStream_t). */
+typedef struct ihipStream_t* rr_stream_t;
+
+typedef enum { RR_INT32 = 0, RR_FLOAT32 = 1, RR_BFLOAT16 = 2 } rr_dtype_t;
+
+typedef enum { RR_SUM = 0, RR_MAX = 1, RR_MIN = 2 } rr_op_t;
+
+typedef enum {
+  RR_SUCCESS = 0,
+  RR_ERROR_INVALID_ARGUMENT = 1,
+  RR_ERROR_UNSUPPORTED = 2,
+  RR_ERROR_HIP = 3
+} rr_status_t;
+
+typedef enum {
+  RR_ALGO_RING_FUSED = 0,  /* one pass: ring-order fold of each chunk, all p outputs written */
+  RR_ALGO_RING_STAGED = 1, /* the ring schedule executed step by step: 2(p-1) launches */
+  RR_ALGO_HIER_FUSED = 2,  /* one pass: group folds, cross-group fold, all p outputs written */
+  RR_ALGO_HIER_STAGED = 3  /* group reduce to the representative, cross-group reduce, broadcast */
+} rr_algo_t;
+
+typedef enum {
+  RR_COLL_ALL_REDUCE = 0,
+  RR_COLL_REDUCE_SCATTER = 1,
+  RR_COLL_ALL_GATHER = 2,
+  RR_COLL_REDUCE = 3,
+  RR_COLL_BROADCAST = 4
+} rr_coll_t;
+
+/*
+ * All-reduce [SEM] [RING]: every rank receives y = x_0 (+) x_1 (+) ... (+) x_{p-1}.
+ *   sendbufs[r]: rank r's input, n elements.   recvbufs[r]: rank r's output, n
+ *   elements.  In place allowed: recvbufs[r] == sendbufs[r] (for every r or
+ *   for some r).  Fold order: ring order per chunk (see above); equivalent to
+ *   the ring's reduce-scatter followed by its all-gather, fused into one pass
+ *   that reads every input once and writes every output once.
+ *   Any n is accepted (chunk bounds floor(c*n/p)).
+ *   Returns RR_ERROR_INVALID_ARGUMENT for: p out of range, NULL arrays or
+ *   buffers, misaligned buffers, overlapping outputs; RR_ERROR_UNSUPPORTED for
+ *   an unknown dtype or op.
+ */
+rr_status_t rr_all_reduce(const void* const* sendbufs, void* const* recvbufs, int p, size_t n,
+                          rr_dtype_t dtype, rr_op_t op, rr_stream_t stream);
+
+/*
+ * All-reduce with an explicit algorithm.
+ *   algo = RR_ALGO_RING_FUSED: same as rr_all_reduce (group_size and workspace ignored).
+ *   algo = RR_ALGO_RING_STAGED: the ring schedule of [RING] run literally, one
+ *     launch per step (2(p-1) steps, plus a copy of the inputs into recvbufs
+ *     when not in place): reduce-scatter step s moves chunk (r-1-s) mod p from
+ *     rank r to rank r+1 and the receiver stores message (+) local; all-gather
+ *     step s moves chunk (r-s) mod p and the receiver overwrites.  Any n (the
+ *     chunk bounds above).  For bfloat16 the partial sums live in a float32 workspace of
+ *     rr_workspace_size() bytes (one rounding at the end); int32/float32 work
+ *     in recvbufs and need no workspace.  Bitwise equal to RR_ALGO_RING_FUSED.
+ *   algo = RR_ALGO_HIER_FUSED [HIER]: ranks form p/group_size contiguous groups
+ *     [j*G, (j+1)*G) whose representative is rank j*G.  Each group's inputs are
+ *     folded ascending in the accumulator type, the group partials are folded
+ *     ascending over groups (no rounding in between), converted once, and
+ *     written to every rank.  One pass; no workspace.
+ *   algo = RR_ALGO_HIER_STAGED: the same arithmetic in the steps of [HIER]:
+ *     (1) each group reduces into an accumulator-type workspace slot of its
+ *     representative, (2-5) the representatives' partials are folded across
+ *     groups and the result written to every representative's recvbuf,
+ *     (6) each representative's result is broadcast inside its group.  Needs
+ *     rr_workspace_size() bytes of workspace.  Bitwise equal to HIER_FUSED.
+ *   group_size: 1 <= group_size <= p and group_size | p (HIER algos only).
+ *   workspace: device memory of at least rr_workspace_size(algo, ...) bytes,
+ *     16-byte aligned, owned by the caller, not aliasing any buffer; may be
+ *     NULL when that size is 0.
+ *   Returns RR_ERROR_INVALID_ARGUMENT additionally for an unknown algo, a bad
+ *   group_size, or a missing, short, misaligned or overlapping workspace.
+ */
+rr_status_t rr_all_reduce_ex(const void* const* sendbufs, void* const* recvbufs, int p, size_t n,
+                             rr_dtype_t dtype, rr_op_t op, rr_algo_t algo, int group_size,
+                             void* workspace, size_t workspace_bytes, rr_stream_t stream);
+
+/*
+ * Reduce-scatter [SEM] [RING]: rank c receives chunk c of y.
+ *   sendbufs[r]: rank r's input, n elements.  recvbufs[c]: n/p elements.
+ *   Requires p | n.  Fold order: ring order (bitwise equal to chunk c of
+ *   rr_all_reduce).  In place allowed: recvbufs[c] == sendbufs[c] + c*(n/p)
+ *   elements (the slot of the rank's own chunk).
+ */
+rr_status_t rr_reduce_scatter(const void* const* sendbufs, void* const* recvbufs, int p, size_t n,
+                              rr_dtype_t dtype, rr_op_t op, rr_stream_t stream);
+
+/*
+ * All-gather [SEM] [RING]: every rank receives the concatenation of the p
+ * shards: recvbufs[r][c*(n/p) + j] = sendbufs[c][j].
+ *   sendbufs[c]: n/p elements.  recvbufs[r]: n elements.  Requires p | n.
+ *   In place allowed: sendbufs[c] == recvbufs[c] + c*(n/p) elements.
+ *   A bit copy: the dtype only sets the element size.
+ */
+rr_status_t rr_all_gather(const void* const* sendbufs, void* const* recvbufs, int p, size_t n,
+                          rr_dtype_t dtype, rr_stream_t stream);
+
+/*
+ * Reduce [SEM] [RING]: the root receives y, folded x_0, x_1, ..., x_{p-1}.
+ *   sendbufs[r]: n elements.  recvbuf: the root's output, n elements.
+ *   root: 0 <= root < p; in place allowed: recvbuf == sendbufs[root].
+ */
+rr_status_t rr_reduce(const void* const* sendbufs, void* recvbuf, int root, int p, size_t n,
+                      rr_dtype_t dtype, rr_op_t op, rr_stream_t stream);
+
+/*
+ * Broadcast [SEM] [RING]: every rank receives a copy of the root's buffer.
+ *   sendbuf: the root's input, n elements.  recvbufs[r]: n elements.
+ *   root: 0 <= root < p; in place allowed: recvbufs[root] == sendbuf (that
+ *   copy is skipped).  A bit copy: the dtype only sets the element size.
+ */
+rr_status_t rr_broadcast(const void* sendbuf, void* const* recvbufs, int root, int p, size_t n,
+                         rr_dtype_t dtype, rr_stream_t stream);
+
+/*
+ * Workspace bytes that rr_all_reduce_ex needs for (algo, p, group_size, n,
+ * dtype): 0 for the fused algorithms and for the staged ring on int32/float32;
+ * p*n*4 for the staged ring on bfloat16; (p/group_size)*n*4 for the staged
+ * hierarchy.  Returns 0 for invalid arguments as well (rr_all_reduce_ex then
+ * reports them).
+ */
+size_t rr_workspace_size(rr_algo_t algo, int p, int group_size, size_t n, rr_dtype_t dtype);
+
+/*
+ * The ring schedule of [RING] as a transfer list (host only; no GPU needed).
+ * Writes at most `cap` transfers, in execution order, into the caller's
+ * arrays: phase (0 = reduce-scatter: the receiver accumulates, 1 = all-gather:
+ * the receiver overwrites), step within the phase, source rank, destination
+ * rank (= source + 1 mod p) and chunk index.  Returns the total number of
+ * transfers, 2(p-1)p, or -1 for p out of range.  Any array may be NULL when
+ * cap is 0 (query the count).
+ */
+int rr_ring_schedule(int p, int* phase, int* step, int* src, int* dst, int* chunk, int cap);
+
+/* Chunk bounds (host only): bounds[c] = floor(c*n/p) for c = 0..p (p+1 values). */
+rr_status_t rr_chunk_bounds(int p, size_t n, size_t* bounds);
+
+/*
+ * Algorithmic HBM bytes of one call (host only): each input element read once
+ * and each output element written once.  all-reduce 2pns; reduce-scatter,
+ * all-gather and reduce (p+1)ns; broadcast ns + p*ns, or ns + (p-1)ns when the
+ * root's copy is in place (in_place != 0).  s = element size.
+ */
+rr_status_t rr_algorithmic_bytes(rr_coll_t coll, int p, size_t n, rr_dtype_t dtype, int in_place,
+                                 uint64_t* bytes);
+
+/*
+ * Bytes moved by the ring schedule per rank (host only), from the transfer
+ * list: sent_rs and sent_ag are the bytes one rank sends in each phase (each
+ * (p-1)/p of the rank's n*s bytes when p | n, the ring cost model of page
+ * "分布式训练/推理", section "Ring all-reduce 的带宽账").  max over ranks.
+ */
+rr_status_t rr_ring_bytes_per_rank(int p, size_t n, rr_dtype_t dtype, uint64_t* sent_rs,
+                                   uint64_t* sent_ag);
+
+/*
+ * Per-level traffic of a hierarchical all-reduce of `bytes_per_rank` bytes
+ * over p ranks in groups of group_size (host only), counting what [HIER]
+ * counts: intra_per_group = bytes the group's own all-reduce moves in step 1
+ * (group_size * bytes_per_rank); cross_per_group_flat = bytes a group sends
+ * across groups when every member ships its own buffer (group_size *
+ * bytes_per_rank); cross_per_group_hier = bytes a group sends across groups
+ * when only its representative ships the group's result (bytes_per_rank).
+ */
+rr_status_t rr_hier_traffic(int p, int group_size, uint64_t bytes_per_rank, uint64_t* intra_per_group,
+                            uint64_t* cross_per_group_flat, uint64_t* cross_per_group_hier);
+
+/* Static description of a status code. */
+const char* rr_status_string(rr_status_t status);
+
+/* Message describing the calling thread's most recent failed call ("" if none). */
+const char* rr_last_error(void);
+
+/* Library version string. */
+const char* rr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RR_H */

@@ -1,0 +1,213 @@
+"""The C ABI of librr.so on the CPU: every symbol declared in include/rr.h is
+exported, and every invalid-argument path returns its status before any HIP
+call (the pointers below are never dereferenced, nothing is launched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import collective_communication_reduction_way_amd as rr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rr.h")
+
+INVALID, UNSUPPORTED = 1, 2
+FAKE = 1 << 40  # a 16-byte aligned address that is never touched
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rr_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for f in ("rr_all_reduce", "rr_reduce_scatter", "rr_all_gather", "rr_reduce", "rr_broadcast"):
+        assert f in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(rr.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    L = rr.lib()
+    assert b"gfx950" in L.rr_version()
+    for st in range(4):
+        assert L.rr_status_string(st)
+
+
+def ptrs(base, p, stride):
+    return rr._ptr_array([base + r * stride for r in range(p)])
+
+
+def ar(p=4, n=1024, dt=1, op=0, algo=0, group=0, send=None, recv=None, ws=None, wsb=0):
+    L = rr.lib()
+    send = send if send is not None else ptrs(FAKE, p, 1 << 20)
+    recv = recv if recv is not None else ptrs(FAKE + (1 << 30), p, 1 << 20)
+    st = L.rr_all_reduce_ex(send, recv, p, n, dt, op, algo, group, ws, wsb, None)
+    return st, L.rr_last_error().decode()
+
+
+@pytest.mark.parametrize("p", [0, -1, 65, 1000])
+def test_all_reduce_bad_p(p):
+    st, msg = ar(p=p)
+    assert st == INVALID and "p=" in msg
+
+
+def test_all_reduce_unknown_dtype_and_op():
+    assert ar(dt=7)[0] == UNSUPPORTED
+    assert ar(op=9)[0] == UNSUPPORTED
+
+
+def test_all_reduce_null_arrays_and_buffers():
+    L = rr.lib()
+    assert L.rr_all_reduce(None, ptrs(FAKE, 4, 1 << 20), 4, 16, 1, 0, None) == INVALID
+    assert L.rr_all_reduce(ptrs(FAKE, 4, 1 << 20), None, 4, 16, 1, 0, None) == INVALID
+    send = rr._ptr_array([FAKE, FAKE + 4096, 0, FAKE + 8192])
+    st, msg = ar(send=send, n=16)
+    assert st == INVALID and "NULL" in msg
+
+
+def test_all_reduce_misaligned():
+    send = rr._ptr_array([FAKE + 2, FAKE + 8192, FAKE + 16384, FAKE + 32768])
+    st, msg = ar(send=send, n=16, dt=1)
+    assert st == INVALID and "aligned" in msg
+    # 2-byte alignment is enough for bf16
+    recv = ptrs(FAKE + (1 << 30), 4, 1 << 20)
+    st2, msg2 = ar(send=send, recv=recv, n=16, dt=2, algo=99)  # stop at the algo check after alignment
+    assert st2 == INVALID and "algo" in msg2
+
+
+def test_all_reduce_overlapping_outputs():
+    recv = rr._ptr_array([FAKE, FAKE + 64, FAKE + (1 << 20), FAKE + (2 << 20)])
+    send = ptrs(FAKE + (1 << 30), 4, 1 << 20)
+    st, msg = ar(send=send, recv=recv, n=64)
+    assert st == INVALID and "overlap" in msg
+
+
+def test_all_reduce_output_overlaps_other_input():
+    send = ptrs(FAKE, 4, 1 << 20)
+    recv = rr._ptr_array([FAKE + (1 << 20), FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30)])
+    st, msg = ar(send=send, recv=recv, n=64)
+    assert st == INVALID and "overlaps input" in msg
+
+
+def test_all_reduce_partial_in_place_is_rejected():
+    send = ptrs(FAKE, 4, 1 << 20)
+    recv = rr._ptr_array([FAKE + 16, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30)])
+    st, _ = ar(send=send, recv=recv, n=64)
+    assert st == INVALID
+
+
+def test_n_zero_is_a_no_op():
+    # fully valid arguments apart from n = 0: nothing is launched
+    assert ar(n=0)[0] == 0
+    L = rr.lib()
+    assert L.rr_reduce_scatter(ptrs(FAKE, 4, 1 << 20), ptrs(FAKE, 4, 1 << 20), 4, 0, 1, 0, None) == 0
+    assert L.rr_all_gather(ptrs(FAKE, 4, 1 << 20), ptrs(FAKE, 4, 1 << 20), 4, 0, 1, None) == 0
+    assert L.rr_reduce(ptrs(FAKE, 4, 1 << 20), FAKE, 0, 4, 0, 1, 0, None) == 0
+    assert L.rr_broadcast(FAKE, ptrs(FAKE, 4, 1 << 20), 0, 4, 0, 1, None) == 0
+
+
+def test_n_too_large():
+    st, msg = ar(n=(1 << 56) + 1)
+    assert st == INVALID and "2^56" in msg
+
+
+@pytest.mark.parametrize("algo,group", [(2, 0), (2, 3), (2, 5), (3, 9), (3, -1)])
+def test_hier_bad_group(algo, group):
+    st, msg = ar(p=8, algo=algo, group=group)
+    assert st == INVALID and "group_size" in msg
+
+
+def test_unknown_algo():
+    assert ar(algo=4)[0] == INVALID
+
+
+def test_staged_workspace_required():
+    st, msg = ar(p=8, n=1024, dt=2, algo=1)
+    assert st == INVALID and "workspace" in msg
+    need = rr.lib().rr_workspace_size(1, 8, 0, 1024, 2)
+    assert need == 8 * 1024 * 4
+    st, msg = ar(p=8, n=1024, dt=2, algo=1, ws=FAKE + (4 << 30), wsb=need - 1)
+    assert st == INVALID and "smaller" in msg
+    st, msg = ar(p=8, n=1024, dt=2, algo=1, ws=FAKE + (4 << 30) + 8, wsb=need)
+    assert st == INVALID and "aligned" in msg
+    # workspace overlapping an output
+    st, msg = ar(p=8, n=1024, dt=2, algo=1, ws=FAKE + (1 << 30), wsb=need)
+    assert st == INVALID and "workspace overlaps" in msg
+
+
+def test_workspace_sizes():
+    L = rr.lib()
+    assert L.rr_workspace_size(0, 8, 0, 1000, 1) == 0
+    assert L.rr_workspace_size(2, 8, 4, 1000, 2) == 0
+    assert L.rr_workspace_size(1, 8, 0, 1000, 1) == 0
+    assert L.rr_workspace_size(1, 8, 0, 1000, 0) == 0
+    assert L.rr_workspace_size(1, 8, 0, 1000, 2) == 8 * 1000 * 4
+    assert L.rr_workspace_size(3, 8, 4, 1000, 2) == 2 * 1000 * 4
+    assert L.rr_workspace_size(3, 8, 2, 1000, 0) == 4 * 1000 * 4
+    assert L.rr_workspace_size(3, 8, 3, 1000, 0) == 0  # invalid group
+
+
+def test_reduce_scatter_validation():
+    L = rr.lib()
+    send = ptrs(FAKE, 4, 1 << 20)
+    recv = ptrs(FAKE + (1 << 30), 4, 1 << 20)
+    assert L.rr_reduce_scatter(send, recv, 4, 1001, 1, 0, None) == INVALID  # p does not divide n
+    assert b"p | n" in L.rr_last_error()
+    assert L.rr_reduce_scatter(send, recv, 4, 1024, 5, 0, None) == UNSUPPORTED
+    assert L.rr_reduce_scatter(send, recv, 4, 1024, 1, 5, None) == UNSUPPORTED
+    # output overlapping another rank's input
+    bad = rr._ptr_array([FAKE + (1 << 20), FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30)])
+    assert L.rr_reduce_scatter(send, bad, 4, 1024, 1, 0, None) == INVALID
+    # in place at the wrong slot (slot of chunk 0 for rank 1)
+    bad2 = rr._ptr_array([FAKE + (5 << 30), FAKE + (1 << 20), FAKE + (2 << 30), FAKE + (3 << 30)])
+    assert L.rr_reduce_scatter(send, bad2, 4, 1024, 1, 0, None) == INVALID
+
+
+def test_all_gather_validation():
+    L = rr.lib()
+    send = ptrs(FAKE, 4, 1 << 20)
+    recv = ptrs(FAKE + (1 << 30), 4, 1 << 20)
+    assert L.rr_all_gather(send, recv, 4, 1001, 1, None) == INVALID
+    assert L.rr_all_gather(send, recv, 4, 1024, 3, None) == UNSUPPORTED
+    # a shard inside another rank's output
+    bad = rr._ptr_array([FAKE + (1 << 30) + (1 << 20), FAKE + (6 << 30), FAKE + (7 << 30), FAKE + (8 << 30)])
+    assert L.rr_all_gather(bad, recv, 4, 1024, 1, None) == INVALID
+
+
+def test_reduce_validation():
+    L = rr.lib()
+    send = ptrs(FAKE, 4, 1 << 20)
+    for root in (-1, 4):
+        assert L.rr_reduce(send, FAKE + (1 << 30), root, 4, 64, 1, 0, None) == INVALID
+    assert L.rr_reduce(send, 0, 0, 4, 64, 1, 0, None) == INVALID
+    # output on a non-root input
+    assert L.rr_reduce(send, FAKE + (1 << 20), 0, 4, 64, 1, 0, None) == INVALID
+    assert L.rr_reduce(send, FAKE + (1 << 30), 0, 4, 64, 1, 3, None) == UNSUPPORTED
+
+
+def test_broadcast_validation():
+    L = rr.lib()
+    recv = ptrs(FAKE + (1 << 30), 4, 1 << 20)
+    for root in (-1, 4):
+        assert L.rr_broadcast(FAKE, recv, root, 4, 64, 1, None) == INVALID
+    assert L.rr_broadcast(0, recv, 0, 4, 64, 1, None) == INVALID
+    # in place at a non-root rank
+    bad = rr._ptr_array([FAKE + (1 << 30), FAKE, FAKE + (2 << 30), FAKE + (3 << 30)])
+    assert L.rr_broadcast(FAKE, bad, 0, 4, 64, 1, None) == INVALID
+    assert L.rr_broadcast(FAKE, recv, 0, 4, 64, 9, None) == UNSUPPORTED
+
+
+def test_last_error_is_per_call():
+    st, msg = ar(p=0)
+    assert st == INVALID and msg
+    assert ar(n=0)[0] == 0
+    assert rr.lib().rr_last_error() == b""

@@ -1,0 +1,442 @@
+"""GPU parity of librr.so against the CPU oracle (calls go through the C ABI).
+
+Tolerances: int32 results are compared bit for bit.  float32 sums in ring
+order must be bit-exact (the oracle folds in the same order).  bf16 outputs
+accumulated in float32 may differ by at most 1 bf16 ulp by specification;
+because both sides fold in the same order and round once the same way, the
+tests below additionally demand bit equality and report the ulp distance when
+it fails.  Every comparison at full size either covers all elements or a
+sample (chunk edges plus random positions) that the oracle folds one by one.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle_pins as PIN
+import workloads as W
+from gpu_util import assert_bitwise, chunk_of, sample_positions, to_dev, to_host
+from oracle import bf16 as B
+from oracle import collectives as C
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+DTYPES = ("int32", "float32", "bfloat16")
+
+
+@pytest.fixture(scope="module")
+def rr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import collective_communication_reduction_way_amd as mod
+
+    mod.lib()
+    return mod
+
+
+def check_equal(got, want, dtype, what):
+    if dtype == "bfloat16":
+        ulp = B.ulp_distance(got, want)
+        assert ulp.max(initial=0) <= 1, f"{what}: {int(ulp.max())} bf16 ulps"
+    assert_bitwise(got, want, what)
+
+
+def rows(t, dtype):
+    return to_host(t, dtype)
+
+
+# ---------------------------------------------------------------------------
+# The pages' worked example and the hand-derived probes.
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_worked_example(rr, dtype):
+    g = json.load(open(os.path.join(GOLDEN, "worked_example.json"), encoding="utf-8"))
+    x = PIN.enc(g["inputs"], dtype)
+    want = PIN.enc([g["all_reduce"]] * 4, dtype)
+    for algo, G in (("ring", 0), ("ring_staged", 0), ("hier", 2), ("hier_staged", 2), ("hier", 4), ("hier", 1)):
+        xs = to_dev(x, dtype)
+        out = torch.empty_like(xs)
+        rr.all_reduce(xs, out, algo=algo, group_size=G)
+        assert_bitwise(rows(out, dtype), want, f"all_reduce {algo} G={G}")
+    xs = to_dev(x, dtype)
+    shards = torch.empty((4, 1), dtype=xs.dtype, device="cuda")
+    rr.reduce_scatter(xs, shards)
+    assert_bitwise(rows(shards, dtype), PIN.enc(g["reduce_scatter"], dtype), "reduce_scatter")
+    full = torch.empty((4, 4), dtype=xs.dtype, device="cuda")
+    rr.all_gather(shards, full)
+    assert_bitwise(rows(full, dtype), PIN.enc([g["all_gather_of_reduce_scatter"]] * 4, dtype), "all_gather")
+    for root in range(4):
+        red = torch.empty(4, dtype=xs.dtype, device="cuda")
+        rr.reduce(xs, red, root=root)
+        assert_bitwise(rows(red, dtype), PIN.enc(g["all_reduce"], dtype), "reduce")
+        bc = torch.empty((4, 4), dtype=xs.dtype, device="cuda")
+        rr.broadcast(red, bc, root=root)
+        assert_bitwise(rows(bc, dtype), want, "broadcast")
+    # in place, as torch.distributed's all_reduce works
+    xs = to_dev(x, dtype)
+    rr.all_reduce(xs)
+    assert_bitwise(rows(xs, dtype), want, "all_reduce in place")
+
+
+@pytest.mark.parametrize("dtype", ("float32", "bfloat16"))
+def test_ring_order_probe(rr, dtype):
+    x = PIN.enc(PIN.ring_order_probe_inputs(), dtype)
+    zeros = PIN.enc(np.zeros((4, 4)), dtype)
+    for algo in ("ring", "ring_staged"):
+        xs = to_dev(x, dtype)
+        out = torch.empty_like(xs)
+        rr.all_reduce(xs, out, algo=algo)
+        assert_bitwise(rows(out, dtype), zeros, algo)
+    xs = to_dev(x, dtype)
+    sh = torch.empty((4, 1), dtype=xs.dtype, device="cuda")
+    rr.reduce_scatter(xs, sh)
+    assert_bitwise(rows(sh, dtype).ravel(), zeros[0], "reduce_scatter")
+
+
+@pytest.mark.parametrize("dtype", ("float32", "bfloat16"))
+def test_reduce_order_probe(rr, dtype):
+    xs = to_dev(PIN.enc(np.array([[PIN.TWO24], [1.0], [1.0], [-PIN.TWO24]]), dtype), dtype)
+    out = torch.empty(1, dtype=xs.dtype, device="cuda")
+    rr.reduce(xs, out)
+    assert PIN.dec(rows(out, dtype), dtype).tolist() == [0.0]
+
+
+@pytest.mark.parametrize("dtype", ("float32", "bfloat16"))
+@pytest.mark.parametrize("algo", ("hier", "hier_staged"))
+def test_hierarchical_probes(rr, dtype, algo):
+    for inputs, G, want in ((PIN.hier_probe_inputs(), 4, 1.0), (PIN.hier_probe_groups_of_2_inputs(), 2, 0.0)):
+        xs = to_dev(PIN.enc(inputs, dtype), dtype)
+        out = torch.empty_like(xs)
+        rr.all_reduce(xs, out, algo=algo, group_size=G)
+        assert np.all(PIN.dec(rows(out, dtype), dtype) == want), (G, rows(out, dtype))
+
+
+def test_int32_wrap(rr):
+    x = np.array([[2 ** 31 - 1, -(2 ** 31), 5, 0], [1, -1, -7, 0]], dtype=np.int32)
+    want = C.all_reduce_ring(x, "sum", "int32")
+    for algo in ("ring", "ring_staged", "hier", "hier_staged"):
+        xs = to_dev(x, "int32")
+        out = torch.empty_like(xs)
+        rr.all_reduce(xs, out, algo=algo, group_size=2)
+        assert_bitwise(rows(out, "int32"), want, algo)
+
+
+@pytest.mark.parametrize("op", ("max", "min"))
+def test_signed_zero_and_nan_rules(rr, op):
+    """Compare-and-select keeps the running value on ties and NaNs: the oracle's
+    pinned rule, checked on every fold path."""
+    nan = np.float32("nan")
+    cols = [(-0.0, 0.0), (0.0, -0.0), (nan, 1.0), (1.0, nan), (nan, -nan), (-0.0, -0.0)]
+    for p in (2, 4):
+        x = np.zeros((p, 4 * len(cols)), dtype=np.float32)
+        for j, (a, b) in enumerate(cols):
+            for k in range(4):  # every rotation position
+                x[:, 4 * j + k] = b
+                x[k % p, 4 * j + k] = a
+        for algo in ("ring", "ring_staged"):
+            xs = to_dev(x, "float32")
+            out = torch.empty_like(xs)
+            rr.all_reduce(xs, out, op=op, algo=algo)
+            assert_bitwise(rows(out, "float32"), C.all_reduce_ring(x, op, "float32"), f"{algo} p={p}")
+        for G in (1, p):
+            xs = to_dev(x, "float32")
+            out = torch.empty_like(xs)
+            rr.all_reduce(xs, out, op=op, algo="hier", group_size=G)
+            assert_bitwise(rows(out, "float32"), C.all_reduce_hier(x, op, "float32", G), f"hier G={G}")
+        red = torch.empty(x.shape[1], dtype=torch.float32, device="cuda")
+        rr.reduce(to_dev(x, "float32"), red, op=op)
+        assert_bitwise(rows(red, "float32"), C.reduce(x, op, "float32"), "reduce")
+
+
+def test_bf16_specials(rr):
+    """bf16 sums of specials (inf, NaN with payloads, overflow to inf,
+    denormals) round exactly as the oracle's codec.  Which NaN an addition
+    returns (inf - inf, NaN + x) is the hardware's choice, not the method's, so
+    NaN results only have to be NaN on both sides; every other output must
+    match bit for bit."""
+    f = np.array([np.inf, -np.inf, 3.0e38, -3.0e38, 1e-39, -1e-39, 2.0 ** -133, 1.0], dtype=np.float32)
+    x = np.stack([B.narrow(f), B.narrow(f[::-1].copy()), B.narrow(f * np.float32(0.5)), B.narrow(-f)])
+    nanbits = np.array([0x7FC1, 0xFFA0, 0x7F81, 0x0001, 0x8001, 0x7F7F, 0xFF7F, 0x0000], dtype=np.uint16)
+    x = np.concatenate([x, np.stack([nanbits] * 4)], axis=1)
+    for algo in ("ring", "ring_staged", "hier", "hier_staged"):
+        xs = to_dev(x, "bfloat16")
+        out = torch.empty_like(xs)
+        with np.errstate(all="ignore"):
+            want = (C.all_reduce_hier(x, "sum", "bfloat16", 2) if algo.startswith("hier")
+                    else C.all_reduce_ring(x, "sum", "bfloat16"))
+        rr.all_reduce(xs, out, algo=algo, group_size=2)
+        got = rows(out, "bfloat16")
+        is_nan = lambda h: (h & 0x7FFF) > 0x7F80  # noqa: E731
+        assert np.array_equal(is_nan(got), is_nan(want)), algo
+        keep = ~is_nan(want)
+        assert_bitwise(got[keep], want[keep], algo)
+        assert np.all(got[is_nan(got)] & 0x0040), "NaN outputs must be quiet"
+
+
+def test_fp32_denormals_are_kept(rr):
+    tiny = np.float32(2.0 ** -149)
+    x = np.full((8, 64), tiny, dtype=np.float32)
+    xs = to_dev(x, "float32")
+    out = torch.empty_like(xs)
+    rr.all_reduce(xs, out)
+    assert np.all(rows(out, "float32") == np.float32(8 * 2.0 ** -149))
+
+
+# ---------------------------------------------------------------------------
+# Closed form at every workload's full shape: x_r[j] = (j mod 16) + r.
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_closed_form_full_size(rr, name):
+    spec = W.WORKLOADS[name]
+    p, n, dtype = spec["p"], spec["n"], spec["dtype"]
+    j = torch.arange(n, device="cuda", dtype=torch.int64) % 16
+    xs = torch.stack([(j + r) for r in range(p)]).to(torch.float32).to(
+        {"int32": torch.int32, "float32": torch.float32, "bfloat16": torch.bfloat16}[dtype])
+    jf = j.to(torch.float64)
+    for op, want in (("sum", p * jf + p * (p - 1) / 2), ("max", jf + p - 1), ("min", jf)):
+        algos = [("ring", 0), ("hier", spec.get("group", 4))]
+        for algo, G in algos:
+            out = torch.empty_like(xs)
+            rr.all_reduce(xs, out, op=op, algo=algo, group_size=G)
+            torch.cuda.synchronize()
+            for r in range(p):
+                assert torch.equal(out[r].to(torch.float64), want), (name, op, algo, r)
+        sh = torch.empty((p, n // p), dtype=xs.dtype, device="cuda")
+        rr.reduce_scatter(xs, sh, op=op)
+        assert torch.equal(sh.reshape(-1).to(torch.float64), want), (name, op, "rs")
+        full = torch.empty_like(xs)
+        rr.all_gather(sh, full)
+        for r in range(p):
+            assert torch.equal(full[r].to(torch.float64), want), (name, op, "ag")
+        red = torch.empty(n, dtype=xs.dtype, device="cuda")
+        rr.reduce(xs, red, op=op, root=p - 1)
+        assert torch.equal(red.to(torch.float64), want), (name, op, "reduce")
+        del out, sh, full, red
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# The five workloads against the oracle.
+
+def test_workload_ar_int32_p4(rr):
+    x = W.make_inputs("ar_int32_p4_n4096")
+    want = C.all_reduce_ring(x, "sum", "int32")
+    for algo in ("ring", "ring_staged"):
+        xs = to_dev(x, "int32")
+        out = torch.empty_like(xs)
+        rr.all_reduce(xs, out, algo=algo)
+        assert_bitwise(rows(out, "int32"), want, algo)
+    # the literal ring takes 2(p-1) = 6 steps for p = 4
+    assert len({(ph, s) for ph, s, *_ in rr.ring_schedule(4)}) == 6
+
+
+def test_workload_ar_fp32_p8_8MiB(rr):
+    x = W.make_inputs("ar_fp32_p8_8MiB")
+    want = C.all_reduce_fold(x, "sum", "float32")
+    for algo in ("ring", "ring_staged"):
+        xs = to_dev(x, "float32")
+        out = torch.empty_like(xs)
+        rr.all_reduce(xs, out, algo=algo)
+        assert_bitwise(rows(out, "float32"), want, algo)
+    # the literal ring simulation of the oracle agrees with its fold formula
+    assert_bitwise(C.all_reduce_ring(x[:, :65536], "sum", "float32"),
+                   C.all_reduce_fold(x[:, :65536], "sum", "float32"), "oracle ring vs fold")
+
+
+def test_workload_hier_bf16_p8g4(rr):
+    x = W.make_inputs("hier_bf16_p8g4_8MiB")
+    want = C.all_reduce_hier(x, "sum", "bfloat16", 4)
+    for algo in ("hier", "hier_staged"):
+        xs = to_dev(x, "bfloat16")
+        out = torch.empty_like(xs)
+        rr.all_reduce(xs, out, algo=algo, group_size=4)
+        check_equal(rows(out, "bfloat16"), want, "bfloat16", algo)
+
+
+@pytest.mark.parametrize("op", ("sum", "max", "min"))
+def test_workload_zero_bucket_fp32_p8(rr, op):
+    spec = W.WORKLOADS["zero_bucket_fp32_p8"]
+    p, n = spec["p"], spec["n"]
+    x = W.make_inputs("zero_bucket_fp32_p8")
+    xs = to_dev(x, "float32")
+    pos = sample_positions(n, p, 1 << 20, seed=41)
+    want = C.fold_elements_ring_order(x[:, pos], chunk_of(pos, n, p), op, "float32")
+    L = n // p
+    sh = torch.empty((p, L), dtype=torch.float32, device="cuda")
+    rr.reduce_scatter(xs, sh, op=op)
+    flat = rows(sh, "float32").reshape(-1)
+    assert_bitwise(flat[pos], want, "reduce_scatter (sampled)")
+    full = torch.empty_like(xs)
+    rr.all_gather(sh, full)
+    ar = torch.empty_like(xs)
+    rr.all_reduce(xs, ar, op=op)
+    torch.cuda.synchronize()
+    # all_reduce == all_gather(reduce_scatter), bitwise, on every element
+    assert torch.equal(full.view(torch.int32), ar.view(torch.int32))
+    for r in range(1, p):
+        assert torch.equal(ar[r].view(torch.int32), ar[0].view(torch.int32))
+    assert_bitwise(rows(ar[0], "float32")[pos], want, "all_reduce (sampled)")
+    # a full-size check of one chunk of every rank's shard against the oracle
+    c = 3
+    lo, hi = c * L, (c + 1) * L
+    want_c = C.fold_elements_ring_order(x[:, lo:hi], np.full(L, c), op, "float32")
+    assert_bitwise(rows(sh[c], "float32"), want_c, "reduce_scatter chunk 3 (full)")
+
+
+def test_workload_tp_rowparallel_bf16_p8(rr):
+    spec = W.WORKLOADS["tp_rowparallel_bf16_p8"]
+    p, n = spec["p"], spec["n"]
+    x = W.make_inputs("tp_rowparallel_bf16_p8")
+    xs = to_dev(x, "bfloat16")
+    out = torch.empty_like(xs)
+    rr.all_reduce(xs, out)
+    torch.cuda.synchronize()
+    for r in range(1, p):
+        assert torch.equal(out[r].view(torch.int16), out[0].view(torch.int16))
+    pos = sample_positions(n, p, 1 << 20, seed=51)
+    want = C.fold_elements_ring_order(x[:, pos], chunk_of(pos, n, p), "sum", "bfloat16")
+    check_equal(rows(out[0], "bfloat16")[pos], want, "bfloat16", "all_reduce (sampled)")
+    # one full chunk
+    c = 5
+    b = C.chunk_bounds(n, p)
+    want_c = C.fold_elements_ring_order(x[:, b[c]:b[c + 1]], np.full(b[c + 1] - b[c], c), "sum", "bfloat16")
+    check_equal(rows(out[0], "bfloat16")[b[c]:b[c + 1]], want_c, "bfloat16", "all_reduce chunk 5 (full)")
+
+
+# ---------------------------------------------------------------------------
+# Sweeps over p, n, dtype, op and algorithm at sizes the oracle handles in
+# full: several tiles, ragged chunk bounds and tails, generic p.
+
+SWEEP = [
+    (2, 1000), (3, 4099), (4, 65536 + 12), (5, 77777), (8, 131072), (8, 262147), (16, 40000), (7, 1),
+    (6, 5), (64, 6400), (1, 1000),
+]
+
+
+@pytest.mark.parametrize("p,n", SWEEP)
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_sweep_all_reduce(rr, p, n, dtype):
+    x = W.random_inputs(11, p, n, dtype, kind="full" if dtype == "int32" else "normal")
+    for op in ("sum", "max", "min"):
+        want = C.all_reduce_fold(x, op, dtype)
+        for algo in ("ring", "ring_staged"):
+            xs = to_dev(x, dtype)
+            out = torch.empty_like(xs)
+            rr.all_reduce(xs, out, op=op, algo=algo)
+            check_equal(rows(out, dtype), want, dtype, f"{algo} {op}")
+        groups = [g for g in (1, 2, 4, p) if p % g == 0]
+        for G in groups:
+            want_h = C.all_reduce_hier(x, op, dtype, G)
+            for algo in ("hier", "hier_staged"):
+                xs = to_dev(x, dtype)
+                out = torch.empty_like(xs)
+                rr.all_reduce(xs, out, op=op, algo=algo, group_size=G)
+                check_equal(rows(out, dtype), want_h, dtype, f"{algo} G={G} {op}")
+        red = torch.empty(n, dtype=to_dev(x[:1], dtype).dtype, device="cuda")
+        rr.reduce(to_dev(x, dtype), red, op=op, root=p // 2)
+        check_equal(rows(red, dtype), C.reduce(x, op, dtype), dtype, f"reduce {op}")
+
+
+@pytest.mark.parametrize("p,L", [(2, 1), (3, 5), (4, 4096), (8, 16411), (16, 999), (64, 64)])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_sweep_reduce_scatter_all_gather(rr, p, L, dtype):
+    n = p * L
+    x = W.random_inputs(12, p, n, dtype, kind="full" if dtype == "int32" else "normal")
+    for op in ("sum", "max", "min"):
+        want = C.reduce_scatter_ring(x, op, dtype)
+        xs = to_dev(x, dtype)
+        sh = torch.empty((p, L), dtype=xs.dtype, device="cuda")
+        rr.reduce_scatter(xs, sh, op=op)
+        check_equal(rows(sh, dtype), want, dtype, f"reduce_scatter {op}")
+        full = torch.empty_like(xs)
+        rr.all_gather(sh, full)
+        assert_bitwise(rows(full, dtype), C.all_gather(want), "all_gather")
+        ar = torch.empty_like(xs)
+        rr.all_reduce(xs, ar, op=op)
+        assert_bitwise(rows(ar, dtype), rows(full, dtype), "all_reduce == all_gather(reduce_scatter)")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_unaligned_buffers_take_the_scalar_path(rr, dtype):
+    """Rank buffers offset by one element (not 16-byte aligned) give the same
+    bits as the aligned vector path."""
+    p, n = 4, 10007
+    x = W.random_inputs(13, p, n, dtype)
+    base = to_dev(np.concatenate([x, x[:, :3]], axis=1), dtype)  # room for the offset
+    ins = [base[r, 1:1 + n] for r in range(p)]
+    outbuf = torch.empty((p, n + 1), dtype=base.dtype, device="cuda")
+    outs = [outbuf[r, 1:1 + n] for r in range(p)]
+    shifted = np.concatenate([x, x[:, :3]], axis=1)[:, 1:1 + n]
+    for op in ("sum", "max"):
+        rr.all_reduce(ins, outs, op=op)
+        got = np.stack([rows(o, dtype) for o in outs])
+        assert_bitwise(got, C.all_reduce_fold(np.ascontiguousarray(shifted), op, dtype), f"all_reduce {op}")
+    red = outbuf[0, 1:1 + n]
+    rr.reduce(ins, red, op="sum")
+    assert_bitwise(rows(red, dtype), C.reduce(np.ascontiguousarray(shifted), "sum", dtype), "reduce")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_in_place_forms(rr, dtype):
+    p, n = 8, 8 * 3001
+    L = n // p
+    x = W.random_inputs(14, p, n, dtype)
+    # all-reduce in place == out of place
+    for algo, G in (("ring", 0), ("ring_staged", 0), ("hier", 4), ("hier_staged", 2)):
+        xs = to_dev(x, dtype)
+        out = torch.empty_like(xs)
+        rr.all_reduce(xs, out, algo=algo, group_size=G)
+        rr.all_reduce(xs, algo=algo, group_size=G)
+        assert_bitwise(rows(xs, dtype), rows(out, dtype), f"in place {algo}")
+    # reduce-scatter into the rank's own chunk slot
+    xs = to_dev(x, dtype)
+    want = C.reduce_scatter_ring(x, "sum", dtype)
+    rr.reduce_scatter(xs, [xs[c, c * L:(c + 1) * L] for c in range(p)])
+    got = np.stack([rows(xs[c, c * L:(c + 1) * L], dtype) for c in range(p)])
+    assert_bitwise(got, want, "reduce_scatter in place")
+    # all-gather from the rank's own chunk slot
+    rr.all_gather([xs[c, c * L:(c + 1) * L] for c in range(p)], xs)
+    assert_bitwise(rows(xs, dtype), C.all_gather(want), "all_gather in place")
+    # reduce in place at the root; broadcast in place at the root
+    xs = to_dev(x, dtype)
+    rr.reduce(xs, xs[5], root=5)
+    assert_bitwise(rows(xs[5], dtype), C.reduce(x, "sum", dtype), "reduce in place")
+    rr.broadcast(xs[5], xs, root=5)
+    assert_bitwise(rows(xs, dtype), C.broadcast(C.reduce(x, "sum", dtype), p), "broadcast in place")
+
+
+def test_separate_allocations_and_streams(rr):
+    """Rank buffers from separate allocations, on a non-default stream."""
+    p, n = 8, 1 << 18
+    x = W.random_inputs(15, p, n, "float32")
+    ins = [to_dev(x[r], "float32") for r in range(p)]
+    outs = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(p)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        rr.all_reduce(ins, outs)
+    s.synchronize()
+    got = np.stack([rows(o, "float32") for o in outs])
+    assert_bitwise(got, C.all_reduce_fold(x, "sum", "float32"), "separate buffers")
+
+
+def test_zero_length_and_rejected_calls_write_nothing(rr):
+    xs = torch.ones((4, 0), dtype=torch.float32, device="cuda")
+    rr.all_reduce(xs, torch.empty_like(xs))
+    a = torch.ones((4, 64), dtype=torch.float32, device="cuda")
+    out = torch.full((4, 64), 7.0, device="cuda")
+    with pytest.raises(rr.RRError):
+        rr.all_reduce(a, out, algo="hier", group_size=3)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
+def test_single_hip_runtime_is_loaded(rr):
+    """librr binds to the HIP runtime torch loaded (one libamdhip64 in the process)."""
+    maps = open("/proc/self/maps").read()
+    libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(libs) == 1, libs
