@@ -38,9 +38,31 @@ struct UnitT<1> {
   using T = uint8_t;
 };
 
-constexpr int kCopyU = 4;
+// Units per lane per tile, and the default workgroup count of a copy: the
+// measured best for 16-byte streaming copies on MI355X is two units per lane
+// with about 8192 workgroups striding over the tiles.
+constexpr int kCopyU = 2;
+constexpr int kCopyGrid = 8192;
 
-template <int B>
+template <bool NT, class T>
+__device__ __forceinline__ T ld(const T* p) {
+  if constexpr (NT) {
+    return __builtin_nontemporal_load(p);
+  } else {
+    return *p;
+  }
+}
+
+template <bool NT, class T>
+__device__ __forceinline__ void st(T* p, T v) {
+  if constexpr (NT) {
+    __builtin_nontemporal_store(v, p);
+  } else {
+    *p = v;
+  }
+}
+
+template <int B, bool NT>
 __global__ __launch_bounds__(kBlock) void k_fanout(FanoutArgs a) {
   using T = typename UnitT<B>::T;
   const int seg = blockIdx.y;
@@ -54,7 +76,7 @@ __global__ __launch_bounds__(kBlock) void k_fanout(FanoutArgs a) {
 #pragma unroll
     for (int u = 0; u < kCopyU; ++u) {
       const uint64_t i = base + static_cast<uint64_t>(u) * kBlock;
-      if (i < units) v[u] = src[i];
+      if (i < units) v[u] = ld<NT>(src + i);
     }
     for (int r = 0; r < a.ndst; ++r) {
       if (r == seg && ((a.skip_diag >> seg) & 1ull)) continue;
@@ -62,13 +84,13 @@ __global__ __launch_bounds__(kBlock) void k_fanout(FanoutArgs a) {
 #pragma unroll
       for (int u = 0; u < kCopyU; ++u) {
         const uint64_t i = base + static_cast<uint64_t>(u) * kBlock;
-        if (i < units) dst[i] = v[u];
+        if (i < units) st<NT>(dst + i, v[u]);
       }
     }
   }
 }
 
-template <int B>
+template <int B, bool NT>
 __global__ __launch_bounds__(kBlock) void k_copy_pairs(PairArgs a) {
   using T = typename UnitT<B>::T;
   const int y = blockIdx.y;
@@ -82,12 +104,12 @@ __global__ __launch_bounds__(kBlock) void k_copy_pairs(PairArgs a) {
 #pragma unroll
     for (int u = 0; u < kCopyU; ++u) {
       const uint64_t i = base + static_cast<uint64_t>(u) * kBlock;
-      if (i < units) v[u] = src[i];
+      if (i < units) v[u] = ld<NT>(src + i);
     }
 #pragma unroll
     for (int u = 0; u < kCopyU; ++u) {
       const uint64_t i = base + static_cast<uint64_t>(u) * kBlock;
-      if (i < units) dst[i] = v[u];
+      if (i < units) st<NT>(dst + i, v[u]);
     }
   }
 }
@@ -169,29 +191,31 @@ hipError_t ring_step_kind(const PairArgs& a, rr_op_t op, int grid_cap, hipStream
 
 }  // namespace
 
-hipError_t launch_fanout(const FanoutArgs& a, int unit_bytes, int grid_cap, hipStream_t s) {
+hipError_t launch_fanout(const FanoutArgs& a, int unit_bytes, int nontemporal, int grid_cap, hipStream_t s) {
   const uint64_t units = a.seg_bytes / static_cast<uint64_t>(unit_bytes);
-  const uint64_t bx = blocks_for(units, static_cast<uint64_t>(kBlock) * kCopyU, a.nseg, grid_cap);
+  const uint64_t bx =
+      blocks_for(units, static_cast<uint64_t>(kBlock) * kCopyU, a.nseg, grid_cap > 0 ? grid_cap : kCopyGrid);
+  const bool nt = nontemporal != 0;
   switch (unit_bytes) {
-    case 16: return go(&k_fanout<16>, a, bx, a.nseg, s);
-    case 4: return go(&k_fanout<4>, a, bx, a.nseg, s);
-    case 2: return go(&k_fanout<2>, a, bx, a.nseg, s);
-    case 1: return go(&k_fanout<1>, a, bx, a.nseg, s);
+    case 16: return nt ? go(&k_fanout<16, true>, a, bx, a.nseg, s) : go(&k_fanout<16, false>, a, bx, a.nseg, s);
+    case 4: return nt ? go(&k_fanout<4, true>, a, bx, a.nseg, s) : go(&k_fanout<4, false>, a, bx, a.nseg, s);
+    case 2: return nt ? go(&k_fanout<2, true>, a, bx, a.nseg, s) : go(&k_fanout<2, false>, a, bx, a.nseg, s);
+    case 1: return nt ? go(&k_fanout<1, true>, a, bx, a.nseg, s) : go(&k_fanout<1, false>, a, bx, a.nseg, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_copy_pairs(const PairArgs& a, int unit_bytes, int grid_cap, hipStream_t s) {
+hipError_t launch_copy_pairs(const PairArgs& a, int unit_bytes, int nontemporal, int grid_cap, hipStream_t s) {
   uint64_t longest = 0;
   for (int y = 0; y < a.npairs; ++y) longest = a.len[y] > longest ? a.len[y] : longest;
-  const uint64_t bx =
-      blocks_for(longest / static_cast<uint64_t>(unit_bytes), static_cast<uint64_t>(kBlock) * kCopyU, a.npairs,
-                 grid_cap);
+  const uint64_t bx = blocks_for(longest / static_cast<uint64_t>(unit_bytes), static_cast<uint64_t>(kBlock) * kCopyU,
+                                 a.npairs, grid_cap > 0 ? grid_cap : kCopyGrid);
+  const bool nt = nontemporal != 0;
   switch (unit_bytes) {
-    case 16: return go(&k_copy_pairs<16>, a, bx, a.npairs, s);
-    case 4: return go(&k_copy_pairs<4>, a, bx, a.npairs, s);
-    case 2: return go(&k_copy_pairs<2>, a, bx, a.npairs, s);
-    case 1: return go(&k_copy_pairs<1>, a, bx, a.npairs, s);
+    case 16: return nt ? go(&k_copy_pairs<16, true>, a, bx, a.npairs, s) : go(&k_copy_pairs<16, false>, a, bx, a.npairs, s);
+    case 4: return nt ? go(&k_copy_pairs<4, true>, a, bx, a.npairs, s) : go(&k_copy_pairs<4, false>, a, bx, a.npairs, s);
+    case 2: return nt ? go(&k_copy_pairs<2, true>, a, bx, a.npairs, s) : go(&k_copy_pairs<2, false>, a, bx, a.npairs, s);
+    case 1: return nt ? go(&k_copy_pairs<1, true>, a, bx, a.npairs, s) : go(&k_copy_pairs<1, false>, a, bx, a.npairs, s);
   }
   return hipErrorInvalidValue;
 }

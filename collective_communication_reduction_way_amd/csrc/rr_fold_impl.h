@@ -96,25 +96,37 @@ __device__ __forceinline__ void fold_scalar(const FoldArgs& a, uint64_t i, uint6
   }
 }
 
+// Addressing of the vector path.  A tile is kBlock*U consecutive groups whose
+// first group is uniform across the workgroup: every rank's tile base is
+// computed once per tile, and lane t, slot u reaches the group at tile base +
+// (t + u*kBlock) groups through a 32-bit offset that stays the same from tile
+// to tile.  Consecutive lanes touch consecutive 16-byte words, so each
+// wavefront-wide access covers whole 64-byte segments.
+
 // Vector path, compile-time p: all p*U loads first, then the folds.
+// `valid` = groups of this tile inside the row (only used when GUARD).
 template <class TI, class TO, class OP, int P, int U, bool NT, FoldMode M, bool GUARD>
-__device__ __forceinline__ void fold_tile(const typename TI::S* const* src, typename TO::S* const* dst,
-                                          uint64_t g0, uint64_t g_end, uint64_t lo, int group) {
+__device__ __forceinline__ void fold_tile(const char* const* sb, char* const* db, uint32_t valid, int group) {
   constexpr int V = group_len<TI, TO>();
+  constexpr uint32_t GBI = V * sizeof(typename TI::S);
+  constexpr uint32_t GBO = V * sizeof(typename TO::S);
+  using SI = typename TI::S;
+  using SO = typename TO::S;
   using A = typename TI::A;
+  const uint32_t lane = threadIdx.x;
   Raw<TI, V> raw[U][P];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const uint64_t g = g0 + static_cast<uint64_t>(u) * kBlock;
-    if (!GUARD || g < g_end) {
+    const uint32_t off = (lane + u * kBlock) * GBI;
+    if (!GUARD || lane + u * kBlock < valid) {
 #pragma unroll
-      for (int k = 0; k < P; ++k) load_group<NT>(raw[u][k], src[k] + g * V);
+      for (int k = 0; k < P; ++k) load_group<NT>(raw[u][k], reinterpret_cast<const SI*>(sb[k] + off));
     }
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const uint64_t g = g0 + static_cast<uint64_t>(u) * kBlock;
-    if (GUARD && g >= g_end) continue;
+    if (GUARD && lane + u * kBlock >= valid) continue;
+    const uint32_t off = (lane + u * kBlock) * GBO;
     A acc[V];
     A tot[V];
     unpack(raw[u][0], acc);
@@ -131,35 +143,34 @@ __device__ __forceinline__ void fold_tile(const typename TI::S* const* src, type
     for (int j = 0; j < V; ++j) acc[j] = fold_finish<OP, M>(acc[j], tot[j], P, group);
     Raw<TO, V> o;
     pack(acc, o);
-    if constexpr (writes_all(M)) {
+    constexpr int ND = writes_all(M) ? P : 1;
 #pragma unroll
-      for (int r = 0; r < P; ++r) store_group<NT>(dst[r] + g * V, o);
-    } else if constexpr (M == FoldMode::kRingShard) {
-      store_group<NT>(dst[0] + (g * V - lo), o);
-    } else {
-      store_group<NT>(dst[0] + g * V, o);
-    }
+    for (int r = 0; r < ND; ++r) store_group<NT>(reinterpret_cast<SO*>(db[r] + off), o);
   }
 }
 
 // Vector path, run-time p: inputs are streamed one rank at a time, U groups
-// per lane in flight.
+// per lane in flight.  `in_base(k)` / `out_base(r)` give the tile's byte base
+// of the k-th input in fold order / of output r.
 template <class TI, class TO, class OP, int U, bool NT, FoldMode M, bool GUARD>
-__device__ __forceinline__ void fold_tile_dyn(const FoldArgs& a, int seg, int p, uint64_t g0, uint64_t g_end,
-                                              uint64_t lo) {
+__device__ __forceinline__ void fold_tile_dyn(const FoldArgs& a, int seg, int p, uint64_t in_tile_off,
+                                              int64_t out_tile_off, uint32_t valid) {
   constexpr int V = group_len<TI, TO>();
+  constexpr uint32_t GBI = V * sizeof(typename TI::S);
+  constexpr uint32_t GBO = V * sizeof(typename TO::S);
   using SI = typename TI::S;
   using SO = typename TO::S;
   using A = typename TI::A;
+  const uint32_t lane = threadIdx.x;
   A acc[U][V];
   A tot[U][V];
   {
-    const SI* s0 = static_cast<const SI*>(a.in[fold_src<M>(0, seg, p)]);
+    const char* s0 = static_cast<const char*>(a.in[fold_src<M>(0, seg, p)]) + in_tile_off;
     Raw<TI, V> raw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint64_t g = g0 + static_cast<uint64_t>(u) * kBlock;
-      if (!GUARD || g < g_end) load_group<NT>(raw[u], s0 + g * V);
+      if (!GUARD || lane + u * kBlock < valid)
+        load_group<NT>(raw[u], reinterpret_cast<const SI*>(s0 + (lane + u * kBlock) * GBI));
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -169,12 +180,12 @@ __device__ __forceinline__ void fold_tile_dyn(const FoldArgs& a, int seg, int p,
     }
   }
   for (int k = 1; k < p; ++k) {
-    const SI* sk = static_cast<const SI*>(a.in[fold_src<M>(k, seg, p)]);
+    const char* sk = static_cast<const char*>(a.in[fold_src<M>(k, seg, p)]) + in_tile_off;
     Raw<TI, V> raw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint64_t g = g0 + static_cast<uint64_t>(u) * kBlock;
-      if (!GUARD || g < g_end) load_group<NT>(raw[u], sk + g * V);
+      if (!GUARD || lane + u * kBlock < valid)
+        load_group<NT>(raw[u], reinterpret_cast<const SI*>(sk + (lane + u * kBlock) * GBI));
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -186,18 +197,17 @@ __device__ __forceinline__ void fold_tile_dyn(const FoldArgs& a, int seg, int p,
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const uint64_t g = g0 + static_cast<uint64_t>(u) * kBlock;
-    if (GUARD && g >= g_end) continue;
+    if (GUARD && lane + u * kBlock >= valid) continue;
+    const uint32_t off = (lane + u * kBlock) * GBO;
 #pragma unroll
     for (int j = 0; j < V; ++j) acc[u][j] = fold_finish<OP, M>(acc[u][j], tot[u][j], p, a.group);
     Raw<TO, V> o;
     pack(acc[u], o);
     if constexpr (writes_all(M)) {
-      for (int r = 0; r < p; ++r) store_group<NT>(static_cast<SO*>(a.out[r]) + g * V, o);
-    } else if constexpr (M == FoldMode::kRingShard) {
-      store_group<NT>(static_cast<SO*>(a.out[seg]) + (g * V - lo), o);
+      for (int r = 0; r < p; ++r)
+        store_group<NT>(reinterpret_cast<SO*>(static_cast<char*>(a.out[r]) + out_tile_off + off), o);
     } else {
-      store_group<NT>(static_cast<SO*>(a.out[seg]) + g * V, o);
+      store_group<NT>(reinterpret_cast<SO*>(static_cast<char*>(a.out[seg]) + out_tile_off + off), o);
     }
   }
 }
@@ -227,35 +237,50 @@ __global__ __launch_bounds__(kBlock) void k_fold(FoldArgs a) {
   const uint64_t ngroups = g_hi - g_lo;
   constexpr uint64_t kTile = static_cast<uint64_t>(kBlock) * U;
   const uint64_t ntiles = (ngroups + kTile - 1) / kTile;
+  constexpr uint64_t GBI = V * sizeof(SI);
+  constexpr uint64_t GBO = V * sizeof(SO);
+  // Byte offset of group g in an output: outputs of kRingShard hold only the
+  // row's chunk, so their group g sits (g*V - lo) elements in.
+  const int64_t out_shift = (M == FoldMode::kRingShard) ? -static_cast<int64_t>(lo * sizeof(SO)) : 0;
   if constexpr (P > 0) {
     // Rotated input pointers and output pointers, uniform across the
     // workgroup (scalar registers).
-    const SI* src[P];
+    const char* src[P];
 #pragma unroll
-    for (int k = 0; k < P; ++k) src[k] = static_cast<const SI*>(a.in[fold_src<M>(k, seg, P)]);
+    for (int k = 0; k < P; ++k) src[k] = static_cast<const char*>(a.in[fold_src<M>(k, seg, P)]);
     constexpr int ND = writes_all(M) ? P : 1;
-    SO* dst[ND];
+    char* dst[ND];
     if constexpr (writes_all(M)) {
 #pragma unroll
-      for (int r = 0; r < P; ++r) dst[r] = static_cast<SO*>(a.out[r]);
+      for (int r = 0; r < P; ++r) dst[r] = static_cast<char*>(a.out[r]);
     } else {
-      dst[0] = static_cast<SO*>(a.out[seg]);
+      dst[0] = static_cast<char*>(a.out[seg]);
     }
     for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-      const uint64_t g0 = g_lo + t * kTile + threadIdx.x;
-      if ((t + 1) * kTile <= ngroups) {
-        fold_tile<TI, TO, OP, P, U, NT, M, false>(src, dst, g0, g_hi, lo, a.group);
+      const uint64_t g_first = g_lo + t * kTile;
+      const char* sb[P];
+#pragma unroll
+      for (int k = 0; k < P; ++k) sb[k] = src[k] + g_first * GBI;
+      char* db[ND];
+#pragma unroll
+      for (int r = 0; r < ND; ++r) db[r] = dst[r] + static_cast<int64_t>(g_first * GBO) + out_shift;
+      const uint64_t rem = ngroups - t * kTile;
+      if (rem >= kTile) {
+        fold_tile<TI, TO, OP, P, U, NT, M, false>(sb, db, 0, a.group);
       } else {
-        fold_tile<TI, TO, OP, P, U, NT, M, true>(src, dst, g0, g_hi, lo, a.group);
+        fold_tile<TI, TO, OP, P, U, NT, M, true>(sb, db, static_cast<uint32_t>(rem), a.group);
       }
     }
   } else {
     for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-      const uint64_t g0 = g_lo + t * kTile + threadIdx.x;
-      if ((t + 1) * kTile <= ngroups) {
-        fold_tile_dyn<TI, TO, OP, U, NT, M, false>(a, seg, p, g0, g_hi, lo);
+      const uint64_t g_first = g_lo + t * kTile;
+      const uint64_t in_off = g_first * GBI;
+      const int64_t out_off = static_cast<int64_t>(g_first * GBO) + out_shift;
+      const uint64_t rem = ngroups - t * kTile;
+      if (rem >= kTile) {
+        fold_tile_dyn<TI, TO, OP, U, NT, M, false>(a, seg, p, in_off, out_off, 0);
       } else {
-        fold_tile_dyn<TI, TO, OP, U, NT, M, true>(a, seg, p, g0, g_hi, lo);
+        fold_tile_dyn<TI, TO, OP, U, NT, M, true>(a, seg, p, in_off, out_off, static_cast<uint32_t>(rem));
       }
     }
   }

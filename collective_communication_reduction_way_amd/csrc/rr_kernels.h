@@ -84,9 +84,11 @@ hipError_t launch_fold_ring_all(const FoldLaunch& f, hipStream_t stream);
 hipError_t launch_fold_ring_shard(const FoldLaunch& f, hipStream_t stream);
 hipError_t launch_fold_asc_one(const FoldLaunch& f, hipStream_t stream);
 hipError_t launch_fold_hier_all(const FoldLaunch& f, hipStream_t stream);
-hipError_t launch_fanout(const FanoutArgs& a, int unit_bytes, int grid_cap, hipStream_t stream);
-// Plain copy: len[] in bytes, unit_bytes in {16, 4, 2, 1}.
-hipError_t launch_copy_pairs(const PairArgs& a, int unit_bytes, int grid_cap, hipStream_t stream);
+// Copies move units of unit_bytes in {16, 4, 2, 1}; nontemporal != 0 uses
+// nontemporal loads and stores; grid_cap 0 = the default workgroup count.
+hipError_t launch_fanout(const FanoutArgs& a, int unit_bytes, int nontemporal, int grid_cap, hipStream_t stream);
+// Plain copy: len[] in bytes.
+hipError_t launch_copy_pairs(const PairArgs& a, int unit_bytes, int nontemporal, int grid_cap, hipStream_t stream);
 // Element conversion: len[] in elements.
 hipError_t launch_convert_pairs(const PairArgs& a, Kind from, Kind to, int grid_cap, hipStream_t stream);
 // Ring reduce-scatter step on accumulator-type buffers: dst = src (+) dst.
