@@ -38,6 +38,7 @@ __all__ = [
     "library_path",
     "lib",
     "version",
+    "barrier_timeouts",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -97,6 +98,7 @@ def lib():
         "rr_hier_traffic": (I, [I, I, ctypes.c_uint64, U64P, U64P, U64P]),
         "rr_status_string": (ctypes.c_char_p, [I]),
         "rr_last_error": (ctypes.c_char_p, []),
+        "rr_barrier_timeouts": (I, [I, U64P]),
         "rr_version": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -105,6 +107,19 @@ def lib():
         fn.argtypes = args
     _lib = L
     return L
+
+
+def barrier_timeouts(device=None):
+    """How often a fused fold's soft phase barrier on `device` (default: the
+    current device) ended by timeout since the library was loaded.  The
+    barrier only shapes HBM traffic, so this counts lost throughput, never
+    wrong results.  Synchronizes the device."""
+    import torch
+
+    dev = torch.cuda.current_device() if device is None else int(device)
+    out = ctypes.c_uint64(0)
+    _check(lib().rr_barrier_timeouts(dev, ctypes.byref(out)), "rr_barrier_timeouts")
+    return int(out.value)
 
 
 def version():

@@ -30,6 +30,9 @@ SOURCES = [
     "rr_fold_hier_all.hip",
     "rr_fold_asc_one.hip",
     "rr_copy.hip",
+    "rr_phase_ring.hip",
+    "rr_phase_hier.hip",
+    "rr_phase.cpp",
     "rr_api.cpp",
     "rr_plan.cpp",
 ]

@@ -55,17 +55,28 @@ int env_int(const char* name, int dflt) {
 }
 
 // Tuning knobs (all optional): RR_UNROLL (1, 2 or 4 groups per lane on the
-// tunable fold kernels), RR_NT (0 = ordinary instead of nontemporal loads and
-// stores there and in the copy kernels), RR_GRID_CAP (maximum workgroups per
-// launch; 0 = one tile per workgroup), RR_LOG (1 = print each launch plan to
-// stderr).  Defaults are the measured best on MI355X: every byte of these
-// collectives is touched once, so nontemporal access (no reuse expected)
-// keeps the caches from holding dead lines.
+// tunable single-pass fold kernels), RR_NT (0 = ordinary instead of
+// nontemporal loads and stores there and in the copy kernels), RR_GRID_CAP
+// (maximum workgroups per single-pass launch; 0 = one tile per workgroup),
+// RR_PHASE (0 = single-pass fold kernel instead of the phased one on aligned
+// buffers), RR_PHASE_SYNC (0 = no barrier between the read and write phases),
+// RR_PHASE_PER_CU (workgroups per compute unit of the phased fold; 0 = by the
+// schedule), RR_PHASE_GRID (explicit workgroup count), RR_PHASE_U (4 = the
+// smaller tile for sums), RR_PHASE_STATIC (1 / 0 = the kernels compiled for
+// p = 8 / the run-time rank loop; -1 = by mode),
+// RR_PHASE_TIMEOUT_US (bound of one barrier wait, default 200),
+// RR_LOG (1 = print each launch plan to stderr).  Defaults are the measured
+// best on MI355X: every byte of these collectives is touched once, so
+// nontemporal access (no reuse expected) keeps the caches from holding dead
+// lines, and separating the read and write traffic of the fused folds in time
+// raises their HBM throughput.
 struct Tuning {
   int unroll;
   int nontemporal;
   int grid_cap;
   int log;
+  int phase;
+  rr::PhaseTuning pt;
 };
 
 Tuning tuning() {
@@ -76,6 +87,17 @@ Tuning tuning() {
   t.grid_cap = env_int("RR_GRID_CAP", 0);
   if (t.grid_cap < 0) t.grid_cap = 0;
   t.log = env_int("RR_LOG", 0);
+  t.phase = env_int("RR_PHASE", 1) ? 1 : 0;
+  t.pt.sync = env_int("RR_PHASE_SYNC", 1) ? 1 : 0;
+  t.pt.per_cu = env_int("RR_PHASE_PER_CU", 0);
+  if (t.pt.per_cu < 0 || t.pt.per_cu > 8) t.pt.per_cu = 0;
+  t.pt.grid = env_int("RR_PHASE_GRID", 0);
+  if (t.pt.grid < 0) t.pt.grid = 0;
+  t.pt.unroll = env_int("RR_PHASE_U", 0) == 4 ? 4 : 0;
+  t.pt.timeout_us = env_int("RR_PHASE_TIMEOUT_US", 200);
+  t.pt.static_p = env_int("RR_PHASE_STATIC", -1);
+  if (t.pt.static_p > 1) t.pt.static_p = 1;
+  if (t.pt.timeout_us < 1) t.pt.timeout_us = 200;
   return t;
 }
 
@@ -184,7 +206,9 @@ void log_fold(const Tuning& t, const char* what, const rr::FoldLaunch& f) {
 
 rr_status_t run_fold(const Tuning& t, const char* what, const rr::FoldLaunch& f, hipStream_t s) {
   log_fold(t, what, f);
-  const hipError_t e = rr::launch_fold(f, s);
+  const bool phased = t.phase && rr::phase_supported(f);
+  if (t.log && phased) fprintf(stderr, "[rr] %s: phased fold\n", what);
+  const hipError_t e = phased ? rr::launch_fold_phase(f, t.pt, s) : rr::launch_fold(f, s);
   if (e != hipSuccess) return hip_fail(e, what);
   return RR_SUCCESS;
 }
@@ -665,6 +689,19 @@ const char* rr_status_string(rr_status_t status) {
     case RR_ERROR_HIP: return "HIP runtime error";
   }
   return "unknown status";
+}
+
+rr_status_t rr_barrier_timeouts(int device, uint64_t* count) {
+  if (!count) return fail(RR_ERROR_INVALID_ARGUMENT, "count is NULL");
+  int ndev = 0;
+  hipError_t e = hipGetDeviceCount(&ndev);
+  if (e != hipSuccess) return hip_fail(e, "barrier_timeouts");
+  if (device < 0 || device >= ndev) return fail(RR_ERROR_INVALID_ARGUMENT, "device %d outside [0, %d)", device, ndev);
+  unsigned long long c = 0;
+  e = rr::phase_barrier_timeouts(device, &c);
+  if (e != hipSuccess) return hip_fail(e, "barrier_timeouts");
+  *count = c;
+  return ok();
 }
 
 const char* rr_last_error(void) { return g_last_error.c_str(); }

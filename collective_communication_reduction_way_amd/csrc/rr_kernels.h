@@ -79,7 +79,26 @@ struct PairArgs {
   int32_t vec;
 };
 
+// Schedule of the phased fold (rr_phase.cpp): per_cu workgroups per compute
+// unit (0 = chosen by the schedule) or an explicit grid; unroll 0 = chosen by
+// the schedule, 4 = the smaller tile (sums only); sync = 1 puts
+// a soft barrier between the read and the write phase of every round;
+// timeout_us bounds each barrier wait.
+struct PhaseTuning {
+  int sync;
+  int per_cu;
+  int grid;
+  int unroll;
+  int timeout_us;
+  int static_p;  // 1 = the kernels compiled for p = 8 serve p = 8, 0 = the run-time loop, -1 = by mode
+};
+
 hipError_t launch_fold(const FoldLaunch& f, hipStream_t stream);
+// The phased fold serves same-kind folds on 16-byte-aligned buffers.
+bool phase_supported(const FoldLaunch& f);
+hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStream_t stream);
+// Number of phase barriers on `device` that ended by timeout since load.
+hipError_t phase_barrier_timeouts(int device, unsigned long long* count);
 hipError_t launch_fold_ring_all(const FoldLaunch& f, hipStream_t stream);
 hipError_t launch_fold_ring_shard(const FoldLaunch& f, hipStream_t stream);
 hipError_t launch_fold_asc_one(const FoldLaunch& f, hipStream_t stream);

@@ -1,0 +1,208 @@
+// rr_phase.cpp -- host side of the phased streaming fold: tiling of the
+// segments into tiles, heads and tails, grid and round count, and the state
+// of the soft barrier (a counter set per stream and a fresh launch tag per
+// launch).  The kernels and the design are in rr_phase_impl.h.
+#include <hip/hip_runtime_api.h>
+#include <string.h>
+
+#include <atomic>
+#include <map>
+#include <mutex>
+
+#include "rr_phase.h"
+
+namespace rr {
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceState {
+  std::once_flag once;
+  int cus = 0;
+  int wall_khz = 0;
+  std::atomic<unsigned long long> launches{0};
+  std::mutex mu;
+  std::map<hipStream_t, uint32_t> slot_of;
+  std::map<uint32_t, int> occupancy;  // resident workgroups per CU, by kernel key
+};
+
+DeviceState g_dev[kMaxDevices];
+
+hipError_t device_of(hipStream_t s, int* dev) {
+  if (s != nullptr) return hipStreamGetDevice(s, dev);
+  return hipGetDevice(dev);
+}
+
+uint32_t slot_for(DeviceState& d, hipStream_t s) {
+  std::lock_guard<std::mutex> lock(d.mu);
+  auto it = d.slot_of.find(s);
+  if (it != d.slot_of.end()) return it->second;
+  const uint32_t slot = static_cast<uint32_t>(d.slot_of.size() % kSyncSlots);
+  d.slot_of.emplace(s, slot);
+  return slot;
+}
+
+// Cut every segment into 16-byte groups and the groups into tiles of `tile`
+// groups; fills the per-segment tables of `a` and returns the tile count.
+uint64_t tile_segments(const FoldLaunch& f, uint64_t V, uint64_t tile, PhaseArgs& a) {
+  uint64_t tiles = 0;
+  const bool ring = f.mode == FoldMode::kRingAll || f.mode == FoldMode::kRingShard;
+  a.edges = 0;
+  for (int sg = 0; sg < f.segments; ++sg) {
+    const uint64_t lo = ring ? f.args.bound[sg] : 0;
+    const uint64_t hi = ring ? f.args.bound[sg + 1] : f.args.n;
+    const uint64_t g_lo = (lo + V - 1) / V;
+    const uint64_t g_hi = hi / V;
+    const uint64_t groups = g_hi > g_lo ? g_hi - g_lo : 0;
+    const uint64_t seg_tiles = (groups + tile - 1) / tile;
+    a.seg_tile[sg] = static_cast<uint32_t>(tiles);
+    a.seg_last[sg] = static_cast<uint32_t>(seg_tiles ? groups - (seg_tiles - 1) * tile : 0);
+    // head [lo, min(g_lo*V, hi)) and tail [max(g_hi, g_lo)*V, hi): each < V
+    const uint64_t head_end = g_lo * V < hi ? g_lo * V : hi;
+    const uint64_t tail_beg = (g_hi > g_lo ? g_hi : g_lo) * V;
+    a.head_len[sg] = static_cast<uint8_t>(head_end > lo ? head_end - lo : 0);
+    a.tail_len[sg] = static_cast<uint8_t>(hi > tail_beg ? hi - tail_beg : 0);
+    if (a.head_len[sg] || a.tail_len[sg]) a.edges = 1;
+    tiles += seg_tiles;
+  }
+  if (tiles >= 0x7FFFFFFFull) return tiles;
+  a.seg_tile[f.segments] = static_cast<uint32_t>(tiles);
+  a.tiles = static_cast<uint32_t>(tiles);
+  // uniform tiling: equal segment lengths (p | n for the ring modes) whose
+  // first element starts a group, hence equal tile counts and last tiles
+  a.uniform_tiles = a.seg_tile[1] - a.seg_tile[0];
+  a.uniform_last = a.seg_last[0];
+  a.seg_len = ring ? f.args.bound[1] - f.args.bound[0] : f.args.n;
+  for (int sg = 0; sg < f.segments; ++sg) {
+    const uint64_t lo = ring ? f.args.bound[sg] : 0;
+    const uint64_t hi = ring ? f.args.bound[sg + 1] : f.args.n;
+    if (hi - lo != a.seg_len || lo != static_cast<uint64_t>(sg) * a.seg_len || lo % V != 0 ||
+        a.seg_tile[sg + 1] - a.seg_tile[sg] != a.uniform_tiles || a.seg_last[sg] != a.uniform_last)
+      a.uniform_tiles = 0;
+  }
+  return tiles;
+}
+
+hipError_t launch_mode(const FoldLaunch& f, const PhaseArgs& a, unsigned grid, int unroll, bool sync, bool static_p,
+                       int* occ, hipStream_t s) {
+  switch (f.mode) {
+    case FoldMode::kRingAll: return phase_launch_ring(a, f.in_kind, f.op, grid, unroll, sync, static_p, occ, s);
+    case FoldMode::kHierAll: return phase_launch_hier(a, f.in_kind, f.op, grid, unroll, sync, static_p, occ, s);
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int phase_default_unroll(Kind k, FoldMode m) { return (m == FoldMode::kHierAll && k == Kind::kBF16) ? 4 : 8; }
+
+bool phase_supported(const FoldLaunch& f) {
+  return (f.mode == FoldMode::kRingAll || f.mode == FoldMode::kHierAll) && f.args.vec &&
+         f.in_kind == f.out_kind && f.segments >= 1 && f.segments <= RR_MAX_RANKS;
+}
+
+// Schedule choice (measured on MI355X; every knob can be forced through
+// PhaseTuning):
+//   ring all-reduce, one round: 8 groups per lane, 2 workgroups per CU, the
+//     kernel compiled for p = 8 when p is 8;
+//   ring all-reduce, several rounds, sums: 4 groups per lane, 4 workgroups
+//     per CU (shorter phases between barriers); the kernel compiled for
+//     p = 8 for bfloat16, the run-time rank loop for 4-byte types;
+//   hierarchical all-reduce: the run-time rank loop, 4 workgroups per CU with
+//     the bfloat16 tile of 4 groups per lane, else 2.
+// With the barrier, the grid never exceeds what the device can keep resident
+// at once (the kernel's occupancy times the compute units): workgroups that
+// had to wait for a free slot would make every barrier run into its timeout.
+hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStream_t s) {
+  int dev = 0;
+  hipError_t e = device_of(s, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  DeviceState& d = g_dev[dev];
+  std::call_once(d.once, [&] {
+    if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) d.cus = 0;
+    if (hipDeviceGetAttribute(&d.wall_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) d.wall_khz = 0;
+  });
+  const uint64_t cus = d.cus > 0 ? static_cast<uint64_t>(d.cus) : 256;
+  const bool ring = f.mode == FoldMode::kRingAll;
+  const uint64_t V = f.in_kind == Kind::kBF16 ? 8 : 4;
+  bool static_p = pt.static_p >= 0 ? pt.static_p != 0 : ring;
+  int unroll = phase_default_unroll(f.in_kind, f.mode);
+  if (pt.unroll == 4 && f.op == RR_SUM) unroll = 4;
+  int per_cu = pt.per_cu > 0 ? pt.per_cu : (unroll == 4 ? 4 : 2);
+
+  PhaseArgs a;
+  memset(&a, 0, sizeof(a));
+  a.f = f.args;
+  a.segments = f.segments;
+  uint64_t tiles = tile_segments(f, V, static_cast<uint64_t>(kBlock) * unroll, a);
+  if (tiles >= 0x7FFFFFFFull) return hipErrorInvalidValue;
+  uint64_t grid = pt.grid > 0 ? static_cast<uint64_t>(pt.grid) : cus * static_cast<uint64_t>(per_cu);
+  if (ring && pt.unroll == 0 && pt.grid == 0 && f.op == RR_SUM && unroll == 8 && tiles > grid) {
+    // several rounds: the smaller tile, more workgroups
+    unroll = 4;
+    if (pt.per_cu <= 0) per_cu = 4;
+    if (pt.static_p < 0) static_p = f.in_kind == Kind::kBF16;
+    tiles = tile_segments(f, V, static_cast<uint64_t>(kBlock) * unroll, a);
+    if (tiles >= 0x7FFFFFFFull) return hipErrorInvalidValue;
+    grid = cus * static_cast<uint64_t>(per_cu);
+  }
+  if (grid > tiles) grid = tiles;
+  if (grid < 1) grid = 1;
+  a.rounds = static_cast<uint32_t>((tiles + grid - 1) / grid);
+  const bool sync = pt.sync && a.rounds > 1 && tiles <= kMaxBarrierTiles;
+  if (sync) {
+    // occupancy of the kernel about to run, cached per device and kernel
+    const uint32_t key = (static_cast<uint32_t>(f.mode) << 16) | (static_cast<uint32_t>(f.in_kind) << 12) |
+                         (static_cast<uint32_t>(f.op) << 8) | (static_cast<uint32_t>(unroll) << 4) |
+                         ((static_p && f.args.p == 8) ? 1u : 0u);
+    int occ = 0;
+    {
+      std::lock_guard<std::mutex> lock(d.mu);
+      auto it = d.occupancy.find(key);
+      if (it != d.occupancy.end()) occ = it->second;
+    }
+    if (occ == 0) {
+      e = launch_mode(f, a, 1, unroll, true, static_p, &occ, s);
+      if (e != hipSuccess) return e;
+      if (occ < 1) occ = 1;
+      std::lock_guard<std::mutex> lock(d.mu);
+      d.occupancy[key] = occ;
+    }
+    const uint64_t resident = cus * static_cast<uint64_t>(occ);
+    if (grid > resident) {
+      grid = resident;
+      a.rounds = static_cast<uint32_t>((tiles + grid - 1) / grid);
+    }
+    a.slot = slot_for(d, s);
+    const unsigned long long id = d.launches.fetch_add(1) + 1;
+    a.tag = (id & ((1ull << (64 - kLaunchShift)) - 1)) << kLaunchShift;
+    const uint64_t khz = d.wall_khz > 0 ? static_cast<uint64_t>(d.wall_khz) : 100000;
+    uint64_t ticks = khz * static_cast<uint64_t>(pt.timeout_us) / 1000;
+    if (ticks < 1) ticks = 1;
+    if (ticks > 0xFFFFFFFFull) ticks = 0xFFFFFFFFull;
+    a.timeout_ticks = static_cast<uint32_t>(ticks);
+  }
+  return launch_mode(f, a, static_cast<unsigned>(grid), unroll, sync, static_p, nullptr, s);
+}
+
+hipError_t phase_barrier_timeouts(int device, unsigned long long* count) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  if (device != cur && (e = hipSetDevice(device)) != hipSuccess) return e;
+  unsigned long long ring = 0;
+  unsigned long long hier = 0;
+  e = phase_timeouts_ring(&ring);
+  if (e == hipSuccess) e = phase_timeouts_hier(&hier);
+  *count = ring + hier;
+  if (device != cur) {
+    const hipError_t e2 = hipSetDevice(cur);
+    if (e == hipSuccess) e = e2;
+  }
+  return e;
+}
+
+}  // namespace rr

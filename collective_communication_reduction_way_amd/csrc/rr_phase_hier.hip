@@ -1,0 +1,14 @@
+// Instantiations of the phased fold for FoldMode::kHierAll (one translation
+// unit per mode so the library builds in parallel).
+#include "rr_phase_impl.h"
+
+namespace rr {
+
+hipError_t phase_launch_hier(const PhaseArgs& a, Kind k, rr_op_t op, unsigned grid, int unroll, bool sync,
+                             bool static_p, int* occ, hipStream_t s) {
+  return phase_dispatch<FoldMode::kHierAll>(a, k, op, grid, unroll, sync, static_p, occ, s);
+}
+
+hipError_t phase_timeouts_hier(unsigned long long* count) { return phase_timeouts_here(count); }
+
+}  // namespace rr

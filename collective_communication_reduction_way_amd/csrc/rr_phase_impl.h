@@ -1,0 +1,369 @@
+// rr_phase_impl.h -- the phased streaming fold (gfx950): the fused ring
+// all-reduce and the fused hierarchical all-reduce on 16-byte-aligned
+// buffers.  Included once per mode (rr_phase_ring.hip, rr_phase_hier.hip);
+// the host side is rr_phase.cpp.
+//
+// What is computed is exactly what k_fold computes (same fold orders, same
+// single rounding; see rr_fold_impl.h): element i of chunk c folds
+// x_{c+1}, ..., x_c, the order in which the reduce-scatter phase of page "LLM
+// Parallelism 基础", section "Ring AllReduce", accumulates chunk c.  Only the
+// schedule of the memory traffic differs.
+//
+// Schedule.  A persistent grid of G workgroups (about two per compute unit)
+// walks the tiles of all chunks in rounds; a tile is kBlock*U 16-byte groups
+// (32 KiB per rank for float32).  In each round a workgroup first reads its
+// tile from every rank, one rank after the other with the next rank's loads
+// in flight while the current one is folded, keeping the partial results in
+// registers; then it writes the result to every output.  HBM serves pure read
+// streams and pure write streams at a much higher rate than an interleaving of
+// both, so between the read phase and the write phase of a round the
+// workgroups meet at a soft grid barrier: for the length of a phase the whole
+// chip then reads, or writes, only.  The barrier orders nothing that the
+// results depend on (every workgroup reads and writes only its own tiles), so
+// it only shapes the traffic: its wait is bounded by a wall-clock timeout, and
+// a workgroup that times out simply goes on.  Results are therefore the same
+// whether or not the barrier ever synchronises (for instance when the
+// workgroups are not all resident because other kernels share the GPU).
+//
+// Barrier state.  Per slot, kSyncSubs arrival counters and one top counter,
+// each a 64-bit word on its own 128-byte line.  Workgroup b arrives on
+// counter b % kSyncSubs (so the arrivals do not all contend for one line);
+// the last arrival of a counter in a round bumps the top counter, and the
+// waiters poll only the top counter.  Every counter holds
+// (launch tag << kLaunchShift) + count: each launch carries a fresh, larger
+// tag and claims a counter with an atomic max before counting on it, which
+// discards whatever older launches left there without any reset.  Slots are
+// assigned per stream, so kernels that may run concurrently use different
+// counters; if two ever share one, barriers pass early or time out, and the
+// results are unaffected.
+//
+// Used for the folds that write every rank (ring and hierarchical
+// all-reduce), whose traffic is half reads and half writes; reduce-scatter
+// and reduce write one output per p inputs and keep the single-pass kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "rr_fold_impl.h"
+#include "rr_phase.h"
+
+namespace rr {
+
+namespace {
+
+// Barrier counters and the timeout count: one copy per translation unit
+// (and per device), zero when the code object loads.
+__device__ __align__(256) unsigned long long g_sync[kSyncSlots * kSyncCounters * kSyncStride];
+__device__ unsigned long long g_sync_timeouts;
+
+
+__device__ __forceinline__ unsigned long long* sync_counter(uint32_t slot, uint32_t i) {
+  return g_sync + (static_cast<size_t>(slot) * kSyncCounters + i) * kSyncStride;
+}
+
+__device__ __forceinline__ unsigned long long atomic_add_relaxed(unsigned long long* p, unsigned long long v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void atomic_max_relaxed(unsigned long long* p, unsigned long long v) {
+  __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void sync_claim(const PhaseArgs& a) {
+  if (threadIdx.x == 0) atomic_max_relaxed(sync_counter(a.slot, blockIdx.x % kSyncSubs), a.tag);
+}
+
+// Arrive at barrier `round` and wait (bounded) until all G workgroups have.
+__device__ __forceinline__ void soft_barrier(const PhaseArgs& a, uint32_t round) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t G = gridDim.x;
+    const uint32_t sub = blockIdx.x % kSyncSubs;
+    const uint32_t nsub = G < kSyncSubs ? G : kSyncSubs;
+    const uint32_t per = G / kSyncSubs + (sub < G % kSyncSubs ? 1u : 0u);  // workgroups on this counter
+    unsigned long long* top = sync_counter(a.slot, kSyncSubs);
+    const unsigned long long seen = atomic_add_relaxed(sync_counter(a.slot, sub), 1ull) + 1 - a.tag;
+    if (seen == static_cast<unsigned long long>(round + 1) * per) {
+      atomic_max_relaxed(top, a.tag);
+      atomic_add_relaxed(top, 1ull);
+    }
+    const unsigned long long target = a.tag + static_cast<unsigned long long>(round + 1) * nsub;
+    const uint64_t t0 = wall_clock64();
+    while (__hip_atomic_load(top, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(2);
+      if (wall_clock64() - t0 > a.timeout_ticks) {
+        atomic_add_relaxed(&g_sync_timeouts, 1ull);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Loads of one rank's tile.  In a partial tile (valid < kBlock*U groups) the
+// lanes past the end re-read the tile's last group instead of branching
+// around the load, so that one code path serves every tile; their values are
+// never stored.
+template <class E, int V, int U>
+__device__ __forceinline__ void load_tile(Raw<E, V> (&x)[U], const char* base, uint32_t valid) {
+  const uint32_t lane = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t g = min(lane + u * kBlock, valid - 1);
+    load_group<true>(x[u], reinterpret_cast<const typename E::S*>(base + g * 16u));
+  }
+}
+
+// Read phase of one tile: fold the p inputs (in the mode's order) into acc.
+// P > 0 (p known at compile time): the rotated source pointers are loaded
+// once into scalar registers and the rank loop is unrolled, leaving the
+// interleaving of loads and folds to the scheduler.  P == 0: a run-time loop
+// that keeps the next rank's loads in flight while the current rank is
+// folded.
+template <class E, class OP, int P, int U, FoldMode M>
+__device__ __forceinline__ void read_fold(const FoldArgs& f, int seg, int p, uint64_t in_off, uint32_t valid,
+                                          typename E::A (&acc)[U][16 / sizeof(typename E::S)]) {
+  constexpr int V = 16 / sizeof(typename E::S);
+  using A = typename E::A;
+  A tot[U][V];
+  if constexpr (P > 0) {
+    const char* src[P];
+#pragma unroll
+    for (int k = 0; k < P; ++k) src[k] = static_cast<const char*>(f.in[fold_src<M>(k, seg, P)]) + in_off;
+    {
+      Raw<E, V> x[U];
+      load_tile(x, src[0], valid);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        unpack(x[u], acc[u]);
+#pragma unroll
+        for (int j = 0; j < V; ++j) tot[u][j] = acc[u][j];
+      }
+    }
+#pragma unroll
+    for (int k = 1; k < P; ++k) {
+      Raw<E, V> x[U];
+      load_tile(x, src[k], valid);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        A v[V];
+        unpack(x[u], v);
+#pragma unroll
+        for (int j = 0; j < V; ++j) fold_step<OP, M>(acc[u][j], tot[u][j], v[j], k, f.group);
+      }
+    }
+  } else {
+    Raw<E, V> cur[U];
+    Raw<E, V> nxt[U];
+    load_tile(cur, static_cast<const char*>(f.in[fold_src<M>(0, seg, p)]) + in_off, valid);
+    if (p > 1) load_tile(nxt, static_cast<const char*>(f.in[fold_src<M>(1, seg, p)]) + in_off, valid);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      unpack(cur[u], acc[u]);
+#pragma unroll
+      for (int j = 0; j < V; ++j) tot[u][j] = acc[u][j];
+    }
+#pragma unroll 1
+    for (int k = 1; k < p; ++k) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+      if (k + 1 < p)
+        load_tile(nxt, static_cast<const char*>(f.in[fold_src<M>(k + 1, seg, p)]) + in_off, valid);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        A x[V];
+        unpack(cur[u], x);
+#pragma unroll
+        for (int j = 0; j < V; ++j) fold_step<OP, M>(acc[u][j], tot[u][j], x[j], k, f.group);
+      }
+    }
+  }
+  const int pp = P > 0 ? P : p;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int j = 0; j < V; ++j) acc[u][j] = fold_finish<OP, M>(acc[u][j], tot[u][j], pp, f.group);
+}
+
+template <bool GUARD, class E, int V, int U>
+__device__ __forceinline__ void store_tile(char* base, const Raw<E, V> (&o)[U], uint32_t valid) {
+  const uint32_t lane = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t g = lane + u * kBlock;
+    if (!GUARD || g < valid) store_group<true>(reinterpret_cast<typename E::S*>(base + g * 16u), o[u]);
+  }
+}
+
+// SYNC: the soft barrier between the phases of a round is compiled in.  The
+// kernel without it is a separate instantiation: barrier code that is
+// present but skipped still costs several percent of throughput (it
+// constrains how the stores can be scheduled after the folds).
+template <class E, class OP, int P, int U, FoldMode M, bool SYNC>
+__global__ __launch_bounds__(kBlock) void k_phase(PhaseArgs a) {
+  using S = typename E::S;
+  using A = typename E::A;
+  constexpr int V = 16 / sizeof(S);
+  constexpr uint32_t kTile = kBlock * U;
+  const int p = P > 0 ? P : a.f.p;
+  if constexpr (SYNC) sync_claim(a);
+  for (uint32_t r = 0; r < a.rounds; ++r) {
+    const uint32_t t = r * gridDim.x + blockIdx.x;
+    const bool live = t < a.tiles;
+    int seg = 0;
+    uint32_t valid = 0;
+    uint64_t off = 0;  // byte offset of the tile's first group in an input buffer
+    uint64_t lo = 0;
+    A acc[U][V];
+    if (live) {
+      uint32_t k;
+      if (a.uniform_tiles) {
+        seg = static_cast<int>(t / a.uniform_tiles);
+        k = t - static_cast<uint32_t>(seg) * a.uniform_tiles;
+        valid = (k + 1 == a.uniform_tiles) ? a.uniform_last : kTile;
+        if constexpr (is_ring(M)) lo = static_cast<uint64_t>(seg) * a.seg_len;
+      } else {
+        while (a.seg_tile[seg + 1] <= t) ++seg;
+        k = t - a.seg_tile[seg];
+        valid = (k + 1 == a.seg_tile[seg + 1] - a.seg_tile[seg]) ? a.seg_last[seg] : kTile;
+        if constexpr (is_ring(M)) lo = a.f.bound[seg];
+      }
+      const uint64_t g0 = (lo + V - 1) / V + static_cast<uint64_t>(k) * kTile;
+      off = g0 * 16;
+      read_fold<E, OP, P, U, M>(a.f, seg, p, off, valid, acc);
+    }
+    if constexpr (SYNC) soft_barrier(a, r);
+    if (live) {
+      Raw<E, V> o[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) pack(acc[u], o[u]);
+      if constexpr (writes_all(M)) {
+        if constexpr (P > 0) {
+          // every output pointer in scalar registers before the first store
+          char* dst[P];
+#pragma unroll
+          for (int q = 0; q < P; ++q) dst[q] = static_cast<char*>(a.f.out[q]) + off;
+          if (valid == kTile) {
+#pragma unroll
+            for (int q = 0; q < P; ++q) store_tile<false>(dst[q], o, valid);
+          } else {
+#pragma unroll
+            for (int q = 0; q < P; ++q) store_tile<true>(dst[q], o, valid);
+          }
+        } else if (valid == kTile) {
+          for (int q = 0; q < p; ++q) store_tile<false>(static_cast<char*>(a.f.out[q]) + off, o, valid);
+        } else {
+          for (int q = 0; q < p; ++q) store_tile<true>(static_cast<char*>(a.f.out[q]) + off, o, valid);
+        }
+      } else {
+        // reduce-scatter outputs hold only the chunk: group g sits at g*V - lo
+        const uint64_t shift = (M == FoldMode::kRingShard) ? lo * sizeof(S) : 0;
+        char* d = static_cast<char*>(a.f.out[seg]) + (off - shift);
+        if (valid == kTile) {
+          store_tile<false>(d, o, valid);
+        } else {
+          store_tile<true>(d, o, valid);
+        }
+      }
+    }
+  }
+}
+
+
+// Heads and tails of the segments (fewer than V elements each), in the same
+// fold order: one workgroup per segment, 2V lanes.  Launched only when a
+// segment has any, after the phased fold on the same stream; the elements are
+// disjoint from the phased fold's groups.
+template <class E, class OP, FoldMode M>
+__global__ __launch_bounds__(64) void k_edges(PhaseArgs a) {
+  constexpr int V = 16 / sizeof(typename E::S);
+  const int seg = blockIdx.x;
+  const int p = a.f.p;
+  uint64_t lo = 0;
+  uint64_t hi = a.f.n;
+  if constexpr (is_ring(M)) {
+    lo = a.f.bound[seg];
+    hi = a.f.bound[seg + 1];
+  }
+  const uint32_t lane = threadIdx.x;
+  if (lane < V) {
+    if (lane < a.head_len[seg]) fold_scalar<E, E, OP, M>(a.f, lo + lane, lo, seg, p);
+  } else if (lane < 2 * V && lane - V < a.tail_len[seg]) {
+    fold_scalar<E, E, OP, M>(a.f, hi - a.tail_len[seg] + (lane - V), lo, seg, p);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side dispatch of one mode's kernels.
+
+// Launch `kernel`, or, when occ is not NULL, only report how many of its
+// workgroups fit on one compute unit at once.
+template <class K>
+hipError_t phase_go(K kernel, const PhaseArgs& a, unsigned grid, unsigned block, int* occ, hipStream_t s) {
+  if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, reinterpret_cast<const void*>(kernel), block, 0);
+  PhaseArgs copy = a;
+  void* kp[] = {&copy};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(block), kp, 0, s);
+}
+
+template <class E, FoldMode M>
+constexpr int phase_unroll() {
+  return (M == FoldMode::kHierAll && sizeof(typename E::S) == 2) ? 4 : 8;
+}
+
+template <class E, class OP, int P, FoldMode M, bool SYNC>
+hipError_t phase_by_u(const PhaseArgs& a, unsigned grid, int unroll, int* occ, hipStream_t s) {
+  constexpr int kU = phase_unroll<E, M>();
+  if (unroll == kU) return phase_go(&k_phase<E, OP, P, kU, M, SYNC>, a, grid, kBlock, occ, s);
+  if constexpr (__is_same(OP, OpSum) && kU != 4) {
+    if (unroll == 4) return phase_go(&k_phase<E, OP, P, 4, M, SYNC>, a, grid, kBlock, occ, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// p = 8 (the rank count of the workloads) is compiled with its rotated
+// pointers in registers; every other p takes the run-time loop.
+template <class E, class OP, FoldMode M>
+hipError_t phase_by_p(const PhaseArgs& a, unsigned grid, int unroll, bool sync, bool static_p, int* occ,
+                      hipStream_t s) {
+  hipError_t e;
+  if (static_p && a.f.p == 8) {
+    e = sync ? phase_by_u<E, OP, 8, M, true>(a, grid, unroll, occ, s)
+             : phase_by_u<E, OP, 8, M, false>(a, grid, unroll, occ, s);
+  } else {
+    e = sync ? phase_by_u<E, OP, 0, M, true>(a, grid, unroll, occ, s)
+             : phase_by_u<E, OP, 0, M, false>(a, grid, unroll, occ, s);
+  }
+  if (e != hipSuccess || occ || !a.edges) return e;
+  return phase_go(&k_edges<E, OP, M>, a, static_cast<unsigned>(a.segments), 64, nullptr, s);
+}
+
+template <class E, FoldMode M>
+hipError_t phase_by_op(const PhaseArgs& a, rr_op_t op, unsigned grid, int unroll, bool sync, bool static_p,
+                       int* occ, hipStream_t s) {
+  switch (op) {
+    case RR_SUM: return phase_by_p<E, OpSum, M>(a, grid, unroll, sync, static_p, occ, s);
+    case RR_MAX: return phase_by_p<E, OpMax, M>(a, grid, unroll, sync, static_p, occ, s);
+    case RR_MIN: return phase_by_p<E, OpMin, M>(a, grid, unroll, sync, static_p, occ, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <FoldMode M>
+hipError_t phase_dispatch(const PhaseArgs& a, Kind k, rr_op_t op, unsigned grid, int unroll, bool sync,
+                          bool static_p, int* occ, hipStream_t s) {
+  switch (k) {
+    case Kind::kI32: return phase_by_op<EI32, M>(a, op, grid, unroll, sync, static_p, occ, s);
+    case Kind::kF32: return phase_by_op<EF32, M>(a, op, grid, unroll, sync, static_p, occ, s);
+    case Kind::kBF16: return phase_by_op<EBF16, M>(a, op, grid, unroll, sync, static_p, occ, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t phase_timeouts_here(unsigned long long* count) {
+  return hipMemcpyFromSymbol(count, HIP_SYMBOL(g_sync_timeouts), sizeof(*count), 0, hipMemcpyDeviceToHost);
+}
+
+}  // namespace
+
+}  // namespace rr

@@ -1,0 +1,14 @@
+// Instantiations of the phased fold for FoldMode::kRingAll (one translation
+// unit per mode so the library builds in parallel).
+#include "rr_phase_impl.h"
+
+namespace rr {
+
+hipError_t phase_launch_ring(const PhaseArgs& a, Kind k, rr_op_t op, unsigned grid, int unroll, bool sync,
+                             bool static_p, int* occ, hipStream_t s) {
+  return phase_dispatch<FoldMode::kRingAll>(a, k, op, grid, unroll, sync, static_p, occ, s);
+}
+
+hipError_t phase_timeouts_ring(unsigned long long* count) { return phase_timeouts_here(count); }
+
+}  // namespace rr

@@ -248,6 +248,18 @@ rr_status_t rr_ring_bytes_per_rank(int p, size_t n, rr_dtype_t dtype, uint64_t* 
 rr_status_t rr_hier_traffic(int p, int group_size, uint64_t bytes_per_rank, uint64_t* intra_per_group,
                             uint64_t* cross_per_group_flat, uint64_t* cross_per_group_hier);
 
+/*
+ * Diagnostics (needs a GPU; synchronizes the device): the number of times,
+ * since the library was loaded, that a workgroup of a fused fold on `device`
+ * stopped waiting at the soft barrier between the read phase and the write
+ * phase of a round because its bounded wait ran out.  That barrier only
+ * shapes the HBM traffic (no result depends on it), so a nonzero count means
+ * lost throughput, never wrong results; it grows when the grid's workgroups
+ * are not all resident at once (other kernels occupying the GPU).
+ * Returns RR_ERROR_INVALID_ARGUMENT for a NULL count or a bad device.
+ */
+rr_status_t rr_barrier_timeouts(int device, uint64_t* count);
+
 /* Static description of a status code. */
 const char* rr_status_string(rr_status_t status);
 
