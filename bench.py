@@ -65,7 +65,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 # Sources that define the fused all-reduce kernel; the traffic record is
 # valid only while their contents are unchanged.
 KERNEL_SOURCES = [os.path.join(ROOT, "collective_communication_reduction_way_amd", "csrc", f) for f in
-                  ("rr_device.h", "rr_kernels.h", "rr_fold_impl.h", "rr_fold_ring_all.hip", "rr_fold_hier_all.hip")]
+                  ("rr_device.h", "rr_kernels.h", "rr_fold_impl.h", "rr_phase.h", "rr_phase_impl.h",
+                   "rr_phase_ring.hip", "rr_phase_hier.hip", "rr_phase.cpp")]
 
 
 def kernel_source_hash():
@@ -122,8 +123,7 @@ def ingest_pmc(workload, fetch_path, write_path):
     for counter, path in (("FETCH_SIZE", fetch_path), ("WRITE_SIZE", write_path)):
         k = per_kernel(path, counter)
         calib = [v for n, vs in k.items() if "k_fanout" in n for v in vs]
-        fused = [v for n, vs in k.items() if "k_fold" in n and any(
-            m in n for m in ("(rr::FoldMode)0", "(rr::FoldMode)3", "FoldModeE0", "FoldModeE3")) for v in vs]
+        fused = [v for n, vs in k.items() if "k_phase" in n for v in vs]
         if not calib or not fused:
             raise SystemExit(f"{path}: no calibration-copy or fused-kernel dispatches found")
         calib_kib = max(calib)
@@ -359,8 +359,8 @@ def main(argv=None):
     kern_ms = ms_step
     value = runner.bytes / (ms_step * 1e-3) / 1e9
     achieved = runner.bytes / (kern_ms * 1e-3) / 1e9
-    kernel = {"ring": "k_fold<..., FoldMode::kRingAll> (fused ring all-reduce)",
-              "hier": "k_fold<..., FoldMode::kHierAll> (fused hierarchical all-reduce)"}[algo]
+    kernel = {"ring": "k_phase<..., FoldMode::kRingAll, ...> (phased fused ring all-reduce)",
+              "hier": "k_phase<..., FoldMode::kHierAll, ...> (phased fused hierarchical all-reduce)"}[algo]
     traffic = load_traffic(args.workload)
     out = {
         "metric": METRIC,

@@ -1,0 +1,108 @@
+"""GPU tests of the phased fold that serves the fused all-reduces on aligned
+buffers: shapes that take several rounds (so the soft barrier between the
+read and the write phase runs), ragged chunk bounds (tiles that do not tile
+the chunks, heads and tails in their own launch), p without a compiled
+kernel, the bounded wait forced to time out, and a requested grid larger
+than the device keeps resident.  The barrier orders no data, so every case
+must match the CPU oracle bit for bit whatever the barrier does.
+"""
+
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_util import assert_bitwise, to_dev, to_host
+from oracle import collectives as C
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+# (p, n): several rounds of 256-lane tiles at the default grid, with chunk
+# bounds floor(c*n/p) that are not multiples of the 16-byte group.
+MULTI_ROUND = [(8, 8 * (1 << 20) + 8 * 3 + 5), (5, 5 * (1 << 21) + 7)]
+
+
+@pytest.fixture(scope="module")
+def rr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import collective_communication_reduction_way_amd as mod
+
+    mod.lib()
+    return mod
+
+
+def run_ar(rr, x, dtype, op, algo, group=0):
+    xs = to_dev(x, dtype)
+    out = torch.empty_like(xs)
+    rr.all_reduce(xs, out, op=op, algo=algo, group_size=group)
+    got = to_host(out, dtype)
+    del xs, out
+    return got
+
+
+@pytest.mark.parametrize("p,n", MULTI_ROUND)
+@pytest.mark.parametrize("dtype", ("int32", "float32", "bfloat16"))
+def test_multi_round_ragged_ring(rr, p, n, dtype):
+    if dtype == "bfloat16":
+        n = 2 * n + 1  # twice the elements per 16-byte group: as many rounds
+    x = W.random_inputs(61, p, n, dtype, kind="full" if dtype == "int32" else "normal")
+    t0 = rr.barrier_timeouts()
+    for op in ("sum", "max"):
+        assert_bitwise(run_ar(rr, x, dtype, op, "ring"), C.all_reduce_fold(x, op, dtype), f"ring {op}")
+    assert rr.barrier_timeouts() == t0, "a phase barrier timed out on an otherwise idle GPU"
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ("float32", "bfloat16"))
+def test_multi_round_ragged_hier(rr, dtype):
+    p, n = 8, 8 * (1 << 20) * (2 if dtype == "bfloat16" else 1) + 13
+    x = W.random_inputs(62, p, n, dtype)
+    for G in (2, 4):
+        assert_bitwise(run_ar(rr, x, dtype, "sum", "hier", G), C.all_reduce_hier(x, "sum", dtype, G),
+                       f"hier G={G}")
+    torch.cuda.empty_cache()
+
+
+def test_forced_barrier_timeouts_keep_results(rr, monkeypatch):
+    """A 1 us bound makes the barrier waits run out; the results must not
+    change, and the timeouts must be counted."""
+    p, n = 8, 8 * (1 << 20) + 40
+    x = W.random_inputs(63, p, n, "float32")
+    want = C.all_reduce_fold(x, "sum", "float32")
+    monkeypatch.setenv("RR_PHASE_TIMEOUT_US", "1")
+    t0 = rr.barrier_timeouts()
+    for _ in range(3):
+        assert_bitwise(run_ar(rr, x, "float32", "sum", "ring"), want, "ring with 1 us barrier bound")
+    assert rr.barrier_timeouts() > t0, "the forced bound never ran out: the timeout path was not exercised"
+    torch.cuda.empty_cache()
+
+
+def test_oversized_grid_is_capped_to_residency(rr, monkeypatch):
+    """Asking for more workgroups per compute unit than fit at once must not
+    leave the barrier waiting on workgroups that cannot run."""
+    p, n = 8, 8 * (1 << 21)
+    x = W.random_inputs(64, p, n, "bfloat16")
+    want = C.all_reduce_fold(x, "sum", "bfloat16")
+    monkeypatch.setenv("RR_PHASE_PER_CU", "8")
+    t0 = rr.barrier_timeouts()
+    assert_bitwise(run_ar(rr, x, "bfloat16", "sum", "ring"), want, "ring, 8 workgroups per CU requested")
+    assert rr.barrier_timeouts() == t0
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("env", [{"RR_PHASE": "0"}, {"RR_PHASE_SYNC": "0"}, {"RR_PHASE_STATIC": "0"},
+                                 {"RR_PHASE_STATIC": "1"}, {"RR_PHASE_U": "4"}, {"RR_PHASE_GRID": "37"}])
+def test_schedules_agree_bitwise(rr, monkeypatch, env):
+    """Every schedule of the fused fold (single pass, phased with and without
+    barrier, compiled or run-time rank loop, both tile sizes, an odd grid)
+    gives the same bits."""
+    p, n = 8, 8 * (1 << 20) + 8 * 7 + 3
+    x = W.random_inputs(65, p, n, "float32")
+    want = C.all_reduce_fold(x, "sum", "float32")
+    want_h = C.all_reduce_hier(x, "sum", "float32", 4)
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    assert_bitwise(run_ar(rr, x, "float32", "sum", "ring"), want, f"ring {env}")
+    assert_bitwise(run_ar(rr, x, "float32", "sum", "hier", 4), want_h, f"hier {env}")
+    torch.cuda.empty_cache()
