@@ -25,6 +25,10 @@ Sources (web pages; cited by title and section):
   "Source Log: 2026-05-05" (hierarchical AllReduce + SHARP, steps 1-6): reduce
   inside each node, one representative (GPU0) per node, the representatives'
   results combined across nodes, the result broadcast back inside each node.
+* "分布式训练/推理", sections on data parallelism (the averaged gradient, the
+  flattened gradient bucket) and tensor parallelism (all-gather of [B, d/p]
+  outputs along dim 1; the scatter strategy's reduce of partial outputs
+  followed by a scatter of output slices).
 
 Readings where the pages are silent (fold order, ring direction, bf16
 rounding, max/min tie rule, int32 overflow) are stated in the docstrings of
@@ -35,19 +39,26 @@ against the worked example, closed forms, hand-computed IEEE-754 probes and
 brute force; none is "parity unpinned".
 """
 
-from . import bf16  # noqa: F401
+from . import bf16, fp16  # noqa: F401
 from .collectives import (  # noqa: F401
+    ALL_DTYPES,
+    ALL_OPS,
     DTYPES,
     OPS,
     all_gather,
+    all_gather_dim1,
+    all_reduce_bucket,
     all_reduce_fold,
     all_reduce_hier,
     all_reduce_ring,
     broadcast,
     chunk_bounds,
     fold_elements_ring_order,
+    gather,
     reduce,
+    reduce_scatter_cols,
     reduce_scatter_ring,
     ring_schedule,
+    scatter,
     simulate_ring,
 )

@@ -18,6 +18,7 @@ import numpy as np
 
 from oracle import bf16 as B
 from oracle import collectives as C
+from oracle import fp16 as H
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -36,6 +37,10 @@ def enc(values, dtype):
         return a.astype(np.int32)
     if dtype == "float32":
         return a.astype(np.float32)
+    if dtype == "float16":
+        h = a.astype(np.float16)
+        assert np.array_equal(h.astype(np.float64), a), "test value not exactly representable in fp16"
+        return h.view(np.uint16)
     f = a.astype(np.float32)
     u = f.view(np.uint32)
     assert np.all((u & 0xFFFF) == 0), "test value not exactly representable in bf16"
@@ -43,9 +48,11 @@ def enc(values, dtype):
 
 
 def dec(arr, dtype):
-    """Oracle storage array -> float64 values (bf16 decoded by bit shifting here,
-    not by the oracle's codec)."""
+    """Oracle storage array -> float64 values (bf16 decoded by bit shifting and
+    fp16 by numpy's float16 here, not by the oracle's codecs)."""
     arr = np.asarray(arr)
+    if dtype == "float16":
+        return np.ascontiguousarray(arr).view(np.float16).astype(np.float64)
     if dtype == "bfloat16":
         return (arr.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     return arr.astype(np.float64)
@@ -481,3 +488,357 @@ def pin_edge_cases():
         assert np.array_equal(dec(y, dtype), np.stack([np.array([25.0, 30.0])] * 5))
     assert C.chunk_bounds(10, 4) == [0, 2, 5, 7, 10]
     assert C.chunk_bounds(2, 5) == [0, 0, 0, 1, 1, 2]
+
+
+# ---------------------------------------------------------------------------
+# binary16 codec: round to nearest even, by hand and against numpy's float16.
+
+def pin_fp16_rounding_hand():
+    cases = [
+        (1.0 + 2.0 ** -11, 0x3C00),          # halfway, even neighbour below
+        (1.0 + 3 * 2.0 ** -11, 0x3C02),      # halfway, even neighbour above
+        (1.0 + 2.0 ** -11 + 2.0 ** -20, 0x3C01),  # just above halfway
+        (65504.0, 0x7BFF),                   # largest finite
+        (65519.0, 0x7BFF),                   # below the midpoint to 2^16
+        (65520.0, 0x7C00),                   # the midpoint: ties to even = 2^16 = inf
+        (-1.5, 0xBE00),
+        (0.0, 0x0000),
+        (-0.0, 0x8000),
+        (2.0 ** -14, 0x0400),                # smallest normal
+        (2.0 ** -24, 0x0001),                # smallest subnormal
+        (2.0 ** -25, 0x0000),                # half of it: tie to even (0)
+        (3 * 2.0 ** -26, 0x0001),            # 0.75 of it rounds up
+        (3 * 2.0 ** -25, 0x0002),            # 1.5 of it: tie to even (2)
+        (2.0 ** -126, 0x0000),               # binary32 normal far below: 0
+        (float("inf"), 0x7C00),
+        (float("-inf"), 0xFC00),
+    ]
+    f = np.array([c[0] for c in cases], dtype=np.float32)
+    got = H.narrow(f)
+    want = np.array([c[1] for c in cases], dtype=np.uint16)
+    assert np.array_equal(got, want), [(hex(a), hex(b)) for a, b in zip(got, want)]
+    # NaNs stay NaN, keep the sign and are quiet
+    u = np.array([0x7F800001, 0xFF800001, 0x7FC00000, 0x7FFFE000], dtype=np.uint32)
+    nan = H.narrow(u.view(np.float32))
+    assert np.array_equal(nan, np.array([0x7E00, 0xFE00, 0x7E00, 0x7FFF], dtype=np.uint16)), [hex(x) for x in nan]
+
+
+def pin_fp16_vs_numpy(seed=11, count=1 << 20):
+    """Against numpy's float16 conversions (an independent implementation of
+    IEEE round to nearest even): every binary16 pattern widens to the value
+    numpy gives it, and a stratified sample of binary32 patterns (every
+    exponent with tie, near-tie and random low bits) narrows to numpy's
+    pattern (NaNs excluded: numpy may keep other payload bits)."""
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    w = H.widen(h)
+    ref = h.view(np.float16).astype(np.float32)
+    ok = ~np.isnan(ref)
+    assert np.array_equal(w[ok].view(np.uint32), ref[ok].view(np.uint32))
+    assert np.all(np.isnan(w[~ok]))
+    rng = np.random.default_rng(seed)
+    u = rng.integers(0, 2 ** 32, size=count, dtype=np.uint64).astype(np.uint32)
+    e = (np.arange(1 << 16, dtype=np.uint32) % 512) << 23
+    u[: 1 << 16] = e | np.uint32(0x1000)       # tie at the normal-range rounding bit
+    u[1 << 16: 2 << 16] = e | np.uint32(0x0FFF)
+    u[2 << 16: 3 << 16] = e | (rng.integers(0, 1 << 23, size=1 << 16, dtype=np.uint64).astype(np.uint32))
+    f = u.view(np.float32)
+    f = f[~np.isnan(f)]
+    with np.errstate(over="ignore"):
+        ref16 = f.astype(np.float16).view(np.uint16)
+    assert np.array_equal(H.narrow(f), ref16)
+
+
+def fp16_ring_order_probe_inputs():
+    """The ring-order probe scaled by 2^-9 so that it fits binary16:
+    2^15 + 2^-9 is halfway between two float32 neighbours (the float32 ulp
+    at 2^15 is 2^-8) and rounds to 2^15, so ring order gives 0 while the
+    ascending fold gives [2^-8, 2^-8, 2^-8, 0]."""
+    return ring_order_probe_inputs() * 2.0 ** -9
+
+
+def pin_fp16_order_probes():
+    xs = enc(fp16_ring_order_probe_inputs(), "float16")
+    for f in (C.all_reduce_ring, C.all_reduce_fold):
+        assert np.array_equal(dec(f(xs, "sum", "float16"), "float16"), np.zeros((4, 4))), f.__name__
+    assert np.array_equal(dec(C.reduce(xs, "sum", "float16"), "float16"), np.array([2.0 ** -8] * 3 + [0.0]))
+    hx = enc(hier_probe_inputs() * 2.0 ** -9, "float16")
+    assert np.array_equal(dec(C.all_reduce_hier(hx, "sum", "float16", 4), "float16"), np.full((8, 1), 2.0 ** -9))
+    for op, want in (("sum", [6, 10, 14, 18]), ("max", [3, 4, 5, 6]), ("min", [0, 1, 2, 3])):
+        g = _golden("worked_example.json")
+        y = C.all_reduce_fold(enc(g["inputs"], "float16"), op, "float16")
+        assert np.array_equal(dec(y, "float16"), np.stack([np.array(want, float)] * 4)), op
+
+
+def pin_fp16_sum_rounds_once():
+    """Sixteen-bit inputs are folded in float32 and rounded once: p = 3,
+    x = [1, 2^-11, 2^-11] sums to 1 + 2^-10 exactly in float32, which is a
+    binary16 value; rounding each partial to binary16 would lose both
+    halves (1 + 2^-11 ties to 1)."""
+    xs = enc([[1.0], [2.0 ** -11], [2.0 ** -11]], "float16")
+    for y in (C.all_reduce_fold(xs, "sum", "float16")[0], C.reduce(xs, "sum", "float16")):
+        assert dec(y, "float16").tolist() == [1.0 + 2.0 ** -10]
+
+
+# ---------------------------------------------------------------------------
+# AVG: the averaged gradient g = (1/p) sum_r grad_r of page "分布式训练/推理"
+# (data parallelism), read as the op's sum fold, one division by p, one
+# conversion.
+
+def pin_avg_worked_example():
+    """The worked example's all-reduce [6, 10, 14, 18] over p = 4 ranks
+    averages to [1.5, 2.5, 3.5, 4.5] (exact in every float dtype)."""
+    g = _golden("worked_example.json")
+    want = np.array([1.5, 2.5, 3.5, 4.5])
+    for dtype in ("float32", "bfloat16", "float16"):
+        xs = enc(g["inputs"], dtype)
+        for f in (C.all_reduce_ring, C.all_reduce_fold):
+            assert np.array_equal(dec(f(xs, "avg", dtype), dtype), np.stack([want] * 4)), (dtype, f.__name__)
+        assert np.array_equal(dec(C.reduce_scatter_ring(xs, "avg", dtype), dtype).ravel(), want), dtype
+        assert np.array_equal(dec(C.reduce(xs, "avg", dtype), dtype), want), dtype
+        for G in (1, 2, 4):
+            assert np.array_equal(dec(C.all_reduce_hier(xs, "avg", dtype, G), dtype), np.stack([want] * 4))
+
+
+def pin_avg_closed_form(p, n):
+    """x_r[j] = (j mod 16) + r averages to (j mod 16) + (p - 1)/2: the sum is
+    exact and so is its quotient by p, which IEEE division returns unchanged."""
+    j = (np.arange(n) % 16).astype(np.float64)
+    want = j + (p - 1) / 2.0
+    for dtype in ("float32", "bfloat16", "float16"):
+        xs = closed_form_inputs(p, n, dtype) if dtype != "float16" else enc(np.stack([j + r for r in range(p)]), dtype)
+        for f in (C.all_reduce_ring, C.all_reduce_fold):
+            assert np.array_equal(dec(f(xs, "avg", dtype), dtype), np.stack([want] * p)), (dtype, p, n)
+        assert np.array_equal(dec(C.reduce(xs, "avg", dtype), dtype), want)
+
+
+def pin_avg_division_probes():
+    """Hand-derived float32 probes of how the mean is formed (p = 3):
+    * x = [1, 2, 2]: the division 5/3 rounds to 0x3FD55555; multiplying by a
+      rounded 1/3 (0x3EAAAAAB) gives 0x3FD55556 instead.
+    * x = [2, 1, 4]: dividing the sum, fl(7/3) = 0x40155555; dividing each
+      term first gives 2/3 + 1/3 + 4/3 = 0x40155556.
+    * bf16 x = [1, 1.5, 2^-7]: the float32 sum 2.5078125 divided by 3 is
+      exactly 0.8359375 = bf16 0x3F56; rounding the sum to bf16 before the
+      division (2.5, a tie to even) gives 0.83203125 = 0x3F55."""
+    xs = np.array([[1.0], [2.0], [2.0]], dtype=np.float32)
+    for y in (C.all_reduce_fold(xs, "avg", "float32")[0], C.reduce(xs, "avg", "float32"),
+              C.all_reduce_ring(xs, "avg", "float32")[0]):
+        assert int(y.view(np.uint32)[0]) == 0x3FD55555, hex(int(y.view(np.uint32)[0]))
+    xs = np.array([[2.0], [1.0], [4.0]], dtype=np.float32)
+    for y in (C.all_reduce_fold(xs, "avg", "float32")[0], C.reduce(xs, "avg", "float32")):
+        assert int(y.view(np.uint32)[0]) == 0x40155555, hex(int(y.view(np.uint32)[0]))
+    xb = enc([[1.0], [1.5], [2.0 ** -7]], "bfloat16")
+    for y in (C.all_reduce_fold(xb, "avg", "bfloat16")[0], C.reduce(xb, "avg", "bfloat16"),
+              C.all_reduce_hier(xb, "avg", "bfloat16", 3)[0]):
+        assert int(y[0]) == 0x3F56, hex(int(y[0]))
+
+
+def pin_avg_correctly_rounded(seed):
+    """The float32 mean is the correctly rounded quotient of the float32 sum
+    (the sum itself is pinned elsewhere): computed here in binary64 and
+    rounded to binary32, which for a quotient of two binary32 values is
+    correctly rounded because 53 >= 2*24 + 2 (Figueroa, "When is double
+    rounding innocuous?", 1995).  The ring's sum is taken from the sum op."""
+    rng = np.random.default_rng(seed)
+    for p in (2, 3, 5, 6, 7, 8):
+        xs = (rng.standard_normal((p, 97)) * np.exp(rng.uniform(-20, 20, size=(p, 97)))).astype(np.float32)
+        s = C.all_reduce_fold(xs, "sum", "float32")[0]
+        want = (s.astype(np.float64) / p).astype(np.float32)
+        got = C.all_reduce_fold(xs, "avg", "float32")[0]
+        assert np.array_equal(bits(got), bits(want)), p
+        rs = C.reduce_scatter_ring(xs[:, : (97 // p) * p], "avg", "float32").ravel()
+        s2 = C.all_reduce_fold(xs[:, : (97 // p) * p], "sum", "float32")[0]
+        assert np.array_equal(bits(rs), bits((s2.astype(np.float64) / p).astype(np.float32)))
+        r = C.reduce(xs, "avg", "float32")
+        assert np.array_equal(bits(r), bits((C.reduce(xs, "sum", "float32").astype(np.float64) / p).astype(np.float32)))
+
+
+def pin_avg_ring_order_and_int():
+    """AVG keeps the ring's fold order (the ring probe averages to 0, not to
+    the ascending fold's 0.5), and is refused for int32."""
+    xs = enc(ring_order_probe_inputs(), "float32")
+    assert np.array_equal(C.all_reduce_ring(xs, "avg", "float32"), np.zeros((4, 4), np.float32))
+    assert np.array_equal(C.all_reduce_fold(xs, "avg", "float32"), np.zeros((4, 4), np.float32))
+    for fn in (lambda: C.all_reduce_fold(np.ones((2, 2), np.int32), "avg", "int32"),
+               lambda: C.reduce(np.ones((2, 2), np.int32), "avg", "int32")):
+        try:
+            fn()
+        except ValueError:
+            continue
+        raise AssertionError("avg over int32 was accepted")
+
+
+# ---------------------------------------------------------------------------
+# Scatter and gather (page "分布式训练/推理", section "通信原语"; page "LLM
+# Parallelism 基础", table of MPI collectives: rank 0 cuts the array into p
+# pieces, one per process; gather collects every process's piece at one).
+
+def pin_scatter_gather():
+    g = _golden("worked_example.json")
+    # the reduce-scatter of the worked example is the scatter of its all-reduce
+    for dtype in ("int32", "float32", "bfloat16", "float16"):
+        ar = C.all_reduce_fold(enc(g["inputs"], dtype), "sum", dtype)[0]
+        sc = C.scatter(ar, 4)
+        assert np.array_equal(dec(sc, dtype), np.array(g["reduce_scatter"], dtype=np.float64))
+        assert np.array_equal(dec(C.gather(sc), dtype), np.array(g["all_gather_of_reduce_scatter"], float))
+    rng = np.random.default_rng(5)
+    for p in (1, 2, 3, 8):
+        for L in (0, 1, 7):
+            x = rng.integers(-100, 100, size=p * L).astype(np.int32)
+            sc = C.scatter(x, p)
+            assert sc.shape == (p, L)
+            for c in range(p):
+                for j in range(L):
+                    assert sc[c, j] == x[c * L + j]
+            assert np.array_equal(C.gather(sc), x)
+            # reduce-scatter is the scatter of the reduced vector (order-free ops)
+            xs = rng.integers(-(2 ** 31), 2 ** 31, size=(p, p * L), dtype=np.int64).astype(np.int32)
+            for op in C.OPS:
+                assert np.array_equal(C.reduce_scatter_ring(xs, op, "int32"), C.scatter(C.reduce(xs, op, "int32"), p))
+            # the gathered reduce-scatter is the ring all-reduce (float32, bitwise)
+            xf = rng.standard_normal((p, p * L)).astype(np.float32)
+            rs = C.reduce_scatter_ring(xf, "sum", "float32")
+            assert np.array_equal(bits(C.gather(rs)), bits(C.all_reduce_fold(xf, "sum", "float32")[0]))
+    try:
+        C.scatter(np.zeros(5, np.int32), 2)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("scatter of 5 elements over 2 ranks was accepted")
+
+
+# ---------------------------------------------------------------------------
+# Bucketed all-reduce: the tensors of a bucket are laid end to end and the
+# ring chunks the bucket, not each tensor.
+
+def pin_bucket():
+    """The ring probe cut into tensors of 1 and 3 elements still folds each
+    element in its bucket chunk's ring order (all zeros); chunking each
+    tensor on its own would put the 1-element tensor's element in chunk 3 of
+    its own ring (order x_0, x_1, x_2, x_3) and give 2.  A one-tensor bucket
+    is the plain all-reduce; integer buckets equal the per-element sum; the
+    worked example and the closed form hold across tensor cuts."""
+    xs = enc(ring_order_probe_inputs(), "float32")
+    for cut in ((1, 3), (2, 2), (3, 1), (1, 1, 1, 1)):
+        parts, o = [], 0
+        for w in cut:
+            parts.append(np.ascontiguousarray(xs[:, o:o + w]))
+            o += w
+        for dtype in ("float32",):
+            out = C.all_reduce_bucket(parts, "sum", dtype)
+            assert [t.shape for t in out] == [t.shape for t in parts]
+            for t in out:
+                assert np.array_equal(t, np.zeros_like(t)), (cut, out)
+    rng = np.random.default_rng(9)
+    for p in (1, 3, 8):
+        sizes = [int(v) for v in rng.integers(0, 40, size=5)]
+        ts = [rng.integers(-(2 ** 31), 2 ** 31, size=(p, m), dtype=np.int64).astype(np.int32) for m in sizes]
+        for op in C.OPS:
+            out = C.all_reduce_bucket(ts, op, "int32")
+            for t, y in zip(ts, out):
+                want = C.reduce(t, op, "int32")
+                assert np.array_equal(y, np.stack([want] * p)), (p, op)
+        xf = rng.standard_normal((p, 50)).astype(np.float32)
+        one = C.all_reduce_bucket([xf], "sum", "float32")[0]
+        assert np.array_equal(bits(one), bits(C.all_reduce_fold(xf, "sum", "float32")))
+    g = _golden("worked_example.json")
+    for dtype in ("float32", "bfloat16", "float16"):
+        x = enc(g["inputs"], dtype)
+        out = C.all_reduce_bucket([x[:, :1], x[:, 1:]], "avg", dtype)
+        assert np.array_equal(dec(np.concatenate(out, axis=1), dtype), np.stack([np.array([1.5, 2.5, 3.5, 4.5])] * 4))
+    p, n = 8, 4099
+    xs = closed_form_inputs(p, n, "float32")
+    out = C.all_reduce_bucket([xs[:, :1000], xs[:, 1000:1001], xs[:, 1001:]], "sum", "float32")
+    assert np.array_equal(dec(np.concatenate(out, axis=1), "float32"), np.stack([closed_form_expected(p, n, "sum")] * p))
+
+
+# ---------------------------------------------------------------------------
+# Tensor-parallel layouts (page "分布式训练/推理", tensor parallelism: the
+# all-gather of [B, d/p] outputs concatenated along dim 1, and the scatter
+# strategy, whose partial [B, D] outputs are summed and cut into feature
+# slices).
+
+def pin_all_gather_dim1():
+    rng = np.random.default_rng(3)
+    for p, B_, w in ((1, 3, 2), (2, 1, 1), (4, 3, 5), (8, 2, 3)):
+        sh = rng.integers(-50, 50, size=(p, B_, w)).astype(np.int32)
+        y = C.all_gather_dim1(sh)
+        assert y.shape == (p, B_, p * w)
+        for r in range(p):
+            for b in range(B_):
+                for c in range(p):
+                    for j in range(w):
+                        assert y[r, b, c * w + j] == sh[c, b, j]
+        # the column slices of a matrix gather back into the matrix
+        M = rng.standard_normal((B_, p * w)).astype(np.float32)
+        cols = np.stack([M[:, c * w:(c + 1) * w] for c in range(p)])
+        assert np.array_equal(C.all_gather_dim1(cols)[p - 1], M)
+
+
+def pin_reduce_scatter_cols():
+    """Row-parallel partial outputs: H_r W_r summed over r is H W (exact for
+    small integers), and rank c keeps feature slice c.  The fold order of
+    slice c is the ring order of chunk c: the ring probe laid out as a
+    1 x 4 row (and as two rows) gives zeros."""
+    rng = np.random.default_rng(4)
+    for p, B_, K, D in ((2, 3, 4, 6), (4, 2, 8, 8), (8, 5, 16, 24)):
+        H_ = rng.integers(-8, 8, size=(B_, K)).astype(np.float64)
+        W_ = rng.integers(-8, 8, size=(K, D)).astype(np.float64)
+        k = K // p
+        parts = np.stack([H_[:, r * k:(r + 1) * k] @ W_[r * k:(r + 1) * k, :] for r in range(p)]).astype(np.float32)
+        full = H_ @ W_
+        got = C.reduce_scatter_cols(parts, "sum", "float32")
+        w = D // p
+        assert got.shape == (p, B_, w)
+        for c in range(p):
+            assert np.array_equal(got[c].astype(np.float64), full[:, c * w:(c + 1) * w]), (p, c)
+        pi = parts.astype(np.int32)
+        for op in C.OPS:
+            red = C.reduce(pi.reshape(p, B_ * D), op, "int32").reshape(B_, D)
+            got = C.reduce_scatter_cols(pi, op, "int32")
+            for c in range(p):
+                assert np.array_equal(got[c], red[:, c * w:(c + 1) * w])
+    probe = ring_order_probe_inputs().astype(np.float32)
+    for rows in (probe[:, None, :], np.stack([probe, probe], axis=1)):
+        got = C.reduce_scatter_cols(rows, "sum", "float32")
+        assert np.array_equal(got, np.zeros_like(got)), got
+    # an all-gather along dim 1 of the slices gives every rank the summed matrix
+    xs = rng.standard_normal((4, 3, 8)).astype(np.float32)
+    ag = C.all_gather_dim1(C.reduce_scatter_cols(xs, "sum", "float32"))
+    flat = C.all_reduce_fold(np.ascontiguousarray(xs.transpose(0, 2, 1)).reshape(4, 24), "sum", "float32")[0]
+    assert np.array_equal(bits(ag[0]), bits(np.ascontiguousarray(flat.reshape(8, 3).T)))
+
+
+# ---------------------------------------------------------------------------
+# Hierarchical variants (page "大模型并行的最小闭环", "Source Log: 2026-05-05").
+
+def pin_hier_variants():
+    """intra="ring": with one group the hierarchical all-reduce is the ring
+    all-reduce of the group (the ring probe gives zeros, the ascending
+    default [2, 2, 2, 0]); integer results and exact sums do not depend on
+    the variant.  wire_round: p = 4, G = 2, bf16 x = [1, 2^-8, 2^-8, 0]; the
+    group partial 1 + 2^-8 rounds (tie to even) to 1 on the wire and the
+    result is 1 (the next tie), while float32 partials give 1 + 2^-7."""
+    xs = enc(ring_order_probe_inputs(), "float32")
+    assert np.array_equal(C.all_reduce_hier(xs, "sum", "float32", 4, intra="ring"), np.zeros((4, 4), np.float32))
+    assert np.array_equal(C.all_reduce_hier(xs, "sum", "float32", 4)[0], np.array([2, 2, 2, 0], np.float32))
+    # two groups of 4, each a copy of the probe, scaled: group partials from the
+    # ring are 0, so the result is 0 (the ascending intra fold gives 2*[2,2,2,0])
+    x8 = np.concatenate([xs, xs])
+    assert np.array_equal(C.all_reduce_hier(x8, "sum", "float32", 4, intra="ring"), np.zeros((8, 4), np.float32))
+    rng = np.random.default_rng(6)
+    for p, G in ((8, 4), (8, 2), (6, 3), (4, 4)):
+        xi = rng.integers(-(2 ** 31), 2 ** 31, size=(p, 37), dtype=np.int64).astype(np.int32)
+        for op in C.OPS:
+            for kw in ({"intra": "ring"}, {"wire_round": True}, {"intra": "ring", "wire_round": True}):
+                assert np.array_equal(C.all_reduce_hier(xi, op, "int32", G, **kw), C.all_reduce_fold(xi, op, "int32"))
+        xc = closed_form_inputs(p, 100, "bfloat16")
+        for kw in ({"intra": "ring"}, {"wire_round": True}):
+            assert np.array_equal(dec(C.all_reduce_hier(xc, "sum", "bfloat16", G, **kw), "bfloat16"),
+                                  np.stack([closed_form_expected(p, 100, "sum")] * p))
+        xf = rng.standard_normal((p, 37)).astype(np.float32)
+        assert np.array_equal(C.all_reduce_hier(xf, "sum", "float32", G, wire_round=True),
+                              C.all_reduce_hier(xf, "sum", "float32", G))
+    xb = enc([[1.0], [2.0 ** -8], [2.0 ** -8], [0.0]], "bfloat16")
+    assert dec(C.all_reduce_hier(xb, "sum", "bfloat16", 2, wire_round=True), "bfloat16")[:, 0].tolist() == [1.0] * 4
+    assert dec(C.all_reduce_hier(xb, "sum", "bfloat16", 2), "bfloat16")[:, 0].tolist() == [1.0 + 2.0 ** -7] * 4

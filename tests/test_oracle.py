@@ -84,3 +84,61 @@ def test_hier_vs_flat():
 
 def test_edge_cases():
     P.pin_edge_cases()
+
+
+def test_fp16_rounding_hand():
+    P.pin_fp16_rounding_hand()
+
+
+def test_fp16_vs_numpy():
+    P.pin_fp16_vs_numpy()
+
+
+def test_fp16_order_probes():
+    P.pin_fp16_order_probes()
+
+
+def test_fp16_sum_rounds_once():
+    P.pin_fp16_sum_rounds_once()
+
+
+def test_avg_worked_example():
+    P.pin_avg_worked_example()
+
+
+@pytest.mark.parametrize("p,n", [(1, 7), (3, 100), (5, 1003), (8, 4099)])
+def test_avg_closed_form(p, n):
+    P.pin_avg_closed_form(p, n)
+
+
+def test_avg_division_probes():
+    P.pin_avg_division_probes()
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_avg_correctly_rounded(seed):
+    P.pin_avg_correctly_rounded(seed)
+
+
+def test_avg_ring_order_and_int():
+    P.pin_avg_ring_order_and_int()
+
+
+def test_scatter_gather():
+    P.pin_scatter_gather()
+
+
+def test_bucket():
+    P.pin_bucket()
+
+
+def test_all_gather_dim1():
+    P.pin_all_gather_dim1()
+
+
+def test_reduce_scatter_cols():
+    P.pin_reduce_scatter_cols()
+
+
+def test_hier_variants():
+    P.pin_hier_variants()

@@ -9,10 +9,15 @@ import pytest
 import oracle_pins as P
 from oracle import bf16 as B
 from oracle import collectives as C
+from oracle import fp16 as H
 
 _combine = C.combine
 _narrow = B.narrow
 _to_acc = C.to_acc
+_finish = C.finish
+_hier = C.all_reduce_hier
+_fold = C.all_reduce_fold
+_h_narrow = H.narrow
 
 
 def _run_all_pins():
@@ -36,6 +41,20 @@ def _run_all_pins():
         ("schedule", lambda: [P.pin_schedule_symbolic(p) for p in (2, 3, 4, 8)]),
         ("hier_vs_flat", lambda: P.pin_hier_vs_flat(1)),
         ("edge_cases", P.pin_edge_cases),
+        ("fp16_hand", P.pin_fp16_rounding_hand),
+        ("fp16_numpy", lambda: P.pin_fp16_vs_numpy(count=1 << 18)),
+        ("fp16_order", P.pin_fp16_order_probes),
+        ("fp16_once", P.pin_fp16_sum_rounds_once),
+        ("avg_worked", P.pin_avg_worked_example),
+        ("avg_closed_form", lambda: [P.pin_avg_closed_form(p, n) for p, n in ((3, 100), (8, 4099))]),
+        ("avg_probes", P.pin_avg_division_probes),
+        ("avg_rounded", lambda: P.pin_avg_correctly_rounded(0)),
+        ("avg_ring_int", P.pin_avg_ring_order_and_int),
+        ("scatter_gather", P.pin_scatter_gather),
+        ("bucket", P.pin_bucket),
+        ("ag_dim1", P.pin_all_gather_dim1),
+        ("rs_cols", P.pin_reduce_scatter_cols),
+        ("hier_variants", P.pin_hier_variants),
     ]
     for name, fn in checks:
         try:
@@ -143,6 +162,61 @@ def _narrow_no_quiet(f):
     return ((u + np.uint32(0x7FFF) + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
+def _h_truncate(f):
+    f = np.ascontiguousarray(f, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.int64)
+    sign = (u >> 16) & 0x8000
+    a = u & 0x7FFFFFFF
+    e = (a >> 23) - 112
+    r = np.where(e > 0, (e << 10) | ((a & 0x7FFFFF) >> 13), 0)
+    r = np.where(e >= 31, 0x7C00, r)
+    return (sign | r).astype(np.uint16)
+
+
+def _h_flush_subnormals(f):
+    h = _h_narrow(f)
+    return np.where((h & 0x7C00) == 0, h & 0x8000, h).astype(np.uint16)
+
+
+def _h_ties_away(f):
+    f = np.ascontiguousarray(f, dtype=np.float32).astype(np.float64)
+    # round half away from zero at the binary16 grid (normal range only)
+    m, e = np.frexp(np.abs(f))
+    q = np.floor(np.abs(f) / np.exp2(e - 11) + 0.5) * np.exp2(e - 11)
+    return (np.sign(f) * q).astype(np.float16).view(np.uint16)
+
+
+def _bucket_per_tensor(tensors, op, dtype):
+    return [C.all_reduce_fold(np.asarray(t), op, dtype) for t in tensors]
+
+
+def _ag_dim1_rows(shards):
+    shards = np.asarray(shards)
+    p, B_, w = shards.shape
+    full = np.concatenate(list(shards), axis=0).reshape(B_, p * w)
+    return np.stack([full] * p)
+
+
+def _rs_cols_ascending(xs, op, dtype):
+    xs = np.asarray(xs)
+    p, B_, D = xs.shape
+    w = D // p
+    out = []
+    for c in range(p):
+        acc = C.to_acc(xs[0, :, c * w:(c + 1) * w], dtype)
+        for r in range(1, p):
+            acc = C.combine(acc, C.to_acc(xs[r, :, c * w:(c + 1) * w], dtype), op)
+        out.append(C.from_acc(C.finish(acc, op, p), dtype))
+    return np.stack(out)
+
+
+def _rs_cols_row_major_chunks(xs, op, dtype):
+    xs = np.asarray(xs)
+    p, B_, D = xs.shape
+    flat = C.reduce_scatter_ring(xs.reshape(p, B_ * D), op, dtype)
+    return flat.reshape(p, B_, D // p)
+
+
 def _to_acc_int_as_float(x, dtype):
     if dtype == "int32":
         return np.asarray(x).astype(np.float32)
@@ -169,6 +243,29 @@ MUTATIONS = {
     "bf16_nan_not_quieted": lambda m: m.setattr(B, "narrow", _narrow_no_quiet),
     "int32_accumulates_in_float": lambda m: m.setattr(C, "to_acc", _to_acc_int_as_float),
     "chunk_bounds_ceil": lambda m: m.setattr(C, "chunk_bounds", lambda n, p: [-((-c * n) // p) for c in range(p + 1)]),
+    "avg_multiplies_by_reciprocal": lambda m: m.setattr(
+        C, "finish", lambda a, op, p: a * (np.float32(1) / np.float32(p)) if op == "avg" else a),
+    "avg_not_divided": lambda m: m.setattr(C, "finish", lambda a, op, p: a),
+    "avg_divides_by_p_minus_1": lambda m: m.setattr(
+        C, "finish", lambda a, op, p: a / np.float32(max(p - 1, 1)) if op == "avg" else a),
+    "avg_rounds_sum_first": lambda m: m.setattr(
+        C, "finish", lambda a, op, p: (B.widen(B.narrow(a)) / np.float32(p)).astype(np.float32)
+        if op == "avg" else a),
+    "fp16_truncates": lambda m: m.setattr(H, "narrow", _h_truncate),
+    "fp16_flushes_subnormals": lambda m: m.setattr(H, "narrow", _h_flush_subnormals),
+    "fp16_ties_away": lambda m: m.setattr(H, "narrow", _h_ties_away),
+    "bucket_chunked_per_tensor": lambda m: m.setattr(C, "all_reduce_bucket", _bucket_per_tensor),
+    "all_gather_dim1_as_rows": lambda m: m.setattr(C, "all_gather_dim1", _ag_dim1_rows),
+    "reduce_scatter_cols_ascending": lambda m: m.setattr(C, "reduce_scatter_cols", _rs_cols_ascending),
+    "reduce_scatter_cols_row_major": lambda m: m.setattr(C, "reduce_scatter_cols", _rs_cols_row_major_chunks),
+    "hier_ignores_intra_ring": lambda m: m.setattr(
+        C, "all_reduce_hier", lambda xs, op, dt, G, intra="reduce", wire_round=False: _hier(xs, op, dt, G, "reduce",
+                                                                                           wire_round)),
+    "hier_ignores_wire_round": lambda m: m.setattr(
+        C, "all_reduce_hier", lambda xs, op, dt, G, intra="reduce", wire_round=False: _hier(xs, op, dt, G, intra)),
+    "scatter_reversed": lambda m: m.setattr(
+        C, "scatter", lambda x, p: np.stack([np.asarray(x)[c * (len(x) // p):(c + 1) * (len(x) // p)]
+                                              for c in range(p)][::-1])),
     "all_gather_reversed": lambda m: m.setattr(
         C, "all_gather", lambda sh: np.stack([np.concatenate(list(np.asarray(sh))[::-1])] * np.asarray(sh).shape[0])),
 }
