@@ -8,7 +8,8 @@ every collective runs in the library's HIP kernels.  There is no fallback: if
 
 Rank buffers are given either as a list of p tensors or as one 2-D tensor
 whose rows are the ranks.  All tensors must be contiguous, on one device and
-of one dtype (int32, float32 or bfloat16).
+of one dtype (int32, float32, bfloat16 or float16).  Ops: "sum", "max",
+"min" and, for the float dtypes, "avg" (the sum divided by p).
 
 Semantics (pages cited by title and section):
   page "分布式训练/推理", section "通信原语：rank、world size 和 collective
@@ -29,6 +30,11 @@ __all__ = [
     "all_gather",
     "reduce",
     "broadcast",
+    "scatter",
+    "gather",
+    "all_reduce_bucket",
+    "all_gather_dim1",
+    "reduce_scatter_dim1",
     "workspace_size",
     "ring_schedule",
     "chunk_bounds",
@@ -44,10 +50,11 @@ __all__ = [
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "librr.so")
 
-DTYPES = {"int32": 0, "float32": 1, "bfloat16": 2}
-OPS = {"sum": 0, "max": 1, "min": 2}
+DTYPES = {"int32": 0, "float32": 1, "bfloat16": 2, "float16": 3}
+OPS = {"sum": 0, "max": 1, "min": 2, "avg": 3}
 ALGOS = {"ring": 0, "ring_staged": 1, "hier": 2, "hier_staged": 3}
-COLLS = {"all_reduce": 0, "reduce_scatter": 1, "all_gather": 2, "reduce": 3, "broadcast": 4}
+COLLS = {"all_reduce": 0, "reduce_scatter": 1, "all_gather": 2, "reduce": 3, "broadcast": 4, "scatter": 5,
+         "gather": 6}
 MAX_RANKS = 64
 
 _lib = None
@@ -90,6 +97,11 @@ def lib():
         "rr_all_gather": (I, [PP, PP, I, S, I, P]),
         "rr_reduce": (I, [PP, P, I, I, S, I, I, P]),
         "rr_broadcast": (I, [P, PP, I, I, S, I, P]),
+        "rr_scatter": (I, [P, PP, I, I, S, I, P]),
+        "rr_gather": (I, [PP, P, I, I, S, I, P]),
+        "rr_all_reduce_bucket": (I, [PP, PP, ctypes.POINTER(ctypes.c_size_t), I, I, I, I, P]),
+        "rr_all_gather_dim1": (I, [PP, PP, I, S, S, I, P]),
+        "rr_reduce_scatter_dim1": (I, [PP, PP, I, S, S, I, I, P]),
         "rr_workspace_size": (S, [I, I, I, S, I]),
         "rr_ring_schedule": (I, [I, IP, IP, IP, IP, IP, I]),
         "rr_chunk_bounds": (I, [I, S, ctypes.POINTER(ctypes.c_size_t)]),
@@ -139,13 +151,17 @@ def _ptr_array(ptrs):
     return arr
 
 
-def _dtype_code(t):
+def _dtype_name(dtype):
     import torch
 
-    m = {torch.int32: "int32", torch.float32: "float32", torch.bfloat16: "bfloat16"}
-    if t.dtype not in m:
-        raise TypeError(f"unsupported dtype {t.dtype}; use int32, float32 or bfloat16")
-    return DTYPES[m[t.dtype]]
+    m = {torch.int32: "int32", torch.float32: "float32", torch.bfloat16: "bfloat16", torch.float16: "float16"}
+    if dtype not in m:
+        raise TypeError(f"unsupported dtype {dtype}; use int32, float32, bfloat16 or float16")
+    return m[dtype]
+
+
+def _dtype_code(t):
+    return DTYPES[_dtype_name(t.dtype)]
 
 
 def _ranks(bufs, what):
@@ -276,12 +292,119 @@ def broadcast(x, outs, root=0, stream=None):
     return outs
 
 
+def scatter(x, outs, root=0, stream=None):
+    """Rank c's output (n/p elements) becomes slice c of the root's buffer ``x``."""
+    outs = _ranks(outs, "scatter outputs")
+    p, n = len(outs), x.numel()
+    if any(o.numel() * p != n or o.dtype != x.dtype for o in outs) or not x.is_contiguous():
+        raise ValueError("scatter: need p outputs of n/p elements of the root buffer's dtype")
+    L = lib()
+    st = L.rr_scatter(x.data_ptr(), _ptr_array([t.data_ptr() for t in outs]), int(root), p, n, _dtype_code(x),
+                      _stream(x, stream))
+    _check(st, "rr_scatter")
+    return outs
+
+
+def gather(ins, out, root=0, stream=None):
+    """The root's output ``out`` (n elements) becomes the p slices in rank order."""
+    ins = _ranks(ins, "gather inputs")
+    p, n = len(ins), out.numel()
+    if any(i.numel() * p != n or i.dtype != out.dtype for i in ins) or not out.is_contiguous():
+        raise ValueError("gather: need p slices of n/p elements of the output's dtype")
+    L = lib()
+    st = L.rr_gather(_ptr_array([t.data_ptr() for t in ins]), out.data_ptr(), int(root), p, n, _dtype_code(out),
+                     _stream(out, stream))
+    _check(st, "rr_gather")
+    return out
+
+
+def all_reduce_bucket(tensors, outs=None, op="sum", stream=None):
+    """All-reduce a bucket of tensors as if they were laid end to end.
+
+    ``tensors[t]`` holds tensor t of every rank (a list of p tensors or a 2-D
+    (p, n_t) tensor); ``outs`` has the same structure (None = in place).  The
+    result is bitwise that of ``all_reduce`` on the concatenated bucket.
+    """
+    tensors = [_ranks(t, f"all_reduce_bucket tensor {i}") for i, t in enumerate(tensors)]
+    outs = tensors if outs is None else [_ranks(t, f"all_reduce_bucket output {i}") for i, t in enumerate(outs)]
+    if not tensors:
+        return outs
+    p = len(tensors[0])
+    dt = tensors[0][0].dtype
+    if len(outs) != len(tensors):
+        raise ValueError("all_reduce_bucket: outputs must match the tensors")
+    send, recv, counts = [], [], []
+    for i, (ti, to) in enumerate(zip(tensors, outs)):
+        if len(ti) != p or len(to) != p:
+            raise ValueError(f"all_reduce_bucket: tensor {i} needs {p} rank buffers")
+        n = ti[0].numel()
+        if any(x.numel() != n or x.dtype != dt for x in list(ti) + list(to)):
+            raise ValueError(f"all_reduce_bucket: tensor {i}: rank buffers and outputs need equal length and dtype")
+        counts.append(n)
+        send += [x.data_ptr() for x in ti]
+        recv += [x.data_ptr() for x in to]
+    cnt = (ctypes.c_size_t * len(counts))(*counts)
+    L = lib()
+    st = L.rr_all_reduce_bucket(_ptr_array(send), _ptr_array(recv), cnt, len(counts), p,
+                                DTYPES[_dtype_name(dt)], _op(op), _stream(tensors[0][0], stream))
+    _check(st, "rr_all_reduce_bucket")
+    return outs
+
+
+def _mats(bufs, what):
+    """A list of p contiguous matrices or a 3-D (p, rows, cols) tensor."""
+    import torch
+
+    if isinstance(bufs, torch.Tensor):
+        if bufs.dim() != 3:
+            raise ValueError(f"{what}: a tensor of rank matrices must be 3-D (p, rows, cols)")
+        bufs = list(bufs.unbind(0))
+    bufs = list(bufs)
+    for t in bufs:
+        if t.dim() != 2 or not t.is_contiguous():
+            raise ValueError(f"{what}: rank matrices must be contiguous 2-D tensors")
+    return bufs
+
+
+def all_gather_dim1(shards, outs, stream=None):
+    """Every rank's [rows, p*w] output becomes the concatenation along dim 1 of
+    the p [rows, w] shards."""
+    shards = _mats(shards, "all_gather_dim1 shards")
+    outs = _mats(outs, "all_gather_dim1 outputs")
+    p = len(shards)
+    rows, w = shards[0].shape
+    if len(outs) != p or any(o.shape != (rows, p * w) for o in outs) or any(s.shape != (rows, w) for s in shards):
+        raise ValueError("all_gather_dim1: need p shards [rows, w] and p outputs [rows, p*w]")
+    L = lib()
+    st = L.rr_all_gather_dim1(_ptr_array([t.data_ptr() for t in shards]), _ptr_array([t.data_ptr() for t in outs]),
+                              p, rows, p * w, _dtype_code(shards[0]), _stream(shards[0], stream))
+    _check(st, "rr_all_gather_dim1")
+    return outs
+
+
+def reduce_scatter_dim1(ins, outs, op="sum", stream=None):
+    """Rank c's [rows, cols/p] output becomes feature slice c of the reduction
+    of the p [rows, cols] inputs (ring order of chunk c)."""
+    ins = _mats(ins, "reduce_scatter_dim1 inputs")
+    outs = _mats(outs, "reduce_scatter_dim1 outputs")
+    p = len(ins)
+    rows, cols = ins[0].shape
+    if cols % p or len(outs) != p or any(o.shape != (rows, cols // p) for o in outs) or any(
+            i.shape != (rows, cols) for i in ins):
+        raise ValueError("reduce_scatter_dim1: need p inputs [rows, cols] and p outputs [rows, cols/p]")
+    L = lib()
+    st = L.rr_reduce_scatter_dim1(_ptr_array([t.data_ptr() for t in ins]), _ptr_array([t.data_ptr() for t in outs]),
+                                  p, rows, cols, _dtype_code(ins[0]), _op(op), _stream(ins[0], stream))
+    _check(st, "rr_reduce_scatter_dim1")
+    return outs
+
+
 def workspace_size(algo, p, group_size, n, dtype):
     """Bytes of workspace rr_all_reduce_ex needs (0 for the fused algorithms)."""
     import torch
 
     if isinstance(dtype, torch.dtype):
-        dtype = {torch.int32: "int32", torch.float32: "float32", torch.bfloat16: "bfloat16"}[dtype]
+        dtype = _dtype_name(dtype)
     return int(lib().rr_workspace_size(ALGOS[algo], int(p), int(group_size), int(n), DTYPES[dtype]))
 
 

@@ -30,6 +30,7 @@ SOURCES = [
     "rr_fold_hier_all.hip",
     "rr_fold_asc_one.hip",
     "rr_copy.hip",
+    "rr_multi.hip",
     "rr_phase_ring.hip",
     "rr_phase_hier.hip",
     "rr_phase.cpp",

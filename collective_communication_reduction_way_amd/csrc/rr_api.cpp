@@ -16,6 +16,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -108,9 +109,15 @@ Kind kind_of(rr_dtype_t d) {
   switch (d) {
     case RR_INT32: return Kind::kI32;
     case RR_FLOAT32: return Kind::kF32;
+    case RR_FLOAT16: return Kind::kF16;
     default: return Kind::kBF16;
   }
 }
+
+bool is_half_dtype(rr_dtype_t d) { return d == RR_BFLOAT16 || d == RR_FLOAT16; }
+
+// AVG divides the folded value by the number of ranks; other ops ignore it.
+int32_t divisor_for(rr_op_t op, int p) { return op == RR_AVG ? p : 0; }
 
 Kind acc_kind_of(rr_dtype_t d) { return d == RR_INT32 ? Kind::kI32 : Kind::kF32; }
 
@@ -122,8 +129,16 @@ rr_status_t check_dtype(rr_dtype_t dt) {
 }
 
 rr_status_t check_op(rr_op_t op) {
-  if (op != RR_SUM && op != RR_MAX && op != RR_MIN)
+  if (op != RR_SUM && op != RR_MAX && op != RR_MIN && op != RR_AVG)
     return fail(RR_ERROR_UNSUPPORTED, "unknown op %d", static_cast<int>(op));
+  return RR_SUCCESS;
+}
+
+// The op must be defined for the dtype: AVG only for the float dtypes.
+rr_status_t check_op_dtype(rr_op_t op, rr_dtype_t dt) {
+  rr_status_t st = check_op(op);
+  if (st) return st;
+  if (op == RR_AVG && dt == RR_INT32) return fail(RR_ERROR_UNSUPPORTED, "AVG is defined for float dtypes only");
   return RR_SUCCESS;
 }
 
@@ -174,6 +189,30 @@ rr_status_t check_aliasing(const std::vector<Range>& outs, const std::vector<Ran
         return fail(RR_ERROR_INVALID_ARGUMENT,
                     "output of rank %d overlaps input of rank %d (only the exact in-place form is allowed)",
                     o.rank, in.rank);
+  return RR_SUCCESS;
+}
+
+// The same rules for many buffers, in O(m log m): outputs sorted by address
+// must not overlap their neighbours; every input is checked against the
+// outputs that could overlap it.
+template <class ALLOWED>
+rr_status_t check_aliasing_sorted(std::vector<Range> outs, const std::vector<Range>& ins, ALLOWED allowed) {
+  outs.erase(std::remove_if(outs.begin(), outs.end(), [](const Range& r) { return r.lo == r.hi; }), outs.end());
+  std::sort(outs.begin(), outs.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  for (size_t i = 1; i < outs.size(); ++i)
+    if (outs[i].lo < outs[i - 1].hi)
+      return fail(RR_ERROR_INVALID_ARGUMENT, "output buffers %d and %d overlap", outs[i - 1].rank, outs[i].rank);
+  for (const Range& in : ins) {
+    if (in.lo == in.hi) continue;
+    // first output ending after in.lo: outputs are disjoint and sorted, so their ends are sorted too
+    size_t k = std::lower_bound(outs.begin(), outs.end(), in.lo, [](const Range& o, uintptr_t v) { return o.hi <= v; }) -
+               outs.begin();
+    for (; k < outs.size() && outs[k].lo < in.hi; ++k)
+      if (!allowed(outs[k], in))
+        return fail(RR_ERROR_INVALID_ARGUMENT,
+                    "output buffer %d overlaps input buffer %d (only the exact in-place form is allowed)",
+                    outs[k].rank, in.rank);
+  }
   return RR_SUCCESS;
 }
 
@@ -240,6 +279,7 @@ rr_status_t ar_ring_fused(const void* const* send, void* const* recv, int p, uin
   f.args.n = n;
   f.args.p = p;
   f.args.group = p;
+  f.args.div = divisor_for(op, p);
   bool vec = true;
   for (int r = 0; r < p; ++r) {
     f.args.in[r] = send[r];
@@ -261,6 +301,7 @@ rr_status_t ar_hier_fused(const void* const* send, void* const* recv, int p, uin
   f.args.n = n;
   f.args.p = p;
   f.args.group = G;
+  f.args.div = divisor_for(op, p);
   bool vec = true;
   for (int r = 0; r < p; ++r) {
     f.args.in[r] = send[r];
@@ -302,7 +343,7 @@ rr_status_t ar_ring_staged(const void* const* send, void* const* recv, int p, ui
   uint64_t b[RR_MAX_RANKS + 1];
   rr::chunk_bounds(p, n, b);
   const std::vector<rr::Transfer> sched = rr::ring_schedule(p);
-  const bool bf16 = dt == RR_BFLOAT16;
+  const bool bf16 = is_half_dtype(dt);  // 16-bit storage: float32 partials in the workspace
   // Working buffers of the reduce-scatter phase (accumulator type).
   std::vector<char*> work(p);
   for (int r = 0; r < p; ++r)
@@ -322,7 +363,7 @@ rr_status_t ar_ring_staged(const void* const* send, void* const* recv, int p, ui
     }
     a.npairs = p;
     a.vec = vec;
-    const hipError_t e = rr::launch_convert_pairs(a, Kind::kBF16, Kind::kF32, t.grid_cap, s);
+    const hipError_t e = rr::launch_convert_pairs(a, kind_of(dt), Kind::kF32, t.grid_cap, s);
     if (e != hipSuccess) return hip_fail(e, "all_reduce(ring, staged): widen");
   } else {
     std::vector<const void*> src;
@@ -360,21 +401,23 @@ rr_status_t ar_ring_staged(const void* const* send, void* const* recv, int p, ui
     const hipError_t e = rr::launch_ring_step(a, acc_kind_of(dt), op, t.grid_cap, s);
     if (e != hipSuccess) return hip_fail(e, "all_reduce(ring, staged): reduce-scatter step");
   }
-  // bf16: the owner of each chunk rounds its reduced chunk once.
-  if (bf16) {
+  // The owner of each chunk finishes its reduced chunk: 16-bit types are
+  // rounded once (AVG divides first); float32 AVG divides in place.
+  if (bf16 || op == RR_AVG) {
     rr::PairArgs a;
     memset(&a, 0, sizeof(a));
     bool vec = true;
     for (int c = 0; c < p; ++c) {
-      a.src[c] = work[c] + b[c] * 4;
+      a.src[c] = work[c] + b[c] * wsz;
       a.dst[c] = static_cast<char*>(recv[c]) + b[c] * esz;
       a.len[c] = b[c + 1] - b[c];
       vec = vec && aligned16(a.src[c]) && aligned16(a.dst[c]);
     }
     a.npairs = p;
     a.vec = vec;
-    const hipError_t e = rr::launch_convert_pairs(a, Kind::kF32, Kind::kBF16, t.grid_cap, s);
-    if (e != hipSuccess) return hip_fail(e, "all_reduce(ring, staged): narrow");
+    a.div = divisor_for(op, p);
+    const hipError_t e = rr::launch_convert_pairs(a, Kind::kF32, kind_of(dt), t.grid_cap, s);
+    if (e != hipSuccess) return hip_fail(e, "all_reduce(ring, staged): finish the reduced chunks");
   }
   // All-gather: one launch per step; the receiver overwrites.
   for (int step = 0; step < p - 1; ++step) {
@@ -404,7 +447,7 @@ rr_status_t ar_hier_staged(const void* const* send, void* const* recv, int p, ui
   f1.mode = rr::FoldMode::kAscOne;
   f1.in_kind = kind_of(dt);
   f1.out_kind = acc_kind_of(dt);
-  f1.op = op;
+  f1.op = op == RR_AVG ? RR_SUM : op;  // group partials; AVG divides at the end
   f1.segments = J;
   f1.args.n = n;
   f1.args.p = G;
@@ -429,6 +472,7 @@ rr_status_t ar_hier_staged(const void* const* send, void* const* recv, int p, ui
   f2.args.n = n;
   f2.args.p = J;
   f2.args.group = J;
+  f2.args.div = divisor_for(op, p);  // the mean is over all p ranks
   for (int j = 0; j < J; ++j) {
     f2.args.in[j] = f1.args.out[j];
     f2.args.out[j] = recv[j * G];
@@ -455,7 +499,7 @@ rr_status_t ar_hier_staged(const void* const* send, void* const* recv, int p, ui
 
 size_t workspace_bytes(rr_algo_t algo, int p, int G, uint64_t n, rr_dtype_t dt) {
   switch (algo) {
-    case RR_ALGO_RING_STAGED: return dt == RR_BFLOAT16 ? static_cast<size_t>(p) * n * 4 : 0;
+    case RR_ALGO_RING_STAGED: return is_half_dtype(dt) ? static_cast<size_t>(p) * n * 4 : 0;
     case RR_ALGO_HIER_STAGED: return static_cast<size_t>(p / G) * n * 4;
     default: return 0;
   }
@@ -469,7 +513,8 @@ rr_status_t rr_all_reduce_ex(const void* const* sendbufs, void* const* recvbufs,
                              rr_op_t op, rr_algo_t algo, int group_size, void* workspace, size_t ws_bytes,
                              rr_stream_t stream) {
   rr_status_t st;
-  if ((st = check_p(p)) || (st = check_dtype(dtype)) || (st = check_op(op)) || (st = check_n(n))) return st;
+  if ((st = check_p(p)) || (st = check_dtype(dtype)) || (st = check_op_dtype(op, dtype)) || (st = check_n(n)))
+    return st;
   if (algo != RR_ALGO_RING_FUSED && algo != RR_ALGO_RING_STAGED && algo != RR_ALGO_HIER_FUSED &&
       algo != RR_ALGO_HIER_STAGED)
     return fail(RR_ERROR_INVALID_ARGUMENT, "unknown algo %d", static_cast<int>(algo));
@@ -523,7 +568,8 @@ rr_status_t rr_all_reduce(const void* const* sendbufs, void* const* recvbufs, in
 rr_status_t rr_reduce_scatter(const void* const* sendbufs, void* const* recvbufs, int p, size_t n, rr_dtype_t dtype,
                               rr_op_t op, rr_stream_t stream) {
   rr_status_t st;
-  if ((st = check_p(p)) || (st = check_dtype(dtype)) || (st = check_op(op)) || (st = check_n(n))) return st;
+  if ((st = check_p(p)) || (st = check_dtype(dtype)) || (st = check_op_dtype(op, dtype)) || (st = check_n(n)))
+    return st;
   if (n % static_cast<size_t>(p))
     return fail(RR_ERROR_INVALID_ARGUMENT, "reduce-scatter needs p | n (p=%d, n=%zu)", p, n);
   const size_t esz = rr::elem_size(dtype);
@@ -548,6 +594,7 @@ rr_status_t rr_reduce_scatter(const void* const* sendbufs, void* const* recvbufs
   f.args.n = n;
   f.args.p = p;
   f.args.group = p;
+  f.args.div = divisor_for(op, p);
   bool vec = (L * esz) % 16 == 0;
   for (int r = 0; r < p; ++r) {
     f.args.in[r] = sendbufs[r];
@@ -605,7 +652,8 @@ rr_status_t rr_all_gather(const void* const* sendbufs, void* const* recvbufs, in
 rr_status_t rr_reduce(const void* const* sendbufs, void* recvbuf, int root, int p, size_t n, rr_dtype_t dtype,
                       rr_op_t op, rr_stream_t stream) {
   rr_status_t st;
-  if ((st = check_p(p)) || (st = check_dtype(dtype)) || (st = check_op(op)) || (st = check_n(n))) return st;
+  if ((st = check_p(p)) || (st = check_dtype(dtype)) || (st = check_op_dtype(op, dtype)) || (st = check_n(n)))
+    return st;
   if (root < 0 || root >= p) return fail(RR_ERROR_INVALID_ARGUMENT, "root=%d outside [0, p=%d)", root, p);
   if (!sendbufs) return fail(RR_ERROR_INVALID_ARGUMENT, "sendbufs is NULL");
   const size_t esz = rr::elem_size(dtype);
@@ -626,6 +674,7 @@ rr_status_t rr_reduce(const void* const* sendbufs, void* recvbuf, int root, int 
   f.args.n = n;
   f.args.p = p;
   f.args.group = p;
+  f.args.div = divisor_for(op, p);
   bool vec = aligned16(recvbuf);
   for (int r = 0; r < p; ++r) {
     f.args.in[r] = sendbufs[r];
@@ -672,6 +721,294 @@ rr_status_t rr_broadcast(const void* sendbuf, void* const* recvbufs, int root, i
   if (t.log) fprintf(stderr, "[rr] broadcast: %d copies of %llu bytes unit=%d\n", m, (unsigned long long)(n * esz), unit);
   const hipError_t e = rr::launch_fanout(a, unit, t.nontemporal, t.grid_cap, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "broadcast");
+  return ok();
+}
+
+// Scatter and gather: p independent slice copies in one launch, the root's
+// own slice skipped when it is already in place.
+rr_status_t rr_scatter(const void* sendbuf, void* const* recvbufs, int root, int p, size_t n, rr_dtype_t dtype,
+                       rr_stream_t stream) {
+  rr_status_t st;
+  if ((st = check_p(p)) || (st = check_dtype(dtype)) || (st = check_n(n))) return st;
+  if (root < 0 || root >= p) return fail(RR_ERROR_INVALID_ARGUMENT, "root=%d outside [0, p=%d)", root, p);
+  if (n % static_cast<size_t>(p)) return fail(RR_ERROR_INVALID_ARGUMENT, "scatter needs p | n (p=%d, n=%zu)", p, n);
+  if (!recvbufs) return fail(RR_ERROR_INVALID_ARGUMENT, "recvbufs is NULL");
+  const size_t esz = rr::elem_size(dtype);
+  if (n == 0) return ok();
+  if ((st = check_buf(sendbuf, esz, "sendbuf", root))) return st;
+  for (int r = 0; r < p; ++r)
+    if ((st = check_buf(recvbufs[r], esz, "recvbufs", r))) return st;
+  const uint64_t L = n / p;
+  std::vector<Range> outs, ins{range_of(sendbuf, n * esz, root)};
+  for (int r = 0; r < p; ++r) outs.push_back(range_of(recvbufs[r], L * esz, r));
+  st = check_aliasing(outs, ins, [&](const Range& o, const Range& i) {
+    return o.rank == root && o.lo == i.lo + static_cast<uintptr_t>(root) * L * esz;
+  });
+  if (st) return st;
+  std::vector<const void*> src;
+  std::vector<void*> dst;
+  std::vector<uint64_t> bytes;
+  for (int c = 0; c < p; ++c) {
+    const char* from = static_cast<const char*>(sendbuf) + static_cast<uint64_t>(c) * L * esz;
+    if (from == recvbufs[c]) continue;  // the root's slice, in place
+    src.push_back(from);
+    dst.push_back(recvbufs[c]);
+    bytes.push_back(L * esz);
+  }
+  if (src.empty()) return ok();
+  st = launch_pairs_copy(tuning(), src, dst, bytes, "scatter", reinterpret_cast<hipStream_t>(stream));
+  return st ? st : ok();
+}
+
+rr_status_t rr_gather(const void* const* sendbufs, void* recvbuf, int root, int p, size_t n, rr_dtype_t dtype,
+                      rr_stream_t stream) {
+  rr_status_t st;
+  if ((st = check_p(p)) || (st = check_dtype(dtype)) || (st = check_n(n))) return st;
+  if (root < 0 || root >= p) return fail(RR_ERROR_INVALID_ARGUMENT, "root=%d outside [0, p=%d)", root, p);
+  if (n % static_cast<size_t>(p)) return fail(RR_ERROR_INVALID_ARGUMENT, "gather needs p | n (p=%d, n=%zu)", p, n);
+  if (!sendbufs) return fail(RR_ERROR_INVALID_ARGUMENT, "sendbufs is NULL");
+  const size_t esz = rr::elem_size(dtype);
+  if (n == 0) return ok();
+  for (int r = 0; r < p; ++r)
+    if ((st = check_buf(sendbufs[r], esz, "sendbufs", r))) return st;
+  if ((st = check_buf(recvbuf, esz, "recvbuf", root))) return st;
+  const uint64_t L = n / p;
+  std::vector<Range> outs{range_of(recvbuf, n * esz, root)}, ins;
+  for (int r = 0; r < p; ++r) ins.push_back(range_of(sendbufs[r], L * esz, r));
+  st = check_aliasing(outs, ins, [&](const Range& o, const Range& i) {
+    return i.rank == root && i.lo == o.lo + static_cast<uintptr_t>(root) * L * esz;
+  });
+  if (st) return st;
+  std::vector<const void*> src;
+  std::vector<void*> dst;
+  std::vector<uint64_t> bytes;
+  for (int c = 0; c < p; ++c) {
+    char* to = static_cast<char*>(recvbuf) + static_cast<uint64_t>(c) * L * esz;
+    if (sendbufs[c] == to) continue;  // the root's slice, in place
+    src.push_back(sendbufs[c]);
+    dst.push_back(to);
+    bytes.push_back(L * esz);
+  }
+  if (src.empty()) return ok();
+  st = launch_pairs_copy(tuning(), src, dst, bytes, "gather", reinterpret_cast<hipStream_t>(stream));
+  return st ? st : ok();
+}
+
+// ---------------------------------------------------------------------------
+// Bucketed all-reduce: tensor t of rank r is sendbufs[t*p + r] (counts[t]
+// elements); the bucket is their concatenation and its chunk c is
+// [floor(c*N/p), floor((c+1)*N/p)) of the N bucket elements.  The host cuts
+// every tensor at the chunk bounds, splits each run into a 16-byte-aligned
+// body and element-wise head and tail, and packs the pieces into as few
+// launches as the argument tables allow.
+
+rr_status_t rr_all_reduce_bucket(const void* const* sendbufs, void* const* recvbufs, const size_t* counts,
+                                 int ntensors, int p, rr_dtype_t dtype, rr_op_t op, rr_stream_t stream) {
+  rr_status_t st;
+  if ((st = check_p(p)) || (st = check_dtype(dtype)) || (st = check_op_dtype(op, dtype))) return st;
+  if (ntensors < 0) return fail(RR_ERROR_INVALID_ARGUMENT, "ntensors=%d is negative", ntensors);
+  if (ntensors == 0) return ok();
+  if (!counts) return fail(RR_ERROR_INVALID_ARGUMENT, "counts is NULL");
+  if (!sendbufs) return fail(RR_ERROR_INVALID_ARGUMENT, "sendbufs is NULL");
+  if (!recvbufs) return fail(RR_ERROR_INVALID_ARGUMENT, "recvbufs is NULL");
+  const size_t esz = rr::elem_size(dtype);
+  uint64_t total = 0;
+  for (int t = 0; t < ntensors; ++t) {
+    if (static_cast<uint64_t>(counts[t]) > kMaxElems || total + counts[t] > kMaxElems)
+      return fail(RR_ERROR_INVALID_ARGUMENT, "the bucket exceeds the limit of 2^56 elements");
+    total += counts[t];
+  }
+  std::vector<Range> outs, ins;
+  for (int t = 0; t < ntensors; ++t) {
+    if (counts[t] == 0) continue;
+    for (int r = 0; r < p; ++r) {
+      const int i = t * p + r;
+      if ((st = check_buf(sendbufs[i], esz, "sendbufs", i)) || (st = check_buf(recvbufs[i], esz, "recvbufs", i)))
+        return st;
+      outs.push_back(range_of(recvbufs[i], counts[t] * esz, i));
+      ins.push_back(range_of(sendbufs[i], counts[t] * esz, i));
+    }
+  }
+  st = check_aliasing_sorted(outs, ins, [](const Range& o, const Range& i) { return o.rank == i.rank && o.lo == i.lo; });
+  if (st) return st;
+  if (total == 0) return ok();
+  const Tuning t = tuning();
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const Kind k = kind_of(dtype);
+  const uint64_t V = 16 / esz;
+  // A tile is kBlock*kBucketU units: 16-byte groups in vector pieces, single
+  // elements in scalar pieces.
+  const uint64_t kTileUnits = static_cast<uint64_t>(rr::kBlock) * rr::kBucketU;
+  const uint64_t kMaxUnits = 1ull << 30;  // keeps the kernel's tile arithmetic in 32 bits
+  uint64_t b[RR_MAX_RANKS + 1];
+  rr::chunk_bounds(p, total, b);
+
+  rr::BucketArgs a;
+  int batch_tensor = -1;  // tensor whose pointers the batch's last slots hold
+  int nslots = 0;
+  int launches = 0;
+  auto reset = [&] {
+    memset(&a, 0, sizeof(a));
+    a.p = p;
+    a.div = divisor_for(op, p);
+    batch_tensor = -1;
+    nslots = 0;
+  };
+  auto flush = [&]() -> rr_status_t {
+    if (a.npieces == 0) return RR_SUCCESS;
+    a.tile0[a.npieces] = a.tiles;
+    if (t.log) fprintf(stderr, "[rr] all_reduce_bucket: launch %d, %d pieces, %u tiles\n", launches, a.npieces, a.tiles);
+    const hipError_t e = rr::launch_bucket(a, k, op, s);
+    if (e != hipSuccess) return hip_fail(e, "all_reduce_bucket");
+    ++launches;
+    reset();
+    return RR_SUCCESS;
+  };
+  // Add a piece of `units` units of tensor `tt` starting at element `start`.
+  auto add = [&](int tt, uint64_t start, uint64_t units, int chunk, bool vec) -> rr_status_t {
+    while (units > 0) {
+      const uint64_t u = units < kMaxUnits ? units : kMaxUnits;
+      if (a.npieces == rr::kBucketPieces || (batch_tensor != tt && nslots + 2 * p > rr::kBucketPtrs)) {
+        rr_status_t e = flush();
+        if (e) return e;
+      }
+      if (batch_tensor != tt) {
+        for (int r = 0; r < p; ++r) {
+          a.ptr[nslots + r] = sendbufs[tt * p + r];
+          a.ptr[nslots + p + r] = recvbufs[tt * p + r];
+        }
+        batch_tensor = tt;
+        nslots += 2 * p;
+      }
+      const int i = a.npieces++;
+      a.start[i] = start;
+      a.units[i] = static_cast<uint32_t>(u);
+      a.tile0[i] = a.tiles;
+      a.base[i] = static_cast<uint16_t>(nslots - 2 * p);
+      a.rot[i] = static_cast<uint8_t>(chunk);
+      a.vec[i] = vec ? 1 : 0;
+      a.tiles += static_cast<uint32_t>((u + kTileUnits - 1) / kTileUnits);
+      start += vec ? u * V : u;
+      units -= u;
+      if (a.tiles > 0x40000000u) {
+        rr_status_t e = flush();
+        if (e) return e;
+      }
+    }
+    return RR_SUCCESS;
+  };
+  reset();
+  uint64_t o = 0;
+  for (int tt = 0; tt < ntensors; ++tt) {
+    const uint64_t n = counts[tt];
+    if (n == 0) continue;
+    bool aligned = true;
+    for (int r = 0; r < p; ++r)
+      aligned = aligned && aligned16(sendbufs[tt * p + r]) && aligned16(recvbufs[tt * p + r]);
+    for (int c = 0; c < p; ++c) {
+      const uint64_t lo = std::max(o, b[c]) - o;
+      const uint64_t hi = std::min(o + n, b[c + 1]) - o;
+      if (b[c + 1] <= o || b[c] >= o + n || lo >= hi) continue;
+      const uint64_t g_lo = (lo + V - 1) / V;
+      const uint64_t g_hi = hi / V;
+      if (aligned && g_hi > g_lo) {
+        if (g_lo * V > lo && (st = add(tt, lo, g_lo * V - lo, c, false))) return st;
+        if ((st = add(tt, g_lo * V, g_hi - g_lo, c, true))) return st;
+        if (hi > g_hi * V && (st = add(tt, g_hi * V, hi - g_hi * V, c, false))) return st;
+      } else if ((st = add(tt, lo, hi - lo, c, false))) {
+        return st;
+      }
+    }
+    o += n;
+  }
+  st = flush();
+  return st ? st : ok();
+}
+
+// ---------------------------------------------------------------------------
+// Tensor-parallel layouts on row-major [rows, cols] matrices, cols = p*w.
+
+rr_status_t check_cols_shape(int p, size_t rows, size_t cols) {
+  if (cols % static_cast<size_t>(p))
+    return fail(RR_ERROR_INVALID_ARGUMENT, "cols=%zu is not divisible by p=%d", cols, p);
+  if (rows > 0 && cols > 0 && (static_cast<uint64_t>(rows) > kMaxElems / static_cast<uint64_t>(cols)))
+    return fail(RR_ERROR_INVALID_ARGUMENT, "rows*cols exceeds the limit of 2^56 elements");
+  return RR_SUCCESS;
+}
+
+rr_status_t rr_all_gather_dim1(const void* const* sendbufs, void* const* recvbufs, int p, size_t rows, size_t cols,
+                               rr_dtype_t dtype, rr_stream_t stream) {
+  rr_status_t st;
+  if ((st = check_p(p)) || (st = check_dtype(dtype)) || (st = check_cols_shape(p, rows, cols))) return st;
+  const size_t esz = rr::elem_size(dtype);
+  const uint64_t n = static_cast<uint64_t>(rows) * cols;
+  if ((st = check_rank_arrays(sendbufs, recvbufs, p, esz, n))) return st;
+  if (n == 0) return ok();
+  const uint64_t w = cols / p;
+  std::vector<Range> outs, ins;
+  for (int r = 0; r < p; ++r) {
+    outs.push_back(range_of(recvbufs[r], n * esz, r));
+    ins.push_back(range_of(sendbufs[r], rows * w * esz, r));
+  }
+  st = check_aliasing(outs, ins, [](const Range&, const Range&) { return false; });
+  if (st) return st;
+  rr::ColsArgs a;
+  memset(&a, 0, sizeof(a));
+  std::vector<uintptr_t> addrs;
+  for (int r = 0; r < p; ++r) {
+    a.src[r] = sendbufs[r];
+    a.dst[r] = recvbufs[r];
+    addrs.push_back(reinterpret_cast<uintptr_t>(sendbufs[r]));
+    addrs.push_back(reinterpret_cast<uintptr_t>(recvbufs[r]));
+  }
+  const int unit = copy_unit(addrs, {w * esz});
+  a.rows = rows;
+  a.wu = w * esz / unit;
+  a.du = cols * esz / unit;
+  a.p = p;
+  const Tuning t = tuning();
+  if (t.log) fprintf(stderr, "[rr] all_gather_dim1: p=%d rows=%zu cols=%zu unit=%d\n", p, rows, cols, unit);
+  const hipError_t e = rr::launch_gather_cols(a, unit, t.nontemporal, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "all_gather_dim1");
+  return ok();
+}
+
+rr_status_t rr_reduce_scatter_dim1(const void* const* sendbufs, void* const* recvbufs, int p, size_t rows,
+                                   size_t cols, rr_dtype_t dtype, rr_op_t op, rr_stream_t stream) {
+  rr_status_t st;
+  if ((st = check_p(p)) || (st = check_dtype(dtype)) || (st = check_op_dtype(op, dtype)) ||
+      (st = check_cols_shape(p, rows, cols)))
+    return st;
+  const size_t esz = rr::elem_size(dtype);
+  const uint64_t n = static_cast<uint64_t>(rows) * cols;
+  if ((st = check_rank_arrays(sendbufs, recvbufs, p, esz, n))) return st;
+  if (n == 0) return ok();
+  const uint64_t w = cols / p;
+  std::vector<Range> outs, ins;
+  for (int r = 0; r < p; ++r) {
+    outs.push_back(range_of(recvbufs[r], rows * w * esz, r));
+    ins.push_back(range_of(sendbufs[r], n * esz, r));
+  }
+  st = check_aliasing(outs, ins, [](const Range&, const Range&) { return false; });
+  if (st) return st;
+  rr::ColsArgs a;
+  memset(&a, 0, sizeof(a));
+  bool vec = (w * esz) % 16 == 0;
+  for (int r = 0; r < p; ++r) {
+    a.src[r] = sendbufs[r];
+    a.dst[r] = recvbufs[r];
+    vec = vec && aligned16(sendbufs[r]) && aligned16(recvbufs[r]);
+  }
+  const uint64_t unit = vec ? 16 : esz;
+  a.rows = rows;
+  a.wu = w * esz / unit;
+  a.du = cols * esz / unit;
+  a.p = p;
+  a.div = divisor_for(op, p);
+  const Tuning t = tuning();
+  if (t.log) fprintf(stderr, "[rr] reduce_scatter_dim1: p=%d rows=%zu cols=%zu vec=%d\n", p, rows, cols, vec ? 1 : 0);
+  const hipError_t e = rr::launch_fold_cols(a, kind_of(dtype), op, vec ? 1 : 0, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "reduce_scatter_dim1");
   return ok();
 }
 

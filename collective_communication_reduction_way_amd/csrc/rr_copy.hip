@@ -114,9 +114,10 @@ __global__ __launch_bounds__(kBlock) void k_copy_pairs(PairArgs a) {
   }
 }
 
-// Element-wise conversion (bf16 <-> f32 for the staged paths) or the ring's
-// reduce-scatter step (dst = src (+) dst, message first).  8 elements per
-// group on the vector path, scalar otherwise (and for the last partial group).
+// Element-wise conversion (16-bit kinds <-> f32 for the staged paths, with
+// AVG's division when a.div > 0) or the ring's reduce-scatter step
+// (dst = src (+) dst, message first).  8 elements per group on the vector
+// path, scalar otherwise (and for the last partial group).
 template <class EF, class ET, class OP, bool STEP>
 __global__ __launch_bounds__(kBlock) void k_pairs_elem(PairArgs a) {
   constexpr int V = 8;
@@ -139,6 +140,11 @@ __global__ __launch_bounds__(kBlock) void k_pairs_elem(PairArgs a) {
       unpack(rd, d);
 #pragma unroll
       for (int j = 0; j < V; ++j) x[j] = OP::apply(x[j], d[j]);
+    } else if constexpr (__is_same(A, float)) {
+      if (a.div > 0) {
+#pragma unroll
+        for (int j = 0; j < V; ++j) x[j] = x[j] / static_cast<float>(a.div);
+      }
     }
     Raw<ET, V> o;
     pack(x, o);
@@ -146,7 +152,11 @@ __global__ __launch_bounds__(kBlock) void k_pairs_elem(PairArgs a) {
   }
   for (uint64_t i = ngroups * V + static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n; i += stride) {
     A x = load_one<EF>(src + i);
-    if constexpr (STEP) x = OP::apply(x, load_one<ET>(dst + i));
+    if constexpr (STEP) {
+      x = OP::apply(x, load_one<ET>(dst + i));
+    } else if constexpr (__is_same(A, float)) {
+      if (a.div > 0) x = x / static_cast<float>(a.div);
+    }
     store_one<ET>(dst + i, x);
   }
 }
@@ -185,6 +195,7 @@ hipError_t ring_step_kind(const PairArgs& a, rr_op_t op, int grid_cap, hipStream
     case RR_SUM: return pairs_elem<E, E, OpSum, true>(a, grid_cap, s);
     case RR_MAX: return pairs_elem<E, E, OpMax, true>(a, grid_cap, s);
     case RR_MIN: return pairs_elem<E, E, OpMin, true>(a, grid_cap, s);
+    case RR_AVG: return pairs_elem<E, E, OpSum, true>(a, grid_cap, s);  // partial sums; the division comes last
   }
   return hipErrorInvalidValue;
 }
@@ -223,6 +234,9 @@ hipError_t launch_copy_pairs(const PairArgs& a, int unit_bytes, int nontemporal,
 hipError_t launch_convert_pairs(const PairArgs& a, Kind from, Kind to, int grid_cap, hipStream_t s) {
   if (from == Kind::kBF16 && to == Kind::kF32) return pairs_elem<EBF16, EF32, OpSum, false>(a, grid_cap, s);
   if (from == Kind::kF32 && to == Kind::kBF16) return pairs_elem<EF32, EBF16, OpSum, false>(a, grid_cap, s);
+  if (from == Kind::kF16 && to == Kind::kF32) return pairs_elem<EF16, EF32, OpSum, false>(a, grid_cap, s);
+  if (from == Kind::kF32 && to == Kind::kF16) return pairs_elem<EF32, EF16, OpSum, false>(a, grid_cap, s);
+  if (from == Kind::kF32 && to == Kind::kF32) return pairs_elem<EF32, EF32, OpSum, false>(a, grid_cap, s);
   return hipErrorInvalidValue;
 }
 

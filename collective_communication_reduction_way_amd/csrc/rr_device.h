@@ -2,8 +2,9 @@
 // (gfx950, CDNA4).  Internal header; not part of the C ABI.
 //
 // Element kinds: each kind names a storage type S and the accumulator type A
-// that folds run in.  bfloat16 is stored as its 16-bit pattern and widened to
-// float32 exactly; every fold of bf16 runs in float32 and is rounded once.
+// that folds run in.  bfloat16 and IEEE binary16 are stored as their 16-bit
+// patterns and widened to float32 exactly; every fold of a 16-bit type runs in
+// float32 and is rounded once.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -25,6 +26,10 @@ struct EBF16 {
   using S = uint16_t;
   using A = float;
 };
+struct EF16 {
+  using S = uint16_t;
+  using A = float;
+};
 
 // ---------------------------------------------------------------------------
 // bfloat16 <-> float32.
@@ -43,6 +48,45 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
   const uint32_t quiet = (u >> 16) | 0x0040u;
   return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? quiet : rounded;
+}
+
+// ---------------------------------------------------------------------------
+// IEEE binary16 <-> float32.
+//
+// widen: the hardware conversion, exact for every binary16 value (subnormals
+// included: the library is built without denormal flushing).
+// narrow: the hardware conversion, which rounds to nearest even in the default
+// rounding mode, gives binary16 subnormals for results below 2^-14 and +-inf
+// for magnitudes that round to 2^16 or more.  A NaN is rebuilt from its bits
+// instead: sign kept, the top 9 payload bits kept, the quiet bit set.
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+  const uint32_t nan = ((u >> 16) & 0x8000u) | 0x7E00u | ((u >> 13) & 0x03FFu);
+  return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? nan : rounded;
+}
+
+// 16-bit storage pattern <-> float32, by kind.
+template <class E>
+__device__ __forceinline__ float half_to_f32(uint32_t h) {
+  if constexpr (__is_same(E, EF16)) {
+    return f16_bits_to_f32(h);
+  } else {
+    return __uint_as_float(h << 16);
+  }
+}
+
+template <class E>
+__device__ __forceinline__ uint32_t f32_to_half(float f) {
+  if constexpr (__is_same(E, EF16)) {
+    return f32_to_f16_bits(f);
+  } else {
+    return f32_to_bf16_bits(f);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -71,7 +115,27 @@ struct OpMin {
     return (v < acc) ? v : acc;
   }
 };
+// AVG (the averaged gradient of data parallelism): folds like a sum, then the
+// accumulator is divided by the number of ranks, one IEEE-754 division
+// (round to nearest even; the build keeps float division correctly rounded),
+// before the one conversion to the storage type.  Float kinds only.
+struct OpAvg : OpSum {};
 
+template <class OP>
+constexpr bool is_avg() {
+  return __is_same(OP, OpAvg);
+}
+
+// The op's last step on a folded value: AVG divides by `div`, others return
+// the value unchanged.
+template <class OP, class A>
+__device__ __forceinline__ A op_finish(A v, int32_t div) {
+  if constexpr (is_avg<OP>()) {
+    return v / static_cast<float>(div);
+  } else {
+    return v;
+  }
+}
 // ---------------------------------------------------------------------------
 // A "group" is V consecutive elements moved with 16-byte accesses.  V is chosen
 // per kernel so that the narrower of its input/output types fills exactly one
@@ -123,17 +187,25 @@ __device__ __forceinline__ void unpack(const Raw<E, V>& r, typename E::A* a) {
         a[j] = static_cast<int32_t>(w);
       }
     }
-  } else {
+  } else if constexpr (__is_same(E, EBF16)) {
 #pragma unroll
     for (int j = 0; j < V; j += 2) {
       const uint32_t w = r.w[j / 8][(j % 8) / 2];
       a[j] = bf16_lo_to_f32(w);
       a[j + 1] = bf16_hi_to_f32(w);
     }
+  } else {
+#pragma unroll
+    for (int j = 0; j < V; j += 2) {
+      const uint32_t w = r.w[j / 8][(j % 8) / 2];
+      a[j] = f16_bits_to_f32(w & 0xFFFFu);
+      a[j + 1] = f16_bits_to_f32(w >> 16);
+    }
   }
 }
 
-// V accumulator values -> raw storage words of kind E (one rounding for bf16).
+// V accumulator values -> raw storage words of kind E (one rounding for the
+// 16-bit kinds).
 template <class E, int V, class A>
 __device__ __forceinline__ void pack(const A* a, Raw<E, V>& r) {
   if constexpr (sizeof(typename E::S) == 4) {
@@ -148,7 +220,7 @@ __device__ __forceinline__ void pack(const A* a, Raw<E, V>& r) {
   } else {
 #pragma unroll
     for (int j = 0; j < V; j += 2) {
-      r.w[j / 8][(j % 8) / 2] = f32_to_bf16_bits(a[j]) | (f32_to_bf16_bits(a[j + 1]) << 16);
+      r.w[j / 8][(j % 8) / 2] = f32_to_half<E>(a[j]) | (f32_to_half<E>(a[j + 1]) << 16);
     }
   }
 }
@@ -156,8 +228,8 @@ __device__ __forceinline__ void pack(const A* a, Raw<E, V>& r) {
 // Scalar element access for heads, tails and unaligned buffers.
 template <class E>
 __device__ __forceinline__ typename E::A load_one(const typename E::S* p) {
-  if constexpr (__is_same(E, EBF16)) {
-    return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+  if constexpr (sizeof(typename E::S) == 2) {
+    return half_to_f32<E>(static_cast<uint32_t>(*p));
   } else {
     return *p;
   }
@@ -165,8 +237,8 @@ __device__ __forceinline__ typename E::A load_one(const typename E::S* p) {
 
 template <class E, class A>
 __device__ __forceinline__ void store_one(typename E::S* p, A v) {
-  if constexpr (__is_same(E, EBF16)) {
-    *p = static_cast<uint16_t>(f32_to_bf16_bits(v));
+  if constexpr (sizeof(typename E::S) == 2) {
+    *p = static_cast<uint16_t>(f32_to_half<E>(v));
   } else {
     *p = v;
   }

@@ -65,12 +65,14 @@ __device__ __forceinline__ void fold_step(A& acc, A& tot, A x, int k, int group)
   }
 }
 
+// The folded value of an element: for the hierarchy the last group's partial
+// joins the total; then the op's last step (AVG: the division by `div`).
 template <class OP, FoldMode M, class A>
-__device__ __forceinline__ A fold_finish(A acc, A tot, int p, int group) {
+__device__ __forceinline__ A fold_finish(A acc, A tot, int p, int group, int32_t div) {
   if constexpr (M == FoldMode::kHierAll) {
-    return (p > group) ? OP::apply(tot, acc) : acc;
+    return op_finish<OP>((p > group) ? OP::apply(tot, acc) : acc, div);
   } else {
-    return acc;
+    return op_finish<OP>(acc, div);
   }
 }
 
@@ -86,7 +88,7 @@ __device__ __forceinline__ void fold_scalar(const FoldArgs& a, uint64_t i, uint6
     const A x = load_one<TI>(static_cast<const SI*>(a.in[fold_src<M>(k, seg, p)]) + i);
     fold_step<OP, M>(acc, tot, x, k, a.group);
   }
-  acc = fold_finish<OP, M>(acc, tot, p, a.group);
+  acc = fold_finish<OP, M>(acc, tot, p, a.group, a.div);
   if constexpr (writes_all(M)) {
     for (int r = 0; r < p; ++r) store_one<TO>(static_cast<SO*>(a.out[r]) + i, acc);
   } else if constexpr (M == FoldMode::kRingShard) {
@@ -106,7 +108,8 @@ __device__ __forceinline__ void fold_scalar(const FoldArgs& a, uint64_t i, uint6
 // Vector path, compile-time p: all p*U loads first, then the folds.
 // `valid` = groups of this tile inside the row (only used when GUARD).
 template <class TI, class TO, class OP, int P, int U, bool NT, FoldMode M, bool GUARD>
-__device__ __forceinline__ void fold_tile(const char* const* sb, char* const* db, uint32_t valid, int group) {
+__device__ __forceinline__ void fold_tile(const char* const* sb, char* const* db, uint32_t valid, int group,
+                                          int32_t div) {
   constexpr int V = group_len<TI, TO>();
   constexpr uint32_t GBI = V * sizeof(typename TI::S);
   constexpr uint32_t GBO = V * sizeof(typename TO::S);
@@ -140,7 +143,7 @@ __device__ __forceinline__ void fold_tile(const char* const* sb, char* const* db
       for (int j = 0; j < V; ++j) fold_step<OP, M>(acc[j], tot[j], x[j], k, group);
     }
 #pragma unroll
-    for (int j = 0; j < V; ++j) acc[j] = fold_finish<OP, M>(acc[j], tot[j], P, group);
+    for (int j = 0; j < V; ++j) acc[j] = fold_finish<OP, M>(acc[j], tot[j], P, group, div);
     Raw<TO, V> o;
     pack(acc, o);
     constexpr int ND = writes_all(M) ? P : 1;
@@ -200,7 +203,7 @@ __device__ __forceinline__ void fold_tile_dyn(const FoldArgs& a, int seg, int p,
     if (GUARD && lane + u * kBlock >= valid) continue;
     const uint32_t off = (lane + u * kBlock) * GBO;
 #pragma unroll
-    for (int j = 0; j < V; ++j) acc[u][j] = fold_finish<OP, M>(acc[u][j], tot[u][j], p, a.group);
+    for (int j = 0; j < V; ++j) acc[u][j] = fold_finish<OP, M>(acc[u][j], tot[u][j], p, a.group, a.div);
     Raw<TO, V> o;
     pack(acc[u], o);
     if constexpr (writes_all(M)) {
@@ -266,9 +269,9 @@ __global__ __launch_bounds__(kBlock) void k_fold(FoldArgs a) {
       for (int r = 0; r < ND; ++r) db[r] = dst[r] + static_cast<int64_t>(g_first * GBO) + out_shift;
       const uint64_t rem = ngroups - t * kTile;
       if (rem >= kTile) {
-        fold_tile<TI, TO, OP, P, U, NT, M, false>(sb, db, 0, a.group);
+        fold_tile<TI, TO, OP, P, U, NT, M, false>(sb, db, 0, a.group, a.div);
       } else {
-        fold_tile<TI, TO, OP, P, U, NT, M, true>(sb, db, static_cast<uint32_t>(rem), a.group);
+        fold_tile<TI, TO, OP, P, U, NT, M, true>(sb, db, static_cast<uint32_t>(rem), a.group, a.div);
       }
     }
   } else {
@@ -366,13 +369,27 @@ hipError_t fold_by_op(const FoldLaunch& f, hipStream_t s) {
     case RR_SUM: return fold_by_p<TI, TO, OpSum, M>(f, s);
     case RR_MAX: return fold_by_p<TI, TO, OpMax, M>(f, s);
     case RR_MIN: return fold_by_p<TI, TO, OpMin, M>(f, s);
+    case RR_AVG:
+      if constexpr (__is_same(typename TI::A, float)) return fold_by_p<TI, TO, OpAvg, M>(f, s);
+      break;
   }
   return hipErrorInvalidValue;
 }
 
-// Same-kind folds for every mode; the mixed bf16 <-> f32 pairs exist for the
-// staged hierarchy (kAscOne writes float32 partials, kHierAll reads them) and
-// always take the run-time-p kernel.
+// Mixed kinds (a 16-bit kind and float32 partials) take the run-time-p kernel.
+template <class TI, class TO, FoldMode M>
+hipError_t fold_mixed_by_op(const FoldLaunch& f, hipStream_t s) {
+  switch (f.op) {
+    case RR_SUM: return fold_go<TI, TO, OpSum, 0, 2, false, M>(f, s);
+    case RR_MAX: return fold_go<TI, TO, OpMax, 0, 2, false, M>(f, s);
+    case RR_MIN: return fold_go<TI, TO, OpMin, 0, 2, false, M>(f, s);
+    case RR_AVG: return fold_go<TI, TO, OpAvg, 0, 2, false, M>(f, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// Same-kind folds for every mode; the mixed 16-bit <-> f32 pairs exist for the
+// staged hierarchy (kAscOne writes float32 partials, kHierAll reads them).
 template <FoldMode M>
 hipError_t fold_by_kind(const FoldLaunch& f, hipStream_t s) {
   if (f.in_kind == f.out_kind) {
@@ -380,24 +397,15 @@ hipError_t fold_by_kind(const FoldLaunch& f, hipStream_t s) {
       case Kind::kI32: return fold_by_op<EI32, EI32, M>(f, s);
       case Kind::kF32: return fold_by_op<EF32, EF32, M>(f, s);
       case Kind::kBF16: return fold_by_op<EBF16, EBF16, M>(f, s);
+      case Kind::kF16: return fold_by_op<EF16, EF16, M>(f, s);
     }
     return hipErrorInvalidValue;
   }
   if constexpr (M == FoldMode::kAscOne || M == FoldMode::kHierAll) {
-    if (f.in_kind == Kind::kBF16 && f.out_kind == Kind::kF32) {
-      switch (f.op) {
-        case RR_SUM: return fold_go<EBF16, EF32, OpSum, 0, 2, false, M>(f, s);
-        case RR_MAX: return fold_go<EBF16, EF32, OpMax, 0, 2, false, M>(f, s);
-        case RR_MIN: return fold_go<EBF16, EF32, OpMin, 0, 2, false, M>(f, s);
-      }
-    }
-    if (f.in_kind == Kind::kF32 && f.out_kind == Kind::kBF16) {
-      switch (f.op) {
-        case RR_SUM: return fold_go<EF32, EBF16, OpSum, 0, 2, false, M>(f, s);
-        case RR_MAX: return fold_go<EF32, EBF16, OpMax, 0, 2, false, M>(f, s);
-        case RR_MIN: return fold_go<EF32, EBF16, OpMin, 0, 2, false, M>(f, s);
-      }
-    }
+    if (f.in_kind == Kind::kBF16 && f.out_kind == Kind::kF32) return fold_mixed_by_op<EBF16, EF32, M>(f, s);
+    if (f.in_kind == Kind::kF32 && f.out_kind == Kind::kBF16) return fold_mixed_by_op<EF32, EBF16, M>(f, s);
+    if (f.in_kind == Kind::kF16 && f.out_kind == Kind::kF32) return fold_mixed_by_op<EF16, EF32, M>(f, s);
+    if (f.in_kind == Kind::kF32 && f.out_kind == Kind::kF16) return fold_mixed_by_op<EF32, EF16, M>(f, s);
   }
   return hipErrorInvalidValue;
 }

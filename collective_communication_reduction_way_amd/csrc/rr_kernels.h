@@ -31,7 +31,9 @@ enum class FoldMode : int {
   kHierAll = 3,
 };
 
-enum class Kind : int { kI32 = 0, kF32 = 1, kBF16 = 2 };
+enum class Kind : int { kI32 = 0, kF32 = 1, kBF16 = 2, kF16 = 3 };
+
+constexpr bool is_half(Kind k) { return k == Kind::kBF16 || k == Kind::kF16; }
 
 struct FoldArgs {
   const void* in[RR_MAX_RANKS];
@@ -41,7 +43,7 @@ struct FoldArgs {
   int32_t p;                          // inputs folded per output element
   int32_t group;                      // kHierAll: group size (divides p)
   int32_t vec;                        // 1: every buffer is 16-byte aligned
-  int32_t pad;
+  int32_t div;                        // AVG: the divisor (the number of ranks); unused otherwise
 };
 
 struct FoldLaunch {
@@ -77,6 +79,8 @@ struct PairArgs {
   uint64_t len[RR_MAX_RANKS];
   int32_t npairs;
   int32_t vec;
+  int32_t div;  // conversions: > 0 divides every value by div first (AVG's last step)
+  int32_t pad;
 };
 
 // Schedule of the phased fold (rr_phase.cpp): per_cu workgroups per compute
@@ -93,6 +97,55 @@ struct PhaseTuning {
   int static_p;  // 1 = the kernels compiled for p = 8 serve p = 8, 0 = the run-time loop, -1 = by mode
 };
 
+// Bucketed all-reduce (rr_multi.hip): the tensors of a bucket are folded as
+// if laid end to end, each element in the ring order of its chunk of the
+// bucket.  One launch serves a batch of "pieces": a piece is a run of
+// elements of one tensor inside one chunk, moved either as 16-byte groups
+// (every pointer of the tensor 16-byte aligned and the run group-aligned) or
+// element by element.  Tables are passed by value (under 4 KiB).
+constexpr int kBucketPtrs = 192;   // pointer slots per launch: p inputs then p outputs per tensor
+constexpr int kBucketPieces = 96;  // pieces per launch
+
+struct BucketArgs {
+  const void* ptr[kBucketPtrs];
+  uint64_t start[kBucketPieces];       // first element of the piece in its tensor
+  uint32_t units[kBucketPieces];       // 16-byte groups (vector pieces) or elements (scalar pieces)
+  uint32_t tile0[kBucketPieces + 1];   // first tile of each piece; tile0[npieces] = tiles
+  uint16_t base[kBucketPieces];        // slot of the piece's tensor's rank-0 input; outputs at base + p
+  uint8_t rot[kBucketPieces];          // chunk c of the bucket: fold order c+1, ..., c (mod p)
+  uint8_t vec[kBucketPieces];          // 1 = 16-byte groups
+  int32_t npieces;
+  int32_t p;
+  int32_t div;  // AVG: p; unused otherwise
+  uint32_t tiles;
+};
+
+// Units per lane and tile of the bucket kernel: a tile is kBlock*kBucketU
+// units, 16-byte groups in vector pieces and single elements in scalar ones.
+constexpr int kBucketU = 4;
+
+hipError_t launch_bucket(const BucketArgs& a, Kind k, rr_op_t op, hipStream_t stream);
+
+// Tensor-parallel layouts (rr_multi.hip) on row-major [rows, cols] matrices
+// with cols = p*w.  "Units" are 16-byte groups, or narrower units (4, 2, 1
+// bytes) for the copy, or single elements for an unaligned fold.
+struct ColsArgs {
+  const void* src[RR_MAX_RANKS];
+  void* dst[RR_MAX_RANKS];
+  uint64_t rows;
+  uint64_t wu;  // units per row of one slice (w elements)
+  uint64_t du;  // units per row of the full matrix (p*w elements)
+  int32_t p;
+  int32_t div;  // AVG: p; unused otherwise
+};
+
+// All-gather along dim 1: dst[r][b, c*w + j] = src[c][b, j] for every r.
+hipError_t launch_gather_cols(const ColsArgs& a, int unit_bytes, int nontemporal, hipStream_t stream);
+// Reduce-scatter along dim 1: dst[c][b, j] = fold over k = 1..p of
+// src[(c+k) mod p][b, c*w + j] (ring order of chunk c), then the op's last
+// step and the one conversion.  vec = 1: 16-byte groups, else elements.
+hipError_t launch_fold_cols(const ColsArgs& a, Kind k, rr_op_t op, int vec, hipStream_t stream);
+
 hipError_t launch_fold(const FoldLaunch& f, hipStream_t stream);
 // The phased fold serves same-kind folds on 16-byte-aligned buffers.
 bool phase_supported(const FoldLaunch& f);
@@ -108,7 +161,9 @@ hipError_t launch_fold_hier_all(const FoldLaunch& f, hipStream_t stream);
 hipError_t launch_fanout(const FanoutArgs& a, int unit_bytes, int nontemporal, int grid_cap, hipStream_t stream);
 // Plain copy: len[] in bytes.
 hipError_t launch_copy_pairs(const PairArgs& a, int unit_bytes, int nontemporal, int grid_cap, hipStream_t stream);
-// Element conversion: len[] in elements.
+// Element conversion (len[] in elements): 16-bit kinds <-> float32, or
+// float32 -> float32 (src may equal dst); with a.div > 0 every value is first
+// divided by a.div.
 hipError_t launch_convert_pairs(const PairArgs& a, Kind from, Kind to, int grid_cap, hipStream_t stream);
 // Ring reduce-scatter step on accumulator-type buffers: dst = src (+) dst.
 hipError_t launch_ring_step(const PairArgs& a, Kind acc_kind, rr_op_t op, int grid_cap,

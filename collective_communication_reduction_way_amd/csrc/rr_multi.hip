@@ -1,0 +1,362 @@
+// rr_multi.hip -- collectives over many tensors and over strided layouts
+// (gfx950): the bucketed all-reduce, and the two tensor-parallel layouts
+// (all-gather along dim 1, reduce-scatter along dim 1).
+//
+// Bucketed all-reduce: page "分布式训练/推理", section "Ring all-reduce 的带宽账"
+// (the gradients are flattened and all-reduced in one call instead of one
+// call per parameter, which cuts the fixed cost per call) and page
+// "分布式训练——如何把大模型分到多张卡上" (DDP synchronises gradients in buckets;
+// gradient_as_bucket_view keeps each gradient as a view of its bucket).  A
+// bucket is the concatenation of its tensors; the ring cuts the bucket, not
+// each tensor, into p chunks, so element e of the bucket folds
+// x_{c+1}, ..., x_c where c is the bucket chunk holding e.  No bucket is ever
+// materialised: the host cuts every tensor at the chunk bounds into pieces
+// and one launch folds up to kBucketPieces pieces of many tensors in place.
+//
+// Tensor-parallel layouts: page "分布式训练/推理", tensor-parallel section.
+// The column-parallel outputs [B, d/p] of the p ranks are concatenated along
+// dim 1 on every rank; in the scatter strategy the partial [B, D] outputs are
+// summed over ranks and rank c keeps feature slice c (psum_scatter).  Slice c
+// is chunk c of the ring over the feature dimension, so its fold order is
+// x_{c+1}, ..., x_c, as for reduce-scatter.
+//
+// All three are HBM streams: every input byte is read once and every output
+// byte written once; the reduction across ranks happens in each lane's
+// registers.
+#include <type_traits>
+
+#include "rr_device.h"
+#include "rr_kernels.h"
+
+namespace rr {
+
+namespace {
+
+// Fold U units per lane over the p ranks, the k-th term (k = 0..p-1) from
+// rank (rot + 1 + k) mod p.  Unit u of the lane sits off[u] bytes into every
+// rank's buffer `ptr[rank]`.  A unit is a 16-byte group of V elements (VEC)
+// or one element.  The next rank's loads are issued before the current
+// rank's values are folded.
+template <class E, class OP, int U, bool VEC>
+struct RotFold {
+  using S = typename E::S;
+  using A = typename E::A;
+  static constexpr int V = VEC ? 16 / static_cast<int>(sizeof(S)) : 1;
+  using Unit = typename std::conditional<VEC, Raw<E, (VEC ? 16 / sizeof(S) : 8)>, S>::type;
+
+  __device__ __forceinline__ static void load(Unit (&x)[U], const char* base, const uint64_t (&off)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if constexpr (VEC) {
+        load_group<true>(x[u], reinterpret_cast<const S*>(base + off[u]));
+      } else {
+        x[u] = __builtin_nontemporal_load(reinterpret_cast<const S*>(base + off[u]));
+      }
+    }
+  }
+
+  __device__ __forceinline__ static void widen(const Unit& x, A (&a)[V]) {
+    if constexpr (VEC) {
+      unpack(x, a);
+    } else if constexpr (sizeof(S) == 2) {
+      a[0] = half_to_f32<E>(static_cast<uint32_t>(x));
+    } else {
+      a[0] = x;
+    }
+  }
+
+  __device__ __forceinline__ static void run(const void* const* ptr, int rot, int p, const uint64_t (&off)[U],
+                                             int32_t div, A (&acc)[U][V]) {
+    int r = rot + 1 >= p ? rot + 1 - p : rot + 1;
+    Unit cur[U];
+    Unit nxt[U];
+    load(cur, static_cast<const char*>(ptr[r]), off);
+    int rn = r + 1 >= p ? 0 : r + 1;
+    if (p > 1) load(nxt, static_cast<const char*>(ptr[rn]), off);
+#pragma unroll
+    for (int u = 0; u < U; ++u) widen(cur[u], acc[u]);
+#pragma unroll 1
+    for (int k = 1; k < p; ++k) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+      rn = rn + 1 >= p ? 0 : rn + 1;
+      if (k + 1 < p) load(nxt, static_cast<const char*>(ptr[rn]), off);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        A x[V];
+        widen(cur[u], x);
+#pragma unroll
+        for (int j = 0; j < V; ++j) acc[u][j] = OP::apply(acc[u][j], x[j]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < V; ++j) acc[u][j] = op_finish<OP>(acc[u][j], div);
+  }
+
+  // Convert once and store unit u to `dst + off`.
+  __device__ __forceinline__ static void store(char* dst, uint64_t off, const A (&a)[V]) {
+    if constexpr (VEC) {
+      Raw<E, V> o;
+      pack(a, o);
+      store_group<true>(reinterpret_cast<S*>(dst + off), o);
+    } else {
+      store_one<E>(reinterpret_cast<S*>(dst + off), a[0]);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Bucketed all-reduce.
+
+template <class E, class OP, bool VEC>
+__device__ __forceinline__ void bucket_tile(const BucketArgs& a, int pc, uint32_t k) {
+  using F = RotFold<E, OP, kBucketU, VEC>;
+  constexpr uint32_t kUnits = static_cast<uint32_t>(kBlock) * kBucketU;
+  constexpr uint32_t kUnitBytes = VEC ? 16u : static_cast<uint32_t>(sizeof(typename E::S));
+  const uint32_t lane = threadIdx.x;
+  const uint32_t valid = min(kUnits, a.units[pc] - k * kUnits);  // units of this tile, >= 1
+  const uint64_t base = a.start[pc] * sizeof(typename E::S) + static_cast<uint64_t>(k) * kUnits * kUnitBytes;
+  uint64_t off[kBucketU];
+#pragma unroll
+  for (int u = 0; u < kBucketU; ++u) off[u] = base + min(lane + u * kBlock, valid - 1) * kUnitBytes;
+  const int p = a.p;
+  typename E::A acc[kBucketU][F::V];
+  F::run(a.ptr + a.base[pc], a.rot[pc], p, off, a.div, acc);
+  for (int r = 0; r < p; ++r) {
+    char* d = static_cast<char*>(const_cast<void*>(a.ptr[a.base[pc] + p + r]));
+#pragma unroll
+    for (int u = 0; u < kBucketU; ++u)
+      if (lane + u * kBlock < valid) F::store(d, off[u], acc[u]);
+  }
+}
+
+template <class E, class OP>
+__global__ __launch_bounds__(kBlock) void k_bucket(BucketArgs a) {
+  for (uint32_t t = blockIdx.x; t < a.tiles; t += gridDim.x) {
+    // the piece of tile t: the last piece whose first tile is <= t
+    int lo = 0;
+    int hi = a.npieces - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.tile0[mid] <= t) {
+        lo = mid;
+      } else {
+        hi = mid - 1;
+      }
+    }
+    const uint32_t k = t - a.tile0[lo];
+    if (a.vec[lo]) {
+      bucket_tile<E, OP, true>(a, lo, k);
+    } else {
+      bucket_tile<E, OP, false>(a, lo, k);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Reduce-scatter along dim 1.  Row b of output c holds w elements: unit i of
+// output c (i = b*wu + j) reads unit b*du + c*wu + j of every input.
+
+template <class E, class OP, bool VEC>
+__global__ __launch_bounds__(kBlock) void k_fold_cols(ColsArgs a) {
+  constexpr int U = 2;
+  using F = RotFold<E, OP, U, VEC>;
+  constexpr uint64_t kUnitBytes = VEC ? 16 : sizeof(typename E::S);
+  const int c = blockIdx.y;
+  const int p = a.p;
+  const uint64_t total = a.rows * a.wu;
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock * U;
+  char* d = static_cast<char*>(a.dst[c]);
+  for (uint64_t t0 = static_cast<uint64_t>(blockIdx.x) * kBlock * U; t0 < total; t0 += stride) {
+    uint64_t in_off[U];
+    uint64_t out_off[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint64_t i = t0 + threadIdx.x + static_cast<uint64_t>(u) * kBlock;
+      ok[u] = i < total;
+      if (!ok[u]) i = total - 1;  // re-read a valid unit; never stored
+      const uint64_t b = i / a.wu;
+      const uint64_t j = i - b * a.wu;
+      in_off[u] = (b * a.du + static_cast<uint64_t>(c) * a.wu + j) * kUnitBytes;
+      out_off[u] = i * kUnitBytes;
+    }
+    typename E::A acc[U][F::V];
+    F::run(a.src, c, p, in_off, a.div, acc);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (ok[u]) F::store(d, out_off[u], acc[u]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// All-gather along dim 1: source c's unit i (row b, column unit j) goes to
+// unit b*du + c*wu + j of every output.
+
+template <int B>
+struct Word;
+template <>
+struct Word<16> {
+  using T = u32x4;
+};
+template <>
+struct Word<4> {
+  using T = uint32_t;
+};
+template <>
+struct Word<2> {
+  using T = uint16_t;
+};
+template <>
+struct Word<1> {
+  using T = uint8_t;
+};
+
+template <int B, bool NT>
+__global__ __launch_bounds__(kBlock) void k_gather_cols(ColsArgs a) {
+  using T = typename Word<B>::T;
+  constexpr int U = 2;
+  const int c = blockIdx.y;
+  const uint64_t total = a.rows * a.wu;
+  const T* src = static_cast<const T*>(a.src[c]);
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock * U;
+  for (uint64_t t0 = static_cast<uint64_t>(blockIdx.x) * kBlock * U; t0 < total; t0 += stride) {
+    T v[U];
+    uint64_t o[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t i = t0 + threadIdx.x + static_cast<uint64_t>(u) * kBlock;
+      const uint64_t ic = i < total ? i : total - 1;
+      if constexpr (NT) {
+        v[u] = __builtin_nontemporal_load(src + ic);
+      } else {
+        v[u] = src[ic];
+      }
+      const uint64_t b = ic / a.wu;
+      o[u] = b * a.du + static_cast<uint64_t>(c) * a.wu + (ic - b * a.wu);
+    }
+    for (int r = 0; r < a.p; ++r) {
+      T* dst = static_cast<T*>(a.dst[r]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (t0 + threadIdx.x + static_cast<uint64_t>(u) * kBlock < total) {
+          if constexpr (NT) {
+            __builtin_nontemporal_store(v[u], dst + o[u]);
+          } else {
+            dst[o[u]] = v[u];
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side dispatch.
+
+constexpr int kMaxDevices = 64;
+int g_cus[kMaxDevices];
+
+// Compute units of the stream's device (0 if unknown), read once per device.
+int cus_of(hipStream_t s) {
+  int dev = 0;
+  if ((s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev)) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return 0;
+  int v = __atomic_load_n(&g_cus[dev], __ATOMIC_RELAXED);
+  if (v == 0 && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+    __atomic_store_n(&g_cus[dev], v, __ATOMIC_RELAXED);
+  return v;
+}
+
+template <class K, class ARGS>
+hipError_t launch(K kernel, const ARGS& args, dim3 grid, hipStream_t s) {
+  ARGS copy = args;
+  void* kp[] = {&copy};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, dim3(kBlock), kp, 0, s);
+}
+
+// Workgroups of a streaming launch: enough to keep every compute unit busy
+// (four per CU), never more than there is work.
+unsigned stream_grid(uint64_t work_units, uint64_t per_block, int rows, hipStream_t s) {
+  const int cus = cus_of(s);
+  uint64_t cap = static_cast<uint64_t>(cus > 0 ? cus : 256) * 4;
+  cap = (cap + static_cast<uint64_t>(rows) - 1) / static_cast<uint64_t>(rows);
+  uint64_t g = (work_units + per_block - 1) / per_block;
+  if (g > cap) g = cap;
+  if (g < 1) g = 1;
+  return static_cast<unsigned>(g);
+}
+
+template <class E>
+hipError_t bucket_by_op(const BucketArgs& a, rr_op_t op, hipStream_t s) {
+  const dim3 grid(stream_grid(a.tiles, 1, 1, s));
+  switch (op) {
+    case RR_SUM: return launch(&k_bucket<E, OpSum>, a, grid, s);
+    case RR_MAX: return launch(&k_bucket<E, OpMax>, a, grid, s);
+    case RR_MIN: return launch(&k_bucket<E, OpMin>, a, grid, s);
+    case RR_AVG:
+      if constexpr (__is_same(typename E::A, float)) return launch(&k_bucket<E, OpAvg>, a, grid, s);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class E, bool VEC>
+hipError_t fold_cols_by_op(const ColsArgs& a, rr_op_t op, hipStream_t s) {
+  const dim3 grid(stream_grid(a.rows * a.wu, static_cast<uint64_t>(kBlock) * 2, a.p, s), a.p);
+  switch (op) {
+    case RR_SUM: return launch(&k_fold_cols<E, OpSum, VEC>, a, grid, s);
+    case RR_MAX: return launch(&k_fold_cols<E, OpMax, VEC>, a, grid, s);
+    case RR_MIN: return launch(&k_fold_cols<E, OpMin, VEC>, a, grid, s);
+    case RR_AVG:
+      if constexpr (__is_same(typename E::A, float)) return launch(&k_fold_cols<E, OpAvg, VEC>, a, grid, s);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class E>
+hipError_t fold_cols_kind(const ColsArgs& a, rr_op_t op, int vec, hipStream_t s) {
+  return vec ? fold_cols_by_op<E, true>(a, op, s) : fold_cols_by_op<E, false>(a, op, s);
+}
+
+}  // namespace
+
+hipError_t launch_bucket(const BucketArgs& a, Kind k, rr_op_t op, hipStream_t s) {
+  if (a.tiles == 0) return hipSuccess;
+  switch (k) {
+    case Kind::kI32: return bucket_by_op<EI32>(a, op, s);
+    case Kind::kF32: return bucket_by_op<EF32>(a, op, s);
+    case Kind::kBF16: return bucket_by_op<EBF16>(a, op, s);
+    case Kind::kF16: return bucket_by_op<EF16>(a, op, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fold_cols(const ColsArgs& a, Kind k, rr_op_t op, int vec, hipStream_t s) {
+  if (a.rows * a.wu == 0) return hipSuccess;
+  switch (k) {
+    case Kind::kI32: return fold_cols_kind<EI32>(a, op, vec, s);
+    case Kind::kF32: return fold_cols_kind<EF32>(a, op, vec, s);
+    case Kind::kBF16: return fold_cols_kind<EBF16>(a, op, vec, s);
+    case Kind::kF16: return fold_cols_kind<EF16>(a, op, vec, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gather_cols(const ColsArgs& a, int unit_bytes, int nontemporal, hipStream_t s) {
+  if (a.rows * a.wu == 0) return hipSuccess;
+  const dim3 grid(stream_grid(a.rows * a.wu, static_cast<uint64_t>(kBlock) * 2, a.p, s), a.p);
+  const bool nt = nontemporal != 0;
+  switch (unit_bytes) {
+    case 16: return nt ? launch(&k_gather_cols<16, true>, a, grid, s) : launch(&k_gather_cols<16, false>, a, grid, s);
+    case 4: return nt ? launch(&k_gather_cols<4, true>, a, grid, s) : launch(&k_gather_cols<4, false>, a, grid, s);
+    case 2: return nt ? launch(&k_gather_cols<2, true>, a, grid, s) : launch(&k_gather_cols<2, false>, a, grid, s);
+    case 1: return nt ? launch(&k_gather_cols<1, true>, a, grid, s) : launch(&k_gather_cols<1, false>, a, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace rr

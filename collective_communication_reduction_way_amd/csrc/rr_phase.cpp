@@ -96,7 +96,7 @@ hipError_t launch_mode(const FoldLaunch& f, const PhaseArgs& a, unsigned grid, i
 
 }  // namespace
 
-int phase_default_unroll(Kind k, FoldMode m) { return (m == FoldMode::kHierAll && k == Kind::kBF16) ? 4 : 8; }
+int phase_default_unroll(Kind k, FoldMode m) { return (m == FoldMode::kHierAll && is_half(k)) ? 4 : 8; }
 
 bool phase_supported(const FoldLaunch& f) {
   return (f.mode == FoldMode::kRingAll || f.mode == FoldMode::kHierAll) && f.args.vec &&
@@ -127,10 +127,11 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
   });
   const uint64_t cus = d.cus > 0 ? static_cast<uint64_t>(d.cus) : 256;
   const bool ring = f.mode == FoldMode::kRingAll;
-  const uint64_t V = f.in_kind == Kind::kBF16 ? 8 : 4;
+  const uint64_t V = is_half(f.in_kind) ? 8 : 4;
+  const bool sum_like = f.op == RR_SUM || f.op == RR_AVG;
   bool static_p = pt.static_p >= 0 ? pt.static_p != 0 : ring;
   int unroll = phase_default_unroll(f.in_kind, f.mode);
-  if (pt.unroll == 4 && f.op == RR_SUM) unroll = 4;
+  if (pt.unroll == 4 && sum_like) unroll = 4;
   int per_cu = pt.per_cu > 0 ? pt.per_cu : (unroll == 4 ? 4 : 2);
 
   PhaseArgs a;
@@ -140,11 +141,11 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
   uint64_t tiles = tile_segments(f, V, static_cast<uint64_t>(kBlock) * unroll, a);
   if (tiles >= 0x7FFFFFFFull) return hipErrorInvalidValue;
   uint64_t grid = pt.grid > 0 ? static_cast<uint64_t>(pt.grid) : cus * static_cast<uint64_t>(per_cu);
-  if (ring && pt.unroll == 0 && pt.grid == 0 && f.op == RR_SUM && unroll == 8 && tiles > grid) {
+  if (ring && pt.unroll == 0 && pt.grid == 0 && sum_like && unroll == 8 && tiles > grid) {
     // several rounds: the smaller tile, more workgroups
     unroll = 4;
     if (pt.per_cu <= 0) per_cu = 4;
-    if (pt.static_p < 0) static_p = f.in_kind == Kind::kBF16;
+    if (pt.static_p < 0) static_p = is_half(f.in_kind);
     tiles = tile_segments(f, V, static_cast<uint64_t>(kBlock) * unroll, a);
     if (tiles >= 0x7FFFFFFFull) return hipErrorInvalidValue;
     grid = cus * static_cast<uint64_t>(per_cu);

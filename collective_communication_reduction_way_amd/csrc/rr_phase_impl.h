@@ -182,7 +182,7 @@ __device__ __forceinline__ void read_fold(const FoldArgs& f, int seg, int p, uin
 #pragma unroll
   for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int j = 0; j < V; ++j) acc[u][j] = fold_finish<OP, M>(acc[u][j], tot[u][j], pp, f.group);
+    for (int j = 0; j < V; ++j) acc[u][j] = fold_finish<OP, M>(acc[u][j], tot[u][j], pp, f.group, f.div);
 }
 
 template <bool GUARD, class E, int V, int U>
@@ -315,7 +315,7 @@ template <class E, class OP, int P, FoldMode M, bool SYNC>
 hipError_t phase_by_u(const PhaseArgs& a, unsigned grid, int unroll, int* occ, hipStream_t s) {
   constexpr int kU = phase_unroll<E, M>();
   if (unroll == kU) return phase_go(&k_phase<E, OP, P, kU, M, SYNC>, a, grid, kBlock, occ, s);
-  if constexpr (__is_same(OP, OpSum) && kU != 4) {
+  if constexpr ((__is_same(OP, OpSum) || __is_same(OP, OpAvg)) && kU != 4) {
     if (unroll == 4) return phase_go(&k_phase<E, OP, P, 4, M, SYNC>, a, grid, kBlock, occ, s);
   }
   return hipErrorInvalidValue;
@@ -345,6 +345,10 @@ hipError_t phase_by_op(const PhaseArgs& a, rr_op_t op, unsigned grid, int unroll
     case RR_SUM: return phase_by_p<E, OpSum, M>(a, grid, unroll, sync, static_p, occ, s);
     case RR_MAX: return phase_by_p<E, OpMax, M>(a, grid, unroll, sync, static_p, occ, s);
     case RR_MIN: return phase_by_p<E, OpMin, M>(a, grid, unroll, sync, static_p, occ, s);
+    case RR_AVG:
+      if constexpr (__is_same(typename E::A, float)) return phase_by_p<E, OpAvg, M>(a, grid, unroll, sync, static_p,
+                                                                                      occ, s);
+      break;
   }
   return hipErrorInvalidValue;
 }
@@ -356,6 +360,7 @@ hipError_t phase_dispatch(const PhaseArgs& a, Kind k, rr_op_t op, unsigned grid,
     case Kind::kI32: return phase_by_op<EI32, M>(a, op, grid, unroll, sync, static_p, occ, s);
     case Kind::kF32: return phase_by_op<EF32, M>(a, op, grid, unroll, sync, static_p, occ, s);
     case Kind::kBF16: return phase_by_op<EBF16, M>(a, op, grid, unroll, sync, static_p, occ, s);
+    case Kind::kF16: return phase_by_op<EF16, M>(a, op, grid, unroll, sync, static_p, occ, s);
   }
   return hipErrorInvalidValue;
 }

@@ -57,6 +57,7 @@ size_t elem_size(rr_dtype_t dt) {
     case RR_INT32: return 4;
     case RR_FLOAT32: return 4;
     case RR_BFLOAT16: return 2;
+    case RR_FLOAT16: return 2;
   }
   return 0;
 }
@@ -100,6 +101,11 @@ rr_status_t rr_algorithmic_bytes(rr_coll_t coll, int p, size_t n, rr_dtype_t dty
     case RR_COLL_ALL_GATHER:
     case RR_COLL_REDUCE: *bytes = (P + 1) * ns; return RR_SUCCESS;
     case RR_COLL_BROADCAST: *bytes = ns + (in_place ? (P - 1) : P) * ns; return RR_SUCCESS;
+    case RR_COLL_SCATTER:
+    case RR_COLL_GATHER:
+      if (n % P) return RR_ERROR_INVALID_ARGUMENT;
+      *bytes = in_place ? 2 * (ns / P) * (P - 1) : 2 * ns;
+      return RR_SUCCESS;
   }
   return RR_ERROR_INVALID_ARGUMENT;
 }

@@ -23,6 +23,17 @@
  *   [HIER] page "大模型并行的最小闭环：集合通信、TP、FSDP/ZeRO-3 到权重分片",
  *          section "Source Log: 2026-05-05" (hierarchical AllReduce + SHARP,
  *          steps 1-6 and the traffic comparison).
+ *   [DP]   page "分布式训练/推理", data-parallel section: the gradient is
+ *          averaged over the p ranks, g = (1/p) sum_r grad L_r, by an
+ *          all-reduce with the AVG op (or SUM followed by a division by the
+ *          world size); the gradients are synchronised in flattened buckets.
+ *   [TP]   page "分布式训练/推理", tensor-parallel section: column-parallel
+ *          outputs [B, d/p] are all-gathered and concatenated along dim 1;
+ *          in the scatter strategy each rank's partial [B, D] output is
+ *          summed over ranks and cut into feature slices (psum_scatter).
+ *   [MPI]  page "LLM Parallelism 基础", table of MPI collectives: scatter
+ *          (the root cuts its array into p pieces, one per process) and
+ *          gather (every process's piece collected at the root).
  *
  * Conventions common to every entry point
  * ----------------------------------------
@@ -37,9 +48,15 @@
  *    every buffer selects the 128-bit vector path; otherwise a scalar path
  *    with the same arithmetic order runs, so results are identical.
  *  - Arithmetic: int32 sums wrap modulo 2^32; float32 sums are IEEE-754
- *    round-to-nearest-even additions; bfloat16 inputs are widened exactly to
- *    float32, folded in float32 and rounded once to bfloat16 (nearest even;
- *    a NaN stays NaN, sign kept, made quiet); denormals are kept (no flush).
+ *    round-to-nearest-even additions; bfloat16 and float16 (IEEE binary16)
+ *    inputs are widened exactly to float32, folded in float32 and rounded
+ *    once to their type (nearest even; float16 results below 2^-14 become
+ *    binary16 subnormals and magnitudes that round to 2^16 or more become
+ *    +-inf; a NaN stays NaN, sign kept, made quiet); denormals are kept (no
+ *    flush).  RR_AVG [DP] folds like RR_SUM, in the same order, then divides
+ *    the float32 accumulator by p (one IEEE division, nearest even) before
+ *    the one conversion; it is defined for the float dtypes only (int32 ->
+ *    RR_ERROR_UNSUPPORTED).
  *    max/min are compare-and-select with the running value first: it is
  *    replaced only by a strictly greater (max) / strictly smaller (min)
  *    value, so ties (+0 vs -0) keep the earlier operand, a NaN running value
@@ -84,9 +101,9 @@ extern "C" {
 /* Opaque HIP stream handle (the same type as hipStream_t). */
 typedef struct ihipStream_t* rr_stream_t;
 
-typedef enum { RR_INT32 = 0, RR_FLOAT32 = 1, RR_BFLOAT16 = 2 } rr_dtype_t;
+typedef enum { RR_INT32 = 0, RR_FLOAT32 = 1, RR_BFLOAT16 = 2, RR_FLOAT16 = 3 } rr_dtype_t;
 
-typedef enum { RR_SUM = 0, RR_MAX = 1, RR_MIN = 2 } rr_op_t;
+typedef enum { RR_SUM = 0, RR_MAX = 1, RR_MIN = 2, RR_AVG = 3 } rr_op_t;
 
 typedef enum {
   RR_SUCCESS = 0,
@@ -107,7 +124,9 @@ typedef enum {
   RR_COLL_REDUCE_SCATTER = 1,
   RR_COLL_ALL_GATHER = 2,
   RR_COLL_REDUCE = 3,
-  RR_COLL_BROADCAST = 4
+  RR_COLL_BROADCAST = 4,
+  RR_COLL_SCATTER = 5,
+  RR_COLL_GATHER = 6
 } rr_coll_t;
 
 /*
@@ -133,9 +152,11 @@ rr_status_t rr_all_reduce(const void* const* sendbufs, void* const* recvbufs, in
  *     when not in place): reduce-scatter step s moves chunk (r-1-s) mod p from
  *     rank r to rank r+1 and the receiver stores message (+) local; all-gather
  *     step s moves chunk (r-s) mod p and the receiver overwrites.  Any n (the
- *     chunk bounds above).  For bfloat16 the partial sums live in a float32 workspace of
- *     rr_workspace_size() bytes (one rounding at the end); int32/float32 work
- *     in recvbufs and need no workspace.  Bitwise equal to RR_ALGO_RING_FUSED.
+ *     chunk bounds above).  For bfloat16 and float16 the partial sums live in
+ *     a float32 workspace of rr_workspace_size() bytes (one rounding at the
+ *     end); int32/float32 work in recvbufs and need no workspace.  RR_AVG:
+ *     the owner of each reduced chunk divides it by p before the all-gather
+ *     phase.  Bitwise equal to RR_ALGO_RING_FUSED.
  *   algo = RR_ALGO_HIER_FUSED [HIER]: ranks form p/group_size contiguous groups
  *     [j*G, (j+1)*G) whose representative is rank j*G.  Each group's inputs are
  *     folded ascending in the accumulator type, the group partials are folded
@@ -196,10 +217,83 @@ rr_status_t rr_broadcast(const void* sendbuf, void* const* recvbufs, int root, i
                          rr_dtype_t dtype, rr_stream_t stream);
 
 /*
+ * Scatter [MPI] [SEM]: rank c receives slice c of the root's buffer:
+ * recvbufs[c][j] = sendbuf[c*(n/p) + j].
+ *   sendbuf: the root's input, n elements.  recvbufs[c]: n/p elements.
+ *   Requires p | n.  root: 0 <= root < p; in place allowed:
+ *   recvbufs[root] == sendbuf + root*(n/p) elements (that copy is skipped).
+ *   A bit copy: the dtype only sets the element size.
+ */
+rr_status_t rr_scatter(const void* sendbuf, void* const* recvbufs, int root, int p, size_t n,
+                       rr_dtype_t dtype, rr_stream_t stream);
+
+/*
+ * Gather [MPI] [SEM]: the root receives the p slices in rank order:
+ * recvbuf[c*(n/p) + j] = sendbufs[c][j].
+ *   sendbufs[c]: n/p elements.  recvbuf: the root's output, n elements.
+ *   Requires p | n.  root: 0 <= root < p; in place allowed:
+ *   sendbufs[root] == recvbuf + root*(n/p) elements (that copy is skipped).
+ */
+rr_status_t rr_gather(const void* const* sendbufs, void* recvbuf, int root, int p, size_t n,
+                      rr_dtype_t dtype, rr_stream_t stream);
+
+/*
+ * Bucketed all-reduce [DP]: one call all-reduces a bucket of ntensors tensors
+ * per rank as if they were laid end to end in one buffer, without copying
+ * them into one.
+ *   sendbufs[t*p + r]: tensor t of rank r, counts[t] elements.
+ *   recvbufs[t*p + r]: its output, counts[t] elements.  In place allowed:
+ *   recvbufs[i] == sendbufs[i] (for any i).
+ *   The bucket of rank r is the concatenation of its tensors 0..ntensors-1
+ *   (N = sum of counts elements); its chunk c is [floor(c*N/p),
+ *   floor((c+1)*N/p)) and every element is folded in the ring order of its
+ *   bucket chunk, so the result is bitwise that of rr_all_reduce on the
+ *   concatenated bucket.  Tensors with counts[t] == 0 are skipped (their
+ *   pointers are not read).  Tensors whose 2p pointers are all 16-byte
+ *   aligned take the 128-bit path inside each chunk; the rest move element
+ *   by element (same results).  The host tables are read during the call
+ *   only.  One launch serves up to 96 runs of up to 192/(2p) tensors; longer
+ *   lists take more launches, all on `stream`.
+ *   Returns RR_ERROR_INVALID_ARGUMENT for a negative ntensors, NULL tables,
+ *   NULL or misaligned buffers of non-empty tensors, overlapping outputs or
+ *   an output overlapping any input other than its own exact in-place form,
+ *   a bucket over 2^56 elements; RR_ERROR_UNSUPPORTED for an unknown dtype or
+ *   op and for RR_AVG on int32.
+ */
+rr_status_t rr_all_reduce_bucket(const void* const* sendbufs, void* const* recvbufs, const size_t* counts,
+                                 int ntensors, int p, rr_dtype_t dtype, rr_op_t op, rr_stream_t stream);
+
+/*
+ * All-gather along dim 1 [TP]: every rank receives the row-major
+ * [rows, cols] matrix whose column block c (columns [c*w, (c+1)*w),
+ * w = cols/p) is rank c's row-major [rows, w] matrix:
+ * recvbufs[r][b*cols + c*w + j] = sendbufs[c][b*w + j].
+ *   Requires p | cols.  No in-place form (outputs must not overlap inputs).
+ *   A bit copy: the dtype only sets the element size; 16-byte units when
+ *   every address and w*s allow, else 4-, 2- or 1-byte units.
+ */
+rr_status_t rr_all_gather_dim1(const void* const* sendbufs, void* const* recvbufs, int p, size_t rows,
+                               size_t cols, rr_dtype_t dtype, rr_stream_t stream);
+
+/*
+ * Reduce-scatter along dim 1 [TP] (psum_scatter of partial outputs): rank c
+ * receives the row-major [rows, w] feature slice c (w = cols/p) of the
+ * reduction of the p row-major [rows, cols] inputs:
+ * recvbufs[c][b*w + j] = x_{c+1} (+) x_{c+2} (+) ... (+) x_c at
+ * [b, c*w + j] (ring order of chunk c of the feature dimension; AVG divides
+ * by p after the fold).
+ *   Requires p | cols.  No in-place form.  The 128-bit path needs every
+ *   buffer 16-byte aligned and w*s a multiple of 16 bytes; otherwise the
+ *   element path runs with the same results.
+ */
+rr_status_t rr_reduce_scatter_dim1(const void* const* sendbufs, void* const* recvbufs, int p, size_t rows,
+                                   size_t cols, rr_dtype_t dtype, rr_op_t op, rr_stream_t stream);
+
+/*
  * Workspace bytes that rr_all_reduce_ex needs for (algo, p, group_size, n,
  * dtype): 0 for the fused algorithms and for the staged ring on int32/float32;
- * p*n*4 for the staged ring on bfloat16; (p/group_size)*n*4 for the staged
- * hierarchy.  Returns 0 for invalid arguments as well (rr_all_reduce_ex then
+ * p*n*4 for the staged ring on bfloat16 and float16; (p/group_size)*n*4 for
+ * the staged hierarchy.  Returns 0 for invalid arguments as well (rr_all_reduce_ex then
  * reports them).
  */
 size_t rr_workspace_size(rr_algo_t algo, int p, int group_size, size_t n, rr_dtype_t dtype);

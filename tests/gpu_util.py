@@ -9,7 +9,8 @@ from oracle import collectives as C
 def torch_dtype(dtype):
     import torch
 
-    return {"int32": torch.int32, "float32": torch.float32, "bfloat16": torch.bfloat16}[dtype]
+    return {"int32": torch.int32, "float32": torch.float32, "bfloat16": torch.bfloat16,
+            "float16": torch.float16}[dtype]
 
 
 def to_dev(arr, dtype, device="cuda"):
@@ -17,19 +18,19 @@ def to_dev(arr, dtype, device="cuda"):
     import torch
 
     arr = np.ascontiguousarray(arr)
-    if dtype == "bfloat16":
-        t = torch.from_numpy(arr.view(np.int16).copy()).view(torch.bfloat16)
+    if dtype in ("bfloat16", "float16"):
+        t = torch.from_numpy(arr.view(np.int16).copy()).view(torch_dtype(dtype))
     else:
         t = torch.from_numpy(arr.copy())
     return t.to(device)
 
 
 def to_host(t, dtype):
-    """Device tensor -> numpy storage array (bf16 as uint16 bit patterns)."""
+    """Device tensor -> numpy storage array (16-bit floats as uint16 bit patterns)."""
     import torch
 
     t = t.detach().cpu().contiguous()
-    if dtype == "bfloat16":
+    if dtype in ("bfloat16", "float16"):
         return t.view(torch.int16).numpy().view(np.uint16).copy()
     return t.numpy().copy()
 

@@ -177,7 +177,7 @@ def test_all_gather_validation():
     send = ptrs(FAKE, 4, 1 << 20)
     recv = ptrs(FAKE + (1 << 30), 4, 1 << 20)
     assert L.rr_all_gather(send, recv, 4, 1001, 1, None) == INVALID
-    assert L.rr_all_gather(send, recv, 4, 1024, 3, None) == UNSUPPORTED
+    assert L.rr_all_gather(send, recv, 4, 1024, 7, None) == UNSUPPORTED
     # a shard inside another rank's output
     bad = rr._ptr_array([FAKE + (1 << 30) + (1 << 20), FAKE + (6 << 30), FAKE + (7 << 30), FAKE + (8 << 30)])
     assert L.rr_all_gather(bad, recv, 4, 1024, 1, None) == INVALID
@@ -191,7 +191,8 @@ def test_reduce_validation():
     assert L.rr_reduce(send, 0, 0, 4, 64, 1, 0, None) == INVALID
     # output on a non-root input
     assert L.rr_reduce(send, FAKE + (1 << 20), 0, 4, 64, 1, 0, None) == INVALID
-    assert L.rr_reduce(send, FAKE + (1 << 30), 0, 4, 64, 1, 3, None) == UNSUPPORTED
+    assert L.rr_reduce(send, FAKE + (1 << 30), 0, 4, 64, 1, 9, None) == UNSUPPORTED
+    assert L.rr_reduce(send, FAKE + (1 << 30), 0, 4, 64, 0, 3, None) == UNSUPPORTED  # AVG over int32
 
 
 def test_broadcast_validation():
@@ -211,3 +212,67 @@ def test_last_error_is_per_call():
     assert st == INVALID and msg
     assert ar(n=0)[0] == 0
     assert rr.lib().rr_last_error() == b""
+
+
+def test_avg_is_float_only():
+    """AVG over int32 is refused for every reducing entry point; over the
+    float dtypes it passes dtype/op validation (an invalid p then decides)."""
+    L = rr.lib()
+    send = ptrs(FAKE, 4, 1 << 20)
+    recv = ptrs(FAKE + (1 << 30), 4, 1 << 20)
+    assert ar(dt=0, op=3)[0] == UNSUPPORTED
+    for algo in (1, 2, 3):
+        assert ar(dt=0, op=3, algo=algo, group=2)[0] == UNSUPPORTED
+    assert L.rr_reduce_scatter(send, recv, 4, 1024, 0, 3, None) == UNSUPPORTED
+    for dt in (1, 2, 3):
+        assert ar(p=0, dt=dt, op=3)[0] == INVALID
+        assert ar(n=0, dt=dt, op=3)[0] == 0
+
+
+def test_float16_dtype():
+    """float16 is a known dtype of element size 2 (misaligned by 2 bytes is
+    fine, by 1 is not)."""
+    L = rr.lib()
+    assert ar(dt=3, p=0)[0] == INVALID
+    assert ar(dt=3, n=0)[0] == 0
+    odd = rr._ptr_array([FAKE + 1] + [FAKE + (r << 20) for r in range(1, 4)])
+    assert ar(dt=3, send=odd)[0] == INVALID
+    out = (ctypes.c_uint64 * 1)()
+    assert L.rr_algorithmic_bytes(0, 8, 1000, 3, 0, out) == 0 and out[0] == 2 * 8 * 1000 * 2
+    assert rr.workspace_size("ring_staged", 8, 0, 1000, "float16") == 8 * 1000 * 4
+    assert rr.workspace_size("ring_staged", 8, 0, 1000, "bfloat16") == 8 * 1000 * 4
+    assert rr.workspace_size("ring_staged", 8, 0, 1000, "float32") == 0
+
+
+def test_scatter_validation():
+    L = rr.lib()
+    recv = ptrs(FAKE + (1 << 30), 4, 1 << 20)
+    for root in (-1, 4):
+        assert L.rr_scatter(FAKE, recv, root, 4, 64, 1, None) == INVALID
+    assert L.rr_scatter(FAKE, recv, 0, 4, 66, 1, None) == INVALID  # p does not divide n
+    assert L.rr_scatter(0, recv, 0, 4, 64, 1, None) == INVALID
+    assert L.rr_scatter(FAKE, None, 0, 4, 64, 1, None) == INVALID
+    assert L.rr_scatter(FAKE, recv, 0, 4, 64, 7, None) == UNSUPPORTED
+    assert L.rr_scatter(FAKE, recv, 0, 4, 0, 1, None) == 0
+    # a slice output inside the root's buffer at the wrong slot
+    bad = rr._ptr_array([FAKE + 16 * 4, FAKE + (2 << 30), FAKE + (3 << 30), FAKE + (4 << 30)])
+    assert L.rr_scatter(FAKE, bad, 0, 4, 64, 1, None) == INVALID
+    # two outputs overlapping
+    bad = rr._ptr_array([FAKE + (1 << 30), FAKE + (1 << 30) + 8, FAKE + (3 << 30), FAKE + (4 << 30)])
+    assert L.rr_scatter(FAKE, bad, 0, 4, 64, 1, None) == INVALID
+
+
+def test_gather_validation():
+    L = rr.lib()
+    send = ptrs(FAKE, 4, 1 << 20)
+    for root in (-1, 4):
+        assert L.rr_gather(send, FAKE + (1 << 30), root, 4, 64, 1, None) == INVALID
+    assert L.rr_gather(send, FAKE + (1 << 30), 0, 4, 66, 1, None) == INVALID
+    assert L.rr_gather(send, 0, 0, 4, 64, 1, None) == INVALID
+    assert L.rr_gather(None, FAKE + (1 << 30), 0, 4, 64, 1, None) == INVALID
+    assert L.rr_gather(send, FAKE + (1 << 30), 0, 4, 64, 7, None) == UNSUPPORTED
+    # the output over rank 1's slice source
+    assert L.rr_gather(send, FAKE + (1 << 20), 0, 4, 64, 1, None) == INVALID
+    out = (ctypes.c_uint64 * 1)()
+    assert L.rr_algorithmic_bytes(5, 4, 64, 1, 0, out) == 0 and out[0] == 2 * 64 * 4
+    assert L.rr_algorithmic_bytes(6, 4, 64, 1, 1, out) == 0 and out[0] == 2 * 48 * 4

@@ -1,0 +1,224 @@
+"""GPU parity of the AVG op and the float16 dtype against the CPU oracle
+(calls go through the C ABI).
+
+AVG is the op's sum fold in the op's order, one IEEE division of the float32
+accumulator by p and one conversion; float16 is widened exactly, folded in
+float32 and rounded once (nearest even, subnormals kept, overflow to inf).
+Both sides take the same steps in the same order, so every comparison is
+bit for bit.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle_pins as PIN
+import workloads as W
+from gpu_util import assert_bitwise, to_dev, to_host
+from oracle import collectives as C
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+FLOATS = ("float32", "bfloat16", "float16")
+
+
+@pytest.fixture(scope="module")
+def rr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import collective_communication_reduction_way_amd as mod
+
+    mod.lib()
+    return mod
+
+
+def run_all_reduce(rr, x, dtype, op, algo, G=0):
+    xs = to_dev(x, dtype)
+    out = torch.empty_like(xs)
+    rr.all_reduce(xs, out, op=op, algo=algo, group_size=G)
+    return to_host(out, dtype)
+
+
+def oracle_all_reduce(x, dtype, op, algo, G=0):
+    if algo.startswith("hier"):
+        return C.all_reduce_hier(x, op, dtype, G)
+    return C.all_reduce_fold(x, op, dtype)
+
+
+ALGOS = (("ring", 0), ("ring_staged", 0), ("hier", 1), ("hier", 2), ("hier", 4), ("hier_staged", 2),
+         ("hier_staged", 4))
+
+
+@pytest.mark.parametrize("dtype", FLOATS)
+def test_avg_worked_example(rr, dtype):
+    """The worked example averages to [1.5, 2.5, 3.5, 4.5] on every rank, by
+    every algorithm, and reduce-scatter / reduce give the same values."""
+    g = json.load(open(os.path.join(GOLDEN, "worked_example.json"), encoding="utf-8"))
+    x = PIN.enc(g["inputs"], dtype)
+    want = PIN.enc([[1.5, 2.5, 3.5, 4.5]] * 4, dtype)
+    for algo, G in ALGOS:
+        assert_bitwise(run_all_reduce(rr, x, dtype, "avg", algo, G), want, f"{algo} G={G}")
+    xs = to_dev(x, dtype)
+    sh = torch.empty((4, 1), dtype=xs.dtype, device="cuda")
+    rr.reduce_scatter(xs, sh, op="avg")
+    assert_bitwise(to_host(sh, dtype).ravel(), want[0], "reduce_scatter avg")
+    red = torch.empty(4, dtype=xs.dtype, device="cuda")
+    rr.reduce(xs, red, op="avg")
+    assert_bitwise(to_host(red, dtype), want[0], "reduce avg")
+
+
+def test_avg_division_probes(rr):
+    """fl(5/3) = 0x3FD55555 (a multiplication by a rounded 1/3 would give
+    0x3FD55556); fl(7/3) = 0x40155555 (dividing each term would give
+    0x40155556); bf16 [1, 1.5, 2^-7] averages to 0x3F56 (rounding the sum
+    to bf16 first would give 0x3F55)."""
+    for vals, want in (([1.0, 2.0, 2.0], 0x3FD55555), ([2.0, 1.0, 4.0], 0x40155555)):
+        x = np.array([[v] * 3 for v in vals], dtype=np.float32)
+        for algo, G in (("ring", 0), ("ring_staged", 0), ("hier", 1), ("hier", 3), ("hier_staged", 1)):
+            got = run_all_reduce(rr, x, "float32", "avg", algo, G)
+            assert np.all(got.view(np.uint32) == want), (vals, algo, G, [hex(v) for v in got.view(np.uint32).ravel()])
+        xs = to_dev(x, "float32")
+        sh = torch.empty((3, 1), dtype=torch.float32, device="cuda")
+        rr.reduce_scatter(xs, sh, op="avg")
+        assert np.all(to_host(sh, "float32").view(np.uint32) == want)
+        red = torch.empty(3, dtype=torch.float32, device="cuda")
+        rr.reduce(xs, red, op="avg")
+        assert np.all(to_host(red, "float32").view(np.uint32) == want)
+    xb = PIN.enc([[1.0] * 3, [1.5] * 3, [2.0 ** -7] * 3], "bfloat16")
+    for algo, G in (("ring", 0), ("ring_staged", 0), ("hier", 3), ("hier_staged", 1)):
+        got = run_all_reduce(rr, xb, "bfloat16", "avg", algo, G)
+        assert np.all(got == 0x3F56), (algo, G, [hex(v) for v in got.ravel()])
+
+
+AVG_SWEEP = [(2, 1000), (3, 4099), (5, 77777), (8, 262147), (6, 5), (64, 6400), (1, 1000), (7, 1)]
+
+
+@pytest.mark.parametrize("p,n", AVG_SWEEP)
+@pytest.mark.parametrize("dtype", FLOATS)
+def test_sweep_avg(rr, p, n, dtype):
+    x = W.random_inputs(21, p, n, dtype)
+    for algo, G in (("ring", 0), ("ring_staged", 0)) + tuple(
+            (a, g) for a in ("hier", "hier_staged") for g in (1, 2, p) if p % g == 0):
+        assert_bitwise(run_all_reduce(rr, x, dtype, "avg", algo, G), oracle_all_reduce(x, dtype, "avg", algo, G),
+                       f"{algo} G={G}")
+    xs = to_dev(x, dtype)
+    red = torch.empty(n, dtype=xs.dtype, device="cuda")
+    rr.reduce(xs, red, op="avg", root=p - 1)
+    assert_bitwise(to_host(red, dtype), C.reduce(x, "avg", dtype), "reduce avg")
+    if n % p == 0:
+        sh = torch.empty((p, n // p), dtype=xs.dtype, device="cuda")
+        rr.reduce_scatter(xs, sh, op="avg")
+        assert_bitwise(to_host(sh, dtype), C.reduce_scatter_ring(x, "avg", dtype), "reduce_scatter avg")
+
+
+FP16_SWEEP = [(2, 1000), (3, 4099), (4, 65536 + 12), (8, 262147), (16, 40000), (6, 5), (64, 6400), (1, 1000)]
+
+
+@pytest.mark.parametrize("p,n", FP16_SWEEP)
+def test_sweep_float16(rr, p, n):
+    """Every op over float16, normal values and every finite bit pattern."""
+    for kind in ("normal", "fp16_patterns"):
+        x = W.random_inputs(22, p, n, "float16", kind=kind)
+        for op in ("sum", "max", "min", "avg"):
+            for algo, G in (("ring", 0), ("ring_staged", 0)) + tuple(
+                    (a, g) for a in ("hier", "hier_staged") for g in (1, 2, p) if p % g == 0):
+                assert_bitwise(run_all_reduce(rr, x, "float16", op, algo, G),
+                               oracle_all_reduce(x, "float16", op, algo, G), f"{kind} {algo} G={G} {op}")
+            xs = to_dev(x, "float16")
+            red = torch.empty(n, dtype=torch.float16, device="cuda")
+            rr.reduce(xs, red, op=op)
+            assert_bitwise(to_host(red, "float16"), C.reduce(x, op, "float16"), f"{kind} reduce {op}")
+
+
+@pytest.mark.parametrize("p,L", [(2, 1), (3, 5), (4, 4096), (8, 16411), (64, 64)])
+def test_float16_reduce_scatter_all_gather(rr, p, L):
+    n = p * L
+    x = W.random_inputs(23, p, n, "float16", kind="fp16_patterns")
+    for op in ("sum", "max", "min", "avg"):
+        want = C.reduce_scatter_ring(x, op, "float16")
+        xs = to_dev(x, "float16")
+        sh = torch.empty((p, L), dtype=torch.float16, device="cuda")
+        rr.reduce_scatter(xs, sh, op=op)
+        assert_bitwise(to_host(sh, "float16"), want, f"reduce_scatter {op}")
+        full = torch.empty_like(xs)
+        rr.all_gather(sh, full)
+        assert_bitwise(to_host(full, "float16"), C.all_gather(want), "all_gather")
+
+
+def test_float16_rounding_cases(rr):
+    """Sums that land on the rounding cases of binary16: ties to even, the
+    largest finite value, the midpoint to 2^16 (inf), subnormal results and
+    their ties, signed zeros."""
+    pairs = [
+        (1.0, 2.0 ** -11),            # 1 + 2^-11: tie, even neighbour 1
+        (1.0, 3 * 2.0 ** -11),        # tie, even neighbour 1 + 2^-9
+        (65504.0, 8.0),               # below the midpoint: 65504
+        (65504.0, 16.0),              # the midpoint 65520: inf
+        (-65504.0, -32.0),            # -inf
+        (2.0 ** -24, 2.0 ** -24),     # subnormal 2^-23
+        (2.0 ** -14, -(2.0 ** -24)),  # largest subnormal
+        (2.0 ** -24, -(2.0 ** -24)),  # +0
+        (-0.0, -0.0),                 # -0
+        (0.5, 2.0 ** -12),            # 0.5 + 2^-12: tie between 0.5 and 0.5 + 2^-11 -> 0.5
+        (2.0 ** -15, 2.0 ** -25 * 0),  # subnormal passes through
+    ]
+    x = PIN.enc([[a for a, _ in pairs], [b for _, b in pairs]], "float16")
+    for op in ("sum", "avg", "max", "min"):
+        for algo, G in (("ring", 0), ("ring_staged", 0), ("hier", 2), ("hier_staged", 1)):
+            assert_bitwise(run_all_reduce(rr, x, "float16", op, algo, G), oracle_all_reduce(x, "float16", op, algo, G),
+                           f"{algo} {op}")
+    y = run_all_reduce(rr, x, "float16", "sum", "ring")[0]
+    assert y[3] == 0x7C00 and y[4] == 0xFC00 and y[2] == 0x7BFF, [hex(v) for v in y]
+    assert y[0] == 0x3C00 and y[1] == 0x3C02 and y[5] == 0x0002 and y[6] == 0x03FF, [hex(v) for v in y]
+    assert y[7] == 0x0000 and y[8] == 0x8000, [hex(v) for v in y]
+
+
+@pytest.mark.parametrize("op", ("sum", "avg"))
+def test_float16_multi_round_phased(rr, op):
+    """Sizes that take several rounds of the phased fold, with ragged chunk
+    bounds, for the ring and the hierarchy."""
+    p, n = 8, 2 * (8 * (1 << 20) + 8 * 3 + 5) + 1
+    x = W.random_inputs(24, p, n, "float16")
+    t0 = rr.barrier_timeouts()
+    assert_bitwise(run_all_reduce(rr, x, "float16", op, "ring"), C.all_reduce_fold(x, op, "float16"), "ring")
+    assert_bitwise(run_all_reduce(rr, x, "float16", op, "hier", 4), C.all_reduce_hier(x, op, "float16", 4), "hier")
+    assert rr.barrier_timeouts() == t0
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ("float32", "bfloat16"))
+def test_avg_multi_round_phased(rr, dtype):
+    p, n = 8, 8 * (1 << 20) * (2 if dtype == "bfloat16" else 1) + 8 * 7 + 3
+    x = W.random_inputs(25, p, n, dtype)
+    assert_bitwise(run_all_reduce(rr, x, dtype, "avg", "ring"), C.all_reduce_fold(x, "avg", dtype), "ring")
+    assert_bitwise(run_all_reduce(rr, x, dtype, "avg", "hier", 2), C.all_reduce_hier(x, "avg", dtype, 2), "hier")
+    torch.cuda.empty_cache()
+
+
+def test_avg_int32_is_rejected(rr):
+    xs = torch.ones((4, 64), dtype=torch.int32, device="cuda")
+    out = torch.full_like(xs, 7)
+    with pytest.raises(rr.RRError):
+        rr.all_reduce(xs, out, op="avg")
+    torch.cuda.synchronize()
+    assert torch.all(out == 7)
+
+
+def test_unaligned_float16(rr):
+    """float16 rank buffers offset by one element take the scalar path with the
+    same bits."""
+    p, n = 4, 10007
+    x = W.random_inputs(26, p, n + 3, "float16", kind="fp16_patterns")
+    base = to_dev(x, "float16")
+    ins = [base[r, 1:1 + n] for r in range(p)]
+    outbuf = torch.empty((p, n + 1), dtype=torch.float16, device="cuda")
+    outs = [outbuf[r, 1:1 + n] for r in range(p)]
+    shifted = np.ascontiguousarray(x[:, 1:1 + n])
+    for op in ("sum", "avg"):
+        rr.all_reduce(ins, outs, op=op)
+        got = np.stack([to_host(o, "float16") for o in outs])
+        assert_bitwise(got, C.all_reduce_fold(shifted, op, "float16"), f"all_reduce {op}")
