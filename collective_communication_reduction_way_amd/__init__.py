@@ -35,6 +35,10 @@ __all__ = [
     "all_reduce_bucket",
     "all_gather_dim1",
     "reduce_scatter_dim1",
+    "all_reduce_hier",
+    "hier_workspace_size",
+    "cost_ring_all_reduce",
+    "cost_hier_all_reduce",
     "workspace_size",
     "ring_schedule",
     "chunk_bounds",
@@ -56,6 +60,11 @@ ALGOS = {"ring": 0, "ring_staged": 1, "hier": 2, "hier_staged": 3}
 COLLS = {"all_reduce": 0, "reduce_scatter": 1, "all_gather": 2, "reduce": 3, "broadcast": 4, "scatter": 5,
          "gather": 6}
 MAX_RANKS = 64
+HIER_INTRA_RING, HIER_WIRE_ROUND, HIER_STAGED = 1, 2, 4
+
+
+class _Link(ctypes.Structure):
+    _fields_ = [("alpha_s", ctypes.c_double), ("bytes_per_s", ctypes.c_double)]
 
 _lib = None
 
@@ -102,6 +111,11 @@ def lib():
         "rr_all_reduce_bucket": (I, [PP, PP, ctypes.POINTER(ctypes.c_size_t), I, I, I, I, P]),
         "rr_all_gather_dim1": (I, [PP, PP, I, S, S, I, P]),
         "rr_reduce_scatter_dim1": (I, [PP, PP, I, S, S, I, I, P]),
+        "rr_all_reduce_hier": (I, [PP, PP, I, S, I, I, I, I, P, S, P]),
+        "rr_hier_workspace_size": (S, [I, I, S, I, I]),
+        "rr_cost_ring_all_reduce": (I, [I, ctypes.c_double, _Link, ctypes.POINTER(ctypes.c_double)]),
+        "rr_cost_hier_all_reduce": (I, [I, ctypes.c_double, _Link, _Link, ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_double), IP]),
         "rr_workspace_size": (S, [I, I, I, S, I]),
         "rr_ring_schedule": (I, [I, IP, IP, IP, IP, IP, I]),
         "rr_chunk_bounds": (I, [I, S, ctypes.POINTER(ctypes.c_size_t)]),
@@ -397,6 +411,71 @@ def reduce_scatter_dim1(ins, outs, op="sum", stream=None):
                                   p, rows, cols, _dtype_code(ins[0]), _op(op), _stream(ins[0], stream))
     _check(st, "rr_reduce_scatter_dim1")
     return outs
+
+
+def _hier_flags(intra, wire_round, staged):
+    if intra not in ("reduce", "ring"):
+        raise ValueError(f"unknown intra-group step {intra!r}; use 'reduce' or 'ring'")
+    return (HIER_INTRA_RING if intra == "ring" else 0) | (HIER_WIRE_ROUND if wire_round else 0) | (
+        HIER_STAGED if staged else 0)
+
+
+def all_reduce_hier(ins, outs=None, op="sum", group_size=1, intra="reduce", wire_round=False, staged=False,
+                    workspace=None, stream=None):
+    """Hierarchical all-reduce over groups of ``group_size`` consecutive ranks.
+
+    intra="ring" forms each group's partial by a ring all-reduce inside the
+    group; wire_round=True rounds every group partial to the storage type
+    before the cross-group fold; staged=True runs the steps one by one
+    through a workspace (allocated with torch when not given).
+    """
+    import torch
+
+    ins = _ranks(ins, "all_reduce_hier inputs")
+    outs = ins if outs is None else _ranks(outs, "all_reduce_hier outputs")
+    p, n = len(ins), ins[0].numel()
+    if len(outs) != p or any(o.numel() != n or o.dtype != ins[0].dtype for o in outs):
+        raise ValueError("all_reduce_hier: outputs must match the inputs in count, length and dtype")
+    flags = _hier_flags(intra, wire_round, staged)
+    need = hier_workspace_size(p, group_size, n, ins[0].dtype, intra, wire_round, staged)
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=ins[0].device)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    st = lib().rr_all_reduce_hier(_ptr_array([t.data_ptr() for t in ins]), _ptr_array([t.data_ptr() for t in outs]),
+                                  p, n, _dtype_code(ins[0]), _op(op), int(group_size), flags, ws_ptr, ws_bytes,
+                                  _stream(ins[0], stream))
+    _check(st, "rr_all_reduce_hier")
+    return outs
+
+
+def hier_workspace_size(p, group_size, n, dtype, intra="reduce", wire_round=False, staged=False):
+    """Bytes of workspace rr_all_reduce_hier needs (0 unless staged)."""
+    import torch
+
+    if isinstance(dtype, torch.dtype):
+        dtype = _dtype_name(dtype)
+    return int(lib().rr_hier_workspace_size(int(p), int(group_size), int(n), DTYPES[dtype],
+                                            _hier_flags(intra, wire_round, staged)))
+
+
+def cost_ring_all_reduce(p, nbytes, alpha_s, bytes_per_s):
+    """Seconds the alpha-beta model gives a ring all-reduce of ``nbytes`` per rank."""
+    out = ctypes.c_double()
+    _check(lib().rr_cost_ring_all_reduce(int(p), float(nbytes), _Link(alpha_s, bytes_per_s), ctypes.byref(out)),
+           "rr_cost_ring_all_reduce")
+    return out.value
+
+
+def cost_hier_all_reduce(group_size, nbytes, fast, slow):
+    """(t_flat, t_hier, use_hier) of the hierarchy's time model; ``fast`` and
+    ``slow`` are (alpha_s, bytes_per_s) pairs."""
+    tf, th, use = ctypes.c_double(), ctypes.c_double(), ctypes.c_int()
+    _check(lib().rr_cost_hier_all_reduce(int(group_size), float(nbytes), _Link(*fast), _Link(*slow),
+                                         ctypes.byref(tf), ctypes.byref(th), ctypes.byref(use)),
+           "rr_cost_hier_all_reduce")
+    return tf.value, th.value, bool(use.value)
 
 
 def workspace_size(algo, p, group_size, n, dtype):

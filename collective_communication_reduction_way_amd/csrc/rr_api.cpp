@@ -291,10 +291,20 @@ rr_status_t ar_ring_fused(const void* const* send, void* const* recv, int p, uin
   return run_fold(t, "all_reduce(ring, fused)", f, s);
 }
 
+// The fold mode of a hierarchical all-reduce with variant flags.  Rounding a
+// partial to a 4-byte storage type is the identity, so the wire modes are
+// used for the 16-bit types only.
+rr::FoldMode hier_mode(rr_dtype_t dt, int flags) {
+  const bool ring = flags & RR_HIER_INTRA_RING;
+  const bool wire = (flags & RR_HIER_WIRE_ROUND) && is_half_dtype(dt);
+  if (ring) return wire ? rr::FoldMode::kHierRingWire : rr::FoldMode::kHierRing;
+  return wire ? rr::FoldMode::kHierAllWire : rr::FoldMode::kHierAll;
+}
+
 rr_status_t ar_hier_fused(const void* const* send, void* const* recv, int p, uint64_t n, rr_dtype_t dt, rr_op_t op,
-                          int G, const Tuning& t, hipStream_t s) {
+                          int G, int flags, const Tuning& t, hipStream_t s) {
   rr::FoldLaunch f = base_fold(t);
-  f.mode = rr::FoldMode::kHierAll;
+  f.mode = hier_mode(dt, flags);
   f.in_kind = f.out_kind = kind_of(dt);
   f.op = op;
   f.segments = 1;
@@ -302,6 +312,11 @@ rr_status_t ar_hier_fused(const void* const* send, void* const* recv, int p, uin
   f.args.p = p;
   f.args.group = G;
   f.args.div = divisor_for(op, p);
+  if (rr::is_hier_ring(f.mode)) {
+    // rows = the G group-chunks, bounds floor(k*n/G)
+    f.segments = G;
+    rr::chunk_bounds(G, n, f.args.bound);
+  }
   bool vec = true;
   for (int r = 0; r < p; ++r) {
     f.args.in[r] = send[r];
@@ -438,15 +453,20 @@ rr_status_t ar_ring_staged(const void* const* send, void* const* recv, int p, ui
 }
 
 rr_status_t ar_hier_staged(const void* const* send, void* const* recv, int p, uint64_t n, rr_dtype_t dt, rr_op_t op,
-                           int G, void* ws, const Tuning& t, hipStream_t s) {
+                           int G, int flags, void* ws, const Tuning& t, hipStream_t s) {
   const int J = p / G;
   const size_t esz = rr::elem_size(dt);
+  // With wire rounding the partials cross groups in the storage type.
+  const bool wire = (flags & RR_HIER_WIRE_ROUND) && is_half_dtype(dt);
+  const Kind part_kind = wire ? kind_of(dt) : acc_kind_of(dt);
+  const uint64_t part_bytes = wire ? esz : 4;
   // Steps 1-2: each group reduces into its representative's partial
-  // (accumulator type, in the workspace).
+  // (accumulator type, or the storage type with wire rounding, in the
+  // workspace).
   rr::FoldLaunch f1 = base_fold(t);
   f1.mode = rr::FoldMode::kAscOne;
   f1.in_kind = kind_of(dt);
-  f1.out_kind = acc_kind_of(dt);
+  f1.out_kind = part_kind;
   f1.op = op == RR_AVG ? RR_SUM : op;  // group partials; AVG divides at the end
   f1.segments = J;
   f1.args.n = n;
@@ -457,7 +477,7 @@ rr_status_t ar_hier_staged(const void* const* send, void* const* recv, int p, ui
     f1.args.in[r] = send[r];
     vec = vec && aligned16(send[r]) && aligned16(recv[r]);
   }
-  for (int j = 0; j < J; ++j) f1.args.out[j] = static_cast<char*>(ws) + static_cast<uint64_t>(j) * n * 4;
+  for (int j = 0; j < J; ++j) f1.args.out[j] = static_cast<char*>(ws) + static_cast<uint64_t>(j) * n * part_bytes;
   f1.args.vec = vec ? 1 : 0;
   rr_status_t st = run_fold(t, "all_reduce(hierarchical, staged): group reduce", f1, s);
   if (st) return st;
@@ -465,7 +485,7 @@ rr_status_t ar_hier_staged(const void* const* send, void* const* recv, int p, ui
   // the result lands at every representative.
   rr::FoldLaunch f2 = base_fold(t);
   f2.mode = rr::FoldMode::kHierAll;
-  f2.in_kind = acc_kind_of(dt);
+  f2.in_kind = part_kind;
   f2.out_kind = kind_of(dt);
   f2.op = op;
   f2.segments = 1;
@@ -497,21 +517,22 @@ rr_status_t ar_hier_staged(const void* const* send, void* const* recv, int p, ui
   return RR_SUCCESS;
 }
 
-size_t workspace_bytes(rr_algo_t algo, int p, int G, uint64_t n, rr_dtype_t dt) {
+size_t workspace_bytes(rr_algo_t algo, int p, int G, uint64_t n, rr_dtype_t dt, int flags = 0) {
   switch (algo) {
     case RR_ALGO_RING_STAGED: return is_half_dtype(dt) ? static_cast<size_t>(p) * n * 4 : 0;
-    case RR_ALGO_HIER_STAGED: return static_cast<size_t>(p / G) * n * 4;
+    case RR_ALGO_HIER_STAGED: {
+      const bool wire = (flags & RR_HIER_WIRE_ROUND) && is_half_dtype(dt);
+      return static_cast<size_t>(p / G) * n * (wire ? rr::elem_size(dt) : 4);
+    }
     default: return 0;
   }
 }
 
-}  // namespace
-
-extern "C" {
-
-rr_status_t rr_all_reduce_ex(const void* const* sendbufs, void* const* recvbufs, int p, size_t n, rr_dtype_t dtype,
-                             rr_op_t op, rr_algo_t algo, int group_size, void* workspace, size_t ws_bytes,
-                             rr_stream_t stream) {
+// rr_all_reduce_ex and rr_all_reduce_hier: `flags` holds the hierarchical
+// variant bits (0 for the ring algorithms).
+rr_status_t all_reduce_impl(const void* const* sendbufs, void* const* recvbufs, int p, size_t n, rr_dtype_t dtype,
+                            rr_op_t op, rr_algo_t algo, int group_size, int flags, void* workspace,
+                            size_t ws_bytes, rr_stream_t stream) {
   rr_status_t st;
   if ((st = check_p(p)) || (st = check_dtype(dtype)) || (st = check_op_dtype(op, dtype)) || (st = check_n(n)))
     return st;
@@ -523,7 +544,7 @@ rr_status_t rr_all_reduce_ex(const void* const* sendbufs, void* const* recvbufs,
     return fail(RR_ERROR_INVALID_ARGUMENT, "group_size=%d must be in [1, p] and divide p=%d", group_size, p);
   const size_t esz = rr::elem_size(dtype);
   if ((st = check_rank_arrays(sendbufs, recvbufs, p, esz, n))) return st;
-  const size_t need = workspace_bytes(algo, p, hier ? group_size : 1, n, dtype);
+  const size_t need = workspace_bytes(algo, p, hier ? group_size : 1, n, dtype, flags);
   if (need > 0 && n > 0) {
     if (!workspace) return fail(RR_ERROR_INVALID_ARGUMENT, "algo %d needs %zu bytes of workspace", algo, need);
     if (ws_bytes < need)
@@ -552,12 +573,43 @@ rr_status_t rr_all_reduce_ex(const void* const* sendbufs, void* const* recvbufs,
   switch (algo) {
     case RR_ALGO_RING_FUSED: st = ar_ring_fused(sendbufs, recvbufs, p, n, dtype, op, t, s); break;
     case RR_ALGO_RING_STAGED: st = ar_ring_staged(sendbufs, recvbufs, p, n, dtype, op, workspace, t, s); break;
-    case RR_ALGO_HIER_FUSED: st = ar_hier_fused(sendbufs, recvbufs, p, n, dtype, op, group_size, t, s); break;
+    case RR_ALGO_HIER_FUSED:
+      st = ar_hier_fused(sendbufs, recvbufs, p, n, dtype, op, group_size, flags, t, s);
+      break;
     case RR_ALGO_HIER_STAGED:
-      st = ar_hier_staged(sendbufs, recvbufs, p, n, dtype, op, group_size, workspace, t, s);
+      st = ar_hier_staged(sendbufs, recvbufs, p, n, dtype, op, group_size, flags, workspace, t, s);
       break;
   }
   return st ? st : ok();
+}
+
+constexpr int kHierFlags = RR_HIER_INTRA_RING | RR_HIER_WIRE_ROUND | RR_HIER_STAGED;
+
+}  // namespace
+
+extern "C" {
+
+rr_status_t rr_all_reduce_ex(const void* const* sendbufs, void* const* recvbufs, int p, size_t n, rr_dtype_t dtype,
+                             rr_op_t op, rr_algo_t algo, int group_size, void* workspace, size_t ws_bytes,
+                             rr_stream_t stream) {
+  return all_reduce_impl(sendbufs, recvbufs, p, n, dtype, op, algo, group_size, 0, workspace, ws_bytes, stream);
+}
+
+rr_status_t rr_all_reduce_hier(const void* const* sendbufs, void* const* recvbufs, int p, size_t n,
+                               rr_dtype_t dtype, rr_op_t op, int group_size, int flags, void* workspace,
+                               size_t ws_bytes, rr_stream_t stream) {
+  if (flags & ~kHierFlags) return fail(RR_ERROR_INVALID_ARGUMENT, "unknown hierarchy flags 0x%x", flags);
+  if ((flags & RR_HIER_STAGED) && (flags & RR_HIER_INTRA_RING))
+    return fail(RR_ERROR_UNSUPPORTED, "the staged hierarchy has no intra-group ring variant");
+  const rr_algo_t algo = (flags & RR_HIER_STAGED) ? RR_ALGO_HIER_STAGED : RR_ALGO_HIER_FUSED;
+  return all_reduce_impl(sendbufs, recvbufs, p, n, dtype, op, algo, group_size, flags, workspace, ws_bytes, stream);
+}
+
+size_t rr_hier_workspace_size(int p, int group_size, size_t n, rr_dtype_t dtype, int flags) {
+  if (p < 1 || p > RR_MAX_RANKS || rr::elem_size(dtype) == 0 || static_cast<uint64_t>(n) > kMaxElems) return 0;
+  if (group_size < 1 || group_size > p || p % group_size || (flags & ~kHierFlags)) return 0;
+  if (!(flags & RR_HIER_STAGED)) return 0;
+  return workspace_bytes(RR_ALGO_HIER_STAGED, p, group_size, n, dtype, flags);
 }
 
 rr_status_t rr_all_reduce(const void* const* sendbufs, void* const* recvbufs, int p, size_t n, rr_dtype_t dtype,

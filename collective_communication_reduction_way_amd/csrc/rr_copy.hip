@@ -255,6 +255,9 @@ hipError_t launch_fold(const FoldLaunch& f, hipStream_t s) {
     case FoldMode::kRingShard: return launch_fold_ring_shard(f, s);
     case FoldMode::kAscOne: return launch_fold_asc_one(f, s);
     case FoldMode::kHierAll: return launch_fold_hier_all(f, s);
+    case FoldMode::kHierRing:
+    case FoldMode::kHierAllWire:
+    case FoldMode::kHierRingWire: return launch_fold_hier_var(f, s);
   }
   return hipErrorInvalidValue;
 }

@@ -33,29 +33,46 @@ constexpr int group_len() {
 }
 
 constexpr bool is_ring(FoldMode m) { return m == FoldMode::kRingAll || m == FoldMode::kRingShard; }
-constexpr bool writes_all(FoldMode m) { return m == FoldMode::kRingAll || m == FoldMode::kHierAll; }
+constexpr bool writes_all(FoldMode m) { return m == FoldMode::kRingAll || is_hier(m); }
 
 // k-th input in the fold order of row `seg`.
 template <FoldMode M>
-__device__ __forceinline__ int fold_src(int k, int seg, int p) {
+__device__ __forceinline__ int fold_src(int k, int seg, int p, int group) {
   if constexpr (is_ring(M)) {
     const int r = seg + 1 + k;  // seg <= p-1 and k <= p-1, so r <= 2p-1
     return r >= p ? r - p : r;
   } else if constexpr (M == FoldMode::kAscOne) {
     return seg * p + k;
+  } else if constexpr (is_hier_ring(M)) {
+    // member i of group j, the group's ring starting after member seg
+    const int j = k / group;
+    const int i = seg + 1 + (k - j * group);  // seg <= group-1, so i <= 2*group-1
+    return j * group + (i >= group ? i - group : i);
   } else {
     return k;
+  }
+}
+
+// A finished group partial as it enters the cross-group fold: for the wire
+// modes rounded to the storage type (nearest even) and widened again.
+template <class E, FoldMode M, class A>
+__device__ __forceinline__ A group_partial(A v) {
+  if constexpr (is_wire(M) && sizeof(typename E::S) == 2) {
+    return half_to_f32<E>(f32_to_half<E>(v));
+  } else {
+    return v;
   }
 }
 
 // Fold step k (k >= 1) of value x into the running state.  For the hierarchy,
 // `acc` is the running group partial and `tot` the running fold of finished
 // groups; a new group starts at every multiple of `group`.
-template <class OP, FoldMode M, class A>
+template <class E, class OP, FoldMode M, class A>
 __device__ __forceinline__ void fold_step(A& acc, A& tot, A x, int k, int group) {
-  if constexpr (M == FoldMode::kHierAll) {
+  if constexpr (is_hier(M)) {
     if (k % group == 0) {
-      tot = (k == group) ? acc : OP::apply(tot, acc);
+      const A g = group_partial<E, M>(acc);
+      tot = (k == group) ? g : OP::apply(tot, g);
       acc = x;
     } else {
       acc = OP::apply(acc, x);
@@ -67,10 +84,11 @@ __device__ __forceinline__ void fold_step(A& acc, A& tot, A x, int k, int group)
 
 // The folded value of an element: for the hierarchy the last group's partial
 // joins the total; then the op's last step (AVG: the division by `div`).
-template <class OP, FoldMode M, class A>
+template <class E, class OP, FoldMode M, class A>
 __device__ __forceinline__ A fold_finish(A acc, A tot, int p, int group, int32_t div) {
-  if constexpr (M == FoldMode::kHierAll) {
-    return op_finish<OP>((p > group) ? OP::apply(tot, acc) : acc, div);
+  if constexpr (is_hier(M)) {
+    const A g = group_partial<E, M>(acc);
+    return op_finish<OP>((p > group) ? OP::apply(tot, g) : g, div);
   } else {
     return op_finish<OP>(acc, div);
   }
@@ -82,13 +100,13 @@ __device__ __forceinline__ void fold_scalar(const FoldArgs& a, uint64_t i, uint6
   using SI = typename TI::S;
   using SO = typename TO::S;
   using A = typename TI::A;
-  A acc = load_one<TI>(static_cast<const SI*>(a.in[fold_src<M>(0, seg, p)]) + i);
+  A acc = load_one<TI>(static_cast<const SI*>(a.in[fold_src<M>(0, seg, p, a.group)]) + i);
   A tot = acc;
   for (int k = 1; k < p; ++k) {
-    const A x = load_one<TI>(static_cast<const SI*>(a.in[fold_src<M>(k, seg, p)]) + i);
-    fold_step<OP, M>(acc, tot, x, k, a.group);
+    const A x = load_one<TI>(static_cast<const SI*>(a.in[fold_src<M>(k, seg, p, a.group)]) + i);
+    fold_step<TI, OP, M>(acc, tot, x, k, a.group);
   }
-  acc = fold_finish<OP, M>(acc, tot, p, a.group, a.div);
+  acc = fold_finish<TI, OP, M>(acc, tot, p, a.group, a.div);
   if constexpr (writes_all(M)) {
     for (int r = 0; r < p; ++r) store_one<TO>(static_cast<SO*>(a.out[r]) + i, acc);
   } else if constexpr (M == FoldMode::kRingShard) {
@@ -140,10 +158,10 @@ __device__ __forceinline__ void fold_tile(const char* const* sb, char* const* db
       A x[V];
       unpack(raw[u][k], x);
 #pragma unroll
-      for (int j = 0; j < V; ++j) fold_step<OP, M>(acc[j], tot[j], x[j], k, group);
+      for (int j = 0; j < V; ++j) fold_step<TI, OP, M>(acc[j], tot[j], x[j], k, group);
     }
 #pragma unroll
-    for (int j = 0; j < V; ++j) acc[j] = fold_finish<OP, M>(acc[j], tot[j], P, group, div);
+    for (int j = 0; j < V; ++j) acc[j] = fold_finish<TI, OP, M>(acc[j], tot[j], P, group, div);
     Raw<TO, V> o;
     pack(acc, o);
     constexpr int ND = writes_all(M) ? P : 1;
@@ -168,7 +186,7 @@ __device__ __forceinline__ void fold_tile_dyn(const FoldArgs& a, int seg, int p,
   A acc[U][V];
   A tot[U][V];
   {
-    const char* s0 = static_cast<const char*>(a.in[fold_src<M>(0, seg, p)]) + in_tile_off;
+    const char* s0 = static_cast<const char*>(a.in[fold_src<M>(0, seg, p, a.group)]) + in_tile_off;
     Raw<TI, V> raw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -183,7 +201,7 @@ __device__ __forceinline__ void fold_tile_dyn(const FoldArgs& a, int seg, int p,
     }
   }
   for (int k = 1; k < p; ++k) {
-    const char* sk = static_cast<const char*>(a.in[fold_src<M>(k, seg, p)]) + in_tile_off;
+    const char* sk = static_cast<const char*>(a.in[fold_src<M>(k, seg, p, a.group)]) + in_tile_off;
     Raw<TI, V> raw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -195,7 +213,7 @@ __device__ __forceinline__ void fold_tile_dyn(const FoldArgs& a, int seg, int p,
       A x[V];
       unpack(raw[u], x);
 #pragma unroll
-      for (int j = 0; j < V; ++j) fold_step<OP, M>(acc[u][j], tot[u][j], x[j], k, a.group);
+      for (int j = 0; j < V; ++j) fold_step<TI, OP, M>(acc[u][j], tot[u][j], x[j], k, a.group);
     }
   }
 #pragma unroll
@@ -203,7 +221,7 @@ __device__ __forceinline__ void fold_tile_dyn(const FoldArgs& a, int seg, int p,
     if (GUARD && lane + u * kBlock >= valid) continue;
     const uint32_t off = (lane + u * kBlock) * GBO;
 #pragma unroll
-    for (int j = 0; j < V; ++j) acc[u][j] = fold_finish<OP, M>(acc[u][j], tot[u][j], p, a.group, a.div);
+    for (int j = 0; j < V; ++j) acc[u][j] = fold_finish<TI, OP, M>(acc[u][j], tot[u][j], p, a.group, a.div);
     Raw<TO, V> o;
     pack(acc[u], o);
     if constexpr (writes_all(M)) {
@@ -224,7 +242,7 @@ __global__ __launch_bounds__(kBlock) void k_fold(FoldArgs a) {
   const int seg = blockIdx.y;
   uint64_t lo = 0;
   uint64_t hi = a.n;
-  if constexpr (is_ring(M)) {
+  if constexpr (uses_bounds(M)) {
     lo = a.bound[seg];
     hi = a.bound[seg + 1];
   }
@@ -250,7 +268,7 @@ __global__ __launch_bounds__(kBlock) void k_fold(FoldArgs a) {
     // workgroup (scalar registers).
     const char* src[P];
 #pragma unroll
-    for (int k = 0; k < P; ++k) src[k] = static_cast<const char*>(a.in[fold_src<M>(k, seg, P)]);
+    for (int k = 0; k < P; ++k) src[k] = static_cast<const char*>(a.in[fold_src<M>(k, seg, P, a.group)]);
     constexpr int ND = writes_all(M) ? P : 1;
     char* dst[ND];
     if constexpr (writes_all(M)) {
@@ -305,7 +323,7 @@ template <class TI, class TO, class OP, int P, int U, bool NT, FoldMode M>
 hipError_t fold_go(const FoldLaunch& f, hipStream_t s) {
   constexpr int V = group_len<TI, TO>();
   uint64_t longest = 0;
-  if constexpr (is_ring(M)) {
+  if constexpr (uses_bounds(M)) {
     for (int c = 0; c < f.segments; ++c) {
       const uint64_t len = f.args.bound[c + 1] - f.args.bound[c];
       if (len > longest) longest = len;

@@ -29,7 +29,27 @@ enum class FoldMode : int {
   // consecutive inputs, the group partials folded ascending; the result goes
   // to out[0..p-1][i].
   kHierAll = 3,
+  // Hierarchical, each group's partial formed by a ring all-reduce of the
+  // group: row y = group-chunk k (bounds floor(k*n/group)); inside group j
+  // the fold order is members (k+1) mod G, ..., k mod G; then as kHierAll.
+  kHierRing = 4,
+  // kHierAll / kHierRing with every group partial rounded to the storage
+  // type and widened again before the cross-group fold (the partial crosses
+  // groups in the storage type).  16-bit kinds only.
+  kHierAllWire = 5,
+  kHierRingWire = 6,
 };
+
+constexpr bool is_hier(FoldMode m) {
+  return m == FoldMode::kHierAll || m == FoldMode::kHierRing || m == FoldMode::kHierAllWire ||
+         m == FoldMode::kHierRingWire;
+}
+constexpr bool is_hier_ring(FoldMode m) { return m == FoldMode::kHierRing || m == FoldMode::kHierRingWire; }
+constexpr bool is_wire(FoldMode m) { return m == FoldMode::kHierAllWire || m == FoldMode::kHierRingWire; }
+// Modes whose rows are bounded by bound[]: the ring's chunks, the group-chunks.
+constexpr bool uses_bounds(FoldMode m) {
+  return m == FoldMode::kRingAll || m == FoldMode::kRingShard || is_hier_ring(m);
+}
 
 enum class Kind : int { kI32 = 0, kF32 = 1, kBF16 = 2, kF16 = 3 };
 
@@ -156,6 +176,8 @@ hipError_t launch_fold_ring_all(const FoldLaunch& f, hipStream_t stream);
 hipError_t launch_fold_ring_shard(const FoldLaunch& f, hipStream_t stream);
 hipError_t launch_fold_asc_one(const FoldLaunch& f, hipStream_t stream);
 hipError_t launch_fold_hier_all(const FoldLaunch& f, hipStream_t stream);
+// The hierarchical variants (kHierRing, kHierAllWire, kHierRingWire), run-time p.
+hipError_t launch_fold_hier_var(const FoldLaunch& f, hipStream_t stream);
 // Copies move units of unit_bytes in {16, 4, 2, 1}; nontemporal != 0 uses
 // nontemporal loads and stores; grid_cap 0 = the default workgroup count.
 hipError_t launch_fanout(const FanoutArgs& a, int unit_bytes, int nontemporal, int grid_cap, hipStream_t stream);

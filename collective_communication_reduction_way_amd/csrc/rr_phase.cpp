@@ -47,7 +47,7 @@ uint32_t slot_for(DeviceState& d, hipStream_t s) {
 // groups; fills the per-segment tables of `a` and returns the tile count.
 uint64_t tile_segments(const FoldLaunch& f, uint64_t V, uint64_t tile, PhaseArgs& a) {
   uint64_t tiles = 0;
-  const bool ring = f.mode == FoldMode::kRingAll || f.mode == FoldMode::kRingShard;
+  const bool ring = uses_bounds(f.mode);  // rows bounded by bound[] (else one row of n)
   a.edges = 0;
   for (int sg = 0; sg < f.segments; ++sg) {
     const uint64_t lo = ring ? f.args.bound[sg] : 0;
@@ -89,6 +89,9 @@ hipError_t launch_mode(const FoldLaunch& f, const PhaseArgs& a, unsigned grid, i
   switch (f.mode) {
     case FoldMode::kRingAll: return phase_launch_ring(a, f.in_kind, f.op, grid, unroll, sync, static_p, occ, s);
     case FoldMode::kHierAll: return phase_launch_hier(a, f.in_kind, f.op, grid, unroll, sync, static_p, occ, s);
+    case FoldMode::kHierRing:
+    case FoldMode::kHierAllWire:
+    case FoldMode::kHierRingWire: return phase_launch_hier_var(a, f.mode, f.in_kind, f.op, grid, unroll, sync, occ, s);
     default: break;
   }
   return hipErrorInvalidValue;
@@ -96,11 +99,11 @@ hipError_t launch_mode(const FoldLaunch& f, const PhaseArgs& a, unsigned grid, i
 
 }  // namespace
 
-int phase_default_unroll(Kind k, FoldMode m) { return (m == FoldMode::kHierAll && is_half(k)) ? 4 : 8; }
+int phase_default_unroll(Kind k, FoldMode m) { return (is_hier(m) && is_half(k)) ? 4 : 8; }
 
 bool phase_supported(const FoldLaunch& f) {
-  return (f.mode == FoldMode::kRingAll || f.mode == FoldMode::kHierAll) && f.args.vec &&
-         f.in_kind == f.out_kind && f.segments >= 1 && f.segments <= RR_MAX_RANKS;
+  return (f.mode == FoldMode::kRingAll || is_hier(f.mode)) && f.args.vec && f.in_kind == f.out_kind &&
+         f.segments >= 1 && f.segments <= RR_MAX_RANKS;
 }
 
 // Schedule choice (measured on MI355X; every knob can be forced through
@@ -196,9 +199,11 @@ hipError_t phase_barrier_timeouts(int device, unsigned long long* count) {
   if (device != cur && (e = hipSetDevice(device)) != hipSuccess) return e;
   unsigned long long ring = 0;
   unsigned long long hier = 0;
+  unsigned long long var = 0;
   e = phase_timeouts_ring(&ring);
   if (e == hipSuccess) e = phase_timeouts_hier(&hier);
-  *count = ring + hier;
+  if (e == hipSuccess) e = phase_timeouts_hier_var(&var);
+  *count = ring + hier + var;
   if (device != cur) {
     const hipError_t e2 = hipSetDevice(cur);
     if (e == hipSuccess) e = e2;

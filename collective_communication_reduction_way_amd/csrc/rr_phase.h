@@ -61,9 +61,14 @@ hipError_t phase_launch_ring(const PhaseArgs& a, Kind k, rr_op_t op, unsigned gr
                              bool static_p, int* occ, hipStream_t s);
 hipError_t phase_launch_hier(const PhaseArgs& a, Kind k, rr_op_t op, unsigned grid, int unroll, bool sync,
                              bool static_p, int* occ, hipStream_t s);
+// The hierarchical variants (kHierRing, kHierAllWire, kHierRingWire), run-time
+// rank loop only (rr_phase_hier_var.hip).
+hipError_t phase_launch_hier_var(const PhaseArgs& a, FoldMode m, Kind k, rr_op_t op, unsigned grid, int unroll,
+                                 bool sync, int* occ, hipStream_t s);
 // Barrier timeouts counted by each translation unit's kernels on the
 // current device.
 hipError_t phase_timeouts_ring(unsigned long long* count);
 hipError_t phase_timeouts_hier(unsigned long long* count);
+hipError_t phase_timeouts_hier_var(unsigned long long* count);
 
 }  // namespace rr

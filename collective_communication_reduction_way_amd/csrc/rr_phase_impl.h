@@ -129,7 +129,7 @@ __device__ __forceinline__ void read_fold(const FoldArgs& f, int seg, int p, uin
   if constexpr (P > 0) {
     const char* src[P];
 #pragma unroll
-    for (int k = 0; k < P; ++k) src[k] = static_cast<const char*>(f.in[fold_src<M>(k, seg, P)]) + in_off;
+    for (int k = 0; k < P; ++k) src[k] = static_cast<const char*>(f.in[fold_src<M>(k, seg, P, f.group)]) + in_off;
     {
       Raw<E, V> x[U];
       load_tile(x, src[0], valid);
@@ -149,14 +149,14 @@ __device__ __forceinline__ void read_fold(const FoldArgs& f, int seg, int p, uin
         A v[V];
         unpack(x[u], v);
 #pragma unroll
-        for (int j = 0; j < V; ++j) fold_step<OP, M>(acc[u][j], tot[u][j], v[j], k, f.group);
+        for (int j = 0; j < V; ++j) fold_step<E, OP, M>(acc[u][j], tot[u][j], v[j], k, f.group);
       }
     }
   } else {
     Raw<E, V> cur[U];
     Raw<E, V> nxt[U];
-    load_tile(cur, static_cast<const char*>(f.in[fold_src<M>(0, seg, p)]) + in_off, valid);
-    if (p > 1) load_tile(nxt, static_cast<const char*>(f.in[fold_src<M>(1, seg, p)]) + in_off, valid);
+    load_tile(cur, static_cast<const char*>(f.in[fold_src<M>(0, seg, p, f.group)]) + in_off, valid);
+    if (p > 1) load_tile(nxt, static_cast<const char*>(f.in[fold_src<M>(1, seg, p, f.group)]) + in_off, valid);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       unpack(cur[u], acc[u]);
@@ -168,13 +168,13 @@ __device__ __forceinline__ void read_fold(const FoldArgs& f, int seg, int p, uin
 #pragma unroll
       for (int u = 0; u < U; ++u) cur[u] = nxt[u];
       if (k + 1 < p)
-        load_tile(nxt, static_cast<const char*>(f.in[fold_src<M>(k + 1, seg, p)]) + in_off, valid);
+        load_tile(nxt, static_cast<const char*>(f.in[fold_src<M>(k + 1, seg, p, f.group)]) + in_off, valid);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         A x[V];
         unpack(cur[u], x);
 #pragma unroll
-        for (int j = 0; j < V; ++j) fold_step<OP, M>(acc[u][j], tot[u][j], x[j], k, f.group);
+        for (int j = 0; j < V; ++j) fold_step<E, OP, M>(acc[u][j], tot[u][j], x[j], k, f.group);
       }
     }
   }
@@ -182,7 +182,7 @@ __device__ __forceinline__ void read_fold(const FoldArgs& f, int seg, int p, uin
 #pragma unroll
   for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int j = 0; j < V; ++j) acc[u][j] = fold_finish<OP, M>(acc[u][j], tot[u][j], pp, f.group, f.div);
+    for (int j = 0; j < V; ++j) acc[u][j] = fold_finish<E, OP, M>(acc[u][j], tot[u][j], pp, f.group, f.div);
 }
 
 template <bool GUARD, class E, int V, int U>
@@ -221,12 +221,12 @@ __global__ __launch_bounds__(kBlock) void k_phase(PhaseArgs a) {
         seg = static_cast<int>(t / a.uniform_tiles);
         k = t - static_cast<uint32_t>(seg) * a.uniform_tiles;
         valid = (k + 1 == a.uniform_tiles) ? a.uniform_last : kTile;
-        if constexpr (is_ring(M)) lo = static_cast<uint64_t>(seg) * a.seg_len;
+        if constexpr (uses_bounds(M)) lo = static_cast<uint64_t>(seg) * a.seg_len;
       } else {
         while (a.seg_tile[seg + 1] <= t) ++seg;
         k = t - a.seg_tile[seg];
         valid = (k + 1 == a.seg_tile[seg + 1] - a.seg_tile[seg]) ? a.seg_last[seg] : kTile;
-        if constexpr (is_ring(M)) lo = a.f.bound[seg];
+        if constexpr (uses_bounds(M)) lo = a.f.bound[seg];
       }
       const uint64_t g0 = (lo + V - 1) / V + static_cast<uint64_t>(k) * kTile;
       off = g0 * 16;
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(64) void k_edges(PhaseArgs a) {
   const int p = a.f.p;
   uint64_t lo = 0;
   uint64_t hi = a.f.n;
-  if constexpr (is_ring(M)) {
+  if constexpr (uses_bounds(M)) {
     lo = a.f.bound[seg];
     hi = a.f.bound[seg + 1];
   }
@@ -308,7 +308,7 @@ hipError_t phase_go(K kernel, const PhaseArgs& a, unsigned grid, unsigned block,
 
 template <class E, FoldMode M>
 constexpr int phase_unroll() {
-  return (M == FoldMode::kHierAll && sizeof(typename E::S) == 2) ? 4 : 8;
+  return (is_hier(M) && sizeof(typename E::S) == 2) ? 4 : 8;
 }
 
 template <class E, class OP, int P, FoldMode M, bool SYNC>
@@ -327,9 +327,11 @@ template <class E, class OP, FoldMode M>
 hipError_t phase_by_p(const PhaseArgs& a, unsigned grid, int unroll, bool sync, bool static_p, int* occ,
                       hipStream_t s) {
   hipError_t e;
-  if (static_p && a.f.p == 8) {
-    e = sync ? phase_by_u<E, OP, 8, M, true>(a, grid, unroll, occ, s)
-             : phase_by_u<E, OP, 8, M, false>(a, grid, unroll, occ, s);
+  // the hierarchical variants are compiled with the run-time loop only
+  constexpr bool kStatic = M == FoldMode::kRingAll || M == FoldMode::kHierAll;
+  if (kStatic && static_p && a.f.p == 8) {
+    e = sync ? phase_by_u<E, OP, kStatic ? 8 : 0, M, true>(a, grid, unroll, occ, s)
+             : phase_by_u<E, OP, kStatic ? 8 : 0, M, false>(a, grid, unroll, occ, s);
   } else {
     e = sync ? phase_by_u<E, OP, 0, M, true>(a, grid, unroll, occ, s)
              : phase_by_u<E, OP, 0, M, false>(a, grid, unroll, occ, s);
@@ -356,12 +358,35 @@ hipError_t phase_by_op(const PhaseArgs& a, rr_op_t op, unsigned grid, int unroll
 template <FoldMode M>
 hipError_t phase_dispatch(const PhaseArgs& a, Kind k, rr_op_t op, unsigned grid, int unroll, bool sync,
                           bool static_p, int* occ, hipStream_t s) {
-  switch (k) {
-    case Kind::kI32: return phase_by_op<EI32, M>(a, op, grid, unroll, sync, static_p, occ, s);
-    case Kind::kF32: return phase_by_op<EF32, M>(a, op, grid, unroll, sync, static_p, occ, s);
-    case Kind::kBF16: return phase_by_op<EBF16, M>(a, op, grid, unroll, sync, static_p, occ, s);
-    case Kind::kF16: return phase_by_op<EF16, M>(a, op, grid, unroll, sync, static_p, occ, s);
+  if constexpr (!is_wire(M)) {
+    if (k == Kind::kI32) return phase_by_op<EI32, M>(a, op, grid, unroll, sync, static_p, occ, s);
+    if (k == Kind::kF32) return phase_by_op<EF32, M>(a, op, grid, unroll, sync, static_p, occ, s);
   }
+  // (rounding a partial to a 4-byte storage type changes nothing: the wire
+  // modes exist for the 16-bit kinds only)
+  if (k == Kind::kBF16) return phase_by_op<EBF16, M>(a, op, grid, unroll, sync, static_p, occ, s);
+  if (k == Kind::kF16) return phase_by_op<EF16, M>(a, op, grid, unroll, sync, static_p, occ, s);
+  return hipErrorInvalidValue;
+}
+
+// Single-pass fold for the hierarchical variants (unaligned buffers): the
+// run-time-p kernel of rr_fold_impl.h.
+template <FoldMode M>
+hipError_t fold_var_dispatch(const FoldLaunch& f, hipStream_t s) {
+  if (f.in_kind != f.out_kind) return hipErrorInvalidValue;
+  if constexpr (!is_wire(M)) {
+    if (f.in_kind == Kind::kI32) {
+      switch (f.op) {
+        case RR_SUM: return fold_go<EI32, EI32, OpSum, 0, 2, false, M>(f, s);
+        case RR_MAX: return fold_go<EI32, EI32, OpMax, 0, 2, false, M>(f, s);
+        case RR_MIN: return fold_go<EI32, EI32, OpMin, 0, 2, false, M>(f, s);
+        default: return hipErrorInvalidValue;
+      }
+    }
+    if (f.in_kind == Kind::kF32) return fold_mixed_by_op<EF32, EF32, M>(f, s);
+  }
+  if (f.in_kind == Kind::kBF16) return fold_mixed_by_op<EBF16, EBF16, M>(f, s);
+  if (f.in_kind == Kind::kF16) return fold_mixed_by_op<EF16, EF16, M>(f, s);
   return hipErrorInvalidValue;
 }
 

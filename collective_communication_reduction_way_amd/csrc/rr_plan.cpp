@@ -139,4 +139,37 @@ rr_status_t rr_hier_traffic(int p, int group_size, uint64_t bytes_per_rank, uint
   return RR_SUCCESS;
 }
 
+// Alpha-beta cost model.  Page "分布式训练/推理": a message costs
+// alpha + bytes/bandwidth (section "从单卡到多卡"); the ring all-reduce runs
+// 2(N-1) rounds of S/N bytes per device (section "Ring all-reduce 的带宽账").
+// Page "大模型并行的最小闭环：集合通信、TP、FSDP/ZeRO-3 到权重分片", section
+// "总体时间模型": flat T_slow(B*N) against hierarchical T_fast(B*N) + T_slow(B).
+namespace {
+
+bool link_ok(const rr_link_t& l) { return l.alpha_s >= 0.0 && l.bytes_per_s > 0.0; }
+
+double message_time(const rr_link_t& l, double bytes) { return l.alpha_s + bytes / l.bytes_per_s; }
+
+}  // namespace
+
+rr_status_t rr_cost_ring_all_reduce(int p, double bytes, rr_link_t link, double* seconds) {
+  if (p < 1 || p > RR_MAX_RANKS || !(bytes >= 0.0) || !link_ok(link) || !seconds) return RR_ERROR_INVALID_ARGUMENT;
+  const double rounds = 2.0 * (p - 1);
+  *seconds = rounds * message_time(link, bytes / p);
+  return RR_SUCCESS;
+}
+
+rr_status_t rr_cost_hier_all_reduce(int group_size, double bytes, rr_link_t fast, rr_link_t slow, double* t_flat,
+                                    double* t_hier, int* use_hier) {
+  if (group_size < 1 || group_size > RR_MAX_RANKS || !(bytes >= 0.0) || !link_ok(fast) || !link_ok(slow))
+    return RR_ERROR_INVALID_ARGUMENT;
+  const double node_bytes = static_cast<double>(group_size) * bytes;
+  const double flat = message_time(slow, node_bytes);
+  const double hier = message_time(fast, node_bytes) + message_time(slow, bytes);
+  if (t_flat) *t_flat = flat;
+  if (t_hier) *t_hier = hier;
+  if (use_hier) *use_hier = hier < flat ? 1 : 0;
+  return RR_SUCCESS;
+}
+
 }  // extern "C"

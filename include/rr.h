@@ -179,6 +179,44 @@ rr_status_t rr_all_reduce_ex(const void* const* sendbufs, void* const* recvbufs,
                              rr_dtype_t dtype, rr_op_t op, rr_algo_t algo, int group_size,
                              void* workspace, size_t workspace_bytes, rr_stream_t stream);
 
+/* Variant bits of rr_all_reduce_hier [HIER]. */
+#define RR_HIER_INTRA_RING 1 /* step 1 as a ring all-reduce inside each group */
+#define RR_HIER_WIRE_ROUND 2 /* group partials rounded to the storage type before crossing groups */
+#define RR_HIER_STAGED 4     /* run the steps of [HIER] one by one (workspace needed) */
+
+/*
+ * Hierarchical all-reduce with the variants of [HIER] (groups of group_size
+ * consecutive ranks, representative = the group's first rank).
+ *   flags = 0: as rr_all_reduce_ex with RR_ALGO_HIER_FUSED (ascending fold
+ *     inside each group, ascending over groups, float32 partials, one
+ *     rounding).
+ *   RR_HIER_INTRA_RING: step 1 as the page words it, an all-reduce inside
+ *     each group run as a ring of its G members: group-chunk k of the n
+ *     elements, [floor(k*n/G), floor((k+1)*n/G)), is folded over the members
+ *     in the order (k+1) mod G, ..., k mod G; the group partials are then
+ *     folded ascending over groups.  Not available with RR_HIER_STAGED
+ *     (RR_ERROR_UNSUPPORTED).
+ *   RR_HIER_WIRE_ROUND: each group's partial is rounded to the storage type
+ *     (nearest even) and widened again before the cross-group fold -- what
+ *     the representative ships across groups.  Changes results for bfloat16
+ *     and float16 only.
+ *   RR_HIER_STAGED: the steps of [HIER] one launch at a time through a
+ *     caller workspace of rr_hier_workspace_size() bytes (as
+ *     RR_ALGO_HIER_STAGED; with RR_HIER_WIRE_ROUND the partials are stored
+ *     in the storage type).
+ *   RR_AVG divides by p after the cross-group fold.  Other rules (aliasing,
+ *   in place, errors) as rr_all_reduce_ex; unknown flag bits ->
+ *   RR_ERROR_INVALID_ARGUMENT.
+ */
+rr_status_t rr_all_reduce_hier(const void* const* sendbufs, void* const* recvbufs, int p, size_t n,
+                               rr_dtype_t dtype, rr_op_t op, int group_size, int flags, void* workspace,
+                               size_t workspace_bytes, rr_stream_t stream);
+
+/* Workspace bytes of rr_all_reduce_hier: 0 without RR_HIER_STAGED; else
+ * (p/group_size)*n*4, or (p/group_size)*n*s with RR_HIER_WIRE_ROUND on a
+ * 16-bit dtype.  0 for invalid arguments. */
+size_t rr_hier_workspace_size(int p, int group_size, size_t n, rr_dtype_t dtype, int flags);
+
 /*
  * Reduce-scatter [SEM] [RING]: rank c receives chunk c of y.
  *   sendbufs[r]: rank r's input, n elements.  recvbufs[c]: n/p elements.
@@ -341,6 +379,31 @@ rr_status_t rr_ring_bytes_per_rank(int p, size_t n, rr_dtype_t dtype, uint64_t* 
  */
 rr_status_t rr_hier_traffic(int p, int group_size, uint64_t bytes_per_rank, uint64_t* intra_per_group,
                             uint64_t* cross_per_group_flat, uint64_t* cross_per_group_hier);
+
+/*
+ * Alpha-beta cost model (host only) [COST]: page "分布式训练/推理", section
+ * "从单卡到多卡" -- one message costs its fixed latency plus its bytes over
+ * the link bandwidth, T = alpha + bytes/bandwidth; section "Ring all-reduce
+ * 的带宽账" -- a ring all-reduce is 2(N-1) rounds in which every device sends
+ * S/N bytes; page "大模型并行的最小闭环：集合通信、TP、FSDP/ZeRO-3 到权重分片",
+ * section "总体时间模型" -- without the hierarchy a node ships B*N bytes over
+ * the slow links, T = T_slow(B*N); with it T = T_fast(B*N) + T_slow(B).
+ */
+typedef struct {
+  double alpha_s;     /* fixed cost of one message, seconds */
+  double bytes_per_s; /* link bandwidth, bytes per second (> 0) */
+} rr_link_t;
+
+/* Ring all-reduce of `bytes` per rank over p ranks on one link class:
+ * 2(p-1) * (alpha + bytes/(p*bandwidth)) seconds (0 for p = 1). */
+rr_status_t rr_cost_ring_all_reduce(int p, double bytes, rr_link_t link, double* seconds);
+
+/* The hierarchy's time model for groups (nodes) of group_size ranks holding
+ * `bytes` each: *t_flat = T_slow(group_size*bytes), *t_hier =
+ * T_fast(group_size*bytes) + T_slow(bytes), T_x(m) = alpha_x + m/bandwidth_x;
+ * *use_hier = 1 when t_hier < t_flat.  Any output pointer may be NULL. */
+rr_status_t rr_cost_hier_all_reduce(int group_size, double bytes, rr_link_t fast, rr_link_t slow, double* t_flat,
+                                    double* t_hier, int* use_hier);
 
 /*
  * Diagnostics (needs a GPU; synchronizes the device): the number of times,

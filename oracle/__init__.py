@@ -39,7 +39,7 @@ against the worked example, closed forms, hand-computed IEEE-754 probes and
 brute force; none is "parity unpinned".
 """
 
-from . import bf16, fp16  # noqa: F401
+from . import bf16, cost, fp16  # noqa: F401
 from .collectives import (  # noqa: F401
     ALL_DTYPES,
     ALL_OPS,

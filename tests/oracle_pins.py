@@ -18,6 +18,7 @@ import numpy as np
 
 from oracle import bf16 as B
 from oracle import collectives as C
+from oracle import cost as K
 from oracle import fp16 as H
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -842,3 +843,44 @@ def pin_hier_variants():
     xb = enc([[1.0], [2.0 ** -8], [2.0 ** -8], [0.0]], "bfloat16")
     assert dec(C.all_reduce_hier(xb, "sum", "bfloat16", 2, wire_round=True), "bfloat16")[:, 0].tolist() == [1.0] * 4
     assert dec(C.all_reduce_hier(xb, "sum", "bfloat16", 2), "bfloat16")[:, 0].tolist() == [1.0 + 2.0 ** -7] * 4
+
+
+# ---------------------------------------------------------------------------
+# Alpha-beta cost model.
+
+def pin_cost_ring():
+    """With no latency, bandwidth times the ring's time is what one rank sends
+    in the schedule (counted from the oracle's own transfer list); with no
+    bytes it is alpha times the schedule's number of steps; p = 1 costs
+    nothing."""
+    for p in (2, 3, 4, 8, 16):
+        n = p * 1000
+        sched = C.ring_schedule(p)
+        b = C.chunk_bounds(n, p)
+        sent = sum(b[c + 1] - b[c] for (_, _, src, _, c) in sched if src == 0) * 4.0
+        t = K.ring_all_reduce(p, n * 4.0, 0.0, 1.0)
+        assert abs(t - sent) <= 1e-9 * sent, (p, t, sent)
+        steps = len({(ph, st) for ph, st, *_ in sched})
+        assert abs(K.ring_all_reduce(p, 0.0, 1e-6, 1e9) - steps * 1e-6) <= 1e-12 * steps * 1e-6
+    assert K.ring_all_reduce(1, 1e6, 1e-6, 1e9) == 0.0
+
+
+def pin_cost_hier_example():
+    """Page "大模型并行的最小闭环", section "Source Log: 2026-05-05": 2 nodes of
+    4 GPUs holding B = 8 MB each.  Without the hierarchy a node ships
+    4 x 8 MB = 32 MB across nodes, with it 8 MB: four times less (= N).  With
+    the link speeds of the table on page "分布式训练/推理" (NVLink about 1.8
+    TB/s, InfiniBand about 0.05 TB/s) and no latency: flat 32e6/0.05e12 =
+    640 us; hierarchical 32e6/1.8e12 + 8e6/0.05e12 = 17.78 + 160 = 177.78 us."""
+    B_, N = 8e6, 4
+    nv, ib = (0.0, 1.8e12), (0.0, 0.05e12)
+    t_flat, t_hier = K.hier_all_reduce(N, B_, nv, ib)
+    assert abs(t_flat - 640e-6) < 1e-12
+    assert abs(t_hier - (32e6 / 1.8e12 + 160e-6)) < 1e-12
+    assert abs(t_flat * ib[1] - 32e6) < 1e-3  # bytes a node ships without the hierarchy
+    # with the intra-node step free, the hierarchy is exactly N times faster
+    tf, th = K.hier_all_reduce(N, B_, (0.0, 1e300), ib)
+    assert abs(tf / th - N) < 1e-9
+    # a latency-bound case: tiny messages, where the extra fast step costs more than it saves
+    tf, th = K.hier_all_reduce(N, 8.0, (5e-6, 1.8e12), (1e-6, 0.05e12))
+    assert th > tf

@@ -276,3 +276,60 @@ def test_gather_validation():
     out = (ctypes.c_uint64 * 1)()
     assert L.rr_algorithmic_bytes(5, 4, 64, 1, 0, out) == 0 and out[0] == 2 * 64 * 4
     assert L.rr_algorithmic_bytes(6, 4, 64, 1, 1, out) == 0 and out[0] == 2 * 48 * 4
+
+
+def hier(flags, p=4, n=1024, dt=2, op=0, group=2, ws=None, wsb=0):
+    L = rr.lib()
+    send = ptrs(FAKE, p, 1 << 20)
+    recv = ptrs(FAKE + (1 << 30), p, 1 << 20)
+    return L.rr_all_reduce_hier(send, recv, p, n, dt, op, group, flags, ws, wsb, None)
+
+
+def test_hier_variant_validation():
+    assert hier(8) == INVALID  # unknown flag bit
+    assert hier(1 | 4) == UNSUPPORTED  # staged + intra ring
+    assert hier(0, group=3) == INVALID
+    assert hier(4) == INVALID  # staged without workspace
+    assert hier(2, dt=0, op=3) == UNSUPPORTED  # AVG over int32
+    for flags in (0, 1, 2, 3, 6):
+        assert hier(flags, n=0) == 0
+    L = rr.lib()
+    assert L.rr_hier_workspace_size(4, 2, 1000, 2, 0) == 0
+    assert L.rr_hier_workspace_size(4, 2, 1000, 2, 4) == 2 * 1000 * 4
+    assert L.rr_hier_workspace_size(4, 2, 1000, 2, 6) == 2 * 1000 * 2  # bf16 partials on the wire
+    assert L.rr_hier_workspace_size(4, 2, 1000, 1, 6) == 2 * 1000 * 4  # float32: rounding is the identity
+    assert L.rr_hier_workspace_size(4, 3, 1000, 2, 4) == 0
+    assert L.rr_hier_workspace_size(4, 2, 1000, 2, 8) == 0
+
+
+def test_bucket_validation():
+    L = rr.lib()
+    send = ptrs(FAKE, 8, 1 << 20)
+    recv = ptrs(FAKE + (1 << 30), 8, 1 << 20)
+    counts = (ctypes.c_size_t * 2)(100, 50)
+    assert L.rr_all_reduce_bucket(send, recv, counts, -1, 4, 1, 0, None) == INVALID
+    assert L.rr_all_reduce_bucket(send, recv, None, 2, 4, 1, 0, None) == INVALID
+    assert L.rr_all_reduce_bucket(None, recv, counts, 2, 4, 1, 0, None) == INVALID
+    assert L.rr_all_reduce_bucket(send, recv, counts, 2, 4, 0, 3, None) == UNSUPPORTED
+    assert L.rr_all_reduce_bucket(send, recv, counts, 0, 4, 1, 0, None) == 0
+    # overlapping outputs across tensors
+    bad = rr._ptr_array([FAKE + (1 << 30) + r * 16 for r in range(8)])
+    assert L.rr_all_reduce_bucket(send, bad, counts, 2, 4, 1, 0, None) == INVALID
+    zero = (ctypes.c_size_t * 2)(0, 0)
+    assert L.rr_all_reduce_bucket(send, recv, zero, 2, 4, 1, 0, None) == 0
+
+
+def test_dim1_validation():
+    L = rr.lib()
+    send = ptrs(FAKE, 4, 1 << 20)
+    recv = ptrs(FAKE + (1 << 30), 4, 1 << 20)
+    assert L.rr_all_gather_dim1(send, recv, 4, 3, 10, 1, None) == INVALID  # 4 does not divide 10
+    assert L.rr_reduce_scatter_dim1(send, recv, 4, 3, 10, 1, 0, None) == INVALID
+    assert L.rr_reduce_scatter_dim1(send, recv, 4, 3, 8, 0, 3, None) == UNSUPPORTED
+    assert L.rr_all_gather_dim1(send, recv, 4, 0, 8, 1, None) == 0
+    # an output over an input
+    bad = rr._ptr_array([FAKE + 64, FAKE + (2 << 30), FAKE + (3 << 30), FAKE + (4 << 30)])
+    assert L.rr_reduce_scatter_dim1(send, bad, 4, 3, 8, 1, 0, None) == INVALID
+    # (the shards are [3, 2]: 24 bytes of float32; an output 8 bytes in overlaps shard 0)
+    bad = rr._ptr_array([FAKE + 8, FAKE + (2 << 30), FAKE + (3 << 30), FAKE + (4 << 30)])
+    assert L.rr_all_gather_dim1(send, bad, 4, 3, 8, 1, None) == INVALID

@@ -142,3 +142,11 @@ def test_reduce_scatter_cols():
 
 def test_hier_variants():
     P.pin_hier_variants()
+
+
+def test_cost_ring():
+    P.pin_cost_ring()
+
+
+def test_cost_hier_example():
+    P.pin_cost_hier_example()

@@ -9,6 +9,7 @@ import pytest
 import oracle_pins as P
 from oracle import bf16 as B
 from oracle import collectives as C
+from oracle import cost as K
 from oracle import fp16 as H
 
 _combine = C.combine
@@ -55,6 +56,8 @@ def _run_all_pins():
         ("ag_dim1", P.pin_all_gather_dim1),
         ("rs_cols", P.pin_reduce_scatter_cols),
         ("hier_variants", P.pin_hier_variants),
+        ("cost_ring", P.pin_cost_ring),
+        ("cost_hier", P.pin_cost_hier_example),
     ]
     for name, fn in checks:
         try:
@@ -266,6 +269,16 @@ MUTATIONS = {
     "scatter_reversed": lambda m: m.setattr(
         C, "scatter", lambda x, p: np.stack([np.asarray(x)[c * (len(x) // p):(c + 1) * (len(x) // p)]
                                               for c in range(p)][::-1])),
+    "cost_ring_p_rounds": lambda m: m.setattr(
+        K, "ring_all_reduce", lambda p, nb, a, bw: 2 * p * (a + nb / p / bw)),
+    "cost_ring_full_message": lambda m: m.setattr(
+        K, "ring_all_reduce", lambda p, nb, a, bw: 2 * (p - 1) * (a + nb / bw)),
+    "cost_hier_links_swapped": lambda m: m.setattr(
+        K, "hier_all_reduce", lambda G, nb, fast, slow: (K.message(*fast, G * nb),
+                                                         K.message(*slow, G * nb) + K.message(*fast, nb))),
+    "cost_hier_ships_node_bytes": lambda m: m.setattr(
+        K, "hier_all_reduce", lambda G, nb, fast, slow: (K.message(*slow, G * nb),
+                                                         K.message(*fast, G * nb) + K.message(*slow, G * nb))),
     "all_gather_reversed": lambda m: m.setattr(
         C, "all_gather", lambda sh: np.stack([np.concatenate(list(np.asarray(sh))[::-1])] * np.asarray(sh).shape[0])),
 }
