@@ -37,7 +37,7 @@ if ROOT not in sys.path:
 METRIC = "all-reduce effective HBM GB/s (p·N bytes in+out / time) and % of MI355X HBM peak"
 HBM_PEAK_GBPS = 8000.0
 COLD_BYTES = 512 << 20
-DTYPE_TAG = {"int32": "i32", "float32": "f32", "bfloat16": "bf16"}
+DTYPE_TAG = {"int32": "i32", "float32": "f32", "bfloat16": "bf16", "float16": "f16"}
 
 
 def parse_args(argv=None):
@@ -154,19 +154,21 @@ def busbw_gibps(kind, p, s_bytes, t_seconds):
 class Runner:
     """Pre-marshalled calls of one collective over rotating buffer sets."""
 
-    def __init__(self, rr, torch, spec, coll, op, algo, group, host_x, nsets, stream):
+    def __init__(self, rr, torch, spec, coll, op, algo, group, host_x, nsets, stream, hier_kw=None):
         import ctypes
 
         self.rr, self.torch, self.stream = rr, torch, stream
         self.L = rr.lib()
+        hier_kw = hier_kw or {}
         p, n, dtype = spec["p"], spec["n"], spec["dtype"]
         self.p, self.n, self.dtype, self.coll, self.algo = p, n, dtype, coll, algo
-        tdt = {"int32": torch.int32, "float32": torch.float32, "bfloat16": torch.bfloat16}[dtype]
+        tdt = {"int32": torch.int32, "float32": torch.float32, "bfloat16": torch.bfloat16,
+               "float16": torch.float16}[dtype]
         dev = torch.device("cuda", 0)
         import numpy as np
 
-        if dtype == "bfloat16":
-            host = torch.from_numpy(host_x.view(np.int16)).view(torch.bfloat16)
+        if dtype in ("bfloat16", "float16"):
+            host = torch.from_numpy(host_x.view(np.int16)).view(tdt)
         else:
             host = torch.from_numpy(host_x)
         L = n // p
@@ -174,13 +176,18 @@ class Runner:
         dt = rr.DTYPES[dtype]
         opc = rr.OPS[op]
         sh = stream.cuda_stream
+        rows = spec.get("rows", 0)
+        cols = n // rows if rows else 0
         for _ in range(nsets):
-            if coll == "all_gather":
+            if coll in ("all_gather", "gather", "all_gather_dim1"):
                 x = host[:, :L].contiguous().to(dev)
                 y = torch.empty((p, n), dtype=tdt, device=dev)
+            elif coll == "scatter":
+                x = host[:1].contiguous().to(dev)
+                y = torch.empty((p, L), dtype=tdt, device=dev)
             else:
                 x = host.to(dev)
-                if coll == "reduce_scatter":
+                if coll in ("reduce_scatter", "reduce_scatter_dim1"):
                     y = torch.empty((p, L), dtype=tdt, device=dev)
                 elif coll == "reduce":
                     y = torch.empty((1, n), dtype=tdt, device=dev)
@@ -188,6 +195,8 @@ class Runner:
                     y = torch.empty((p, n), dtype=tdt, device=dev)
             ws = None
             need = rr.workspace_size(algo, p, group, n, dtype) if coll == "all_reduce" else 0
+            if coll == "all_reduce_hier":
+                need = rr.hier_workspace_size(p, group, n, dtype, **hier_kw)
             if need:
                 ws = torch.empty(need, dtype=torch.uint8, device=dev)
             send = rr._ptr_array([x[r].data_ptr() for r in range(x.shape[0])])
@@ -210,14 +219,62 @@ class Runner:
             elif coll == "broadcast":
                 xp = x[0].data_ptr()
                 call = (lambda xp=xp, d=recv: Lb.rr_broadcast(xp, d, 0, p, n, dt, sh))
+            elif coll == "scatter":
+                xp = x[0].data_ptr()
+                call = (lambda xp=xp, d=recv: Lb.rr_scatter(xp, d, 0, p, n, dt, sh))
+            elif coll == "gather":
+                yp = y[0].data_ptr()
+                call = (lambda s=send, yp=yp: Lb.rr_gather(s, yp, 0, p, n, dt, sh))
+            elif coll == "all_reduce_hier":
+                fl = rr._hier_flags(hier_kw.get("intra", "reduce"), hier_kw.get("wire_round", False),
+                                    hier_kw.get("staged", False))
+                wp, wb = (ws.data_ptr(), need) if ws is not None else (None, 0)
+                call = (lambda s=send, d=recv, fl=fl, wp=wp, wb=wb:
+                        Lb.rr_all_reduce_hier(s, d, p, n, dt, opc, group, fl, wp, wb, sh))
+            elif coll == "reduce_scatter_dim1":
+                call = (lambda s=send, d=recv: Lb.rr_reduce_scatter_dim1(s, d, p, rows, cols, dt, opc, sh))
+            elif coll == "all_gather_dim1":
+                call = (lambda s=send, d=recv: Lb.rr_all_gather_dim1(s, d, p, rows, cols, dt, sh))
             else:
                 raise ValueError(coll)
             self.sets.append((x, y, ws, send, recv, call))
-        self.bytes = rr.algorithmic_bytes(coll, p, n, dtype)
+        base = {"all_reduce_hier": "all_reduce", "reduce_scatter_dim1": "reduce_scatter",
+                "all_gather_dim1": "all_gather"}.get(coll, coll)
+        self.bytes = rr.algorithmic_bytes(base, p, n, dtype)
         self._ctypes = ctypes
 
     def step(self, i):
         st = self.sets[i % len(self.sets)][5]()
+        if st != 0:
+            raise RuntimeError(f"librr call failed: {self.L.rr_last_error().decode()}")
+
+
+class BucketRunner:
+    """Pre-marshalled bucketed all-reduce calls over rotating buffer sets: the
+    tensors of a named gradient bucket, one allocation per tensor and rank."""
+
+    def __init__(self, rr, torch, W, name, op, nsets, stream):
+        import ctypes
+
+        spec = W.BUCKETS[name]
+        self.L = rr.lib()
+        p = spec["p"]
+        parts = W.bucket_inputs(name)
+        counts = [t.shape[1] for t in parts]
+        dt, opc, sh = rr.DTYPES[spec["dtype"]], rr.OPS[op], stream.cuda_stream
+        cnt = (ctypes.c_size_t * len(counts))(*counts)
+        self.sets = []
+        for _ in range(nsets):
+            xs = [torch.from_numpy(t).to("cuda") for t in parts]
+            ys = [torch.empty_like(x) for x in xs]
+            send = rr._ptr_array([x[r].data_ptr() for x in xs for r in range(p)])
+            recv = rr._ptr_array([y[r].data_ptr() for y in ys for r in range(p)])
+            call = (lambda s=send, d=recv: self.L.rr_all_reduce_bucket(s, d, cnt, len(counts), p, dt, opc, sh))
+            self.sets.append((xs, ys, send, recv, cnt, call))
+        self.bytes = 2 * p * sum(counts) * 4
+
+    def step(self, i):
+        st = self.sets[i % len(self.sets)][-1]()
         if st != 0:
             raise RuntimeError(f"librr call failed: {self.L.rr_last_error().decode()}")
 
@@ -408,9 +465,9 @@ def extra(args, torch, rr, W, spec, host_x, stream, cpm, op, main_runner):
     p, n, dtype = spec["p"], spec["n"], spec["dtype"]
     esz = np.dtype(W.STORAGE[dtype]).itemsize
 
-    def report(tag, runner, steps, cold):
+    def report(tag, runner, steps, cold, workload=None):
         ms, _, _ = timed(torch, runner, steps, 5, stream, cpm, per_launch=False)
-        print(json.dumps({"extra": tag, "workload": args.workload, "cold_cache": cold,
+        print(json.dumps({"extra": tag, "workload": workload or args.workload, "cold_cache": cold,
                           "GBps": round(runner.bytes / ms / 1e6, 2), "ms_per_step": round(ms, 6),
                           "frac_of_peak": round(runner.bytes / ms / 1e6 / HBM_PEAK_GBPS, 4)}),
               file=sys.stderr, flush=True)
@@ -435,6 +492,56 @@ def extra(args, torch, rr, W, spec, host_x, stream, cpm, op, main_runner):
         report(f"all_reduce_{algo}" + (f"_g{G}" if G else ""), r, max(10, args.steps // 4), True)
         del r
         torch.cuda.empty_cache()
+    # AVG over the same buffers (the DDP gradient average)
+    if dtype != "int32":
+        r = Runner(rr, torch, spec, "all_reduce", "avg", main_runner.algo, spec.get("group", 0), host_x, nsets,
+                   stream)
+        report(f"all_reduce_{main_runner.algo}_avg", r, max(10, args.steps // 2), True)
+        del r
+        torch.cuda.empty_cache()
+    # scatter and gather of the rank-sized buffer
+    for coll in ("scatter", "gather"):
+        k = 1 + math.ceil(COLD_BYTES / (2 * n * esz))
+        r = Runner(rr, torch, spec, coll, op, "ring", 0, host_x, k, stream)
+        report(coll, r, max(10, args.steps // 2), True)
+        del r
+        torch.cuda.empty_cache()
+    # float16 all-reduce of the same byte size per rank
+    if esz == 4:
+        spec16 = dict(spec, dtype="float16", n=2 * n)
+        x16 = W.random_inputs(7, p, 2 * n, "float16")
+        r = Runner(rr, torch, spec16, "all_reduce", "sum", "ring", 0, x16, nsets, stream)
+        report("all_reduce_ring_float16", r, max(10, args.steps // 2), True, f"{args.workload} as float16")
+        del r, x16
+        torch.cuda.empty_cache()
+    # hierarchical variants on the hierarchy's workload
+    hspec = W.WORKLOADS["hier_bf16_p8g4_8MiB"]
+    hx = W.make_inputs("hier_bf16_p8g4_8MiB")
+    hsets = 1 + math.ceil(COLD_BYTES / (2 * hspec["p"] * hspec["n"] * 2))
+    for tag, kw in (("hier_default", {}), ("hier_intra_ring", dict(intra="ring")),
+                    ("hier_wire_round", dict(wire_round=True)),
+                    ("hier_intra_ring_wire_round", dict(intra="ring", wire_round=True))):
+        r = Runner(rr, torch, hspec, "all_reduce_hier", "sum", "hier", hspec["group"], hx, hsets, stream, hier_kw=kw)
+        report(f"all_reduce_{tag}", r, max(10, args.steps // 2), True, "hier_bf16_p8g4_8MiB")
+        del r
+        torch.cuda.empty_cache()
+    del hx
+    # bucketed all-reduce of one transformer block's gradients
+    br = BucketRunner(rr, torch, W, "gpt2_block_fp32_p8", "avg", 1 + math.ceil(COLD_BYTES / (2 * 8 * 7087872 * 4)),
+                      stream)
+    report("all_reduce_bucket_avg", br, max(10, args.steps // 2), True, "gpt2_block_fp32_p8")
+    del br
+    torch.cuda.empty_cache()
+    # tensor-parallel layouts at the row-parallel shape (8, 2048, 4096) bf16 per rank
+    tspec = dict(W.WORKLOADS["tp_rowparallel_bf16_p8"], rows=8 * 2048)
+    tx = W.make_inputs("tp_rowparallel_bf16_p8")
+    tsets = 1 + math.ceil(COLD_BYTES / ((tspec["p"] + 1) * tspec["n"] * 2))
+    for coll in ("reduce_scatter_dim1", "all_gather_dim1"):
+        r = Runner(rr, torch, tspec, coll, "sum", "ring", 0, tx, tsets, stream)
+        report(coll, r, max(10, args.steps // 4), True, "tp_rowparallel_bf16_p8")
+        del r
+        torch.cuda.empty_cache()
+    del tx
     # copy ceiling: torch's device-to-device copy of 1 GiB
     a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
