@@ -34,6 +34,7 @@ SOURCES = [
     "rr_phase_ring.hip",
     "rr_phase_hier.hip",
     "rr_phase_hier_var.hip",
+    "rr_phase_one.hip",
     "rr_phase.cpp",
     "rr_api.cpp",
     "rr_plan.cpp",

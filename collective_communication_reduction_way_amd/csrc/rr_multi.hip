@@ -157,31 +157,41 @@ __global__ __launch_bounds__(kBlock) void k_bucket(BucketArgs a) {
 
 // ---------------------------------------------------------------------------
 // Reduce-scatter along dim 1.  Row b of output c holds w elements: unit i of
-// output c (i = b*wu + j) reads unit b*du + c*wu + j of every input.
+// output c (i = b*wu + j) reads unit b*du + c*wu + j of every input.  IDX is
+// the index type: 32-bit when rows*du < 2^32 (cheap division), else 64-bit.
 
-template <class E, class OP, bool VEC>
+template <class IDX>
+__device__ __forceinline__ void row_split(IDX i, IDX w, IDX& b, IDX& j) {
+  b = i / w;
+  j = i - b * w;
+}
+
+template <class E, class OP, bool VEC, class IDX>
 __global__ __launch_bounds__(kBlock) void k_fold_cols(ColsArgs a) {
-  constexpr int U = 2;
+  constexpr int U = 4;
   using F = RotFold<E, OP, U, VEC>;
   constexpr uint64_t kUnitBytes = VEC ? 16 : sizeof(typename E::S);
   const int c = blockIdx.y;
   const int p = a.p;
-  const uint64_t total = a.rows * a.wu;
-  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock * U;
+  const IDX wu = static_cast<IDX>(a.wu);
+  const IDX du = static_cast<IDX>(a.du);
+  const IDX total = static_cast<IDX>(a.rows) * wu;
+  const IDX col0 = static_cast<IDX>(c) * wu;
+  const IDX stride = static_cast<IDX>(gridDim.x) * kBlock * U;
   char* d = static_cast<char*>(a.dst[c]);
-  for (uint64_t t0 = static_cast<uint64_t>(blockIdx.x) * kBlock * U; t0 < total; t0 += stride) {
+  for (IDX t0 = static_cast<IDX>(blockIdx.x) * kBlock * U; t0 < total; t0 += stride) {
     uint64_t in_off[U];
     uint64_t out_off[U];
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      uint64_t i = t0 + threadIdx.x + static_cast<uint64_t>(u) * kBlock;
+      IDX i = t0 + threadIdx.x + static_cast<IDX>(u) * kBlock;
       ok[u] = i < total;
       if (!ok[u]) i = total - 1;  // re-read a valid unit; never stored
-      const uint64_t b = i / a.wu;
-      const uint64_t j = i - b * a.wu;
-      in_off[u] = (b * a.du + static_cast<uint64_t>(c) * a.wu + j) * kUnitBytes;
-      out_off[u] = i * kUnitBytes;
+      IDX b, j;
+      row_split(i, wu, b, j);
+      in_off[u] = (static_cast<uint64_t>(b) * du + col0 + j) * kUnitBytes;
+      out_off[u] = static_cast<uint64_t>(i) * kUnitBytes;
     }
     typename E::A acc[U][F::V];
     F::run(a.src, c, p, in_off, a.div, acc);
@@ -192,8 +202,11 @@ __global__ __launch_bounds__(kBlock) void k_fold_cols(ColsArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// All-gather along dim 1: source c's unit i (row b, column unit j) goes to
-// unit b*du + c*wu + j of every output.
+// All-gather along dim 1, walked in output order: unit i of every output
+// (row b = i / du, column unit q = i % du) comes from source c = q / wu,
+// unit b*wu + (q - c*wu).  Consecutive lanes write consecutive units of all p
+// outputs (long contiguous runs at the same offsets) and read runs of wu
+// units from one source.
 
 template <int B>
 struct Word;
@@ -214,38 +227,40 @@ struct Word<1> {
   using T = uint8_t;
 };
 
-template <int B, bool NT>
+template <int B, bool NT, class IDX>
 __global__ __launch_bounds__(kBlock) void k_gather_cols(ColsArgs a) {
   using T = typename Word<B>::T;
-  constexpr int U = 2;
-  const int c = blockIdx.y;
-  const uint64_t total = a.rows * a.wu;
-  const T* src = static_cast<const T*>(a.src[c]);
-  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock * U;
-  for (uint64_t t0 = static_cast<uint64_t>(blockIdx.x) * kBlock * U; t0 < total; t0 += stride) {
+  constexpr int U = 4;
+  const IDX wu = static_cast<IDX>(a.wu);
+  const IDX du = static_cast<IDX>(a.du);
+  const IDX total = static_cast<IDX>(a.rows) * du;
+  const IDX stride = static_cast<IDX>(gridDim.x) * kBlock * U;
+  for (IDX t0 = static_cast<IDX>(blockIdx.x) * kBlock * U; t0 < total; t0 += stride) {
     T v[U];
-    uint64_t o[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint64_t i = t0 + threadIdx.x + static_cast<uint64_t>(u) * kBlock;
-      const uint64_t ic = i < total ? i : total - 1;
+      const IDX i = t0 + threadIdx.x + static_cast<IDX>(u) * kBlock;
+      const IDX ic = i < total ? i : total - 1;
+      IDX b, q, c, j;
+      row_split(ic, du, b, q);
+      row_split(q, wu, c, j);
+      const T* src = static_cast<const T*>(a.src[c]) + static_cast<uint64_t>(b) * wu + j;
       if constexpr (NT) {
-        v[u] = __builtin_nontemporal_load(src + ic);
+        v[u] = __builtin_nontemporal_load(src);
       } else {
-        v[u] = src[ic];
+        v[u] = *src;
       }
-      const uint64_t b = ic / a.wu;
-      o[u] = b * a.du + static_cast<uint64_t>(c) * a.wu + (ic - b * a.wu);
     }
     for (int r = 0; r < a.p; ++r) {
       T* dst = static_cast<T*>(a.dst[r]);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        if (t0 + threadIdx.x + static_cast<uint64_t>(u) * kBlock < total) {
+        const IDX i = t0 + threadIdx.x + static_cast<IDX>(u) * kBlock;
+        if (i < total) {
           if constexpr (NT) {
-            __builtin_nontemporal_store(v[u], dst + o[u]);
+            __builtin_nontemporal_store(v[u], dst + i);
           } else {
-            dst[o[u]] = v[u];
+            dst[i] = v[u];
           }
         }
       }
@@ -303,15 +318,21 @@ hipError_t bucket_by_op(const BucketArgs& a, rr_op_t op, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <class E, bool VEC>
+// 32-bit unit indices when every index of the launch, including a loop
+// counter one grid stride past the end, fits: rows*du + stride < 2^32.  The
+// stride is at most stream_grid's cap (4 workgroups per CU) times kBlock*4
+// units, far below the 2^24 margin kept here.
+bool small_index(const ColsArgs& a) { return a.du > 0 && a.rows < (0xFFFFFFFFull - (1ull << 24)) / a.du; }
+
+template <class E, bool VEC, class IDX>
 hipError_t fold_cols_by_op(const ColsArgs& a, rr_op_t op, hipStream_t s) {
-  const dim3 grid(stream_grid(a.rows * a.wu, static_cast<uint64_t>(kBlock) * 2, a.p, s), a.p);
+  const dim3 grid(stream_grid(a.rows * a.wu, static_cast<uint64_t>(kBlock) * 4, a.p, s), a.p);
   switch (op) {
-    case RR_SUM: return launch(&k_fold_cols<E, OpSum, VEC>, a, grid, s);
-    case RR_MAX: return launch(&k_fold_cols<E, OpMax, VEC>, a, grid, s);
-    case RR_MIN: return launch(&k_fold_cols<E, OpMin, VEC>, a, grid, s);
+    case RR_SUM: return launch(&k_fold_cols<E, OpSum, VEC, IDX>, a, grid, s);
+    case RR_MAX: return launch(&k_fold_cols<E, OpMax, VEC, IDX>, a, grid, s);
+    case RR_MIN: return launch(&k_fold_cols<E, OpMin, VEC, IDX>, a, grid, s);
     case RR_AVG:
-      if constexpr (__is_same(typename E::A, float)) return launch(&k_fold_cols<E, OpAvg, VEC>, a, grid, s);
+      if constexpr (__is_same(typename E::A, float)) return launch(&k_fold_cols<E, OpAvg, VEC, IDX>, a, grid, s);
       break;
   }
   return hipErrorInvalidValue;
@@ -319,7 +340,16 @@ hipError_t fold_cols_by_op(const ColsArgs& a, rr_op_t op, hipStream_t s) {
 
 template <class E>
 hipError_t fold_cols_kind(const ColsArgs& a, rr_op_t op, int vec, hipStream_t s) {
-  return vec ? fold_cols_by_op<E, true>(a, op, s) : fold_cols_by_op<E, false>(a, op, s);
+  if (small_index(a))
+    return vec ? fold_cols_by_op<E, true, uint32_t>(a, op, s) : fold_cols_by_op<E, false, uint32_t>(a, op, s);
+  return vec ? fold_cols_by_op<E, true, uint64_t>(a, op, s) : fold_cols_by_op<E, false, uint64_t>(a, op, s);
+}
+
+template <int B, bool NT>
+hipError_t gather_cols_go(const ColsArgs& a, hipStream_t s) {
+  const dim3 grid(stream_grid(a.rows * a.du, static_cast<uint64_t>(kBlock) * 4, 1, s));
+  return small_index(a) ? launch(&k_gather_cols<B, NT, uint32_t>, a, grid, s)
+                        : launch(&k_gather_cols<B, NT, uint64_t>, a, grid, s);
 }
 
 }  // namespace
@@ -348,13 +378,12 @@ hipError_t launch_fold_cols(const ColsArgs& a, Kind k, rr_op_t op, int vec, hipS
 
 hipError_t launch_gather_cols(const ColsArgs& a, int unit_bytes, int nontemporal, hipStream_t s) {
   if (a.rows * a.wu == 0) return hipSuccess;
-  const dim3 grid(stream_grid(a.rows * a.wu, static_cast<uint64_t>(kBlock) * 2, a.p, s), a.p);
   const bool nt = nontemporal != 0;
   switch (unit_bytes) {
-    case 16: return nt ? launch(&k_gather_cols<16, true>, a, grid, s) : launch(&k_gather_cols<16, false>, a, grid, s);
-    case 4: return nt ? launch(&k_gather_cols<4, true>, a, grid, s) : launch(&k_gather_cols<4, false>, a, grid, s);
-    case 2: return nt ? launch(&k_gather_cols<2, true>, a, grid, s) : launch(&k_gather_cols<2, false>, a, grid, s);
-    case 1: return nt ? launch(&k_gather_cols<1, true>, a, grid, s) : launch(&k_gather_cols<1, false>, a, grid, s);
+    case 16: return nt ? gather_cols_go<16, true>(a, s) : gather_cols_go<16, false>(a, s);
+    case 4: return nt ? gather_cols_go<4, true>(a, s) : gather_cols_go<4, false>(a, s);
+    case 2: return nt ? gather_cols_go<2, true>(a, s) : gather_cols_go<2, false>(a, s);
+    case 1: return nt ? gather_cols_go<1, true>(a, s) : gather_cols_go<1, false>(a, s);
   }
   return hipErrorInvalidValue;
 }

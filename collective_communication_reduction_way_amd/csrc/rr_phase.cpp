@@ -92,6 +92,8 @@ hipError_t launch_mode(const FoldLaunch& f, const PhaseArgs& a, unsigned grid, i
     case FoldMode::kHierRing:
     case FoldMode::kHierAllWire:
     case FoldMode::kHierRingWire: return phase_launch_hier_var(a, f.mode, f.in_kind, f.op, grid, unroll, sync, occ, s);
+    case FoldMode::kRingShard:
+    case FoldMode::kAscOne: return phase_launch_one(a, f.mode, f.in_kind, f.op, grid, unroll, sync, static_p, occ, s);
     default: break;
   }
   return hipErrorInvalidValue;
@@ -102,8 +104,9 @@ hipError_t launch_mode(const FoldLaunch& f, const PhaseArgs& a, unsigned grid, i
 int phase_default_unroll(Kind k, FoldMode m) { return (is_hier(m) && is_half(k)) ? 4 : 8; }
 
 bool phase_supported(const FoldLaunch& f) {
-  return (f.mode == FoldMode::kRingAll || is_hier(f.mode)) && f.args.vec && f.in_kind == f.out_kind &&
-         f.segments >= 1 && f.segments <= RR_MAX_RANKS;
+  const bool mode_ok = f.mode == FoldMode::kRingAll || is_hier(f.mode) || f.mode == FoldMode::kRingShard ||
+                       f.mode == FoldMode::kAscOne;
+  return mode_ok && f.args.vec && f.in_kind == f.out_kind && f.segments >= 1 && f.segments <= RR_MAX_RANKS;
 }
 
 // Schedule choice (measured on MI355X; every knob can be forced through
@@ -114,7 +117,9 @@ bool phase_supported(const FoldLaunch& f) {
 //     per CU (shorter phases between barriers); the kernel compiled for
 //     p = 8 for bfloat16, the run-time rank loop for 4-byte types;
 //   hierarchical all-reduce: the run-time rank loop, 4 workgroups per CU with
-//     the bfloat16 tile of 4 groups per lane, else 2.
+//     the bfloat16 tile of 4 groups per lane, else 2;
+//   reduce-scatter and reduce: 4 groups per lane for sums (8 for max/min),
+//     4 workgroups per CU, the kernel compiled for p = 8, no barrier.
 // With the barrier, the grid never exceeds what the device can keep resident
 // at once (the kernel's occupancy times the compute units): workgroups that
 // had to wait for a free slot would make every barrier run into its timeout.
@@ -132,10 +137,15 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
   const bool ring = f.mode == FoldMode::kRingAll;
   const uint64_t V = is_half(f.in_kind) ? 8 : 4;
   const bool sum_like = f.op == RR_SUM || f.op == RR_AVG;
-  bool static_p = pt.static_p >= 0 ? pt.static_p != 0 : ring;
+  // the kernels compiled for p = 8: default for the modes that read p inputs
+  // and write one output or all of them in ring order
+  bool static_p = pt.static_p >= 0 ? pt.static_p != 0
+                                   : (ring || f.mode == FoldMode::kRingShard || f.mode == FoldMode::kAscOne);
+  // reduce-scatter and reduce: one output per p inputs
+  const bool one_out = f.mode == FoldMode::kRingShard || f.mode == FoldMode::kAscOne;
   int unroll = phase_default_unroll(f.in_kind, f.mode);
-  if (pt.unroll == 4 && sum_like) unroll = 4;
-  int per_cu = pt.per_cu > 0 ? pt.per_cu : (unroll == 4 ? 4 : 2);
+  if ((pt.unroll == 4 || (one_out && pt.unroll == 0)) && sum_like) unroll = 4;
+  int per_cu = pt.per_cu > 0 ? pt.per_cu : (unroll == 4 || one_out ? 4 : 2);
 
   PhaseArgs a;
   memset(&a, 0, sizeof(a));
@@ -156,7 +166,9 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
   if (grid > tiles) grid = tiles;
   if (grid < 1) grid = 1;
   a.rounds = static_cast<uint32_t>((tiles + grid - 1) / grid);
-  const bool sync = pt.sync && a.rounds > 1 && tiles <= kMaxBarrierTiles;
+  // Writes are 1/(p+1) of the traffic of the one-output modes: separating the
+  // phases gains nothing there (measured), so they run without the barrier.
+  const bool sync = pt.sync && !one_out && a.rounds > 1 && tiles <= kMaxBarrierTiles;
   if (sync) {
     // occupancy of the kernel about to run, cached per device and kernel
     const uint32_t key = (static_cast<uint32_t>(f.mode) << 16) | (static_cast<uint32_t>(f.in_kind) << 12) |
@@ -200,10 +212,12 @@ hipError_t phase_barrier_timeouts(int device, unsigned long long* count) {
   unsigned long long ring = 0;
   unsigned long long hier = 0;
   unsigned long long var = 0;
+  unsigned long long one = 0;
   e = phase_timeouts_ring(&ring);
   if (e == hipSuccess) e = phase_timeouts_hier(&hier);
   if (e == hipSuccess) e = phase_timeouts_hier_var(&var);
-  *count = ring + hier + var;
+  if (e == hipSuccess) e = phase_timeouts_one(&one);
+  *count = ring + hier + var + one;
   if (device != cur) {
     const hipError_t e2 = hipSetDevice(cur);
     if (e == hipSuccess) e = e2;

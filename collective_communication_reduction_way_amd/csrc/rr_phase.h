@@ -70,5 +70,10 @@ hipError_t phase_launch_hier_var(const PhaseArgs& a, FoldMode m, Kind k, rr_op_t
 hipError_t phase_timeouts_ring(unsigned long long* count);
 hipError_t phase_timeouts_hier(unsigned long long* count);
 hipError_t phase_timeouts_hier_var(unsigned long long* count);
+// Reduce-scatter (kRingShard) and reduce (kAscOne): one output per input
+// set (rr_phase_one.hip).
+hipError_t phase_launch_one(const PhaseArgs& a, FoldMode m, Kind k, rr_op_t op, unsigned grid, int unroll, bool sync,
+                            bool static_p, int* occ, hipStream_t s);
+hipError_t phase_timeouts_one(unsigned long long* count);
 
 }  // namespace rr

@@ -38,8 +38,8 @@
 // results are unaffected.
 //
 // Used for the folds that write every rank (ring and hierarchical
-// all-reduce), whose traffic is half reads and half writes; reduce-scatter
-// and reduce write one output per p inputs and keep the single-pass kernel.
+// all-reduce), whose traffic is half reads and half writes, and for
+// reduce-scatter and reduce, which write one output per p inputs.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -328,13 +328,16 @@ hipError_t phase_by_p(const PhaseArgs& a, unsigned grid, int unroll, bool sync, 
                       hipStream_t s) {
   hipError_t e;
   // the hierarchical variants are compiled with the run-time loop only
-  constexpr bool kStatic = M == FoldMode::kRingAll || M == FoldMode::kHierAll;
+  constexpr bool kStatic = M == FoldMode::kRingAll || M == FoldMode::kHierAll || M == FoldMode::kRingShard ||
+                           M == FoldMode::kAscOne;
+  // reduce-scatter and reduce are compiled without the barrier
+  constexpr bool kSync = writes_all(M);
   if (kStatic && static_p && a.f.p == 8) {
-    e = sync ? phase_by_u<E, OP, kStatic ? 8 : 0, M, true>(a, grid, unroll, occ, s)
-             : phase_by_u<E, OP, kStatic ? 8 : 0, M, false>(a, grid, unroll, occ, s);
+    e = (kSync && sync) ? phase_by_u<E, OP, kStatic ? 8 : 0, M, kSync>(a, grid, unroll, occ, s)
+                        : phase_by_u<E, OP, kStatic ? 8 : 0, M, false>(a, grid, unroll, occ, s);
   } else {
-    e = sync ? phase_by_u<E, OP, 0, M, true>(a, grid, unroll, occ, s)
-             : phase_by_u<E, OP, 0, M, false>(a, grid, unroll, occ, s);
+    e = (kSync && sync) ? phase_by_u<E, OP, 0, M, kSync>(a, grid, unroll, occ, s)
+                        : phase_by_u<E, OP, 0, M, false>(a, grid, unroll, occ, s);
   }
   if (e != hipSuccess || occ || !a.edges) return e;
   return phase_go(&k_edges<E, OP, M>, a, static_cast<unsigned>(a.segments), 64, nullptr, s);

@@ -1,0 +1,21 @@
+// Instantiations of the phased fold for the folds with one output per set of
+// p inputs: FoldMode::kRingShard (reduce-scatter, chunk c to rank c) and
+// FoldMode::kAscOne (reduce to the root).
+#include "rr_phase_impl.h"
+
+namespace rr {
+
+hipError_t phase_launch_one(const PhaseArgs& a, FoldMode m, Kind k, rr_op_t op, unsigned grid, int unroll, bool sync,
+                            bool static_p, int* occ, hipStream_t s) {
+  switch (m) {
+    case FoldMode::kRingShard:
+      return phase_dispatch<FoldMode::kRingShard>(a, k, op, grid, unroll, sync, static_p, occ, s);
+    case FoldMode::kAscOne: return phase_dispatch<FoldMode::kAscOne>(a, k, op, grid, unroll, sync, static_p, occ, s);
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t phase_timeouts_one(unsigned long long* count) { return phase_timeouts_here(count); }
+
+}  // namespace rr

@@ -106,3 +106,34 @@ def test_schedules_agree_bitwise(rr, monkeypatch, env):
     assert_bitwise(run_ar(rr, x, "float32", "sum", "ring"), want, f"ring {env}")
     assert_bitwise(run_ar(rr, x, "float32", "sum", "hier", 4), want_h, f"hier {env}")
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("env", [{"RR_PHASE": "0"}, {}, {"RR_PHASE_SYNC": "0"}, {"RR_PHASE_STATIC": "0"},
+                                 {"RR_PHASE_U": "4"}, {"RR_PHASE_GRID": "37"}, {"RR_PHASE_PER_CU": "8"}])
+def test_reduce_scatter_and_reduce_schedules_agree(rr, monkeypatch, env):
+    """Reduce-scatter (one chunk per rank) and reduce (one output) through the
+    single-pass kernel and every schedule of the phased one, at a size that
+    takes several rounds: the same bits as the oracle."""
+    p, L = 8, (1 << 20) + 8 * 3
+    n = p * L
+    x = W.random_inputs(66, p, n, "float32")
+    want_rs = C.reduce_scatter_ring(x, "sum", "float32")
+    want_red = C.reduce(x, "sum", "float32")
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    t0 = rr.barrier_timeouts()
+    xs = to_dev(x, "float32")
+    sh = torch.empty((p, L), dtype=torch.float32, device="cuda")
+    rr.reduce_scatter(xs, sh)
+    assert_bitwise(to_host(sh, "float32"), want_rs, f"reduce_scatter {env}")
+    red = torch.empty(n, dtype=torch.float32, device="cuda")
+    rr.reduce(xs, red, root=3)
+    assert_bitwise(to_host(red, "float32"), want_red, f"reduce {env}")
+    xb = W.random_inputs(67, p, n + 5, "bfloat16")  # a tail that is not a whole group
+    red_b = torch.empty(n + 5, dtype=torch.bfloat16, device="cuda")
+    rr.reduce(to_dev(xb, "bfloat16"), red_b)
+    assert_bitwise(to_host(red_b, "bfloat16"), C.reduce(xb, "sum", "bfloat16"), f"reduce bf16 {env}")
+    if env.get("RR_PHASE_PER_CU") != "8":
+        assert rr.barrier_timeouts() == t0
+    del xs, sh, red, red_b
+    torch.cuda.empty_cache()
