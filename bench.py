@@ -485,7 +485,7 @@ def extra(args, torch, rr, W, spec, host_x, stream, cpm, op, main_runner):
         report(coll, r, max(10, args.steps // 2), True)
         del r
         torch.cuda.empty_cache()
-    for algo, G in (("ring_staged", 0), ("hier", 4), ("hier_staged", 4)):
+    for algo, G in (("ring_staged", 0), ("ring_persistent", 0), ("hier", 4), ("hier_staged", 4)):
         if p % max(G, 1):
             continue
         r = Runner(rr, torch, spec, "all_reduce", op, algo, G, host_x, nsets, stream)

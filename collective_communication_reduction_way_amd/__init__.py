@@ -49,6 +49,7 @@ __all__ = [
     "lib",
     "version",
     "barrier_timeouts",
+    "ring_exec_failures",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -56,7 +57,7 @@ _LIB_PATH = os.path.join(_HERE, "librr.so")
 
 DTYPES = {"int32": 0, "float32": 1, "bfloat16": 2, "float16": 3}
 OPS = {"sum": 0, "max": 1, "min": 2, "avg": 3}
-ALGOS = {"ring": 0, "ring_staged": 1, "hier": 2, "hier_staged": 3}
+ALGOS = {"ring": 0, "ring_staged": 1, "hier": 2, "hier_staged": 3, "ring_persistent": 4}
 COLLS = {"all_reduce": 0, "reduce_scatter": 1, "all_gather": 2, "reduce": 3, "broadcast": 4, "scatter": 5,
          "gather": 6}
 MAX_RANKS = 64
@@ -125,6 +126,7 @@ def lib():
         "rr_status_string": (ctypes.c_char_p, [I]),
         "rr_last_error": (ctypes.c_char_p, []),
         "rr_barrier_timeouts": (I, [I, U64P]),
+        "rr_ring_exec_failures": (I, [I, U64P]),
         "rr_version": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -145,6 +147,19 @@ def barrier_timeouts(device=None):
     dev = torch.cuda.current_device() if device is None else int(device)
     out = ctypes.c_uint64(0)
     _check(lib().rr_barrier_timeouts(dev, ctypes.byref(out)), "rr_barrier_timeouts")
+    return int(out.value)
+
+
+def ring_exec_failures(device=None):
+    """How many launches of the persistent ring executor (algo
+    "ring_persistent") on `device` stopped on a timed-out wait since the
+    library was loaded (their outputs are incomplete).  Synchronizes the
+    device."""
+    import torch
+
+    dev = torch.cuda.current_device() if device is None else int(device)
+    out = ctypes.c_uint64(0)
+    _check(lib().rr_ring_exec_failures(dev, ctypes.byref(out)), "rr_ring_exec_failures")
     return int(out.value)
 
 
@@ -220,8 +235,9 @@ def all_reduce(ins, outs=None, op="sum", algo="ring", group_size=0, workspace=No
     """Every rank's output becomes the reduction of all p inputs.
 
     outs=None reduces in place.  algo: "ring" (one fused pass in ring order),
-    "ring_staged" (the ring schedule step by step), "hier" / "hier_staged"
-    (groups of ``group_size`` consecutive ranks).  The staged algorithms may
+    "ring_staged" (the ring schedule step by step, one launch per step),
+    "ring_persistent" (the ring schedule in one persistent kernel), "hier" /
+    "hier_staged" (groups of ``group_size`` consecutive ranks).  The staged algorithms may
     need a device workspace of ``workspace_size(...)`` bytes (a uint8 tensor);
     when it is not given, one is allocated with torch for the call.
     """

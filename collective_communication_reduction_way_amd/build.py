@@ -31,6 +31,7 @@ SOURCES = [
     "rr_fold_asc_one.hip",
     "rr_copy.hip",
     "rr_multi.hip",
+    "rr_exec.hip",
     "rr_phase_ring.hip",
     "rr_phase_hier.hip",
     "rr_phase_hier_var.hip",

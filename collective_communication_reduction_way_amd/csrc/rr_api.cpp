@@ -66,11 +66,20 @@ int env_int(const char* name, int dflt) {
 // smaller tile for sums), RR_PHASE_STATIC (1 / 0 = the kernels compiled for
 // p = 8 / the run-time rank loop; -1 = by mode),
 // RR_PHASE_TIMEOUT_US (bound of one barrier wait, default 200),
+// RR_EXEC_TIMEOUT_US (bound of one wait of the persistent ring executor on a
+// neighbour's flag, default 1 s), RR_EXEC_PER_CU (cap on its workgroups per
+// compute unit; 0 = as many as stay resident), RR_EXEC_SLICES (slices per
+// chunk, 1..64; 0 = by chunk size),
 // RR_LOG (1 = print each launch plan to stderr).  Defaults are the measured
 // best on MI355X: every byte of these collectives is touched once, so
 // nontemporal access (no reuse expected) keeps the caches from holding dead
 // lines, and separating the read and write traffic of the fused folds in time
 // raises their HBM throughput.
+// Slices per chunk of the persistent ring executor (0 = by size): every
+// worker writes its XCD's L2 back once per step, so fewer, larger workers
+// measured faster -- 16 slices at 1 MiB chunks, 32 at 12 MiB chunks.
+constexpr int kExecDefaultSlices = 0;
+
 struct Tuning {
   int unroll;
   int nontemporal;
@@ -78,6 +87,9 @@ struct Tuning {
   int log;
   int phase;
   rr::PhaseTuning pt;
+  int exec_timeout_us;
+  int exec_per_cu;
+  int exec_slices;
 };
 
 Tuning tuning() {
@@ -99,6 +111,11 @@ Tuning tuning() {
   t.pt.static_p = env_int("RR_PHASE_STATIC", -1);
   if (t.pt.static_p > 1) t.pt.static_p = 1;
   if (t.pt.timeout_us < 1) t.pt.timeout_us = 200;
+  t.exec_timeout_us = env_int("RR_EXEC_TIMEOUT_US", 1000000);
+  if (t.exec_timeout_us < 1) t.exec_timeout_us = 1;
+  t.exec_per_cu = env_int("RR_EXEC_PER_CU", 0);
+  if (t.exec_per_cu < 0) t.exec_per_cu = 0;
+  t.exec_slices = env_int("RR_EXEC_SLICES", kExecDefaultSlices);
   return t;
 }
 
@@ -452,6 +469,33 @@ rr_status_t ar_ring_staged(const void* const* send, void* const* recv, int p, ui
   return RR_SUCCESS;
 }
 
+// The ring schedule in one persistent kernel: the staged algorithm's
+// buffers (float32 workspace slots for 16-bit types, else the outputs as
+// working buffers) and arithmetic, steps handed on through device flags.
+rr_status_t ar_ring_exec(const void* const* send, void* const* recv, int p, uint64_t n, rr_dtype_t dt, rr_op_t op,
+                         void* ws, const Tuning& t, hipStream_t s) {
+  rr::ExecArgs a;
+  memset(&a, 0, sizeof(a));
+  const bool half = is_half_dtype(dt);
+  bool vec = true;
+  for (int r = 0; r < p; ++r) {
+    a.in[r] = send[r];
+    a.out[r] = recv[r];
+    a.work[r] = half ? static_cast<char*>(ws) + static_cast<uint64_t>(r) * n * 4 : recv[r];
+    vec = vec && aligned16(send[r]) && aligned16(recv[r]) && aligned16(a.work[r]);
+  }
+  rr::chunk_bounds(p, n, a.bound);
+  a.p = p;
+  a.div = divisor_for(op, p);
+  a.vec = vec ? 1 : 0;
+  int slices = t.exec_slices;
+  if (slices <= 0) slices = (a.bound[1] - a.bound[0]) * rr::elem_size(dt) > (4ull << 20) ? 32 : 16;
+  if (t.log) fprintf(stderr, "[rr] all_reduce(ring, persistent): p=%d n=%llu vec=%d\n", p, (unsigned long long)n, a.vec);
+  const hipError_t e = rr::launch_ring_exec(a, kind_of(dt), op, t.exec_per_cu, slices, t.exec_timeout_us, s);
+  if (e != hipSuccess) return hip_fail(e, "all_reduce(ring, persistent)");
+  return RR_SUCCESS;
+}
+
 rr_status_t ar_hier_staged(const void* const* send, void* const* recv, int p, uint64_t n, rr_dtype_t dt, rr_op_t op,
                            int G, int flags, void* ws, const Tuning& t, hipStream_t s) {
   const int J = p / G;
@@ -519,7 +563,8 @@ rr_status_t ar_hier_staged(const void* const* send, void* const* recv, int p, ui
 
 size_t workspace_bytes(rr_algo_t algo, int p, int G, uint64_t n, rr_dtype_t dt, int flags = 0) {
   switch (algo) {
-    case RR_ALGO_RING_STAGED: return is_half_dtype(dt) ? static_cast<size_t>(p) * n * 4 : 0;
+    case RR_ALGO_RING_STAGED:
+    case RR_ALGO_RING_PERSISTENT: return is_half_dtype(dt) ? static_cast<size_t>(p) * n * 4 : 0;
     case RR_ALGO_HIER_STAGED: {
       const bool wire = (flags & RR_HIER_WIRE_ROUND) && is_half_dtype(dt);
       return static_cast<size_t>(p / G) * n * (wire ? rr::elem_size(dt) : 4);
@@ -537,7 +582,7 @@ rr_status_t all_reduce_impl(const void* const* sendbufs, void* const* recvbufs, 
   if ((st = check_p(p)) || (st = check_dtype(dtype)) || (st = check_op_dtype(op, dtype)) || (st = check_n(n)))
     return st;
   if (algo != RR_ALGO_RING_FUSED && algo != RR_ALGO_RING_STAGED && algo != RR_ALGO_HIER_FUSED &&
-      algo != RR_ALGO_HIER_STAGED)
+      algo != RR_ALGO_HIER_STAGED && algo != RR_ALGO_RING_PERSISTENT)
     return fail(RR_ERROR_INVALID_ARGUMENT, "unknown algo %d", static_cast<int>(algo));
   const bool hier = algo == RR_ALGO_HIER_FUSED || algo == RR_ALGO_HIER_STAGED;
   if (hier && (group_size < 1 || group_size > p || p % group_size))
@@ -573,6 +618,7 @@ rr_status_t all_reduce_impl(const void* const* sendbufs, void* const* recvbufs, 
   switch (algo) {
     case RR_ALGO_RING_FUSED: st = ar_ring_fused(sendbufs, recvbufs, p, n, dtype, op, t, s); break;
     case RR_ALGO_RING_STAGED: st = ar_ring_staged(sendbufs, recvbufs, p, n, dtype, op, workspace, t, s); break;
+    case RR_ALGO_RING_PERSISTENT: st = ar_ring_exec(sendbufs, recvbufs, p, n, dtype, op, workspace, t, s); break;
     case RR_ALGO_HIER_FUSED:
       st = ar_hier_fused(sendbufs, recvbufs, p, n, dtype, op, group_size, flags, t, s);
       break;
@@ -1089,6 +1135,19 @@ rr_status_t rr_barrier_timeouts(int device, uint64_t* count) {
   unsigned long long c = 0;
   e = rr::phase_barrier_timeouts(device, &c);
   if (e != hipSuccess) return hip_fail(e, "barrier_timeouts");
+  *count = c;
+  return ok();
+}
+
+rr_status_t rr_ring_exec_failures(int device, uint64_t* count) {
+  if (!count) return fail(RR_ERROR_INVALID_ARGUMENT, "count is NULL");
+  int ndev = 0;
+  hipError_t e = hipGetDeviceCount(&ndev);
+  if (e != hipSuccess) return hip_fail(e, "ring_exec_failures");
+  if (device < 0 || device >= ndev) return fail(RR_ERROR_INVALID_ARGUMENT, "device %d outside [0, %d)", device, ndev);
+  unsigned long long c = 0;
+  e = rr::ring_exec_failures(device, &c);
+  if (e != hipSuccess) return hip_fail(e, "ring_exec_failures");
   *count = c;
   return ok();
 }

@@ -1,0 +1,361 @@
+// rr_exec.hip -- the ring schedule executed by one persistent kernel (gfx950).
+//
+// Page "LLM Parallelism 基础", section "Ring AllReduce": p-1 reduce-scatter
+// steps in which every rank passes one chunk to the next rank, which
+// accumulates it, then p-1 all-gather steps in which the next rank
+// overwrites its copy.  The staged algorithm runs each step as a launch of
+// its own; here one launch runs them all, the ranks advancing independently
+// and handing chunks on through completion flags in device memory -- the
+// structure a multi-GPU ring has, with the rank buffers playing the part of
+// peer memory.
+//
+// Workers.  The workgroups are (slice b, rank q) pairs, slice-major.  Every
+// chunk is cut into B slices; worker (b, q) performs rank q's side of every
+// step for slice b of the chunk that step moves.  Workers of different
+// slices never wait for each other.
+//
+// Steps of worker (b, q), with r = q-1 mod p the ring predecessor:
+//   t = 0          copy-in: slice b of every chunk of rank q into its working
+//                  buffer (float32 for 16-bit types, else the output itself);
+//   t = 1..p-1     reduce-scatter step s = t-1: chunk c = (r-1-s) mod p,
+//                  work[q] = work[r] (+) work[q] on slice b (message first, as
+//                  the receiver of the ring accumulates); after the last one
+//                  rank q owns chunk q and finishes it (AVG's division, the
+//                  one rounding of 16-bit types) into its output;
+//   t = p..2p-2    all-gather step s = t-p: chunk c = (r-s) mod p,
+//                  out[q] = out[r] on slice b.
+// flag[q][b] counts the steps worker (b, q) has completed.  Step t of (b, q)
+// reads what (b, r) wrote in step t-1, so it waits for flag[r][b] >= t.  When
+// the working buffer is the output (4-byte types), all-gather step s
+// overwrites the chunk that (b, q+1) read from rank q in reduce-scatter step
+// s, so it also waits for flag[q+1][b] >= s+2.  Every wait points to an
+// earlier step, so the waits form no cycle.
+//
+// Memory ordering.  The flags order data between workgroups on different
+// XCDs, each with its own L2.  To publish a step, every wave waits until its
+// stores are acknowledged by the L2 (s_waitcnt 0), the workgroup meets at a
+// barrier, and thread 0 takes an agent-scope release fence -- on gfx950 an
+// L2 write-back of the whole XCD's L2 (buffer_wbl2 sc1), which therefore
+// covers every wave's stores -- before it raises the flag.  A waiter's
+// thread 0 sees the flag and takes an agent-scope acquire fence, which
+// invalidates the CU's L1 and the XCD's L2 for every wave (buffer_inv sc1),
+// before the workgroup barrier that releases the readers.  One write-back
+// and one invalidation per workgroup and step: a fence in every thread
+// measured five times slower (each write-back walks the L2).
+//
+// Flags hold (launch tag << 24) + steps; each launch has a fresh, larger tag
+// and raises flags with atomic max, so nothing needs resetting.  Every wait
+// is bounded by a wall-clock timeout; a worker that times out (workers not
+// all resident, for instance) raises the slot's abort word, counts the
+// failure and stops, and every other waiter of the launch stops as soon as
+// it sees the abort word.  A failed launch leaves its outputs incomplete;
+// rr_ring_exec_failures() reports it.  The host caps the grid at what the
+// device keeps resident, and workgroups are dispatched in order, so a slice's
+// workers start together.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <algorithm>
+#include <map>
+#include <mutex>
+
+#include "rr_device.h"
+#include "rr_kernels.h"
+
+namespace rr {
+
+namespace {
+
+constexpr int kExecSlots = 16;
+constexpr int kExecMaxWorkers = 2048;  // p * B per launch
+constexpr int kExecStride = 8;         // 64-bit words: one 64-byte line per flag
+constexpr int kExecShift = 24;         // flag = (tag << 24) + steps
+
+__device__ __align__(256) unsigned long long g_exec_flags[kExecSlots * kExecMaxWorkers * kExecStride];
+__device__ __align__(256) unsigned long long g_exec_abort[kExecSlots * 16];
+__device__ unsigned long long g_exec_failures;
+
+__device__ __forceinline__ unsigned long long* exec_flag(uint32_t slot, int worker) {
+  return g_exec_flags + (static_cast<size_t>(slot) * kExecMaxWorkers + worker) * kExecStride;
+}
+
+// Wait until *f >= target, the launch's abort word is raised, or the bound
+// runs out.  Thread 0 only.  Returns false when the launch must stop.
+__device__ bool wait_flag(const ExecArgs& a, const unsigned long long* f, unsigned long long target) {
+  unsigned long long* abort_word = g_exec_abort + a.slot * 16;
+  const uint64_t t0 = wall_clock64();
+  while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    if (__hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= a.tag) return false;
+    __builtin_amdgcn_s_sleep(1);
+    if (wall_clock64() - t0 > a.timeout_ticks) {
+      // the first worker to give up on this launch counts it
+      const unsigned long long was = __hip_atomic_fetch_max(abort_word, a.tag, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT);
+      if (was < a.tag) __hip_atomic_fetch_add(&g_exec_failures, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+  }
+  return true;
+}
+
+// Apply `f` to the elements [e0, e1) of a slice: whole 8-element units where
+// every buffer involved is 16-byte aligned (vec), single elements elsewhere.
+template <class FV, class FS>
+__device__ __forceinline__ void for_slice(uint64_t e0, uint64_t e1, bool vec, FV&& fv, FS&& fs) {
+  const uint32_t lane = threadIdx.x;
+  uint64_t u0 = e1, u1 = e1;
+  if (vec) {
+    u0 = (e0 + 7) / 8 * 8;
+    u1 = e1 / 8 * 8;
+    if (u1 < u0) u0 = u1 = e1;
+  }
+  for (uint64_t i = e0 + lane; i < (vec ? u0 : e1); i += kBlock) fs(i);
+  for (uint64_t g = u0 / 8 + lane; g < u1 / 8; g += kBlock) fv(g * 8);
+  for (uint64_t i = u1 + lane; i < e1; i += kBlock) fs(i);
+}
+
+// E: storage kind; EA: accumulator kind of the working buffers.
+template <class E, class EA, class OP>
+__global__ __launch_bounds__(kBlock) void k_ring_exec(ExecArgs a) {
+  using S = typename E::S;
+  using SA = typename EA::S;
+  using A = typename E::A;
+  const int p = a.p;
+  const int b = blockIdx.x / p;
+  const int q = blockIdx.x - b * p;
+  const int r = q == 0 ? p - 1 : q - 1;
+  const int nx = q + 1 == p ? 0 : q + 1;
+  const bool vec = a.vec != 0;
+  constexpr bool kSeparate = !__is_same(E, EA);  // working buffers apart from the outputs
+  __shared__ int go;
+  auto slice_lo = [&](int c) {
+    const uint64_t len = a.bound[c + 1] - a.bound[c];
+    return a.bound[c] + len * static_cast<uint64_t>(b) / static_cast<uint64_t>(a.nslices);
+  };
+  auto slice_hi = [&](int c) {
+    const uint64_t len = a.bound[c + 1] - a.bound[c];
+    return a.bound[c] + len * static_cast<uint64_t>(b + 1) / static_cast<uint64_t>(a.nslices);
+  };
+  SA* wq = static_cast<SA*>(a.work[q]);
+  for (int t = 0; t <= 2 * p - 2; ++t) {
+    // wait for the predecessor's step t-1 (and, for an all-gather overwrite
+    // of a working buffer, for the successor's read of it)
+    if (t > 0) {
+      if (threadIdx.x == 0) {
+        bool ok = wait_flag(a, exec_flag(a.slot, b * p + r), a.tag + static_cast<unsigned long long>(t));
+        if (ok && !kSeparate && t >= p)
+          ok = wait_flag(a, exec_flag(a.slot, b * p + nx), a.tag + static_cast<unsigned long long>(t - p + 2));
+        if (ok) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        go = ok ? 1 : 0;
+      }
+      __syncthreads();
+      if (!go) return;
+    }
+    if (t == 0) {
+      // copy-in of slice b of every chunk of rank q
+      const S* in = static_cast<const S*>(a.in[q]);
+      if (kSeparate || static_cast<const void*>(in) != static_cast<const void*>(wq)) {
+        for (int c = 0; c < p; ++c) {
+          for_slice(
+              slice_lo(c), slice_hi(c), vec,
+              [&](uint64_t i) {
+                Raw<E, 8> x;
+                load_group<true>(x, in + i);
+                A v[8];
+                unpack(x, v);
+                Raw<EA, 8> y;
+                pack(v, y);
+                store_group<true>(wq + i, y);
+              },
+              [&](uint64_t i) { store_one<EA>(wq + i, load_one<E>(in + i)); });
+        }
+      }
+    } else if (t < p) {
+      // reduce-scatter step s: the message from rank r is folded first
+      const int s = t - 1;
+      int c = r - 1 - s;
+      while (c < 0) c += p;
+      const SA* wr = static_cast<const SA*>(a.work[r]);
+      for_slice(
+          slice_lo(c), slice_hi(c), vec,
+          [&](uint64_t i) {
+            Raw<EA, 8> m, l;
+            load_group<false>(m, wr + i);
+            load_group<false>(l, wq + i);
+            A vm[8], vl[8];
+            unpack(m, vm);
+            unpack(l, vl);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) vm[j] = OP::apply(vm[j], vl[j]);
+            pack(vm, m);
+            store_group<false>(wq + i, m);
+          },
+          [&](uint64_t i) { store_one<EA>(wq + i, OP::apply(load_one<EA>(wr + i), load_one<EA>(wq + i))); });
+      if (t == p - 1 && (kSeparate || is_avg<OP>())) {
+        // rank q now owns chunk q: the op's last step, the one conversion
+        __syncthreads();
+        S* oq = static_cast<S*>(a.out[q]);
+        for_slice(
+            slice_lo(q), slice_hi(q), vec,
+            [&](uint64_t i) {
+              Raw<EA, 8> x;
+              load_group<false>(x, wq + i);
+              A v[8];
+              unpack(x, v);
+#pragma unroll
+              for (int j = 0; j < 8; ++j) v[j] = op_finish<OP>(v[j], a.div);
+              Raw<E, 8> y;
+              pack(v, y);
+              store_group<false>(oq + i, y);
+            },
+            [&](uint64_t i) { store_one<E>(oq + i, op_finish<OP>(load_one<EA>(wq + i), a.div)); });
+      }
+    } else {
+      // all-gather step s: rank q overwrites its copy of chunk c
+      const int s = t - p;
+      int c = r - s;
+      while (c < 0) c += p;
+      const S* orr = static_cast<const S*>(a.out[r]);
+      S* oq = static_cast<S*>(a.out[q]);
+      for_slice(
+          slice_lo(c), slice_hi(c), vec,
+          [&](uint64_t i) {
+            Raw<E, 8> x;
+            load_group<false>(x, orr + i);
+            store_group<false>(oq + i, x);
+          },
+          [&](uint64_t i) { oq[i] = orr[i]; });
+    }
+    // publish step t: every wave's stores acknowledged, then one release
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_fetch_max(exec_flag(a.slot, b * p + q), a.tag + static_cast<unsigned long long>(t + 1),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side: per-device launch tags, a slot per stream, the resident-grid cap.
+
+constexpr int kMaxDevices = 64;
+
+struct ExecDevice {
+  std::once_flag once;
+  int cus = 0;
+  int wall_khz = 0;
+  unsigned long long launches = 0;
+  std::mutex mu;
+  std::map<hipStream_t, uint32_t> slot_of;
+  std::map<uint32_t, int> occupancy;
+};
+
+ExecDevice g_exec_dev[kMaxDevices];
+
+template <class E, class EA, class OP>
+hipError_t exec_go(ExecArgs a, int budget_per_cu_cap, int max_slices, int timeout_us, hipStream_t s, ExecDevice& d,
+                   uint32_t key) {
+  const void* kernel = reinterpret_cast<const void*>(&k_ring_exec<E, EA, OP>);
+  int occ = 0;
+  {
+    std::lock_guard<std::mutex> lock(d.mu);
+    auto it = d.occupancy.find(key);
+    if (it != d.occupancy.end()) occ = it->second;
+  }
+  if (occ == 0) {
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kBlock, 0);
+    if (e != hipSuccess) return e;
+    if (occ < 1) occ = 1;
+    std::lock_guard<std::mutex> lock(d.mu);
+    d.occupancy[key] = occ;
+  }
+  if (budget_per_cu_cap > 0 && occ > budget_per_cu_cap) occ = budget_per_cu_cap;
+  const int cus = d.cus > 0 ? d.cus : 256;
+  // slices: as many as stay resident together, at most max_slices, at least 1
+  int slices = (cus * occ) / a.p;
+  if (slices > max_slices) slices = max_slices;
+  if (slices * a.p > kExecMaxWorkers) slices = kExecMaxWorkers / a.p;
+  // no slice shorter than one 8-element unit per lane of the smallest chunk
+  uint64_t shortest = ~0ull;
+  for (int c = 0; c < a.p; ++c) shortest = std::min<uint64_t>(shortest, a.bound[c + 1] - a.bound[c]);
+  const uint64_t by_size = shortest / (8ull * kBlock) + 1;
+  if (static_cast<uint64_t>(slices) > by_size) slices = static_cast<int>(by_size);
+  if (slices < 1) slices = 1;
+  a.nslices = slices;
+  {
+    // One slot per stream, never shared: the flags order data, and launches
+    // on two streams may run at the same time.  (Launches on one stream
+    // run one after the other, so they reuse its slot.)
+    std::lock_guard<std::mutex> lock(d.mu);
+    auto it = d.slot_of.find(s);
+    if (it == d.slot_of.end()) {
+      if (d.slot_of.size() >= static_cast<size_t>(kExecSlots)) return hipErrorOutOfMemory;
+      it = d.slot_of.emplace(s, static_cast<uint32_t>(d.slot_of.size())).first;
+    }
+    a.slot = it->second;
+    const unsigned long long id = ++d.launches;
+    a.tag = (id & ((1ull << (64 - kExecShift)) - 1)) << kExecShift;
+  }
+  const uint64_t khz = d.wall_khz > 0 ? static_cast<uint64_t>(d.wall_khz) : 100000;
+  uint64_t ticks = khz * static_cast<uint64_t>(timeout_us) / 1000;
+  if (ticks < 1) ticks = 1;
+  a.timeout_ticks = ticks;
+  void* kp[] = {&a};
+  return hipLaunchKernel(kernel, dim3(static_cast<unsigned>(slices * a.p)), dim3(kBlock), kp, 0, s);
+}
+
+template <class E, class EA>
+hipError_t exec_by_op(const ExecArgs& a, rr_op_t op, int cap, int ms, int timeout_us, hipStream_t s, ExecDevice& d,
+                      uint32_t key) {
+  switch (op) {
+    case RR_SUM: return exec_go<E, EA, OpSum>(a, cap, ms, timeout_us, s, d, key);
+    case RR_MAX: return exec_go<E, EA, OpMax>(a, cap, ms, timeout_us, s, d, key);
+    case RR_MIN: return exec_go<E, EA, OpMin>(a, cap, ms, timeout_us, s, d, key);
+    case RR_AVG:
+      if constexpr (__is_same(typename E::A, float)) return exec_go<E, EA, OpAvg>(a, cap, ms, timeout_us, s, d, key);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_ring_exec(const ExecArgs& a, Kind k, rr_op_t op, int per_cu_cap, int max_slices, int timeout_us,
+                            hipStream_t s) {
+  int dev = 0;
+  hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  ExecDevice& d = g_exec_dev[dev];
+  std::call_once(d.once, [&] {
+    if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) d.cus = 0;
+    if (hipDeviceGetAttribute(&d.wall_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) d.wall_khz = 0;
+  });
+  const uint32_t key = (static_cast<uint32_t>(k) << 8) | static_cast<uint32_t>(op);
+  if (max_slices < 1 || max_slices > 64) max_slices = 64;
+  switch (k) {
+    case Kind::kI32: return exec_by_op<EI32, EI32>(a, op, per_cu_cap, max_slices, timeout_us, s, d, key);
+    case Kind::kF32: return exec_by_op<EF32, EF32>(a, op, per_cu_cap, max_slices, timeout_us, s, d, key);
+    case Kind::kBF16: return exec_by_op<EBF16, EF32>(a, op, per_cu_cap, max_slices, timeout_us, s, d, key);
+    case Kind::kF16: return exec_by_op<EF16, EF32>(a, op, per_cu_cap, max_slices, timeout_us, s, d, key);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t ring_exec_failures(int device, unsigned long long* count) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  if (device != cur && (e = hipSetDevice(device)) != hipSuccess) return e;
+  e = hipMemcpyFromSymbol(count, HIP_SYMBOL(g_exec_failures), sizeof(*count), 0, hipMemcpyDeviceToHost);
+  if (device != cur) {
+    const hipError_t e2 = hipSetDevice(cur);
+    if (e == hipSuccess) e = e2;
+  }
+  return e;
+}
+
+}  // namespace rr

@@ -166,6 +166,33 @@ hipError_t launch_gather_cols(const ColsArgs& a, int unit_bytes, int nontemporal
 // step and the one conversion.  vec = 1: 16-byte groups, else elements.
 hipError_t launch_fold_cols(const ColsArgs& a, Kind k, rr_op_t op, int vec, hipStream_t stream);
 
+// The ring schedule in one persistent kernel (rr_exec.hip).  in/out: the
+// ranks' inputs and outputs; work: the ranks' working buffers (float32 slots
+// of a workspace for 16-bit types, else the outputs).  nslices, slot, tag and
+// timeout_ticks are set by the launcher.
+struct ExecArgs {
+  const void* in[RR_MAX_RANKS];
+  void* out[RR_MAX_RANKS];
+  void* work[RR_MAX_RANKS];
+  uint64_t bound[RR_MAX_RANKS + 1];  // chunk bounds floor(c*n/p)
+  uint64_t timeout_ticks;            // bounded wait per flag, wall-clock ticks
+  unsigned long long tag;            // launch tag << 24
+  int32_t p;
+  int32_t nslices;
+  int32_t div;   // AVG: p
+  int32_t vec;   // 1: every buffer 16-byte aligned
+  uint32_t slot;
+  int32_t pad;
+};
+
+// per_cu_cap > 0 limits the workers per compute unit; max_slices (1..64)
+// limits the slices per chunk; timeout_us bounds each wait of a worker on a
+// flag.
+hipError_t launch_ring_exec(const ExecArgs& a, Kind k, rr_op_t op, int per_cu_cap, int max_slices, int timeout_us,
+                            hipStream_t stream);
+// Launches of the ring executor on `device` that stopped on a timed-out wait.
+hipError_t ring_exec_failures(int device, unsigned long long* count);
+
 hipError_t launch_fold(const FoldLaunch& f, hipStream_t stream);
 // The phased fold serves same-kind folds on 16-byte-aligned buffers.
 bool phase_supported(const FoldLaunch& f);

@@ -116,7 +116,8 @@ typedef enum {
   RR_ALGO_RING_FUSED = 0,  /* one pass: ring-order fold of each chunk, all p outputs written */
   RR_ALGO_RING_STAGED = 1, /* the ring schedule executed step by step: 2(p-1) launches */
   RR_ALGO_HIER_FUSED = 2,  /* one pass: group folds, cross-group fold, all p outputs written */
-  RR_ALGO_HIER_STAGED = 3  /* group reduce to the representative, cross-group reduce, broadcast */
+  RR_ALGO_HIER_STAGED = 3, /* group reduce to the representative, cross-group reduce, broadcast */
+  RR_ALGO_RING_PERSISTENT = 4 /* the ring schedule in one persistent kernel with per-step flags */
 } rr_algo_t;
 
 typedef enum {
@@ -168,6 +169,17 @@ rr_status_t rr_all_reduce(const void* const* sendbufs, void* const* recvbufs, in
  *     groups and the result written to every representative's recvbuf,
  *     (6) each representative's result is broadcast inside its group.  Needs
  *     rr_workspace_size() bytes of workspace.  Bitwise equal to HIER_FUSED.
+ *   algo = RR_ALGO_RING_PERSISTENT [RING]: the same schedule and arithmetic
+ *     as RR_ALGO_RING_STAGED in ONE launch: every chunk is cut into slices
+ *     and a workgroup per (slice, rank) performs that rank's side of every
+ *     step for its slice, waiting on device-side completion flags of its
+ *     ring neighbours (bounded waits) instead of on launch boundaries.
+ *     Workspace as RR_ALGO_RING_STAGED.  Bitwise equal to RR_ALGO_RING_FUSED.
+ *     If a wait runs out (the workgroups were not all resident, e.g. other
+ *     kernels filled the GPU), the launch stops and its outputs are
+ *     incomplete; rr_ring_exec_failures() counts such launches.  Up to 16
+ *     distinct streams per device may use this algorithm (its step flags are
+ *     kept per stream); a 17th returns RR_ERROR_HIP.
  *   group_size: 1 <= group_size <= p and group_size | p (HIER algos only).
  *   workspace: device memory of at least rr_workspace_size(algo, ...) bytes,
  *     16-byte aligned, owned by the caller, not aliasing any buffer; may be
@@ -416,6 +428,15 @@ rr_status_t rr_cost_hier_all_reduce(int group_size, double bytes, rr_link_t fast
  * Returns RR_ERROR_INVALID_ARGUMENT for a NULL count or a bad device.
  */
 rr_status_t rr_barrier_timeouts(int device, uint64_t* count);
+
+/*
+ * Diagnostics (needs a GPU; synchronizes the device): the number of
+ * RR_ALGO_RING_PERSISTENT launches on `device` that stopped because a wait
+ * on a neighbour's step flag ran out (their outputs are incomplete) since the
+ * library was loaded.  Returns RR_ERROR_INVALID_ARGUMENT for a NULL count or
+ * a bad device.
+ */
+rr_status_t rr_ring_exec_failures(int device, uint64_t* count);
 
 /* Static description of a status code. */
 const char* rr_status_string(rr_status_t status);

@@ -127,7 +127,23 @@ def test_hier_bad_group(algo, group):
 
 
 def test_unknown_algo():
-    assert ar(algo=4)[0] == INVALID
+    assert ar(algo=9)[0] == INVALID
+    assert ar(algo=-1)[0] == INVALID
+
+
+def test_persistent_ring_validation():
+    """The persistent ring executor needs the staged ring's workspace for
+    16-bit dtypes and none for 4-byte ones; every error path returns before
+    any launch."""
+    L = rr.lib()
+    for dt in (2, 3):
+        st, msg = ar(p=8, n=1024, dt=dt, algo=4)
+        assert st == INVALID and "workspace" in msg
+        assert L.rr_workspace_size(4, 8, 0, 1024, dt) == 8 * 1024 * 4
+    assert L.rr_workspace_size(4, 8, 0, 1024, 1) == 0
+    assert ar(algo=4, p=0)[0] == INVALID
+    assert ar(algo=4, dt=0, op=3)[0] == UNSUPPORTED
+    assert ar(algo=4, n=0)[0] == 0
 
 
 def test_staged_workspace_required():

@@ -49,8 +49,8 @@ def oracle_all_reduce(x, dtype, op, algo, G=0):
     return C.all_reduce_fold(x, op, dtype)
 
 
-ALGOS = (("ring", 0), ("ring_staged", 0), ("hier", 1), ("hier", 2), ("hier", 4), ("hier_staged", 2),
-         ("hier_staged", 4))
+ALGOS = (("ring", 0), ("ring_staged", 0), ("ring_persistent", 0), ("hier", 1), ("hier", 2), ("hier", 4),
+         ("hier_staged", 2), ("hier_staged", 4))
 
 
 @pytest.mark.parametrize("dtype", FLOATS)
@@ -101,7 +101,7 @@ AVG_SWEEP = [(2, 1000), (3, 4099), (5, 77777), (8, 262147), (6, 5), (64, 6400), 
 @pytest.mark.parametrize("dtype", FLOATS)
 def test_sweep_avg(rr, p, n, dtype):
     x = W.random_inputs(21, p, n, dtype)
-    for algo, G in (("ring", 0), ("ring_staged", 0)) + tuple(
+    for algo, G in (("ring", 0), ("ring_staged", 0), ("ring_persistent", 0)) + tuple(
             (a, g) for a in ("hier", "hier_staged") for g in (1, 2, p) if p % g == 0):
         assert_bitwise(run_all_reduce(rr, x, dtype, "avg", algo, G), oracle_all_reduce(x, dtype, "avg", algo, G),
                        f"{algo} G={G}")
@@ -124,7 +124,7 @@ def test_sweep_float16(rr, p, n):
     for kind in ("normal", "fp16_patterns"):
         x = W.random_inputs(22, p, n, "float16", kind=kind)
         for op in ("sum", "max", "min", "avg"):
-            for algo, G in (("ring", 0), ("ring_staged", 0)) + tuple(
+            for algo, G in (("ring", 0), ("ring_staged", 0), ("ring_persistent", 0)) + tuple(
                     (a, g) for a in ("hier", "hier_staged") for g in (1, 2, p) if p % g == 0):
                 assert_bitwise(run_all_reduce(rr, x, "float16", op, algo, G),
                                oracle_all_reduce(x, "float16", op, algo, G), f"{kind} {algo} G={G} {op}")

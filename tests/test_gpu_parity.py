@@ -323,7 +323,7 @@ def test_sweep_all_reduce(rr, p, n, dtype):
     x = W.random_inputs(11, p, n, dtype, kind="full" if dtype == "int32" else "normal")
     for op in ("sum", "max", "min"):
         want = C.all_reduce_fold(x, op, dtype)
-        for algo in ("ring", "ring_staged"):
+        for algo in ("ring", "ring_staged", "ring_persistent"):
             xs = to_dev(x, dtype)
             out = torch.empty_like(xs)
             rr.all_reduce(xs, out, op=op, algo=algo)
@@ -386,7 +386,7 @@ def test_in_place_forms(rr, dtype):
     L = n // p
     x = W.random_inputs(14, p, n, dtype)
     # all-reduce in place == out of place
-    for algo, G in (("ring", 0), ("ring_staged", 0), ("hier", 4), ("hier_staged", 2)):
+    for algo, G in (("ring", 0), ("ring_staged", 0), ("ring_persistent", 0), ("hier", 4), ("hier_staged", 2)):
         xs = to_dev(x, dtype)
         out = torch.empty_like(xs)
         rr.all_reduce(xs, out, algo=algo, group_size=G)

@@ -1,0 +1,95 @@
+"""GPU tests of the persistent ring executor (algo "ring_persistent"): the
+ring schedule of page "LLM Parallelism 基础", section "Ring AllReduce", run
+by one launch whose workgroups hand chunks on through device-side step flags.
+It must give the bits of the fused pass and of the oracle's literal ring
+simulation, at full sizes, in place, on unaligned buffers; a wait forced to
+time out from the host must end the launch (counted, never hung).
+"""
+
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_util import assert_bitwise, to_dev, to_host
+from oracle import collectives as C
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import collective_communication_reduction_way_amd as mod
+
+    mod.lib()
+    return mod
+
+
+def run(rr, x, dtype, op="sum", algo="ring_persistent"):
+    xs = to_dev(x, dtype)
+    out = torch.empty_like(xs)
+    rr.all_reduce(xs, out, op=op, algo=algo)
+    return to_host(out, dtype)
+
+
+@pytest.mark.parametrize("name", ["ar_int32_p4_n4096", "ar_fp32_p8_8MiB", "hier_bf16_p8g4_8MiB"])
+def test_workloads_match_the_literal_ring(rr, name):
+    x = W.make_inputs(name)
+    dtype = W.WORKLOADS[name]["dtype"]
+    f0 = rr.ring_exec_failures()
+    want = C.all_reduce_ring(x, "sum", dtype) if x.shape[1] <= 4096 else C.all_reduce_fold(x, "sum", dtype)
+    assert_bitwise(run(rr, x, dtype), want, name)
+    assert rr.ring_exec_failures() == f0
+
+
+@pytest.mark.parametrize("dtype", ("float32", "bfloat16", "float16"))
+def test_large_ragged(rr, dtype):
+    """Chunks of unequal length and many slices per chunk, every op."""
+    p, n = 8, 8 * (1 << 20) + 8 * 5 + 3
+    x = W.random_inputs(81, p, n, dtype)
+    f0 = rr.ring_exec_failures()
+    for op in ("sum", "avg", "max"):
+        assert_bitwise(run(rr, x, dtype, op), C.all_reduce_fold(x, op, dtype), op)
+    assert rr.ring_exec_failures() == f0
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ("int32", "float32", "bfloat16"))
+def test_in_place_and_unaligned(rr, dtype):
+    p, n = 6, 6 * 4001 + 5
+    x = W.random_inputs(82, p, n + 3, dtype, kind="full" if dtype == "int32" else "normal")
+    want = C.all_reduce_fold(np.ascontiguousarray(x[:, :n]), "sum", dtype)
+    xs = to_dev(np.ascontiguousarray(x[:, :n]), dtype)
+    rr.all_reduce(xs, algo="ring_persistent")
+    assert_bitwise(to_host(xs, dtype), want, "in place")
+    base = to_dev(x, dtype)
+    ins = [base[r, 1:1 + n] for r in range(p)]
+    outbuf = torch.empty((p, n + 1), dtype=base.dtype, device="cuda")
+    outs = [outbuf[r, 1:1 + n] for r in range(p)]
+    rr.all_reduce(ins, outs, algo="ring_persistent")
+    got = np.stack([to_host(o, dtype) for o in outs])
+    assert_bitwise(got, C.all_reduce_fold(np.ascontiguousarray(x[:, 1:1 + n]), "sum", dtype), "unaligned")
+
+
+def test_forced_timeout_ends_the_launch(rr, monkeypatch):
+    """A 1 us bound on every wait (set from the host) makes workers give up:
+    the launch must end, be counted, and a following normal launch on the
+    same stream must be correct."""
+    p, n = 8, 8 * (1 << 20)
+    x = W.random_inputs(83, p, n, "float32")
+    f0 = rr.ring_exec_failures()
+    monkeypatch.setenv("RR_EXEC_TIMEOUT_US", "1")
+    xs = to_dev(x, "float32")
+    out = torch.empty_like(xs)
+    for _ in range(3):
+        rr.all_reduce(xs, out, algo="ring_persistent")
+    torch.cuda.synchronize()
+    assert rr.ring_exec_failures() > f0, "the 1 us bound never ran out"
+    monkeypatch.delenv("RR_EXEC_TIMEOUT_US")
+    f1 = rr.ring_exec_failures()
+    rr.all_reduce(xs, out, algo="ring_persistent")
+    assert_bitwise(to_host(out, "float32"), C.all_reduce_fold(x, "sum", "float32"), "after the failed launches")
+    assert rr.ring_exec_failures() == f1
+    torch.cuda.empty_cache()
