@@ -66,7 +66,8 @@ int env_int(const char* name, int dflt) {
 // smaller tile for sums), RR_PHASE_STATIC (1 / 0 = the kernels compiled for
 // p = 8 / the run-time rank loop; -1 = by mode),
 // RR_PHASE_TIMEOUT_US (bound of one barrier wait, default 200),
-// RR_EXEC_TIMEOUT_US (bound of one wait of the persistent ring executor on a
+// RR_MULTI_PER_CU (workgroups per compute unit of the bucket and dim-1
+// kernels; 0 = the default), RR_EXEC_TIMEOUT_US (bound of one wait of the persistent ring executor on a
 // neighbour's flag, default 1 s), RR_EXEC_PER_CU (cap on its workgroups per
 // compute unit; 0 = as many as stay resident), RR_EXEC_SLICES (slices per
 // chunk, 1..64; 0 = by chunk size),
@@ -87,6 +88,7 @@ struct Tuning {
   int log;
   int phase;
   rr::PhaseTuning pt;
+  int multi_per_cu;
   int exec_timeout_us;
   int exec_per_cu;
   int exec_slices;
@@ -103,7 +105,7 @@ Tuning tuning() {
   t.phase = env_int("RR_PHASE", 1) ? 1 : 0;
   t.pt.sync = env_int("RR_PHASE_SYNC", 1) ? 1 : 0;
   t.pt.per_cu = env_int("RR_PHASE_PER_CU", 0);
-  if (t.pt.per_cu < 0 || t.pt.per_cu > 8) t.pt.per_cu = 0;
+  if (t.pt.per_cu < 0 || t.pt.per_cu > 64) t.pt.per_cu = 0;
   t.pt.grid = env_int("RR_PHASE_GRID", 0);
   if (t.pt.grid < 0) t.pt.grid = 0;
   t.pt.unroll = env_int("RR_PHASE_U", 0) == 4 ? 4 : 0;
@@ -111,6 +113,8 @@ Tuning tuning() {
   t.pt.static_p = env_int("RR_PHASE_STATIC", -1);
   if (t.pt.static_p > 1) t.pt.static_p = 1;
   if (t.pt.timeout_us < 1) t.pt.timeout_us = 200;
+  t.multi_per_cu = env_int("RR_MULTI_PER_CU", 0);
+  if (t.multi_per_cu < 0 || t.multi_per_cu > 64) t.multi_per_cu = 0;
   t.exec_timeout_us = env_int("RR_EXEC_TIMEOUT_US", 1000000);
   if (t.exec_timeout_us < 1) t.exec_timeout_us = 1;
   t.exec_per_cu = env_int("RR_EXEC_PER_CU", 0);
@@ -956,7 +960,7 @@ rr_status_t rr_all_reduce_bucket(const void* const* sendbufs, void* const* recvb
     if (a.npieces == 0) return RR_SUCCESS;
     a.tile0[a.npieces] = a.tiles;
     if (t.log) fprintf(stderr, "[rr] all_reduce_bucket: launch %d, %d pieces, %u tiles\n", launches, a.npieces, a.tiles);
-    const hipError_t e = rr::launch_bucket(a, k, op, s);
+    const hipError_t e = rr::launch_bucket(a, k, op, t.multi_per_cu, s);
     if (e != hipSuccess) return hip_fail(e, "all_reduce_bucket");
     ++launches;
     reset();
@@ -1066,7 +1070,8 @@ rr_status_t rr_all_gather_dim1(const void* const* sendbufs, void* const* recvbuf
   a.p = p;
   const Tuning t = tuning();
   if (t.log) fprintf(stderr, "[rr] all_gather_dim1: p=%d rows=%zu cols=%zu unit=%d\n", p, rows, cols, unit);
-  const hipError_t e = rr::launch_gather_cols(a, unit, t.nontemporal, reinterpret_cast<hipStream_t>(stream));
+  const hipError_t e =
+      rr::launch_gather_cols(a, unit, t.nontemporal, t.multi_per_cu, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "all_gather_dim1");
   return ok();
 }
@@ -1105,7 +1110,8 @@ rr_status_t rr_reduce_scatter_dim1(const void* const* sendbufs, void* const* rec
   a.div = divisor_for(op, p);
   const Tuning t = tuning();
   if (t.log) fprintf(stderr, "[rr] reduce_scatter_dim1: p=%d rows=%zu cols=%zu vec=%d\n", p, rows, cols, vec ? 1 : 0);
-  const hipError_t e = rr::launch_fold_cols(a, kind_of(dtype), op, vec ? 1 : 0, reinterpret_cast<hipStream_t>(stream));
+  const hipError_t e = rr::launch_fold_cols(a, kind_of(dtype), op, vec ? 1 : 0, t.multi_per_cu,
+                                            reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "reduce_scatter_dim1");
   return ok();
 }

@@ -144,7 +144,9 @@ struct BucketArgs {
 // units, 16-byte groups in vector pieces and single elements in scalar ones.
 constexpr int kBucketU = 4;
 
-hipError_t launch_bucket(const BucketArgs& a, Kind k, rr_op_t op, hipStream_t stream);
+// per_cu: workgroups per compute unit of the launch (the kernels stride over
+// their work); 0 = the default.
+hipError_t launch_bucket(const BucketArgs& a, Kind k, rr_op_t op, int per_cu, hipStream_t stream);
 
 // Tensor-parallel layouts (rr_multi.hip) on row-major [rows, cols] matrices
 // with cols = p*w.  "Units" are 16-byte groups, or narrower units (4, 2, 1
@@ -160,11 +162,11 @@ struct ColsArgs {
 };
 
 // All-gather along dim 1: dst[r][b, c*w + j] = src[c][b, j] for every r.
-hipError_t launch_gather_cols(const ColsArgs& a, int unit_bytes, int nontemporal, hipStream_t stream);
+hipError_t launch_gather_cols(const ColsArgs& a, int unit_bytes, int nontemporal, int per_cu, hipStream_t stream);
 // Reduce-scatter along dim 1: dst[c][b, j] = fold over k = 1..p of
 // src[(c+k) mod p][b, c*w + j] (ring order of chunk c), then the op's last
 // step and the one conversion.  vec = 1: 16-byte groups, else elements.
-hipError_t launch_fold_cols(const ColsArgs& a, Kind k, rr_op_t op, int vec, hipStream_t stream);
+hipError_t launch_fold_cols(const ColsArgs& a, Kind k, rr_op_t op, int vec, int per_cu, hipStream_t stream);
 
 // The ring schedule in one persistent kernel (rr_exec.hip).  in/out: the
 // ranks' inputs and outputs; work: the ranks' working buffers (float32 slots

@@ -292,11 +292,16 @@ hipError_t launch(K kernel, const ARGS& args, dim3 grid, hipStream_t s) {
   return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, dim3(kBlock), kp, 0, s);
 }
 
-// Workgroups of a streaming launch: enough to keep every compute unit busy
-// (four per CU), never more than there is work.
-unsigned stream_grid(uint64_t work_units, uint64_t per_block, int rows, hipStream_t s) {
+// Workgroups of a streaming launch: per_cu per compute unit, never more than
+// there is work.  Defaults (measured): 32 per CU for the dim-1 layouts (the
+// grid oversubscribes the device, about one tile per workgroup), 4 for the
+// bucket.
+constexpr int kColsPerCu = 32;
+constexpr int kBucketPerCu = 4;
+
+unsigned stream_grid(uint64_t work_units, uint64_t per_block, int rows, int per_cu, hipStream_t s) {
   const int cus = cus_of(s);
-  uint64_t cap = static_cast<uint64_t>(cus > 0 ? cus : 256) * 4;
+  uint64_t cap = static_cast<uint64_t>(cus > 0 ? cus : 256) * static_cast<uint64_t>(per_cu);
   cap = (cap + static_cast<uint64_t>(rows) - 1) / static_cast<uint64_t>(rows);
   uint64_t g = (work_units + per_block - 1) / per_block;
   if (g > cap) g = cap;
@@ -305,8 +310,8 @@ unsigned stream_grid(uint64_t work_units, uint64_t per_block, int rows, hipStrea
 }
 
 template <class E>
-hipError_t bucket_by_op(const BucketArgs& a, rr_op_t op, hipStream_t s) {
-  const dim3 grid(stream_grid(a.tiles, 1, 1, s));
+hipError_t bucket_by_op(const BucketArgs& a, rr_op_t op, int per_cu, hipStream_t s) {
+  const dim3 grid(stream_grid(a.tiles, 1, 1, per_cu > 0 ? per_cu : kBucketPerCu, s));
   switch (op) {
     case RR_SUM: return launch(&k_bucket<E, OpSum>, a, grid, s);
     case RR_MAX: return launch(&k_bucket<E, OpMax>, a, grid, s);
@@ -320,13 +325,14 @@ hipError_t bucket_by_op(const BucketArgs& a, rr_op_t op, hipStream_t s) {
 
 // 32-bit unit indices when every index of the launch, including a loop
 // counter one grid stride past the end, fits: rows*du + stride < 2^32.  The
-// stride is at most stream_grid's cap (4 workgroups per CU) times kBlock*4
-// units, far below the 2^24 margin kept here.
-bool small_index(const ColsArgs& a) { return a.du > 0 && a.rows < (0xFFFFFFFFull - (1ull << 24)) / a.du; }
+// stride is at most (compute units) * (workgroups per CU, <= 64) * kBlock * 4
+// units, below 2^28 for up to 1024 compute units: that is the margin kept.
+bool small_index(const ColsArgs& a) { return a.du > 0 && a.rows < (0xFFFFFFFFull - (1ull << 28)) / a.du; }
 
 template <class E, bool VEC, class IDX>
-hipError_t fold_cols_by_op(const ColsArgs& a, rr_op_t op, hipStream_t s) {
-  const dim3 grid(stream_grid(a.rows * a.wu, static_cast<uint64_t>(kBlock) * 4, a.p, s), a.p);
+hipError_t fold_cols_by_op(const ColsArgs& a, rr_op_t op, int per_cu, hipStream_t s) {
+  const dim3 grid(stream_grid(a.rows * a.wu, static_cast<uint64_t>(kBlock) * 4, a.p, per_cu > 0 ? per_cu : kColsPerCu, s),
+                  a.p);
   switch (op) {
     case RR_SUM: return launch(&k_fold_cols<E, OpSum, VEC, IDX>, a, grid, s);
     case RR_MAX: return launch(&k_fold_cols<E, OpMax, VEC, IDX>, a, grid, s);
@@ -339,51 +345,51 @@ hipError_t fold_cols_by_op(const ColsArgs& a, rr_op_t op, hipStream_t s) {
 }
 
 template <class E>
-hipError_t fold_cols_kind(const ColsArgs& a, rr_op_t op, int vec, hipStream_t s) {
+hipError_t fold_cols_kind(const ColsArgs& a, rr_op_t op, int vec, int pc, hipStream_t s) {
   if (small_index(a))
-    return vec ? fold_cols_by_op<E, true, uint32_t>(a, op, s) : fold_cols_by_op<E, false, uint32_t>(a, op, s);
-  return vec ? fold_cols_by_op<E, true, uint64_t>(a, op, s) : fold_cols_by_op<E, false, uint64_t>(a, op, s);
+    return vec ? fold_cols_by_op<E, true, uint32_t>(a, op, pc, s) : fold_cols_by_op<E, false, uint32_t>(a, op, pc, s);
+  return vec ? fold_cols_by_op<E, true, uint64_t>(a, op, pc, s) : fold_cols_by_op<E, false, uint64_t>(a, op, pc, s);
 }
 
 template <int B, bool NT>
-hipError_t gather_cols_go(const ColsArgs& a, hipStream_t s) {
-  const dim3 grid(stream_grid(a.rows * a.du, static_cast<uint64_t>(kBlock) * 4, 1, s));
+hipError_t gather_cols_go(const ColsArgs& a, int per_cu, hipStream_t s) {
+  const dim3 grid(stream_grid(a.rows * a.du, static_cast<uint64_t>(kBlock) * 4, 1, per_cu > 0 ? per_cu : kColsPerCu, s));
   return small_index(a) ? launch(&k_gather_cols<B, NT, uint32_t>, a, grid, s)
                         : launch(&k_gather_cols<B, NT, uint64_t>, a, grid, s);
 }
 
 }  // namespace
 
-hipError_t launch_bucket(const BucketArgs& a, Kind k, rr_op_t op, hipStream_t s) {
+hipError_t launch_bucket(const BucketArgs& a, Kind k, rr_op_t op, int per_cu, hipStream_t s) {
   if (a.tiles == 0) return hipSuccess;
   switch (k) {
-    case Kind::kI32: return bucket_by_op<EI32>(a, op, s);
-    case Kind::kF32: return bucket_by_op<EF32>(a, op, s);
-    case Kind::kBF16: return bucket_by_op<EBF16>(a, op, s);
-    case Kind::kF16: return bucket_by_op<EF16>(a, op, s);
+    case Kind::kI32: return bucket_by_op<EI32>(a, op, per_cu, s);
+    case Kind::kF32: return bucket_by_op<EF32>(a, op, per_cu, s);
+    case Kind::kBF16: return bucket_by_op<EBF16>(a, op, per_cu, s);
+    case Kind::kF16: return bucket_by_op<EF16>(a, op, per_cu, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_fold_cols(const ColsArgs& a, Kind k, rr_op_t op, int vec, hipStream_t s) {
+hipError_t launch_fold_cols(const ColsArgs& a, Kind k, rr_op_t op, int vec, int per_cu, hipStream_t s) {
   if (a.rows * a.wu == 0) return hipSuccess;
   switch (k) {
-    case Kind::kI32: return fold_cols_kind<EI32>(a, op, vec, s);
-    case Kind::kF32: return fold_cols_kind<EF32>(a, op, vec, s);
-    case Kind::kBF16: return fold_cols_kind<EBF16>(a, op, vec, s);
-    case Kind::kF16: return fold_cols_kind<EF16>(a, op, vec, s);
+    case Kind::kI32: return fold_cols_kind<EI32>(a, op, vec, per_cu, s);
+    case Kind::kF32: return fold_cols_kind<EF32>(a, op, vec, per_cu, s);
+    case Kind::kBF16: return fold_cols_kind<EBF16>(a, op, vec, per_cu, s);
+    case Kind::kF16: return fold_cols_kind<EF16>(a, op, vec, per_cu, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gather_cols(const ColsArgs& a, int unit_bytes, int nontemporal, hipStream_t s) {
+hipError_t launch_gather_cols(const ColsArgs& a, int unit_bytes, int nontemporal, int per_cu, hipStream_t s) {
   if (a.rows * a.wu == 0) return hipSuccess;
   const bool nt = nontemporal != 0;
   switch (unit_bytes) {
-    case 16: return nt ? gather_cols_go<16, true>(a, s) : gather_cols_go<16, false>(a, s);
-    case 4: return nt ? gather_cols_go<4, true>(a, s) : gather_cols_go<4, false>(a, s);
-    case 2: return nt ? gather_cols_go<2, true>(a, s) : gather_cols_go<2, false>(a, s);
-    case 1: return nt ? gather_cols_go<1, true>(a, s) : gather_cols_go<1, false>(a, s);
+    case 16: return nt ? gather_cols_go<16, true>(a, per_cu, s) : gather_cols_go<16, false>(a, per_cu, s);
+    case 4: return nt ? gather_cols_go<4, true>(a, per_cu, s) : gather_cols_go<4, false>(a, per_cu, s);
+    case 2: return nt ? gather_cols_go<2, true>(a, per_cu, s) : gather_cols_go<2, false>(a, per_cu, s);
+    case 1: return nt ? gather_cols_go<1, true>(a, per_cu, s) : gather_cols_go<1, false>(a, per_cu, s);
   }
   return hipErrorInvalidValue;
 }

@@ -119,7 +119,8 @@ bool phase_supported(const FoldLaunch& f) {
 //   hierarchical all-reduce: the run-time rank loop, 4 workgroups per CU with
 //     the bfloat16 tile of 4 groups per lane, else 2;
 //   reduce-scatter and reduce: 4 groups per lane for sums (8 for max/min),
-//     4 workgroups per CU, the kernel compiled for p = 8, no barrier.
+//     32 workgroups per CU (the grid oversubscribes the device; workgroups
+//     start as others finish), the kernel compiled for p = 8, no barrier.
 // With the barrier, the grid never exceeds what the device can keep resident
 // at once (the kernel's occupancy times the compute units): workgroups that
 // had to wait for a free slot would make every barrier run into its timeout.
@@ -145,7 +146,9 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
   const bool one_out = f.mode == FoldMode::kRingShard || f.mode == FoldMode::kAscOne;
   int unroll = phase_default_unroll(f.in_kind, f.mode);
   if ((pt.unroll == 4 || (one_out && pt.unroll == 0)) && sum_like) unroll = 4;
-  int per_cu = pt.per_cu > 0 ? pt.per_cu : (unroll == 4 || one_out ? 4 : 2);
+  // one-output modes run without the barrier, so nothing ties their grid to
+  // residency: 32 workgroups per CU (about one tile each) measured best
+  int per_cu = pt.per_cu > 0 ? pt.per_cu : (one_out ? 32 : (unroll == 4 ? 4 : 2));
 
   PhaseArgs a;
   memset(&a, 0, sizeof(a));
