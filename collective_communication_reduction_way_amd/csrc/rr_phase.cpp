@@ -169,6 +169,18 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
     tiles = tile_segments(f, V, static_cast<uint64_t>(kBlock) * unroll, a);
     if (tiles >= 0x7FFFFFFFull) return hipErrorInvalidValue;
     grid = cus * static_cast<uint64_t>(per_cu);
+  } else if (ring && pt.unroll == 0 && pt.grid == 0 && sum_like && unroll == 8 &&
+             (tiles < cus || (is_half(f.in_kind) && tiles < 2 * cus))) {
+    // one round with too few tiles of 8 groups per lane to fill the device
+    // (fewer than one per CU; for 16-bit types, which also convert, fewer
+    // than two): the smaller tile.  With at most one tile per CU all p = 8
+    // ranks unrolled measured best, with more the run-time rank loop.
+    unroll = 4;
+    if (pt.per_cu <= 0) per_cu = 4;
+    tiles = tile_segments(f, V, static_cast<uint64_t>(kBlock) * unroll, a);
+    if (tiles >= 0x7FFFFFFFull) return hipErrorInvalidValue;
+    if (pt.static_p < 0) static_p = tiles <= cus;
+    grid = cus * static_cast<uint64_t>(per_cu);
   }
   if (grid > tiles) grid = tiles;
   if (grid < 1) grid = 1;
