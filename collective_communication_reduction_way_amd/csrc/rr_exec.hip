@@ -44,7 +44,12 @@
 // measured five times slower (each write-back walks the L2).
 //
 // Flags hold (launch tag << 24) + steps; each launch has a fresh, larger tag
-// and raises flags with atomic max, so nothing needs resetting.  Every wait
+// and raises flags with atomic max, so nothing needs resetting -- except
+// under graph capture: a graph replays its kernel arguments unchanged, so a
+// captured launch carries the fixed tag 1 (eager launches use 2, 3, ...)
+// and a reset of the slot's flags and abort word is captured just before it.
+// Without it, a replay would find the previous replay's flags already at
+// their final values and read chunks before they are written.  Every wait
 // is bounded by a wall-clock timeout; a worker that times out (workers not
 // all resident, for instance) raises the slot's abort word, counts the
 // failure and stops, and every other waiter of the launch stops as soon as
@@ -70,6 +75,7 @@ constexpr int kExecSlots = 16;
 constexpr int kExecMaxWorkers = 2048;  // p * B per launch
 constexpr int kExecStride = 8;         // 64-bit words: one 64-byte line per flag
 constexpr int kExecShift = 24;         // flag = (tag << 24) + steps
+constexpr unsigned long long kExecCapturedTag = 1ull << kExecShift;
 
 __device__ __align__(256) unsigned long long g_exec_flags[kExecSlots * kExecMaxWorkers * kExecStride];
 __device__ __align__(256) unsigned long long g_exec_abort[kExecSlots * 16];
@@ -77,6 +83,14 @@ __device__ unsigned long long g_exec_failures;
 
 __device__ __forceinline__ unsigned long long* exec_flag(uint32_t slot, int worker) {
   return g_exec_flags + (static_cast<size_t>(slot) * kExecMaxWorkers + worker) * kExecStride;
+}
+
+// Clear the flags of workers [0, workers) of a slot and its abort word
+// (ahead of a captured launch).
+__global__ __launch_bounds__(kBlock) void k_exec_reset(uint32_t slot, int workers) {
+  for (int w = threadIdx.x; w < workers; w += kBlock)
+    __hip_atomic_store(exec_flag(slot, w), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_store(g_exec_abort + slot * 16, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Wait until *f >= target, the launch's abort word is raised, or the bound
@@ -296,8 +310,23 @@ hipError_t exec_go(ExecArgs a, int budget_per_cu_cap, int max_slices, int timeou
       it = d.slot_of.emplace(s, static_cast<uint32_t>(d.slot_of.size())).first;
     }
     a.slot = it->second;
-    const unsigned long long id = ++d.launches;
+  }
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t ce = hipStreamIsCapturing(s, &cs);
+  if (ce != hipSuccess) return ce;
+  if (cs == hipStreamCaptureStatusActive) {
+    a.captured = 1;
+    a.tag = kExecCapturedTag;
+    uint32_t slot = a.slot;
+    int workers = slices * a.p;
+    void* rp[] = {&slot, &workers};
+    ce = hipLaunchKernel(reinterpret_cast<const void*>(&k_exec_reset), dim3(1), dim3(kBlock), rp, 0, s);
+    if (ce != hipSuccess) return ce;
+  } else {
+    std::lock_guard<std::mutex> lock(d.mu);
+    const unsigned long long id = ++d.launches + 1;  // 2, 3, ...: 1 belongs to captured launches
     a.tag = (id & ((1ull << (64 - kExecShift)) - 1)) << kExecShift;
+    if (a.tag <= kExecCapturedTag) a.tag = 2 * kExecCapturedTag;
   }
   const uint64_t khz = d.wall_khz > 0 ? static_cast<uint64_t>(d.wall_khz) : 100000;
   uint64_t ticks = khz * static_cast<uint64_t>(timeout_us) / 1000;

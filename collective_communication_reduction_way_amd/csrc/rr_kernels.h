@@ -184,7 +184,7 @@ struct ExecArgs {
   int32_t div;   // AVG: p
   int32_t vec;   // 1: every buffer 16-byte aligned
   uint32_t slot;
-  int32_t pad;
+  int32_t captured;  // 1: launched under graph capture (fixed tag, flags reset first)
 };
 
 // per_cu_cap > 0 limits the workers per compute unit; max_slices (1..64)

@@ -212,8 +212,18 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
       a.rounds = static_cast<uint32_t>((tiles + grid - 1) / grid);
     }
     a.slot = slot_for(d, s);
-    const unsigned long long id = d.launches.fetch_add(1) + 1;
-    a.tag = (id & ((1ull << (64 - kLaunchShift)) - 1)) << kLaunchShift;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(s, &cs);
+    if (e != hipSuccess) return e;
+    if (cs == hipStreamCaptureStatusActive) {
+      a.captured = 1;
+      a.tag = kCapturedTag;
+    } else {
+      // tags 2, 3, ...: 1 belongs to captured launches
+      const unsigned long long id = d.launches.fetch_add(1) + 2;
+      a.tag = (id & ((1ull << (64 - kLaunchShift)) - 1)) << kLaunchShift;
+      if (a.tag <= kCapturedTag) a.tag = 2 * kCapturedTag;
+    }
     const uint64_t khz = d.wall_khz > 0 ? static_cast<uint64_t>(d.wall_khz) : 100000;
     uint64_t ticks = khz * static_cast<uint64_t>(pt.timeout_us) / 1000;
     if (ticks < 1) ticks = 1;

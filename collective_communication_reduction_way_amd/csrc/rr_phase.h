@@ -16,6 +16,11 @@ constexpr int kSyncCounters = kSyncSubs + 1;       // arrival counters, then the
 constexpr int kSyncStride = 16;                    // 64-bit words: one 128-byte line per counter
 constexpr int kLaunchShift = 24;                   // counter = (launch tag << 24) + count
 constexpr uint64_t kMaxBarrierTiles = 1ull << 23;  // arrivals per launch stay below 2^24
+// Launch tag of a launch captured into a graph: a graph replays its kernel
+// arguments unchanged, so such a launch always carries this tag (eager
+// launches use 2, 3, ...), and a reset of the slot's counters is captured
+// just before it.
+constexpr unsigned long long kCapturedTag = 1ull << kLaunchShift;
 
 // Per-segment tiling is computed on the host, so that the kernel makes no
 // 64-bit comparisons of uniform values: with ROCm 7.2's compiler, a 64-bit
@@ -42,6 +47,7 @@ struct PhaseArgs {
   uint32_t timeout_ticks;  // bounded wait per barrier, in wall-clock ticks
   unsigned long long tag;  // launch tag << kLaunchShift
   int32_t segments;
+  int32_t captured;  // 1: launched under graph capture (tag = kCapturedTag; reset first)
 };
 
 // Groups per lane per tile of the phased fold: 8 (32 KiB per rank and tile

@@ -73,6 +73,14 @@ __device__ __forceinline__ void sync_claim(const PhaseArgs& a) {
   if (threadIdx.x == 0) atomic_max_relaxed(sync_counter(a.slot, blockIdx.x % kSyncSubs), a.tag);
 }
 
+// Clear one slot's counters: captured ahead of a launch whose tag is fixed
+// (graph replays), so that every replay counts from zero like an eager
+// launch with a fresh tag.
+__global__ __launch_bounds__(64) void k_sync_reset(uint32_t slot) {
+  if (threadIdx.x < static_cast<uint32_t>(kSyncCounters))
+    __hip_atomic_store(sync_counter(slot, threadIdx.x), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Arrive at barrier `round` and wait (bounded) until all G workgroups have.
 __device__ __forceinline__ void soft_barrier(const PhaseArgs& a, uint32_t round) {
   __syncthreads();
@@ -375,6 +383,13 @@ hipError_t phase_by_op(const PhaseArgs& a, rr_op_t op, unsigned grid, int unroll
 template <FoldMode M>
 hipError_t phase_dispatch(const PhaseArgs& a, Kind k, rr_op_t op, unsigned grid, int unroll, bool sync,
                           bool static_p, int* occ, hipStream_t s) {
+  if (sync && occ == nullptr && a.captured) {
+    // this translation unit's counters, cleared on the same stream first
+    uint32_t slot = a.slot;
+    void* kp[] = {&slot};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&k_sync_reset), dim3(1), dim3(64), kp, 0, s);
+    if (e != hipSuccess) return e;
+  }
   if constexpr (!is_wire(M)) {
     if (k == Kind::kI32) return phase_by_op<EI32, M>(a, op, grid, unroll, sync, static_p, occ, s);
     if (k == Kind::kF32) return phase_by_op<EF32, M>(a, op, grid, unroll, sync, static_p, occ, s);

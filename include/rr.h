@@ -73,6 +73,16 @@
  *    `stream` (NULL = the null stream of the current device) and returns.
  *    The library never synchronizes.  Completion is observed through the
  *    stream.  Buffers must stay valid until the work completes.
+ *  - Graph capture: every call may be captured into a HIP graph (no
+ *    allocation, no memset, no synchronization on the call path; call once
+ *    before capturing, so that per-kernel set-up stays out of the graph).  A
+ *    graph replays its launch arguments unchanged, so launches that keep
+ *    per-launch state in device memory (the soft barrier of the multi-round
+ *    fused fold, the step flags of RR_ALGO_RING_PERSISTENT) detect capture,
+ *    take a fixed tag, and capture a reset of that state just before
+ *    themselves.  That state is kept per capturing stream: replay a graph on
+ *    the stream it was captured on, or on a stream with no work of the same
+ *    calls in flight.
  *  - Errors: return codes only.  All validation happens before the first
  *    launch, so a call that returns RR_ERROR_INVALID_ARGUMENT or
  *    RR_ERROR_UNSUPPORTED has written nothing.  A launch failure returns
