@@ -960,7 +960,7 @@ rr_status_t rr_all_reduce_bucket(const void* const* sendbufs, void* const* recvb
     if (a.npieces == 0) return RR_SUCCESS;
     a.tile0[a.npieces] = a.tiles;
     if (t.log) fprintf(stderr, "[rr] all_reduce_bucket: launch %d, %d pieces, %u tiles\n", launches, a.npieces, a.tiles);
-    const hipError_t e = rr::launch_bucket(a, k, op, t.multi_per_cu, s);
+    const hipError_t e = rr::launch_bucket(a, k, op, t.multi_per_cu, t.pt.sync, t.pt.timeout_us, s);
     if (e != hipSuccess) return hip_fail(e, "all_reduce_bucket");
     ++launches;
     reset();

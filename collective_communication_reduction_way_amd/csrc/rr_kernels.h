@@ -126,6 +126,17 @@ struct PhaseTuning {
 constexpr int kBucketPtrs = 192;   // pointer slots per launch: p inputs then p outputs per tensor
 constexpr int kBucketPieces = 96;  // pieces per launch
 
+// The barrier fields of one launch (rr_sync.h): the stream's counter slot,
+// the launch tag (kCapturedTag under graph capture, then captured = 1), and
+// the bound of one wait in wall-clock ticks.
+struct SyncArgs {
+  unsigned long long tag;
+  uint32_t slot;
+  uint32_t timeout_ticks;
+  int32_t captured;
+  int32_t pad;
+};
+
 struct BucketArgs {
   const void* ptr[kBucketPtrs];
   uint64_t start[kBucketPieces];       // first element of the piece in its tensor
@@ -138,6 +149,8 @@ struct BucketArgs {
   int32_t p;
   int32_t div;  // AVG: p; unused otherwise
   uint32_t tiles;
+  uint32_t rounds;  // tiles / grid, rounded up
+  SyncArgs sync;    // the soft barrier between the read and write phases (multi-round launches)
 };
 
 // Units per lane and tile of the bucket kernel: a tile is kBlock*kBucketU
@@ -145,8 +158,13 @@ struct BucketArgs {
 constexpr int kBucketU = 4;
 
 // per_cu: workgroups per compute unit of the launch (the kernels stride over
-// their work); 0 = the default.
-hipError_t launch_bucket(const BucketArgs& a, Kind k, rr_op_t op, int per_cu, hipStream_t stream);
+// their work); 0 = the default.  sync: a launch of several rounds separates
+// the read and the write phase of each round with the soft barrier
+// (timeout_us bounds one wait).
+hipError_t launch_bucket(const BucketArgs& a, Kind k, rr_op_t op, int per_cu, int sync, int timeout_us,
+                         hipStream_t stream);
+// Barrier timeouts of the bucket kernel on the current device.
+hipError_t bucket_timeouts(unsigned long long* count);
 
 // Tensor-parallel layouts (rr_multi.hip) on row-major [rows, cols] matrices
 // with cols = p*w.  "Units" are 16-byte groups, or narrower units (4, 2, 1

@@ -27,6 +27,7 @@
 
 #include "rr_device.h"
 #include "rr_kernels.h"
+#include "rr_sync.h"
 
 namespace rr {
 
@@ -110,20 +111,29 @@ struct RotFold {
 // ---------------------------------------------------------------------------
 // Bucketed all-reduce.
 
-template <class E, class OP, bool VEC>
-__device__ __forceinline__ void bucket_tile(const BucketArgs& a, int pc, uint32_t k) {
-  using F = RotFold<E, OP, kBucketU, VEC>;
+// Tile k of piece pc: byte offsets of the lane's units (lanes past the end
+// re-read the tile's last unit; never stored) and the valid unit count.
+template <class E, bool VEC>
+__device__ __forceinline__ uint32_t bucket_offsets(const BucketArgs& a, int pc, uint32_t k,
+                                                   uint64_t (&off)[kBucketU]) {
   constexpr uint32_t kUnits = static_cast<uint32_t>(kBlock) * kBucketU;
   constexpr uint32_t kUnitBytes = VEC ? 16u : static_cast<uint32_t>(sizeof(typename E::S));
   const uint32_t lane = threadIdx.x;
   const uint32_t valid = min(kUnits, a.units[pc] - k * kUnits);  // units of this tile, >= 1
   const uint64_t base = a.start[pc] * sizeof(typename E::S) + static_cast<uint64_t>(k) * kUnits * kUnitBytes;
-  uint64_t off[kBucketU];
 #pragma unroll
   for (int u = 0; u < kBucketU; ++u) off[u] = base + min(lane + u * kBlock, valid - 1) * kUnitBytes;
+  return valid;
+}
+
+// Write the folded tile to all p outputs of piece pc.
+template <class E, class OP, bool VEC>
+__device__ __forceinline__ void bucket_store(const BucketArgs& a, int pc, uint32_t valid,
+                                             const uint64_t (&off)[kBucketU],
+                                             const typename E::A (&acc)[kBucketU][RotFold<E, OP, kBucketU, VEC>::V]) {
+  using F = RotFold<E, OP, kBucketU, VEC>;
+  const uint32_t lane = threadIdx.x;
   const int p = a.p;
-  typename E::A acc[kBucketU][F::V];
-  F::run(a.ptr + a.base[pc], a.rot[pc], p, off, a.div, acc);
   for (int r = 0; r < p; ++r) {
     char* d = static_cast<char*>(const_cast<void*>(a.ptr[a.base[pc] + p + r]));
 #pragma unroll
@@ -132,26 +142,56 @@ __device__ __forceinline__ void bucket_tile(const BucketArgs& a, int pc, uint32_
   }
 }
 
-template <class E, class OP>
+// The piece of tile t: the last piece whose first tile is <= t.
+__device__ __forceinline__ int bucket_piece(const BucketArgs& a, uint32_t t) {
+  int lo = 0;
+  int hi = a.npieces - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.tile0[mid] <= t) {
+      lo = mid;
+    } else {
+      hi = mid - 1;
+    }
+  }
+  return lo;
+}
+
+// Rounds of gridDim.x tiles.  In a round a workgroup folds its tile from
+// every rank into registers, then writes it to every output.  SYNC (several
+// rounds): the workgroups meet at the soft barrier between the two phases,
+// so that for the length of a phase the device only reads, or only writes
+// (as in the phased fold).  Tiles of scalar pieces (elements of tensors that
+// are not 16-byte aligned) are written before the barrier.
+template <class E, class OP, bool SYNC>
 __global__ __launch_bounds__(kBlock) void k_bucket(BucketArgs a) {
-  for (uint32_t t = blockIdx.x; t < a.tiles; t += gridDim.x) {
-    // the piece of tile t: the last piece whose first tile is <= t
-    int lo = 0;
-    int hi = a.npieces - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.tile0[mid] <= t) {
-        lo = mid;
+  using FV = RotFold<E, OP, kBucketU, true>;
+  using FS = RotFold<E, OP, kBucketU, false>;
+  if constexpr (SYNC) sync_claim_at(a.sync.slot, a.sync.tag);
+  for (uint32_t r = 0; r < a.rounds; ++r) {
+    const uint32_t t = r * gridDim.x + blockIdx.x;
+    const bool live = t < a.tiles;
+    int pc = 0;
+    bool vec = false;
+    uint32_t valid = 0;
+    uint64_t off[kBucketU];
+    typename E::A acc[kBucketU][FV::V];
+    if (live) {
+      pc = bucket_piece(a, t);
+      const uint32_t k = t - a.tile0[pc];
+      vec = a.vec[pc] != 0;
+      if (vec) {
+        valid = bucket_offsets<E, true>(a, pc, k, off);
+        FV::run(a.ptr + a.base[pc], a.rot[pc], a.p, off, a.div, acc);
       } else {
-        hi = mid - 1;
+        typename E::A one[kBucketU][FS::V];
+        valid = bucket_offsets<E, false>(a, pc, k, off);
+        FS::run(a.ptr + a.base[pc], a.rot[pc], a.p, off, a.div, one);
+        bucket_store<E, OP, false>(a, pc, valid, off, one);
       }
     }
-    const uint32_t k = t - a.tile0[lo];
-    if (a.vec[lo]) {
-      bucket_tile<E, OP, true>(a, lo, k);
-    } else {
-      bucket_tile<E, OP, false>(a, lo, k);
-    }
+    if constexpr (SYNC) soft_barrier_at(a.sync.slot, a.sync.tag, a.sync.timeout_ticks, r);
+    if (live && vec) bucket_store<E, OP, true>(a, pc, valid, off, acc);
   }
 }
 
@@ -309,15 +349,48 @@ unsigned stream_grid(uint64_t work_units, uint64_t per_block, int rows, int per_
   return static_cast<unsigned>(g);
 }
 
+// Workgroups of k_bucket<..., true> that one compute unit keeps resident,
+// per (kind, op), queried once.
+template <class E, class OP>
+int bucket_occupancy() {
+  static int occ = 0;
+  int v = __atomic_load_n(&occ, __ATOMIC_RELAXED);
+  if (v == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, reinterpret_cast<const void*>(&k_bucket<E, OP, true>),
+                                                     kBlock, 0) != hipSuccess || v < 1)
+      v = 1;
+    __atomic_store_n(&occ, v, __ATOMIC_RELAXED);
+  }
+  return v;
+}
+
+template <class E, class OP>
+hipError_t bucket_go(BucketArgs a, int per_cu, int sync, int timeout_us, hipStream_t s) {
+  unsigned grid = stream_grid(a.tiles, 1, 1, per_cu > 0 ? per_cu : kBucketPerCu, s);
+  a.rounds = (a.tiles + grid - 1) / grid;
+  if (sync && a.rounds > 1) {
+    // the barrier needs every workgroup resident at once
+    const int cus = cus_of(s);
+    const uint64_t resident = static_cast<uint64_t>(cus > 0 ? cus : 256) * bucket_occupancy<E, OP>();
+    if (grid > resident) grid = static_cast<unsigned>(resident);
+    a.rounds = (a.tiles + grid - 1) / grid;
+    hipError_t e = phase_sync_args(s, timeout_us, &a.sync);
+    if (e != hipSuccess) return e;
+    e = sync_reset_if_captured(a.sync, s);
+    if (e != hipSuccess) return e;
+    return launch(&k_bucket<E, OP, true>, a, dim3(grid), s);
+  }
+  return launch(&k_bucket<E, OP, false>, a, dim3(grid), s);
+}
+
 template <class E>
-hipError_t bucket_by_op(const BucketArgs& a, rr_op_t op, int per_cu, hipStream_t s) {
-  const dim3 grid(stream_grid(a.tiles, 1, 1, per_cu > 0 ? per_cu : kBucketPerCu, s));
+hipError_t bucket_by_op(const BucketArgs& a, rr_op_t op, int per_cu, int sync, int timeout_us, hipStream_t s) {
   switch (op) {
-    case RR_SUM: return launch(&k_bucket<E, OpSum>, a, grid, s);
-    case RR_MAX: return launch(&k_bucket<E, OpMax>, a, grid, s);
-    case RR_MIN: return launch(&k_bucket<E, OpMin>, a, grid, s);
+    case RR_SUM: return bucket_go<E, OpSum>(a, per_cu, sync, timeout_us, s);
+    case RR_MAX: return bucket_go<E, OpMax>(a, per_cu, sync, timeout_us, s);
+    case RR_MIN: return bucket_go<E, OpMin>(a, per_cu, sync, timeout_us, s);
     case RR_AVG:
-      if constexpr (__is_same(typename E::A, float)) return launch(&k_bucket<E, OpAvg>, a, grid, s);
+      if constexpr (__is_same(typename E::A, float)) return bucket_go<E, OpAvg>(a, per_cu, sync, timeout_us, s);
       break;
   }
   return hipErrorInvalidValue;
@@ -360,16 +433,19 @@ hipError_t gather_cols_go(const ColsArgs& a, int per_cu, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_bucket(const BucketArgs& a, Kind k, rr_op_t op, int per_cu, hipStream_t s) {
+hipError_t launch_bucket(const BucketArgs& a, Kind k, rr_op_t op, int per_cu, int sync, int timeout_us,
+                         hipStream_t s) {
   if (a.tiles == 0) return hipSuccess;
   switch (k) {
-    case Kind::kI32: return bucket_by_op<EI32>(a, op, per_cu, s);
-    case Kind::kF32: return bucket_by_op<EF32>(a, op, per_cu, s);
-    case Kind::kBF16: return bucket_by_op<EBF16>(a, op, per_cu, s);
-    case Kind::kF16: return bucket_by_op<EF16>(a, op, per_cu, s);
+    case Kind::kI32: return bucket_by_op<EI32>(a, op, per_cu, sync, timeout_us, s);
+    case Kind::kF32: return bucket_by_op<EF32>(a, op, per_cu, sync, timeout_us, s);
+    case Kind::kBF16: return bucket_by_op<EBF16>(a, op, per_cu, sync, timeout_us, s);
+    case Kind::kF16: return bucket_by_op<EF16>(a, op, per_cu, sync, timeout_us, s);
   }
   return hipErrorInvalidValue;
 }
+
+hipError_t bucket_timeouts(unsigned long long* count) { return sync_timeouts_here(count); }
 
 hipError_t launch_fold_cols(const ColsArgs& a, Kind k, rr_op_t op, int vec, int per_cu, hipStream_t s) {
   if (a.rows * a.wu == 0) return hipSuccess;

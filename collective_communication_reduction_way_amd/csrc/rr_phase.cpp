@@ -43,6 +43,47 @@ uint32_t slot_for(DeviceState& d, hipStream_t s) {
   return slot;
 }
 
+DeviceState* state_of(hipStream_t s, hipError_t* err) {
+  int dev = 0;
+  *err = device_of(s, &dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  DeviceState& d = g_dev[dev];
+  std::call_once(d.once, [&] {
+    if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) d.cus = 0;
+    if (hipDeviceGetAttribute(&d.wall_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) d.wall_khz = 0;
+  });
+  return &d;
+}
+
+// Slot, tag and wait bound of a barrier launch on stream s.  Eager launches
+// take tags 2, 3, ...; a launch under graph capture takes kCapturedTag (its
+// launcher captures a reset of the counters ahead of it).
+hipError_t sync_args_on(DeviceState& d, hipStream_t s, int timeout_us, SyncArgs* y) {
+  memset(y, 0, sizeof(*y));
+  y->slot = slot_for(d, s);
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  const hipError_t e = hipStreamIsCapturing(s, &cs);
+  if (e != hipSuccess) return e;
+  if (cs == hipStreamCaptureStatusActive) {
+    y->captured = 1;
+    y->tag = kCapturedTag;
+  } else {
+    const unsigned long long id = d.launches.fetch_add(1) + 2;
+    y->tag = (id & ((1ull << (64 - kLaunchShift)) - 1)) << kLaunchShift;
+    if (y->tag <= kCapturedTag) y->tag = 2 * kCapturedTag;
+  }
+  const uint64_t khz = d.wall_khz > 0 ? static_cast<uint64_t>(d.wall_khz) : 100000;
+  uint64_t ticks = khz * static_cast<uint64_t>(timeout_us > 0 ? timeout_us : 1) / 1000;
+  if (ticks < 1) ticks = 1;
+  if (ticks > 0xFFFFFFFFull) ticks = 0xFFFFFFFFull;
+  y->timeout_ticks = static_cast<uint32_t>(ticks);
+  return hipSuccess;
+}
+
 // Cut every segment into 16-byte groups and the groups into tiles of `tile`
 // groups; fills the per-segment tables of `a` and returns the tile count.
 uint64_t tile_segments(const FoldLaunch& f, uint64_t V, uint64_t tile, PhaseArgs& a) {
@@ -125,15 +166,10 @@ bool phase_supported(const FoldLaunch& f) {
 // at once (the kernel's occupancy times the compute units): workgroups that
 // had to wait for a free slot would make every barrier run into its timeout.
 hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStream_t s) {
-  int dev = 0;
-  hipError_t e = device_of(s, &dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  DeviceState& d = g_dev[dev];
-  std::call_once(d.once, [&] {
-    if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) d.cus = 0;
-    if (hipDeviceGetAttribute(&d.wall_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) d.wall_khz = 0;
-  });
+  hipError_t e = hipSuccess;
+  DeviceState* dp = state_of(s, &e);
+  if (!dp) return e;
+  DeviceState& d = *dp;
   const uint64_t cus = d.cus > 0 ? static_cast<uint64_t>(d.cus) : 256;
   const bool ring = f.mode == FoldMode::kRingAll;
   const uint64_t V = is_half(f.in_kind) ? 8 : 4;
@@ -211,26 +247,22 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
       grid = resident;
       a.rounds = static_cast<uint32_t>((tiles + grid - 1) / grid);
     }
-    a.slot = slot_for(d, s);
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    e = hipStreamIsCapturing(s, &cs);
+    SyncArgs y;
+    e = sync_args_on(d, s, pt.timeout_us, &y);
     if (e != hipSuccess) return e;
-    if (cs == hipStreamCaptureStatusActive) {
-      a.captured = 1;
-      a.tag = kCapturedTag;
-    } else {
-      // tags 2, 3, ...: 1 belongs to captured launches
-      const unsigned long long id = d.launches.fetch_add(1) + 2;
-      a.tag = (id & ((1ull << (64 - kLaunchShift)) - 1)) << kLaunchShift;
-      if (a.tag <= kCapturedTag) a.tag = 2 * kCapturedTag;
-    }
-    const uint64_t khz = d.wall_khz > 0 ? static_cast<uint64_t>(d.wall_khz) : 100000;
-    uint64_t ticks = khz * static_cast<uint64_t>(pt.timeout_us) / 1000;
-    if (ticks < 1) ticks = 1;
-    if (ticks > 0xFFFFFFFFull) ticks = 0xFFFFFFFFull;
-    a.timeout_ticks = static_cast<uint32_t>(ticks);
+    a.slot = y.slot;
+    a.tag = y.tag;
+    a.timeout_ticks = y.timeout_ticks;
+    a.captured = y.captured;
   }
   return launch_mode(f, a, static_cast<unsigned>(grid), unroll, sync, static_p, nullptr, s);
+}
+
+hipError_t phase_sync_args(hipStream_t s, int timeout_us, SyncArgs* y) {
+  hipError_t e = hipSuccess;
+  DeviceState* d = state_of(s, &e);
+  if (!d) return e;
+  return sync_args_on(*d, s, timeout_us, y);
 }
 
 hipError_t phase_barrier_timeouts(int device, unsigned long long* count) {
@@ -242,11 +274,13 @@ hipError_t phase_barrier_timeouts(int device, unsigned long long* count) {
   unsigned long long hier = 0;
   unsigned long long var = 0;
   unsigned long long one = 0;
+  unsigned long long bucket = 0;
   e = phase_timeouts_ring(&ring);
   if (e == hipSuccess) e = phase_timeouts_hier(&hier);
   if (e == hipSuccess) e = phase_timeouts_hier_var(&var);
   if (e == hipSuccess) e = phase_timeouts_one(&one);
-  *count = ring + hier + var + one;
+  if (e == hipSuccess) e = bucket_timeouts(&bucket);
+  *count = ring + hier + var + one + bucket;
   if (device != cur) {
     const hipError_t e2 = hipSetDevice(cur);
     if (e == hipSuccess) e = e2;

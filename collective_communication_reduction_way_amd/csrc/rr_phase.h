@@ -50,6 +50,10 @@ struct PhaseArgs {
   int32_t captured;  // 1: launched under graph capture (tag = kCapturedTag; reset first)
 };
 
+// Fill `y` for a launch with a barrier on stream s (any translation unit:
+// each keeps its own counters, the slots are per stream).
+hipError_t phase_sync_args(hipStream_t s, int timeout_us, SyncArgs* y);
+
 // Groups per lane per tile of the phased fold: 8 (32 KiB per rank and tile
 // for 4-byte types); 4 for the bfloat16 hierarchy, whose second set of
 // partials (the running total over groups) would otherwise cost too many

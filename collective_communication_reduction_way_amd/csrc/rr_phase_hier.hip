@@ -9,6 +9,6 @@ hipError_t phase_launch_hier(const PhaseArgs& a, Kind k, rr_op_t op, unsigned gr
   return phase_dispatch<FoldMode::kHierAll>(a, k, op, grid, unroll, sync, static_p, occ, s);
 }
 
-hipError_t phase_timeouts_hier(unsigned long long* count) { return phase_timeouts_here(count); }
+hipError_t phase_timeouts_hier(unsigned long long* count) { return sync_timeouts_here(count); }
 
 }  // namespace rr

@@ -19,7 +19,7 @@ hipError_t phase_launch_hier_var(const PhaseArgs& a, FoldMode m, Kind k, rr_op_t
   return hipErrorInvalidValue;
 }
 
-hipError_t phase_timeouts_hier_var(unsigned long long* count) { return phase_timeouts_here(count); }
+hipError_t phase_timeouts_hier_var(unsigned long long* count) { return sync_timeouts_here(count); }
 
 hipError_t launch_fold_hier_var(const FoldLaunch& f, hipStream_t s) {
   switch (f.mode) {

@@ -46,66 +46,17 @@
 
 #include "rr_fold_impl.h"
 #include "rr_phase.h"
+#include "rr_sync.h"
 
 namespace rr {
 
 namespace {
 
-// Barrier counters and the timeout count: one copy per translation unit
-// (and per device), zero when the code object loads.
-__device__ __align__(256) unsigned long long g_sync[kSyncSlots * kSyncCounters * kSyncStride];
-__device__ unsigned long long g_sync_timeouts;
+// The soft barrier, on this mode's PhaseArgs (rr_sync.h).
+__device__ __forceinline__ void sync_claim(const PhaseArgs& a) { sync_claim_at(a.slot, a.tag); }
 
-
-__device__ __forceinline__ unsigned long long* sync_counter(uint32_t slot, uint32_t i) {
-  return g_sync + (static_cast<size_t>(slot) * kSyncCounters + i) * kSyncStride;
-}
-
-__device__ __forceinline__ unsigned long long atomic_add_relaxed(unsigned long long* p, unsigned long long v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void atomic_max_relaxed(unsigned long long* p, unsigned long long v) {
-  __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void sync_claim(const PhaseArgs& a) {
-  if (threadIdx.x == 0) atomic_max_relaxed(sync_counter(a.slot, blockIdx.x % kSyncSubs), a.tag);
-}
-
-// Clear one slot's counters: captured ahead of a launch whose tag is fixed
-// (graph replays), so that every replay counts from zero like an eager
-// launch with a fresh tag.
-__global__ __launch_bounds__(64) void k_sync_reset(uint32_t slot) {
-  if (threadIdx.x < static_cast<uint32_t>(kSyncCounters))
-    __hip_atomic_store(sync_counter(slot, threadIdx.x), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Arrive at barrier `round` and wait (bounded) until all G workgroups have.
 __device__ __forceinline__ void soft_barrier(const PhaseArgs& a, uint32_t round) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t G = gridDim.x;
-    const uint32_t sub = blockIdx.x % kSyncSubs;
-    const uint32_t nsub = G < kSyncSubs ? G : kSyncSubs;
-    const uint32_t per = G / kSyncSubs + (sub < G % kSyncSubs ? 1u : 0u);  // workgroups on this counter
-    unsigned long long* top = sync_counter(a.slot, kSyncSubs);
-    const unsigned long long seen = atomic_add_relaxed(sync_counter(a.slot, sub), 1ull) + 1 - a.tag;
-    if (seen == static_cast<unsigned long long>(round + 1) * per) {
-      atomic_max_relaxed(top, a.tag);
-      atomic_add_relaxed(top, 1ull);
-    }
-    const unsigned long long target = a.tag + static_cast<unsigned long long>(round + 1) * nsub;
-    const uint64_t t0 = wall_clock64();
-    while (__hip_atomic_load(top, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(2);
-      if (wall_clock64() - t0 > a.timeout_ticks) {
-        atomic_add_relaxed(&g_sync_timeouts, 1ull);
-        break;
-      }
-    }
-  }
-  __syncthreads();
+  soft_barrier_at(a.slot, a.tag, a.timeout_ticks, round);
 }
 
 // Loads of one rank's tile.  In a partial tile (valid < kBlock*U groups) the
@@ -385,9 +336,10 @@ hipError_t phase_dispatch(const PhaseArgs& a, Kind k, rr_op_t op, unsigned grid,
                           bool static_p, int* occ, hipStream_t s) {
   if (sync && occ == nullptr && a.captured) {
     // this translation unit's counters, cleared on the same stream first
-    uint32_t slot = a.slot;
-    void* kp[] = {&slot};
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&k_sync_reset), dim3(1), dim3(64), kp, 0, s);
+    SyncArgs y{};
+    y.slot = a.slot;
+    y.captured = 1;
+    const hipError_t e = sync_reset_if_captured(y, s);
     if (e != hipSuccess) return e;
   }
   if constexpr (!is_wire(M)) {
@@ -420,10 +372,6 @@ hipError_t fold_var_dispatch(const FoldLaunch& f, hipStream_t s) {
   if (f.in_kind == Kind::kBF16) return fold_mixed_by_op<EBF16, EBF16, M>(f, s);
   if (f.in_kind == Kind::kF16) return fold_mixed_by_op<EF16, EF16, M>(f, s);
   return hipErrorInvalidValue;
-}
-
-hipError_t phase_timeouts_here(unsigned long long* count) {
-  return hipMemcpyFromSymbol(count, HIP_SYMBOL(g_sync_timeouts), sizeof(*count), 0, hipMemcpyDeviceToHost);
 }
 
 }  // namespace

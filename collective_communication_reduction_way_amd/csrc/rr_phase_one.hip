@@ -16,6 +16,6 @@ hipError_t phase_launch_one(const PhaseArgs& a, FoldMode m, Kind k, rr_op_t op, 
   return hipErrorInvalidValue;
 }
 
-hipError_t phase_timeouts_one(unsigned long long* count) { return phase_timeouts_here(count); }
+hipError_t phase_timeouts_one(unsigned long long* count) { return sync_timeouts_here(count); }
 
 }  // namespace rr

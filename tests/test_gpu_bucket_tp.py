@@ -118,6 +118,33 @@ def test_bucket_gpt2_block_full_size(rr):
     torch.cuda.empty_cache()
 
 
+def test_bucket_barrier(rr, monkeypatch):
+    """A bucket of several rounds separates its read and write phases with
+    the soft barrier.  A 1 us bound makes the waits run out: the results must
+    not change and the timeouts must be counted.  Without the barrier, and
+    with more workgroups per CU requested than fit at once (the grid is
+    capped at residency, so no wait runs out), the bits are the same."""
+    p = 8
+    sizes = [3 * (1 << 20) + 5, 1 << 22, 777]
+    parts = [W.random_inputs(81 + i, p, n, "float32") for i, n in enumerate(sizes)]
+    want = C.all_reduce_bucket(parts, "avg", "float32")
+    t0 = rr.barrier_timeouts()
+    check_bucket(run_bucket(rr, parts, "float32", "avg"), want, "default")
+    assert rr.barrier_timeouts() == t0
+    monkeypatch.setenv("RR_MULTI_PER_CU", "64")
+    check_bucket(run_bucket(rr, parts, "float32", "avg"), want, "64 workgroups per CU requested")
+    assert rr.barrier_timeouts() == t0
+    monkeypatch.delenv("RR_MULTI_PER_CU")
+    monkeypatch.setenv("RR_PHASE_SYNC", "0")
+    check_bucket(run_bucket(rr, parts, "float32", "avg"), want, "no barrier")
+    monkeypatch.delenv("RR_PHASE_SYNC")
+    monkeypatch.setenv("RR_PHASE_TIMEOUT_US", "1")
+    for _ in range(2):
+        check_bucket(run_bucket(rr, parts, "float32", "avg"), want, "1 us barrier bound")
+    assert rr.barrier_timeouts() > t0, "the forced bound never ran out: the bucket's barrier was not exercised"
+    torch.cuda.empty_cache()
+
+
 def test_bucket_empty_and_rejected(rr):
     assert rr.all_reduce_bucket([]) == []
     a = torch.ones((4, 64), dtype=torch.int32, device="cuda")
