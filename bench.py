@@ -65,7 +65,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 # Sources that define the fused all-reduce kernel; the traffic record is
 # valid only while their contents are unchanged.
 KERNEL_SOURCES = [os.path.join(ROOT, "collective_communication_reduction_way_amd", "csrc", f) for f in
-                  ("rr_device.h", "rr_kernels.h", "rr_fold_impl.h", "rr_phase.h", "rr_phase_impl.h",
+                  ("rr_device.h", "rr_kernels.h", "rr_fold_impl.h", "rr_phase.h", "rr_phase_impl.h", "rr_sync.h",
                    "rr_phase_ring.hip", "rr_phase_hier.hip", "rr_phase.cpp")]
 
 
