@@ -63,7 +63,8 @@ int env_int(const char* name, int dflt) {
 // buffers), RR_PHASE_SYNC (0 = no barrier between the read and write phases),
 // RR_PHASE_PER_CU (workgroups per compute unit of the phased fold; 0 = by the
 // schedule), RR_PHASE_GRID (explicit workgroup count), RR_PHASE_U (4 = the
-// smaller tile for sums), RR_PHASE_STATIC (1 / 0 = the kernels compiled for
+// smaller tile for sums, 8 = the mode's default tile everywhere, 0 = by the
+// schedule), RR_PHASE_STATIC (1 / 0 = the kernels compiled for
 // p = 8 / the run-time rank loop; -1 = by mode),
 // RR_PHASE_TIMEOUT_US (bound of one barrier wait, default 200),
 // RR_MULTI_PER_CU (workgroups per compute unit of the bucket and dim-1
@@ -108,7 +109,8 @@ Tuning tuning() {
   if (t.pt.per_cu < 0 || t.pt.per_cu > 64) t.pt.per_cu = 0;
   t.pt.grid = env_int("RR_PHASE_GRID", 0);
   if (t.pt.grid < 0) t.pt.grid = 0;
-  t.pt.unroll = env_int("RR_PHASE_U", 0) == 4 ? 4 : 0;
+  t.pt.unroll = env_int("RR_PHASE_U", 0);
+  if (t.pt.unroll != 4 && t.pt.unroll != 8) t.pt.unroll = 0;
   t.pt.timeout_us = env_int("RR_PHASE_TIMEOUT_US", 200);
   t.pt.static_p = env_int("RR_PHASE_STATIC", -1);
   if (t.pt.static_p > 1) t.pt.static_p = 1;
