@@ -215,6 +215,15 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
     if (pt.per_cu <= 0) per_cu = 4;
     tiles = tile_segments(f, V, static_cast<uint64_t>(kBlock) * unroll, a);
     if (tiles >= 0x7FFFFFFFull) return hipErrorInvalidValue;
+    // at most half as many tiles as CUs (small launches): 2 groups per lane,
+    // then 1, as long as the tiles still fit one per CU (1 MiB fp32 per rank:
+    // 29% -> 39-40% of the HBM peak; 3 MiB, where the halving would give 1.5
+    // tiles per CU, stays at 4 groups)
+    while (unroll > 1 && 2 * tiles <= cus) {
+      unroll /= 2;
+      tiles = tile_segments(f, V, static_cast<uint64_t>(kBlock) * unroll, a);
+      if (tiles >= 0x7FFFFFFFull) return hipErrorInvalidValue;
+    }
     if (pt.static_p < 0) static_p = tiles <= cus;
     grid = cus * static_cast<uint64_t>(per_cu);
   }

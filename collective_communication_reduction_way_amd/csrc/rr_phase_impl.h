@@ -290,6 +290,12 @@ hipError_t phase_by_u(const PhaseArgs& a, unsigned grid, int unroll, int* occ, h
   if (unroll == kU) return phase_go(&k_phase<E, OP, P, kU, M, SYNC>, a, grid, kBlock, occ, s);
   if constexpr ((__is_same(OP, OpSum) || __is_same(OP, OpAvg)) && kU != 4) {
     if (unroll == 4) return phase_go(&k_phase<E, OP, P, 4, M, SYNC>, a, grid, kBlock, occ, s);
+    // one-round launches of the ring all-reduce too small for a tile of 4
+    // groups per lane on every CU
+    if constexpr (M == FoldMode::kRingAll && !SYNC) {
+      if (unroll == 2) return phase_go(&k_phase<E, OP, P, 2, M, false>, a, grid, kBlock, occ, s);
+      if (unroll == 1) return phase_go(&k_phase<E, OP, P, 1, M, false>, a, grid, kBlock, occ, s);
+    }
   }
   return hipErrorInvalidValue;
 }

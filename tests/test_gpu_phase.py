@@ -137,3 +137,19 @@ def test_reduce_scatter_and_reduce_schedules_agree(rr, monkeypatch, env):
         assert rr.barrier_timeouts() == t0
     del xs, sh, red, red_b
     torch.cuda.empty_cache()
+
+
+# Per-rank lengths whose one-round launch takes the tile of 4, 2 or 1 groups
+# per lane (fewer 8-group tiles than CUs), with ragged chunk tails, p = 8
+# (the kernels compiled for p = 8), 4 and 5 (the run-time loop).
+SMALL = [(8, 1 << 20), (8, (1 << 19) + 13), (8, (1 << 18) + 3), (8, 65536), (8, 5000), (4, 1 << 19), (5, 300007),
+         (8, (3 << 20) + 24)]
+
+
+@pytest.mark.parametrize("p,n", SMALL)
+@pytest.mark.parametrize("dtype", ("int32", "float32", "bfloat16", "float16"))
+def test_small_one_round_tiles(rr, p, n, dtype):
+    x = W.random_inputs(65, p, n, dtype, kind="full" if dtype == "int32" else "normal")
+    ops = ("sum", "max") + (("avg",) if dtype != "int32" else ())
+    for op in ops:
+        assert_bitwise(run_ar(rr, x, dtype, op, "ring"), C.all_reduce_ring(x, op, dtype), f"{op}")
