@@ -153,15 +153,17 @@ bool phase_supported(const FoldLaunch& f) {
 // Schedule choice (measured on MI355X; every knob can be forced through
 // PhaseTuning):
 //   ring all-reduce, one round: 8 groups per lane, 2 workgroups per CU, the
-//     kernel compiled for p = 8 when p is 8;
-//   ring all-reduce, several rounds, sums: 4 groups per lane, 4 workgroups
-//     per CU (shorter phases between barriers); the kernel compiled for
-//     p = 8 for bfloat16, the run-time rank loop for 4-byte types;
+//     kernel compiled for p = 8 when p is 8 (float16: the run-time loop);
+//     fewer 8-group tiles than CUs (16-bit types: than 2 per CU): 4 groups
+//     per lane, then 2 and 1 while the tiles still fit one per CU;
+//   ring all-reduce, several rounds: 4 groups per lane, 4 workgroups per CU
+//     (shorter phases between barriers); the kernel compiled for p = 8 for
+//     bfloat16, the run-time rank loop for the other types;
 //   hierarchical all-reduce: the run-time rank loop, 4 workgroups per CU with
-//     the bfloat16 tile of 4 groups per lane, else 2;
-//   reduce-scatter and reduce: 4 groups per lane for sums (8 for max/min),
-//     32 workgroups per CU (the grid oversubscribes the device; workgroups
-//     start as others finish), the kernel compiled for p = 8, no barrier.
+//     the 16-bit tile of 4 groups per lane, else 2;
+//   reduce-scatter and reduce: 4 groups per lane, 32 workgroups per CU (the
+//     grid oversubscribes the device; workgroups start as others finish),
+//     the kernel compiled for p = 8, no barrier.
 // With the barrier, the grid never exceeds what the device can keep resident
 // at once (the kernel's occupancy times the compute units): workgroups that
 // had to wait for a free slot would make every barrier run into its timeout.
@@ -173,7 +175,10 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
   const uint64_t cus = d.cus > 0 ? static_cast<uint64_t>(d.cus) : 256;
   const bool ring = f.mode == FoldMode::kRingAll;
   const uint64_t V = is_half(f.in_kind) ? 8 : 4;
-  const bool sum_like = f.op == RR_SUM || f.op == RR_AVG;
+  // the kernels with fewer than 8 groups per lane exist for every op of the
+  // ring all-reduce, reduce-scatter and reduce, and for sums elsewhere
+  const bool small_ok = f.op == RR_SUM || f.op == RR_AVG || f.mode == FoldMode::kRingAll ||
+                        f.mode == FoldMode::kRingShard || f.mode == FoldMode::kAscOne;
   // the kernels compiled for p = 8: default for the modes that read p inputs
   // and write one output or all of them in ring order, binary16 excepted:
   // with every rank unrolled its conversions are hoisted past 256 registers
@@ -185,7 +190,7 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
   // reduce-scatter and reduce: one output per p inputs
   const bool one_out = f.mode == FoldMode::kRingShard || f.mode == FoldMode::kAscOne;
   int unroll = phase_default_unroll(f.in_kind, f.mode);
-  if ((pt.unroll == 4 || (one_out && pt.unroll == 0)) && sum_like) unroll = 4;
+  if ((pt.unroll == 4 || (one_out && pt.unroll == 0)) && small_ok) unroll = 4;
   // one-output modes run without the barrier, so nothing ties their grid to
   // residency: 32 workgroups per CU (about one tile each) measured best
   int per_cu = pt.per_cu > 0 ? pt.per_cu : (one_out ? 32 : (unroll == 4 ? 4 : 2));
@@ -197,7 +202,7 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
   uint64_t tiles = tile_segments(f, V, static_cast<uint64_t>(kBlock) * unroll, a);
   if (tiles >= 0x7FFFFFFFull) return hipErrorInvalidValue;
   uint64_t grid = pt.grid > 0 ? static_cast<uint64_t>(pt.grid) : cus * static_cast<uint64_t>(per_cu);
-  if (ring && pt.unroll == 0 && pt.grid == 0 && sum_like && unroll == 8 && tiles > grid) {
+  if (ring && pt.unroll == 0 && pt.grid == 0 && small_ok && unroll == 8 && tiles > grid) {
     // several rounds: the smaller tile, more workgroups
     unroll = 4;
     if (pt.per_cu <= 0) per_cu = 4;
@@ -205,7 +210,7 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
     tiles = tile_segments(f, V, static_cast<uint64_t>(kBlock) * unroll, a);
     if (tiles >= 0x7FFFFFFFull) return hipErrorInvalidValue;
     grid = cus * static_cast<uint64_t>(per_cu);
-  } else if (ring && pt.unroll == 0 && pt.grid == 0 && sum_like && unroll == 8 &&
+  } else if (ring && pt.unroll == 0 && pt.grid == 0 && small_ok && unroll == 8 &&
              (tiles < cus || (is_half(f.in_kind) && tiles < 2 * cus))) {
     // one round with too few tiles of 8 groups per lane to fill the device
     // (fewer than one per CU; for 16-bit types, which also convert, fewer

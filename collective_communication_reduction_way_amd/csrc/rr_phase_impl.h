@@ -288,7 +288,11 @@ template <class E, class OP, int P, FoldMode M, bool SYNC>
 hipError_t phase_by_u(const PhaseArgs& a, unsigned grid, int unroll, int* occ, hipStream_t s) {
   constexpr int kU = phase_unroll<E, M>();
   if (unroll == kU) return phase_go(&k_phase<E, OP, P, kU, M, SYNC>, a, grid, kBlock, occ, s);
-  if constexpr ((__is_same(OP, OpSum) || __is_same(OP, OpAvg)) && kU != 4) {
+  // the smaller tiles: for sums in every mode, for every op in the modes
+  // whose schedule uses them (ring all-reduce, reduce-scatter, reduce)
+  constexpr bool kSmall = __is_same(OP, OpSum) || __is_same(OP, OpAvg) || M == FoldMode::kRingAll ||
+                          M == FoldMode::kRingShard || M == FoldMode::kAscOne;
+  if constexpr (kSmall && kU != 4) {
     if (unroll == 4) return phase_go(&k_phase<E, OP, P, 4, M, SYNC>, a, grid, kBlock, occ, s);
     // one-round launches of the ring all-reduce too small for a tile of 4
     // groups per lane on every CU
