@@ -232,6 +232,15 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
     if (pt.static_p < 0) static_p = tiles <= cus;
     grid = cus * static_cast<uint64_t>(per_cu);
   }
+  if (one_out && pt.unroll == 0 && pt.grid == 0 && unroll == 4) {
+    // reduce-scatter and reduce too small for a tile of 4 groups per lane on
+    // every CU: 2, then 1, while the tiles still fit one per CU
+    while (unroll > 1 && 2 * tiles <= cus) {
+      unroll /= 2;
+      tiles = tile_segments(f, V, static_cast<uint64_t>(kBlock) * unroll, a);
+      if (tiles >= 0x7FFFFFFFull) return hipErrorInvalidValue;
+    }
+  }
   if (grid > tiles) grid = tiles;
   if (grid < 1) grid = 1;
   a.rounds = static_cast<uint32_t>((tiles + grid - 1) / grid);

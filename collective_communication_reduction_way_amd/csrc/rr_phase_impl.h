@@ -294,9 +294,9 @@ hipError_t phase_by_u(const PhaseArgs& a, unsigned grid, int unroll, int* occ, h
                           M == FoldMode::kRingShard || M == FoldMode::kAscOne;
   if constexpr (kSmall && kU != 4) {
     if (unroll == 4) return phase_go(&k_phase<E, OP, P, 4, M, SYNC>, a, grid, kBlock, occ, s);
-    // one-round launches of the ring all-reduce too small for a tile of 4
-    // groups per lane on every CU
-    if constexpr (M == FoldMode::kRingAll && !SYNC) {
+    // launches too small for a tile of 4 groups per lane on every CU (ring
+    // all-reduce in one round, reduce-scatter, reduce)
+    if constexpr ((M == FoldMode::kRingAll || M == FoldMode::kRingShard || M == FoldMode::kAscOne) && !SYNC) {
       if (unroll == 2) return phase_go(&k_phase<E, OP, P, 2, M, false>, a, grid, kBlock, occ, s);
       if (unroll == 1) return phase_go(&k_phase<E, OP, P, 1, M, false>, a, grid, kBlock, occ, s);
     }

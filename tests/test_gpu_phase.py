@@ -153,3 +153,21 @@ def test_small_one_round_tiles(rr, p, n, dtype):
     ops = ("sum", "max") + (("avg",) if dtype != "int32" else ())
     for op in ops:
         assert_bitwise(run_ar(rr, x, dtype, op, "ring"), C.all_reduce_ring(x, op, dtype), f"{op}")
+
+
+@pytest.mark.parametrize("p,n", [(8, 1 << 20), (8, (1 << 19) + 88), (8, 40000), (5, 300005), (8, (1 << 18) + 8)])
+@pytest.mark.parametrize("dtype", ("int32", "float32", "bfloat16", "float16"))
+def test_small_reduce_scatter_and_reduce_tiles(rr, p, n, dtype):
+    """Reduce-scatter and reduce small enough for the tiles of 2 and 1
+    groups per lane (chunks that are not whole 16-byte groups included)."""
+    x = W.random_inputs(66, p, n, dtype, kind="full" if dtype == "int32" else "normal")
+    xs = to_dev(x, dtype)
+    for op in ("sum", "min") + (("avg",) if dtype != "int32" else ()):
+        outs = torch.empty((p, n // p), dtype=xs.dtype, device="cuda")
+        rr.reduce_scatter(xs, outs, op=op)
+        assert_bitwise(to_host(outs, dtype), C.reduce_scatter_ring(x, op, dtype), f"reduce_scatter {op}")
+        if op == "avg":
+            continue
+        red = torch.empty(n, dtype=xs.dtype, device="cuda")
+        rr.reduce(xs, red, root=0, op=op)
+        assert_bitwise(to_host(red, dtype), C.reduce(x, op, dtype), f"reduce {op}")
