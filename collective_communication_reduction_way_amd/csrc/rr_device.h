@@ -35,19 +35,29 @@ struct EF16 {
 // bfloat16 <-> float32.
 //
 // widen: the 16 bits become the upper half of a float32 (exact).
-// narrow: round to nearest, ties to even, done on the integer pattern: adding
+// narrow: round to nearest, ties to even, as on the integer pattern: adding
 // 0x7FFF plus the lowest kept bit and truncating rounds half-way cases to the
 // even neighbour; a mantissa carry moves into the exponent, so overflow gives
 // +-inf.  A NaN keeps sign and top payload and gets the quiet bit (0x0040 in
 // bf16) so it cannot become an infinity.  Denormals round like any value.
+// gfx950's conversion instruction (v_cvt_pk_bf16_f32, two values per
+// instruction) gives exactly these bits: an exhaustive comparison over all
+// 2^32 float32 inputs, in the floating-point mode the library is built with
+// (denormals kept, round to nearest even), found no difference.
 __device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-  const uint32_t quiet = (u >> 16) | 0x0040u;
-  return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? quiet : rounded;
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two values narrowed by one instruction: lo in bits 0-15, hi in 16-31.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_bits(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // ---------------------------------------------------------------------------
@@ -217,6 +227,9 @@ __device__ __forceinline__ void pack(const A* a, Raw<E, V>& r) {
         r.w[j / 4][j % 4] = static_cast<uint32_t>(a[j]);
       }
     }
+  } else if constexpr (__is_same(E, EBF16)) {
+#pragma unroll
+    for (int j = 0; j < V; j += 2) r.w[j / 8][(j % 8) / 2] = f32x2_to_bf16x2_bits(a[j], a[j + 1]);
   } else {
 #pragma unroll
     for (int j = 0; j < V; j += 2) {
