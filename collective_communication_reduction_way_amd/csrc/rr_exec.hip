@@ -257,17 +257,58 @@ __global__ __launch_bounds__(kBlock) void k_ring_exec(ExecArgs a) {
 
 constexpr int kMaxDevices = 64;
 
+// A slot's flags belong to one stream at a time.  `done` is recorded after
+// the slot's last eager launch; once it has completed, no launch uses the
+// slot any more and the next eager call returns it to the free list.  A slot
+// whose stream captured a launch into a graph stays with that stream
+// (replays may come at any time).
+struct ExecSlot {
+  hipStream_t owner = nullptr;
+  bool used = false;
+  bool pinned = false;
+  hipEvent_t done = nullptr;
+};
+
 struct ExecDevice {
   std::once_flag once;
   int cus = 0;
   int wall_khz = 0;
   unsigned long long launches = 0;
-  std::mutex mu;
-  std::map<hipStream_t, uint32_t> slot_of;
+  std::mutex mu;  // slots, tags and the launches that use them
+  ExecSlot slots[kExecSlots];
   std::map<uint32_t, int> occupancy;
 };
 
 ExecDevice g_exec_dev[kMaxDevices];
+
+// Return to the free list every slot whose last launch has completed.  Eager
+// calls only: querying an event is not allowed while a stream is being
+// captured.  Called with d.mu held.
+void exec_release_done(ExecDevice& d) {
+  for (ExecSlot& x : d.slots) {
+    if (x.used && !x.pinned && x.done && hipEventQuery(x.done) == hipSuccess) {
+      x.used = false;
+      x.owner = nullptr;
+    }
+  }
+}
+
+// The slot of stream s: its own, else a free one (after releasing the
+// completed ones, when not capturing).  -1 when none is free.  Called with
+// d.mu held.
+int exec_slot_for(ExecDevice& d, hipStream_t s, bool captured) {
+  for (int i = 0; i < kExecSlots; ++i)
+    if (d.slots[i].used && d.slots[i].owner == s) return i;
+  if (!captured) exec_release_done(d);
+  for (int i = 0; i < kExecSlots; ++i) {
+    if (!d.slots[i].used) {
+      d.slots[i].used = true;
+      d.slots[i].owner = s;
+      return i;
+    }
+  }
+  return -1;
+}
 
 template <class E, class EA, class OP>
 hipError_t exec_go(ExecArgs a, int budget_per_cu_cap, int max_slices, int timeout_us, hipStream_t s, ExecDevice& d,
@@ -299,41 +340,45 @@ hipError_t exec_go(ExecArgs a, int budget_per_cu_cap, int max_slices, int timeou
   if (static_cast<uint64_t>(slices) > by_size) slices = static_cast<int>(by_size);
   if (slices < 1) slices = 1;
   a.nslices = slices;
-  {
-    // One slot per stream, never shared: the flags order data, and launches
-    // on two streams may run at the same time.  (Launches on one stream
-    // run one after the other, so they reuse its slot.)
-    std::lock_guard<std::mutex> lock(d.mu);
-    auto it = d.slot_of.find(s);
-    if (it == d.slot_of.end()) {
-      if (d.slot_of.size() >= static_cast<size_t>(kExecSlots)) return hipErrorOutOfMemory;
-      it = d.slot_of.emplace(s, static_cast<uint32_t>(d.slot_of.size())).first;
-    }
-    a.slot = it->second;
-  }
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  hipError_t ce = hipStreamIsCapturing(s, &cs);
-  if (ce != hipSuccess) return ce;
-  if (cs == hipStreamCaptureStatusActive) {
-    a.captured = 1;
-    a.tag = kExecCapturedTag;
-    uint32_t slot = a.slot;
-    int workers = slices * a.p;
-    void* rp[] = {&slot, &workers};
-    ce = hipLaunchKernel(reinterpret_cast<const void*>(&k_exec_reset), dim3(1), dim3(kBlock), rp, 0, s);
-    if (ce != hipSuccess) return ce;
-  } else {
-    std::lock_guard<std::mutex> lock(d.mu);
-    const unsigned long long id = ++d.launches + 1;  // 2, 3, ...: 1 belongs to captured launches
-    a.tag = (id & ((1ull << (64 - kExecShift)) - 1)) << kExecShift;
-    if (a.tag <= kExecCapturedTag) a.tag = 2 * kExecCapturedTag;
-  }
   const uint64_t khz = d.wall_khz > 0 ? static_cast<uint64_t>(d.wall_khz) : 100000;
   uint64_t ticks = khz * static_cast<uint64_t>(timeout_us) / 1000;
   if (ticks < 1) ticks = 1;
   a.timeout_ticks = ticks;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(s, &cs);
+  if (e != hipSuccess) return e;
+  const bool captured = cs == hipStreamCaptureStatusActive;
+  // The flags order data, so launches that may run at the same time (on
+  // different streams) never share a slot.  The lock covers the choice of
+  // the slot, the launch and the record of its completion event, so that no
+  // other thread can take the slot in between.
+  std::lock_guard<std::mutex> lock(d.mu);
+  const int si = exec_slot_for(d, s, captured);
+  if (si < 0) return hipErrorOutOfMemory;
+  ExecSlot& slot = d.slots[si];
+  a.slot = static_cast<uint32_t>(si);
+  if (captured) {
+    a.captured = 1;
+    a.tag = kExecCapturedTag;
+    slot.pinned = true;
+    uint32_t sl = a.slot;
+    int workers = slices * a.p;
+    void* rp[] = {&sl, &workers};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&k_exec_reset), dim3(1), dim3(kBlock), rp, 0, s);
+    if (e != hipSuccess) return e;
+  } else {
+    const unsigned long long id = ++d.launches + 1;  // 2, 3, ...: 1 belongs to captured launches
+    a.tag = (id & ((1ull << (64 - kExecShift)) - 1)) << kExecShift;
+    if (a.tag <= kExecCapturedTag) a.tag = 2 * kExecCapturedTag;
+  }
   void* kp[] = {&a};
-  return hipLaunchKernel(kernel, dim3(static_cast<unsigned>(slices * a.p)), dim3(kBlock), kp, 0, s);
+  e = hipLaunchKernel(kernel, dim3(static_cast<unsigned>(slices * a.p)), dim3(kBlock), kp, 0, s);
+  if (e != hipSuccess || captured) return e;
+  // the completion event lets the slot pass to another stream later; if it
+  // cannot be recorded, the slot simply stays with this stream
+  if (!slot.done && hipEventCreateWithFlags(&slot.done, hipEventDisableTiming) != hipSuccess) slot.done = nullptr;
+  if (!slot.done || hipEventRecord(slot.done, s) != hipSuccess) slot.pinned = true;
+  return hipSuccess;
 }
 
 template <class E, class EA>

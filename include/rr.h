@@ -187,9 +187,13 @@ rr_status_t rr_all_reduce(const void* const* sendbufs, void* const* recvbufs, in
  *     Workspace as RR_ALGO_RING_STAGED.  Bitwise equal to RR_ALGO_RING_FUSED.
  *     If a wait runs out (the workgroups were not all resident, e.g. other
  *     kernels filled the GPU), the launch stops and its outputs are
- *     incomplete; rr_ring_exec_failures() counts such launches.  Up to 16
- *     distinct streams per device may use this algorithm (its step flags are
- *     kept per stream); a 17th returns RR_ERROR_HIP.
+ *     incomplete; rr_ring_exec_failures() counts such launches.  Its step
+ *     flags come in 16 slots per device, each used by one stream at a time:
+ *     a stream keeps its slot while it has one, and every call that is not
+ *     being captured frees the slots whose last launch has completed.  A
+ *     call while 16 other streams hold slots with launches in flight (or
+ *     pinned, below) returns RR_ERROR_HIP.  A slot whose stream captured a
+ *     launch into a graph stays with that stream.
  *   group_size: 1 <= group_size <= p and group_size | p (HIER algos only).
  *   workspace: device memory of at least rr_workspace_size(algo, ...) bytes,
  *     16-byte aligned, owned by the caller, not aliasing any buffer; may be

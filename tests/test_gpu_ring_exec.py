@@ -93,3 +93,24 @@ def test_forced_timeout_ends_the_launch(rr, monkeypatch):
     assert_bitwise(to_host(out, "float32"), C.all_reduce_fold(x, "sum", "float32"), "after the failed launches")
     assert rr.ring_exec_failures() == f1
     torch.cuda.empty_cache()
+
+
+def test_slots_pass_between_streams(rr):
+    """The step flags come in 16 slots per device; a slot whose last launch
+    has completed passes to another stream, so 20 streams used one after the
+    other all get one (each result checked)."""
+    p, n = 4, 65536 + 5
+    x = W.random_inputs(88, p, n, "float32")
+    want = C.all_reduce_ring(x, "sum", "float32")
+    xs = to_dev(x, "float32")
+    streams = [torch.cuda.Stream() for _ in range(20)]
+    assert len({s.cuda_stream for s in streams}) == 20
+    torch.cuda.synchronize()
+    f0 = rr.ring_exec_failures()
+    for i, s in enumerate(streams):
+        with torch.cuda.stream(s):
+            ys = torch.empty_like(xs)
+            rr.all_reduce(xs, ys, algo="ring_persistent")
+            s.synchronize()
+            assert_bitwise(to_host(ys, "float32"), want, f"stream {i}")
+    assert rr.ring_exec_failures() == f0
