@@ -71,16 +71,17 @@ int env_int(const char* name, int dflt) {
 // kernels; 0 = the default), RR_EXEC_TIMEOUT_US (bound of one wait of the persistent ring executor on a
 // neighbour's flag, default 1 s), RR_EXEC_PER_CU (cap on its workgroups per
 // compute unit; 0 = as many as stay resident), RR_EXEC_SLICES (slices per
-// chunk, 1..64; 0 = by chunk size),
+// chunk, 1..64; default 64),
 // RR_LOG (1 = print each launch plan to stderr).  Defaults are the measured
 // best on MI355X: every byte of these collectives is touched once, so
 // nontemporal access (no reuse expected) keeps the caches from holding dead
 // lines, and separating the read and write traffic of the fused folds in time
 // raises their HBM throughput.
-// Slices per chunk of the persistent ring executor (0 = by size): every
-// worker writes its XCD's L2 back once per step, so fewer, larger workers
-// measured faster -- 16 slices at 1 MiB chunks, 32 at 12 MiB chunks.
-constexpr int kExecDefaultSlices = 0;
+// Slices per chunk of the persistent ring executor (at most 64; fewer when
+// the device cannot keep them resident or the chunks are short).  With the
+// workers of a slice on one XCD, more slices measured faster: at 1 MiB
+// chunks 226 / 145 / 102 / 100 us for 8 / 16 / 32 / 64 slices.
+constexpr int kExecDefaultSlices = 64;
 
 struct Tuning {
   int unroll;
@@ -494,8 +495,7 @@ rr_status_t ar_ring_exec(const void* const* send, void* const* recv, int p, uint
   a.p = p;
   a.div = divisor_for(op, p);
   a.vec = vec ? 1 : 0;
-  int slices = t.exec_slices;
-  if (slices <= 0) slices = (a.bound[1] - a.bound[0]) * rr::elem_size(dt) > (4ull << 20) ? 32 : 16;
+  const int slices = t.exec_slices > 0 ? t.exec_slices : kExecDefaultSlices;
   if (t.log) fprintf(stderr, "[rr] all_reduce(ring, persistent): p=%d n=%llu vec=%d\n", p, (unsigned long long)n, a.vec);
   const hipError_t e = rr::launch_ring_exec(a, kind_of(dt), op, t.exec_per_cu, slices, t.exec_timeout_us, s);
   if (e != hipSuccess) return hip_fail(e, "all_reduce(ring, persistent)");

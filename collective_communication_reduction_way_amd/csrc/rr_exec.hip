@@ -31,10 +31,18 @@
 // s, so it also waits for flag[q+1][b] >= s+2.  Every wait points to an
 // earlier step, so the waits form no cycle.
 //
-// Memory ordering.  The flags order data between workgroups on different
-// XCDs, each with its own L2.  To publish a step, every wave waits until its
-// stores are acknowledged by the L2 (s_waitcnt 0), the workgroup meets at a
-// barrier, and thread 0 takes an agent-scope release fence -- on gfx950 an
+// Memory ordering.  The flags order data between workgroups that may run on
+// different XCDs, each with its own L2.  The slices are laid out so that a
+// slice's p workers are workgroups congruent modulo the XCD count, which the
+// dispatcher places on one XCD when it deals workgroups to the XCDs in turn.
+// This is checked, not assumed: at the start each worker publishes the XCD it
+// runs on (tagged with the launch) and reads its slice's p entries.  When they
+// all agree, the slice exchanges data inside one L2, coherent for its CUs: a
+// step is published once every wave's stores are acknowledged by the L2
+// (s_waitcnt 0, barrier) and the flag is raised, and a waiter that sees the
+// flag only invalidates its CU's L1 (buffer_inv sc0).  Otherwise, to publish
+// a step, every wave waits until its stores are acknowledged by the L2
+// (s_waitcnt 0), the workgroup meets at a barrier, and thread 0 takes an agent-scope release fence -- on gfx950 an
 // L2 write-back of the whole XCD's L2 (buffer_wbl2 sc1), which therefore
 // covers every wave's stores -- before it raises the flag.  A waiter's
 // thread 0 sees the flag and takes an agent-scope acquire fence, which
@@ -49,7 +57,8 @@
 // captured launch carries the fixed tag 1 (eager launches use 2, 3, ...)
 // and a reset of the slot's flags and abort word is captured just before it.
 // Without it, a replay would find the previous replay's flags already at
-// their final values and read chunks before they are written.  Every wait
+// their final values and read chunks before they are written.  The reset
+// clears the placement words too.  Every wait
 // is bounded by a wall-clock timeout; a worker that times out (workers not
 // all resident, for instance) raises the slot's abort word, counts the
 // failure and stops, and every other waiter of the launch stops as soon as
@@ -76,9 +85,12 @@ constexpr int kExecMaxWorkers = 2048;  // p * B per launch
 constexpr int kExecStride = 8;         // 64-bit words: one 64-byte line per flag
 constexpr int kExecShift = 24;         // flag = (tag << 24) + steps
 constexpr unsigned long long kExecCapturedTag = 1ull << kExecShift;
+constexpr int kExecXcds = 8;           // XCDs of an MI355X (the placement is checked at run time)
 
 __device__ __align__(256) unsigned long long g_exec_flags[kExecSlots * kExecMaxWorkers * kExecStride];
 __device__ __align__(256) unsigned long long g_exec_abort[kExecSlots * 16];
+// Placement of each worker, published at the start of a launch: tag + XCC id.
+__device__ __align__(256) unsigned long long g_exec_place[kExecSlots * kExecMaxWorkers];
 __device__ unsigned long long g_exec_failures;
 
 __device__ __forceinline__ unsigned long long* exec_flag(uint32_t slot, int worker) {
@@ -88,8 +100,11 @@ __device__ __forceinline__ unsigned long long* exec_flag(uint32_t slot, int work
 // Clear the flags of workers [0, workers) of a slot and its abort word
 // (ahead of a captured launch).
 __global__ __launch_bounds__(kBlock) void k_exec_reset(uint32_t slot, int workers) {
-  for (int w = threadIdx.x; w < workers; w += kBlock)
+  for (int w = threadIdx.x; w < workers; w += kBlock) {
     __hip_atomic_store(exec_flag(slot, w), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(g_exec_place + static_cast<size_t>(slot) * kExecMaxWorkers + w, 0ull, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
   if (threadIdx.x == 0) __hip_atomic_store(g_exec_abort + slot * 16, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -110,6 +125,15 @@ __device__ bool wait_flag(const ExecArgs& a, const unsigned long long* f, unsign
     }
   }
   return true;
+}
+
+// Invalidate this CU's L1 vector cache (and wait for it): after it, loads
+// read the XCD's L2.  The acquire of a slice whose workers all run on one XCD.
+__device__ __forceinline__ void l1_invalidate() { asm volatile("buffer_inv sc0\n\ts_waitcnt vmcnt(0)" ::: "memory"); }
+
+// The XCC (XCD) this wave runs on.
+__device__ __forceinline__ uint32_t xcc_id() {
+  return __builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xFu;  // HW_REG_XCC_ID, bits 0-3
 }
 
 // Apply `f` to the elements [e0, e1) of a slice: whole 8-element units where
@@ -135,13 +159,25 @@ __global__ __launch_bounds__(kBlock) void k_ring_exec(ExecArgs a) {
   using SA = typename EA::S;
   using A = typename E::A;
   const int p = a.p;
-  const int b = blockIdx.x / p;
-  const int q = blockIdx.x - b * p;
+  // worker (slice b, rank q).  With a.xcds > 0 the p workers of a slice are
+  // workgroups congruent mod a.xcds: one XCD each when the dispatcher deals
+  // workgroups to the XCDs in turn (checked below, not assumed).
+  int b, q;
+  if (a.xcds > 0) {
+    const int j = static_cast<int>(blockIdx.x) / a.xcds;
+    const int jb = j / p;
+    b = jb * a.xcds + (static_cast<int>(blockIdx.x) - j * a.xcds);
+    q = j - jb * p;
+  } else {
+    b = blockIdx.x / p;
+    q = blockIdx.x - b * p;
+  }
   const int r = q == 0 ? p - 1 : q - 1;
   const int nx = q + 1 == p ? 0 : q + 1;
   const bool vec = a.vec != 0;
   constexpr bool kSeparate = !__is_same(E, EA);  // working buffers apart from the outputs
   __shared__ int go;
+  __shared__ int local;  // 1: every worker of the slice runs on this XCD
   auto slice_lo = [&](int c) {
     const uint64_t len = a.bound[c + 1] - a.bound[c];
     return a.bound[c] + len * static_cast<uint64_t>(b) / static_cast<uint64_t>(a.nslices);
@@ -151,6 +187,27 @@ __global__ __launch_bounds__(kBlock) void k_ring_exec(ExecArgs a) {
     return a.bound[c] + len * static_cast<uint64_t>(b + 1) / static_cast<uint64_t>(a.nslices);
   };
   SA* wq = static_cast<SA*>(a.work[q]);
+  if (threadIdx.x == 0) {
+    // Placement: publish this worker's XCC, wait for the slice's p workers,
+    // and take the XCD-local protocol only if they all share it.  Every
+    // worker of a slice reads the same p words, so all take the same one.
+    bool ok = true;
+    bool same = a.xcds > 0;
+    if (same) {
+      unsigned long long* pl = g_exec_place + static_cast<size_t>(a.slot) * kExecMaxWorkers;
+      const unsigned long long mine = xcc_id();
+      __hip_atomic_store(pl + b * p + q, a.tag + mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int k = 0; k < p && ok; ++k) {
+        ok = wait_flag(a, pl + b * p + k, a.tag);
+        if (ok && __hip_atomic_load(pl + b * p + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.tag + mine)
+          same = false;
+      }
+    }
+    go = ok ? 1 : 0;
+    local = same ? 1 : 0;
+  }
+  __syncthreads();
+  if (!go) return;
   for (int t = 0; t <= 2 * p - 2; ++t) {
     // wait for the predecessor's step t-1 (and, for an all-gather overwrite
     // of a working buffer, for the successor's read of it)
@@ -159,7 +216,13 @@ __global__ __launch_bounds__(kBlock) void k_ring_exec(ExecArgs a) {
         bool ok = wait_flag(a, exec_flag(a.slot, b * p + r), a.tag + static_cast<unsigned long long>(t));
         if (ok && !kSeparate && t >= p)
           ok = wait_flag(a, exec_flag(a.slot, b * p + nx), a.tag + static_cast<unsigned long long>(t - p + 2));
-        if (ok) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        if (ok) {
+          if (local) {
+            l1_invalidate();
+          } else {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+          }
+        }
         go = ok ? 1 : 0;
       }
       __syncthreads();
@@ -245,7 +308,9 @@ __global__ __launch_bounds__(kBlock) void k_ring_exec(ExecArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      // XCD-local: the stores are in the XCD's L2 (acknowledged above), which
+      // every worker of the slice reads; else write the L2 back for all XCDs
+      if (!local) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       __hip_atomic_fetch_max(exec_flag(a.slot, b * p + q), a.tag + static_cast<unsigned long long>(t + 1),
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -339,6 +404,13 @@ hipError_t exec_go(ExecArgs a, int budget_per_cu_cap, int max_slices, int timeou
   const uint64_t by_size = shortest / (8ull * kBlock) + 1;
   if (static_cast<uint64_t>(slices) > by_size) slices = static_cast<int>(by_size);
   if (slices < 1) slices = 1;
+  // a multiple of the XCD count: the workers of each slice then share an XCD
+  // when workgroups are dealt to the XCDs in turn (checked by the kernel)
+  a.xcds = 0;
+  if (slices >= kExecXcds) {
+    slices -= slices % kExecXcds;
+    a.xcds = kExecXcds;
+  }
   a.nslices = slices;
   const uint64_t khz = d.wall_khz > 0 ? static_cast<uint64_t>(d.wall_khz) : 100000;
   uint64_t ticks = khz * static_cast<uint64_t>(timeout_us) / 1000;

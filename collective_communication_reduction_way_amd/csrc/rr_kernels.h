@@ -203,6 +203,8 @@ struct ExecArgs {
   int32_t vec;   // 1: every buffer 16-byte aligned
   uint32_t slot;
   int32_t captured;  // 1: launched under graph capture (fixed tag, flags reset first)
+  int32_t xcds;      // > 0: workers of a slice are workgroups congruent mod xcds (one XCD each)
+  int32_t pad;
 };
 
 // per_cu_cap > 0 limits the workers per compute unit; max_slices (1..64)
