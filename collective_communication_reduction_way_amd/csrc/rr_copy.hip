@@ -62,6 +62,10 @@ __device__ __forceinline__ void st(T* p, T v) {
   }
 }
 
+// One source to p outputs.  NT: nontemporal loads; the stores are plain in
+// either case (against nontemporal stores, with sources cold in every
+// cache: +2.2 to +2.9 points of the HBM peak for all-gather and broadcast
+// at 8 and 96 MiB per rank).
 template <int B, bool NT>
 __global__ __launch_bounds__(kBlock) void k_fanout(FanoutArgs a) {
   using T = typename UnitT<B>::T;
@@ -84,7 +88,7 @@ __global__ __launch_bounds__(kBlock) void k_fanout(FanoutArgs a) {
 #pragma unroll
       for (int u = 0; u < kCopyU; ++u) {
         const uint64_t i = base + static_cast<uint64_t>(u) * kBlock;
-        if (i < units) st<NT>(dst + i, v[u]);
+        if (i < units) st<false>(dst + i, v[u]);
       }
     }
   }

@@ -38,6 +38,10 @@ uint32_t slot_for(DeviceState& d, hipStream_t s) {
   std::lock_guard<std::mutex> lock(d.mu);
   auto it = d.slot_of.find(s);
   if (it != d.slot_of.end()) return it->second;
+  // a program that keeps making streams must not grow the map without bound;
+  // starting the assignment afresh only makes some streams share counters,
+  // which costs time, never results (the barrier orders no data)
+  if (d.slot_of.size() >= 4096) d.slot_of.clear();
   const uint32_t slot = static_cast<uint32_t>(d.slot_of.size() % kSyncSlots);
   d.slot_of.emplace(s, slot);
   return slot;
