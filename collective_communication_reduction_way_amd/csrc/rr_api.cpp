@@ -72,7 +72,8 @@ int env_int(const char* name, int dflt) {
 // neighbour's flag, default 1 s), RR_EXEC_PER_CU (cap on its workgroups per
 // compute unit; 0 = as many as stay resident), RR_EXEC_SLICES (slices per
 // chunk, 1..64; default 64),
-// RR_LOG (1 = print each launch plan to stderr).  Defaults are the measured
+// RR_COPY_U (16-byte units per lane of the all-gather and broadcast fan-out:
+// 1, 2, 4 or 8; default 4), RR_LOG (1 = print each launch plan to stderr).  Defaults are the measured
 // best on MI355X: every byte of these collectives is touched once, so
 // nontemporal access (no reuse expected) keeps the caches from holding dead
 // lines, and separating the read and write traffic of the fused folds in time
@@ -94,6 +95,7 @@ struct Tuning {
   int exec_timeout_us;
   int exec_per_cu;
   int exec_slices;
+  int copy_u;
 };
 
 Tuning tuning() {
@@ -123,6 +125,7 @@ Tuning tuning() {
   t.exec_per_cu = env_int("RR_EXEC_PER_CU", 0);
   if (t.exec_per_cu < 0) t.exec_per_cu = 0;
   t.exec_slices = env_int("RR_EXEC_SLICES", kExecDefaultSlices);
+  t.copy_u = env_int("RR_COPY_U", 4);
   return t;
 }
 
@@ -748,7 +751,7 @@ rr_status_t rr_all_gather(const void* const* sendbufs, void* const* recvbufs, in
   const Tuning t = tuning();
   const int unit = copy_unit(addrs, {L * esz});
   if (t.log) fprintf(stderr, "[rr] all_gather: p=%d shard_bytes=%llu unit=%d\n", p, (unsigned long long)(L * esz), unit);
-  const hipError_t e = rr::launch_fanout(a, unit, t.nontemporal, t.grid_cap, reinterpret_cast<hipStream_t>(stream));
+  const hipError_t e = rr::launch_fanout(a, unit, t.nontemporal, t.grid_cap, t.copy_u, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "all_gather");
   return ok();
 }
@@ -823,7 +826,7 @@ rr_status_t rr_broadcast(const void* sendbuf, void* const* recvbufs, int root, i
   const Tuning t = tuning();
   const int unit = copy_unit(addrs, {n * esz});
   if (t.log) fprintf(stderr, "[rr] broadcast: %d copies of %llu bytes unit=%d\n", m, (unsigned long long)(n * esz), unit);
-  const hipError_t e = rr::launch_fanout(a, unit, t.nontemporal, t.grid_cap, reinterpret_cast<hipStream_t>(stream));
+  const hipError_t e = rr::launch_fanout(a, unit, t.nontemporal, t.grid_cap, t.copy_u, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "broadcast");
   return ok();
 }

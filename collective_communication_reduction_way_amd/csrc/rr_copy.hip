@@ -66,19 +66,19 @@ __device__ __forceinline__ void st(T* p, T v) {
 // either case (against nontemporal stores, with sources cold in every
 // cache: +2.2 to +2.9 points of the HBM peak for all-gather and broadcast
 // at 8 and 96 MiB per rank).
-template <int B, bool NT>
+template <int B, bool NT, int U = kCopyU>
 __global__ __launch_bounds__(kBlock) void k_fanout(FanoutArgs a) {
   using T = typename UnitT<B>::T;
   const int seg = blockIdx.y;
   const uint64_t units = a.seg_bytes / B;
   const T* src = static_cast<const T*>(a.src[seg]);
   const uint64_t dst_off = static_cast<uint64_t>(seg) * (a.dst_seg_stride / B);
-  constexpr uint64_t kTile = static_cast<uint64_t>(kBlock) * kCopyU;
+  constexpr uint64_t kTile = static_cast<uint64_t>(kBlock) * U;
   for (uint64_t base = static_cast<uint64_t>(blockIdx.x) * kTile + threadIdx.x; base < units;
        base += static_cast<uint64_t>(gridDim.x) * kTile) {
-    T v[kCopyU];
+    T v[U];
 #pragma unroll
-    for (int u = 0; u < kCopyU; ++u) {
+    for (int u = 0; u < U; ++u) {
       const uint64_t i = base + static_cast<uint64_t>(u) * kBlock;
       if (i < units) v[u] = ld<NT>(src + i);
     }
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kBlock) void k_fanout(FanoutArgs a) {
       if (r == seg && ((a.skip_diag >> seg) & 1ull)) continue;
       T* dst = static_cast<T*>(a.dst[r]) + dst_off;
 #pragma unroll
-      for (int u = 0; u < kCopyU; ++u) {
+      for (int u = 0; u < U; ++u) {
         const uint64_t i = base + static_cast<uint64_t>(u) * kBlock;
         if (i < units) st<false>(dst + i, v[u]);
       }
@@ -206,13 +206,30 @@ hipError_t ring_step_kind(const PairArgs& a, rr_op_t op, int grid_cap, hipStream
 
 }  // namespace
 
-hipError_t launch_fanout(const FanoutArgs& a, int unit_bytes, int nontemporal, int grid_cap, hipStream_t s) {
+hipError_t launch_fanout(const FanoutArgs& a, int unit_bytes, int nontemporal, int grid_cap, int units_per_lane,
+                         hipStream_t s) {
   const uint64_t units = a.seg_bytes / static_cast<uint64_t>(unit_bytes);
+  const bool nt = nontemporal != 0;
+  if (unit_bytes == 16) {
+    // 16-byte units: `units_per_lane` (1, 2, 4 or 8) per lane, and without a
+    // cap one tile per workgroup.  A grid that strides leaves some
+    // workgroups one tile more than others at the end of the launch; at 96
+    // MiB per rank (768 tiles of 4 units per lane per shard) one tile each
+    // measured 64.0% -> 68.3% of the HBM peak for all-gather and 64.3% ->
+    // 67.9% for broadcast against 8192 striding workgroups of 2 units per
+    // lane; 8 MiB per rank is within noise (68.3-69.3%) for every choice.
+    const int u = (units_per_lane == 1 || units_per_lane == 2 || units_per_lane == 8) ? units_per_lane : 4;
+    const uint64_t bx = blocks_for(units, static_cast<uint64_t>(kBlock) * u, a.nseg, grid_cap);
+    switch (u) {
+      case 1: return nt ? go(&k_fanout<16, true, 1>, a, bx, a.nseg, s) : go(&k_fanout<16, false, 1>, a, bx, a.nseg, s);
+      case 2: return nt ? go(&k_fanout<16, true, 2>, a, bx, a.nseg, s) : go(&k_fanout<16, false, 2>, a, bx, a.nseg, s);
+      case 8: return nt ? go(&k_fanout<16, true, 8>, a, bx, a.nseg, s) : go(&k_fanout<16, false, 8>, a, bx, a.nseg, s);
+      default: return nt ? go(&k_fanout<16, true, 4>, a, bx, a.nseg, s) : go(&k_fanout<16, false, 4>, a, bx, a.nseg, s);
+    }
+  }
   const uint64_t bx =
       blocks_for(units, static_cast<uint64_t>(kBlock) * kCopyU, a.nseg, grid_cap > 0 ? grid_cap : kCopyGrid);
-  const bool nt = nontemporal != 0;
   switch (unit_bytes) {
-    case 16: return nt ? go(&k_fanout<16, true>, a, bx, a.nseg, s) : go(&k_fanout<16, false>, a, bx, a.nseg, s);
     case 4: return nt ? go(&k_fanout<4, true>, a, bx, a.nseg, s) : go(&k_fanout<4, false>, a, bx, a.nseg, s);
     case 2: return nt ? go(&k_fanout<2, true>, a, bx, a.nseg, s) : go(&k_fanout<2, false>, a, bx, a.nseg, s);
     case 1: return nt ? go(&k_fanout<1, true>, a, bx, a.nseg, s) : go(&k_fanout<1, false>, a, bx, a.nseg, s);

@@ -360,6 +360,25 @@ def test_sweep_reduce_scatter_all_gather(rr, p, L, dtype):
         assert_bitwise(rows(ar, dtype), rows(full, dtype), "all_reduce == all_gather(reduce_scatter)")
 
 
+@pytest.mark.parametrize("env", [{}, {"RR_COPY_U": "1"}, {"RR_COPY_U": "2"}, {"RR_COPY_U": "8"},
+                                 {"RR_GRID_CAP": "37"}, {"RR_COPY_U": "2", "RR_GRID_CAP": "8192"}])
+def test_fanout_tilings_agree(rr, monkeypatch, env):
+    """All-gather and broadcast through every tile depth of the fan-out
+    kernel, one tile per workgroup or a capped grid that strides over the
+    tiles (a shard that is not a whole number of tiles): the oracle's bits."""
+    p, L = 8, 3 * 4096 + 5 * 4 + 4  # float32 shards of 3 tiles of 4096 plus a partial one
+    x = W.random_inputs(14, p, p * L, "float32")
+    sh = C.reduce_scatter_ring(x, "sum", "float32")
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    full = torch.empty((p, p * L), dtype=torch.float32, device="cuda")
+    rr.all_gather(to_dev(sh, "float32"), full)
+    assert_bitwise(rows(full, "float32"), C.all_gather(sh), f"all_gather {env}")
+    out = torch.empty((p, p * L), dtype=torch.float32, device="cuda")
+    rr.broadcast(to_dev(x[5], "float32"), out, root=5)
+    assert_bitwise(rows(out, "float32"), C.broadcast(x[5], p), f"broadcast {env}")
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_unaligned_buffers_take_the_scalar_path(rr, dtype):
     """Rank buffers offset by one element (not 16-byte aligned) give the same
