@@ -115,6 +115,7 @@ struct PhaseTuning {
   int unroll;
   int timeout_us;
   int static_p;  // 1 = the kernels compiled for p = 8 serve p = 8, 0 = the run-time loop, -1 = by mode
+  int strips;    // tiles per run of interleaved tiles (PhaseArgs::strips); 1 = contiguous tiles, 0 = by mode
 };
 
 // Bucketed all-reduce (rr_multi.hip): the tensors of a bucket are folded as

@@ -48,6 +48,12 @@ struct PhaseArgs {
   unsigned long long tag;  // launch tag << kLaunchShift
   int32_t segments;
   int32_t captured;  // 1: launched under graph capture (tag = kCapturedTag; reset first)
+  // Interleaved tiles (uniform tilings only): the first strip_tiles tiles of
+  // every segment form runs of `strips` tiles whose strips (kBlock groups
+  // each) interleave: tile j of a run takes strips j, j + strips, ...  The
+  // other tiles, and every tile when strips <= 1, are contiguous.
+  uint32_t strips;
+  uint32_t strip_tiles;
 };
 
 // Fill `y` for a launch with a barrier on stream s (any translation unit:

@@ -63,12 +63,15 @@ __device__ __forceinline__ void soft_barrier(const PhaseArgs& a, uint32_t round)
 // lanes past the end re-read the tile's last group instead of branching
 // around the load, so that one code path serves every tile; their values are
 // never stored.
+//
+// `gap`: groups between the end of one strip of kBlock groups and the start
+// of the next (0 for a contiguous tile; only whole tiles interleave).
 template <class E, int V, int U>
-__device__ __forceinline__ void load_tile(Raw<E, V> (&x)[U], const char* base, uint32_t valid) {
+__device__ __forceinline__ void load_tile(Raw<E, V> (&x)[U], const char* base, uint32_t valid, uint32_t gap) {
   const uint32_t lane = threadIdx.x;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const uint32_t g = min(lane + u * kBlock, valid - 1);
+    const uint32_t g = min(lane + u * kBlock, valid - 1) + u * gap;
     load_group<true>(x[u], reinterpret_cast<const typename E::S*>(base + g * 16u));
   }
 }
@@ -81,7 +84,7 @@ __device__ __forceinline__ void load_tile(Raw<E, V> (&x)[U], const char* base, u
 // folded.
 template <class E, class OP, int P, int U, FoldMode M>
 __device__ __forceinline__ void read_fold(const FoldArgs& f, int seg, int p, uint64_t in_off, uint32_t valid,
-                                          typename E::A (&acc)[U][16 / sizeof(typename E::S)]) {
+                                          uint32_t gap, typename E::A (&acc)[U][16 / sizeof(typename E::S)]) {
   constexpr int V = 16 / sizeof(typename E::S);
   using A = typename E::A;
   A tot[U][V];
@@ -91,7 +94,7 @@ __device__ __forceinline__ void read_fold(const FoldArgs& f, int seg, int p, uin
     for (int k = 0; k < P; ++k) src[k] = static_cast<const char*>(f.in[fold_src<M>(k, seg, P, f.group)]) + in_off;
     {
       Raw<E, V> x[U];
-      load_tile(x, src[0], valid);
+      load_tile(x, src[0], valid, gap);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         unpack(x[u], acc[u]);
@@ -102,7 +105,7 @@ __device__ __forceinline__ void read_fold(const FoldArgs& f, int seg, int p, uin
 #pragma unroll
     for (int k = 1; k < P; ++k) {
       Raw<E, V> x[U];
-      load_tile(x, src[k], valid);
+      load_tile(x, src[k], valid, gap);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         A v[V];
@@ -114,8 +117,8 @@ __device__ __forceinline__ void read_fold(const FoldArgs& f, int seg, int p, uin
   } else {
     Raw<E, V> cur[U];
     Raw<E, V> nxt[U];
-    load_tile(cur, static_cast<const char*>(f.in[fold_src<M>(0, seg, p, f.group)]) + in_off, valid);
-    if (p > 1) load_tile(nxt, static_cast<const char*>(f.in[fold_src<M>(1, seg, p, f.group)]) + in_off, valid);
+    load_tile(cur, static_cast<const char*>(f.in[fold_src<M>(0, seg, p, f.group)]) + in_off, valid, gap);
+    if (p > 1) load_tile(nxt, static_cast<const char*>(f.in[fold_src<M>(1, seg, p, f.group)]) + in_off, valid, gap);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       unpack(cur[u], acc[u]);
@@ -127,7 +130,7 @@ __device__ __forceinline__ void read_fold(const FoldArgs& f, int seg, int p, uin
 #pragma unroll
       for (int u = 0; u < U; ++u) cur[u] = nxt[u];
       if (k + 1 < p)
-        load_tile(nxt, static_cast<const char*>(f.in[fold_src<M>(k + 1, seg, p, f.group)]) + in_off, valid);
+        load_tile(nxt, static_cast<const char*>(f.in[fold_src<M>(k + 1, seg, p, f.group)]) + in_off, valid, gap);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         A x[V];
@@ -145,12 +148,12 @@ __device__ __forceinline__ void read_fold(const FoldArgs& f, int seg, int p, uin
 }
 
 template <bool GUARD, class E, int V, int U>
-__device__ __forceinline__ void store_tile(char* base, const Raw<E, V> (&o)[U], uint32_t valid) {
+__device__ __forceinline__ void store_tile(char* base, const Raw<E, V> (&o)[U], uint32_t valid, uint32_t gap) {
   const uint32_t lane = threadIdx.x;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint32_t g = lane + u * kBlock;
-    if (!GUARD || g < valid) store_group<true>(reinterpret_cast<typename E::S*>(base + g * 16u), o[u]);
+    if (!GUARD || g < valid) store_group<true>(reinterpret_cast<typename E::S*>(base + (g + u * gap) * 16u), o[u]);
   }
 }
 
@@ -187,6 +190,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(phase_wa
     uint32_t valid = 0;
     uint64_t off = 0;  // byte offset of the tile's first group in an input buffer
     uint64_t lo = 0;
+    uint32_t gap = 0;  // groups between a tile's strips (interleaved tiles)
     A acc[U][V];
     if (live) {
       uint32_t k;
@@ -201,9 +205,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(phase_wa
         valid = (k + 1 == a.seg_tile[seg + 1] - a.seg_tile[seg]) ? a.seg_last[seg] : kTile;
         if constexpr (uses_bounds(M)) lo = a.f.bound[seg];
       }
-      const uint64_t g0 = (lo + V - 1) / V + static_cast<uint64_t>(k) * kTile;
+      uint64_t gk = static_cast<uint64_t>(k) * kTile;  // the tile's first group in the segment
+      if (a.strips > 1 && k < a.strip_tiles) {
+        const uint32_t run = k / a.strips;
+        const uint32_t j = k - run * a.strips;
+        gk = static_cast<uint64_t>(run) * a.strips * kTile + j * kBlock;
+        gap = (a.strips - 1) * kBlock;
+      }
+      const uint64_t g0 = (lo + V - 1) / V + gk;
       off = g0 * 16;
-      read_fold<E, OP, P, U, M>(a.f, seg, p, off, valid, acc);
+      read_fold<E, OP, P, U, M>(a.f, seg, p, off, valid, gap, acc);
     }
     if constexpr (SYNC) soft_barrier(a, r);
     if (live) {
@@ -218,24 +229,24 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(phase_wa
           for (int q = 0; q < P; ++q) dst[q] = static_cast<char*>(a.f.out[q]) + off;
           if (valid == kTile) {
 #pragma unroll
-            for (int q = 0; q < P; ++q) store_tile<false>(dst[q], o, valid);
+            for (int q = 0; q < P; ++q) store_tile<false>(dst[q], o, valid, gap);
           } else {
 #pragma unroll
-            for (int q = 0; q < P; ++q) store_tile<true>(dst[q], o, valid);
+            for (int q = 0; q < P; ++q) store_tile<true>(dst[q], o, valid, gap);
           }
         } else if (valid == kTile) {
-          for (int q = 0; q < p; ++q) store_tile<false>(static_cast<char*>(a.f.out[q]) + off, o, valid);
+          for (int q = 0; q < p; ++q) store_tile<false>(static_cast<char*>(a.f.out[q]) + off, o, valid, gap);
         } else {
-          for (int q = 0; q < p; ++q) store_tile<true>(static_cast<char*>(a.f.out[q]) + off, o, valid);
+          for (int q = 0; q < p; ++q) store_tile<true>(static_cast<char*>(a.f.out[q]) + off, o, valid, gap);
         }
       } else {
         // reduce-scatter outputs hold only the chunk: group g sits at g*V - lo
         const uint64_t shift = (M == FoldMode::kRingShard) ? lo * sizeof(S) : 0;
         char* d = static_cast<char*>(a.f.out[seg]) + (off - shift);
         if (valid == kTile) {
-          store_tile<false>(d, o, valid);
+          store_tile<false>(d, o, valid, gap);
         } else {
-          store_tile<true>(d, o, valid);
+          store_tile<true>(d, o, valid, gap);
         }
       }
     }

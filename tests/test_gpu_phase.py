@@ -171,3 +171,48 @@ def test_small_reduce_scatter_and_reduce_tiles(rr, p, n, dtype):
         red = torch.empty(n, dtype=xs.dtype, device="cuda")
         rr.reduce(xs, red, root=0, op=op)
         assert_bitwise(to_host(red, dtype), C.reduce(x, op, dtype), f"reduce {op}")
+
+
+# Interleaved tiles (runs of S tiles whose 256-group strips interleave) on
+# uniform tilings with a partial last tile in every segment, in one round and
+# in several: (collective, dtype, op, group, p, n).
+STRIPED = [
+    ("ring", "float32", "sum", 0, 8, 8 * 600012),
+    ("ring", "int32", "max", 0, 8, 8 * 600012),
+    ("ring", "bfloat16", "sum", 0, 8, 8 * 163864),
+    ("ring", "float16", "sum", 0, 8, 8 * 163864),
+    ("ring", "float32", "min", 0, 6, 6 * 900004),
+    ("hier", "float32", "sum", 4, 8, 8 * 600012),
+    ("hier", "bfloat16", "sum", 2, 8, 8 * 163864),
+    ("reduce_scatter", "float32", "sum", 0, 8, 8 * 600012),
+    ("reduce", "bfloat16", "sum", 0, 8, 8 * 600016),
+]
+
+
+@pytest.mark.parametrize("strips", ("0", "1", "3", "8"))
+@pytest.mark.parametrize("coll,dtype,op,group,p,n", STRIPED)
+def test_interleaved_tiles(rr, monkeypatch, strips, coll, dtype, op, group, p, n):
+    """Every tile layout of the phased fold (the schedule's default, forced
+    contiguous, runs of 3 and of 8 interleaved tiles) gives the oracle's
+    bits; no barrier waits out its bound."""
+    kind = "full" if dtype == "int32" else ("fp16_patterns" if dtype == "float16" else "normal")
+    x = W.random_inputs(69, p, n, dtype, kind=kind)
+    monkeypatch.setenv("RR_PHASE_STRIPS", strips)
+    t0 = rr.barrier_timeouts()
+    what = f"{coll} {dtype} {op} p={p} n={n} strips={strips}"
+    if coll == "ring":
+        assert_bitwise(run_ar(rr, x, dtype, op, "ring"), C.all_reduce_fold(x, op, dtype), what)
+    elif coll == "hier":
+        assert_bitwise(run_ar(rr, x, dtype, op, "hier", group), C.all_reduce_hier(x, op, dtype, group), what)
+    elif coll == "reduce_scatter":
+        xs = to_dev(x, dtype)
+        sh = torch.empty((p, n // p), dtype=xs.dtype, device="cuda")
+        rr.reduce_scatter(xs, sh, op=op)
+        assert_bitwise(to_host(sh, dtype), C.reduce_scatter_ring(x, op, dtype), what)
+    else:
+        xs = to_dev(x, dtype)
+        red = torch.empty(n, dtype=xs.dtype, device="cuda")
+        rr.reduce(xs, red, op=op, root=2)
+        assert_bitwise(to_host(red, dtype), C.reduce(x, op, dtype), what)
+    assert rr.barrier_timeouts() == t0
+    torch.cuda.empty_cache()
