@@ -285,25 +285,18 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
   }
   // Interleaved tiles: whole runs of `strips` full tiles at the start of
   // every segment (uniform tilings only).  Measured with the bench on one
-  // MI355X, each figure against contiguous tiles on the same box: the
-  // folds that write every rank gain when a launch has several rounds
-  // (96 MiB float32 all-reduce 72.8% -> 75.4% of the HBM peak with runs of
-  // 8; 128 MiB bfloat16 74.0% -> 76.8% with runs of 4), and for 16-bit
-  // types in one round (hierarchical bfloat16 8 MiB 72.5% -> 73.4%); the
-  // 8 MiB float32 all-reduce loses 3 points with runs of 4 and keeps
-  // contiguous tiles, and reduce-scatter and reduce gained nothing.
+  // MI355X, each figure against the kernels without interleaving on the
+  // same box: the folds that write every rank gain when a launch has
+  // several rounds (96 MiB float32 all-reduce 72.8% -> 75.6% of the HBM
+  // peak with runs of 8; 128 MiB bfloat16 74.5% -> 77.1% with runs of 4).
+  // One-round launches (8 MiB per rank) lost with it, and reduce-scatter
+  // and reduce gained nothing.
+  // Only the kernels of these modes compiled with the barrier can
+  // interleave (can_interleave in rr_phase_impl.h).
+  const bool interleaves = (ring || is_hier(f.mode)) && sync;
   int strips = pt.strips;
-  if (strips == 0) {
-    strips = 1;
-    if (ring || is_hier(f.mode)) {
-      if (a.rounds > 1) {
-        strips = (ring && !is_half(f.in_kind)) ? 8 : 4;
-      } else if (is_half(f.in_kind)) {
-        strips = 4;
-      }
-    }
-  }
-  if (strips > 1 && a.uniform_tiles != 0) {
+  if (strips == 0) strips = (ring && !is_half(f.in_kind)) ? 8 : 4;
+  if (strips > 1 && interleaves && a.uniform_tiles != 0) {
     const uint32_t tile = static_cast<uint32_t>(kBlock * unroll);
     const uint32_t full = a.uniform_last == tile ? a.uniform_tiles : a.uniform_tiles - 1;
     a.strips = static_cast<uint32_t>(strips);

@@ -64,14 +64,17 @@ __device__ __forceinline__ void soft_barrier(const PhaseArgs& a, uint32_t round)
 // around the load, so that one code path serves every tile; their values are
 // never stored.
 //
-// `gap`: groups between the end of one strip of kBlock groups and the start
-// of the next (0 for a contiguous tile; only whole tiles interleave).
-template <class E, int V, int U>
+// IL (kernels that can interleave their tiles): `gap` groups lie between the
+// end of one strip of kBlock groups and the start of the next (0 for a
+// contiguous tile; only whole tiles interleave).  Without IL the gap is not
+// part of the code at all.
+template <bool IL, class E, int V, int U>
 __device__ __forceinline__ void load_tile(Raw<E, V> (&x)[U], const char* base, uint32_t valid, uint32_t gap) {
   const uint32_t lane = threadIdx.x;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const uint32_t g = min(lane + u * kBlock, valid - 1) + u * gap;
+    uint32_t g = min(lane + u * kBlock, valid - 1);
+    if constexpr (IL) g += u * gap;
     load_group<true>(x[u], reinterpret_cast<const typename E::S*>(base + g * 16u));
   }
 }
@@ -82,7 +85,7 @@ __device__ __forceinline__ void load_tile(Raw<E, V> (&x)[U], const char* base, u
 // interleaving of loads and folds to the scheduler.  P == 0: a run-time loop
 // that keeps the next rank's loads in flight while the current rank is
 // folded.
-template <class E, class OP, int P, int U, FoldMode M>
+template <class E, class OP, int P, int U, FoldMode M, bool IL>
 __device__ __forceinline__ void read_fold(const FoldArgs& f, int seg, int p, uint64_t in_off, uint32_t valid,
                                           uint32_t gap, typename E::A (&acc)[U][16 / sizeof(typename E::S)]) {
   constexpr int V = 16 / sizeof(typename E::S);
@@ -94,7 +97,7 @@ __device__ __forceinline__ void read_fold(const FoldArgs& f, int seg, int p, uin
     for (int k = 0; k < P; ++k) src[k] = static_cast<const char*>(f.in[fold_src<M>(k, seg, P, f.group)]) + in_off;
     {
       Raw<E, V> x[U];
-      load_tile(x, src[0], valid, gap);
+      load_tile<IL>(x, src[0], valid, gap);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         unpack(x[u], acc[u]);
@@ -105,7 +108,7 @@ __device__ __forceinline__ void read_fold(const FoldArgs& f, int seg, int p, uin
 #pragma unroll
     for (int k = 1; k < P; ++k) {
       Raw<E, V> x[U];
-      load_tile(x, src[k], valid, gap);
+      load_tile<IL>(x, src[k], valid, gap);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         A v[V];
@@ -117,8 +120,8 @@ __device__ __forceinline__ void read_fold(const FoldArgs& f, int seg, int p, uin
   } else {
     Raw<E, V> cur[U];
     Raw<E, V> nxt[U];
-    load_tile(cur, static_cast<const char*>(f.in[fold_src<M>(0, seg, p, f.group)]) + in_off, valid, gap);
-    if (p > 1) load_tile(nxt, static_cast<const char*>(f.in[fold_src<M>(1, seg, p, f.group)]) + in_off, valid, gap);
+    load_tile<IL>(cur, static_cast<const char*>(f.in[fold_src<M>(0, seg, p, f.group)]) + in_off, valid, gap);
+    if (p > 1) load_tile<IL>(nxt, static_cast<const char*>(f.in[fold_src<M>(1, seg, p, f.group)]) + in_off, valid, gap);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       unpack(cur[u], acc[u]);
@@ -130,7 +133,7 @@ __device__ __forceinline__ void read_fold(const FoldArgs& f, int seg, int p, uin
 #pragma unroll
       for (int u = 0; u < U; ++u) cur[u] = nxt[u];
       if (k + 1 < p)
-        load_tile(nxt, static_cast<const char*>(f.in[fold_src<M>(k + 1, seg, p, f.group)]) + in_off, valid, gap);
+        load_tile<IL>(nxt, static_cast<const char*>(f.in[fold_src<M>(k + 1, seg, p, f.group)]) + in_off, valid, gap);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         A x[V];
@@ -147,13 +150,17 @@ __device__ __forceinline__ void read_fold(const FoldArgs& f, int seg, int p, uin
     for (int j = 0; j < V; ++j) acc[u][j] = fold_finish<E, OP, M>(acc[u][j], tot[u][j], pp, f.group, f.div);
 }
 
-template <bool GUARD, class E, int V, int U>
+template <bool GUARD, bool IL, class E, int V, int U>
 __device__ __forceinline__ void store_tile(char* base, const Raw<E, V> (&o)[U], uint32_t valid, uint32_t gap) {
   const uint32_t lane = threadIdx.x;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint32_t g = lane + u * kBlock;
-    if (!GUARD || g < valid) store_group<true>(reinterpret_cast<typename E::S*>(base + (g + u * gap) * 16u), o[u]);
+    if constexpr (IL) {
+      if (!GUARD || g < valid) store_group<true>(reinterpret_cast<typename E::S*>(base + (g + u * gap) * 16u), o[u]);
+    } else {
+      if (!GUARD || g < valid) store_group<true>(reinterpret_cast<typename E::S*>(base + g * 16u), o[u]);
+    }
   }
 }
 
@@ -171,6 +178,17 @@ constexpr int phase_waves() {
   return 1;
 }
 
+// Kernels that can lay their tiles out interleaved (PhaseArgs::strips): the
+// folds that write every rank, with the barrier (several rounds).  The
+// others are compiled without that arithmetic: in the one-round float32
+// all-reduce its mere presence, with the layout switched off, cost about 3
+// points of the HBM peak, and the one-round bfloat16 hierarchy lost 2.3
+// points with it switched on.
+template <class E, FoldMode M, bool SYNC>
+constexpr bool can_interleave() {
+  return writes_all(M) && SYNC;
+}
+
 // SYNC: the soft barrier between the phases of a round is compiled in.  The
 // kernel without it is a separate instantiation: barrier code that is
 // present but skipped still costs several percent of throughput (it
@@ -181,6 +199,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(phase_wa
   using A = typename E::A;
   constexpr int V = 16 / sizeof(S);
   constexpr uint32_t kTile = kBlock * U;
+  constexpr bool IL = can_interleave<E, M, SYNC>();
   const int p = P > 0 ? P : a.f.p;
   if constexpr (SYNC) sync_claim(a);
   for (uint32_t r = 0; r < a.rounds; ++r) {
@@ -205,16 +224,20 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(phase_wa
         valid = (k + 1 == a.seg_tile[seg + 1] - a.seg_tile[seg]) ? a.seg_last[seg] : kTile;
         if constexpr (uses_bounds(M)) lo = a.f.bound[seg];
       }
-      uint64_t gk = static_cast<uint64_t>(k) * kTile;  // the tile's first group in the segment
-      if (a.strips > 1 && k < a.strip_tiles) {
-        const uint32_t run = k / a.strips;
-        const uint32_t j = k - run * a.strips;
-        gk = static_cast<uint64_t>(run) * a.strips * kTile + j * kBlock;
-        gap = (a.strips - 1) * kBlock;
+      if constexpr (IL) {
+        uint64_t gk = static_cast<uint64_t>(k) * kTile;  // the tile's first group in the segment
+        if (a.strips > 1 && k < a.strip_tiles) {
+          const uint32_t run = k / a.strips;
+          const uint32_t j = k - run * a.strips;
+          gk = static_cast<uint64_t>(run) * a.strips * kTile + j * kBlock;
+          gap = (a.strips - 1) * kBlock;
+        }
+        off = ((lo + V - 1) / V + gk) * 16;
+      } else {
+        const uint64_t g0 = (lo + V - 1) / V + static_cast<uint64_t>(k) * kTile;
+        off = g0 * 16;
       }
-      const uint64_t g0 = (lo + V - 1) / V + gk;
-      off = g0 * 16;
-      read_fold<E, OP, P, U, M>(a.f, seg, p, off, valid, gap, acc);
+      read_fold<E, OP, P, U, M, IL>(a.f, seg, p, off, valid, gap, acc);
     }
     if constexpr (SYNC) soft_barrier(a, r);
     if (live) {
@@ -229,24 +252,24 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(phase_wa
           for (int q = 0; q < P; ++q) dst[q] = static_cast<char*>(a.f.out[q]) + off;
           if (valid == kTile) {
 #pragma unroll
-            for (int q = 0; q < P; ++q) store_tile<false>(dst[q], o, valid, gap);
+            for (int q = 0; q < P; ++q) store_tile<false, IL>(dst[q], o, valid, gap);
           } else {
 #pragma unroll
-            for (int q = 0; q < P; ++q) store_tile<true>(dst[q], o, valid, gap);
+            for (int q = 0; q < P; ++q) store_tile<true, IL>(dst[q], o, valid, gap);
           }
         } else if (valid == kTile) {
-          for (int q = 0; q < p; ++q) store_tile<false>(static_cast<char*>(a.f.out[q]) + off, o, valid, gap);
+          for (int q = 0; q < p; ++q) store_tile<false, IL>(static_cast<char*>(a.f.out[q]) + off, o, valid, gap);
         } else {
-          for (int q = 0; q < p; ++q) store_tile<true>(static_cast<char*>(a.f.out[q]) + off, o, valid, gap);
+          for (int q = 0; q < p; ++q) store_tile<true, IL>(static_cast<char*>(a.f.out[q]) + off, o, valid, gap);
         }
       } else {
         // reduce-scatter outputs hold only the chunk: group g sits at g*V - lo
         const uint64_t shift = (M == FoldMode::kRingShard) ? lo * sizeof(S) : 0;
         char* d = static_cast<char*>(a.f.out[seg]) + (off - shift);
         if (valid == kTile) {
-          store_tile<false>(d, o, valid, gap);
+          store_tile<false, IL>(d, o, valid, gap);
         } else {
-          store_tile<true>(d, o, valid, gap);
+          store_tile<true, IL>(d, o, valid, gap);
         }
       }
     }
