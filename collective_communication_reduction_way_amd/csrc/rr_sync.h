@@ -70,7 +70,10 @@ __device__ __forceinline__ void soft_barrier_at(uint32_t slot, unsigned long lon
     unsigned long long* top = sync_counter(slot, kSyncSubs);
     const unsigned long long seen = atomic_add_relaxed(sync_counter(slot, sub), 1ull) + 1 - tag;
     if (seen == static_cast<unsigned long long>(round + 1) * per) {
-      atomic_max_relaxed(top, tag);
+      // the top counter is claimed for the launch by the first completion of
+      // every sub-counter (round 0); later rounds find it claimed, and the
+      // claim would only add a serial atomic to the barrier's critical path
+      if (round == 0) atomic_max_relaxed(top, tag);
       atomic_add_relaxed(top, 1ull);
     }
     const unsigned long long target = tag + static_cast<unsigned long long>(round + 1) * nsub;
