@@ -962,6 +962,7 @@ rr_status_t rr_all_reduce_bucket(const void* const* sendbufs, void* const* recvb
     memset(&a, 0, sizeof(a));
     a.p = p;
     a.div = divisor_for(op, p);
+    a.strips = static_cast<uint32_t>(t.pt.strips);  // 0: by the round count (rr_multi.hip)
     batch_tensor = -1;
     nslots = 0;
   };

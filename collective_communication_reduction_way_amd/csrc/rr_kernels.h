@@ -152,6 +152,10 @@ struct BucketArgs {
   uint32_t tiles;
   uint32_t rounds;  // tiles / grid, rounded up
   SyncArgs sync;    // the soft barrier between the read and write phases (multi-round launches)
+  // Multi-round launches: runs of `strips` whole tiles of a vector piece
+  // whose kBlock-unit strips interleave (tile j of a run takes strips j,
+  // j + strips, ...); 0 or 1 = contiguous tiles.
+  uint32_t strips;
 };
 
 // Units per lane and tile of the bucket kernel: a tile is kBlock*kBucketU

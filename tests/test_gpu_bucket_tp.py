@@ -145,6 +145,26 @@ def test_bucket_barrier(rr, monkeypatch):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("strips", ("1", "2", "3", "8"))
+def test_bucket_interleaved_tiles(rr, monkeypatch, strips):
+    """A multi-round bucket whose vector pieces hold whole tiles taken in runs
+    of interleaved tiles (1 = contiguous), with ragged and unaligned tensors
+    beside them: the oracle's bits for sum and max, and no wait runs out."""
+    p = 8
+    sizes = [3 * (1 << 20) + 5, 1 << 22, 777, 9 * 4096 + 8, (1 << 21) + 4]
+    parts = [W.random_inputs(91 + i, p, n, "float32") for i, n in enumerate(sizes)]
+    monkeypatch.setenv("RR_PHASE_STRIPS", strips)
+    t0 = rr.barrier_timeouts()
+    for op in ("sum", "max"):
+        check_bucket(run_bucket(rr, parts, "float32", op), C.all_reduce_bucket(parts, op, "float32"),
+                     f"{op} strips={strips}")
+    bparts = [W.random_inputs(95 + i, p, n, "bfloat16") for i, n in enumerate((1 << 23, 4099))]
+    check_bucket(run_bucket(rr, bparts, "bfloat16", "avg"), C.all_reduce_bucket(bparts, "avg", "bfloat16"),
+                 f"bf16 avg strips={strips}")
+    assert rr.barrier_timeouts() == t0
+    torch.cuda.empty_cache()
+
+
 def test_bucket_empty_and_rejected(rr):
     assert rr.all_reduce_bucket([]) == []
     a = torch.ones((4, 64), dtype=torch.int32, device="cuda")
