@@ -37,6 +37,13 @@
 // counters; if two ever share one, barriers pass early or time out, and the
 // results are unaffected.
 //
+// Interleaved tiles.  In the launches with the barrier (several rounds) the
+// whole tiles of a segment are taken in runs of PhaseArgs::strips tiles
+// whose strips of kBlock groups interleave: tile j of a run holds strips j,
+// j + strips, j + 2*strips, ... of the run, so that neighbouring workgroups
+// share one region of memory instead of each owning U contiguous strips.
+// That layout is compiled only into those kernels (can_interleave below).
+//
 // Used for the folds that write every rank (ring and hierarchical
 // all-reduce), whose traffic is half reads and half writes, and for
 // reduce-scatter and reduce, which write one output per p inputs.
