@@ -43,6 +43,8 @@ struct UnitT<1> {
 // with about 8192 workgroups striding over the tiles.
 constexpr int kCopyU = 2;
 constexpr int kCopyGrid = 8192;
+// Fan-out launches that write at most this many bytes use nontemporal stores.
+constexpr uint64_t kFanoutNtStoreBytes = 128ull << 20;
 
 template <bool NT, class T>
 __device__ __forceinline__ T ld(const T* p) {
@@ -62,11 +64,9 @@ __device__ __forceinline__ void st(T* p, T v) {
   }
 }
 
-// One source to p outputs.  NT: nontemporal loads; the stores are plain in
-// either case (against nontemporal stores, with sources cold in every
-// cache: +2.2 to +2.9 points of the HBM peak for all-gather and broadcast
-// at 8 and 96 MiB per rank).
-template <int B, bool NT, int U = kCopyU>
+// One source to p outputs.  NT: nontemporal loads; NTS: nontemporal stores
+// (chosen by the bytes a launch writes, see launch_fanout).
+template <int B, bool NT, int U = kCopyU, bool NTS = false>
 __global__ __launch_bounds__(kBlock) void k_fanout(FanoutArgs a) {
   using T = typename UnitT<B>::T;
   const int seg = blockIdx.y;
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kBlock) void k_fanout(FanoutArgs a) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint64_t i = base + static_cast<uint64_t>(u) * kBlock;
-        if (i < units) st<false>(dst + i, v[u]);
+        if (i < units) st<NTS>(dst + i, v[u]);
       }
     }
   }
@@ -218,8 +218,25 @@ hipError_t launch_fanout(const FanoutArgs& a, int unit_bytes, int nontemporal, i
     // measured 64.0% -> 68.3% of the HBM peak for all-gather and 64.3% ->
     // 67.9% for broadcast against 8192 striding workgroups of 2 units per
     // lane; 8 MiB per rank is within noise (68.3-69.3%) for every choice.
+    //
+    // Stores: nontemporal while the launch writes at most kFanoutNtStoreBytes
+    // (half the 256 MB Infinity Cache), plain above.  Sweep with cold
+    // sources, all-gather and broadcast alike, plain -> nontemporal: 4 / 8 /
+    // 16 MiB per rank (32-128 MiB written) 55.5 -> 65.0%, 67.9 -> 72.1%,
+    // 66.7 -> 69.4% of the HBM peak; 24 / 32 / 48 / 64 / 96 MiB per rank
+    // 68.4 -> 67.0%, 66.5 -> 65.5%, 67.6 -> 64.4%, 66.7 -> 63.5%,
+    // 67.8 -> 63.5%.
     const int u = (units_per_lane == 1 || units_per_lane == 2 || units_per_lane == 8) ? units_per_lane : 4;
     const uint64_t bx = blocks_for(units, static_cast<uint64_t>(kBlock) * u, a.nseg, grid_cap);
+    const uint64_t written = a.seg_bytes * static_cast<uint64_t>(a.nseg) * static_cast<uint64_t>(a.ndst);
+    if (nt && written <= kFanoutNtStoreBytes) {
+      switch (u) {
+        case 1: return go(&k_fanout<16, true, 1, true>, a, bx, a.nseg, s);
+        case 2: return go(&k_fanout<16, true, 2, true>, a, bx, a.nseg, s);
+        case 8: return go(&k_fanout<16, true, 8, true>, a, bx, a.nseg, s);
+        default: return go(&k_fanout<16, true, 4, true>, a, bx, a.nseg, s);
+      }
+    }
     switch (u) {
       case 1: return nt ? go(&k_fanout<16, true, 1>, a, bx, a.nseg, s) : go(&k_fanout<16, false, 1>, a, bx, a.nseg, s);
       case 2: return nt ? go(&k_fanout<16, true, 2>, a, bx, a.nseg, s) : go(&k_fanout<16, false, 2>, a, bx, a.nseg, s);
