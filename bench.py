@@ -357,6 +357,7 @@ def cpu_baseline(spec, host_x, op, seconds):
             break
     bytes_per = 2 * p * m * s
     what = "all_reduce_hier" if fn is not None else "all_reduce_ring"
+    threaded = None if fn is not None else threaded_formula_fold(sample, op, dtype, min(seconds, 5.0))
     return {
         "value": round(bytes_per * reps / el / 1e9, 4),
         "unit": "GB/s",
@@ -367,6 +368,64 @@ def cpu_baseline(spec, host_x, op, seconds):
         "host_cpus": os.cpu_count(),
         "affinity_cpus": len(os.sched_getaffinity(0)),
         "numpy": np.__version__,
+        "threaded_formula_fold": threaded,
+    }
+
+
+def threaded_formula_fold(sample, op, dtype, seconds):
+    """Second CPU timing: the oracle's per-chunk ring-order fold (the steps of
+    oracle.all_reduce_fold: to_acc, combine in the order x_{c+1}, ..., x_c,
+    finish, from_acc) over pieces of every chunk in a thread pool with one
+    worker per CPU of the affinity set (NumPy releases the GIL in its loops);
+    every rank's output row is written, as in the all-reduce.  The result is
+    checked against oracle.all_reduce_fold before timing."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    from oracle import collectives as C
+
+    p, m = sample.shape
+    threads = len(os.sched_getaffinity(0))
+    b = C.chunk_bounds(m, p)
+    pieces = []
+    for c in range(p):
+        lo, hi = b[c], b[c + 1]
+        k = max(1, min(threads, (hi - lo) // 4096))
+        for j in range(k):
+            a0 = lo + (hi - lo) * j // k
+            a1 = lo + (hi - lo) * (j + 1) // k
+            if a1 > a0:
+                pieces.append((c, a0, a1))
+    out = np.empty_like(sample)
+
+    def work(piece):
+        # the steps of oracle.all_reduce_fold, on one piece of chunk c
+        c, a0, a1 = piece
+        acc = C.to_acc(sample[(c + 1) % p, a0:a1], dtype)
+        for k in range(2, p + 1):
+            acc = C.combine(acc, C.to_acc(sample[(c + k) % p, a0:a1], dtype), op)
+        out[:, a0:a1] = C.from_acc(C.finish(acc, op, p), dtype)[None, :]
+
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        list(pool.map(work, pieces))
+        if not np.array_equal(out.view(np.uint8), C.all_reduce_fold(sample, op, dtype).view(np.uint8)):
+            raise RuntimeError("threaded formula fold differs from oracle.all_reduce_fold")
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            list(pool.map(work, pieces))
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or reps >= 1000:
+                break
+    s = sample.dtype.itemsize
+    return {
+        "value": round(2 * p * m * s * reps / el / 1e9, 4),
+        "unit": "GB/s",
+        "threads": threads,
+        "sample": f"the steps of oracle.all_reduce_fold over {len(pieces)} pieces of the {p} chunks of the same "
+                  f"sample, {threads} worker threads, {reps} calls in {el:.1f} s",
     }
 
 
