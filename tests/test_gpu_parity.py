@@ -379,6 +379,25 @@ def test_fanout_tilings_agree(rr, monkeypatch, env):
     assert_bitwise(rows(out, "float32"), C.broadcast(x[5], p), f"broadcast {env}")
 
 
+@pytest.mark.parametrize("L", [524288, 524292])
+def test_fanout_store_policy_boundary(rr, L):
+    """The fan-out stores nontemporal while a launch writes at most 128 MiB
+    and plain above: an all-gather of 8 float32 shards that writes exactly
+    128 MiB, and one that writes 16 bytes per shard and rank more, give the
+    oracle's bits, as does the broadcast of the same 8L elements."""
+    p = 8
+    x = W.random_inputs(15, p, L, "float32")
+    full = torch.empty((p, p * L), dtype=torch.float32, device="cuda")
+    rr.all_gather(to_dev(x, "float32"), full)
+    assert_bitwise(rows(full, "float32"), C.all_gather(x), f"all_gather L={L}")
+    src = np.ascontiguousarray(x.reshape(-1))
+    out = torch.empty((p, p * L), dtype=torch.float32, device="cuda")
+    rr.broadcast(to_dev(src, "float32"), out, root=0)
+    assert_bitwise(rows(out, "float32"), C.broadcast(src, p), f"broadcast L={L}")
+    del full, out
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_unaligned_buffers_take_the_scalar_path(rr, dtype):
     """Rank buffers offset by one element (not 16-byte aligned) give the same
