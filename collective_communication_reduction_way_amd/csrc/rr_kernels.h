@@ -233,7 +233,8 @@ hipError_t launch_fold_hier_all(const FoldLaunch& f, hipStream_t stream);
 // The hierarchical variants (kHierRing, kHierAllWire, kHierRingWire), run-time p.
 hipError_t launch_fold_hier_var(const FoldLaunch& f, hipStream_t stream);
 // Copies move units of unit_bytes in {16, 4, 2, 1}; nontemporal != 0 uses
-// nontemporal loads (and, for copy_pairs, stores); grid_cap 0 = the default
+// nontemporal loads, and nontemporal stores for copy_pairs and for a fan-out
+// of 16-byte units that writes at most 128 MiB; grid_cap 0 = the default
 // workgroup count (fan-out of 16-byte units: one tile per workgroup, with
 // units_per_lane units per lane, 4 unless 1, 2 or 8).
 hipError_t launch_fanout(const FanoutArgs& a, int unit_bytes, int nontemporal, int grid_cap, int units_per_lane,
