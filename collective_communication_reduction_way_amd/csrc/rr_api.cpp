@@ -411,21 +411,19 @@ rr_status_t ar_ring_staged(const void* const* send, void* const* recv, int p, ui
     a.vec = vec;
     const hipError_t e = rr::launch_convert_pairs(a, kind_of(dt), Kind::kF32, t.grid_cap, s);
     if (e != hipSuccess) return hip_fail(e, "all_reduce(ring, staged): widen");
-  } else {
-    std::vector<const void*> src;
-    std::vector<void*> dst;
-    std::vector<uint64_t> bytes;
-    for (int r = 0; r < p; ++r)
-      if (send[r] != recv[r]) {
-        src.push_back(send[r]);
-        dst.push_back(recv[r]);
-        bytes.push_back(n * esz);
-      }
-    if (!src.empty()) {
-      st = launch_pairs_copy(t, src, dst, bytes, "all_reduce(ring, staged): copy in", s);
+  } else if (p == 1) {
+    if (send[0] != recv[0]) {
+      st = launch_pairs_copy(t, {send[0]}, {recv[0]}, {n * esz}, "all_reduce(ring, staged): copy", s);
       if (st) return st;
     }
   }
+  // 4-byte types need no copy of the inputs into the receive buffers: in
+  // reduce-scatter step s the receiver's own chunk has not been written yet
+  // (it receives that chunk only in this step), so it is read from its
+  // input, and the message is the sender's input in step 0 and the sender's
+  // buffer (the chunk it received in step s - 1) later; every chunk of every
+  // buffer is written by the reduce-scatter or the all-gather phase.
+  const bool direct = !bf16;
   // Reduce-scatter: one launch per step, p transfers each.
   for (int step = 0; step < p - 1; ++step) {
     rr::PairArgs a;
@@ -435,10 +433,16 @@ rr_status_t ar_ring_staged(const void* const* send, void* const* recv, int p, ui
     for (const rr::Transfer& x : sched) {
       if (x.phase != 0 || x.step != step) continue;
       const uint64_t off = b[x.chunk] * wsz;
-      a.src[m] = work[x.src] + off;
+      if (direct) {
+        a.src[m] = static_cast<const char*>(step == 0 ? send[x.src] : recv[x.src]) + off;
+        a.aux[m] = static_cast<const char*>(send[x.dst]) + off;
+      } else {
+        a.src[m] = work[x.src] + off;
+        a.aux[m] = work[x.dst] + off;
+      }
       a.dst[m] = work[x.dst] + off;
       a.len[m] = b[x.chunk + 1] - b[x.chunk];
-      vec = vec && aligned16(a.src[m]) && aligned16(a.dst[m]);
+      vec = vec && aligned16(a.src[m]) && aligned16(a.dst[m]) && aligned16(a.aux[m]);
       ++m;
     }
     a.npairs = m;

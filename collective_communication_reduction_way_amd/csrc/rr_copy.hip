@@ -120,7 +120,8 @@ __global__ __launch_bounds__(kBlock) void k_copy_pairs(PairArgs a) {
 
 // Element-wise conversion (16-bit kinds <-> f32 for the staged paths, with
 // AVG's division when a.div > 0) or the ring's reduce-scatter step
-// (dst = src (+) dst, message first).  8 elements per group on the vector
+// (dst = src (+) aux, message first; aux is the receiver's own value, its
+// buffer or, before the receiver has written that chunk, its input).  8 elements per group on the vector
 // path, scalar otherwise (and for the last partial group).
 template <class EF, class ET, class OP, bool STEP>
 __global__ __launch_bounds__(kBlock) void k_pairs_elem(PairArgs a) {
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(kBlock) void k_pairs_elem(PairArgs a) {
     unpack(rs, x);
     if constexpr (STEP) {
       Raw<ET, V> rd;
-      load_group<false>(rd, dst + g * V);
+      load_group<false>(rd, static_cast<const typename ET::S*>(a.aux[y]) + g * V);
       A d[V];
       unpack(rd, d);
 #pragma unroll
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(kBlock) void k_pairs_elem(PairArgs a) {
   for (uint64_t i = ngroups * V + static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n; i += stride) {
     A x = load_one<EF>(src + i);
     if constexpr (STEP) {
-      x = OP::apply(x, load_one<ET>(dst + i));
+      x = OP::apply(x, load_one<ET>(static_cast<const typename ET::S*>(a.aux[y]) + i));
     } else if constexpr (__is_same(A, float)) {
       if (a.div > 0) x = x / static_cast<float>(a.div);
     }

@@ -96,6 +96,9 @@ struct FanoutArgs {
 struct PairArgs {
   const void* src[RR_MAX_RANKS];
   void* dst[RR_MAX_RANKS];
+  // Ring reduce-scatter step only: where the receiver's own value is read
+  // (dst = src (+) aux); the other kinds of launch leave it unused.
+  const void* aux[RR_MAX_RANKS];
   uint64_t len[RR_MAX_RANKS];
   int32_t npairs;
   int32_t vec;
