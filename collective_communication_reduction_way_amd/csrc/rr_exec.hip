@@ -229,9 +229,12 @@ __global__ __launch_bounds__(kBlock) void k_ring_exec(ExecArgs a) {
       if (!go) return;
     }
     if (t == 0) {
-      // copy-in of slice b of every chunk of rank q
+      // copy-in of slice b of every chunk of rank q into the float32
+      // working buffer (16-bit kinds).  4-byte kinds fold straight from the
+      // inputs instead (reduce-scatter below), so their step 0 moves nothing
+      // unless p = 1 (no steps follow: the output is the input's copy).
       const S* in = static_cast<const S*>(a.in[q]);
-      if (kSeparate || static_cast<const void*>(in) != static_cast<const void*>(wq)) {
+      if (kSeparate || (p == 1 && static_cast<const void*>(in) != static_cast<const void*>(wq))) {
         for (int c = 0; c < p; ++c) {
           for_slice(
               slice_lo(c), slice_hi(c), vec,
@@ -248,17 +251,29 @@ __global__ __launch_bounds__(kBlock) void k_ring_exec(ExecArgs a) {
         }
       }
     } else if (t < p) {
-      // reduce-scatter step s: the message from rank r is folded first
+      // reduce-scatter step s: the message from rank r is folded first.
+      // Without working buffers apart from the outputs, rank q's own chunk
+      // c is still unwritten (q folds it in this step only), so it is read
+      // from q's input, and the message is r's input in step 0 (r's chunk
+      // c is unwritten too) and r's output later (the chunk r folded in
+      // step s - 1).  Only q writes its output, and an input that is also
+      // the output is overwritten by q's all-gather step 0 only after the
+      // successor's step-0 read (the wait above).
       const int s = t - 1;
       int c = r - 1 - s;
       while (c < 0) c += p;
       const SA* wr = static_cast<const SA*>(a.work[r]);
+      const SA* lq = wq;
+      if constexpr (!kSeparate) {
+        if (s == 0) wr = static_cast<const SA*>(a.in[r]);
+        lq = static_cast<const SA*>(a.in[q]);
+      }
       for_slice(
           slice_lo(c), slice_hi(c), vec,
           [&](uint64_t i) {
             Raw<EA, 8> m, l;
             load_group<false>(m, wr + i);
-            load_group<false>(l, wq + i);
+            load_group<false>(l, lq + i);
             A vm[8], vl[8];
             unpack(m, vm);
             unpack(l, vl);
@@ -267,7 +282,7 @@ __global__ __launch_bounds__(kBlock) void k_ring_exec(ExecArgs a) {
             pack(vm, m);
             store_group<false>(wq + i, m);
           },
-          [&](uint64_t i) { store_one<EA>(wq + i, OP::apply(load_one<EA>(wr + i), load_one<EA>(wq + i))); });
+          [&](uint64_t i) { store_one<EA>(wq + i, OP::apply(load_one<EA>(wr + i), load_one<EA>(lq + i))); });
       if (t == p - 1 && (kSeparate || is_avg<OP>())) {
         // rank q now owns chunk q: the op's last step, the one conversion
         __syncthreads();

@@ -398,14 +398,16 @@ def test_fanout_store_policy_boundary(rr, L):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("algo", ["ring_staged", "ring_persistent"])
 @pytest.mark.parametrize("p,n", [(2, 1001), (3, 4099), (5, 5 * 4096 + 7), (8, 8 * 65536 + 4)])
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_staged_ring_reads_no_output_before_writing_it(rr, p, n, dtype):
-    """The staged ring folds straight from the inputs (no copy into the
-    outputs first): outputs filled with NaN (all ones for int32) beforehand,
-    one rank in place, every op -- the oracle's bits, equal to the fused
-    pass."""
+def test_staged_ring_reads_no_output_before_writing_it(rr, p, n, dtype, algo):
+    """The staged ring and the persistent executor fold 4-byte types straight
+    from the inputs (no copy into the outputs first): outputs filled with NaN
+    (all ones for int32) beforehand, one rank in place, every op -- the
+    oracle's bits."""
     x = W.random_inputs(16, p, n, dtype, kind="full" if dtype == "int32" else "normal")
+    f0 = rr.ring_exec_failures()
     for op in ("sum", "max", "min") + (("avg",) if dtype != "int32" else ()):
         xs = to_dev(x, dtype)
         out = torch.empty_like(xs)
@@ -415,10 +417,11 @@ def test_staged_ring_reads_no_output_before_writing_it(rr, p, n, dtype):
             out.fill_(float("nan"))
         outs = [out[r] for r in range(p)]
         outs[p - 1] = xs[p - 1]  # in place for the last rank
-        rr.all_reduce([xs[r] for r in range(p)], outs, op=op, algo="ring_staged")
+        rr.all_reduce([xs[r] for r in range(p)], outs, op=op, algo=algo)
         got = np.stack([rows(o, dtype) for o in outs])
         ref = C.all_reduce_fold(x, op, dtype)
-        assert_bitwise(got, ref, f"staged {op} p={p} n={n}")
+        assert_bitwise(got, ref, f"{algo} {op} p={p} n={n}")
+    assert rr.ring_exec_failures() == f0, "an executor wait timed out"
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
