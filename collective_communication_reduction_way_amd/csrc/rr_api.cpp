@@ -561,19 +561,27 @@ rr_status_t ar_hier_staged(const void* const* send, void* const* recv, int p, ui
   f2.args.vec = vec ? 1 : 0;
   st = run_fold(t, "all_reduce(hierarchical, staged): cross-group reduce", f2, s);
   if (st) return st;
-  // Step 6: each representative broadcasts inside its group.
+  // Step 6: each representative broadcasts inside its group, one fan-out
+  // launch per group (the representative's buffer is read once and written
+  // to its G - 1 members; as G - 1 pair copies it was read G - 1 times).
   if (G > 1) {
-    std::vector<const void*> src;
-    std::vector<void*> dst;
-    std::vector<uint64_t> bytes;
-    for (int j = 0; j < J; ++j)
+    for (int j = 0; j < J; ++j) {
+      rr::FanoutArgs a;
+      memset(&a, 0, sizeof(a));
+      std::vector<uintptr_t> addrs{reinterpret_cast<uintptr_t>(recv[j * G])};
+      a.src[0] = recv[j * G];
       for (int i = 1; i < G; ++i) {
-        src.push_back(recv[j * G]);
-        dst.push_back(recv[j * G + i]);
-        bytes.push_back(n * esz);
+        a.dst[i - 1] = recv[j * G + i];
+        addrs.push_back(reinterpret_cast<uintptr_t>(recv[j * G + i]));
       }
-    st = launch_pairs_copy(t, src, dst, bytes, "all_reduce(hierarchical, staged): group broadcast", s);
-    if (st) return st;
+      a.seg_bytes = n * esz;
+      a.dst_seg_stride = 0;
+      a.nseg = 1;
+      a.ndst = G - 1;
+      const int unit = copy_unit(addrs, {n * esz});
+      const hipError_t e = rr::launch_fanout(a, unit, t.nontemporal, t.grid_cap, t.copy_u, s);
+      if (e != hipSuccess) return hip_fail(e, "all_reduce(hierarchical, staged): group broadcast");
+    }
   }
   return RR_SUCCESS;
 }
