@@ -159,13 +159,15 @@ rr_status_t rr_all_reduce(const void* const* sendbufs, void* const* recvbufs, in
  * All-reduce with an explicit algorithm.
  *   algo = RR_ALGO_RING_FUSED: same as rr_all_reduce (group_size and workspace ignored).
  *   algo = RR_ALGO_RING_STAGED: the ring schedule of [RING] run literally, one
- *     launch per step (2(p-1) steps, plus a copy of the inputs into recvbufs
- *     when not in place): reduce-scatter step s moves chunk (r-1-s) mod p from
- *     rank r to rank r+1 and the receiver stores message (+) local; all-gather
- *     step s moves chunk (r-s) mod p and the receiver overwrites.  Any n (the
- *     chunk bounds above).  For bfloat16 and float16 the partial sums live in
- *     a float32 workspace of rr_workspace_size() bytes (one rounding at the
- *     end); int32/float32 work in recvbufs and need no workspace.  RR_AVG:
+ *     launch per step (2(p-1) steps): reduce-scatter step s moves chunk
+ *     (r-1-s) mod p from rank r to rank r+1 and the receiver stores
+ *     message (+) local; all-gather step s moves chunk (r-s) mod p and the
+ *     receiver overwrites.  Any n (the chunk bounds above).  For bfloat16 and
+ *     float16 the partial sums live in a float32 workspace of
+ *     rr_workspace_size() bytes, filled from the inputs first (one rounding
+ *     at the end); int32/float32 work in recvbufs, need no workspace and read
+ *     each not yet written value from sendbufs (no copy of the inputs into
+ *     recvbufs first; recvbufs are written before they are read).  RR_AVG:
  *     the owner of each reduced chunk divides it by p before the all-gather
  *     phase.  Bitwise equal to RR_ALGO_RING_FUSED.
  *   algo = RR_ALGO_HIER_FUSED [HIER]: ranks form p/group_size contiguous groups
