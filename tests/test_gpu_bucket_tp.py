@@ -145,12 +145,12 @@ def test_bucket_barrier(rr, monkeypatch):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("p", (5, 8))
 @pytest.mark.parametrize("strips", ("1", "2", "3", "8"))
-def test_bucket_interleaved_tiles(rr, monkeypatch, strips):
+def test_bucket_interleaved_tiles(rr, monkeypatch, strips, p):
     """A multi-round bucket whose vector pieces hold whole tiles taken in runs
     of interleaved tiles (1 = contiguous), with ragged and unaligned tensors
     beside them: the oracle's bits for sum and max, and no wait runs out."""
-    p = 8
     sizes = [3 * (1 << 20) + 5, 1 << 22, 777, 9 * 4096 + 8, (1 << 21) + 4]
     parts = [W.random_inputs(91 + i, p, n, "float32") for i, n in enumerate(sizes)]
     monkeypatch.setenv("RR_PHASE_STRIPS", strips)
