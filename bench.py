@@ -4,23 +4,29 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--extra]
 
 One step is one collective call over one batch of synthetic rank buffers
-already resident in HBM: for the default workload, a sum all-reduce of p = 8
-ranks x 2,097,152 float32 (8 MiB per rank) through ``rr_all_reduce`` -- host
-validation and planning, the ring chunk plan, and the single fused kernel that
-folds every chunk in ring order and writes all p outputs (reduce-scatter and
-all-gather in one pass).
+already resident in HBM.  The default workload is the largest one: the
+row-parallel partial outputs of a tensor-parallel linear layer, p = 8 ranks x
+(8, 2048, 4096) bfloat16 (128 MiB per rank), sum all-reduce through
+``rr_all_reduce`` -- host validation and planning, the ring chunk plan, and
+the single fused kernel that folds every chunk in ring order in float32 and
+writes all p outputs (reduce-scatter and all-gather in one pass).
 
 Metric: algorithmic HBM bytes per step / time, bytes = 2 p n s for an
 all-reduce (every input read once, every output written once), in GB/s
-(10^9 B/s), and its fraction of MI355X's 8 TB/s HBM peak.  The 128 MiB of
-rank buffers fit in the 256 MB Infinity Cache, so steps rotate over enough
-buffer sets that each set is evicted by >= 512 MiB of other traffic before it
-is used again (cold cache).  A bounded spin kernel queued before the timed
-region lets the host run ahead, so host launch cost does not idle the GPU.
+(10^9 B/s), and its fraction of MI355X's 8 TB/s HBM peak.  Steps rotate over
+enough buffer sets that each set is evicted from the 256 MB Infinity Cache by
+>= 512 MiB of other traffic before it is used again (cold cache).  A bounded
+spin kernel queued before the timed region lets the host run ahead, so host
+launch cost does not idle the GPU.
+
+Besides the timed region, the line reports the spread of single launches (a
+separate pass with events around every launch), the copy ceilings of the
+same box (a 1 GiB hipMemcpyAsync device-to-device copy and librr's own copy
+kernel), and the CPU oracle timed on the host's cores.
 
 Prints ONE JSON line on stdout.  ``--extra`` prints further measurements
-(other collectives, staged algorithms, cache-hot figures, copy ceiling) as
-JSON lines on stderr.
+(the other workloads and collectives, staged algorithms, cache-hot figures)
+as JSON lines on stderr.
 """
 
 import argparse
@@ -45,7 +51,10 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="ar_fp32_p8_8MiB")
+    ap.add_argument("--workload", default="tp_rowparallel_bf16_p8")
+    ap.add_argument("--spread-steps", type=int, default=50,
+                    help="launches of the separate per-launch pass (min / median / max); 0 = skip")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the copy ceilings")
     ap.add_argument("--op", default=None, help="sum, max or min (default: the workload's first op)")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate over (0 = enough for a cold cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -54,6 +63,11 @@ def parse_args(argv=None):
     ap.add_argument("--calibration-copy", action="store_true",
                     help="launch one plain 256 MiB copy (librr's copy kernel) before timing, as the known-size "
                          "reference for HBM byte counters")
+    ap.add_argument("--probe-cases", action="store_true",
+                    help="run copies of known size (64 MiB to 512 MiB) and one launch pair of each workload's "
+                         "collectives, separated by spin-kernel markers, for rocprofv3 --pmc runs; then exit")
+    ap.add_argument("--ingest-probe", nargs="+", metavar="DB",
+                    help="print per-case counter values of --probe-cases runs (rocprofv3 *_results.db files)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH", "WRITE"),
                     help="turn the outputs of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; *_results.db or "
                          "counter_collection.csv) into the traffic record under profiles/, then exit")
@@ -138,6 +152,117 @@ def ingest_pmc(workload, fetch_path, write_path):
     with open(traffic_path(workload), "w", encoding="utf-8") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
+
+
+PROBE_CASES = [
+    # (name, algorithmic read bytes, algorithmic write bytes) per launch
+    ("copy_64MiB", 64 << 20, 64 << 20), ("copy_96MiB", 96 << 20, 96 << 20), ("copy_128MiB", 128 << 20, 128 << 20),
+    ("copy_256MiB", 256 << 20, 256 << 20), ("copy_512MiB", 512 << 20, 512 << 20),
+    ("ar_fp32_p8_8MiB all_reduce", 8 * (8 << 20), 8 * (8 << 20)),
+    ("hier_bf16_p8g4_8MiB all_reduce", 8 * (8 << 20), 8 * (8 << 20)),
+    ("zero_bucket_fp32_p8 all_reduce", 8 * (96 << 20), 8 * (96 << 20)),
+    ("zero_bucket_fp32_p8 reduce_scatter", 8 * (96 << 20), 96 << 20),
+    ("zero_bucket_fp32_p8 all_gather", 96 << 20, 8 * (96 << 20)),
+    ("zero_bucket_fp32_p8 broadcast", 96 << 20, 8 * (96 << 20)),
+    ("tp_rowparallel_bf16_p8 all_reduce", 8 * (128 << 20), 8 * (128 << 20)),
+]
+
+
+def probe_cases():
+    """Each case of PROBE_CASES launched twice, after a one-workgroup spin
+    kernel that marks where the case's dispatches begin (for --ingest-probe).
+    Inputs are drawn on the device: only the bytes matter here.  Copies are
+    librr's copy kernel (a broadcast to one rank)."""
+    import torch
+
+    import collective_communication_reduction_way_amd as rr
+
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+
+    def case(fn):
+        torch.cuda._sleep(1)  # the marker
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+
+    for mib in (64, 96, 128, 256, 512):
+        src = torch.ones((mib << 20) // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        case(lambda: rr.broadcast(src, [dst], root=0))
+        del src, dst
+        torch.cuda.empty_cache()
+
+    def pair(p, n, dt):
+        x = torch.randn((p, n), device=dev, generator=g).to(dt)
+        return x, torch.empty_like(x)
+
+    x, y = pair(8, 2097152, torch.float32)
+    case(lambda: rr.all_reduce(x, y))
+    x, y = pair(8, 4194304, torch.bfloat16)
+    case(lambda: rr.all_reduce(x, y, algo="hier", group_size=4))
+    del x, y
+    torch.cuda.empty_cache()
+    x, y = pair(8, 25165824, torch.float32)
+    sh = torch.empty((8, 25165824 // 8), device=dev)
+    case(lambda: rr.all_reduce(x, y))
+    case(lambda: rr.reduce_scatter(x, sh))
+    case(lambda: rr.all_gather(sh, y))
+    case(lambda: rr.broadcast(x[0], y, root=0))
+    del x, y, sh
+    torch.cuda.empty_cache()
+    x, y = pair(8, 67108864, torch.bfloat16)
+    case(lambda: rr.all_reduce(x, y))
+    torch.cuda._sleep(1)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe_cases": [c[0] for c in PROBE_CASES]}), flush=True)
+    return 0
+
+
+def ingest_probe(dbs):
+    """Per case of --probe-cases: the librr kernels' counter values (last of
+    the case's two launches), each HBM byte counter against the case's
+    algorithmic bytes.  TCC_EA0_RDREQ_DRAM_32B / TCC_EA0_WRREQ_WRITE_DRAM_32B
+    count 32-byte units (a 64-byte request as 2, a 128-byte one as 4);
+    FETCH_SIZE / WRITE_SIZE are KiB."""
+    import collections
+    import sqlite3
+
+    for db in dbs:
+        con = sqlite3.connect(db)
+        rows = con.execute("select dispatch_id, kernel_name, counter_name, value from counters_collection "
+                           "order by dispatch_id").fetchall()
+        con.close()
+        disp = collections.OrderedDict()
+        for did, kn, cn, v in rows:
+            d = disp.setdefault(did, {"k": kn, "c": {}})
+            d["c"][cn] = d["c"].get(cn, 0.0) + v
+        groups, cur = [], None
+        for d in disp.values():
+            if "spin_kernel" in d["k"]:
+                if cur is not None:
+                    groups.append(cur)
+                cur = []
+            elif cur is not None and "rr::" in d["k"]:
+                cur.append(d)
+        print(f"== {os.path.basename(db)}")
+        for (name, rd, wr), grp in zip(PROBE_CASES, groups):
+            kernels = collections.OrderedDict()
+            for d in grp:
+                kernels.setdefault(d["k"].replace("void rr::(anonymous namespace)::", "").split("(")[0], []).append(d)
+            for kname, ds in kernels.items():
+                c = ds[-1]["c"]
+                cells = []
+                for cn, v in sorted(c.items()):
+                    if cn in ("TCC_EA0_RDREQ_DRAM_32B_sum", "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum", "FETCH_SIZE",
+                              "WRITE_SIZE"):
+                        unit = 32 if cn.endswith("32B_sum") else 1024
+                        ref = rd if ("RDREQ" in cn or cn == "FETCH_SIZE") else wr
+                        cells.append(f"{cn}={v:.0f} ({v * unit / ref:.4f}x)")
+                    else:
+                        cells.append(f"{cn}={v:.0f}")
+                print(f"{name:36s} {kname[:48]:48s} " + " ".join(cells))
 
 
 def busbw_gibps(kind, p, s_bytes, t_seconds):
@@ -332,6 +457,81 @@ def timed(torch, runner, steps, warmup, stream, cycles_per_ms, per_launch=True):
     return region_ms / steps, kern, wall
 
 
+def launch_spread(torch, runner, steps, stream, cycles_per_ms):
+    """A separate pass (after the timed region, not inside it): `steps`
+    launches, each between its own pair of HIP events on the launch stream,
+    queued behind a spin so that they run back to back.  Returns min, median,
+    max and mean per-launch milliseconds and the GB/s at the median and min."""
+    times = []
+    for i in range(3):
+        runner.step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    with torch.cuda.stream(stream):
+        if cycles_per_ms:
+            torch.cuda._sleep(int(min(50.0, 0.05 * steps + 1.0) * cycles_per_ms))
+        for i in range(steps):
+            evs[i][0].record(stream)
+            runner.step(i)
+            evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    times = sorted(a.elapsed_time(b) for a, b in evs)
+    med = times[len(times) // 2] if len(times) % 2 else 0.5 * (times[len(times) // 2 - 1] + times[len(times) // 2])
+    return {
+        "launches": steps, "min_ms": round(times[0], 6), "median_ms": round(med, 6), "max_ms": round(times[-1], 6),
+        "mean_ms": round(sum(times) / len(times), 6),
+        "GBps_at_median": round(runner.bytes / (med * 1e-3) / 1e9, 2),
+        "GBps_at_min": round(runner.bytes / (times[0] * 1e-3) / 1e9, 2),
+    }
+
+
+def copy_ceilings(torch, rr, stream, nbytes=1 << 30, reps=10):
+    """What a plain copy reaches on the same box, as the achievable reference
+    for the collectives: a hipMemcpyAsync device-to-device copy of 1 GiB, and
+    librr's own copy kernel (a broadcast to one rank: the fan-out kernel with
+    one destination) on the same buffers.  GB/s count the bytes read plus the
+    bytes written (2 x 1 GiB per copy)."""
+    import ctypes
+
+    hip = ctypes.CDLL("libamdhip64.so.7")  # the HIP runtime torch has loaded
+    hip.hipMemcpyAsync.restype = ctypes.c_int
+    hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(3)]
+    for b in bufs:
+        b.fill_(1)
+    L = rr.lib()
+    sh = stream.cuda_stream
+
+    def memcpy(i):
+        src, dst = bufs[i % 3], bufs[(i + 1) % 3]
+        if hip.hipMemcpyAsync(dst.data_ptr(), src.data_ptr(), nbytes, 3, sh) != 0:  # 3: device to device
+            raise RuntimeError("hipMemcpyAsync failed")
+
+    def librr_copy(i):
+        src, dst = bufs[i % 3], bufs[(i + 1) % 3]
+        if L.rr_broadcast(src.data_ptr(), rr._ptr_array([dst.data_ptr()]), 0, 1, nbytes // 4, rr.DTYPES["float32"],
+                          sh) != 0:
+            raise RuntimeError(L.rr_last_error().decode())
+
+    res = {}
+    for name, fn in (("hip_memcpy_d2d_1GiB", memcpy), ("librr_copy_kernel_1GiB", librr_copy)):
+        for i in range(2):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(reps):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        gbps = 2 * nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"GBps": round(gbps, 2), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4), "ms": round(ms, 6)}
+    del bufs
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(spec, host_x, op, seconds):
     """Time the oracle's literal ring simulation (as it stands, NumPy, one
     thread) on a bounded sample of the same inputs."""
@@ -434,6 +634,11 @@ def main(argv=None):
     if args.ingest_pmc:
         ingest_pmc(args.workload, *args.ingest_pmc)
         return 0
+    if args.ingest_probe:
+        ingest_probe(args.ingest_probe)
+        return 0
+    if args.probe_cases:
+        return probe_cases()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the p virtual ranks live in one GPU's HBM and no collective crosses "
               f"GPUs; --gpus {args.gpus} is not supported (run with --gpus 1).", file=sys.stderr)
@@ -467,17 +672,18 @@ def main(argv=None):
         stream.synchronize()
         del src, dst
     cpm = spin_cycles_per_ms(torch, stream)
-    # One step is one launch of the fused kernel, so the kernel's average
-    # launch duration is the timed region (HIP events on the launch stream)
-    # divided by the number of launches.  Events around every launch would
-    # add their own cost to each ~25 us launch, so none are recorded inside.
+    # The timed region: exactly `steps` steps between HIP events on the launch
+    # stream.  One step is one launch of the fused kernel (the workloads have
+    # no chunk heads or tails, so no second launch), so the kernel's average
+    # launch duration is the region divided by the launches.
     ms_step, _, wall = timed(torch, runner, args.steps, args.warmup, stream, cpm, per_launch=False)
-    kern_ms = ms_step
+    launch_ms = ms_step
     value = runner.bytes / (ms_step * 1e-3) / 1e9
-    achieved = runner.bytes / (kern_ms * 1e-3) / 1e9
+    achieved = runner.bytes / (launch_ms * 1e-3) / 1e9
     kernel = {"ring": "k_phase<..., FoldMode::kRingAll, ...> (phased fused ring all-reduce)",
               "hier": "k_phase<..., FoldMode::kHierAll, ...> (phased fused hierarchical all-reduce)"}[algo]
     traffic = load_traffic(args.workload)
+    esz = np.dtype(W.STORAGE[dtype]).itemsize
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -492,20 +698,25 @@ def main(argv=None):
         "dtype": DTYPE_TAG[dtype],
         "data": "synthetic",
         "config": {
-            "workload": args.workload, "p": p, "n_per_rank": n, "op": op,
-            "algo": "ring_fused" if algo == "ring" else f"hier_fused_g{group}",
+            "workload": args.workload, "p": p, "n_per_rank": n, "shape_per_rank": list(spec.get("shape", (n,))),
+            "op": op, "algo": "ring_fused" if algo == "ring" else f"hier_fused_g{group}",
             "bytes_per_step": runner.bytes, "cold_cache_buffer_sets": nsets,
         },
         "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": kernel,
-            "launch_ms": round(kern_ms, 6), "launches_per_step": 1,
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+            "traffic_over_algorithmic": round(traffic / runner.bytes, 5) if traffic else None,
+            "kernel": kernel, "launch_ms": round(launch_ms, 6), "launch_ms_from": "timed region / launches",
+            "launches_per_step": 1,
         },
         "wall_s_timed_region": round(wall, 4),
-        "page_busbw_GiBps": round(busbw_gibps("all_reduce", p, n * np.dtype(W.STORAGE[dtype]).itemsize,
-                                              ms_step * 1e-3), 2),
+        "page_busbw_GiBps": round(busbw_gibps("all_reduce", p, n * esz, ms_step * 1e-3), 2),
     }
+    if args.spread_steps > 0:
+        out["per_launch"] = launch_spread(torch, runner, args.spread_steps, stream, cpm)
+    if not args.no_ceilings:
+        out["copy_ceilings"] = copy_ceilings(torch, rr, stream)
     if args.extra:
         extra(args, torch, rr, W, spec, host_x, stream, cpm, op, runner)
     del runner
@@ -518,24 +729,97 @@ def main(argv=None):
     return 0
 
 
-def extra(args, torch, rr, W, spec, host_x, stream, cpm, op, main_runner):
+def workload_lines(args, torch, rr, W, stream, cpm, report):
+    """Every workload other than the headline one, each with the collectives
+    its configuration names: the int32 p = 4 all-reduce (launch latency per
+    call), the 8 MiB fp32 all-reduce, the hierarchical bf16 all-reduce and the
+    gradient bucket's all-reduce (sum, max, min), reduce-scatter, all-gather,
+    the reduce-scatter -> all-gather pair, and broadcast."""
     import numpy as np
 
-    p, n, dtype = spec["p"], spec["n"], spec["dtype"]
-    esz = np.dtype(W.STORAGE[dtype]).itemsize
+    for name in ("ar_int32_p4_n4096", "ar_fp32_p8_8MiB", "hier_bf16_p8g4_8MiB", "zero_bucket_fp32_p8"):
+        if name == args.workload:
+            continue
+        spec = W.WORKLOADS[name]
+        x = W.make_inputs(name)
+        p, n, dtype = spec["p"], spec["n"], spec["dtype"]
+        esz = np.dtype(W.STORAGE[dtype]).itemsize
+        algo = "hier" if spec["algo"] == "hier" else "ring"
+        sets = 1 + math.ceil(COLD_BYTES / (2 * p * n * esz))
+        for op in spec["ops"]:
+            r = Runner(rr, torch, spec, "all_reduce", op, algo, spec.get("group", 0), x, sets, stream)
+            report(f"all_reduce_{algo}_{op}", r, 200 if n * esz <= (8 << 20) else 40, True, name)
+            del r
+            torch.cuda.empty_cache()
+        if spec["coll"] == "rs_ag":
+            for coll in ("reduce_scatter", "all_gather", "broadcast"):
+                fp = {"reduce_scatter": (p + 1) * n * esz, "all_gather": (p + 1) * n * esz,
+                      "broadcast": (2 * p) * n * esz}[coll]
+                r = Runner(rr, torch, spec, coll, "sum", "ring", 0, x, 1 + math.ceil(COLD_BYTES / fp), stream)
+                report(coll, r, 40, True, name)
+                del r
+                torch.cuda.empty_cache()
+            r = PairRunner(rr, torch, spec, x, 2, stream)
+            report("reduce_scatter_then_all_gather", r, 40, True, name)
+            del r
+            torch.cuda.empty_cache()
+        del x
+
+
+class PairRunner:
+    """Reduce-scatter then all-gather of its shards, one step each pair; the
+    bytes counted are the all-reduce's 2pns (the pair moves (p+1)ns twice)."""
+
+    def __init__(self, rr, torch, spec, host_x, nsets, stream):
+        p, n = spec["p"], spec["n"]
+        self.L = rr.lib()
+        dt = rr.DTYPES[spec["dtype"]]
+        sh = stream.cuda_stream
+        self.sets = []
+        for _ in range(nsets):
+            x = torch.from_numpy(host_x).to("cuda")
+            s = torch.empty((p, n // p), dtype=x.dtype, device="cuda")
+            y = torch.empty_like(x)
+            a = rr._ptr_array([x[r].data_ptr() for r in range(p)])
+            b = rr._ptr_array([s[r].data_ptr() for r in range(p)])
+            c = rr._ptr_array([y[r].data_ptr() for r in range(p)])
+            self.sets.append((x, s, y, a, b, c,
+                              lambda a=a, b=b, c=c: (self.L.rr_reduce_scatter(a, b, p, n, dt, 0, sh) or
+                                                     self.L.rr_all_gather(b, c, p, n, dt, sh))))
+        self.bytes = 2 * p * n * host_x.dtype.itemsize
+
+    def step(self, i):
+        if self.sets[i % len(self.sets)][-1]() != 0:
+            raise RuntimeError(f"librr call failed: {self.L.rr_last_error().decode()}")
+
+
+def extra(args, torch, rr, W, spec, host_x, stream, cpm, op, main_runner):
+    import numpy as np
 
     def report(tag, runner, steps, cold, workload=None):
         ms, _, _ = timed(torch, runner, steps, 5, stream, cpm, per_launch=False)
         print(json.dumps({"extra": tag, "workload": workload or args.workload, "cold_cache": cold,
                           "GBps": round(runner.bytes / ms / 1e6, 2), "ms_per_step": round(ms, 6),
+                          "us_per_call": round(ms * 1e3, 3),
                           "frac_of_peak": round(runner.bytes / ms / 1e6 / HBM_PEAK_GBPS, 4)}),
               file=sys.stderr, flush=True)
 
-    nsets = len(main_runner.sets)
     # cache-hot figure of the main collective: one buffer set, back to back
     hot = Runner(rr, torch, spec, "all_reduce", op, main_runner.algo, spec.get("group", 0), host_x, 1, stream)
     report(f"all_reduce_{main_runner.algo}_cache_hot", hot, args.steps, False)
     del hot
+    main_runner.sets.clear()
+    torch.cuda.empty_cache()
+    workload_lines(args, torch, rr, W, stream, cpm, report)
+    # the other collectives, algorithms and layouts on the 8 MiB fp32 workload
+    args.workload = "ar_fp32_p8_8MiB"
+    spec = W.WORKLOADS[args.workload]
+    host_x = W.make_inputs(args.workload)
+    op = "sum"
+    p, n, dtype = spec["p"], spec["n"], spec["dtype"]
+    esz = np.dtype(W.STORAGE[dtype]).itemsize
+    nsets = 1 + math.ceil(COLD_BYTES / (2 * p * n * esz))
+    main_algo = "ring"
     for coll in ("reduce_scatter", "all_gather", "reduce", "broadcast"):
         fp = {"reduce_scatter": (p + 1) * n * esz, "all_gather": (p + 1) * n * esz, "reduce": (p + 1) * n * esz,
               "broadcast": (2 * p) * n * esz}[coll]
@@ -553,9 +837,9 @@ def extra(args, torch, rr, W, spec, host_x, stream, cpm, op, main_runner):
         torch.cuda.empty_cache()
     # AVG over the same buffers (the DDP gradient average)
     if dtype != "int32":
-        r = Runner(rr, torch, spec, "all_reduce", "avg", main_runner.algo, spec.get("group", 0), host_x, nsets,
+        r = Runner(rr, torch, spec, "all_reduce", "avg", main_algo, spec.get("group", 0), host_x, nsets,
                    stream)
-        report(f"all_reduce_{main_runner.algo}_avg", r, max(10, args.steps // 2), True)
+        report(f"all_reduce_{main_algo}_avg", r, max(10, args.steps // 2), True)
         del r
         torch.cuda.empty_cache()
     # scatter and gather of the rank-sized buffer
@@ -601,23 +885,6 @@ def extra(args, torch, rr, W, spec, host_x, stream, cpm, op, main_runner):
         del r
         torch.cuda.empty_cache()
     del tx
-    # copy ceiling: torch's device-to-device copy of 1 GiB
-    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    b = torch.empty_like(a)
-    for _ in range(3):
-        b.copy_(a)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(10):
-        b.copy_(a)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / 10
-    print(json.dumps({"extra": "copy_ceiling_torch_d2d_1GiB", "GBps": round(2 * (1 << 30) / ms / 1e6, 2)}),
-          file=sys.stderr, flush=True)
-    del a, b
-    torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

@@ -50,6 +50,7 @@ __all__ = [
     "version",
     "barrier_timeouts",
     "ring_exec_failures",
+    "reload_tuning",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -128,6 +129,7 @@ def lib():
         "rr_barrier_timeouts": (I, [I, U64P]),
         "rr_ring_exec_failures": (I, [I, U64P]),
         "rr_version": (ctypes.c_char_p, []),
+        "rr_reload_tuning": (None, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -165,6 +167,12 @@ def ring_exec_failures(device=None):
 
 def version():
     return lib().rr_version().decode()
+
+
+def reload_tuning():
+    """Read the RR_* tuning variables of the environment again (the library
+    reads them once, at its first call); later calls use the new values."""
+    lib().rr_reload_tuning()
 
 
 def _check(status, func):
@@ -225,6 +233,22 @@ def _stream(t, stream):
     return stream.cuda_stream
 
 
+def _call_workspace(nbytes, t, stream):
+    """A device workspace for one call, allocated with torch on the current
+    stream.  When the kernels go to another stream, the tensor is marked as
+    used by that stream, so that torch's caching allocator does not hand the
+    block to new work on the current stream while those kernels still write
+    it (the tensor is freed as soon as the call returns)."""
+    import torch
+
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=t.device)
+    if stream is not None:
+        if isinstance(stream, int):
+            stream = torch.cuda.ExternalStream(stream, device=t.device)
+        ws.record_stream(stream)
+    return ws
+
+
 def _op(op):
     if op not in OPS:
         raise ValueError(f"unknown op {op!r}; use one of {sorted(OPS)}")
@@ -241,8 +265,6 @@ def all_reduce(ins, outs=None, op="sum", algo="ring", group_size=0, workspace=No
     need a device workspace of ``workspace_size(...)`` bytes (a uint8 tensor);
     when it is not given, one is allocated with torch for the call.
     """
-    import torch
-
     ins = _ranks(ins, "all_reduce inputs")
     outs = ins if outs is None else _ranks(outs, "all_reduce outputs")
     p, n = len(ins), ins[0].numel()
@@ -258,7 +280,7 @@ def all_reduce(ins, outs=None, op="sum", algo="ring", group_size=0, workspace=No
     ws_ptr, ws_bytes = None, 0
     if need:
         if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=ins[0].device)
+            workspace = _call_workspace(need, ins[0], stream)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     L = lib()
     st = L.rr_all_reduce_ex(_ptr_array([t.data_ptr() for t in ins]), _ptr_array([t.data_ptr() for t in outs]),
@@ -445,8 +467,6 @@ def all_reduce_hier(ins, outs=None, op="sum", group_size=1, intra="reduce", wire
     before the cross-group fold; staged=True runs the steps one by one
     through a workspace (allocated with torch when not given).
     """
-    import torch
-
     ins = _ranks(ins, "all_reduce_hier inputs")
     outs = ins if outs is None else _ranks(outs, "all_reduce_hier outputs")
     p, n = len(ins), ins[0].numel()
@@ -457,7 +477,7 @@ def all_reduce_hier(ins, outs=None, op="sum", group_size=1, intra="reduce", wire
     ws_ptr, ws_bytes = None, 0
     if need:
         if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=ins[0].device)
+            workspace = _call_workspace(need, ins[0], stream)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     st = lib().rr_all_reduce_hier(_ptr_array([t.data_ptr() for t in ins]), _ptr_array([t.data_ptr() for t in outs]),
                                   p, n, _dtype_code(ins[0]), _op(op), int(group_size), flags, ws_ptr, ws_bytes,

@@ -17,6 +17,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -100,7 +102,14 @@ struct Tuning {
   int copy_u;
 };
 
-Tuning tuning() {
+// The environment is read once per process, at the first call (or by
+// rr_reload_tuning), into an immutable snapshot; the call path only loads the
+// snapshot's pointer, so no collective call reads the environment (getenv
+// races with setenv in multithreaded hosts, and costs host time on the
+// latency-bound small calls).  A reload publishes a new snapshot and keeps
+// the old ones alive, since a call on another thread may still be reading
+// one; reloads are rare (tuning sweeps and tests), so they are never freed.
+Tuning read_tuning() {
   Tuning t;
   t.unroll = env_int("RR_UNROLL", 2);
   if (t.unroll != 1 && t.unroll != 2 && t.unroll != 4) t.unroll = 2;
@@ -131,6 +140,22 @@ Tuning tuning() {
   t.exec_slices = env_int("RR_EXEC_SLICES", kExecDefaultSlices);
   t.copy_u = env_int("RR_COPY_U", 4);
   return t;
+}
+
+std::atomic<const Tuning*> g_tuning{nullptr};
+std::mutex g_tuning_mu;
+
+void publish_tuning() {
+  std::lock_guard<std::mutex> lk(g_tuning_mu);
+  g_tuning.store(new Tuning(read_tuning()), std::memory_order_release);
+}
+
+const Tuning& tuning() {
+  static std::once_flag once;
+  std::call_once(once, [] {
+    if (!g_tuning.load(std::memory_order_acquire)) publish_tuning();
+  });
+  return *g_tuning.load(std::memory_order_acquire);
 }
 
 constexpr uint64_t kMaxElems = 1ull << 56;
@@ -509,8 +534,21 @@ rr_status_t ar_ring_exec(const void* const* send, void* const* recv, int p, uint
   const int slices = t.exec_slices > 0 ? t.exec_slices : kExecDefaultSlices;
   if (t.log) fprintf(stderr, "[rr] all_reduce(ring, persistent): p=%d n=%llu vec=%d\n", p, (unsigned long long)n, a.vec);
   const hipError_t e = rr::launch_ring_exec(a, kind_of(dt), op, t.exec_per_cu, slices, t.exec_timeout_us, s);
+  if (e == hipErrorOutOfMemory)
+    return fail(RR_ERROR_HIP,
+                "all_reduce(ring, persistent): no free step-flag slot on this device (16 for streams with launches "
+                "in flight, 48 for launches captured into graphs, each kept for the rest of the process)");
   if (e != hipSuccess) return hip_fail(e, "all_reduce(ring, persistent)");
   return RR_SUCCESS;
+}
+
+// Bytes between the group partials of the staged hierarchy in its
+// workspace: n partial values (the accumulator type, or the storage type
+// with wire rounding on a 16-bit dtype) rounded up to a multiple of 16.
+uint64_t hier_part_stride(uint64_t n, rr_dtype_t dt, int flags) {
+  const bool wire = (flags & RR_HIER_WIRE_ROUND) && is_half_dtype(dt);
+  const uint64_t bytes = n * (wire ? rr::elem_size(dt) : 4);
+  return (bytes + 15) / 16 * 16;
 }
 
 rr_status_t ar_hier_staged(const void* const* send, void* const* recv, int p, uint64_t n, rr_dtype_t dt, rr_op_t op,
@@ -520,7 +558,9 @@ rr_status_t ar_hier_staged(const void* const* send, void* const* recv, int p, ui
   // With wire rounding the partials cross groups in the storage type.
   const bool wire = (flags & RR_HIER_WIRE_ROUND) && is_half_dtype(dt);
   const Kind part_kind = wire ? kind_of(dt) : acc_kind_of(dt);
-  const uint64_t part_bytes = wire ? esz : 4;
+  // each group's partial starts on a 16-byte boundary of the workspace, so
+  // that the vector path's 16-byte accesses stay aligned for any n
+  const uint64_t part_stride = hier_part_stride(n, dt, flags);
   // Steps 1-2: each group reduces into its representative's partial
   // (accumulator type, or the storage type with wire rounding, in the
   // workspace).
@@ -538,7 +578,7 @@ rr_status_t ar_hier_staged(const void* const* send, void* const* recv, int p, ui
     f1.args.in[r] = send[r];
     vec = vec && aligned16(send[r]) && aligned16(recv[r]);
   }
-  for (int j = 0; j < J; ++j) f1.args.out[j] = static_cast<char*>(ws) + static_cast<uint64_t>(j) * n * part_bytes;
+  for (int j = 0; j < J; ++j) f1.args.out[j] = static_cast<char*>(ws) + static_cast<uint64_t>(j) * part_stride;
   f1.args.vec = vec ? 1 : 0;
   rr_status_t st = run_fold(t, "all_reduce(hierarchical, staged): group reduce", f1, s);
   if (st) return st;
@@ -590,10 +630,7 @@ size_t workspace_bytes(rr_algo_t algo, int p, int G, uint64_t n, rr_dtype_t dt, 
   switch (algo) {
     case RR_ALGO_RING_STAGED:
     case RR_ALGO_RING_PERSISTENT: return is_half_dtype(dt) ? static_cast<size_t>(p) * n * 4 : 0;
-    case RR_ALGO_HIER_STAGED: {
-      const bool wire = (flags & RR_HIER_WIRE_ROUND) && is_half_dtype(dt);
-      return static_cast<size_t>(p / G) * n * (wire ? rr::elem_size(dt) : 4);
-    }
+    case RR_ALGO_HIER_STAGED: return static_cast<size_t>(p / G) * hier_part_stride(n, dt, flags);
     default: return 0;
   }
 }
@@ -638,7 +675,7 @@ rr_status_t all_reduce_impl(const void* const* sendbufs, void* const* recvbufs, 
   }
   st = check_aliasing(outs, ins, [](const Range& o, const Range& i) { return o.rank == i.rank && o.lo == i.lo; });
   if (st) return st;
-  const Tuning t = tuning();
+  const Tuning& t = tuning();
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   switch (algo) {
     case RR_ALGO_RING_FUSED: st = ar_ring_fused(sendbufs, recvbufs, p, n, dtype, op, t, s); break;
@@ -708,7 +745,7 @@ rr_status_t rr_reduce_scatter(const void* const* sendbufs, void* const* recvbufs
     return o.rank == i.rank && o.lo == i.lo + static_cast<uintptr_t>(o.rank) * L * esz;
   });
   if (st) return st;
-  const Tuning t = tuning();
+  const Tuning& t = tuning();
   rr::FoldLaunch f = base_fold(t);
   f.mode = rr::FoldMode::kRingShard;
   f.in_kind = f.out_kind = kind_of(dtype);
@@ -764,7 +801,7 @@ rr_status_t rr_all_gather(const void* const* sendbufs, void* const* recvbufs, in
   a.dst_seg_stride = L * esz;
   a.nseg = p;
   a.ndst = p;
-  const Tuning t = tuning();
+  const Tuning& t = tuning();
   const int unit = copy_unit(addrs, {L * esz});
   if (t.log) fprintf(stderr, "[rr] all_gather: p=%d shard_bytes=%llu unit=%d\n", p, (unsigned long long)(L * esz), unit);
   const hipError_t e = rr::launch_fanout(a, unit, t.nontemporal, t.grid_cap, t.copy_u, reinterpret_cast<hipStream_t>(stream));
@@ -788,7 +825,7 @@ rr_status_t rr_reduce(const void* const* sendbufs, void* recvbuf, int root, int 
   for (int r = 0; r < p; ++r) ins.push_back(range_of(sendbufs[r], n * esz, r));
   st = check_aliasing(outs, ins, [](const Range& o, const Range& i) { return o.rank == i.rank && o.lo == i.lo; });
   if (st) return st;
-  const Tuning t = tuning();
+  const Tuning& t = tuning();
   rr::FoldLaunch f = base_fold(t);
   f.mode = rr::FoldMode::kAscOne;
   f.in_kind = f.out_kind = kind_of(dtype);
@@ -839,7 +876,7 @@ rr_status_t rr_broadcast(const void* sendbuf, void* const* recvbufs, int root, i
   a.dst_seg_stride = 0;
   a.nseg = 1;
   a.ndst = m;
-  const Tuning t = tuning();
+  const Tuning& t = tuning();
   const int unit = copy_unit(addrs, {n * esz});
   if (t.log) fprintf(stderr, "[rr] broadcast: %d copies of %llu bytes unit=%d\n", m, (unsigned long long)(n * esz), unit);
   const hipError_t e = rr::launch_fanout(a, unit, t.nontemporal, t.grid_cap, t.copy_u, reinterpret_cast<hipStream_t>(stream));
@@ -955,7 +992,7 @@ rr_status_t rr_all_reduce_bucket(const void* const* sendbufs, void* const* recvb
   st = check_aliasing_sorted(outs, ins, [](const Range& o, const Range& i) { return o.rank == i.rank && o.lo == i.lo; });
   if (st) return st;
   if (total == 0) return ok();
-  const Tuning t = tuning();
+  const Tuning& t = tuning();
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const Kind k = kind_of(dtype);
   const uint64_t V = 16 / esz;
@@ -1090,7 +1127,7 @@ rr_status_t rr_all_gather_dim1(const void* const* sendbufs, void* const* recvbuf
   a.wu = w * esz / unit;
   a.du = cols * esz / unit;
   a.p = p;
-  const Tuning t = tuning();
+  const Tuning& t = tuning();
   if (t.log) fprintf(stderr, "[rr] all_gather_dim1: p=%d rows=%zu cols=%zu unit=%d\n", p, rows, cols, unit);
   const hipError_t e =
       rr::launch_gather_cols(a, unit, t.nontemporal, t.multi_per_cu, reinterpret_cast<hipStream_t>(stream));
@@ -1130,7 +1167,7 @@ rr_status_t rr_reduce_scatter_dim1(const void* const* sendbufs, void* const* rec
   a.du = cols * esz / unit;
   a.p = p;
   a.div = divisor_for(op, p);
-  const Tuning t = tuning();
+  const Tuning& t = tuning();
   if (t.log) fprintf(stderr, "[rr] reduce_scatter_dim1: p=%d rows=%zu cols=%zu vec=%d\n", p, rows, cols, vec ? 1 : 0);
   const hipError_t e = rr::launch_fold_cols(a, kind_of(dtype), op, vec ? 1 : 0, t.multi_per_cu,
                                             reinterpret_cast<hipStream_t>(stream));
@@ -1178,6 +1215,11 @@ rr_status_t rr_ring_exec_failures(int device, uint64_t* count) {
   if (e != hipSuccess) return hip_fail(e, "ring_exec_failures");
   *count = c;
   return ok();
+}
+
+void rr_reload_tuning(void) {
+  tuning();  // the first snapshot, if no call has taken it yet
+  publish_tuning();
 }
 
 const char* rr_last_error(void) { return g_last_error.c_str(); }

@@ -20,8 +20,9 @@
 //   t = 1..p-1     reduce-scatter step s = t-1: chunk c = (r-1-s) mod p,
 //                  work[q] = work[r] (+) work[q] on slice b (message first, as
 //                  the receiver of the ring accumulates); after the last one
-//                  rank q owns chunk q and finishes it (AVG's division, the
-//                  one rounding of 16-bit types) into its output;
+//                  (after the copy-in when p = 1) rank q owns chunk q and
+//                  finishes it (AVG's division, the one rounding of 16-bit
+//                  types) into its output;
 //   t = p..2p-2    all-gather step s = t-p: chunk c = (r-s) mod p,
 //                  out[q] = out[r] on slice b.
 // flag[q][b] counts the steps worker (b, q) has completed.  Step t of (b, q)
@@ -80,7 +81,8 @@ namespace rr {
 
 namespace {
 
-constexpr int kExecSlots = 16;
+constexpr int kExecStreamSlots = 16;  // slots [0, 16): one per stream with launches in flight
+constexpr int kExecSlots = 64;        // slots [16, 64): one per launch captured into a graph
 constexpr int kExecMaxWorkers = 2048;  // p * B per launch
 constexpr int kExecStride = 8;         // 64-bit words: one 64-byte line per flag
 constexpr int kExecShift = 24;         // flag = (tag << 24) + steps
@@ -283,25 +285,6 @@ __global__ __launch_bounds__(kBlock) void k_ring_exec(ExecArgs a) {
             store_group<false>(wq + i, m);
           },
           [&](uint64_t i) { store_one<EA>(wq + i, OP::apply(load_one<EA>(wr + i), load_one<EA>(lq + i))); });
-      if (t == p - 1 && (kSeparate || is_avg<OP>())) {
-        // rank q now owns chunk q: the op's last step, the one conversion
-        __syncthreads();
-        S* oq = static_cast<S*>(a.out[q]);
-        for_slice(
-            slice_lo(q), slice_hi(q), vec,
-            [&](uint64_t i) {
-              Raw<EA, 8> x;
-              load_group<false>(x, wq + i);
-              A v[8];
-              unpack(x, v);
-#pragma unroll
-              for (int j = 0; j < 8; ++j) v[j] = op_finish<OP>(v[j], a.div);
-              Raw<E, 8> y;
-              pack(v, y);
-              store_group<false>(oq + i, y);
-            },
-            [&](uint64_t i) { store_one<E>(oq + i, op_finish<OP>(load_one<EA>(wq + i), a.div)); });
-      }
     } else {
       // all-gather step s: rank q overwrites its copy of chunk c
       const int s = t - p;
@@ -317,6 +300,27 @@ __global__ __launch_bounds__(kBlock) void k_ring_exec(ExecArgs a) {
             store_group<false>(oq + i, x);
           },
           [&](uint64_t i) { oq[i] = orr[i]; });
+    }
+    if (t == p - 1 && (kSeparate || is_avg<OP>())) {
+      // rank q now owns chunk q (after the last reduce-scatter step, or
+      // after the copy-in when p = 1 and there is no such step): the op's
+      // last step, the one conversion
+      __syncthreads();
+      S* oq = static_cast<S*>(a.out[q]);
+      for_slice(
+          slice_lo(q), slice_hi(q), vec,
+          [&](uint64_t i) {
+            Raw<EA, 8> x;
+            load_group<false>(x, wq + i);
+            A v[8];
+            unpack(x, v);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = op_finish<OP>(v[j], a.div);
+            Raw<E, 8> y;
+            pack(v, y);
+            store_group<false>(oq + i, y);
+          },
+          [&](uint64_t i) { store_one<E>(oq + i, op_finish<OP>(load_one<EA>(wq + i), a.div)); });
     }
     // publish step t: every wave's stores acknowledged, then one release
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -337,15 +341,19 @@ __global__ __launch_bounds__(kBlock) void k_ring_exec(ExecArgs a) {
 
 constexpr int kMaxDevices = 64;
 
-// A slot's flags belong to one stream at a time.  `done` is recorded after
-// the slot's last eager launch; once it has completed, no launch uses the
-// slot any more and the next eager call returns it to the free list.  A slot
-// whose stream captured a launch into a graph stays with that stream
-// (replays may come at any time).
+// A slot's flags belong to one stream at a time, or to one captured launch.
+// `done` is recorded after the slot's last eager launch; once it has
+// completed, no launch uses the slot any more and the next eager call
+// returns it to the free list.  A launch captured into a graph takes a slot
+// of its own and keeps it for the rest of the process (`graph`): replays may
+// come at any time, on any stream, and two captured launches -- of one graph
+// or of two, even when captured on the same stream -- must never share
+// flags, since two graphs may be replayed at the same time.
 struct ExecSlot {
   hipStream_t owner = nullptr;
   bool used = false;
   bool pinned = false;
+  bool graph = false;
   hipEvent_t done = nullptr;
 };
 
@@ -373,17 +381,23 @@ void exec_release_done(ExecDevice& d) {
   }
 }
 
-// The slot of stream s: its own, else a free one (after releasing the
-// completed ones, when not capturing).  -1 when none is free.  Called with
+// The slot of an eager launch on stream s: the stream's own, else a free one
+// (after releasing the completed ones).  A captured launch always takes a
+// free slot of its own, pinned to it.  -1 when none is free.  Called with
 // d.mu held.
 int exec_slot_for(ExecDevice& d, hipStream_t s, bool captured) {
-  for (int i = 0; i < kExecSlots; ++i)
-    if (d.slots[i].used && d.slots[i].owner == s) return i;
-  if (!captured) exec_release_done(d);
-  for (int i = 0; i < kExecSlots; ++i) {
-    if (!d.slots[i].used) {
-      d.slots[i].used = true;
-      d.slots[i].owner = s;
+  if (!captured) {
+    for (int i = 0; i < kExecStreamSlots; ++i)
+      if (d.slots[i].used && d.slots[i].owner == s) return i;
+    exec_release_done(d);
+  }
+  for (int i = captured ? kExecStreamSlots : 0; i < (captured ? kExecSlots : kExecStreamSlots); ++i) {
+    ExecSlot& x = d.slots[i];
+    if (!x.used) {
+      x.used = true;
+      x.graph = captured;
+      x.pinned = captured;
+      x.owner = captured ? nullptr : s;
       return i;
     }
   }
@@ -447,7 +461,6 @@ hipError_t exec_go(ExecArgs a, int budget_per_cu_cap, int max_slices, int timeou
   if (captured) {
     a.captured = 1;
     a.tag = kExecCapturedTag;
-    slot.pinned = true;
     uint32_t sl = a.slot;
     int workers = slices * a.p;
     void* rp[] = {&sl, &workers};

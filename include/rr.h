@@ -80,9 +80,10 @@
  *    per-launch state in device memory (the soft barrier of the multi-round
  *    fused fold, the step flags of RR_ALGO_RING_PERSISTENT) detect capture,
  *    take a fixed tag, and capture a reset of that state just before
- *    themselves.  That state is kept per capturing stream: replay a graph on
- *    the stream it was captured on, or on a stream with no work of the same
- *    calls in flight.
+ *    themselves.  The executor's flags order data, so each captured
+ *    executor launch owns a slot of flags (see RR_ALGO_RING_PERSISTENT); the
+ *    barrier's counters order nothing and are kept per capturing stream
+ *    (sharing them only costs time).
  *  - Errors: return codes only.  All validation happens before the first
  *    launch, so a call that returns RR_ERROR_INVALID_ARGUMENT or
  *    RR_ERROR_UNSUPPORTED has written nothing.  A launch failure returns
@@ -190,12 +191,15 @@ rr_status_t rr_all_reduce(const void* const* sendbufs, void* const* recvbufs, in
  *     If a wait runs out (the workgroups were not all resident, e.g. other
  *     kernels filled the GPU), the launch stops and its outputs are
  *     incomplete; rr_ring_exec_failures() counts such launches.  Its step
- *     flags come in 16 slots per device, each used by one stream at a time:
- *     a stream keeps its slot while it has one, and every call that is not
- *     being captured frees the slots whose last launch has completed.  A
- *     call while 16 other streams hold slots with launches in flight (or
- *     pinned, below) returns RR_ERROR_HIP.  A slot whose stream captured a
- *     launch into a graph stays with that stream.
+ *     flags come in slots.  An eager launch uses its stream's slot, one of
+ *     16 per device: a stream keeps its slot while it has one, and every
+ *     call that is not being captured frees the slots whose last launch has
+ *     completed.  A launch captured into a graph takes a slot of its own,
+ *     one of 48 more per device, and keeps it for the rest of the process,
+ *     so that two captured launches never share flags (graphs captured on
+ *     one stream may be replayed concurrently on different streams); one
+ *     graph must not be replayed while an earlier replay of the same graph is
+ *     still running.  A call that finds no free slot returns RR_ERROR_HIP.
  *   group_size: 1 <= group_size <= p and group_size | p (HIER algos only).
  *   workspace: device memory of at least rr_workspace_size(algo, ...) bytes,
  *     16-byte aligned, owned by the caller, not aliasing any buffer; may be
@@ -241,8 +245,9 @@ rr_status_t rr_all_reduce_hier(const void* const* sendbufs, void* const* recvbuf
                                size_t workspace_bytes, rr_stream_t stream);
 
 /* Workspace bytes of rr_all_reduce_hier: 0 without RR_HIER_STAGED; else
- * (p/group_size)*n*4, or (p/group_size)*n*s with RR_HIER_WIRE_ROUND on a
- * 16-bit dtype.  0 for invalid arguments. */
+ * (p/group_size) group partials of n*4 bytes, or n*s with
+ * RR_HIER_WIRE_ROUND on a 16-bit dtype, each rounded up to a multiple of 16
+ * bytes (every partial starts 16-byte aligned).  0 for invalid arguments. */
 size_t rr_hier_workspace_size(int p, int group_size, size_t n, rr_dtype_t dtype, int flags);
 
 /*
@@ -358,9 +363,9 @@ rr_status_t rr_reduce_scatter_dim1(const void* const* sendbufs, void* const* rec
 /*
  * Workspace bytes that rr_all_reduce_ex needs for (algo, p, group_size, n,
  * dtype): 0 for the fused algorithms and for the staged ring on int32/float32;
- * p*n*4 for the staged ring on bfloat16 and float16; (p/group_size)*n*4 for
- * the staged hierarchy.  Returns 0 for invalid arguments as well (rr_all_reduce_ex then
- * reports them).
+ * p*n*4 for the staged ring on bfloat16 and float16; (p/group_size) times
+ * n*4 rounded up to a multiple of 16 for the staged hierarchy.  Returns 0 for
+ * invalid arguments as well (rr_all_reduce_ex then reports them).
  */
 size_t rr_workspace_size(rr_algo_t algo, int p, int group_size, size_t n, rr_dtype_t dtype);
 
@@ -453,6 +458,17 @@ rr_status_t rr_barrier_timeouts(int device, uint64_t* count);
  * a bad device.
  */
 rr_status_t rr_ring_exec_failures(int device, uint64_t* count);
+
+/*
+ * Tuning knobs (RR_* environment variables: tile depths, workgroups per
+ * compute unit, barrier and wait bounds, store policies, launch logging) are
+ * read from the environment once per process, at the first call of any entry
+ * point, never on the call path.  rr_reload_tuning() reads them again; calls
+ * that start after it returns use the new values (calls already in progress
+ * on other threads finish with the old ones).  No result depends on a knob:
+ * they select among schedules that compute the same bits.
+ */
+void rr_reload_tuning(void);
 
 /* Static description of a status code. */
 const char* rr_status_string(rr_status_t status);

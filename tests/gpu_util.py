@@ -66,3 +66,15 @@ def sample_positions(n, p, count, seed):
 def chunk_of(positions, n, p):
     b = np.array(C.chunk_bounds(n, p), dtype=np.int64)
     return np.searchsorted(b[1:], positions, side="right")
+
+
+def ring_fold_blocks(x, op, dtype, block=1 << 20):
+    """The oracle's ring-order fold of EVERY element of (p, n) inputs, in
+    blocks of at most ``block`` elements that each lie inside one chunk (so
+    that host memory stays bounded at full size).  Yields (lo, hi, result)."""
+    p, n = x.shape
+    b = C.chunk_bounds(n, p)
+    for c in range(p):
+        for lo in range(b[c], b[c + 1], block):
+            hi = min(lo + block, b[c + 1])
+            yield lo, hi, C.fold_elements_ring_order(x[:, lo:hi], np.full(hi - lo, c), op, dtype)

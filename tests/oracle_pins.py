@@ -284,6 +284,48 @@ def pin_bf16_vs_torch(seed=7, count=1 << 20):
     assert np.array_equal(B.narrow(f), want)
 
 
+def pin_bf16_ulp_distance(seed=5, count=1 << 16):
+    """The bf16 ulp distance that the "at most 1 bf16 ulp" tolerance is read
+    with: the number of steps between two values in the ordered list of all
+    distinct non-NaN bf16 values (+0 and -0 one value, the infinities at the
+    ends).  That list is built here by sorting every non-NaN pattern's value
+    (decoded by bit shifting, not by the oracle's codec); hand cases pin the
+    places where a sign-magnitude key goes wrong."""
+    hand = [
+        (0x3F80, 0x3F81, 1),  # 1 and its successor
+        (0xBF80, 0xBF81, 1),  # the same below zero
+        (0x0000, 0x8000, 0),  # +0 and -0 are one value
+        (0x0001, 0x8001, 2),  # smallest denormals of both signs: -d, 0, +d
+        (0x8000, 0x0001, 1),  # -0 to the smallest positive denormal
+        (0x7F7F, 0x7F80, 1),  # largest finite to +inf
+        (0xFF7F, 0xFF80, 1),  # most negative finite to -inf
+        (0x7F80, 0xFF80, 2 * 0x7F80),  # -inf to +inf spans the whole list
+        (0x4000, 0x3F80, 128),  # one binade of 7 mantissa bits: 1 -> 2
+    ]
+    a = np.array([h[0] for h in hand], dtype=np.uint16)
+    b = np.array([h[1] for h in hand], dtype=np.uint16)
+    want = np.array([h[2] for h in hand])
+    got = B.ulp_distance(a, b)
+    assert np.array_equal(got, want), list(zip(got.tolist(), want.tolist()))
+    # brute force: rank of each value among the distinct non-NaN values
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    keep = (pats & 0x7FFF) <= 0x7F80
+    vals = dec(pats[keep], "bfloat16")
+    distinct = np.unique(vals)  # -0.0 == +0.0: one entry
+    rank = dict(zip(pats[keep].tolist(), np.searchsorted(distinct, vals).tolist()))
+    rng = np.random.default_rng(seed)
+    pool = pats[keep]
+    x = rng.choice(pool, size=count)
+    y = rng.choice(pool, size=count)
+    # neighbours too, where an off-by-one would show
+    y[: count // 2] = np.clip(x[: count // 2].astype(np.int64) + rng.integers(-2, 3, size=count // 2), 0, 0xFFFF)
+    y = y.astype(np.uint16)
+    ok = (y & 0x7FFF) <= 0x7F80
+    x, y = x[ok], y[ok]
+    want = np.abs(np.array([rank[v] for v in x.tolist()]) - np.array([rank[v] for v in y.tolist()]))
+    assert np.array_equal(B.ulp_distance(x, y), want)
+
+
 # ---------------------------------------------------------------------------
 # Integer and max/min rules.
 

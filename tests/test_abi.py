@@ -170,6 +170,9 @@ def test_workspace_sizes():
     assert L.rr_workspace_size(3, 8, 4, 1000, 2) == 2 * 1000 * 4
     assert L.rr_workspace_size(3, 8, 2, 1000, 0) == 4 * 1000 * 4
     assert L.rr_workspace_size(3, 8, 3, 1000, 0) == 0  # invalid group
+    # the staged hierarchy's group partials each start on a 16-byte boundary
+    assert L.rr_workspace_size(3, 8, 4, 1001, 2) == 2 * 4016
+    assert L.rr_workspace_size(3, 6, 2, 4099, 1) == 3 * 16400
 
 
 def test_reduce_scatter_validation():
@@ -315,6 +318,8 @@ def test_hier_variant_validation():
     assert L.rr_hier_workspace_size(4, 2, 1000, 2, 6) == 2 * 1000 * 2  # bf16 partials on the wire
     assert L.rr_hier_workspace_size(4, 2, 1000, 1, 6) == 2 * 1000 * 4  # float32: rounding is the identity
     assert L.rr_hier_workspace_size(4, 3, 1000, 2, 4) == 0
+    assert L.rr_hier_workspace_size(4, 2, 1001, 2, 4) == 2 * 4016
+    assert L.rr_hier_workspace_size(4, 2, 1001, 2, 6) == 2 * 2016  # bf16 partials: 2002 bytes, rounded up
     assert L.rr_hier_workspace_size(4, 2, 1000, 2, 8) == 0
 
 

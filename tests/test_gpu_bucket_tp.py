@@ -118,7 +118,7 @@ def test_bucket_gpt2_block_full_size(rr):
     torch.cuda.empty_cache()
 
 
-def test_bucket_barrier(rr, monkeypatch):
+def test_bucket_barrier(rr, tuning):
     """A bucket of several rounds separates its read and write phases with
     the soft barrier.  A 1 us bound makes the waits run out: the results must
     not change and the timeouts must be counted.  Without the barrier, and
@@ -131,14 +131,14 @@ def test_bucket_barrier(rr, monkeypatch):
     t0 = rr.barrier_timeouts()
     check_bucket(run_bucket(rr, parts, "float32", "avg"), want, "default")
     assert rr.barrier_timeouts() == t0
-    monkeypatch.setenv("RR_MULTI_PER_CU", "64")
+    tuning.set("RR_MULTI_PER_CU", "64")
     check_bucket(run_bucket(rr, parts, "float32", "avg"), want, "64 workgroups per CU requested")
     assert rr.barrier_timeouts() == t0
-    monkeypatch.delenv("RR_MULTI_PER_CU")
-    monkeypatch.setenv("RR_PHASE_SYNC", "0")
+    tuning.unset("RR_MULTI_PER_CU")
+    tuning.set("RR_PHASE_SYNC", "0")
     check_bucket(run_bucket(rr, parts, "float32", "avg"), want, "no barrier")
-    monkeypatch.delenv("RR_PHASE_SYNC")
-    monkeypatch.setenv("RR_PHASE_TIMEOUT_US", "1")
+    tuning.unset("RR_PHASE_SYNC")
+    tuning.set("RR_PHASE_TIMEOUT_US", "1")
     for _ in range(2):
         check_bucket(run_bucket(rr, parts, "float32", "avg"), want, "1 us barrier bound")
     assert rr.barrier_timeouts() > t0, "the forced bound never ran out: the bucket's barrier was not exercised"
@@ -147,13 +147,13 @@ def test_bucket_barrier(rr, monkeypatch):
 
 @pytest.mark.parametrize("p", (5, 8))
 @pytest.mark.parametrize("strips", ("1", "2", "3", "8"))
-def test_bucket_interleaved_tiles(rr, monkeypatch, strips, p):
+def test_bucket_interleaved_tiles(rr, tuning, strips, p):
     """A multi-round bucket whose vector pieces hold whole tiles taken in runs
     of interleaved tiles (1 = contiguous), with ragged and unaligned tensors
     beside them: the oracle's bits for sum and max, and no wait runs out."""
     sizes = [3 * (1 << 20) + 5, 1 << 22, 777, 9 * 4096 + 8, (1 << 21) + 4]
     parts = [W.random_inputs(91 + i, p, n, "float32") for i, n in enumerate(sizes)]
-    monkeypatch.setenv("RR_PHASE_STRIPS", strips)
+    tuning.set("RR_PHASE_STRIPS", strips)
     t0 = rr.barrier_timeouts()
     for op in ("sum", "max"):
         check_bucket(run_bucket(rr, parts, "float32", op), C.all_reduce_bucket(parts, op, "float32"),

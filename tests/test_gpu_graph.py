@@ -211,3 +211,37 @@ def test_bucket_and_tp_layouts_graph(rr):
                      make, dtype, "bucket + dim-1 layouts")
     del g
     torch.cuda.empty_cache()
+
+
+def test_executor_graphs_replayed_concurrently(rr):
+    """Two graphs, each holding one persistent-executor all-reduce, captured
+    one after the other (on the same capture stream), then replayed at the
+    same time on two different streams, three times: each captured launch
+    owns its own step flags, so neither replay's flag reset or flags disturb
+    the other, and both give the oracle's bits with no wait timing out."""
+    p, n, dtype = 4, 65536 + 5, "float32"
+    tdt = torch_dtype(dtype)
+    xa, xb = (torch.zeros((p, n), dtype=tdt, device="cuda") for _ in range(2))
+    ya, yb = torch.zeros_like(xa), torch.zeros_like(xb)
+    ga = capture(lambda: rr.all_reduce(xa, ya, algo="ring_persistent"))
+    gb = capture(lambda: rr.all_reduce(xb, yb, algo="ring_persistent"))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    f0 = rr.ring_exec_failures()
+    for k in range(REPLAYS):
+        x1, x2 = inputs_for(200 + k, p, n, dtype), inputs_for(300 + k, p, n, dtype)
+        load(xa, x1, dtype)
+        load(xb, x2, dtype)
+        ya.fill_(0)
+        yb.fill_(0)
+        torch.cuda.synchronize()
+        # both streams start after the same short spin, so the replays overlap
+        for s, g in ((s1, ga), (s2, gb)):
+            with torch.cuda.stream(s):
+                torch.cuda._sleep(2_000_000)
+                g.replay()
+        torch.cuda.synchronize()
+        assert_bitwise(to_host(ya, dtype), C.all_reduce_ring(x1, "sum", dtype), f"graph a, replay {k}")
+        assert_bitwise(to_host(yb, dtype), C.all_reduce_ring(x2, "sum", dtype), f"graph b, replay {k}")
+    assert rr.ring_exec_failures() == f0, "an executor wait timed out"
+    del ga, gb
+    torch.cuda.empty_cache()

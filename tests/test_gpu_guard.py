@@ -1,0 +1,214 @@
+"""Stores stay inside their buffers.
+
+Every output (and every caller workspace) lives in one allocation with
+GUARD bytes of a sentinel before, between and after the buffers.  Each
+kernel family runs at shapes that take its partial and edge paths -- partial
+tiles, the heads and tails of chunks, interleaved tiles of multi-round
+launches, element pieces of a bucket, dim-1 rows, unaligned (scalar path)
+buffers, the staged and persistent ring's steps -- and afterwards the outputs
+must equal the oracle and every guard byte must still hold the sentinel.  A
+store past the end of one rank's buffer would otherwise land in the next
+rank's buffer, where the following kernel or the next rank's own output could
+hide it before the check.
+"""
+
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_util import assert_bitwise, to_dev, to_host, torch_dtype
+from oracle import collectives as C
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+GUARD = 4096
+SENTINEL = 0xA5
+ESZ = {"int32": 4, "float32": 4, "bfloat16": 2, "float16": 2}
+
+
+@pytest.fixture(scope="module")
+def rr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import collective_communication_reduction_way_amd as mod
+
+    mod.lib()
+    return mod
+
+
+class Guarded:
+    """Buffers of the given byte sizes in one sentinel-filled allocation,
+    GUARD bytes apart and from the ends; ``shift`` bytes moves every buffer
+    off 16-byte alignment (a multiple of the element size)."""
+
+    def __init__(self, sizes, dtype, shift=0):
+        self.sizes = list(sizes)
+        self.dtype = dtype
+        self.offsets = []
+        o = GUARD + shift
+        for nb in self.sizes:
+            self.offsets.append(o)
+            o += (nb + 255) // 256 * 256 + GUARD
+        self.total = o + GUARD
+        self.buf = torch.full((self.total,), SENTINEL, dtype=torch.uint8, device="cuda")
+
+    def view(self, i, shape=None):
+        o, nb = self.offsets[i], self.sizes[i]
+        t = self.buf[o:o + nb].view(torch_dtype(self.dtype))
+        return t if shape is None else t.view(shape)
+
+    def views(self, shape=None):
+        return [self.view(i, shape) for i in range(len(self.sizes))]
+
+    def check_guards(self, what):
+        host = self.buf.cpu().numpy()
+        owned = np.zeros(self.total, dtype=bool)
+        for o, nb in zip(self.offsets, self.sizes):
+            owned[o:o + nb] = True
+        bad = np.nonzero((host != SENTINEL) & ~owned)[0]
+        if bad.size:
+            # name the buffer whose end (or start) the first bad byte follows
+            first = int(bad[0])
+            after = max((i for i, o in enumerate(self.offsets) if o <= first), default=-1)
+            raise AssertionError(f"{what}: {bad.size} guard bytes overwritten, first at byte {first} "
+                                 f"(after buffer {after})")
+
+
+def host(t, dtype):
+    return to_host(t, dtype)
+
+
+def inputs(seed, p, n, dtype):
+    return W.random_inputs(seed, p, n, dtype, kind="full" if dtype == "int32" else "normal")
+
+
+# (algo, group, dtype, p, n, shift): the fused fold with edges and several
+# rounds, one-round 16-bit tiles with ragged chunks, the single-pass fold on
+# unaligned buffers, the staged and persistent rings, the staged hierarchy.
+AR_CASES = [
+    ("ring", 0, "float32", 8, 8 * (5 << 20) + 29, 0),
+    ("ring", 0, "bfloat16", 8, 8 * (3 << 20) + 13, 0),
+    ("ring", 0, "float16", 6, 6 * 70001 + 5, 0),
+    ("ring", 0, "float32", 5, 77777, 4),
+    ("ring", 0, "bfloat16", 3, 4099, 2),
+    ("hier", 4, "bfloat16", 8, 8 * (3 << 20) + 11, 0),
+    ("hier", 2, "float32", 8, 8 * (5 << 20) + 3, 0),
+    ("ring_staged", 0, "float32", 5, 5 * 4099 + 3, 0),
+    ("ring_staged", 0, "bfloat16", 8, 8 * 65536 + 7, 0),
+    ("ring_persistent", 0, "float32", 8, 8 * 65536 + 5, 0),
+    ("ring_persistent", 0, "bfloat16", 4, 100003, 0),
+    ("hier_staged", 2, "bfloat16", 8, 8 * 65536 + 9, 0),
+    ("hier_staged", 4, "float32", 8, 1001, 4),
+]
+
+
+@pytest.mark.parametrize("case", range(len(AR_CASES)))
+def test_all_reduce_stays_in_bounds(rr, case):
+    algo, G, dtype, p, n, shift = AR_CASES[case]
+    x = inputs(400 + case, p, n, dtype)
+    want = C.all_reduce_hier(x, "sum", dtype, G) if algo.startswith("hier") else C.all_reduce_fold(x, "sum", dtype)
+    tdt = torch_dtype(dtype)
+    # one allocation per rank input, shifted the same way as the outputs
+    k = shift // ESZ[dtype]
+    ins = [to_dev(np.concatenate([x[r, :k], x[r], x[r, :8]]), dtype)[k:k + n] for r in range(p)]
+    out = Guarded([n * ESZ[dtype]] * p, dtype, shift)
+    need = rr.workspace_size(algo, p, G, n, tdt)
+    ws = Guarded([need], "bfloat16") if need else None  # bytes only: the dtype sets nothing here
+    f0 = rr.ring_exec_failures()
+    rr.all_reduce(ins, out.views(), algo=algo, group_size=G,
+                  workspace=ws.buf[ws.offsets[0]:ws.offsets[0] + need] if ws else None)
+    torch.cuda.synchronize()
+    what = f"{algo} G={G} {dtype} p={p} n={n} shift={shift}"
+    out.check_guards(what + " outputs")
+    if ws:
+        ws.check_guards(what + " workspace")
+    got = np.stack([host(v, dtype) for v in out.views()])
+    assert_bitwise(got, want, what)
+    assert rr.ring_exec_failures() == f0
+
+
+@pytest.mark.parametrize("dtype,p,L", [("float32", 8, (1 << 20) + 3), ("bfloat16", 8, (3 << 18) + 5),
+                                       ("int32", 5, 4099)])
+def test_reduce_scatter_all_gather_reduce_stay_in_bounds(rr, dtype, p, L):
+    n = p * L
+    x = inputs(420, p, n, dtype)
+    xs = to_dev(x, dtype)
+    sh = Guarded([L * ESZ[dtype]] * p, dtype)
+    rr.reduce_scatter(xs, sh.views(), op="max")
+    torch.cuda.synchronize()
+    sh.check_guards(f"reduce_scatter {dtype} p={p} L={L}")
+    want_rs = C.reduce_scatter_ring(x, "max", dtype)
+    assert_bitwise(np.stack([host(v, dtype) for v in sh.views()]), want_rs, "reduce_scatter")
+    full = Guarded([n * ESZ[dtype]] * p, dtype)
+    rr.all_gather(sh.views(), full.views())
+    torch.cuda.synchronize()
+    full.check_guards(f"all_gather {dtype} p={p} L={L}")
+    assert_bitwise(np.stack([host(v, dtype) for v in full.views()]), C.all_gather(want_rs), "all_gather")
+    red = Guarded([n * ESZ[dtype]], dtype)
+    rr.reduce(xs, red.view(0), root=p - 1, op="sum")
+    torch.cuda.synchronize()
+    red.check_guards(f"reduce {dtype} p={p} L={L}")
+    assert_bitwise(host(red.view(0), dtype), C.reduce(x, "sum", dtype), "reduce")
+
+
+@pytest.mark.parametrize("nbytes", [3 * 16384 + 16 * 7, 3 * 16384 + 4 * 5, 1 << 22])
+def test_broadcast_scatter_gather_stay_in_bounds(rr, nbytes):
+    """Broadcast through the fan-out (16-byte units with a partial tile,
+    4-byte units), scatter and gather through the pair copies."""
+    p, dtype = 8, "float32"
+    n = nbytes // 4
+    n -= n % p
+    x = inputs(430, 1, n, dtype)[0]
+    src = to_dev(x, dtype)
+    bc = Guarded([n * 4] * p, dtype)
+    rr.broadcast(src, bc.views(), root=2)
+    torch.cuda.synchronize()
+    bc.check_guards(f"broadcast n={n}")
+    assert_bitwise(np.stack([host(v, dtype) for v in bc.views()]), C.broadcast(x, p), "broadcast")
+    sc = Guarded([n // p * 4] * p, dtype)
+    rr.scatter(src, sc.views(), root=1)
+    torch.cuda.synchronize()
+    sc.check_guards(f"scatter n={n}")
+    assert_bitwise(np.stack([host(v, dtype) for v in sc.views()]), C.scatter(x, p), "scatter")
+    ga = Guarded([n * 4], dtype)
+    rr.gather(sc.views(), ga.view(0), root=4)
+    torch.cuda.synchronize()
+    ga.check_guards(f"gather n={n}")
+    assert_bitwise(host(ga.view(0), dtype), x, "gather")
+
+
+def test_bucket_stays_in_bounds(rr):
+    """A bucket whose tensors end mid-tile, mid-group and mid-chunk, with one
+    tensor unaligned (element pieces): every output slot guarded."""
+    p, dtype = 8, "float32"
+    sizes = [3 * (1 << 20) + 5, 777, 1 << 21, 9 * 4096 + 3, 1]
+    parts = [inputs(440 + i, p, m, dtype) for i, m in enumerate(sizes)]
+    want = C.all_reduce_bucket(parts, "sum", dtype)
+    ins = [to_dev(t, dtype) for t in parts]
+    outs = [Guarded([m * 4] * p, dtype, shift=4 if i == 3 else 0) for i, m in enumerate(sizes)]
+    # the unaligned tensor's inputs are unaligned too: one element of filler first
+    ins[3] = [to_dev(np.concatenate([parts[3][r, :1], parts[3][r]]), dtype)[1:] for r in range(p)]
+    rr.all_reduce_bucket(ins, [o.views() for o in outs], op="sum")
+    torch.cuda.synchronize()
+    for i, (o, w) in enumerate(zip(outs, want)):
+        o.check_guards(f"bucket tensor {i} ({sizes[i]} elements)")
+        assert_bitwise(np.stack([host(v, dtype) for v in o.views()]), w, f"bucket tensor {i}")
+
+
+@pytest.mark.parametrize("dtype,rows,w", [("bfloat16", 33, 64), ("float32", 17, 5), ("bfloat16", 1029, 512)])
+def test_dim1_layouts_stay_in_bounds(rr, dtype, rows, w):
+    p = 8
+    xm = inputs(450, p, rows * p * w, dtype).reshape(p, rows, p * w)
+    want_rs = C.reduce_scatter_cols(xm, "sum", dtype)
+    rs = Guarded([rows * w * ESZ[dtype]] * p, dtype)
+    rr.reduce_scatter_dim1(to_dev(xm, dtype), rs.views((rows, w)))
+    torch.cuda.synchronize()
+    rs.check_guards(f"reduce_scatter_dim1 {dtype} [{rows}, {p}x{w}]")
+    assert_bitwise(np.stack([host(v, dtype) for v in rs.views((rows, w))]), want_rs, "reduce_scatter_dim1")
+    ag = Guarded([rows * p * w * ESZ[dtype]] * p, dtype)
+    rr.all_gather_dim1(rs.views((rows, w)), ag.views((rows, p * w)))
+    torch.cuda.synchronize()
+    ag.check_guards(f"all_gather_dim1 {dtype} [{rows}, {p}x{w}]")
+    assert_bitwise(np.stack([host(v, dtype) for v in ag.views((rows, p * w))]), C.all_gather_dim1(want_rs),
+                   "all_gather_dim1")

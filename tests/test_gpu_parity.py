@@ -17,7 +17,7 @@ import pytest
 
 import oracle_pins as PIN
 import workloads as W
-from gpu_util import assert_bitwise, chunk_of, sample_positions, to_dev, to_host
+from gpu_util import assert_bitwise, ring_fold_blocks, to_dev, to_host
 from oracle import bf16 as B
 from oracle import collectives as C
 
@@ -259,17 +259,17 @@ def test_workload_hier_bf16_p8g4(rr):
 
 @pytest.mark.parametrize("op", ("sum", "max", "min"))
 def test_workload_zero_bucket_fp32_p8(rr, op):
+    """The gradient bucket at full size (8 x 25,165,824 float32): the
+    reduce-scatter and the all-reduce against the oracle on every element
+    (the oracle folds in blocks of 2^20 elements to bound host memory), and
+    all-gather(reduce-scatter) == all-reduce on every element of every rank."""
     spec = W.WORKLOADS["zero_bucket_fp32_p8"]
     p, n = spec["p"], spec["n"]
     x = W.make_inputs("zero_bucket_fp32_p8")
     xs = to_dev(x, "float32")
-    pos = sample_positions(n, p, 1 << 20, seed=41)
-    want = C.fold_elements_ring_order(x[:, pos], chunk_of(pos, n, p), op, "float32")
     L = n // p
     sh = torch.empty((p, L), dtype=torch.float32, device="cuda")
     rr.reduce_scatter(xs, sh, op=op)
-    flat = rows(sh, "float32").reshape(-1)
-    assert_bitwise(flat[pos], want, "reduce_scatter (sampled)")
     full = torch.empty_like(xs)
     rr.all_gather(sh, full)
     ar = torch.empty_like(xs)
@@ -279,15 +279,17 @@ def test_workload_zero_bucket_fp32_p8(rr, op):
     assert torch.equal(full.view(torch.int32), ar.view(torch.int32))
     for r in range(1, p):
         assert torch.equal(ar[r].view(torch.int32), ar[0].view(torch.int32))
-    assert_bitwise(rows(ar[0], "float32")[pos], want, "all_reduce (sampled)")
-    # a full-size check of one chunk of every rank's shard against the oracle
-    c = 3
-    lo, hi = c * L, (c + 1) * L
-    want_c = C.fold_elements_ring_order(x[:, lo:hi], np.full(L, c), op, "float32")
-    assert_bitwise(rows(sh[c], "float32"), want_c, "reduce_scatter chunk 3 (full)")
+    flat = rows(sh, "float32").reshape(-1)  # rank c's shard is chunk c: the shards laid end to end
+    got = rows(ar[0], "float32")
+    for lo, hi, want in ring_fold_blocks(x, op, "float32"):
+        assert_bitwise(flat[lo:hi], want, f"reduce_scatter [{lo}, {hi})")
+        assert_bitwise(got[lo:hi], want, f"all_reduce [{lo}, {hi})")
 
 
 def test_workload_tp_rowparallel_bf16_p8(rr):
+    """The row-parallel partial outputs at full size (8 x (8, 2048, 4096)
+    bfloat16): every element of the all-reduce against the oracle (blocks of
+    2^20 elements), every rank identical."""
     spec = W.WORKLOADS["tp_rowparallel_bf16_p8"]
     p, n = spec["p"], spec["n"]
     x = W.make_inputs("tp_rowparallel_bf16_p8")
@@ -297,14 +299,9 @@ def test_workload_tp_rowparallel_bf16_p8(rr):
     torch.cuda.synchronize()
     for r in range(1, p):
         assert torch.equal(out[r].view(torch.int16), out[0].view(torch.int16))
-    pos = sample_positions(n, p, 1 << 20, seed=51)
-    want = C.fold_elements_ring_order(x[:, pos], chunk_of(pos, n, p), "sum", "bfloat16")
-    check_equal(rows(out[0], "bfloat16")[pos], want, "bfloat16", "all_reduce (sampled)")
-    # one full chunk
-    c = 5
-    b = C.chunk_bounds(n, p)
-    want_c = C.fold_elements_ring_order(x[:, b[c]:b[c + 1]], np.full(b[c + 1] - b[c], c), "sum", "bfloat16")
-    check_equal(rows(out[0], "bfloat16")[b[c]:b[c + 1]], want_c, "bfloat16", "all_reduce chunk 5 (full)")
+    got = rows(out[0], "bfloat16")
+    for lo, hi, want in ring_fold_blocks(x, "sum", "bfloat16"):
+        check_equal(got[lo:hi], want, "bfloat16", f"all_reduce [{lo}, {hi})")
 
 
 # ---------------------------------------------------------------------------
@@ -362,7 +359,7 @@ def test_sweep_reduce_scatter_all_gather(rr, p, L, dtype):
 
 @pytest.mark.parametrize("env", [{}, {"RR_COPY_U": "1"}, {"RR_COPY_U": "2"}, {"RR_COPY_U": "8"},
                                  {"RR_GRID_CAP": "37"}, {"RR_COPY_U": "2", "RR_GRID_CAP": "8192"}])
-def test_fanout_tilings_agree(rr, monkeypatch, env):
+def test_fanout_tilings_agree(rr, tuning, env):
     """All-gather and broadcast through every tile depth of the fan-out
     kernel, one tile per workgroup or a capped grid that strides over the
     tiles (a shard that is not a whole number of tiles): the oracle's bits."""
@@ -370,7 +367,7 @@ def test_fanout_tilings_agree(rr, monkeypatch, env):
     x = W.random_inputs(14, p, p * L, "float32")
     sh = C.reduce_scatter_ring(x, "sum", "float32")
     for k, v in env.items():
-        monkeypatch.setenv(k, v)
+        tuning.set(k, v)
     full = torch.empty((p, p * L), dtype=torch.float32, device="cuda")
     rr.all_gather(to_dev(sh, "float32"), full)
     assert_bitwise(rows(full, "float32"), C.all_gather(sh), f"all_gather {env}")
@@ -399,13 +396,16 @@ def test_fanout_store_policy_boundary(rr, L):
 
 
 @pytest.mark.parametrize("algo", ["ring_staged", "ring_persistent"])
-@pytest.mark.parametrize("p,n", [(2, 1001), (3, 4099), (5, 5 * 4096 + 7), (8, 8 * 65536 + 4)])
-@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("p,n", [(1, 1001), (1, 3 * 4096 + 5), (2, 1001), (3, 4099), (5, 5 * 4096 + 7),
+                                 (8, 8 * 65536 + 4)])
+@pytest.mark.parametrize("dtype", DTYPES + ("float16",))
 def test_staged_ring_reads_no_output_before_writing_it(rr, p, n, dtype, algo):
     """The staged ring and the persistent executor fold 4-byte types straight
     from the inputs (no copy into the outputs first): outputs filled with NaN
-    (all ones for int32) beforehand, one rank in place, every op -- the
-    oracle's bits."""
+    (all ones for int32) beforehand, one rank in place (none when p = 1, where
+    an in-place output would already hold the answer), every op -- the
+    oracle's bits.  p = 1 also checks that 16-bit outputs are written at all
+    (the one rank's finishing conversion with no reduce-scatter step)."""
     x = W.random_inputs(16, p, n, dtype, kind="full" if dtype == "int32" else "normal")
     f0 = rr.ring_exec_failures()
     for op in ("sum", "max", "min") + (("avg",) if dtype != "int32" else ()):
@@ -416,7 +416,8 @@ def test_staged_ring_reads_no_output_before_writing_it(rr, p, n, dtype, algo):
         else:
             out.fill_(float("nan"))
         outs = [out[r] for r in range(p)]
-        outs[p - 1] = xs[p - 1]  # in place for the last rank
+        if p > 1:
+            outs[p - 1] = xs[p - 1]  # in place for the last rank
         rr.all_reduce([xs[r] for r in range(p)], outs, op=op, algo=algo)
         got = np.stack([rows(o, dtype) for o in outs])
         ref = C.all_reduce_fold(x, op, dtype)

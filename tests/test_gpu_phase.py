@@ -64,13 +64,13 @@ def test_multi_round_ragged_hier(rr, dtype):
     torch.cuda.empty_cache()
 
 
-def test_forced_barrier_timeouts_keep_results(rr, monkeypatch):
+def test_forced_barrier_timeouts_keep_results(rr, tuning):
     """A 1 us bound makes the barrier waits run out; the results must not
     change, and the timeouts must be counted."""
     p, n = 8, 8 * (1 << 20) + 40
     x = W.random_inputs(63, p, n, "float32")
     want = C.all_reduce_fold(x, "sum", "float32")
-    monkeypatch.setenv("RR_PHASE_TIMEOUT_US", "1")
+    tuning.set("RR_PHASE_TIMEOUT_US", "1")
     t0 = rr.barrier_timeouts()
     for _ in range(3):
         assert_bitwise(run_ar(rr, x, "float32", "sum", "ring"), want, "ring with 1 us barrier bound")
@@ -78,13 +78,13 @@ def test_forced_barrier_timeouts_keep_results(rr, monkeypatch):
     torch.cuda.empty_cache()
 
 
-def test_oversized_grid_is_capped_to_residency(rr, monkeypatch):
+def test_oversized_grid_is_capped_to_residency(rr, tuning):
     """Asking for more workgroups per compute unit than fit at once must not
     leave the barrier waiting on workgroups that cannot run."""
     p, n = 8, 8 * (1 << 21)
     x = W.random_inputs(64, p, n, "bfloat16")
     want = C.all_reduce_fold(x, "sum", "bfloat16")
-    monkeypatch.setenv("RR_PHASE_PER_CU", "8")
+    tuning.set("RR_PHASE_PER_CU", "8")
     t0 = rr.barrier_timeouts()
     assert_bitwise(run_ar(rr, x, "bfloat16", "sum", "ring"), want, "ring, 8 workgroups per CU requested")
     assert rr.barrier_timeouts() == t0
@@ -93,7 +93,7 @@ def test_oversized_grid_is_capped_to_residency(rr, monkeypatch):
 
 @pytest.mark.parametrize("env", [{"RR_PHASE": "0"}, {"RR_PHASE_SYNC": "0"}, {"RR_PHASE_STATIC": "0"},
                                  {"RR_PHASE_STATIC": "1"}, {"RR_PHASE_U": "4"}, {"RR_PHASE_GRID": "37"}])
-def test_schedules_agree_bitwise(rr, monkeypatch, env):
+def test_schedules_agree_bitwise(rr, tuning, env):
     """Every schedule of the fused fold (single pass, phased with and without
     barrier, compiled or run-time rank loop, both tile sizes, an odd grid)
     gives the same bits."""
@@ -102,7 +102,7 @@ def test_schedules_agree_bitwise(rr, monkeypatch, env):
     want = C.all_reduce_fold(x, "sum", "float32")
     want_h = C.all_reduce_hier(x, "sum", "float32", 4)
     for k, v in env.items():
-        monkeypatch.setenv(k, v)
+        tuning.set(k, v)
     assert_bitwise(run_ar(rr, x, "float32", "sum", "ring"), want, f"ring {env}")
     assert_bitwise(run_ar(rr, x, "float32", "sum", "hier", 4), want_h, f"hier {env}")
     torch.cuda.empty_cache()
@@ -110,7 +110,7 @@ def test_schedules_agree_bitwise(rr, monkeypatch, env):
 
 @pytest.mark.parametrize("env", [{"RR_PHASE": "0"}, {}, {"RR_PHASE_SYNC": "0"}, {"RR_PHASE_STATIC": "0"},
                                  {"RR_PHASE_U": "4"}, {"RR_PHASE_GRID": "37"}, {"RR_PHASE_PER_CU": "8"}])
-def test_reduce_scatter_and_reduce_schedules_agree(rr, monkeypatch, env):
+def test_reduce_scatter_and_reduce_schedules_agree(rr, tuning, env):
     """Reduce-scatter (one chunk per rank) and reduce (one output) through the
     single-pass kernel and every schedule of the phased one, at a size that
     takes several rounds: the same bits as the oracle."""
@@ -120,7 +120,7 @@ def test_reduce_scatter_and_reduce_schedules_agree(rr, monkeypatch, env):
     want_rs = C.reduce_scatter_ring(x, "sum", "float32")
     want_red = C.reduce(x, "sum", "float32")
     for k, v in env.items():
-        monkeypatch.setenv(k, v)
+        tuning.set(k, v)
     t0 = rr.barrier_timeouts()
     xs = to_dev(x, "float32")
     sh = torch.empty((p, L), dtype=torch.float32, device="cuda")
@@ -191,13 +191,13 @@ STRIPED = [
 
 @pytest.mark.parametrize("strips", ("0", "1", "3", "8"))
 @pytest.mark.parametrize("coll,dtype,op,group,p,n", STRIPED)
-def test_interleaved_tiles(rr, monkeypatch, strips, coll, dtype, op, group, p, n):
+def test_interleaved_tiles(rr, tuning, strips, coll, dtype, op, group, p, n):
     """Every tile layout of the phased fold (the schedule's default, forced
     contiguous, runs of 3 and of 8 interleaved tiles) gives the oracle's
     bits; no barrier waits out its bound."""
     kind = "full" if dtype == "int32" else ("fp16_patterns" if dtype == "float16" else "normal")
     x = W.random_inputs(69, p, n, dtype, kind=kind)
-    monkeypatch.setenv("RR_PHASE_STRIPS", strips)
+    tuning.set("RR_PHASE_STRIPS", strips)
     t0 = rr.barrier_timeouts()
     what = f"{coll} {dtype} {op} p={p} n={n} strips={strips}"
     if coll == "ring":

@@ -73,21 +73,21 @@ def test_in_place_and_unaligned(rr, dtype):
     assert_bitwise(got, C.all_reduce_fold(np.ascontiguousarray(x[:, 1:1 + n]), "sum", dtype), "unaligned")
 
 
-def test_forced_timeout_ends_the_launch(rr, monkeypatch):
+def test_forced_timeout_ends_the_launch(rr, tuning):
     """A 1 us bound on every wait (set from the host) makes workers give up:
     the launch must end, be counted, and a following normal launch on the
     same stream must be correct."""
     p, n = 8, 8 * (1 << 20)
     x = W.random_inputs(83, p, n, "float32")
     f0 = rr.ring_exec_failures()
-    monkeypatch.setenv("RR_EXEC_TIMEOUT_US", "1")
+    tuning.set("RR_EXEC_TIMEOUT_US", "1")
     xs = to_dev(x, "float32")
     out = torch.empty_like(xs)
     for _ in range(3):
         rr.all_reduce(xs, out, algo="ring_persistent")
     torch.cuda.synchronize()
     assert rr.ring_exec_failures() > f0, "the 1 us bound never ran out"
-    monkeypatch.delenv("RR_EXEC_TIMEOUT_US")
+    tuning.unset("RR_EXEC_TIMEOUT_US")
     f1 = rr.ring_exec_failures()
     rr.all_reduce(xs, out, algo="ring_persistent")
     assert_bitwise(to_host(out, "float32"), C.all_reduce_fold(x, "sum", "float32"), "after the failed launches")

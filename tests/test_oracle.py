@@ -47,6 +47,10 @@ def test_bf16_nan():
     P.pin_bf16_nan()
 
 
+def test_bf16_ulp_distance():
+    P.pin_bf16_ulp_distance()
+
+
 def test_bf16_vs_torch():
     P.pin_bf16_vs_torch()
 

@@ -19,6 +19,13 @@ _finish = C.finish
 _hier = C.all_reduce_hier
 _fold = C.all_reduce_fold
 _h_narrow = H.narrow
+_ulp = B.ulp_distance
+
+
+def _ulp_key(key):
+    """An ulp distance built on another 16-bit key (planted mistakes)."""
+    return lambda a, b: np.abs(key(np.asarray(a, dtype=np.uint16).astype(np.int64)) -
+                               key(np.asarray(b, dtype=np.uint16).astype(np.int64)))
 
 
 def _run_all_pins():
@@ -33,6 +40,7 @@ def _run_all_pins():
         ("hier_probe", lambda: [P.pin_hier_probe(d) for d in ("float32", "bfloat16")]),
         ("bf16_hand", P.pin_bf16_rounding_hand),
         ("bf16_nan", P.pin_bf16_nan),
+        ("bf16_ulp", lambda: P.pin_bf16_ulp_distance(count=1 << 12)),
         ("bf16_torch", lambda: P.pin_bf16_vs_torch(count=1 << 18)),
         ("int32_wrap", P.pin_int32_wrap),
         ("signed_zero", P.pin_max_min_signed_zero),
@@ -279,6 +287,12 @@ MUTATIONS = {
     "cost_hier_ships_node_bytes": lambda m: m.setattr(
         K, "hier_all_reduce", lambda G, nb, fast, slow: (K.message(*slow, G * nb),
                                                          K.message(*fast, G * nb) + K.message(*slow, G * nb))),
+    "ulp_signed_zero_apart": lambda m: m.setattr(B, "ulp_distance", _ulp_key(
+        lambda h: np.where(h & 0x8000, -(h & 0x7FFF) - 1, h & 0x7FFF))),
+    "ulp_sign_ignored": lambda m: m.setattr(B, "ulp_distance", _ulp_key(lambda h: h & 0x7FFF)),
+    "ulp_unsigned_pattern": lambda m: m.setattr(B, "ulp_distance", _ulp_key(lambda h: h)),
+    "ulp_one_step_short": lambda m: m.setattr(B, "ulp_distance", lambda a, b: np.maximum(
+        _ulp(a, b) - (_ulp(a, b) > 1), 0)),
     "all_gather_reversed": lambda m: m.setattr(
         C, "all_gather", lambda sh: np.stack([np.concatenate(list(np.asarray(sh))[::-1])] * np.asarray(sh).shape[0])),
 }
