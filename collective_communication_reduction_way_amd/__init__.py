@@ -104,6 +104,7 @@ def lib():
     sig = {
         "rr_all_reduce": (I, [PP, PP, I, S, I, I, P]),
         "rr_all_reduce_ex": (I, [PP, PP, I, S, I, I, I, I, P, S, P]),
+        "rr_all_reduce_ex_noalloc": (I, [PP, PP, I, S, I, I, I, I, P]),
         "rr_reduce_scatter": (I, [PP, PP, I, S, I, I, P]),
         "rr_all_gather": (I, [PP, PP, I, S, I, P]),
         "rr_reduce": (I, [PP, P, I, I, S, I, I, P]),

@@ -32,6 +32,7 @@ SOURCES = [
     "rr_copy.hip",
     "rr_multi.hip",
     "rr_exec.hip",
+    "rr_scratch.hip",
     "rr_phase_ring.hip",
     "rr_phase_hier.hip",
     "rr_phase_hier_var.hip",

@@ -695,6 +695,14 @@ constexpr int kHierFlags = RR_HIER_INTRA_RING | RR_HIER_WIRE_ROUND | RR_HIER_STA
 
 }  // namespace
 
+namespace rr {
+
+// A failure message for rr_last_error() from the library's other
+// translation units (rr_scratch.hip).
+rr_status_t record_failure(rr_status_t st, const char* msg) { return fail(st, "%s", msg); }
+
+}  // namespace rr
+
 extern "C" {
 
 rr_status_t rr_all_reduce_ex(const void* const* sendbufs, void* const* recvbufs, int p, size_t n, rr_dtype_t dtype,

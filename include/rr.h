@@ -211,6 +211,37 @@ rr_status_t rr_all_reduce_ex(const void* const* sendbufs, void* const* recvbufs,
                              rr_dtype_t dtype, rr_op_t op, rr_algo_t algo, int group_size,
                              void* workspace, size_t workspace_bytes, rr_stream_t stream);
 
+/* Bytes of the library's fixed device scratch used by rr_all_reduce_ex_noalloc. */
+#define RR_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+/*
+ * rr_all_reduce_ex without a caller workspace, allocating nothing: for
+ * callers that cannot allocate device memory at the call (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments, results and errors as rr_all_reduce_ex, except that the
+ * workspace of the staged algorithms is a fixed array of
+ * RR_NOALLOC_SCRATCH_BYTES in the library's device memory, which each GPU the
+ * library runs on holds until the process ends.  The call makes no
+ * allocation of any kind (no hipMalloc, no allocating library routine).
+ *   algo: RR_ALGO_RING_FUSED and RR_ALGO_HIER_FUSED need no workspace and
+ *     behave exactly as in rr_all_reduce_ex; RR_ALGO_RING_STAGED and
+ *     RR_ALGO_HIER_STAGED use the scratch for what rr_workspace_size()
+ *     reports; RR_ALGO_RING_PERSISTENT -> RR_ERROR_UNSUPPORTED (its first
+ *     launch on a stream creates a completion event).
+ *   Returns RR_ERROR_INVALID_ARGUMENT, writing nothing, when
+ *   rr_workspace_size(algo, p, group_size, n, dtype) exceeds
+ *   RR_NOALLOC_SCRATCH_BYTES.
+ *   Every call on a GPU shares that GPU's scratch, which keeps the last
+ *   call's contents (the staged algorithms write every workspace element
+ *   before reading it, so nothing needs clearing).  Calls that overlap in
+ *   time on one GPU -- on different streams, or from different host threads
+ *   without ordering -- race on the scratch and give undefined results;
+ *   calls on one stream are ordered and safe.
+ */
+rr_status_t rr_all_reduce_ex_noalloc(const void* const* sendbufs, void* const* recvbufs, int p, size_t n,
+                                     rr_dtype_t dtype, rr_op_t op, rr_algo_t algo, int group_size,
+                                     rr_stream_t stream);
+
 /* Variant bits of rr_all_reduce_hier [HIER]. */
 #define RR_HIER_INTRA_RING 1 /* step 1 as a ring all-reduce inside each group */
 #define RR_HIER_WIRE_ROUND 2 /* group partials rounded to the storage type before crossing groups */

@@ -354,3 +354,27 @@ def test_dim1_validation():
     # (the shards are [3, 2]: 24 bytes of float32; an output 8 bytes in overlaps shard 0)
     bad = rr._ptr_array([FAKE + 8, FAKE + (2 << 30), FAKE + (3 << 30), FAKE + (4 << 30)])
     assert L.rr_all_gather_dim1(send, bad, 4, 3, 8, 1, None) == INVALID
+
+
+def test_noalloc_refusals_before_any_launch():
+    """rr_all_reduce_ex_noalloc refuses a workspace need above its fixed
+    scratch (RR_NOALLOC_SCRATCH_BYTES = 64 MiB) and the persistent executor,
+    and passes invalid arguments on to rr_all_reduce_ex's checks -- all
+    before any HIP call."""
+    L = rr.lib()
+    scratch = 64 << 20
+    p, dt_bf16, staged, hier_staged, persistent = 8, 2, 1, 3, 4
+    send, recv = ptrs(FAKE, p, 1 << 30), ptrs(FAKE + (64 << 30), p, 1 << 30)
+    n = scratch // (p * 4) + 8  # the staged ring's float32 partials: p*n*4 bytes
+    assert L.rr_workspace_size(staged, p, 0, n, dt_bf16) > scratch
+    assert L.rr_all_reduce_ex_noalloc(send, recv, p, n, dt_bf16, 0, staged, 0, None) == INVALID
+    assert b"scratch" in L.rr_last_error()
+    # the staged hierarchy: (p/G) partials of n*4 bytes, each rounded up to 16
+    n = scratch // 8 + 4
+    assert L.rr_all_reduce_ex_noalloc(send, recv, p, n, dt_bf16, 0, hier_staged, 2, None) == INVALID
+    assert b"scratch" in L.rr_last_error()
+    assert L.rr_all_reduce_ex_noalloc(send, recv, p, 1024, dt_bf16, 0, persistent, 0, None) == UNSUPPORTED
+    # invalid arguments reach rr_all_reduce_ex's own checks
+    assert L.rr_all_reduce_ex_noalloc(send, recv, 0, 1024, dt_bf16, 0, staged, 0, None) == INVALID
+    assert b"p=" in L.rr_last_error()
+    assert L.rr_all_reduce_ex_noalloc(send, recv, p, 1024, 9, 0, staged, 0, None) == UNSUPPORTED
