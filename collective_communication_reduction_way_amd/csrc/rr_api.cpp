@@ -77,7 +77,10 @@ int env_int(const char* name, int dflt) {
 // compute unit; 0 = as many as stay resident), RR_EXEC_SLICES (slices per
 // chunk, 1..64; default 64),
 // RR_COPY_U (16-byte units per lane of the all-gather and broadcast fan-out:
-// 1, 2, 4 or 8; default 4), RR_LOG (1 = print each launch plan to stderr).  Defaults are the measured
+// 1, 2, 4 or 8; default 4), RR_FANOUT_XCD (destinations per workgroup of the
+// XCD-laid-out fan-out: 1, 2 or 4; 0 = never; default by the bytes written),
+// RR_FANOUT_WIN (its blocks per XCD window; 0 = default),
+// RR_LOG (1 = print each launch plan to stderr).  Defaults are the measured
 // best on MI355X: every byte of these collectives is touched once, so
 // nontemporal access (no reuse expected) keeps the caches from holding dead
 // lines, and separating the read and write traffic of the fused folds in time
@@ -100,6 +103,8 @@ struct Tuning {
   int exec_per_cu;
   int exec_slices;
   int copy_u;
+  int fanout_xcd;
+  int fanout_win;
 };
 
 // The environment is read once per process, at the first call (or by
@@ -139,6 +144,10 @@ Tuning read_tuning() {
   if (t.exec_per_cu < 0) t.exec_per_cu = 0;
   t.exec_slices = env_int("RR_EXEC_SLICES", kExecDefaultSlices);
   t.copy_u = env_int("RR_COPY_U", 4);
+  t.fanout_xcd = env_int("RR_FANOUT_XCD", -1);
+  if (t.fanout_xcd != 0 && t.fanout_xcd != 1 && t.fanout_xcd != 2 && t.fanout_xcd != 4) t.fanout_xcd = -1;
+  t.fanout_win = env_int("RR_FANOUT_WIN", 0);
+  if (t.fanout_win < 0 || t.fanout_win > 4096) t.fanout_win = 0;
   return t;
 }
 
@@ -619,7 +628,7 @@ rr_status_t ar_hier_staged(const void* const* send, void* const* recv, int p, ui
       a.nseg = 1;
       a.ndst = G - 1;
       const int unit = copy_unit(addrs, {n * esz});
-      const hipError_t e = rr::launch_fanout(a, unit, t.nontemporal, t.grid_cap, t.copy_u, s);
+      const hipError_t e = rr::launch_fanout(a, unit, t.nontemporal, t.grid_cap, t.copy_u, t.fanout_xcd, t.fanout_win, s);
       if (e != hipSuccess) return hip_fail(e, "all_reduce(hierarchical, staged): group broadcast");
     }
   }
@@ -812,7 +821,8 @@ rr_status_t rr_all_gather(const void* const* sendbufs, void* const* recvbufs, in
   const Tuning& t = tuning();
   const int unit = copy_unit(addrs, {L * esz});
   if (t.log) fprintf(stderr, "[rr] all_gather: p=%d shard_bytes=%llu unit=%d\n", p, (unsigned long long)(L * esz), unit);
-  const hipError_t e = rr::launch_fanout(a, unit, t.nontemporal, t.grid_cap, t.copy_u, reinterpret_cast<hipStream_t>(stream));
+  const hipError_t e = rr::launch_fanout(a, unit, t.nontemporal, t.grid_cap, t.copy_u, t.fanout_xcd,
+                                       t.fanout_win, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "all_gather");
   return ok();
 }
@@ -887,7 +897,8 @@ rr_status_t rr_broadcast(const void* sendbuf, void* const* recvbufs, int root, i
   const Tuning& t = tuning();
   const int unit = copy_unit(addrs, {n * esz});
   if (t.log) fprintf(stderr, "[rr] broadcast: %d copies of %llu bytes unit=%d\n", m, (unsigned long long)(n * esz), unit);
-  const hipError_t e = rr::launch_fanout(a, unit, t.nontemporal, t.grid_cap, t.copy_u, reinterpret_cast<hipStream_t>(stream));
+  const hipError_t e = rr::launch_fanout(a, unit, t.nontemporal, t.grid_cap, t.copy_u, t.fanout_xcd,
+                                       t.fanout_win, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "broadcast");
   return ok();
 }

@@ -94,6 +94,56 @@ __global__ __launch_bounds__(kBlock) void k_fanout(FanoutArgs a) {
   }
 }
 
+// One-to-many copy laid out for the XCDs (16-byte units).  The sources are
+// cut into blocks of kBlock units (4 KiB); a workgroup copies one block to D
+// destinations and exits.  Block b belongs to XCD b mod kXcds; each XCD takes
+// its blocks in windows of W, and inside a window destination group by
+// destination group: W consecutive workgroups of the XCD write W consecutive
+// blocks to group g, the next W write the same blocks to group g + 1, and so
+// on.  The dispatcher deals workgroups to the XCDs in turn, so the workgroups
+// of a window run on one XCD close together: a block, read with ordinary
+// (cached) loads, comes from HBM once and from that XCD's L2 for the other
+// groups, and every workgroup writes one 4 KiB block per destination, the
+// store pattern at which HBM takes writes fastest.  Placement only affects
+// speed: a workgroup that runs elsewhere reads its block again, with the same
+// result.
+//
+// Workgroup w: x = w mod kXcds, j = w div kXcds, window v = j div (G W),
+// group g = (j mod (G W)) div W, block b = (v W + j mod W) kXcds + x, with
+// G = ceil(ndst / D); blocks are numbered segment by segment.  w ranges over
+// kXcds * W * G * ceil(ceil(blocks / kXcds) / W), so blocks past the last and
+// destinations past ndst exit.  The uniform block arithmetic is 32-bit (the
+// host launches this kernel only when the grid, hence every block index, is
+// below 2^31): no 64-bit comparison of uniform values steers a branch here.
+constexpr int kXcds = 8;
+
+template <int D>
+__global__ __launch_bounds__(kBlock) void k_fanout_xcd(FanoutArgs a, uint32_t blocks_per_seg, uint32_t blocks,
+                                                       uint32_t W) {
+  const uint32_t w = blockIdx.x;
+  const uint32_t x = w % kXcds;
+  const uint32_t j = w / kXcds;
+  const uint32_t G = (static_cast<uint32_t>(a.ndst) + D - 1) / D;
+  const uint32_t v = j / (G * W);
+  const uint32_t rem = j - v * G * W;
+  const uint32_t g = rem / W;
+  const uint32_t b = (v * W + (rem - g * W)) * kXcds + x;
+  if (b >= blocks) return;
+  const int seg = static_cast<int>(b / blocks_per_seg);
+  const uint64_t units = a.seg_bytes / 16;
+  const uint64_t i = static_cast<uint64_t>(b - static_cast<uint32_t>(seg) * blocks_per_seg) * kBlock + threadIdx.x;
+  if (i >= units) return;
+  const u32x4 val = static_cast<const u32x4*>(a.src[seg])[i];
+  const uint64_t dst_off = static_cast<uint64_t>(seg) * (a.dst_seg_stride / 16);
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    const int r = static_cast<int>(g) * D + d;
+    if (r >= a.ndst) break;
+    if (r == seg && ((a.skip_diag >> seg) & 1ull)) continue;
+    __builtin_nontemporal_store(val, static_cast<u32x4*>(a.dst[r]) + dst_off + i);
+  }
+}
+
 template <int B, bool NT>
 __global__ __launch_bounds__(kBlock) void k_copy_pairs(PairArgs a) {
   using T = typename UnitT<B>::T;
@@ -208,9 +258,46 @@ hipError_t ring_step_kind(const PairArgs& a, rr_op_t op, int grid_cap, hipStream
 }  // namespace
 
 hipError_t launch_fanout(const FanoutArgs& a, int unit_bytes, int nontemporal, int grid_cap, int units_per_lane,
-                         hipStream_t s) {
+                         int xcd_dst, int xcd_window, hipStream_t s) {
   const uint64_t units = a.seg_bytes / static_cast<uint64_t>(unit_bytes);
   const bool nt = nontemporal != 0;
+  if (unit_bytes == 16 && nt && grid_cap == 0 && xcd_dst != 0) {
+    // The XCD layout (k_fanout_xcd), two destinations per workgroup, windows
+    // of one block, for launches that write at least 192 MiB; smaller ones
+    // keep the tile kernel below.  Measured on MI355X against the tile
+    // kernel, % of the 8 TB/s HBM peak, the launch's buffers among two
+    // rotating sets: all-gather p = 8 at 24 / 32 / 64 / 96 / 128 MiB per rank
+    // 66.8 -> 80.7, 66.7 -> 78.4, 66.5 -> 76.5, 68.3 -> 86.6-87.4, 65.4 ->
+    // 73.6; broadcast p = 8 of 96 MiB 67.5 -> 72.6-86; p = 4, 96 MiB per rank
+    // 71.4 -> 74.1; p = 16, 48 MiB per rank 63.9 -> 81.4.  At 8 and 16 MiB
+    // per rank it lost (71.5 -> 55, 69 -> 67).  The layout is fast while the
+    // GPU's address translations of the buffers are cached: with a 4 GiB
+    // sweep of other memory between launches it falls to the tile kernel's
+    // rate (66-67%), where one destination per workgroup, faster still with
+    // warm translations (81-91%), falls to 46-49%; so two destinations it is.
+    const uint64_t written = a.seg_bytes * static_cast<uint64_t>(a.nseg) * static_cast<uint64_t>(a.ndst);
+    int D = xcd_dst;
+    if (D < 0) D = written >= (192ull << 20) ? 2 : 0;
+    const uint32_t W = xcd_window > 0 ? static_cast<uint32_t>(xcd_window) : 1u;
+    if (D == 1 || D == 2 || D == 4) {
+      const uint64_t bps = (units + kBlock - 1) / kBlock;
+      const uint64_t blocks = bps * static_cast<uint64_t>(a.nseg);
+      const uint64_t G = (static_cast<uint64_t>(a.ndst) + D - 1) / D;
+      const uint64_t per_xcd = (blocks + kXcds - 1) / kXcds;
+      const uint64_t grid = (per_xcd + W - 1) / W * W * G * kXcds;
+      if (grid <= 0x7FFFFFFFull) {
+        FanoutArgs copy = a;
+        uint32_t bps_arg = static_cast<uint32_t>(bps);
+        uint32_t blocks_arg = static_cast<uint32_t>(blocks);
+        uint32_t w_arg = W;
+        void* kp[] = {&copy, &bps_arg, &blocks_arg, &w_arg};
+        const void* k = D == 1 ? reinterpret_cast<const void*>(&k_fanout_xcd<1>)
+                               : (D == 2 ? reinterpret_cast<const void*>(&k_fanout_xcd<2>)
+                                         : reinterpret_cast<const void*>(&k_fanout_xcd<4>));
+        return hipLaunchKernel(k, dim3(static_cast<unsigned>(grid)), dim3(kBlock), kp, 0, s);
+      }
+    }
+  }
   if (unit_bytes == 16) {
     // 16-byte units: `units_per_lane` (1, 2, 4 or 8) per lane, and without a
     // cap one tile per workgroup.  A grid that strides leaves some

@@ -240,8 +240,12 @@ hipError_t launch_fold_hier_var(const FoldLaunch& f, hipStream_t stream);
 // of 16-byte units that writes at most 128 MiB; grid_cap 0 = the default
 // workgroup count (fan-out of 16-byte units: one tile per workgroup, with
 // units_per_lane units per lane, 4 unless 1, 2 or 8).
+// One source segment per seg to every destination.  xcd_dst: destinations
+// per workgroup of the XCD layout (1, 2 or 4), 0 = never, -1 = by the bytes
+// written; xcd_window: its blocks per XCD window (0 = default) (see
+// rr_copy.hip).
 hipError_t launch_fanout(const FanoutArgs& a, int unit_bytes, int nontemporal, int grid_cap, int units_per_lane,
-                         hipStream_t stream);
+                         int xcd_dst, int xcd_window, hipStream_t stream);
 // Plain copy: len[] in bytes.
 hipError_t launch_copy_pairs(const PairArgs& a, int unit_bytes, int nontemporal, int grid_cap, hipStream_t stream);
 // Element conversion (len[] in elements): 16-bit kinds <-> float32, or

@@ -129,7 +129,7 @@ def test_all_reduce_stays_in_bounds(rr, case):
 
 
 @pytest.mark.parametrize("dtype,p,L", [("float32", 8, (1 << 20) + 3), ("bfloat16", 8, (3 << 18) + 5),
-                                       ("int32", 5, 4099)])
+                                       ("int32", 5, 4099), ("float32", 8, (4 << 20) + 4)])
 def test_reduce_scatter_all_gather_reduce_stay_in_bounds(rr, dtype, p, L):
     n = p * L
     x = inputs(420, p, n, dtype)
@@ -152,10 +152,13 @@ def test_reduce_scatter_all_gather_reduce_stay_in_bounds(rr, dtype, p, L):
     assert_bitwise(host(red.view(0), dtype), C.reduce(x, "sum", dtype), "reduce")
 
 
+@pytest.mark.parametrize("xcd", ("-1", "1", "2"))
 @pytest.mark.parametrize("nbytes", [3 * 16384 + 16 * 7, 3 * 16384 + 4 * 5, 1 << 22])
-def test_broadcast_scatter_gather_stay_in_bounds(rr, nbytes):
-    """Broadcast through the fan-out (16-byte units with a partial tile,
-    4-byte units), scatter and gather through the pair copies."""
+def test_broadcast_scatter_gather_stay_in_bounds(rr, tuning, nbytes, xcd):
+    """Broadcast through the fan-out (16-byte units with a partial tile, also
+    through the XCD layout forced at this size, and 4-byte units), scatter
+    and gather through the pair copies."""
+    tuning.set("RR_FANOUT_XCD", xcd)
     p, dtype = 8, "float32"
     n = nbytes // 4
     n -= n % p

@@ -358,7 +358,10 @@ def test_sweep_reduce_scatter_all_gather(rr, p, L, dtype):
 
 
 @pytest.mark.parametrize("env", [{}, {"RR_COPY_U": "1"}, {"RR_COPY_U": "2"}, {"RR_COPY_U": "8"},
-                                 {"RR_GRID_CAP": "37"}, {"RR_COPY_U": "2", "RR_GRID_CAP": "8192"}])
+                                 {"RR_GRID_CAP": "37"}, {"RR_COPY_U": "2", "RR_GRID_CAP": "8192"},
+                                 {"RR_FANOUT_XCD": "1"}, {"RR_FANOUT_XCD": "2"}, {"RR_FANOUT_XCD": "4"},
+                                 {"RR_FANOUT_XCD": "0"}, {"RR_FANOUT_XCD": "1", "RR_FANOUT_WIN": "4"},
+                                 {"RR_FANOUT_XCD": "2", "RR_FANOUT_WIN": "3"}])
 def test_fanout_tilings_agree(rr, tuning, env):
     """All-gather and broadcast through every tile depth of the fan-out
     kernel, one tile per workgroup or a capped grid that strides over the
@@ -393,6 +396,33 @@ def test_fanout_store_policy_boundary(rr, L):
     assert_bitwise(rows(out, "float32"), C.broadcast(src, p), f"broadcast L={L}")
     del full, out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("xcd,win", (("1", "1"), ("2", "1"), ("4", "1"), ("1", "4"), ("2", "5"), ("4", "256")))
+@pytest.mark.parametrize("p", (8, 5, 3))
+def test_fanout_xcd_layout_in_place(rr, tuning, xcd, win, p):
+    """The XCD-laid-out fan-out (forced at a small size; destinations per
+    workgroup and blocks per window) for all-gather in place (each rank's
+    shard already in its slot, whose copy is skipped) and out of place, and
+    for broadcast with the root's copy in place: the oracle's bits, shards
+    with a partial 4 KiB block."""
+    tuning.set("RR_FANOUT_XCD", xcd)
+    tuning.set("RR_FANOUT_WIN", win)
+    L = 2 * 1024 + 8  # float32 shard: two 4 KiB blocks and 32 bytes
+    x = W.random_inputs(15, p, p * L, "float32")
+    sh = C.reduce_scatter_ring(x, "sum", "float32")
+    full = to_dev(np.zeros((p, p * L), dtype=np.float32), "float32")
+    for r in range(p):
+        full[r, r * L:(r + 1) * L] = to_dev(sh[r], "float32")
+    rr.all_gather([full[r, r * L:(r + 1) * L] for r in range(p)], full)
+    assert_bitwise(rows(full, "float32"), C.all_gather(sh), f"all_gather in place xcd={xcd} p={p}")
+    out = torch.empty((p, p * L), dtype=torch.float32, device="cuda")
+    rr.all_gather(to_dev(sh, "float32"), out)
+    assert_bitwise(rows(out, "float32"), C.all_gather(sh), f"all_gather xcd={xcd} p={p}")
+    bc = to_dev(x, "float32")
+    root = p // 2
+    rr.broadcast(bc[root], bc, root=root)
+    assert_bitwise(rows(bc, "float32"), C.broadcast(x[root], p), f"broadcast in place xcd={xcd} p={p}")
 
 
 @pytest.mark.parametrize("algo", ["ring_staged", "ring_persistent"])
