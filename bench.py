@@ -113,34 +113,28 @@ def load_traffic(workload):
 def ingest_pmc(workload, fetch_path, write_path):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the fused kernel, each
     scaled by what the same counter reads for the calibration copy of known
-    size, averaged over the profiled launches.  Reads rocprofv3's SQLite
-    output (*_results.db, view counters_collection) or its CSV output."""
-    import csv
+    size (the run's first librr copy dispatch, launched by
+    --calibration-copy before anything else of librr), averaged over the
+    profiled launches of the fused kernel.  Reads rocprofv3's SQLite output
+    (*_results.db, view counters_collection)."""
     import sqlite3
 
-    def per_kernel(path, counter):
-        out = {}
-        if path.endswith(".db"):
-            con = sqlite3.connect(path)
-            rows = con.execute("select kernel_name, counter_name, value from counters_collection").fetchall()
-            con.close()
-        else:
-            rows = [(r.get("Kernel_Name", ""), r.get("Counter_Name", counter), r.get("Counter_Value", "nan"))
-                    for r in csv.DictReader(open(path, encoding="utf-8"))]
-        for name, cname, val in rows:
-            if cname == counter:
-                out.setdefault(name, []).append(float(val))
-        return out
+    def dispatches(path, counter):
+        con = sqlite3.connect(path)
+        rows = con.execute("select dispatch_id, kernel_name, value from counters_collection where counter_name = ? "
+                           "order by dispatch_id", (counter,)).fetchall()
+        con.close()
+        return rows
 
     rec = {"workload": workload, "kernel_source_sha256": kernel_source_hash(), "counters": {}}
     total = 0.0
     for counter, path in (("FETCH_SIZE", fetch_path), ("WRITE_SIZE", write_path)):
-        k = per_kernel(path, counter)
-        calib = [v for n, vs in k.items() if "k_fanout" in n for v in vs]
-        fused = [v for n, vs in k.items() if "k_phase" in n for v in vs]
+        rows = dispatches(path, counter)
+        calib = [v for _, name, v in rows if "k_fanout" in name][:1]
+        fused = [v for _, name, v in rows if "k_phase" in name]
         if not calib or not fused:
             raise SystemExit(f"{path}: no calibration-copy or fused-kernel dispatches found")
-        calib_kib = max(calib)
+        calib_kib = calib[0]
         scale = CALIB_BYTES / (calib_kib * 1024.0)
         per_launch = sum(fused) / len(fused) * 1024.0 * scale
         rec["counters"][counter] = {"fused_kib_per_dispatch_mean": sum(fused) / len(fused),
@@ -749,6 +743,8 @@ def workload_lines(args, torch, rr, W, stream, cpm, report):
         for op in spec["ops"]:
             r = Runner(rr, torch, spec, "all_reduce", op, algo, spec.get("group", 0), x, sets, stream)
             report(f"all_reduce_{algo}_{op}", r, 200 if n * esz <= (8 << 20) else 40, True, name)
+            if n * esz * p <= (1 << 20):
+                call_latency(torch, r, stream, name)
             del r
             torch.cuda.empty_cache()
         if spec["coll"] == "rs_ag":
@@ -764,6 +760,24 @@ def workload_lines(args, torch, rr, W, stream, cpm, report):
             del r
             torch.cuda.empty_cache()
         del x
+
+
+def call_latency(torch, runner, stream, name, calls=2000):
+    """A launch-bound call: the host time of one librr call (validation, plan
+    and launch, through ctypes) over `calls` back-to-back calls, and the GPU
+    time per launch from events around 200 launches queued behind a spin."""
+    for i in range(20):
+        runner.step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(calls):
+        runner.step(i)
+    host_us = (time.perf_counter() - t0) / calls * 1e6
+    torch.cuda.synchronize()
+    spread = launch_spread(torch, runner, 200, stream, spin_cycles_per_ms(torch, stream))
+    print(json.dumps({"extra": "call_latency", "workload": name, "host_us_per_call": round(host_us, 3),
+                      "gpu_us_per_launch_median": round(spread["median_ms"] * 1e3, 3),
+                      "gpu_us_per_launch_min": round(spread["min_ms"] * 1e3, 3)}), file=sys.stderr, flush=True)
 
 
 class PairRunner:
