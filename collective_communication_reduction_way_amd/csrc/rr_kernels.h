@@ -119,6 +119,8 @@ struct PhaseTuning {
   int timeout_us;
   int static_p;  // 1 = the kernels compiled for p = 8 serve p = 8, 0 = the run-time loop, -1 = by mode
   int strips;    // tiles per run of interleaved tiles (PhaseArgs::strips); 1 = contiguous tiles, 0 = by mode
+  int batch;     // reduce-scatter / reduce: tiles per workgroup and round of the batched kernel (2, 4);
+                 // 1 = never batched, 0 = by the schedule
 };
 
 // Bucketed all-reduce (rr_multi.hip): the tensors of a bucket are folded as

@@ -90,6 +90,11 @@ hipError_t phase_timeouts_hier_var(unsigned long long* count);
 // set (rr_phase_one.hip).
 hipError_t phase_launch_one(const PhaseArgs& a, FoldMode m, Kind k, rr_op_t op, unsigned grid, int unroll, bool sync,
                             bool static_p, int* occ, hipStream_t s);
+// The same folds in batched rounds (k_phase_batch): `batch` (2 or 4) tiles of
+// 4 groups per lane per workgroup and round, the soft barrier between the
+// read and the write phase; the grid must be resident.
+hipError_t phase_launch_one_batch(const PhaseArgs& a, FoldMode m, Kind k, rr_op_t op, unsigned grid, int batch,
+                                  bool static_p, int* occ, hipStream_t s);
 hipError_t phase_timeouts_one(unsigned long long* count);
 
 }  // namespace rr

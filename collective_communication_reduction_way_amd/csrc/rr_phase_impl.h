@@ -284,6 +284,77 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(phase_wa
 }
 
 
+// Batched rounds for the folds that write one output per p inputs
+// (reduce-scatter, reduce).  Their reads alone stream at the read ceiling,
+// but the writes interleaved with them, though only 1/(p+1) of the bytes,
+// cost about ten points of the HBM peak (96 MiB float32 per rank: 86% with
+// the writes dropped, 75% with them).  So, like the folds that write every
+// rank, they separate the phases, with K tiles per round to keep the write
+// phase short against the barrier: in round r, workgroup b folds tiles
+// t = (r K + j) G + b for j < K, keeping the K results in registers, meets
+// the others at the soft barrier, then writes the K results.  Tiles are
+// contiguous (no interleaving); the barrier orders nothing the results depend
+// on, as in k_phase.
+template <class E, class OP, int P, int U, int K, FoldMode M>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void k_phase_batch(PhaseArgs a) {
+  using S = typename E::S;
+  using A = typename E::A;
+  constexpr int V = 16 / sizeof(S);
+  constexpr uint32_t kTile = kBlock * U;
+  static_assert(M == FoldMode::kRingShard || M == FoldMode::kAscOne, "one-output folds only");
+  const int p = P > 0 ? P : a.f.p;
+  sync_claim(a);
+  for (uint32_t r = 0; r < a.rounds; ++r) {
+    A acc[K][U][V];
+    int seg[K];
+    uint32_t valid[K];
+    uint64_t off[K];
+    uint64_t lo[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const uint32_t t = (r * K + j) * gridDim.x + blockIdx.x;
+      seg[j] = 0;
+      valid[j] = 0;
+      off[j] = 0;
+      lo[j] = 0;
+      if (t < a.tiles) {
+        uint32_t k;
+        if (a.uniform_tiles) {
+          seg[j] = static_cast<int>(t / a.uniform_tiles);
+          k = t - static_cast<uint32_t>(seg[j]) * a.uniform_tiles;
+          valid[j] = (k + 1 == a.uniform_tiles) ? a.uniform_last : kTile;
+          if constexpr (uses_bounds(M)) lo[j] = static_cast<uint64_t>(seg[j]) * a.seg_len;
+        } else {
+          int sg = 0;
+          while (a.seg_tile[sg + 1] <= t) ++sg;
+          seg[j] = sg;
+          k = t - a.seg_tile[sg];
+          valid[j] = (k + 1 == a.seg_tile[sg + 1] - a.seg_tile[sg]) ? a.seg_last[sg] : kTile;
+          if constexpr (uses_bounds(M)) lo[j] = a.f.bound[sg];
+        }
+        off[j] = ((lo[j] + V - 1) / V + static_cast<uint64_t>(k) * kTile) * 16;
+        read_fold<E, OP, P, U, M, false>(a.f, seg[j], p, off[j], valid[j], 0, acc[j]);
+      }
+    }
+    soft_barrier(a, r);
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      if (valid[j] == 0) continue;
+      Raw<E, V> o[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) pack(acc[j][u], o[u]);
+      // reduce-scatter outputs hold only the chunk: group g sits at g*V - lo
+      const uint64_t shift = (M == FoldMode::kRingShard) ? lo[j] * sizeof(S) : 0;
+      char* d = static_cast<char*>(a.f.out[seg[j]]) + (off[j] - shift);
+      if (valid[j] == kTile) {
+        store_tile<false, false>(d, o, valid[j], 0);
+      } else {
+        store_tile<true, false>(d, o, valid[j], 0);
+      }
+    }
+  }
+}
+
 // Heads and tails of the segments (fewer than V elements each), in the same
 // fold order: one workgroup per segment, 2V lanes.  Launched only when a
 // segment has any, after the phased fold on the same stream; the elements are
@@ -401,6 +472,55 @@ hipError_t phase_dispatch(const PhaseArgs& a, Kind k, rr_op_t op, unsigned grid,
   // modes exist for the 16-bit kinds only)
   if (k == Kind::kBF16) return phase_by_op<EBF16, M>(a, op, grid, unroll, sync, static_p, occ, s);
   if (k == Kind::kF16) return phase_by_op<EF16, M>(a, op, grid, unroll, sync, static_p, occ, s);
+  return hipErrorInvalidValue;
+}
+
+// The batched one-output kernels: K tiles of 4 groups per lane per round.
+template <class E, class OP, FoldMode M>
+hipError_t batch_by_p(const PhaseArgs& a, unsigned grid, int K, bool static_p, int* occ, hipStream_t s) {
+  hipError_t e;
+  if (static_p && a.f.p == 8) {
+    e = K == 2 ? phase_go(&k_phase_batch<E, OP, 8, 4, 2, M>, a, grid, kBlock, occ, s)
+               : phase_go(&k_phase_batch<E, OP, 8, 4, 4, M>, a, grid, kBlock, occ, s);
+  } else {
+    e = K == 2 ? phase_go(&k_phase_batch<E, OP, 0, 4, 2, M>, a, grid, kBlock, occ, s)
+               : phase_go(&k_phase_batch<E, OP, 0, 4, 4, M>, a, grid, kBlock, occ, s);
+  }
+  if (e != hipSuccess || occ || !a.edges) return e;
+  return phase_go(&k_edges<E, OP, M>, a, static_cast<unsigned>(a.segments), 64, nullptr, s);
+}
+
+template <class E, FoldMode M>
+hipError_t batch_by_op(const PhaseArgs& a, rr_op_t op, unsigned grid, int K, bool static_p, int* occ,
+                       hipStream_t s) {
+  switch (op) {
+    case RR_SUM: return batch_by_p<E, OpSum, M>(a, grid, K, static_p, occ, s);
+    case RR_MAX: return batch_by_p<E, OpMax, M>(a, grid, K, static_p, occ, s);
+    case RR_MIN: return batch_by_p<E, OpMin, M>(a, grid, K, static_p, occ, s);
+    case RR_AVG:
+      if constexpr (__is_same(typename E::A, float)) return batch_by_p<E, OpAvg, M>(a, grid, K, static_p, occ, s);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <FoldMode M>
+hipError_t batch_dispatch(const PhaseArgs& a, Kind k, rr_op_t op, unsigned grid, int K, bool static_p, int* occ,
+                          hipStream_t s) {
+  if (occ == nullptr && a.captured) {
+    // this translation unit's counters, cleared on the same stream first
+    SyncArgs y{};
+    y.slot = a.slot;
+    y.captured = 1;
+    const hipError_t e = sync_reset_if_captured(y, s);
+    if (e != hipSuccess) return e;
+  }
+  switch (k) {
+    case Kind::kI32: return batch_by_op<EI32, M>(a, op, grid, K, static_p, occ, s);
+    case Kind::kF32: return batch_by_op<EF32, M>(a, op, grid, K, static_p, occ, s);
+    case Kind::kBF16: return batch_by_op<EBF16, M>(a, op, grid, K, static_p, occ, s);
+    case Kind::kF16: return batch_by_op<EF16, M>(a, op, grid, K, static_p, occ, s);
+  }
   return hipErrorInvalidValue;
 }
 

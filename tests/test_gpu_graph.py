@@ -146,7 +146,8 @@ def test_hier_variants_graph(rr):
 
 def test_rs_ag_reduce_broadcast_graph(rr):
     """A sequence in one graph: reduce-scatter, all-gather of its shards,
-    reduce to a root and broadcast of the root's result."""
+    reduce to a root and broadcast of the root's result (32 MiB per rank:
+    reduce-scatter and reduce take the batched rounds behind the barrier)."""
     p, n, dtype = 8, 8 * 1048576 + 8 * 3, "float32"
     L = n // p
     tdt = torch_dtype(dtype)

@@ -109,11 +109,15 @@ def test_schedules_agree_bitwise(rr, tuning, env):
 
 
 @pytest.mark.parametrize("env", [{"RR_PHASE": "0"}, {}, {"RR_PHASE_SYNC": "0"}, {"RR_PHASE_STATIC": "0"},
-                                 {"RR_PHASE_U": "4"}, {"RR_PHASE_GRID": "37"}, {"RR_PHASE_PER_CU": "8"}])
+                                 {"RR_PHASE_U": "4"}, {"RR_PHASE_GRID": "37"}, {"RR_PHASE_PER_CU": "8"},
+                                 {"RR_PHASE_BATCH": "1"}, {"RR_PHASE_BATCH": "2"}, {"RR_PHASE_BATCH": "4"},
+                                 {"RR_PHASE_BATCH": "4", "RR_PHASE_PER_CU": "1"},
+                                 {"RR_PHASE_BATCH": "2", "RR_PHASE_STATIC": "0"}])
 def test_reduce_scatter_and_reduce_schedules_agree(rr, tuning, env):
     """Reduce-scatter (one chunk per rank) and reduce (one output) through the
-    single-pass kernel and every schedule of the phased one, at a size that
-    takes several rounds: the same bits as the oracle."""
+    single-pass kernel and every schedule of the phased one (with and without
+    the batched rounds), at a size that takes several rounds: the same bits as
+    the oracle."""
     p, L = 8, (1 << 20) + 8 * 3
     n = p * L
     x = W.random_inputs(66, p, n, "float32")
@@ -136,6 +140,33 @@ def test_reduce_scatter_and_reduce_schedules_agree(rr, tuning, env):
     if env.get("RR_PHASE_PER_CU") != "8":
         assert rr.barrier_timeouts() == t0
     del xs, sh, red, red_b
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("env", [{"RR_PHASE_BATCH": "2", "RR_PHASE_PER_CU": "1"},
+                                 {"RR_PHASE_BATCH": "4", "RR_PHASE_PER_CU": "1"}])
+@pytest.mark.parametrize("p,dtype,op", [(8, "float32", "sum"), (8, "float32", "max"), (8, "bfloat16", "sum"),
+                                        (8, "float16", "avg"), (8, "int32", "min"), (5, "float32", "sum")])
+def test_batched_rounds_ragged_chunks(rr, tuning, env, p, dtype, op):
+    """The batched reduce-scatter and reduce where the chunk boundaries fall
+    inside 16-byte groups (heads and tails, per-chunk tilings that differ),
+    with one workgroup per CU so that 8 MiB per rank already takes several
+    rounds: the same bits as the oracle."""
+    L = (1 << 19) + 5
+    n = p * L
+    x = W.random_inputs(68, p, n, dtype, kind="full" if dtype == "int32" else "normal")
+    for k, v in env.items():
+        tuning.set(k, v)
+    t0 = rr.barrier_timeouts()
+    xs = to_dev(x, dtype)
+    sh = torch.empty((p, L), dtype=xs.dtype, device="cuda")
+    rr.reduce_scatter(xs, sh, op=op)
+    assert_bitwise(to_host(sh, dtype), C.reduce_scatter_ring(x, op, dtype), f"reduce_scatter {p} {dtype} {op} {env}")
+    red = torch.empty(n, dtype=xs.dtype, device="cuda")
+    rr.reduce(xs, red, root=p - 1, op=op)
+    assert_bitwise(to_host(red, dtype), C.reduce(x, op, dtype), f"reduce {p} {dtype} {op} {env}")
+    assert rr.barrier_timeouts() == t0
+    del xs, sh, red
     torch.cuda.empty_cache()
 
 
