@@ -72,7 +72,8 @@ int env_int(const char* name, int dflt) {
 // RR_PHASE_STRIPS (runs of that many tiles whose 256-group strips
 // interleave, 1 = contiguous tiles, 0 = by the schedule), RR_PHASE_BATCH
 // (reduce-scatter and reduce: tiles per workgroup and round of the batched
-// kernel, 2 or 4; 1 = never; 0 = by the schedule),
+// kernel, 2 or 4; 1 = never; 0 = by the schedule), RR_AR_BATCH (the same
+// for the ring all-reduce of several rounds),
 // RR_MULTI_PER_CU (workgroups per compute unit of the bucket and dim-1
 // kernels; 0 = the default), RR_EXEC_TIMEOUT_US (bound of one wait of the persistent ring executor on a
 // neighbour's flag, default 1 s), RR_EXEC_PER_CU (cap on its workgroups per
@@ -138,6 +139,8 @@ Tuning read_tuning() {
   if (t.pt.strips < 0 || t.pt.strips > 16) t.pt.strips = 0;
   t.pt.batch = env_int("RR_PHASE_BATCH", 0);
   if (t.pt.batch != 1 && t.pt.batch != 2 && t.pt.batch != 4) t.pt.batch = 0;
+  t.pt.ar_batch = env_int("RR_AR_BATCH", 0);
+  if (t.pt.ar_batch != 1 && t.pt.ar_batch != 2 && t.pt.ar_batch != 4) t.pt.ar_batch = 0;
   if (t.pt.static_p > 1) t.pt.static_p = 1;
   if (t.pt.timeout_us < 1) t.pt.timeout_us = 200;
   t.multi_per_cu = env_int("RR_MULTI_PER_CU", 0);

@@ -121,6 +121,7 @@ struct PhaseTuning {
   int strips;    // tiles per run of interleaved tiles (PhaseArgs::strips); 1 = contiguous tiles, 0 = by mode
   int batch;     // reduce-scatter / reduce: tiles per workgroup and round of the batched kernel (2, 4);
                  // 1 = never batched, 0 = by the schedule
+  int ar_batch;  // ring all-reduce of several rounds: the same for its batched kernel
 };
 
 // Bucketed all-reduce (rr_multi.hip): the tensors of a bucket are folded as

@@ -144,6 +144,55 @@ hipError_t launch_mode(const FoldLaunch& f, const PhaseArgs& a, unsigned grid, i
   return hipErrorInvalidValue;
 }
 
+// The batched kernel (k_phase_batch) of a mode: launch, or only report its
+// occupancy when occ is not NULL.
+hipError_t launch_batch_mode(const FoldLaunch& f, const PhaseArgs& a, unsigned grid, int K, bool sp, int* occ,
+                             hipStream_t s) {
+  if (f.mode == FoldMode::kRingAll) return phase_launch_ring_batch(a, f.in_kind, f.op, grid, K, sp, occ, s);
+  return phase_launch_one_batch(a, f.mode, f.in_kind, f.op, grid, K, sp, occ, s);
+}
+
+// Workgroups of the batched kernel that fit on one compute unit, cached per
+// device and kernel.
+hipError_t batch_occupancy(DeviceState& d, const FoldLaunch& f, const PhaseArgs& a, int K, bool sp, hipStream_t s,
+                           int* occ) {
+  const uint32_t key = 0x80000000u | (static_cast<uint32_t>(f.mode) << 16) |
+                       (static_cast<uint32_t>(f.in_kind) << 12) | (static_cast<uint32_t>(f.op) << 8) |
+                       (static_cast<uint32_t>(K) << 4) | (sp ? 1u : 0u);
+  {
+    std::lock_guard<std::mutex> lock(d.mu);
+    auto it = d.occupancy.find(key);
+    if (it != d.occupancy.end()) {
+      *occ = it->second;
+      return hipSuccess;
+    }
+  }
+  int o = 0;
+  const hipError_t e = launch_batch_mode(f, a, 1, K, sp, &o, s);
+  if (e != hipSuccess) return e;
+  if (o < 1) o = 1;
+  std::lock_guard<std::mutex> lock(d.mu);
+  d.occupancy[key] = o;
+  *occ = o;
+  return hipSuccess;
+}
+
+// Launch the batched kernel on `resident` workgroups (all resident at once),
+// with a barrier slot of stream s.
+hipError_t launch_batched(DeviceState& d, const FoldLaunch& f, const PhaseArgs& a, uint64_t tiles, uint64_t resident,
+                          int K, bool sp, const PhaseTuning& pt, hipStream_t s) {
+  PhaseArgs b = a;
+  b.rounds = static_cast<uint32_t>((tiles + resident * K - 1) / (resident * K));
+  SyncArgs y;
+  const hipError_t e = sync_args_on(d, s, pt.timeout_us, &y);
+  if (e != hipSuccess) return e;
+  b.slot = y.slot;
+  b.tag = y.tag;
+  b.timeout_ticks = y.timeout_ticks;
+  b.captured = y.captured;
+  return launch_batch_mode(f, b, static_cast<unsigned>(resident), K, sp, nullptr, s);
+}
+
 }  // namespace
 
 int phase_default_unroll(Kind k, FoldMode m) { return (is_hier(m) && is_half(k)) ? 4 : 8; }
@@ -161,9 +210,11 @@ bool phase_supported(const FoldLaunch& f) {
 //     kernel compiled for p = 8 when p is 8 (float16: the run-time loop);
 //     fewer 8-group tiles than CUs (16-bit types: than 2 per CU): 4 groups
 //     per lane, then 2 and 1 while the tiles still fit one per CU;
-//   ring all-reduce, several rounds: 4 groups per lane, 4 workgroups per CU
-//     (shorter phases between barriers); the kernel compiled for p = 8 for
-//     bfloat16, the run-time rank loop for the other types;
+//   ring all-reduce, several rounds: 4 groups per lane; with at least one
+//     full round of 4 tiles per workgroup at 2 workgroups per CU, the batched
+//     kernel (below), else 4 workgroups per CU of one tile each (shorter
+//     phases between barriers), the kernel compiled for p = 8 for bfloat16,
+//     the run-time rank loop for the other types;
 //   hierarchical all-reduce: the run-time rank loop, 4 workgroups per CU with
 //     the 16-bit tile of 4 groups per lane, else 2;
 //   reduce-scatter and reduce: 4 groups per lane; with at least one full
@@ -209,8 +260,10 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
   uint64_t tiles = tile_segments(f, V, static_cast<uint64_t>(kBlock) * unroll, a);
   if (tiles >= 0x7FFFFFFFull) return hipErrorInvalidValue;
   uint64_t grid = pt.grid > 0 ? static_cast<uint64_t>(pt.grid) : cus * static_cast<uint64_t>(per_cu);
+  bool several = false;  // ring all-reduce of several rounds, default tiling
   if (ring && pt.unroll == 0 && pt.grid == 0 && small_ok && unroll == 8 && tiles > grid) {
     // several rounds: the smaller tile, more workgroups
+    several = true;
     unroll = 4;
     if (pt.per_cu <= 0) per_cu = 4;
     if (pt.static_p < 0) static_p = f.in_kind == Kind::kBF16;
@@ -239,6 +292,49 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
     if (pt.static_p < 0) static_p = tiles <= cus;
     grid = cus * static_cast<uint64_t>(per_cu);
   }
+  if (several && pt.ar_batch != 1 && pt.sync && tiles <= kMaxBarrierTiles) {
+    // The ring all-reduce of several rounds in batched rounds (k_phase_batch):
+    // K tiles of 4 groups per lane per workgroup and round at 2 or 3
+    // workgroups per CU, interleaved in runs, the write phase output by
+    // output.  Measured
+    // through this library on one MI355X, p = 8, against one tile per
+    // workgroup and round at 4 per CU: float32 32 MiB per rank 75.5% ->
+    // 80.4-81.8% of the HBM peak, 96 MiB 76% -> 78.3-78.5%, 128 MiB 76.5% ->
+    // 78.2-78.6%; bfloat16 128 MiB 77% -> 78.8-79.1%.
+    const bool sp = (pt.static_p >= 0 ? pt.static_p != 0 : !f16) && f.args.p == 8;
+    const int K = pt.ar_batch == 2 || pt.ar_batch == 4 ? pt.ar_batch : 4;
+    int occ = 0;
+    e = batch_occupancy(d, f, a, K, sp, s, &occ);
+    if (e != hipSuccess) return e;
+    // Workgroups per CU: as asked, else 3 or 2 (as many as stay resident),
+    // whichever leaves fewer empty tile slots in the last round, ties to the
+    // fewer rounds.  Full rounds measured best: float32 48 MiB per rank in one
+    // round at 3 per CU 81.6%, in two at 2 per CU (the second half empty)
+    // 78.5%; 32 MiB in one round at 2 per CU 81.7%.
+    uint64_t per_cu_b = 0;
+    uint64_t best_waste = ~0ull;
+    const int asked[2] = {pt.per_cu > 0 ? pt.per_cu : 3, pt.per_cu > 0 ? pt.per_cu : 2};
+    for (int c : asked) {
+      const uint64_t pc = static_cast<uint64_t>(c < occ ? c : occ);
+      const uint64_t slots = cus * pc * static_cast<uint64_t>(K);
+      if (tiles < slots) continue;  // not even one full round
+      const uint64_t waste = (tiles + slots - 1) / slots * slots - tiles;
+      if (waste < best_waste) {
+        best_waste = waste;
+        per_cu_b = pc;
+      }
+    }
+    if (per_cu_b > 0) {
+      const int strips = pt.strips > 0 ? pt.strips : 8;
+      if (strips > 1 && a.uniform_tiles != 0) {
+        const uint32_t tile = static_cast<uint32_t>(kBlock * unroll);
+        const uint32_t full = a.uniform_last == tile ? a.uniform_tiles : a.uniform_tiles - 1;
+        a.strips = static_cast<uint32_t>(strips);
+        a.strip_tiles = full - full % a.strips;
+      }
+      return launch_batched(d, f, a, tiles, cus * per_cu_b, K, sp, pt, s);
+    }
+  }
   if (one_out && pt.batch != 1 && pt.unroll == 0 && pt.grid == 0 && pt.sync && unroll == 4 &&
       tiles <= kMaxBarrierTiles) {
     // Reduce-scatter and reduce with at least one full round of K tiles per
@@ -251,42 +347,16 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
     // 16 MiB and below (less than one full round) the batches lost.
     const int K = pt.batch == 2 || pt.batch == 4 ? pt.batch : 4;
     const bool sp = static_p && f.args.p == 8;
-    const uint32_t key = 0x80000000u | (static_cast<uint32_t>(f.mode) << 16) |
-                         (static_cast<uint32_t>(f.in_kind) << 12) | (static_cast<uint32_t>(f.op) << 8) |
-                         (static_cast<uint32_t>(K) << 4) | (sp ? 1u : 0u);
     int occ = 0;
-    {
-      std::lock_guard<std::mutex> lock(d.mu);
-      auto it = d.occupancy.find(key);
-      if (it != d.occupancy.end()) occ = it->second;
-    }
-    if (occ == 0) {
-      e = phase_launch_one_batch(a, f.mode, f.in_kind, f.op, 1, K, sp, &occ, s);
-      if (e != hipSuccess) return e;
-      if (occ < 1) occ = 1;
-      std::lock_guard<std::mutex> lock(d.mu);
-      d.occupancy[key] = occ;
-    }
+    e = batch_occupancy(d, f, a, K, sp, s, &occ);
+    if (e != hipSuccess) return e;
     // Two workgroups per CU unless asked otherwise, never more than stay
     // resident: 4 per CU measured worse for float32 (128 MiB per rank, two
     // full rounds: 77% against 80% with 2 per CU) and no better for
     // bfloat16.
     const int want = pt.per_cu > 0 ? pt.per_cu : 2;
-    uint64_t per_cu_b = static_cast<uint64_t>(want < occ ? want : occ);
-    if (tiles < cus * per_cu_b * static_cast<uint64_t>(K)) per_cu_b = 0;  // not one full round
-    if (per_cu_b > 0) {
-      const uint64_t resident = cus * per_cu_b;
-      PhaseArgs b = a;
-      b.rounds = static_cast<uint32_t>((tiles + resident * K - 1) / (resident * K));
-      SyncArgs y;
-      e = sync_args_on(d, s, pt.timeout_us, &y);
-      if (e != hipSuccess) return e;
-      b.slot = y.slot;
-      b.tag = y.tag;
-      b.timeout_ticks = y.timeout_ticks;
-      b.captured = y.captured;
-      return phase_launch_one_batch(b, f.mode, f.in_kind, f.op, static_cast<unsigned>(resident), K, sp, nullptr, s);
-    }
+    const uint64_t per_cu_b = static_cast<uint64_t>(want < occ ? want : occ);
+    if (tiles >= cus * per_cu_b * static_cast<uint64_t>(K)) return launch_batched(d, f, a, tiles, cus * per_cu_b, K, sp, pt, s);
   }
   if (one_out && pt.unroll == 0 && pt.grid == 0 && unroll == 4) {
     // reduce-scatter and reduce too small for a tile of 4 groups per lane on

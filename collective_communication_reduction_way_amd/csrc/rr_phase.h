@@ -75,6 +75,12 @@ int phase_default_unroll(Kind k, FoldMode m);
 // the selected kernel fit on one compute unit.
 hipError_t phase_launch_ring(const PhaseArgs& a, Kind k, rr_op_t op, unsigned grid, int unroll, bool sync,
                              bool static_p, int* occ, hipStream_t s);
+// The ring all-reduce in batched rounds (k_phase_batch): `batch` (2 or 4)
+// tiles of 4 groups per lane per workgroup and round, interleaved in runs of
+// PhaseArgs::strips tiles, the soft barrier between the phases; the grid must
+// be resident.
+hipError_t phase_launch_ring_batch(const PhaseArgs& a, Kind k, rr_op_t op, unsigned grid, int batch, bool static_p,
+                                   int* occ, hipStream_t s);
 hipError_t phase_launch_hier(const PhaseArgs& a, Kind k, rr_op_t op, unsigned grid, int unroll, bool sync,
                              bool static_p, int* occ, hipStream_t s);
 // The hierarchical variants (kHierRing, kHierAllWire, kHierRingWire), run-time

@@ -171,6 +171,25 @@ __device__ __forceinline__ void store_tile(char* base, const Raw<E, V> (&o)[U], 
   }
 }
 
+// Store drain between the outputs of the folds that write every rank, in the
+// launches without the barrier (one round): each wave waits until its stores
+// to one output have left before it issues those to the next, so that the
+// chip writes one output's region at a time instead of spreading its writes
+// over all p buffers while other workgroups still read.  Measured through
+// this library on one MI355X, p = 8: 16 MiB float32 per rank 71% -> 75.7% of
+// the HBM peak, 8 MiB bfloat16 72.5% -> 74%, the 8 MiB bfloat16 hierarchy
+// 75.3% -> 76.5%.  With the barrier (the write phase already separate) it
+// lost 0.5-2 points, so those kernels are compiled without it.
+// RR_DRAIN_STORES=0 at build time compiles it out (for comparisons).
+#ifndef RR_DRAIN_STORES
+#define RR_DRAIN_STORES 1
+#endif
+__device__ __forceinline__ void drain_stores() {
+#if RR_DRAIN_STORES
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#endif
+}
+
 // Waves per SIMD that the register allocation must leave room for (1 = no
 // bound).  For the 4-byte types of the modes without running totals a bound
 // of three keeps more loads in flight than the allocation the scheduler picks
@@ -259,15 +278,27 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(phase_wa
           for (int q = 0; q < P; ++q) dst[q] = static_cast<char*>(a.f.out[q]) + off;
           if (valid == kTile) {
 #pragma unroll
-            for (int q = 0; q < P; ++q) store_tile<false, IL>(dst[q], o, valid, gap);
+            for (int q = 0; q < P; ++q) {
+              store_tile<false, IL>(dst[q], o, valid, gap);
+              if constexpr (!SYNC) drain_stores();
+            }
           } else {
 #pragma unroll
-            for (int q = 0; q < P; ++q) store_tile<true, IL>(dst[q], o, valid, gap);
+            for (int q = 0; q < P; ++q) {
+              store_tile<true, IL>(dst[q], o, valid, gap);
+              if constexpr (!SYNC) drain_stores();
+            }
           }
         } else if (valid == kTile) {
-          for (int q = 0; q < p; ++q) store_tile<false, IL>(static_cast<char*>(a.f.out[q]) + off, o, valid, gap);
+          for (int q = 0; q < p; ++q) {
+            store_tile<false, IL>(static_cast<char*>(a.f.out[q]) + off, o, valid, gap);
+            if constexpr (!SYNC) drain_stores();
+          }
         } else {
-          for (int q = 0; q < p; ++q) store_tile<true, IL>(static_cast<char*>(a.f.out[q]) + off, o, valid, gap);
+          for (int q = 0; q < p; ++q) {
+            store_tile<true, IL>(static_cast<char*>(a.f.out[q]) + off, o, valid, gap);
+            if constexpr (!SYNC) drain_stores();
+          }
         }
       } else {
         // reduce-scatter outputs hold only the chunk: group g sits at g*V - lo
@@ -284,30 +315,35 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(phase_wa
 }
 
 
-// Batched rounds for the folds that write one output per p inputs
-// (reduce-scatter, reduce).  Their reads alone stream at the read ceiling,
-// but the writes interleaved with them, though only 1/(p+1) of the bytes,
-// cost about ten points of the HBM peak (96 MiB float32 per rank: 86% with
-// the writes dropped, 75% with them).  So, like the folds that write every
-// rank, they separate the phases, with K tiles per round to keep the write
-// phase short against the barrier: in round r, workgroup b folds tiles
-// t = (r K + j) G + b for j < K, keeping the K results in registers, meets
-// the others at the soft barrier, then writes the K results.  Tiles are
-// contiguous (no interleaving); the barrier orders nothing the results depend
-// on, as in k_phase.
+// Batched rounds: in round r, workgroup b folds tiles t = (r K + j) G + b for
+// j < K, keeping the K results in registers, meets the others at the soft
+// barrier, then writes the K results.  Fewer, larger rounds than k_phase,
+// with more loads in flight per workgroup in the read phase.
+//   Reduce-scatter and reduce (one output per p inputs): their reads alone
+// stream at the read ceiling, but the writes interleaved with them, though
+// only 1/(p+1) of the bytes, cost about ten points of the HBM peak (96 MiB
+// float32 per rank: 86% with the writes dropped, 75% with them); batching
+// separates the phases and keeps the write phase short against the barrier.
+// Tiles are contiguous.
+//   Ring all-reduce (every output): the tiles interleave in runs as in
+// k_phase, and the write phase goes output by output for all K tiles.
+// The barrier orders nothing the results depend on, as in k_phase.
 template <class E, class OP, int P, int U, int K, FoldMode M>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void k_phase_batch(PhaseArgs a) {
   using S = typename E::S;
   using A = typename E::A;
   constexpr int V = 16 / sizeof(S);
   constexpr uint32_t kTile = kBlock * U;
-  static_assert(M == FoldMode::kRingShard || M == FoldMode::kAscOne, "one-output folds only");
+  static_assert(M == FoldMode::kRingShard || M == FoldMode::kAscOne || M == FoldMode::kRingAll,
+                "batched rounds: reduce-scatter, reduce and the ring all-reduce");
+  constexpr bool IL = M == FoldMode::kRingAll;
   const int p = P > 0 ? P : a.f.p;
   sync_claim(a);
   for (uint32_t r = 0; r < a.rounds; ++r) {
     A acc[K][U][V];
     int seg[K];
     uint32_t valid[K];
+    uint32_t gap[K];
     uint64_t off[K];
     uint64_t lo[K];
 #pragma unroll
@@ -315,6 +351,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
       const uint32_t t = (r * K + j) * gridDim.x + blockIdx.x;
       seg[j] = 0;
       valid[j] = 0;
+      gap[j] = 0;
       off[j] = 0;
       lo[j] = 0;
       if (t < a.tiles) {
@@ -332,24 +369,49 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
           valid[j] = (k + 1 == a.seg_tile[sg + 1] - a.seg_tile[sg]) ? a.seg_last[sg] : kTile;
           if constexpr (uses_bounds(M)) lo[j] = a.f.bound[sg];
         }
-        off[j] = ((lo[j] + V - 1) / V + static_cast<uint64_t>(k) * kTile) * 16;
-        read_fold<E, OP, P, U, M, false>(a.f, seg[j], p, off[j], valid[j], 0, acc[j]);
+        uint64_t gk = static_cast<uint64_t>(k) * kTile;  // the tile's first group in the segment
+        if constexpr (IL) {
+          if (a.strips > 1 && k < a.strip_tiles) {
+            const uint32_t run = k / a.strips;
+            const uint32_t jj = k - run * a.strips;
+            gk = static_cast<uint64_t>(run) * a.strips * kTile + jj * kBlock;
+            gap[j] = (a.strips - 1) * kBlock;
+          }
+        }
+        off[j] = ((lo[j] + V - 1) / V + gk) * 16;
+        read_fold<E, OP, P, U, M, IL>(a.f, seg[j], p, off[j], valid[j], gap[j], acc[j]);
       }
     }
     soft_barrier(a, r);
+    Raw<E, V> o[K][U];
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
-      if (valid[j] == 0) continue;
-      Raw<E, V> o[U];
+    for (int j = 0; j < K; ++j)
 #pragma unroll
-      for (int u = 0; u < U; ++u) pack(acc[j][u], o[u]);
-      // reduce-scatter outputs hold only the chunk: group g sits at g*V - lo
-      const uint64_t shift = (M == FoldMode::kRingShard) ? lo[j] * sizeof(S) : 0;
-      char* d = static_cast<char*>(a.f.out[seg[j]]) + (off[j] - shift);
-      if (valid[j] == kTile) {
-        store_tile<false, false>(d, o, valid[j], 0);
-      } else {
-        store_tile<true, false>(d, o, valid[j], 0);
+      for (int u = 0; u < U; ++u) pack(acc[j][u], o[j][u]);
+    if constexpr (M == FoldMode::kRingAll) {
+      for (int q = 0; q < p; ++q) {
+        char* d = static_cast<char*>(a.f.out[q]);
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          if (valid[j] == kTile) {
+            store_tile<false, IL>(d + off[j], o[j], valid[j], gap[j]);
+          } else if (valid[j] != 0) {
+            store_tile<true, IL>(d + off[j], o[j], valid[j], gap[j]);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        if (valid[j] == 0) continue;
+        // reduce-scatter outputs hold only the chunk: group g sits at g*V - lo
+        const uint64_t shift = (M == FoldMode::kRingShard) ? lo[j] * sizeof(S) : 0;
+        char* d = static_cast<char*>(a.f.out[seg[j]]) + (off[j] - shift);
+        if (valid[j] == kTile) {
+          store_tile<false, false>(d, o[j], valid[j], 0);
+        } else {
+          store_tile<true, false>(d, o[j], valid[j], 0);
+        }
       }
     }
   }

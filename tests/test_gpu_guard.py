@@ -84,11 +84,14 @@ def inputs(seed, p, n, dtype):
 
 
 # (algo, group, dtype, p, n, shift): the fused fold with edges and several
-# rounds, one-round 16-bit tiles with ragged chunks, the single-pass fold on
+# rounds, batched rounds with interleaved runs and a partial last tile per
+# chunk, one-round 16-bit tiles with ragged chunks, the single-pass fold on
 # unaligned buffers, the staged and persistent rings, the staged hierarchy.
 AR_CASES = [
     ("ring", 0, "float32", 8, 8 * (5 << 20) + 29, 0),
     ("ring", 0, "bfloat16", 8, 8 * (3 << 20) + 13, 0),
+    ("ring", 0, "float32", 8, 8 * ((1 << 20) + 16), 0),
+    ("ring", 0, "bfloat16", 8, 8 * ((2 << 20) + 24), 0),
     ("ring", 0, "float16", 6, 6 * 70001 + 5, 0),
     ("ring", 0, "float32", 5, 77777, 4),
     ("ring", 0, "bfloat16", 3, 4099, 2),

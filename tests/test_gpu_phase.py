@@ -170,6 +170,37 @@ def test_batched_rounds_ragged_chunks(rr, tuning, env, p, dtype, op):
     torch.cuda.empty_cache()
 
 
+AR_BATCH_CASES = [
+    # (p, n, dtype, op): uniform chunks (interleaved runs), ragged chunks
+    # (per-chunk tilings, heads and tails), 16-bit types, p = 5 (run-time
+    # rank loop)
+    (8, 8 << 20, "float32", "sum"),
+    (8, (8 << 20) + 8 * 5 + 3, "float32", "max"),
+    (8, 16 << 20, "bfloat16", "avg"),
+    (8, (8 << 20) + 8 * 8 * 5, "float16", "sum"),
+    (5, 5 * (3 << 21), "int32", "min"),
+]
+
+
+@pytest.mark.parametrize("env", [{}, {"RR_AR_BATCH": "2"}, {"RR_AR_BATCH": "4", "RR_PHASE_PER_CU": "1"},
+                                 {"RR_AR_BATCH": "2", "RR_PHASE_STRIPS": "16"},
+                                 {"RR_AR_BATCH": "4", "RR_PHASE_STATIC": "0"}, {"RR_AR_BATCH": "1"}])
+@pytest.mark.parametrize("case", range(len(AR_BATCH_CASES)))
+def test_ring_all_reduce_batched_rounds(rr, tuning, env, case):
+    """The ring all-reduce of several rounds in batched rounds (K tiles per
+    workgroup and round, interleaved runs, the write phase output by output)
+    and in single-tile rounds: the same bits as the oracle."""
+    p, n, dtype, op = AR_BATCH_CASES[case]
+    x = W.random_inputs(69 + case, p, n, dtype, kind="full" if dtype == "int32" else "normal")
+    want = C.all_reduce_fold(x, op, dtype)
+    for k, v in env.items():
+        tuning.set(k, v)
+    t0 = rr.barrier_timeouts()
+    assert_bitwise(run_ar(rr, x, dtype, op, "ring"), want, f"ring {p} {n} {dtype} {op} {env}")
+    assert rr.barrier_timeouts() == t0
+    torch.cuda.empty_cache()
+
+
 # Per-rank lengths whose one-round launch takes the tile of 4, 2 or 1 groups
 # per lane (fewer 8-group tiles than CUs), with ragged chunk tails, p = 8
 # (the kernels compiled for p = 8), 4 and 5 (the run-time loop).
