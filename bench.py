@@ -674,7 +674,8 @@ def main(argv=None):
     launch_ms = ms_step
     value = runner.bytes / (ms_step * 1e-3) / 1e9
     achieved = runner.bytes / (launch_ms * 1e-3) / 1e9
-    kernel = {"ring": "k_phase<..., FoldMode::kRingAll, ...> (phased fused ring all-reduce)",
+    kernel = {"ring": "k_phase / k_phase_batch <..., FoldMode::kRingAll, ...> (phased fused ring all-reduce; "
+                      "launches of several rounds take the batched kernel)",
               "hier": "k_phase<..., FoldMode::kHierAll, ...> (phased fused hierarchical all-reduce)"}[algo]
     traffic = load_traffic(args.workload)
     esz = np.dtype(W.STORAGE[dtype]).itemsize
@@ -744,6 +745,12 @@ def workload_lines(args, torch, rr, W, stream, cpm, report):
             r = Runner(rr, torch, spec, "all_reduce", op, algo, spec.get("group", 0), x, sets, stream)
             report(f"all_reduce_{algo}_{op}", r, 200 if n * esz <= (8 << 20) else 40, True, name)
             if n * esz * p <= (1 << 20):
+                # a launch-bound call: also with one buffer set, as a training
+                # loop that reuses its buffers calls it (caches and address
+                # translations warm), and its host cost per call
+                del r
+                r = Runner(rr, torch, spec, "all_reduce", op, algo, spec.get("group", 0), x, 1, stream)
+                report(f"all_reduce_{algo}_{op}_cache_hot", r, 200, False, name)
                 call_latency(torch, r, stream, name)
             del r
             torch.cuda.empty_cache()
