@@ -193,6 +193,29 @@ hipError_t launch_batched(DeviceState& d, const FoldLaunch& f, const PhaseArgs& 
   return launch_batch_mode(f, b, static_cast<unsigned>(resident), K, sp, nullptr, s);
 }
 
+// Workgroups per CU of a batched launch: `asked` if > 0, else 3 or 2, each
+// capped at the kernel's occupancy, whichever leaves fewer empty tile slots
+// in the last round (ties: the fewer rounds); 0 when not even one round of
+// K tiles per workgroup is full.  Full rounds measured best (float32 48 MiB
+// per rank, all-reduce: one round at 3 per CU 80.1-81.0%, two at 2 per CU
+// with the second half empty 77-78%; reduce-scatter 80.8% against 78%).
+uint64_t batch_per_cu(uint64_t tiles, uint64_t cus, int K, int occ, int asked) {
+  uint64_t best = 0;
+  uint64_t best_waste = ~0ull;
+  const int options[2] = {asked > 0 ? asked : 3, asked > 0 ? asked : 2};
+  for (int c : options) {
+    const uint64_t pc = static_cast<uint64_t>(c < occ ? c : occ);
+    const uint64_t slots = cus * pc * static_cast<uint64_t>(K);
+    if (pc == 0 || tiles < slots) continue;
+    const uint64_t waste = (tiles + slots - 1) / slots * slots - tiles;
+    if (waste < best_waste) {
+      best_waste = waste;
+      best = pc;
+    }
+  }
+  return best;
+}
+
 }  // namespace
 
 int phase_default_unroll(Kind k, FoldMode m) { return (is_hier(m) && is_half(k)) ? 4 : 8; }
@@ -306,24 +329,7 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
     int occ = 0;
     e = batch_occupancy(d, f, a, K, sp, s, &occ);
     if (e != hipSuccess) return e;
-    // Workgroups per CU: as asked, else 3 or 2 (as many as stay resident),
-    // whichever leaves fewer empty tile slots in the last round, ties to the
-    // fewer rounds.  Full rounds measured best: float32 48 MiB per rank in one
-    // round at 3 per CU 81.6%, in two at 2 per CU (the second half empty)
-    // 78.5%; 32 MiB in one round at 2 per CU 81.7%.
-    uint64_t per_cu_b = 0;
-    uint64_t best_waste = ~0ull;
-    const int asked[2] = {pt.per_cu > 0 ? pt.per_cu : 3, pt.per_cu > 0 ? pt.per_cu : 2};
-    for (int c : asked) {
-      const uint64_t pc = static_cast<uint64_t>(c < occ ? c : occ);
-      const uint64_t slots = cus * pc * static_cast<uint64_t>(K);
-      if (tiles < slots) continue;  // not even one full round
-      const uint64_t waste = (tiles + slots - 1) / slots * slots - tiles;
-      if (waste < best_waste) {
-        best_waste = waste;
-        per_cu_b = pc;
-      }
-    }
+    const uint64_t per_cu_b = batch_per_cu(tiles, cus, K, occ, pt.per_cu);
     if (per_cu_b > 0) {
       const int strips = pt.strips > 0 ? pt.strips : 8;
       if (strips > 1 && a.uniform_tiles != 0) {
@@ -350,13 +356,10 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
     int occ = 0;
     e = batch_occupancy(d, f, a, K, sp, s, &occ);
     if (e != hipSuccess) return e;
-    // Two workgroups per CU unless asked otherwise, never more than stay
-    // resident: 4 per CU measured worse for float32 (128 MiB per rank, two
-    // full rounds: 77% against 80% with 2 per CU) and no better for
-    // bfloat16.
-    const int want = pt.per_cu > 0 ? pt.per_cu : 2;
-    const uint64_t per_cu_b = static_cast<uint64_t>(want < occ ? want : occ);
-    if (tiles >= cus * per_cu_b * static_cast<uint64_t>(K)) return launch_batched(d, f, a, tiles, cus * per_cu_b, K, sp, pt, s);
+    // 4 per CU measured worse for float32 (128 MiB per rank, two full rounds:
+    // 77% against 80% with 2 per CU), hence at most 3
+    const uint64_t per_cu_b = batch_per_cu(tiles, cus, K, occ, pt.per_cu);
+    if (per_cu_b > 0) return launch_batched(d, f, a, tiles, cus * per_cu_b, K, sp, pt, s);
   }
   if (one_out && pt.unroll == 0 && pt.grid == 0 && unroll == 4) {
     // reduce-scatter and reduce too small for a tile of 4 groups per lane on
