@@ -540,11 +540,18 @@ hipError_t phase_dispatch(const PhaseArgs& a, Kind k, rr_op_t op, unsigned grid,
 // The batched one-output kernels: K tiles of 4 groups per lane per round.
 template <class E, class OP, FoldMode M>
 hipError_t batch_by_p(const PhaseArgs& a, unsigned grid, int K, bool static_p, int* occ, hipStream_t s) {
-  hipError_t e;
-  if (static_p && a.f.p == 8) {
-    e = K == 2 ? phase_go(&k_phase_batch<E, OP, 8, 4, 2, M>, a, grid, kBlock, occ, s)
-               : phase_go(&k_phase_batch<E, OP, 8, 4, 4, M>, a, grid, kBlock, occ, s);
-  } else {
+  hipError_t e = hipErrorInvalidValue;
+  bool launched = false;
+  // binary16 takes the run-time rank loop only: with all p = 8 ranks
+  // unrolled its conversions are hoisted past 256 registers and spill
+  if constexpr (!__is_same(E, EF16)) {
+    if (static_p && a.f.p == 8) {
+      e = K == 2 ? phase_go(&k_phase_batch<E, OP, 8, 4, 2, M>, a, grid, kBlock, occ, s)
+                 : phase_go(&k_phase_batch<E, OP, 8, 4, 4, M>, a, grid, kBlock, occ, s);
+      launched = true;
+    }
+  }
+  if (!launched) {
     e = K == 2 ? phase_go(&k_phase_batch<E, OP, 0, 4, 2, M>, a, grid, kBlock, occ, s)
                : phase_go(&k_phase_batch<E, OP, 0, 4, 4, M>, a, grid, kBlock, occ, s);
   }
