@@ -40,8 +40,15 @@
 // runs on (tagged with the launch) and reads its slice's p entries.  When they
 // all agree, the slice exchanges data inside one L2, coherent for its CUs: a
 // step is published once every wave's stores are acknowledged by the L2
-// (s_waitcnt 0, barrier) and the flag is raised, and a waiter that sees the
-// flag only invalidates its CU's L1 (buffer_inv sc0).  Otherwise, to publish
+// (s_waitcnt 0, barrier) and the flag is raised, with no write-back.  The
+// waiter still takes the agent-scope acquire (buffer_inv sc1), which drops
+// its CU's L1 copies: a reader does read an address twice (a chunk's
+// reduce-scatter partial, then p steps later its final value), and the
+// workgroup-scope invalidation (buffer_inv sc0) does not touch the L1 -- a
+// probe on MI355X, two CUs of one XCD exchanging one 4 KiB region 2000 times,
+// read the previous value in 99.95% of the words with it and with plain
+// loads alone, in none with buffer_inv sc1 (1.6 us per exchange).  Otherwise,
+// to publish
 // a step, every wave waits until its stores are acknowledged by the L2
 // (s_waitcnt 0), the workgroup meets at a barrier, and thread 0 takes an agent-scope release fence -- on gfx950 an
 // L2 write-back of the whole XCD's L2 (buffer_wbl2 sc1), which therefore
@@ -129,10 +136,6 @@ __device__ bool wait_flag(const ExecArgs& a, const unsigned long long* f, unsign
   return true;
 }
 
-// Invalidate this CU's L1 vector cache (and wait for it): after it, loads
-// read the XCD's L2.  The acquire of a slice whose workers all run on one XCD.
-__device__ __forceinline__ void l1_invalidate() { asm volatile("buffer_inv sc0\n\ts_waitcnt vmcnt(0)" ::: "memory"); }
-
 // The XCC (XCD) this wave runs on.
 __device__ __forceinline__ uint32_t xcc_id() {
   return __builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xFu;  // HW_REG_XCC_ID, bits 0-3
@@ -218,13 +221,7 @@ __global__ __launch_bounds__(kBlock) void k_ring_exec(ExecArgs a) {
         bool ok = wait_flag(a, exec_flag(a.slot, b * p + r), a.tag + static_cast<unsigned long long>(t));
         if (ok && !kSeparate && t >= p)
           ok = wait_flag(a, exec_flag(a.slot, b * p + nx), a.tag + static_cast<unsigned long long>(t - p + 2));
-        if (ok) {
-          if (local) {
-            l1_invalidate();
-          } else {
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-          }
-        }
+        if (ok) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         go = ok ? 1 : 0;
       }
       __syncthreads();

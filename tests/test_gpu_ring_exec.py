@@ -56,6 +56,21 @@ def test_large_ragged(rr, dtype):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("slices", ("1", "8", "20"))
+@pytest.mark.parametrize("dtype", ("float32", "bfloat16"))
+def test_slice_counts(rr, tuning, slices, dtype):
+    """Fewer slices per chunk than the default (one slice: no XCD-local
+    layout; 20, rounded down to a multiple of the XCD count): the same
+    bits."""
+    p, n = 8, 8 * (1 << 20) + 8 * 3 + 1
+    x = W.random_inputs(84, p, n, dtype)
+    tuning.set("RR_EXEC_SLICES", slices)
+    f0 = rr.ring_exec_failures()
+    assert_bitwise(run(rr, x, dtype), C.all_reduce_fold(x, "sum", dtype), f"{slices} slices")
+    assert rr.ring_exec_failures() == f0
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("dtype", ("int32", "float32", "bfloat16"))
 def test_in_place_and_unaligned(rr, dtype):
     p, n = 6, 6 * 4001 + 5
