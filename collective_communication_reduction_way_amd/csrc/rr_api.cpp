@@ -1156,7 +1156,7 @@ rr_status_t rr_all_gather_dim1(const void* const* sendbufs, void* const* recvbuf
   const Tuning& t = tuning();
   if (t.log) fprintf(stderr, "[rr] all_gather_dim1: p=%d rows=%zu cols=%zu unit=%d\n", p, rows, cols, unit);
   const hipError_t e =
-      rr::launch_gather_cols(a, unit, t.nontemporal, t.multi_per_cu, reinterpret_cast<hipStream_t>(stream));
+      rr::launch_gather_cols(a, unit, t.nontemporal, t.multi_per_cu, t.fanout_xcd, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "all_gather_dim1");
   return ok();
 }

@@ -191,7 +191,10 @@ struct ColsArgs {
 };
 
 // All-gather along dim 1: dst[r][b, c*w + j] = src[c][b, j] for every r.
-hipError_t launch_gather_cols(const ColsArgs& a, int unit_bytes, int nontemporal, int per_cu, hipStream_t stream);
+// xcd_dst: destinations per workgroup of the XCD layout (1, 2, 4), 0 = never,
+// -1 = by the bytes written.
+hipError_t launch_gather_cols(const ColsArgs& a, int unit_bytes, int nontemporal, int per_cu, int xcd_dst,
+                              hipStream_t stream);
 // Reduce-scatter along dim 1: dst[c][b, j] = fold over k = 1..p of
 // src[(c+k) mod p][b, c*w + j] (ring order of chunk c), then the op's last
 // step and the one conversion.  vec = 1: 16-byte groups, else elements.

@@ -323,6 +323,43 @@ __global__ __launch_bounds__(kBlock) void k_gather_cols(ColsArgs a) {
   }
 }
 
+// All-gather along dim 1 in the XCD layout of the fan-out (k_fanout_xcd in
+// rr_copy.hip): the outputs are cut into blocks of kBlock 16-byte units (4
+// KiB); a workgroup moves one block to D destinations and exits.  Block b
+// belongs to XCD b mod 8, and the G = ceil(p / D) workgroups of a block are
+// congruent modulo 8 and consecutive in that XCD's dispatch order (the
+// dispatcher deals workgroups to the 8 XCDs in turn), so the block's source
+// runs are read from HBM once, with ordinary cached loads, and from the XCD's
+// L2 by the others.  Workgroup w: XCD x = w mod 8, j = w / 8, block
+// (j / G) * 8 + x, destinations (j mod G) * D ...  Placement only decides
+// speed: a workgroup that lands elsewhere reads its source again.  All
+// uniform index arithmetic is 32-bit; only the per-lane unit index is wider.
+template <int D, class IDX>
+__global__ __launch_bounds__(kBlock) void k_gather_cols_xcd(ColsArgs a, uint32_t G, uint32_t blocks) {
+  const uint32_t w = blockIdx.x;
+  const uint32_t x = w % 8;
+  const uint32_t j = w / 8;
+  const uint32_t v = j / G;
+  const uint32_t g = j - v * G;
+  const uint32_t blk = v * 8 + x;
+  if (blk >= blocks) return;
+  const IDX wu = static_cast<IDX>(a.wu);
+  const IDX du = static_cast<IDX>(a.du);
+  const IDX total = static_cast<IDX>(a.rows) * du;
+  const IDX i = static_cast<IDX>(blk) * kBlock + threadIdx.x;
+  if (i >= total) return;
+  IDX b, q, c, jj;
+  row_split(i, du, b, q);
+  row_split(q, wu, c, jj);
+  const u32x4 val = static_cast<const u32x4*>(a.src[c])[static_cast<uint64_t>(b) * wu + jj];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    const int r = static_cast<int>(g) * D + d;
+    if (r >= a.p) break;
+    __builtin_nontemporal_store(val, static_cast<u32x4*>(a.dst[r]) + i);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Host-side dispatch.
 
@@ -478,9 +515,41 @@ hipError_t launch_fold_cols(const ColsArgs& a, Kind k, rr_op_t op, int vec, int 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gather_cols(const ColsArgs& a, int unit_bytes, int nontemporal, int per_cu, hipStream_t s) {
+hipError_t launch_gather_cols(const ColsArgs& a, int unit_bytes, int nontemporal, int per_cu, int xcd_dst,
+                              hipStream_t s) {
   if (a.rows * a.wu == 0) return hipSuccess;
   const bool nt = nontemporal != 0;
+  // The XCD layout, two destinations per workgroup, for launches of 16-byte
+  // units that write at least 192 MiB (the fan-out's rule); xcd_dst forces
+  // the destinations per workgroup (1, 2, 4) or turns it off (0).
+  if (unit_bytes == 16 && nt && per_cu <= 0 && xcd_dst != 0) {
+    const uint64_t units = a.rows * a.du;
+    const uint64_t written = units * 16 * static_cast<uint64_t>(a.p);
+    const int D = xcd_dst < 0 ? (written >= (192ull << 20) ? 2 : 0) : xcd_dst;
+    const uint64_t blocks = (units + kBlock - 1) / kBlock;
+    const uint64_t G = (static_cast<uint64_t>(a.p) + (D > 0 ? D : 1) - 1) / (D > 0 ? D : 1);
+    const uint64_t grid = (blocks + 7) / 8 * 8 * G;
+    if ((D == 1 || D == 2 || D == 4) && grid <= 0x7FFFFFFFull && blocks <= 0xFFFFFFFFull) {
+      const uint32_t g32 = static_cast<uint32_t>(G);
+      const uint32_t b32 = static_cast<uint32_t>(blocks);
+      const bool small = units + kBlock <= 0xFFFFFFFFull;
+      const dim3 gd(static_cast<unsigned>(grid));
+      void* kp[3];
+      ColsArgs copy = a;
+      uint32_t gg = g32, bb = b32;
+      kp[0] = &copy;
+      kp[1] = &gg;
+      kp[2] = &bb;
+      const void* k = nullptr;
+      if (D == 1) k = small ? reinterpret_cast<const void*>(&k_gather_cols_xcd<1, uint32_t>)
+                            : reinterpret_cast<const void*>(&k_gather_cols_xcd<1, uint64_t>);
+      if (D == 2) k = small ? reinterpret_cast<const void*>(&k_gather_cols_xcd<2, uint32_t>)
+                            : reinterpret_cast<const void*>(&k_gather_cols_xcd<2, uint64_t>);
+      if (D == 4) k = small ? reinterpret_cast<const void*>(&k_gather_cols_xcd<4, uint32_t>)
+                            : reinterpret_cast<const void*>(&k_gather_cols_xcd<4, uint64_t>);
+      return hipLaunchKernel(k, gd, dim3(kBlock), kp, 0, s);
+    }
+  }
   switch (unit_bytes) {
     case 16: return nt ? gather_cols_go<16, true>(a, per_cu, s) : gather_cols_go<16, false>(a, per_cu, s);
     case 4: return nt ? gather_cols_go<4, true>(a, per_cu, s) : gather_cols_go<4, false>(a, per_cu, s);

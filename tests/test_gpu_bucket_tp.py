@@ -193,6 +193,21 @@ def test_all_gather_dim1(rr, p, rows, w, dtype):
     assert_bitwise(to_host(out, dtype), C.all_gather_dim1(sh), "all_gather_dim1")
 
 
+@pytest.mark.parametrize("xcd", ("1", "2", "4"))
+@pytest.mark.parametrize("p,rows,w,dtype", [(8, 33, 64, "float32"), (16, 9, 128, "bfloat16"), (4, 7, 8, "bfloat16"),
+                                            (3, 100, 12, "float32"), (8, 1, 4, "int32"), (5, 301, 40, "float16")])
+def test_all_gather_dim1_xcd_layout(rr, tuning, xcd, p, rows, w, dtype):
+    """The XCD layout of the dim-1 all-gather (4 KiB output blocks, 1, 2 or 4
+    destinations per workgroup, partial last block), forced at small
+    shapes: the same bits as the oracle."""
+    tuning.set("RR_FANOUT_XCD", xcd)
+    sh = W.random_inputs(63, p, rows * w, dtype, kind="full" if dtype == "int32" else "normal").reshape(p, rows, w)
+    dev = to_dev(sh, dtype)
+    out = torch.empty((p, rows, p * w), dtype=dev.dtype, device="cuda")
+    rr.all_gather_dim1(dev, out)
+    assert_bitwise(to_host(out, dtype), C.all_gather_dim1(sh), f"all_gather_dim1 xcd={xcd}")
+
+
 @pytest.mark.parametrize("p,rows,w", TP_SHAPES)
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_reduce_scatter_dim1(rr, p, rows, w, dtype):

@@ -202,8 +202,13 @@ def test_bucket_stays_in_bounds(rr):
         assert_bitwise(np.stack([host(v, dtype) for v in o.views()]), w, f"bucket tensor {i}")
 
 
+@pytest.mark.parametrize("xcd", ("-1", "1", "2", "4"))
 @pytest.mark.parametrize("dtype,rows,w", [("bfloat16", 33, 64), ("float32", 17, 5), ("bfloat16", 1029, 512)])
-def test_dim1_layouts_stay_in_bounds(rr, dtype, rows, w):
+def test_dim1_layouts_stay_in_bounds(rr, tuning, dtype, rows, w, xcd):
+    """Both dim-1 layouts at ragged shapes; the all-gather also in the XCD
+    layout with 1, 2 or 4 destinations per workgroup (forced: these shapes
+    write less than it is chosen for by itself)."""
+    tuning.set("RR_FANOUT_XCD", xcd)
     p = 8
     xm = inputs(450, p, rows * p * w, dtype).reshape(p, rows, p * w)
     want_rs = C.reduce_scatter_cols(xm, "sum", dtype)
