@@ -15,22 +15,25 @@
 // slices never wait for each other.
 //
 // Steps of worker (b, q), with r = q-1 mod p the ring predecessor:
-//   t = 0          copy-in: slice b of every chunk of rank q into its working
-//                  buffer (float32 for 16-bit types, else the output itself);
 //   t = 1..p-1     reduce-scatter step s = t-1: chunk c = (r-1-s) mod p,
-//                  work[q] = work[r] (+) work[q] on slice b (message first, as
-//                  the receiver of the ring accumulates); after the last one
-//                  (after the copy-in when p = 1) rank q owns chunk q and
-//                  finishes it (AVG's division, the one rounding of 16-bit
-//                  types) into its output;
+//                  work[q] = m (+) in[q] on slice b, the message m first (the
+//                  receiver of the ring accumulates): m is r's input in step
+//                  0 and work[r], the partial sum r wrote in step s-1, after
+//                  that; q's own contribution is read from its input, where
+//                  it still is.  The last step completes chunk q and writes
+//                  it finished (AVG's division, the one rounding of 16-bit
+//                  types) to q's output instead of work[q].  The working
+//                  buffers are float32 for 16-bit types, else the outputs.
 //   t = p..2p-2    all-gather step s = t-p: chunk c = (r-s) mod p,
 //                  out[q] = out[r] on slice b.
-// flag[q][b] counts the steps worker (b, q) has completed.  Step t of (b, q)
-// reads what (b, r) wrote in step t-1, so it waits for flag[r][b] >= t.  When
-// the working buffer is the output (4-byte types), all-gather step s
-// overwrites the chunk that (b, q+1) read from rank q in reduce-scatter step
-// s, so it also waits for flag[q+1][b] >= s+2.  Every wait points to an
-// earlier step, so the waits form no cycle.
+// Step 0 of the ring (each rank's own copy) moves nothing: step 1 reads the
+// inputs.  flag[q][b] = t + 1 once worker (b, q) has completed step t.  Step
+// t >= 2 of (b, q) reads what (b, r) wrote in step t-1, so it waits for
+// flag[r][b] >= t.  All-gather step s overwrites chunk r-s of q's output,
+// which (b, q+1) read in reduce-scatter step s when the outputs are the
+// working buffers (4-byte types), and in step 0 (s = 0) when q runs in
+// place, so it then also waits for flag[q+1][b] >= s+2.  Every wait points
+// to an earlier step, so the waits form no cycle.  p = 1 is one copy.
 //
 // Memory ordering.  The flags order data between workgroups that may run on
 // different XCDs, each with its own L2.  The slices are laid out so that a
@@ -40,18 +43,24 @@
 // runs on (tagged with the launch) and reads its slice's p entries.  When they
 // all agree, the slice exchanges data inside one L2, coherent for its CUs: a
 // step is published once every wave's stores are acknowledged by the L2
-// (s_waitcnt 0, barrier) and the flag is raised, with no write-back.  The
-// waiter still takes the agent-scope acquire (buffer_inv sc1), which drops
-// its CU's L1 copies: a reader does read an address twice (a chunk's
-// reduce-scatter partial, then p steps later its final value), and the
-// workgroup-scope invalidation (buffer_inv sc0) does not touch the L1 -- a
-// probe on MI355X, two CUs of one XCD exchanging one 4 KiB region 2000 times,
-// read the previous value in 99.95% of the words with it and with plain
-// loads alone, in none with buffer_inv sc1 (1.6 us per exchange).  Otherwise,
-// to publish
-// a step, every wave waits until its stores are acknowledged by the L2
-// (s_waitcnt 0), the workgroup meets at a barrier, and thread 0 takes an agent-scope release fence -- on gfx950 an
-// L2 write-back of the whole XCD's L2 (buffer_wbl2 sc1), which therefore
+// (s_waitcnt 0, barrier) and the flag is raised, with no write-back, and the
+// waiter takes no fence.  What remains is each CU's own L1, which the other
+// CUs' stores do not update: a read must not be served by a line the CU
+// cached before the data changed.  Within a launch only all-gather steps
+// repeat a read of an address on a CU: with the outputs as working buffers
+// (4-byte kinds), step s >= 1 reads predecessor chunks that a reduce-scatter
+// step read while they held partial sums; in place, step 1 reads the chunk
+// that reduce-scatter step 0 read as input.  Those copies use device-scope
+// loads (sc1), served by the L2 around the L1.  A probe on MI355X settled which
+// forms work: two CUs of one XCD exchanging one 4 KiB region 2000 times read
+// the previous value in 99.95% of the words with plain loads, with or
+// without the workgroup-scope invalidation (buffer_inv sc0, which leaves the
+// L1 alone in this mode), and in none with device-scope loads or after the
+// agent-scope acquire (buffer_inv sc1).  An acquire before every step
+// instead costs 25% at 8 MiB per rank.  A slice whose workers are not all on
+// one XCD publishes a step as follows: every wave waits until its stores are
+// acknowledged by the L2 (s_waitcnt 0), the workgroup meets at a barrier, and
+// thread 0 takes an agent-scope release fence -- on gfx950 an L2 write-back of the whole XCD's L2 (buffer_wbl2 sc1), which therefore
 // covers every wave's stores -- before it raises the flag.  A waiter's
 // thread 0 sees the flag and takes an agent-scope acquire fence, which
 // invalidates the CU's L1 and the XCD's L2 for every wave (buffer_inv sc1),
@@ -80,6 +89,7 @@
 #include <algorithm>
 #include <map>
 #include <mutex>
+#include <type_traits>
 
 #include "rr_device.h"
 #include "rr_kernels.h"
@@ -141,20 +151,104 @@ __device__ __forceinline__ uint32_t xcc_id() {
   return __builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xFu;  // HW_REG_XCC_ID, bits 0-3
 }
 
-// Apply `f` to the elements [e0, e1) of a slice: whole 8-element units where
+// Apply `f` to the elements [e0, e1) of a slice: whole U-element units where
 // every buffer involved is 16-byte aligned (vec), single elements elsewhere.
-template <class FV, class FS>
+template <int U, class FV, class FS>
 __device__ __forceinline__ void for_slice(uint64_t e0, uint64_t e1, bool vec, FV&& fv, FS&& fs) {
   const uint32_t lane = threadIdx.x;
   uint64_t u0 = e1, u1 = e1;
   if (vec) {
-    u0 = (e0 + 7) / 8 * 8;
-    u1 = e1 / 8 * 8;
+    u0 = (e0 + U - 1) / U * U;
+    u1 = e1 / U * U;
     if (u1 < u0) u0 = u1 = e1;
   }
   for (uint64_t i = e0 + lane; i < (vec ? u0 : e1); i += kBlock) fs(i);
-  for (uint64_t g = u0 / 8 + lane; g < u1 / 8; g += kBlock) fv(g * 8);
+  for (uint64_t g = u0 / U + lane; g < u1 / U; g += kBlock) fv(g * U);
   for (uint64_t i = u1 + lane; i < e1; i += kBlock) fs(i);
+}
+
+// Copy the elements [e0, e1) of a slice from src to dst: 16-byte words where
+// both buffers are 16-byte aligned (vec), two words per lane and pass at a
+// distance of one workgroup, so that every wave access is 1 KiB of
+// consecutive bytes and each lane has two loads in flight; single elements
+// elsewhere.  COHERENT (slices under 4 GiB): every load is
+// device-scope (sc1), served by the XCD's L2 around the CU's L1.
+template <bool COHERENT, class S>
+__device__ __forceinline__ void copy_slice(const S* src, S* dst, uint64_t e0, uint64_t e1, bool vec) {
+  constexpr int W = 16 / static_cast<int>(sizeof(S));
+  const uint32_t lane = threadIdx.x;
+  uint64_t u0 = e1, u1 = e1;
+  if (vec) {
+    u0 = (e0 + W - 1) / W * W;
+    u1 = e1 / W * W;
+    if (u1 < u0) u0 = u1 = e1;
+  }
+  // COHERENT: a raw buffer over the slice (0x00020000: the gfx9 descriptor
+  // word 3 for untyped 32-bit accesses); unused otherwise
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<S*>(src + e0), 0, static_cast<int>(static_cast<uint32_t>((e1 - e0) * sizeof(S))), 0x00020000);
+  auto one = [&](uint64_t i) {
+    if constexpr (COHERENT) {
+      using B = std::conditional_t<sizeof(S) == 4, uint32_t, uint16_t>;
+      const B v = __hip_atomic_load(reinterpret_cast<const B*>(src + i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      reinterpret_cast<B*>(dst)[i] = v;
+    } else {
+      dst[i] = src[i];
+    }
+  };
+  auto word = [&](uint64_t g) -> u32x4 {
+    if constexpr (COHERENT) {
+      return __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>((g * W - e0) * sizeof(S)), 0, 16);
+    } else {
+      return reinterpret_cast<const u32x4*>(src)[g];
+    }
+  };
+  for (uint64_t i = e0 + lane; i < (vec ? u0 : e1); i += kBlock) one(i);
+  const uint64_t g1 = u1 / W;
+  uint64_t g = u0 / W + lane;
+  u32x4* d = reinterpret_cast<u32x4*>(dst);
+  for (; g + kBlock < g1; g += 2 * kBlock) {
+    const u32x4 x = word(g);
+    const u32x4 y = word(g + kBlock);
+    d[g] = x;
+    d[g + kBlock] = y;
+  }
+  if (g < g1) d[g] = word(g);
+  for (uint64_t i = u1 + lane; i < e1; i += kBlock) one(i);
+}
+
+// dst = msg (+) own on the elements [e0, e1) of a slice, the message first;
+// FINISH: then the op's last step (AVG's division) before the conversion to
+// dst's kind.  The kinds share one accumulator type.
+template <class EM, class EO, class ED, class OP, bool FINISH>
+__device__ __forceinline__ void fold_step(const typename EM::S* msg, const typename EO::S* own, typename ED::S* dst,
+                                          uint64_t e0, uint64_t e1, bool vec, int32_t div) {
+  using A = typename ED::A;
+  constexpr int U = 8;
+  for_slice<U>(
+      e0, e1, vec,
+      [&](uint64_t i) {
+        Raw<EM, U> m;
+        Raw<EO, U> l;
+        load_group<false>(m, msg + i);
+        load_group<false>(l, own + i);
+        A vm[U], vl[U];
+        unpack(m, vm);
+        unpack(l, vl);
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+          vm[j] = OP::apply(vm[j], vl[j]);
+          if constexpr (FINISH) vm[j] = op_finish<OP>(vm[j], div);
+        }
+        Raw<ED, U> d;
+        pack(vm, d);
+        store_group<false>(dst + i, d);
+      },
+      [&](uint64_t i) {
+        A v = OP::apply(load_one<EM>(msg + i), load_one<EO>(own + i));
+        if constexpr (FINISH) v = op_finish<OP>(v, div);
+        store_one<ED>(dst + i, v);
+      });
 }
 
 // E: storage kind; EA: accumulator kind of the working buffers.
@@ -181,6 +275,7 @@ __global__ __launch_bounds__(kBlock) void k_ring_exec(ExecArgs a) {
   const int nx = q + 1 == p ? 0 : q + 1;
   const bool vec = a.vec != 0;
   constexpr bool kSeparate = !__is_same(E, EA);  // working buffers apart from the outputs
+  constexpr int U = 8;  // elements per unit of a lane
   __shared__ int go;
   __shared__ int local;  // 1: every worker of the slice runs on this XCD
   auto slice_lo = [&](int c) {
@@ -190,6 +285,20 @@ __global__ __launch_bounds__(kBlock) void k_ring_exec(ExecArgs a) {
   auto slice_hi = [&](int c) {
     const uint64_t len = a.bound[c + 1] - a.bound[c];
     return a.bound[c] + len * static_cast<uint64_t>(b + 1) / static_cast<uint64_t>(a.nslices);
+  };
+  // Step t re-reads addresses that this worker read before in the launch
+  // (the predecessor's output; its L1 lines may be stale): with the outputs
+  // as working buffers, all-gather steps s >= 1 read chunks that a
+  // reduce-scatter step read while they held partial sums; in place, all-
+  // gather step 1 reads the chunk that step 0 read as the predecessor's
+  // input.  No other read in a launch repeats an address on one CU: a
+  // slice's data crosses only between the p workers of that slice, and
+  // slices that share an XCD are never adjacent (no shared cache lines).
+  auto reread = [&](int t) { return kSeparate ? t == p + 1 && a.in[r] == a.out[r] : t >= p + 1; };
+  auto coherent_fits = [&](int t) {
+    int c = r - (t - p);
+    while (c < 0) c += p;
+    return (slice_hi(c) - slice_lo(c)) * sizeof(S) < (1ull << 32);
   };
   SA* wq = static_cast<SA*>(a.work[q]);
   if (threadIdx.x == 0) {
@@ -213,75 +322,75 @@ __global__ __launch_bounds__(kBlock) void k_ring_exec(ExecArgs a) {
   }
   __syncthreads();
   if (!go) return;
-  for (int t = 0; t <= 2 * p - 2; ++t) {
-    // wait for the predecessor's step t-1 (and, for an all-gather overwrite
-    // of a working buffer, for the successor's read of it)
-    if (t > 0) {
+  // p = 1: the output is the input, through the op's last step
+  if (p == 1) {
+    const S* in = static_cast<const S*>(a.in[0]);
+    S* o = static_cast<S*>(a.out[0]);
+    if (static_cast<const void*>(in) != static_cast<const void*>(o) || is_avg<OP>()) {
+      for_slice<U>(
+          slice_lo(0), slice_hi(0), vec,
+          [&](uint64_t i) {
+            Raw<E, U> x;
+            load_group<false>(x, in + i);
+            A v[U];
+            unpack(x, v);
+#pragma unroll
+            for (int j = 0; j < U; ++j) v[j] = op_finish<OP>(v[j], a.div);
+            pack(v, x);
+            store_group<false>(o + i, x);
+          },
+          [&](uint64_t i) { store_one<E>(o + i, op_finish<OP>(load_one<E>(in + i), a.div)); });
+    }
+    return;
+  }
+  const bool in_place_q = a.in[q] == a.out[q];
+  // Step t = 1 .. 2p-2 (step 0, a copy-in, moves nothing: the first
+  // reduce-scatter step reads the inputs); flag = t + 1 once step t is done.
+  for (int t = 1; t <= 2 * p - 2; ++t) {
+    // wait for the predecessor's step t-1 (the inputs of step 1 are ready at
+    // the launch), and before an all-gather overwrite of a buffer that the
+    // successor reads, for that read: with the outputs as working buffers,
+    // the partial sum it read in reduce-scatter step s; else, in place, the
+    // input chunk it read in step 0
+    if (t > 1) {
       if (threadIdx.x == 0) {
         bool ok = wait_flag(a, exec_flag(a.slot, b * p + r), a.tag + static_cast<unsigned long long>(t));
-        if (ok && !kSeparate && t >= p)
+        if (ok && t >= p && (!kSeparate || (t == p && in_place_q)))
           ok = wait_flag(a, exec_flag(a.slot, b * p + nx), a.tag + static_cast<unsigned long long>(t - p + 2));
-        if (ok) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        // XCD-local slices need no acquire except where a re-read reads
+        // around the CU's L1 and cannot (a slice of 4 GiB or more)
+        if (ok && (!local || (reread(t) && !coherent_fits(t)))) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         go = ok ? 1 : 0;
       }
       __syncthreads();
       if (!go) return;
     }
-    if (t == 0) {
-      // copy-in of slice b of every chunk of rank q into the float32
-      // working buffer (16-bit kinds).  4-byte kinds fold straight from the
-      // inputs instead (reduce-scatter below), so their step 0 moves nothing
-      // unless p = 1 (no steps follow: the output is the input's copy).
-      const S* in = static_cast<const S*>(a.in[q]);
-      if (kSeparate || (p == 1 && static_cast<const void*>(in) != static_cast<const void*>(wq))) {
-        for (int c = 0; c < p; ++c) {
-          for_slice(
-              slice_lo(c), slice_hi(c), vec,
-              [&](uint64_t i) {
-                Raw<E, 8> x;
-                load_group<true>(x, in + i);
-                A v[8];
-                unpack(x, v);
-                Raw<EA, 8> y;
-                pack(v, y);
-                store_group<true>(wq + i, y);
-              },
-              [&](uint64_t i) { store_one<EA>(wq + i, load_one<E>(in + i)); });
-        }
-      }
-    } else if (t < p) {
-      // reduce-scatter step s: the message from rank r is folded first.
-      // Without working buffers apart from the outputs, rank q's own chunk
-      // c is still unwritten (q folds it in this step only), so it is read
-      // from q's input, and the message is r's input in step 0 (r's chunk
-      // c is unwritten too) and r's output later (the chunk r folded in
-      // step s - 1).  Only q writes its output, and an input that is also
+    if (t < p) {
+      // reduce-scatter step s: message (+) own chunk, the message first.
+      // q's own contribution to chunk c is read from its input, where it
+      // still is (q folds chunk c in this step only); the message is r's
+      // input in step 0 and the partial sum r wrote in step s - 1 after
+      // that.  The last step completes chunk q and finishes it into q's
+      // output (AVG's division, the one rounding of 16-bit kinds).  Only q
+      // writes its working buffer and its output, and an input that is also
       // the output is overwritten by q's all-gather step 0 only after the
       // successor's step-0 read (the wait above).
       const int s = t - 1;
       int c = r - 1 - s;
       while (c < 0) c += p;
-      const SA* wr = static_cast<const SA*>(a.work[r]);
-      const SA* lq = wq;
-      if constexpr (!kSeparate) {
-        if (s == 0) wr = static_cast<const SA*>(a.in[r]);
-        lq = static_cast<const SA*>(a.in[q]);
+      const uint64_t lo = slice_lo(c), hi = slice_hi(c);
+      const S* own = static_cast<const S*>(a.in[q]);
+      const bool first = s == 0, last = s == p - 2;
+      if (first && last) {
+        fold_step<E, E, E, OP, true>(static_cast<const S*>(a.in[r]), own, static_cast<S*>(a.out[q]), lo, hi, vec, a.div);
+      } else if (first) {
+        fold_step<E, E, EA, OP, false>(static_cast<const S*>(a.in[r]), own, wq, lo, hi, vec, a.div);
+      } else if (last) {
+        fold_step<EA, E, E, OP, true>(static_cast<const SA*>(a.work[r]), own, static_cast<S*>(a.out[q]), lo, hi, vec,
+                                      a.div);
+      } else {
+        fold_step<EA, E, EA, OP, false>(static_cast<const SA*>(a.work[r]), own, wq, lo, hi, vec, a.div);
       }
-      for_slice(
-          slice_lo(c), slice_hi(c), vec,
-          [&](uint64_t i) {
-            Raw<EA, 8> m, l;
-            load_group<false>(m, wr + i);
-            load_group<false>(l, lq + i);
-            A vm[8], vl[8];
-            unpack(m, vm);
-            unpack(l, vl);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) vm[j] = OP::apply(vm[j], vl[j]);
-            pack(vm, m);
-            store_group<false>(wq + i, m);
-          },
-          [&](uint64_t i) { store_one<EA>(wq + i, OP::apply(load_one<EA>(wr + i), load_one<EA>(lq + i))); });
     } else {
       // all-gather step s: rank q overwrites its copy of chunk c
       const int s = t - p;
@@ -289,35 +398,11 @@ __global__ __launch_bounds__(kBlock) void k_ring_exec(ExecArgs a) {
       while (c < 0) c += p;
       const S* orr = static_cast<const S*>(a.out[r]);
       S* oq = static_cast<S*>(a.out[q]);
-      for_slice(
-          slice_lo(c), slice_hi(c), vec,
-          [&](uint64_t i) {
-            Raw<E, 8> x;
-            load_group<false>(x, orr + i);
-            store_group<false>(oq + i, x);
-          },
-          [&](uint64_t i) { oq[i] = orr[i]; });
-    }
-    if (t == p - 1 && (kSeparate || is_avg<OP>())) {
-      // rank q now owns chunk q (after the last reduce-scatter step, or
-      // after the copy-in when p = 1 and there is no such step): the op's
-      // last step, the one conversion
-      __syncthreads();
-      S* oq = static_cast<S*>(a.out[q]);
-      for_slice(
-          slice_lo(q), slice_hi(q), vec,
-          [&](uint64_t i) {
-            Raw<EA, 8> x;
-            load_group<false>(x, wq + i);
-            A v[8];
-            unpack(x, v);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = op_finish<OP>(v[j], a.div);
-            Raw<E, 8> y;
-            pack(v, y);
-            store_group<false>(oq + i, y);
-          },
-          [&](uint64_t i) { store_one<E>(oq + i, op_finish<OP>(load_one<EA>(wq + i), a.div)); });
+      if (local && reread(t) && coherent_fits(t)) {
+        copy_slice<true>(orr, oq, slice_lo(c), slice_hi(c), vec);
+      } else {
+        copy_slice<false>(orr, oq, slice_lo(c), slice_hi(c), vec);
+      }
     }
     // publish step t: every wave's stores acknowledged, then one release
     __atomic_signal_fence(__ATOMIC_SEQ_CST);

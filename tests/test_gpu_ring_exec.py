@@ -88,6 +88,26 @@ def test_in_place_and_unaligned(rr, dtype):
     assert_bitwise(got, C.all_reduce_fold(np.ascontiguousarray(x[:, 1:1 + n]), "sum", dtype), "unaligned")
 
 
+@pytest.mark.parametrize("dtype", ("int32", "float32"))
+@pytest.mark.parametrize("p,n", ((4, 100003), (8, 3 * (1 << 16) + 7)))
+def test_all_gather_rereads_after_partial_sums(rr, dtype, p, n):
+    """4-byte kinds fold into the outputs, so an all-gather step reads
+    predecessor chunks that a reduce-scatter step read while they held
+    partial sums (and, in place, that the first step read as input).  Slices
+    small enough to stay in a CU's L1 between the two reads, but still laid
+    out one XCD per slice: the second read must see the final values, in
+    place and out of place, on every launch."""
+    f0 = rr.ring_exec_failures()
+    for rep in range(4):
+        x = W.random_inputs(90 + rep, p, n, dtype, kind="full" if dtype == "int32" else "normal")
+        want = C.all_reduce_fold(x, "sum", dtype)
+        assert_bitwise(run(rr, x, dtype), want, f"out of place, launch {rep}")
+        xs = to_dev(x, dtype)
+        rr.all_reduce(xs, algo="ring_persistent")
+        assert_bitwise(to_host(xs, dtype), want, f"in place, launch {rep}")
+    assert rr.ring_exec_failures() == f0
+
+
 def test_forced_timeout_ends_the_launch(rr, tuning):
     """A 1 us bound on every wait (set from the host) makes workers give up:
     the launch must end, be counted, and a following normal launch on the
