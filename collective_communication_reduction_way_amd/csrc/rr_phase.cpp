@@ -195,18 +195,20 @@ hipError_t launch_batched(DeviceState& d, const FoldLaunch& f, const PhaseArgs& 
 
 // Workgroups per CU of a batched launch: `asked` if > 0, else 3 or 2, each
 // capped at the kernel's occupancy, whichever leaves fewer empty tile slots
-// in the last round (ties: the fewer rounds); 0 when not even one round of
-// K tiles per workgroup is full.  Full rounds measured best (float32 48 MiB
-// per rank, all-reduce: one round at 3 per CU 80.1-81.0%, two at 2 per CU
-// with the second half empty 77-78%; reduce-scatter 80.8% against 78%).
-uint64_t batch_per_cu(uint64_t tiles, uint64_t cus, int K, int occ, int asked) {
+// in the last round (ties: the fewer rounds).  Full rounds measured best
+// (float32 48 MiB per rank, all-reduce: one round at 3 per CU 80.1-81.0%,
+// two at 2 per CU with the second half empty 77-78%; reduce-scatter 80.8%
+// against 78%).  0 when not even one round of K tiles per workgroup is full,
+// unless `partial`: then a single round that is not full counts too, with
+// its empty slots as the waste.
+uint64_t batch_per_cu(uint64_t tiles, uint64_t cus, int K, int occ, int asked, bool partial) {
   uint64_t best = 0;
   uint64_t best_waste = ~0ull;
   const int options[2] = {asked > 0 ? asked : 3, asked > 0 ? asked : 2};
   for (int c : options) {
     const uint64_t pc = static_cast<uint64_t>(c < occ ? c : occ);
     const uint64_t slots = cus * pc * static_cast<uint64_t>(K);
-    if (pc == 0 || tiles < slots) continue;
+    if (pc == 0 || (tiles < slots && !partial)) continue;
     const uint64_t waste = (tiles + slots - 1) / slots * slots - tiles;
     if (waste < best_waste) {
       best_waste = waste;
@@ -233,11 +235,12 @@ bool phase_supported(const FoldLaunch& f) {
 //     kernel compiled for p = 8 when p is 8 (float16: the run-time loop);
 //     fewer 8-group tiles than CUs (16-bit types: than 2 per CU): 4 groups
 //     per lane, then 2 and 1 while the tiles still fit one per CU;
-//   ring all-reduce, several rounds: 4 groups per lane; with at least one
-//     full round of 4 tiles per workgroup at 2 workgroups per CU, the batched
-//     kernel (below), else 4 workgroups per CU of one tile each (shorter
-//     phases between barriers), the kernel compiled for p = 8 for bfloat16,
-//     the run-time rank loop for the other types;
+//   ring all-reduce, several rounds: 4 groups per lane; the batched kernel
+//     (below), in one partial round when the tiles do not fill one round of
+//     4 tiles per workgroup; with the batches switched off, 4 workgroups per
+//     CU of one tile each (shorter phases between barriers), the kernel
+//     compiled for p = 8 for bfloat16, the run-time rank loop for the other
+//     types;
 //   hierarchical all-reduce: the run-time rank loop, 4 workgroups per CU with
 //     the 16-bit tile of 4 groups per lane, else 2;
 //   reduce-scatter and reduce: 4 groups per lane; with at least one full
@@ -323,13 +326,19 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
     // through this library on one MI355X, p = 8, against one tile per
     // workgroup and round at 4 per CU: float32 32 MiB per rank 75.5% ->
     // 80.4-81.8% of the HBM peak, 96 MiB 76% -> 78.3-78.5%, 128 MiB 76.5% ->
-    // 78.2-78.6%; bfloat16 128 MiB 77% -> 78.8-79.1%.
+    // 78.2-78.6%; bfloat16 128 MiB 77% -> 78.8-79.1%.  Below one full round
+    // (16-32 MiB per rank) a single partial round, same run: float32 18 / 20
+    // / 24 / 27 / 30 MiB 70-71 / 72 / 75 / 74 / 74-75% -> 75-76 / 77.5 / 79 /
+    // 76-77 / 78.5-79%, bfloat16 18 / 20 / 22 / 26 / 30 MiB 69-70 / 72 / 72 /
+    // 75 / 74% -> 77 / 78 / 78 / 78 / 79%; and where the last round would be
+    // short, one partial round at 3 per CU (float32 34 / 36 / 40 / 44 MiB
+    // 76.6 / 77.6 / 75.5 / 77% -> 79.3 / 80.5 / 80 / 80.3%).
     const bool sp = (pt.static_p >= 0 ? pt.static_p != 0 : !f16) && f.args.p == 8;
     const int K = pt.ar_batch == 2 || pt.ar_batch == 4 ? pt.ar_batch : 4;
     int occ = 0;
     e = batch_occupancy(d, f, a, K, sp, s, &occ);
     if (e != hipSuccess) return e;
-    const uint64_t per_cu_b = batch_per_cu(tiles, cus, K, occ, pt.per_cu);
+    const uint64_t per_cu_b = batch_per_cu(tiles, cus, K, occ, pt.per_cu, true);
     if (per_cu_b > 0) {
       const int strips = pt.strips > 0 ? pt.strips : 8;
       if (strips > 1 && a.uniform_tiles != 0) {
@@ -358,7 +367,7 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
     if (e != hipSuccess) return e;
     // 4 per CU measured worse for float32 (128 MiB per rank, two full rounds:
     // 77% against 80% with 2 per CU), hence at most 3
-    const uint64_t per_cu_b = batch_per_cu(tiles, cus, K, occ, pt.per_cu);
+    const uint64_t per_cu_b = batch_per_cu(tiles, cus, K, occ, pt.per_cu, false);
     if (per_cu_b > 0) return launch_batched(d, f, a, tiles, cus * per_cu_b, K, sp, pt, s);
   }
   if (one_out && pt.unroll == 0 && pt.grid == 0 && unroll == 4) {

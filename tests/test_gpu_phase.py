@@ -179,6 +179,11 @@ AR_BATCH_CASES = [
     (8, 16 << 20, "bfloat16", "avg"),
     (8, (8 << 20) + 8 * 8 * 5, "float16", "sum"),
     (5, 5 * (3 << 21), "int32", "min"),
+    # fewer tiles than one full round (16-44 MiB per rank): one partial round
+    (8, 18 << 18, "float32", "sum"),
+    (8, 7087872, "float32", "avg"),
+    (8, (10 << 20) + 8 * 3 + 5, "bfloat16", "max"),
+    (8, 10 << 20, "float32", "min"),
 ]
 
 
