@@ -73,7 +73,8 @@ int env_int(const char* name, int dflt) {
 // interleave, 1 = contiguous tiles, 0 = by the schedule), RR_PHASE_BATCH
 // (reduce-scatter and reduce: tiles per workgroup and round of the batched
 // kernel, 2 or 4; 1 = never; 0 = by the schedule), RR_AR_BATCH (the same
-// for the ring all-reduce of several rounds),
+// for the ring all-reduce of several rounds; 1 also keeps the bucketed
+// all-reduce at one tile per workgroup and round),
 // RR_MULTI_PER_CU (workgroups per compute unit of the bucket and dim-1
 // kernels; 0 = the default), RR_EXEC_TIMEOUT_US (bound of one wait of the persistent ring executor on a
 // neighbour's flag, default 1 s), RR_EXEC_PER_CU (cap on its workgroups per
@@ -1045,7 +1046,7 @@ rr_status_t rr_all_reduce_bucket(const void* const* sendbufs, void* const* recvb
     if (a.npieces == 0) return RR_SUCCESS;
     a.tile0[a.npieces] = a.tiles;
     if (t.log) fprintf(stderr, "[rr] all_reduce_bucket: launch %d, %d pieces, %u tiles\n", launches, a.npieces, a.tiles);
-    const hipError_t e = rr::launch_bucket(a, k, op, t.multi_per_cu, t.pt.sync, t.pt.timeout_us, s);
+    const hipError_t e = rr::launch_bucket(a, k, op, t.multi_per_cu, t.pt.sync, t.pt.ar_batch, t.pt.timeout_us, s);
     if (e != hipSuccess) return hip_fail(e, "all_reduce_bucket");
     ++launches;
     reset();

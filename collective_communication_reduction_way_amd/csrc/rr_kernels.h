@@ -171,8 +171,9 @@ constexpr int kBucketU = 4;
 // per_cu: workgroups per compute unit of the launch (the kernels stride over
 // their work); 0 = the default.  sync: a launch of several rounds separates
 // the read and the write phase of each round with the soft barrier
-// (timeout_us bounds one wait).
-hipError_t launch_bucket(const BucketArgs& a, Kind k, rr_op_t op, int per_cu, int sync, int timeout_us,
+// (timeout_us bounds one wait); batch = 1 keeps one tile per workgroup and
+// round, else such a launch takes the batched rounds.
+hipError_t launch_bucket(const BucketArgs& a, Kind k, rr_op_t op, int per_cu, int sync, int batch, int timeout_us,
                          hipStream_t stream);
 // Barrier timeouts of the bucket kernel on the current device.
 hipError_t bucket_timeouts(unsigned long long* count);

@@ -145,15 +145,19 @@ def test_bucket_barrier(rr, tuning):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("batch", ("0", "1"))
 @pytest.mark.parametrize("p", (5, 8))
 @pytest.mark.parametrize("strips", ("1", "2", "3", "8"))
-def test_bucket_interleaved_tiles(rr, tuning, strips, p):
+def test_bucket_interleaved_tiles(rr, tuning, strips, p, batch):
     """A multi-round bucket whose vector pieces hold whole tiles taken in runs
     of interleaved tiles (1 = contiguous), with ragged and unaligned tensors
-    beside them: the oracle's bits for sum and max, and no wait runs out."""
+    beside them, in batched rounds (several tiles per workgroup and round,
+    one partial round here) and in single-tile rounds (batch 1): the
+    oracle's bits for sum and max, and no wait runs out."""
     sizes = [3 * (1 << 20) + 5, 1 << 22, 777, 9 * 4096 + 8, (1 << 21) + 4]
     parts = [W.random_inputs(91 + i, p, n, "float32") for i, n in enumerate(sizes)]
     tuning.set("RR_PHASE_STRIPS", strips)
+    tuning.set("RR_AR_BATCH", batch)
     t0 = rr.barrier_timeouts()
     for op in ("sum", "max"):
         check_bucket(run_bucket(rr, parts, "float32", op), C.all_reduce_bucket(parts, op, "float32"),
@@ -161,6 +165,24 @@ def test_bucket_interleaved_tiles(rr, tuning, strips, p):
     bparts = [W.random_inputs(95 + i, p, n, "bfloat16") for i, n in enumerate((1 << 23, 4099))]
     check_bucket(run_bucket(rr, bparts, "bfloat16", "avg"), C.all_reduce_bucket(bparts, "avg", "bfloat16"),
                  f"bf16 avg strips={strips}")
+    assert rr.barrier_timeouts() == t0
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("per_cu", ("0", "1", "2"))
+def test_bucket_batched_rounds(rr, tuning, per_cu):
+    """A bucket of several batched rounds (4 tiles per workgroup and round;
+    1 or 2 workgroups per CU requested, or the schedule's choice), ragged
+    and unaligned tensors among large ones, float32 and bfloat16: the
+    oracle's bits, and no wait runs out."""
+    p = 8
+    sizes = [3 * (1 << 22) + 5, 1 << 22, 777, (1 << 21) + 4]
+    parts = [W.random_inputs(71 + i, p, n, "float32") for i, n in enumerate(sizes)]
+    tuning.set("RR_MULTI_PER_CU", per_cu)
+    t0 = rr.barrier_timeouts()
+    check_bucket(run_bucket(rr, parts, "float32", "sum"), C.all_reduce_bucket(parts, "sum", "float32"), "float32")
+    bparts = [W.random_inputs(75 + i, p, n, "bfloat16") for i, n in enumerate((3 * (1 << 23) + 3, 4099, 1 << 22))]
+    check_bucket(run_bucket(rr, bparts, "bfloat16", "avg"), C.all_reduce_bucket(bparts, "avg", "bfloat16"), "bfloat16")
     assert rr.barrier_timeouts() == t0
     torch.cuda.empty_cache()
 
