@@ -168,11 +168,12 @@ __device__ __forceinline__ void for_slice(uint64_t e0, uint64_t e1, bool vec, FV
 }
 
 // Copy the elements [e0, e1) of a slice from src to dst: 16-byte words where
-// both buffers are 16-byte aligned (vec), two words per lane and pass at a
-// distance of one workgroup, so that every wave access is 1 KiB of
-// consecutive bytes and each lane has two loads in flight; single elements
-// elsewhere.  COHERENT (slices under 4 GiB): every load is
-// device-scope (sc1), served by the XCD's L2 around the CU's L1.
+// both buffers are 16-byte aligned (vec), kCopyBatch words per lane and pass
+// at a distance of one workgroup, all loaded before the first is stored
+// (every wave access is 1 KiB of consecutive bytes); single elements
+// elsewhere.  COHERENT (slices under 4 GiB): every load is device-scope
+// (sc1), served by the XCD's L2 around the CU's L1.
+constexpr int kCopyBatch = 8;
 template <bool COHERENT, class S>
 __device__ __forceinline__ void copy_slice(const S* src, S* dst, uint64_t e0, uint64_t e1, bool vec) {
   constexpr int W = 16 / static_cast<int>(sizeof(S));
@@ -205,50 +206,72 @@ __device__ __forceinline__ void copy_slice(const S* src, S* dst, uint64_t e0, ui
   };
   for (uint64_t i = e0 + lane; i < (vec ? u0 : e1); i += kBlock) one(i);
   const uint64_t g1 = u1 / W;
-  uint64_t g = u0 / W + lane;
   u32x4* d = reinterpret_cast<u32x4*>(dst);
-  for (; g + kBlock < g1; g += 2 * kBlock) {
-    const u32x4 x = word(g);
-    const u32x4 y = word(g + kBlock);
-    d[g] = x;
-    d[g + kBlock] = y;
+  for (uint64_t g0 = u0 / W + lane; g0 < g1; g0 += kCopyBatch * kBlock) {
+    u32x4 x[kCopyBatch];
+#pragma unroll
+    for (int j = 0; j < kCopyBatch; ++j)
+      if (g0 + j * kBlock < g1) x[j] = word(g0 + j * kBlock);
+#pragma unroll
+    for (int j = 0; j < kCopyBatch; ++j)
+      if (g0 + j * kBlock < g1) d[g0 + j * kBlock] = x[j];
   }
-  if (g < g1) d[g] = word(g);
   for (uint64_t i = u1 + lane; i < e1; i += kBlock) one(i);
 }
 
 // dst = msg (+) own on the elements [e0, e1) of a slice, the message first;
 // FINISH: then the op's last step (AVG's division) before the conversion to
-// dst's kind.  The kinds share one accumulator type.
+// dst's kind.  The kinds share one accumulator type.  8-element units,
+// kFoldBatch per lane and pass at a distance of one workgroup, all loaded
+// before the first is folded and stored.
+constexpr int kFoldBatch = 4;
 template <class EM, class EO, class ED, class OP, bool FINISH>
 __device__ __forceinline__ void fold_step(const typename EM::S* msg, const typename EO::S* own, typename ED::S* dst,
                                           uint64_t e0, uint64_t e1, bool vec, int32_t div) {
   using A = typename ED::A;
   constexpr int U = 8;
-  for_slice<U>(
-      e0, e1, vec,
-      [&](uint64_t i) {
-        Raw<EM, U> m;
-        Raw<EO, U> l;
-        load_group<false>(m, msg + i);
-        load_group<false>(l, own + i);
-        A vm[U], vl[U];
-        unpack(m, vm);
-        unpack(l, vl);
+  const uint32_t lane = threadIdx.x;
+  uint64_t u0 = e1, u1 = e1;
+  if (vec) {
+    u0 = (e0 + U - 1) / U * U;
+    u1 = e1 / U * U;
+    if (u1 < u0) u0 = u1 = e1;
+  }
+  auto one = [&](uint64_t i) {
+    A v = OP::apply(load_one<EM>(msg + i), load_one<EO>(own + i));
+    if constexpr (FINISH) v = op_finish<OP>(v, div);
+    store_one<ED>(dst + i, v);
+  };
+  for (uint64_t i = e0 + lane; i < (vec ? u0 : e1); i += kBlock) one(i);
+  const uint64_t g1 = u1 / U;
+  for (uint64_t g0 = u0 / U + lane; g0 < g1; g0 += kFoldBatch * kBlock) {
+    Raw<EM, U> m[kFoldBatch];
+    Raw<EO, U> l[kFoldBatch];
 #pragma unroll
-        for (int j = 0; j < U; ++j) {
-          vm[j] = OP::apply(vm[j], vl[j]);
-          if constexpr (FINISH) vm[j] = op_finish<OP>(vm[j], div);
+    for (int j = 0; j < kFoldBatch; ++j) {
+      if (g0 + j * kBlock < g1) {
+        load_group<false>(m[j], msg + (g0 + j * kBlock) * U);
+        load_group<false>(l[j], own + (g0 + j * kBlock) * U);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kFoldBatch; ++j) {
+      if (g0 + j * kBlock < g1) {
+        A vm[U], vl[U];
+        unpack(m[j], vm);
+        unpack(l[j], vl);
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+          vm[k] = OP::apply(vm[k], vl[k]);
+          if constexpr (FINISH) vm[k] = op_finish<OP>(vm[k], div);
         }
-        Raw<ED, U> d;
-        pack(vm, d);
-        store_group<false>(dst + i, d);
-      },
-      [&](uint64_t i) {
-        A v = OP::apply(load_one<EM>(msg + i), load_one<EO>(own + i));
-        if constexpr (FINISH) v = op_finish<OP>(v, div);
-        store_one<ED>(dst + i, v);
-      });
+        Raw<ED, U> o;
+        pack(vm, o);
+        store_group<false>(dst + (g0 + j * kBlock) * U, o);
+      }
+    }
+  }
+  for (uint64_t i = u1 + lane; i < e1; i += kBlock) one(i);
 }
 
 // E: storage kind; EA: accumulator kind of the working buffers.
