@@ -133,7 +133,7 @@ Tuning read_tuning() {
   t.pt.grid = env_int("RR_PHASE_GRID", 0);
   if (t.pt.grid < 0) t.pt.grid = 0;
   t.pt.unroll = env_int("RR_PHASE_U", 0);
-  if (t.pt.unroll != 4 && t.pt.unroll != 8) t.pt.unroll = 0;
+  if (t.pt.unroll != 1 && t.pt.unroll != 2 && t.pt.unroll != 4 && t.pt.unroll != 8) t.pt.unroll = 0;
   t.pt.timeout_us = env_int("RR_PHASE_TIMEOUT_US", 200);
   t.pt.static_p = env_int("RR_PHASE_STATIC", -1);
   t.pt.strips = env_int("RR_PHASE_STRIPS", 0);

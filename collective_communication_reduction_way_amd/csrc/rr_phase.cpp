@@ -275,6 +275,9 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
   const bool one_out = f.mode == FoldMode::kRingShard || f.mode == FoldMode::kAscOne;
   int unroll = phase_default_unroll(f.in_kind, f.mode);
   if ((pt.unroll == 4 || (one_out && pt.unroll == 0)) && small_ok) unroll = 4;
+  // 2 and 1 groups per lane: compiled for the ring all-reduce, reduce-scatter
+  // and reduce without the barrier
+  if ((pt.unroll == 1 || pt.unroll == 2) && small_ok && (ring || one_out)) unroll = pt.unroll;
   // one-output modes run without the barrier, so nothing ties their grid to
   // residency: 32 workgroups per CU (about one tile each) measured best
   int per_cu = pt.per_cu > 0 ? pt.per_cu : (one_out ? 32 : (unroll == 4 ? 4 : 2));
@@ -296,6 +299,30 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
     tiles = tile_segments(f, V, static_cast<uint64_t>(kBlock) * unroll, a);
     if (tiles >= 0x7FFFFFFFull) return hipErrorInvalidValue;
     grid = cus * static_cast<uint64_t>(per_cu);
+  } else if (ring && pt.unroll == 0 && pt.grid == 0 && small_ok && unroll == 8 && tiles > cus &&
+             tiles < 2 * cus) {
+    // one round of between one and two tiles of 8 groups per lane per CU:
+    // the tile that spreads the launch most evenly, one tile per workgroup,
+    // the run-time rank loop (float32 keeps p = 8 unrolled with 8 groups).
+    // Measured through this library on one MI355X, p = 8, against 8 groups
+    // per lane at 2 workgroups per CU (16-bit types: 4 groups, 4 per CU):
+    // float32 8.5 / 9.5 / 10 MiB per rank (up to 1.25 tiles of 8 groups per
+    // CU) with 2 groups 59 / 60 / 63% -> 74 / 74.5 / 75% of the HBM peak,
+    // 10.5 / 11 / 11.5 MiB (up to 1.5) with 4 groups 64 / 67 / 70.5% -> 73 /
+    // 72 / 75%; bfloat16 8.5 / 10 MiB 67.6 / 71.6% -> 73.4 / 73.9%, 13.5 /
+    // 14 / 15 MiB (above 1.5) with 8 groups 69 / 69.4 / 69.1% -> 74.4 /
+    // 73.8 / 74.5%.
+    if (4 * tiles <= 5 * cus) {
+      unroll = 2;
+    } else if (2 * tiles <= 3 * cus) {
+      unroll = 4;
+    }
+    if (pt.static_p < 0) static_p = unroll == 8 && !is_half(f.in_kind);
+    if (unroll != 8) {
+      tiles = tile_segments(f, V, static_cast<uint64_t>(kBlock) * unroll, a);
+      if (tiles >= 0x7FFFFFFFull) return hipErrorInvalidValue;
+    }
+    grid = tiles;
   } else if (ring && pt.unroll == 0 && pt.grid == 0 && small_ok && unroll == 8 &&
              (tiles < cus || (is_half(f.in_kind) && tiles < 2 * cus))) {
     // one round with too few tiles of 8 groups per lane to fill the device
@@ -385,7 +412,7 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
   // Writes are 1/(p+1) of the traffic of the one-output modes: a barrier
   // between the phases of one tile per workgroup gained nothing there
   // (measured); only the batched kernel above separates them.
-  const bool sync = pt.sync && !one_out && a.rounds > 1 && tiles <= kMaxBarrierTiles;
+  const bool sync = pt.sync && !one_out && a.rounds > 1 && unroll >= 4 && tiles <= kMaxBarrierTiles;
   if (sync) {
     // occupancy of the kernel about to run, cached per device and kernel
     const uint32_t key = (static_cast<uint32_t>(f.mode) << 16) | (static_cast<uint32_t>(f.in_kind) << 12) |

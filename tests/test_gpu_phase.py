@@ -222,6 +222,23 @@ def test_small_one_round_tiles(rr, p, n, dtype):
         assert_bitwise(run_ar(rr, x, dtype, op, "ring"), C.all_reduce_ring(x, op, dtype), f"{op}")
 
 
+# Per-rank lengths of one round with between one and two 8-group tiles per
+# CU (the tile that spreads the launch most evenly: 2, 4 or 8 groups per
+# lane, one tile per workgroup), aligned and ragged, p = 8 and 5.
+SPREAD = [(8, 2228224, "float32"), (8, 2752512 + 8 * 7 + 3, "float32"), (8, 3538944, "float32"),
+          (8, 4456448 + 8 * 3 + 5, "bfloat16"), (8, 5767168, "bfloat16"), (8, 7077888, "bfloat16"),
+          (5, 5 * 530000 + 3, "float32"), (5, 5 * 1500000, "float16")]
+
+
+@pytest.mark.parametrize("case", range(len(SPREAD)))
+def test_one_round_spread_tiles(rr, case):
+    p, n, dtype = SPREAD[case]
+    x = W.random_inputs(67 + case, p, n, dtype, kind="normal")
+    for op in ("sum", "max", "avg"):
+        assert_bitwise(run_ar(rr, x, dtype, op, "ring"), C.all_reduce_fold(x, op, dtype), f"{p} {n} {dtype} {op}")
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("p,n", [(8, 1 << 20), (8, (1 << 19) + 88), (8, 40000), (5, 300005), (8, (1 << 18) + 8)])
 @pytest.mark.parametrize("dtype", ("int32", "float32", "bfloat16", "float16"))
 def test_small_reduce_scatter_and_reduce_tiles(rr, p, n, dtype):
