@@ -65,8 +65,9 @@ int env_int(const char* name, int dflt) {
 // buffers), RR_PHASE_SYNC (0 = no barrier between the read and write phases),
 // RR_PHASE_PER_CU (workgroups per compute unit of the phased fold; 0 = by the
 // schedule), RR_PHASE_GRID (explicit workgroup count), RR_PHASE_U (4 = the
-// smaller tile for sums, 8 = the mode's default tile everywhere, 0 = by the
-// schedule), RR_PHASE_STATIC (1 / 0 = the kernels compiled for
+// smaller tile for sums, 8 = the mode's default tile everywhere, 2 or 1 =
+// the smallest tiles, ring all-reduce, reduce-scatter and reduce without the
+// barrier, 0 = by the schedule), RR_PHASE_STATIC (1 / 0 = the kernels compiled for
 // p = 8 / the run-time rank loop; -1 = by mode),
 // RR_PHASE_TIMEOUT_US (bound of one barrier wait, default 200),
 // RR_PHASE_STRIPS (runs of that many tiles whose 256-group strips

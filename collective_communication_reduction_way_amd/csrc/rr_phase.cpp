@@ -233,8 +233,11 @@ bool phase_supported(const FoldLaunch& f) {
 // below):
 //   ring all-reduce, one round: 8 groups per lane, 2 workgroups per CU, the
 //     kernel compiled for p = 8 when p is 8 (float16: the run-time loop);
-//     fewer 8-group tiles than CUs (16-bit types: than 2 per CU): 4 groups
-//     per lane, then 2 and 1 while the tiles still fit one per CU;
+//     between one and two 8-group tiles per CU: 2, 4 or 8 groups as the
+//     8-group tiles number up to 1.25, 1.5 or 2 per CU, one tile per
+//     workgroup, the run-time loop (float32 with 8 groups: p = 8 compiled);
+//     fewer 8-group tiles than CUs (16-bit types: exactly one per CU too): 4
+//     groups per lane, then 2 and 1 while the tiles still fit one per CU;
 //   ring all-reduce, several rounds: 4 groups per lane; the batched kernel
 //     (below), in one partial round when the tiles do not fill one round of
 //     4 tiles per workgroup; with the batches switched off, 4 workgroups per
