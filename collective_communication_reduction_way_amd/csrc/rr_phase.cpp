@@ -199,16 +199,16 @@ hipError_t launch_batched(DeviceState& d, const FoldLaunch& f, const PhaseArgs& 
 // (float32 48 MiB per rank, all-reduce: one round at 3 per CU 80.1-81.0%,
 // two at 2 per CU with the second half empty 77-78%; reduce-scatter 80.8%
 // against 78%).  0 when not even one round of K tiles per workgroup is full,
-// unless `partial`: then a single round that is not full counts too, with
-// its empty slots as the waste.
-uint64_t batch_per_cu(uint64_t tiles, uint64_t cus, int K, int occ, int asked, bool partial) {
+// except that a single round at least `min_fill` percent full counts too,
+// with its empty slots as the waste (min_fill > 100: never).
+uint64_t batch_per_cu(uint64_t tiles, uint64_t cus, int K, int occ, int asked, int min_fill) {
   uint64_t best = 0;
   uint64_t best_waste = ~0ull;
   const int options[2] = {asked > 0 ? asked : 3, asked > 0 ? asked : 2};
   for (int c : options) {
     const uint64_t pc = static_cast<uint64_t>(c < occ ? c : occ);
     const uint64_t slots = cus * pc * static_cast<uint64_t>(K);
-    if (pc == 0 || (tiles < slots && !partial)) continue;
+    if (pc == 0 || (tiles < slots && tiles * 100 < slots * static_cast<uint64_t>(min_fill))) continue;
     const uint64_t waste = (tiles + slots - 1) / slots * slots - tiles;
     if (waste < best_waste) {
       best_waste = waste;
@@ -368,7 +368,7 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
     int occ = 0;
     e = batch_occupancy(d, f, a, K, sp, s, &occ);
     if (e != hipSuccess) return e;
-    const uint64_t per_cu_b = batch_per_cu(tiles, cus, K, occ, pt.per_cu, true);
+    const uint64_t per_cu_b = batch_per_cu(tiles, cus, K, occ, pt.per_cu, 0);
     if (per_cu_b > 0) {
       const int strips = pt.strips > 0 ? pt.strips : 8;
       if (strips > 1 && a.uniform_tiles != 0) {
@@ -397,7 +397,11 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
     if (e != hipSuccess) return e;
     // 4 per CU measured worse for float32 (128 MiB per rank, two full rounds:
     // 77% against 80% with 2 per CU), hence at most 3
-    const uint64_t per_cu_b = batch_per_cu(tiles, cus, K, occ, pt.per_cu, false);
+    // one partial round when at least 70% full: float32 / bfloat16 24 and
+    // 28 MiB per rank (75% and 87.5% full) 77.5-78.5% -> 79.3-79.9% of the
+    // HBM peak for reduce-scatter and reduce; at 50-62.5% full (16, 20 MiB)
+    // the partial round lost 1-2 points
+    const uint64_t per_cu_b = batch_per_cu(tiles, cus, K, occ, pt.per_cu, 70);
     if (per_cu_b > 0) return launch_batched(d, f, a, tiles, cus * per_cu_b, K, sp, pt, s);
   }
   if (one_out && pt.unroll == 0 && pt.grid == 0 && unroll == 4) {

@@ -143,6 +143,26 @@ def test_reduce_scatter_and_reduce_schedules_agree(rr, tuning, env):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("p,L,dtype", [(8, 24 << 18, "float32"), (8, (28 << 18) + 8 * 3 + 5, "float32"),
+                                       (8, 10 << 20, "float32"), (8, (24 << 19) + 16, "bfloat16"), (5, 7 << 20, "int32")])
+def test_reduce_scatter_and_reduce_partial_round(rr, p, L, dtype):
+    """Reduce-scatter and reduce of 24-40 MiB per rank: one batched round that
+    is at least 70% full, aligned and ragged chunks, p = 8 and 5."""
+    n = p * L
+    x = W.random_inputs(70, p, n, dtype, kind="full" if dtype == "int32" else "normal")
+    t0 = rr.barrier_timeouts()
+    xs = to_dev(x, dtype)
+    sh = torch.empty((p, L), dtype=xs.dtype, device="cuda")
+    rr.reduce_scatter(xs, sh)
+    assert_bitwise(to_host(sh, dtype), C.reduce_scatter_ring(x, "sum", dtype), f"reduce_scatter {p} {L} {dtype}")
+    red = torch.empty(n, dtype=xs.dtype, device="cuda")
+    rr.reduce(xs, red, root=1)
+    assert_bitwise(to_host(red, dtype), C.reduce(x, "sum", dtype), f"reduce {p} {L} {dtype}")
+    assert rr.barrier_timeouts() == t0
+    del xs, sh, red
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("env", [{"RR_PHASE_BATCH": "2", "RR_PHASE_PER_CU": "1"},
                                  {"RR_PHASE_BATCH": "4", "RR_PHASE_PER_CU": "1"}])
 @pytest.mark.parametrize("p,dtype,op", [(8, "float32", "sum"), (8, "float32", "max"), (8, "bfloat16", "sum"),
