@@ -66,6 +66,9 @@ def parse_args(argv=None):
     ap.add_argument("--probe-cases", action="store_true",
                     help="run copies of known size (64 MiB to 512 MiB) and one launch pair of each workload's "
                          "collectives, separated by spin-kernel markers, for rocprofv3 --pmc runs; then exit")
+    ap.add_argument("--survey", action="store_true",
+                    help="measure every collective, float32 and bfloat16, p = 8, at per-rank sizes from 2 to 128 MiB "
+                         "(one JSON line per dtype and collective, percent of the HBM peak); then exit")
     ap.add_argument("--ingest-probe", nargs="+", metavar="DB",
                     help="print per-case counter values of --probe-cases runs (rocprofv3 *_results.db files)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH", "WRITE"),
@@ -623,6 +626,42 @@ def threaded_formula_fold(sample, op, dtype, seconds):
     }
 
 
+SURVEY_MIB = (2, 4, 6, 8, 10, 12, 16, 20, 24, 28, 32, 40, 48, 64, 96, 128)
+
+
+def survey(steps):
+    """Every collective of the library on synthetic float32 and bfloat16
+    inputs, p = 8, at the per-rank sizes of SURVEY_MIB: for each, the rate
+    over `steps` timed launches with the cold-cache buffer rotation of the
+    bench line, as a fraction of the HBM peak (algorithmic bytes)."""
+    import numpy as np
+    import torch
+
+    import collective_communication_reduction_way_amd as rr
+
+    stream = torch.cuda.Stream()
+    cpm = spin_cycles_per_ms(torch, stream)
+    reads_writes = {"all_reduce": 16, "reduce_scatter": 9, "all_gather": 9, "reduce": 9, "broadcast": 16}
+    for dtype, esz in (("float32", 4), ("bfloat16", 2)):
+        for coll in ("all_reduce", "reduce_scatter", "all_gather", "reduce", "broadcast"):
+            row = {}
+            for mib in SURVEY_MIB:
+                n = (mib << 20) // esz
+                spec = dict(p=8, n=n, dtype=dtype)
+                x = np.random.default_rng(mib).standard_normal((8, n), dtype=np.float32)
+                if dtype == "bfloat16":
+                    x = (x.view(np.uint32) >> 16).astype(np.uint16)
+                nsets = 1 + math.ceil(COLD_BYTES / (reads_writes[coll] * n * esz))
+                r = Runner(rr, torch, spec, coll, "sum", "ring", 0, x, nsets, stream)
+                ms, _, _ = timed(torch, r, steps, 5, stream, cpm, per_launch=False)
+                row[str(mib)] = round(r.bytes / ms / 1e6 / HBM_PEAK_GBPS * 100, 1)
+                del r
+                torch.cuda.empty_cache()
+            print(json.dumps({"survey": coll, "dtype": dtype, "p": 8, "pct_of_hbm_peak_by_MiB_per_rank": row}),
+                  flush=True)
+    return 0
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.ingest_pmc:
@@ -633,6 +672,8 @@ def main(argv=None):
         return 0
     if args.probe_cases:
         return probe_cases()
+    if args.survey:
+        return survey(min(args.steps, 40))
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the p virtual ranks live in one GPU's HBM and no collective crosses "
               f"GPUs; --gpus {args.gpus} is not supported (run with --gpus 1).", file=sys.stderr)
