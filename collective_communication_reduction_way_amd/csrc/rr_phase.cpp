@@ -149,6 +149,7 @@ hipError_t launch_mode(const FoldLaunch& f, const PhaseArgs& a, unsigned grid, i
 hipError_t launch_batch_mode(const FoldLaunch& f, const PhaseArgs& a, unsigned grid, int K, bool sp, int* occ,
                              hipStream_t s) {
   if (f.mode == FoldMode::kRingAll) return phase_launch_ring_batch(a, f.in_kind, f.op, grid, K, sp, occ, s);
+  if (f.mode == FoldMode::kHierAll) return phase_launch_hier_batch(a, f.in_kind, f.op, grid, K, occ, s);
   return phase_launch_one_batch(a, f.mode, f.in_kind, f.op, grid, K, sp, occ, s);
 }
 
@@ -379,6 +380,33 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
       }
       return launch_batched(d, f, a, tiles, cus * per_cu_b, K, sp, pt, s);
     }
+  }
+  if (f.mode == FoldMode::kHierAll && pt.unroll == 0 && pt.grid == 0 && pt.ar_batch != 1 && pt.sync &&
+      tiles > grid) {
+    // The hierarchical all-reduce of several rounds in batched rounds: as the
+    // ring's (K tiles of 4 groups per lane per workgroup and round, one
+    // partial round allowed, interleaved runs), with the run-time rank loop.
+    const int K = pt.ar_batch == 2 || pt.ar_batch == 4 ? pt.ar_batch : 4;
+    const uint64_t tiles4 = tile_segments(f, V, static_cast<uint64_t>(kBlock) * 4, a);
+    if (tiles4 >= 0x7FFFFFFFull) return hipErrorInvalidValue;
+    if (tiles4 <= kMaxBarrierTiles) {
+      int occ = 0;
+      e = batch_occupancy(d, f, a, K, false, s, &occ);
+      if (e != hipSuccess) return e;
+      const uint64_t per_cu_b = batch_per_cu(tiles4, cus, K, occ, pt.per_cu, 0);
+      if (per_cu_b > 0) {
+        const int strips = pt.strips > 0 ? pt.strips : 8;
+        if (strips > 1 && a.uniform_tiles != 0) {
+          const uint32_t tile = static_cast<uint32_t>(kBlock * 4);
+          const uint32_t full = a.uniform_last == tile ? a.uniform_tiles : a.uniform_tiles - 1;
+          a.strips = static_cast<uint32_t>(strips);
+          a.strip_tiles = full - full % a.strips;
+        }
+        return launch_batched(d, f, a, tiles4, cus * per_cu_b, K, false, pt, s);
+      }
+    }
+    tiles = tile_segments(f, V, static_cast<uint64_t>(kBlock) * unroll, a);
+    if (tiles >= 0x7FFFFFFFull) return hipErrorInvalidValue;
   }
   if (one_out && pt.batch != 1 && pt.unroll == 0 && pt.grid == 0 && pt.sync && unroll == 4 &&
       tiles <= kMaxBarrierTiles) {

@@ -83,6 +83,10 @@ hipError_t phase_launch_ring_batch(const PhaseArgs& a, Kind k, rr_op_t op, unsig
                                    int* occ, hipStream_t s);
 hipError_t phase_launch_hier(const PhaseArgs& a, Kind k, rr_op_t op, unsigned grid, int unroll, bool sync,
                              bool static_p, int* occ, hipStream_t s);
+// The hierarchical all-reduce (kHierAll) in batched rounds, as
+// phase_launch_ring_batch, with the run-time rank loop.
+hipError_t phase_launch_hier_batch(const PhaseArgs& a, Kind k, rr_op_t op, unsigned grid, int batch, int* occ,
+                                   hipStream_t s);
 // The hierarchical variants (kHierRing, kHierAllWire, kHierRingWire), run-time
 // rank loop only (rr_phase_hier_var.hip).
 hipError_t phase_launch_hier_var(const PhaseArgs& a, FoldMode m, Kind k, rr_op_t op, unsigned grid, int unroll,

@@ -325,8 +325,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(phase_wa
 // float32 per rank: 86% with the writes dropped, 75% with them); batching
 // separates the phases and keeps the write phase short against the barrier.
 // Tiles are contiguous.
-//   Ring all-reduce (every output): the tiles interleave in runs as in
-// k_phase, and the write phase goes output by output for all K tiles.
+//   Ring and hierarchical all-reduce (every output): the tiles interleave in
+// runs as in k_phase, and the write phase goes output by output for all K
+// tiles.
 // The barrier orders nothing the results depend on, as in k_phase.
 template <class E, class OP, int P, int U, int K, FoldMode M>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void k_phase_batch(PhaseArgs a) {
@@ -334,9 +335,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
   using A = typename E::A;
   constexpr int V = 16 / sizeof(S);
   constexpr uint32_t kTile = kBlock * U;
-  static_assert(M == FoldMode::kRingShard || M == FoldMode::kAscOne || M == FoldMode::kRingAll,
-                "batched rounds: reduce-scatter, reduce and the ring all-reduce");
-  constexpr bool IL = M == FoldMode::kRingAll;
+  static_assert(M == FoldMode::kRingShard || M == FoldMode::kAscOne || M == FoldMode::kRingAll ||
+                    M == FoldMode::kHierAll,
+                "batched rounds: reduce-scatter, reduce, the ring and the hierarchical all-reduce");
+  constexpr bool IL = writes_all(M);
   const int p = P > 0 ? P : a.f.p;
   sync_claim(a);
   for (uint32_t r = 0; r < a.rounds; ++r) {
@@ -388,7 +390,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     for (int j = 0; j < K; ++j)
 #pragma unroll
       for (int u = 0; u < U; ++u) pack(acc[j][u], o[j][u]);
-    if constexpr (M == FoldMode::kRingAll) {
+    if constexpr (writes_all(M)) {
       for (int q = 0; q < p; ++q) {
         char* d = static_cast<char*>(a.f.out[q]);
 #pragma unroll
@@ -543,8 +545,9 @@ hipError_t batch_by_p(const PhaseArgs& a, unsigned grid, int K, bool static_p, i
   hipError_t e = hipErrorInvalidValue;
   bool launched = false;
   // binary16 takes the run-time rank loop only: with all p = 8 ranks
-  // unrolled its conversions are hoisted past 256 registers and spill
-  if constexpr (!__is_same(E, EF16)) {
+  // unrolled its conversions are hoisted past 256 registers and spill; the
+  // hierarchy (two accumulators per value) too
+  if constexpr (!__is_same(E, EF16) && M != FoldMode::kHierAll) {
     if (static_p && a.f.p == 8) {
       e = K == 2 ? phase_go(&k_phase_batch<E, OP, 8, 4, 2, M>, a, grid, kBlock, occ, s)
                  : phase_go(&k_phase_batch<E, OP, 8, 4, 4, M>, a, grid, kBlock, occ, s);

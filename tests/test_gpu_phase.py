@@ -64,6 +64,33 @@ def test_multi_round_ragged_hier(rr, dtype):
     torch.cuda.empty_cache()
 
 
+HIER_BATCH_CASES = [
+    # (p, G, n, dtype, op): one partial batched round, full rounds, ragged
+    # lengths, groups of 2, 3 and 4
+    (8, 4, 6 << 20, "float32", "sum"),
+    (8, 2, (12 << 20) + 8 * 5 + 3, "bfloat16", "max"),
+    (6, 3, (5 << 20) + 7, "float32", "avg"),
+    (8, 4, 20 << 20, "bfloat16", "sum"),
+]
+
+
+@pytest.mark.parametrize("env", [{}, {"RR_AR_BATCH": "1"}, {"RR_AR_BATCH": "2"}, {"RR_PHASE_STRIPS": "1"}])
+@pytest.mark.parametrize("case", range(len(HIER_BATCH_CASES)))
+def test_hier_batched_rounds(rr, tuning, env, case):
+    """The hierarchical all-reduce of several rounds in batched rounds (K
+    tiles per workgroup and round, interleaved runs, the write phase output
+    by output) and in single-tile rounds: the oracle's bits, no wait runs
+    out."""
+    p, G, n, dtype, op = HIER_BATCH_CASES[case]
+    x = W.random_inputs(76 + case, p, n, dtype)
+    for k, v in env.items():
+        tuning.set(k, v)
+    t0 = rr.barrier_timeouts()
+    assert_bitwise(run_ar(rr, x, dtype, op, "hier", G), C.all_reduce_hier(x, op, dtype, G), f"{p} {G} {n} {env}")
+    assert rr.barrier_timeouts() == t0
+    torch.cuda.empty_cache()
+
+
 def test_forced_barrier_timeouts_keep_results(rr, tuning):
     """A 1 us bound makes the barrier waits run out; the results must not
     change, and the timeouts must be counted."""
