@@ -246,7 +246,9 @@ bool phase_supported(const FoldLaunch& f) {
 //     compiled for p = 8 for bfloat16, the run-time rank loop for the other
 //     types;
 //   hierarchical all-reduce: the run-time rank loop, 4 workgroups per CU with
-//     the 16-bit tile of 4 groups per lane, else 2;
+//     the 16-bit tile of 4 groups per lane, else 2; with several rounds the
+//     batched kernel as for the ring (bfloat16 / float32 24-128 MiB per rank
+//     72.8-75.3 / 73.5-75.1% -> 76.3-81.0 / 77.5-81.8% of the HBM peak);
 //   reduce-scatter and reduce: 4 groups per lane; with at least one full
 //     round of 4 tiles per workgroup at 2 workgroups per CU, the batched
 //     kernel behind the barrier (below), else 32 workgroups per CU (the grid
