@@ -150,6 +150,7 @@ hipError_t launch_batch_mode(const FoldLaunch& f, const PhaseArgs& a, unsigned g
                              hipStream_t s) {
   if (f.mode == FoldMode::kRingAll) return phase_launch_ring_batch(a, f.in_kind, f.op, grid, K, sp, occ, s);
   if (f.mode == FoldMode::kHierAll) return phase_launch_hier_batch(a, f.in_kind, f.op, grid, K, occ, s);
+  if (is_hier(f.mode)) return phase_launch_hier_var_batch(a, f.mode, f.in_kind, f.op, grid, K, occ, s);
   return phase_launch_one_batch(a, f.mode, f.in_kind, f.op, grid, K, sp, occ, s);
 }
 
@@ -383,11 +384,11 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
       return launch_batched(d, f, a, tiles, cus * per_cu_b, K, sp, pt, s);
     }
   }
-  if (f.mode == FoldMode::kHierAll && pt.unroll == 0 && pt.grid == 0 && pt.ar_batch != 1 && pt.sync &&
-      tiles > grid) {
-    // The hierarchical all-reduce of several rounds in batched rounds: as the
-    // ring's (K tiles of 4 groups per lane per workgroup and round, one
-    // partial round allowed, interleaved runs), with the run-time rank loop.
+  if (is_hier(f.mode) && pt.unroll == 0 && pt.grid == 0 && pt.ar_batch != 1 && pt.sync && tiles > grid) {
+    // The hierarchical all-reduce and its variants of several rounds in
+    // batched rounds: as the ring's (K tiles of 4 groups per lane per
+    // workgroup and round, one partial round allowed, interleaved runs),
+    // with the run-time rank loop.
     const int K = pt.ar_batch == 2 || pt.ar_batch == 4 ? pt.ar_batch : 4;
     const uint64_t tiles4 = tile_segments(f, V, static_cast<uint64_t>(kBlock) * 4, a);
     if (tiles4 >= 0x7FFFFFFFull) return hipErrorInvalidValue;

@@ -91,6 +91,9 @@ hipError_t phase_launch_hier_batch(const PhaseArgs& a, Kind k, rr_op_t op, unsig
 // rank loop only (rr_phase_hier_var.hip).
 hipError_t phase_launch_hier_var(const PhaseArgs& a, FoldMode m, Kind k, rr_op_t op, unsigned grid, int unroll,
                                  bool sync, int* occ, hipStream_t s);
+// The same in batched rounds (as phase_launch_hier_batch).
+hipError_t phase_launch_hier_var_batch(const PhaseArgs& a, FoldMode m, Kind k, rr_op_t op, unsigned grid, int batch,
+                                       int* occ, hipStream_t s);
 // Barrier timeouts counted by each translation unit's kernels on the
 // current device.
 hipError_t phase_timeouts_ring(unsigned long long* count);

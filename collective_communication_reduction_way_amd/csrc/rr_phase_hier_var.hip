@@ -1,7 +1,8 @@
 // Instantiations for the hierarchical variants (FoldMode::kHierRing, the
 // page-literal ring all-reduce inside each group, and the two modes that
-// round every group partial to the storage type): the phased fold and the
-// single-pass fold for unaligned buffers, both with the run-time rank loop.
+// round every group partial to the storage type): the phased fold, its
+// batched rounds and the single-pass fold for unaligned buffers, all with the
+// run-time rank loop.
 #include "rr_phase_impl.h"
 
 namespace rr {
@@ -14,6 +15,18 @@ hipError_t phase_launch_hier_var(const PhaseArgs& a, FoldMode m, Kind k, rr_op_t
       return phase_dispatch<FoldMode::kHierAllWire>(a, k, op, grid, unroll, sync, false, occ, s);
     case FoldMode::kHierRingWire:
       return phase_dispatch<FoldMode::kHierRingWire>(a, k, op, grid, unroll, sync, false, occ, s);
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t phase_launch_hier_var_batch(const PhaseArgs& a, FoldMode m, Kind k, rr_op_t op, unsigned grid, int batch,
+                                       int* occ, hipStream_t s) {
+  switch (m) {
+    case FoldMode::kHierRing: return batch_dispatch<FoldMode::kHierRing>(a, k, op, grid, batch, false, occ, s);
+    case FoldMode::kHierAllWire: return batch_dispatch<FoldMode::kHierAllWire>(a, k, op, grid, batch, false, occ, s);
+    case FoldMode::kHierRingWire:
+      return batch_dispatch<FoldMode::kHierRingWire>(a, k, op, grid, batch, false, occ, s);
     default: break;
   }
   return hipErrorInvalidValue;

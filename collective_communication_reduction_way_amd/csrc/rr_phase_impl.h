@@ -335,9 +335,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
   using A = typename E::A;
   constexpr int V = 16 / sizeof(S);
   constexpr uint32_t kTile = kBlock * U;
-  static_assert(M == FoldMode::kRingShard || M == FoldMode::kAscOne || M == FoldMode::kRingAll ||
-                    M == FoldMode::kHierAll,
-                "batched rounds: reduce-scatter, reduce, the ring and the hierarchical all-reduce");
+  static_assert(M == FoldMode::kRingShard || M == FoldMode::kAscOne || writes_all(M),
+                "batched rounds: reduce-scatter, reduce, the ring and the hierarchical all-reduces");
   constexpr bool IL = writes_all(M);
   const int p = P > 0 ? P : a.f.p;
   sync_claim(a);
@@ -547,7 +546,7 @@ hipError_t batch_by_p(const PhaseArgs& a, unsigned grid, int K, bool static_p, i
   // binary16 takes the run-time rank loop only: with all p = 8 ranks
   // unrolled its conversions are hoisted past 256 registers and spill; the
   // hierarchy (two accumulators per value) too
-  if constexpr (!__is_same(E, EF16) && M != FoldMode::kHierAll) {
+  if constexpr (!__is_same(E, EF16) && !is_hier(M)) {
     if (static_p && a.f.p == 8) {
       e = K == 2 ? phase_go(&k_phase_batch<E, OP, 8, 4, 2, M>, a, grid, kBlock, occ, s)
                  : phase_go(&k_phase_batch<E, OP, 8, 4, 4, M>, a, grid, kBlock, occ, s);

@@ -79,10 +79,13 @@ def test_variants_sweep(rr, p, n, dtype):
                 assert_bitwise(run(rr, x, dtype, op, G, **kw), want(x, dtype, op, G, **kw), f"G={G} {kw} {op}")
 
 
+@pytest.mark.parametrize("batch", ("0", "1"))
 @pytest.mark.parametrize("dtype", ("float32", "bfloat16", "float16"))
-def test_variants_multi_round(rr, dtype):
+def test_variants_multi_round(rr, tuning, dtype, batch):
     """Sizes that take several rounds of the phased fold (with its barrier),
-    ragged group-chunk bounds."""
+    ragged group-chunk bounds, in batched rounds (batch 0, the default) and
+    in single-tile rounds (batch 1)."""
+    tuning.set("RR_AR_BATCH", batch)
     p = 8
     n = 8 * (1 << 20) * (2 if dtype != "float32" else 1) + 13
     x = W.random_inputs(72, p, n, dtype)
