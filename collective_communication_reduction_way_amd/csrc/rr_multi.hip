@@ -115,10 +115,9 @@ struct RotFold {
 // re-read the tile's last unit; never stored) and the valid unit count.
 // IL (the kernel with the barrier): the whole tiles at the start of a vector
 // piece are taken in runs of a.strips tiles whose strips interleave.
-template <class E, bool VEC, bool IL>
-__device__ __forceinline__ uint32_t bucket_offsets(const BucketArgs& a, int pc, uint32_t k,
-                                                   uint64_t (&off)[kBucketU]) {
-  constexpr uint32_t kUnits = static_cast<uint32_t>(kBlock) * kBucketU;
+template <class E, bool VEC, bool IL, int U>
+__device__ __forceinline__ uint32_t bucket_offsets(const BucketArgs& a, int pc, uint32_t k, uint64_t (&off)[U]) {
+  constexpr uint32_t kUnits = static_cast<uint32_t>(kBlock) * U;
   constexpr uint32_t kUnitBytes = VEC ? 16u : static_cast<uint32_t>(sizeof(typename E::S));
   const uint32_t lane = threadIdx.x;
   if constexpr (IL && VEC) {
@@ -130,29 +129,28 @@ __device__ __forceinline__ uint32_t bucket_offsets(const BucketArgs& a, int pc, 
       const uint64_t base =
           a.start[pc] * sizeof(typename E::S) + (static_cast<uint64_t>(run) * S * kUnits + j * kBlock) * kUnitBytes;
 #pragma unroll
-      for (int u = 0; u < kBucketU; ++u) off[u] = base + static_cast<uint64_t>(lane + u * S * kBlock) * kUnitBytes;
+      for (int u = 0; u < U; ++u) off[u] = base + static_cast<uint64_t>(lane + u * S * kBlock) * kUnitBytes;
       return kUnits;
     }
   }
   const uint32_t valid = min(kUnits, a.units[pc] - k * kUnits);  // units of this tile, >= 1
   const uint64_t base = a.start[pc] * sizeof(typename E::S) + static_cast<uint64_t>(k) * kUnits * kUnitBytes;
 #pragma unroll
-  for (int u = 0; u < kBucketU; ++u) off[u] = base + min(lane + u * kBlock, valid - 1) * kUnitBytes;
+  for (int u = 0; u < U; ++u) off[u] = base + min(lane + u * kBlock, valid - 1) * kUnitBytes;
   return valid;
 }
 
 // Write the folded tile to all p outputs of piece pc.
-template <class E, class OP, bool VEC>
-__device__ __forceinline__ void bucket_store(const BucketArgs& a, int pc, uint32_t valid,
-                                             const uint64_t (&off)[kBucketU],
-                                             const typename E::A (&acc)[kBucketU][RotFold<E, OP, kBucketU, VEC>::V]) {
-  using F = RotFold<E, OP, kBucketU, VEC>;
+template <class E, class OP, bool VEC, int U>
+__device__ __forceinline__ void bucket_store(const BucketArgs& a, int pc, uint32_t valid, const uint64_t (&off)[U],
+                                             const typename E::A (&acc)[U][RotFold<E, OP, U, VEC>::V]) {
+  using F = RotFold<E, OP, U, VEC>;
   const uint32_t lane = threadIdx.x;
   const int p = a.p;
   for (int r = 0; r < p; ++r) {
     char* d = static_cast<char*>(const_cast<void*>(a.ptr[a.base[pc] + p + r]));
 #pragma unroll
-    for (int u = 0; u < kBucketU; ++u)
+    for (int u = 0; u < U; ++u)
       if (lane + u * kBlock < valid) F::store(d, off[u], acc[u]);
   }
 }
@@ -179,17 +177,17 @@ __device__ __forceinline__ int bucket_piece(const BucketArgs& a, uint32_t t) {
 // the two phases, so that for the length of a phase the device only reads,
 // or only writes (as in the phased fold).  Tiles of scalar pieces (elements
 // of tensors that are not 16-byte aligned) are written before the barrier.
-template <class E, class OP, bool SYNC, int K>
+template <class E, class OP, bool SYNC, int K, int U>
 __global__ __launch_bounds__(kBlock) void k_bucket(BucketArgs a) {
-  using FV = RotFold<E, OP, kBucketU, true>;
-  using FS = RotFold<E, OP, kBucketU, false>;
+  using FV = RotFold<E, OP, U, true>;
+  using FS = RotFold<E, OP, U, false>;
   if constexpr (SYNC) sync_claim_at(a.sync.slot, a.sync.tag);
   for (uint32_t r = 0; r < a.rounds; ++r) {
     int pc[K];
     bool vec[K];
     uint32_t valid[K];
-    uint64_t off[K][kBucketU];
-    typename E::A acc[K][kBucketU][FV::V];
+    uint64_t off[K][U];
+    typename E::A acc[K][U][FV::V];
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       const uint32_t t = (r * K + j) * gridDim.x + blockIdx.x;
@@ -201,20 +199,20 @@ __global__ __launch_bounds__(kBlock) void k_bucket(BucketArgs a) {
         const uint32_t k = t - a.tile0[pc[j]];
         vec[j] = a.vec[pc[j]] != 0;
         if (vec[j]) {
-          valid[j] = bucket_offsets<E, true, SYNC>(a, pc[j], k, off[j]);
+          valid[j] = bucket_offsets<E, true, SYNC, U>(a, pc[j], k, off[j]);
           FV::run(a.ptr + a.base[pc[j]], a.rot[pc[j]], a.p, off[j], a.div, acc[j]);
         } else {
-          typename E::A one[kBucketU][FS::V];
-          const uint32_t n1 = bucket_offsets<E, false, SYNC>(a, pc[j], k, off[j]);
+          typename E::A one[U][FS::V];
+          const uint32_t n1 = bucket_offsets<E, false, SYNC, U>(a, pc[j], k, off[j]);
           FS::run(a.ptr + a.base[pc[j]], a.rot[pc[j]], a.p, off[j], a.div, one);
-          bucket_store<E, OP, false>(a, pc[j], n1, off[j], one);
+          bucket_store<E, OP, false, U>(a, pc[j], n1, off[j], one);
         }
       }
     }
     if constexpr (SYNC) soft_barrier_at(a.sync.slot, a.sync.tag, a.sync.timeout_ticks, r);
 #pragma unroll
     for (int j = 0; j < K; ++j)
-      if (vec[j]) bucket_store<E, OP, true>(a, pc[j], valid[j], off[j], acc[j]);
+      if (vec[j]) bucket_store<E, OP, true, U>(a, pc[j], valid[j], off[j], acc[j]);
   }
 }
 
@@ -411,15 +409,15 @@ unsigned stream_grid(uint64_t work_units, uint64_t per_block, int rows, int per_
   return static_cast<unsigned>(g);
 }
 
-// Workgroups of k_bucket<..., true, K> that one compute unit keeps
+// Workgroups of k_bucket<..., true, K, kBucketU> that one compute unit keeps
 // resident, per (kind, op, K), queried once.
 template <class E, class OP, int K>
 int bucket_occupancy() {
   static int occ = 0;
   int v = __atomic_load_n(&occ, __ATOMIC_RELAXED);
   if (v == 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, reinterpret_cast<const void*>(&k_bucket<E, OP, true, K>),
-                                                     kBlock, 0) != hipSuccess || v < 1)
+    const void* kernel = reinterpret_cast<const void*>(&k_bucket<E, OP, true, K, kBucketU>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kernel, kBlock, 0) != hipSuccess || v < 1)
       v = 1;
     __atomic_store_n(&occ, v, __ATOMIC_RELAXED);
   }
@@ -464,7 +462,7 @@ hipError_t bucket_go(BucketArgs a, int per_cu, int sync, int batch, int timeout_
       grid = static_cast<unsigned>(ncu * best);
       a.rounds = static_cast<uint32_t>((a.tiles + static_cast<uint64_t>(grid) * K - 1) / (static_cast<uint64_t>(grid) * K));
       if (a.strips == 0) a.strips = 8;
-      return launch(&k_bucket<E, OP, true, K>, a, dim3(grid), s);
+      return launch(&k_bucket<E, OP, true, K, kBucketU>, a, dim3(grid), s);
     }
     // the barrier needs every workgroup resident at once
     const uint64_t resident = ncu * bucket_occupancy<E, OP, 1>();
@@ -475,9 +473,24 @@ hipError_t bucket_go(BucketArgs a, int per_cu, int sync, int batch, int timeout_
     // while a GPT-2 block's 12 gradients (27 MiB, 2 rounds) lost 1-3
     // points with any run length
     if (a.strips == 0) a.strips = a.rounds >= 3 ? 2 : 1;
-    return launch(&k_bucket<E, OP, true, 1>, a, dim3(grid), s);
+    return launch(&k_bucket<E, OP, true, 1, kBucketU>, a, dim3(grid), s);
   }
-  return launch(&k_bucket<E, OP, false, 1>, a, dim3(grid), s);
+  // One round of between one and two tiles of twice the units per CU (the
+  // ring all-reduce's rule): tiles of 8 units per lane, one per workgroup.
+  if (batch != 1 && per_cu <= 0) {
+    const int cus = cus_of(s);
+    const uint64_t ncu = static_cast<uint64_t>(cus > 0 ? cus : 256);
+    constexpr uint32_t kUnits8 = static_cast<uint32_t>(kBlock) * 8;
+    uint32_t tiles8 = 0;
+    for (int i = 0; i < a.npieces; ++i) tiles8 += (a.units[i] + kUnits8 - 1) / kUnits8;
+    if (tiles8 > ncu && tiles8 < 2 * ncu) {
+      for (int i = 0; i < a.npieces; ++i) a.tile0[i + 1] = a.tile0[i] + (a.units[i] + kUnits8 - 1) / kUnits8;
+      a.tiles = tiles8;
+      a.rounds = 1;
+      return launch(&k_bucket<E, OP, false, 1, 8>, a, dim3(tiles8), s);
+    }
+  }
+  return launch(&k_bucket<E, OP, false, 1, kBucketU>, a, dim3(grid), s);
 }
 
 template <class E>

@@ -118,6 +118,22 @@ def test_bucket_gpt2_block_full_size(rr):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("batch", ("0", "1"))
+@pytest.mark.parametrize("dtype,scale", [("bfloat16", 1), ("float32", 2), ("float16", 1)])
+def test_bucket_one_round_tile_sizes(rr, tuning, dtype, scale, batch):
+    """One-round buckets of GPT-2 block shapes (13.5 MiB per rank): tiles of
+    8 units per lane, one per workgroup, where they number between one and
+    two per CU (batch 0, the default), and the tiles of 4 units (batch 1);
+    every element against the oracle."""
+    p = 8
+    sizes = [max(8, n // scale) + 3 * i for i, n in enumerate(W.BUCKETS["gpt2_block_fp32_p8"]["sizes"])]
+    parts = [W.random_inputs(101 + i, p, n, dtype) for i, n in enumerate(sizes)]
+    tuning.set("RR_AR_BATCH", batch)
+    for op in ("avg", "max"):
+        check_bucket(run_bucket(rr, parts, dtype, op), C.all_reduce_bucket(parts, op, dtype), f"{dtype} {op}")
+    torch.cuda.empty_cache()
+
+
 def test_bucket_barrier(rr, tuning):
     """A bucket of several rounds separates its read and write phases with
     the soft barrier.  A 1 us bound makes the waits run out: the results must
