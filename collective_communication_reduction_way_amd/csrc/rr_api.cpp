@@ -74,8 +74,8 @@ int env_int(const char* name, int dflt) {
 // interleave, 1 = contiguous tiles, 0 = by the schedule), RR_PHASE_BATCH
 // (reduce-scatter and reduce: tiles per workgroup and round of the batched
 // kernel, 2 or 4; 1 = never; 0 = by the schedule), RR_AR_BATCH (the same
-// for the ring all-reduce of several rounds; 1 also keeps the bucketed
-// all-reduce at one tile per workgroup and round),
+// for the ring and hierarchical all-reduces of several rounds; 1 also keeps
+// the bucketed all-reduce at one tile of 4 units per workgroup and round),
 // RR_MULTI_PER_CU (workgroups per compute unit of the bucket and dim-1
 // kernels; 0 = the default), RR_EXEC_TIMEOUT_US (bound of one wait of the persistent ring executor on a
 // neighbour's flag, default 1 s), RR_EXEC_PER_CU (cap on its workgroups per
