@@ -71,7 +71,7 @@ int env_int(const char* name, int dflt) {
 // p = 8 / the run-time rank loop; -1 = by mode),
 // RR_PHASE_TIMEOUT_US (bound of one barrier wait, default 200),
 // RR_PHASE_STRIPS (runs of that many tiles whose 256-group strips
-// interleave, 1 = contiguous tiles, 0 = by the schedule), RR_PHASE_BATCH
+// interleave, up to 64; 1 = contiguous tiles, 0 = by the schedule), RR_PHASE_BATCH
 // (reduce-scatter and reduce: tiles per workgroup and round of the batched
 // kernel, 2 or 4; 1 = never; 0 = by the schedule), RR_AR_BATCH (the same
 // for the ring and hierarchical all-reduces of several rounds; 1 also keeps
@@ -138,7 +138,7 @@ Tuning read_tuning() {
   t.pt.timeout_us = env_int("RR_PHASE_TIMEOUT_US", 200);
   t.pt.static_p = env_int("RR_PHASE_STATIC", -1);
   t.pt.strips = env_int("RR_PHASE_STRIPS", 0);
-  if (t.pt.strips < 0 || t.pt.strips > 16) t.pt.strips = 0;
+  if (t.pt.strips < 0 || t.pt.strips > 64) t.pt.strips = 0;
   t.pt.batch = env_int("RR_PHASE_BATCH", 0);
   if (t.pt.batch != 1 && t.pt.batch != 2 && t.pt.batch != 4) t.pt.batch = 0;
   t.pt.ar_batch = env_int("RR_AR_BATCH", 0);

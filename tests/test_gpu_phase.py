@@ -235,7 +235,8 @@ AR_BATCH_CASES = [
 
 
 @pytest.mark.parametrize("env", [{}, {"RR_AR_BATCH": "2"}, {"RR_AR_BATCH": "4", "RR_PHASE_PER_CU": "1"},
-                                 {"RR_AR_BATCH": "2", "RR_PHASE_STRIPS": "16"},
+                                 {"RR_AR_BATCH": "2", "RR_PHASE_STRIPS": "16"}, {"RR_PHASE_STRIPS": "8"},
+                                 {"RR_PHASE_STRIPS": "64"},
                                  {"RR_AR_BATCH": "4", "RR_PHASE_STATIC": "0"}, {"RR_AR_BATCH": "1"}])
 @pytest.mark.parametrize("case", range(len(AR_BATCH_CASES)))
 def test_ring_all_reduce_batched_rounds(rr, tuning, env, case):
