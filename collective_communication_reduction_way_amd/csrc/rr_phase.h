@@ -15,7 +15,7 @@ constexpr int kSyncSubs = 8;                       // arrival counters per set
 constexpr int kSyncCounters = kSyncSubs + 1;       // arrival counters, then the top counter
 constexpr int kSyncStride = 16;                    // 64-bit words: one 128-byte line per counter
 constexpr int kLaunchShift = 24;                   // counter = (launch tag << 24) + count
-constexpr uint64_t kMaxBarrierTiles = 1ull << 23;  // arrivals per launch stay below 2^24
+constexpr uint64_t kMaxBarrierTiles = 1ull << 23;  // a counter's arrivals (2 per round) stay below 2^24
 // Launch tag of a launch captured into a graph: a graph replays its kernel
 // arguments unchanged, so such a launch always carries this tag (eager
 // launches use 2, 3, ...), and a reset of the slot's counters is captured

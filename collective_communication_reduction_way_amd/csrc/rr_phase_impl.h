@@ -17,8 +17,18 @@
 // registers; then it writes the result to every output.  HBM serves pure read
 // streams and pure write streams at a much higher rate than an interleaving of
 // both, so between the read phase and the write phase of a round the
-// workgroups meet at a soft grid barrier: for the length of a phase the whole
-// chip then reads, or writes, only.  The barrier orders nothing that the
+// workgroups meet at a soft grid barrier, and in batched rounds
+// (k_phase_batch) the folds that write every rank meet again between a
+// round's write phase and the next round's read phase: for the length of a
+// phase the whole chip then reads, or writes, only.  Without the second
+// barrier the workgroups that finish their stores first start the next
+// round's reads while the others still write; per-workgroup wall-clock stamps
+// of a 96 MiB float32 all-reduce (two batched rounds) showed each pure phase
+// at about 85% of the HBM peak and that mixed stretch at about 75%, and the
+// second barrier took the launch from 78% to 81% (128 MiB bfloat16, four
+// rounds: 80.5% -> 83%).  In k_phase's rounds of one tile per workgroup the
+// phases are short and the second barrier lost up to 2.5 points, so those
+// rounds keep one.  The barrier orders nothing that the
 // results depend on (every workgroup reads and writes only its own tiles), so
 // it only shapes the traffic: its wait is bounded by a wall-clock timeout, and
 // a workgroup that times out simply goes on.  Results are therefore the same
@@ -338,6 +348,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
   static_assert(M == FoldMode::kRingShard || M == FoldMode::kAscOne || writes_all(M),
                 "batched rounds: reduce-scatter, reduce, the ring and the hierarchical all-reduces");
   constexpr bool IL = writes_all(M);
+  // WB: the workgroups meet again between a round's write phase and the
+  // next round's read phase (the folds that write every rank).
+  constexpr bool WB = writes_all(M);
   const int p = P > 0 ? P : a.f.p;
   sync_claim(a);
   for (uint32_t r = 0; r < a.rounds; ++r) {
@@ -383,7 +396,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         read_fold<E, OP, P, U, M, IL>(a.f, seg[j], p, off[j], valid[j], gap[j], acc[j]);
       }
     }
-    soft_barrier(a, r);
+    soft_barrier(a, WB ? 2 * r : r);
     Raw<E, V> o[K][U];
 #pragma unroll
     for (int j = 0; j < K; ++j)
@@ -414,6 +427,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
           store_tile<true, false>(d, o[j], valid[j], 0);
         }
       }
+    }
+    if constexpr (WB) {
+      if (r + 1 < a.rounds) soft_barrier(a, 2 * r + 1);
     }
   }
 }

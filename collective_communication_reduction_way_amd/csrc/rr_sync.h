@@ -1,6 +1,7 @@
 // rr_sync.h -- the soft grid barrier between the read phase and the write
-// phase of a round (gfx950), shared by the phased fold (rr_phase_impl.h) and
-// the bucketed all-reduce (rr_multi.hip).  Internal header.
+// phase of a round, and between the rounds (gfx950), shared by the phased
+// fold (rr_phase_impl.h) and the bucketed all-reduce (rr_multi.hip).
+// Internal header.
 //
 // Per slot, kSyncSubs arrival counters and one top counter, each a 64-bit
 // word on its own 128-byte line.  Workgroup b arrives on counter
@@ -58,7 +59,9 @@ __global__ __launch_bounds__(64) void k_sync_reset(uint32_t slot) {
     __hip_atomic_store(sync_counter(slot, threadIdx.x), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Arrive at barrier `round` and wait (bounded) until all G workgroups have.
+// Arrive at barrier number `round` of the launch (0, 1, 2, ... in order: one
+// or two per round of the kernel) and wait (bounded) until all G workgroups
+// have.
 __device__ __forceinline__ void soft_barrier_at(uint32_t slot, unsigned long long tag, uint32_t timeout_ticks,
                                                 uint32_t round) {
   __syncthreads();
