@@ -21,7 +21,7 @@ launch cost does not idle the GPU.
 
 Besides the timed region, the line reports the spread of single launches (a
 separate pass with events around every launch), the copy ceilings of the
-same box (a 1 GiB hipMemcpyAsync device-to-device copy and librr's own copy
+same machine (a 1 GiB hipMemcpyAsync device-to-device copy and librr's own copy
 kernel), and the CPU oracle timed on the host's cores.
 
 Prints ONE JSON line on stdout.  ``--extra`` prints further measurements
@@ -483,7 +483,7 @@ def launch_spread(torch, runner, steps, stream, cycles_per_ms):
 
 
 def copy_ceilings(torch, rr, stream, nbytes=1 << 30, reps=10):
-    """What a plain copy reaches on the same box, as the achievable reference
+    """What a plain copy reaches on the same machine, as the achievable reference
     for the collectives: a hipMemcpyAsync device-to-device copy of 1 GiB, and
     librr's own copy kernel (a broadcast to one rank: the fan-out kernel with
     one destination) on the same buffers.  GB/s count the bytes read plus the

@@ -366,7 +366,9 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
     // 76-77 / 78.5-79%, bfloat16 18 / 20 / 22 / 26 / 30 MiB 69-70 / 72 / 72 /
     // 75 / 74% -> 77 / 78 / 78 / 78 / 79%; and where the last round would be
     // short, one partial round at 3 per CU (float32 34 / 36 / 40 / 44 MiB
-    // 76.6 / 77.6 / 75.5 / 77% -> 79.3 / 80.5 / 80 / 80.3%).
+    // 76.6 / 77.6 / 75.5 / 77% -> 79.3 / 80.5 / 80 / 80.3%).  With the
+    // workgroups meeting again before each later read phase (k_phase_batch):
+    // float32 96 / 128 MiB 81 / 83%, bfloat16 128 MiB 83%.
     const bool sp = (pt.static_p >= 0 ? pt.static_p != 0 : !f16) && f.args.p == 8;
     const int K = pt.ar_batch == 2 || pt.ar_batch == 4 ? pt.ar_batch : 4;
     int occ = 0;
@@ -422,7 +424,7 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
     // workgroup and round behind the soft barrier, so that the writes come in
     // bursts instead of trickling between the reads.  Measured through this
     // library on one MI355X, p = 8, against one tile per workgroup without a
-    // barrier (two boxes): float32 96 MiB per rank 75-76% -> 79-81.5% of the
+    // barrier (two machines): float32 96 MiB per rank 75-76% -> 79-81.5% of the
     // HBM peak, bfloat16 128 MiB 75% -> 80.5-82%, 64 MiB 75% -> 80%; at
     // 16 MiB and below (less than one full round) the batches lost.
     const int K = pt.batch == 2 || pt.batch == 4 ? pt.batch : 4;
@@ -489,7 +491,7 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
   // Interleaved tiles: whole runs of `strips` full tiles at the start of
   // every segment (uniform tilings only).  Measured with the bench on one
   // MI355X, each figure against the kernels without interleaving on the
-  // same box: the folds that write every rank gain when a launch has
+  // same machine: the folds that write every rank gain when a launch has
   // several rounds (96 MiB float32 all-reduce 72.8% -> 75.6% of the HBM
   // peak with runs of 8; 128 MiB bfloat16 74.5% -> 77.1% with runs of 4).
   // One-round launches (8 MiB per rank) lost with it, and reduce-scatter

@@ -85,7 +85,7 @@ __device__ __forceinline__ void soft_barrier_at(uint32_t slot, unsigned long lon
     // clocks between polls eases that line for the increments the waiters
     // wait for (sleep 2 / 4 / 8 / 16 / 32: 96 MiB fp32 all-reduce 76.0 /
     // 76.3 / 76.4 / 76.2 / 75.1%, 128 MiB bf16 77.7 / 77.9 / 78.0 / 77.6 /
-    // 76.1%, the same box).
+    // 76.1%, the same machine).
     while (__hip_atomic_load(top, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
       __builtin_amdgcn_s_sleep(8);
       if (wall_clock64() - t0 > timeout_ticks) {
