@@ -297,7 +297,21 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
   if (tiles >= 0x7FFFFFFFull) return hipErrorInvalidValue;
   uint64_t grid = pt.grid > 0 ? static_cast<uint64_t>(pt.grid) : cus * static_cast<uint64_t>(per_cu);
   bool several = false;  // ring all-reduce of several rounds, default tiling
-  if (ring && pt.unroll == 0 && pt.grid == 0 && small_ok && unroll == 8 && tiles > grid) {
+  // Batched rounds (below) also take the ring all-reduces of more than 13,
+  // and the hierarchical ones of more than 12, strips of kBlock groups per
+  // CU, which one round of their default tile would hold: one batched round
+  // with the barrier against one barrier-free round, measured through this
+  // library on one MI355X, p = 8 (per-rank MiB): ring float32 13 / 14 / 16
+  // MiB 75.0 / 73.7 / 76.8% -> 73.5 / 74.1 / 78.1% of the HBM peak,
+  // bfloat16 13 / 16 MiB 74.6 / 75.9% -> 72.7 / 77.1%, float16 16 MiB 75.6%
+  // -> 77.7%; hierarchical bfloat16 12 / 13 / 16 MiB 77.7 / 65.0 / 74.8% ->
+  // 71.5 / 71.5 / 76.7%, with wire rounding 16 MiB 70.9% -> 72.3%, float32
+  // 16 MiB 75.9% -> 77.5%; at 10 and 12 MiB the barrier-free ring round
+  // stays ahead by 3-7 points.
+  const uint64_t batch_strips_per_cu = is_hier(f.mode) ? 12 : 13;
+  const bool batch_early = pt.ar_batch != 1 && pt.sync;
+  if (ring && pt.unroll == 0 && pt.grid == 0 && small_ok && unroll == 8 &&
+      (tiles > grid || (batch_early && tiles * unroll > batch_strips_per_cu * cus))) {
     // several rounds: the smaller tile, more workgroups
     several = true;
     unroll = 4;
@@ -318,7 +332,8 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
     // 10.5 / 11 / 11.5 MiB (up to 1.5) with 4 groups 64 / 67 / 70.5% -> 73 /
     // 72 / 75%; bfloat16 8.5 / 10 MiB 67.6 / 71.6% -> 73.4 / 73.9%, 13.5 /
     // 14 / 15 MiB (above 1.5) with 8 groups 69 / 69.4 / 69.1% -> 74.4 /
-    // 73.8 / 74.5%.
+    // 73.8 / 74.5%.  Above 1.5 tiles per CU the batched round above now
+    // takes the launch, unless batches are switched off.
     if (4 * tiles <= 5 * cus) {
       unroll = 2;
     } else if (2 * tiles <= 3 * cus) {
@@ -390,7 +405,8 @@ hipError_t launch_fold_phase(const FoldLaunch& f, const PhaseTuning& pt, hipStre
       return launch_batched(d, f, a, tiles, cus * per_cu_b, K, sp, pt, s);
     }
   }
-  if (is_hier(f.mode) && pt.unroll == 0 && pt.grid == 0 && pt.ar_batch != 1 && pt.sync && tiles > grid) {
+  if (is_hier(f.mode) && pt.unroll == 0 && pt.grid == 0 && pt.ar_batch != 1 && pt.sync &&
+      (tiles > grid || tiles * static_cast<uint64_t>(unroll) > batch_strips_per_cu * cus)) {
     // The hierarchical all-reduce and its variants of several rounds in
     // batched rounds: as the ring's (K tiles of 4 groups per lane per
     // workgroup and round, one partial round allowed, interleaved runs),

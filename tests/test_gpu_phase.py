@@ -278,10 +278,16 @@ SPREAD = [(8, 2228224, "float32"), (8, 2752512 + 8 * 7 + 3, "float32"), (8, 3538
           (5, 5 * 530000 + 3, "float32"), (5, 5 * 1500000, "float16")]
 
 
+@pytest.mark.parametrize("env", [{}, {"RR_AR_BATCH": "1"}])
 @pytest.mark.parametrize("case", range(len(SPREAD)))
-def test_one_round_spread_tiles(rr, case):
+def test_one_round_spread_tiles(rr, tuning, env, case):
+    """Between one and two tiles of 8 groups per lane per CU: the one-round
+    tiles of 2, 4 or 8 groups, or above 1.5 per CU one batched round (with
+    batches switched off, the 8-group round)."""
     p, n, dtype = SPREAD[case]
     x = W.random_inputs(67 + case, p, n, dtype, kind="normal")
+    for k, v in env.items():
+        tuning.set(k, v)
     for op in ("sum", "max", "avg"):
         assert_bitwise(run_ar(rr, x, dtype, op, "ring"), C.all_reduce_fold(x, op, dtype), f"{p} {n} {dtype} {op}")
     torch.cuda.empty_cache()
