@@ -263,8 +263,12 @@ hipError_t launch_fanout(const FanoutArgs& a, int unit_bytes, int nontemporal, i
   const bool nt = nontemporal != 0;
   if (unit_bytes == 16 && nt && grid_cap == 0 && xcd_dst != 0) {
     // The XCD layout (k_fanout_xcd), two destinations per workgroup, windows
-    // of one block, for launches that write at least 192 MiB; smaller ones
-    // keep the tile kernel below.  Measured on MI355X against the tile
+    // of one block, for launches that write more than kFanoutNtStoreBytes
+    // (128 MiB); smaller ones keep the tile kernel below, with nontemporal
+    // stores.  All-gather p = 8 at 12 / 16 / 18 / 20 / 22 MiB per rank, tile
+    // kernel -> XCD layout: 78.6 -> 75.1, 70.7 -> 71.4, 69.5 -> 81.2, 72.5
+    // -> 78.0, 66.6 -> 84.8% of the HBM peak; broadcast 16 / 20 MiB 71.8 ->
+    // 70.8, 73.8 -> 78.3%; bfloat16 all-gather 20 MiB 72.7 -> 78.9%.  Measured on MI355X against the tile
     // kernel, % of the 8 TB/s HBM peak, the launch's buffers among two
     // rotating sets: all-gather p = 8 at 24 / 32 / 64 / 96 / 128 MiB per rank
     // 66.8 -> 80.7, 66.7 -> 78.4, 66.5 -> 76.5, 68.3 -> 86.6-87.4, 65.4 ->
@@ -277,7 +281,7 @@ hipError_t launch_fanout(const FanoutArgs& a, int unit_bytes, int nontemporal, i
     // warm translations (81-91%), falls to 46-49%; so two destinations it is.
     const uint64_t written = a.seg_bytes * static_cast<uint64_t>(a.nseg) * static_cast<uint64_t>(a.ndst);
     int D = xcd_dst;
-    if (D < 0) D = written >= (192ull << 20) ? 2 : 0;
+    if (D < 0) D = written > kFanoutNtStoreBytes ? 2 : 0;
     const uint32_t W = xcd_window > 0 ? static_cast<uint32_t>(xcd_window) : 1u;
     if (D == 1 || D == 2 || D == 4) {
       const uint64_t bps = (units + kBlock - 1) / kBlock;

@@ -580,8 +580,9 @@ hipError_t launch_gather_cols(const ColsArgs& a, int unit_bytes, int nontemporal
   if (a.rows * a.wu == 0) return hipSuccess;
   const bool nt = nontemporal != 0;
   // The XCD layout, two destinations per workgroup, for launches of 16-byte
-  // units that write at least 192 MiB (the fan-out's rule); xcd_dst forces
-  // the destinations per workgroup (1, 2, 4) or turns it off (0).
+  // units that write at least 192 MiB (as measured for this layout; the
+  // plain fan-out switches above 128 MiB); xcd_dst forces the destinations
+  // per workgroup (1, 2, 4) or turns it off (0).
   if (unit_bytes == 16 && nt && per_cu <= 0 && xcd_dst != 0) {
     const uint64_t units = a.rows * a.du;
     const uint64_t written = units * 16 * static_cast<uint64_t>(a.p);

@@ -379,12 +379,17 @@ def test_fanout_tilings_agree(rr, tuning, env):
     assert_bitwise(rows(out, "float32"), C.broadcast(x[5], p), f"broadcast {env}")
 
 
+@pytest.mark.parametrize("xcd", [None, "0"])
 @pytest.mark.parametrize("L", [524288, 524292])
-def test_fanout_store_policy_boundary(rr, L):
-    """The fan-out stores nontemporal while a launch writes at most 128 MiB
-    and plain above: an all-gather of 8 float32 shards that writes exactly
-    128 MiB, and one that writes 16 bytes per shard and rank more, give the
-    oracle's bits, as does the broadcast of the same 8L elements."""
+def test_fanout_store_policy_boundary(rr, tuning, L, xcd):
+    """The fan-out's tile kernel stores nontemporal while a launch writes at
+    most 128 MiB; above, the XCD layout takes the launch (or, with it
+    switched off, the tile kernel with plain stores): an all-gather of 8
+    float32 shards that writes exactly 128 MiB, and one that writes 16 bytes
+    per shard and rank more, give the oracle's bits, as does the broadcast of
+    the same 8L elements."""
+    if xcd is not None:
+        tuning.set("RR_FANOUT_XCD", xcd)
     p = 8
     x = W.random_inputs(15, p, L, "float32")
     full = torch.empty((p, p * L), dtype=torch.float32, device="cuda")
